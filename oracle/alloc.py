@@ -19,7 +19,9 @@ T, HD, floor(Bbar / (4 T)) rounded down to a multiple of s_T (Bbar = 2N/ratio,
 the average per-tensor budget: U_T alone may take at most half of it) and the
 numerical rank of every layer's token spectrum; R_D is the smallest of D and
 the layers' feature numerical ranks.  Numerical rank counts eigenvalues above
-n * 2^-23 * lambda_1 (fp32 working precision, n = spectrum length).
+n * 2^-23 * lambda_1 (fp32 working precision, n = the Gram's dimension,
+min(T, HD) or D).  Only the leading R_T token eigenvalues are ever read, so a
+spectrum truncated after them gives the same plan.
 
 Bytes.  The compressed record size (see ``blob_bytes``); the budget is
 floor(2 * N_total / ratio), i.e. relative to bf16 storage.
@@ -86,11 +88,12 @@ def rank_cap_T(H: int, T: int, D: int, ratio: float, step: int = 32) -> int:
     return min(T, H * D, (q // step) * step)
 
 
-def numerical_rank(lam) -> int:
+def numerical_rank(lam, n: int) -> int:
+    """Count of eigenvalues above n * 2^-23 * lambda_1 (n = Gram dimension)."""
     lam = [float(v) for v in lam]
     if not lam or lam[0] <= 0.0:
         return 0
-    thr = len(lam) * (2.0 ** -23) * lam[0]
+    thr = float(n) * (2.0 ** -23) * lam[0]
     return sum(1 for v in lam if v > thr)
 
 
@@ -150,14 +153,15 @@ def allocate(spectra, n_layers: int, H: int, T: int, D: int, ratio: float,
     n_total = N * 2 * n_layers
     budget = int(math.floor(2.0 * n_total / ratio))
     cap = r_T_cap if r_T_cap > 0 else rank_cap_T(H, T, D, ratio, step_T)
+    n_T = min(T, H * D)
     n_groups = (n_layers + group_layers - 1) // group_layers
     units = []
     for g in range(n_groups):
         layers = list(range(g * group_layers, min(n_layers, (g + 1) * group_layers)))
         for kind in (0, 1):
             specs = [spectra[l][kind] for l in layers]
-            R_T = min([cap] + [numerical_rank(s[0]) for s in specs])
-            R_D = min([D] + [numerical_rank(s[1]) for s in specs])
+            R_T = min([cap] + [numerical_rank(s[0], n_T) for s in specs])
+            R_D = min([D] + [numerical_rank(s[1], D) for s in specs])
             m = menu(R_T, R_D, bits, step_T, step_D)
             pts = []
             for i, ch in enumerate(m):
