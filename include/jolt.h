@@ -1,0 +1,202 @@
+/*
+ * jolt.h -- C ABI of the JoLT KV-cache codec hot path on AMD Instinct MI355X
+ * (CDNA4, gfx950).
+ *
+ * Method: "A JoLT for the KV Cache: Near-Lossless KV Cache Compression via
+ * Joint Tucker and JL-Residual Allocation for LLMs" (arXiv 2607.12550v2),
+ * abstract: each layer's K or V cache is a third-order tensor over heads,
+ * tokens and features; a partial Tucker decomposition compresses only the
+ * token and feature axes; a random orthogonal rotation followed by low-bit
+ * quantization restores the energy the truncation drops; one Lagrangian dual
+ * allocates Tucker ranks and residual bit-widths per layer group, separately
+ * for keys and values, under one byte budget; FlashJoLT computes the factors
+ * with a randomized SVD.
+ *
+ * Conventions for every entry point
+ *   - Tensors are X[H][T][D] row-major (D fastest), bf16 or fp32, in device
+ *     memory.  D must be 128 (the head dimension of the models the method is
+ *     evaluated on); T >= 1, H >= 1.
+ *   - Every device buffer (inputs, outputs, compressed records, workspaces)
+ *     is allocated and owned by the caller.  The library allocates no device
+ *     memory and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously unless the entry point says it synchronizes.
+ *   - Arguments are validated before any work is enqueued; on error nothing
+ *     is enqueued and no output is written.  No C++ exception crosses the ABI.
+ *   - A device-side fault surfaces as JOLT_EHIP from the next call that
+ *     synchronizes.  Calls on distinct streams with distinct workspaces may
+ *     run concurrently from several host threads.
+ */
+#ifndef JOLT_H
+#define JOLT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  JOLT_OK = 0,
+  JOLT_EINVAL = -1,     /* bad argument (shape, dtype, choice, NULL pointer) */
+  JOLT_ENOSPACE = -2,   /* workspace or record buffer too small               */
+  JOLT_EBUDGET = -3,    /* byte budget below the cheapest plan                */
+  JOLT_ERANGE = -4,     /* non-finite input                                   */
+  JOLT_EFORMAT = -5,    /* record header: bad magic, version or shape         */
+  JOLT_EHIP = -6,       /* HIP runtime error (launch, copy or device fault)   */
+  JOLT_ENODEV = -7      /* no usable gfx950 device                            */
+} jolt_status;
+
+typedef enum { JOLT_BF16 = 0, JOLT_F32 = 1 } jolt_dtype;
+typedef enum { JOLT_EXACT = 0, JOLT_FLASH = 1 } jolt_method;
+
+/* Shape of one K or V tensor of one layer. */
+typedef struct {
+  int32_t H, T, D;      /* heads, tokens, features (D == 128)                */
+  int32_t dtype;        /* jolt_dtype of the input and of decoded output     */
+} jolt_shape;
+
+/* Ranks and residual bits of one tensor.  (0, 0, b) = no Tucker part: the
+ * whole tensor is the residual.  Otherwise 1 <= r_T <= min(T, H*D),
+ * 1 <= r_D <= D.  bits in 1..4. */
+typedef struct { int32_t r_T, r_D, bits; } jolt_choice;
+
+/* Allocation request for a whole cache: n_layers layers x {K, V}, all of one
+ * shape.  Tensor index i = layer * 2 + kind (kind 0 = K, 1 = V).
+ * Source: JoLT abstract, "a single Lagrangian dual ... per layer group and
+ * separately for keys and values, under one byte budget". */
+typedef struct {
+  jolt_shape shape;
+  int32_t n_layers;
+  int32_t group_layers;   /* layers per allocation group (4)                  */
+  double budget_ratio;    /* budget = floor(2 * H*T*D * 2*n_layers / ratio) B  */
+  int32_t bit_menu[4];    /* residual bit-widths offered, each in 1..4         */
+  int32_t n_bits;         /* 1..4                                              */
+  int32_t method;         /* jolt_method                                       */
+  int32_t oversample;     /* FlashJoLT sketch oversampling p (10)              */
+  int32_t power_iters;    /* FlashJoLT power iterations q (1)                  */
+  int32_t r_T_cap;        /* 0 = min(T, HD, floor(Bbar/(4T)) to a step multiple)*/
+  int32_t step_T, step_D; /* rank grid steps (0 = 32 and 16)                   */
+  uint64_t seed;          /* seeds the sketch (FlashJoLT) and the rotation     */
+} jolt_alloc_req;
+
+/* Allocation result.  Host arrays are caller-owned; optional ones may be NULL. */
+typedef struct {
+  jolt_choice* choice;       /* out [n_groups * 2], index g * 2 + kind         */
+  uint64_t* tensor_bytes;    /* out, optional [2 * n_layers]                   */
+  double* spectra_T;         /* out, optional [2 * n_layers][jolt_spectrum_len]*/
+  double* spectra_D;         /* out, optional [2 * n_layers][D]                */
+  double* frob2;             /* out, optional [2 * n_layers]: ||X||_F^2        */
+  double objective;          /* out: predicted sum of relative squared errors  */
+  uint64_t total_bytes;      /* out: bytes of all records under the plan       */
+  uint64_t budget_bytes;     /* out                                            */
+  int32_t r_T_cap;           /* out: columns of U_T kept per tensor            */
+} jolt_plan;
+
+/* ---------------------------------------------------------------- sizes */
+
+/* Bytes of one compressed record: a 64-byte header padded to 256, then
+ * 256-aligned sections U_T bf16 [T][r_T], U_D bf16 [D][r_D], core bf16
+ * [H][r_T][r_D], scales bf16 [H][T][D/32][2] (offset, step), codes
+ * [H][T][D/32][4*bits] bytes.  0 if the arguments are invalid. */
+size_t jolt_blob_bytes(const jolt_shape* shape, jolt_choice choice);
+
+/* Device workspace needed by jolt_allocate for the request (0 if invalid). */
+size_t jolt_workspace_bytes(const jolt_alloc_req* req);
+
+/* Length of each token-mode spectrum jolt_allocate reports: the cap r_T_cap
+ * (the leading eigenvalues that the allocator and the factors use). */
+int32_t jolt_spectrum_len(const jolt_alloc_req* req);
+
+/* Device workspace of jolt_encode / jolt_decode for one tensor. */
+size_t jolt_encode_workspace_bytes(const jolt_shape* shape, jolt_choice choice);
+size_t jolt_decode_workspace_bytes(const jolt_shape* shape, jolt_choice choice);
+
+/* Bytes of a prepared rotation (jolt_rotation). */
+size_t jolt_rotation_bytes(int32_t D);
+
+/* ------------------------------------------------------------ hot path */
+
+/* Spectra, factors and allocation for a whole cache.
+ * x_dev[i] (i = layer * 2 + kind) points at tensor i on the device.
+ * Computes, per tensor, ||X||^2, the token- and feature-mode spectra and
+ * orthonormal fp32 factors (U_T: r_T_cap columns, U_D: D columns) by Gram
+ * eigendecomposition (method EXACT) or the seeded randomized SVD (FLASH),
+ * keeps the factors in ws_dev (read them with jolt_factors), copies the
+ * spectra to the host (the only synchronization: it waits on `stream`), and
+ * runs the Lagrangian dual (jolt_plan_from_spectra).  ws_bytes must be at
+ * least jolt_workspace_bytes(req).  Errors: EINVAL, ENOSPACE, EBUDGET,
+ * ERANGE (non-finite ||X||^2), EHIP. */
+jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev,
+                          void* ws_dev, size_t ws_bytes, void* stream,
+                          jolt_plan* plan);
+
+/* Device addresses of tensor i's factors inside a workspace filled by
+ * jolt_allocate: U_T fp32 [T][ld_T] (ld_T = r_T_cap, leading columns first)
+ * and U_D fp32 [D][D].  Pure pointer arithmetic, no device access. */
+jolt_status jolt_factors(const jolt_alloc_req* req, void* ws_dev, int32_t tensor,
+                         const float** U_T, int32_t* ld_T, const float** U_D);
+
+/* The seeded rotation Q (D x D, Haar: QR of a counter-based Gaussian matrix
+ * with diag(R) > 0), prepared on the host in fp64 and uploaded to q_dev
+ * (jolt_rotation_bytes(D) bytes: fp32 Q then bf16 Q).  Synchronizes `stream`.
+ * Source: JoLT abstract, "a random orthogonal rotation followed by low-bit
+ * quantization". */
+jolt_status jolt_rotation(uint64_t seed, int32_t D, void* q_dev, size_t q_bytes,
+                          void* stream);
+
+/* Encode one tensor with the given factors: stores bf16 U_T[:, :r_T],
+ * U_D[:, :r_D] and core G_h = U_T^T X_h U_D, takes the residual against the
+ * stored parts, rotates it (Y = R Q^T along features), quantizes Y in groups
+ * of 32 with per-group bf16 (offset, step) and packs the codes.  U_T_dev is
+ * fp32 [T][ld_T], U_D_dev fp32 [D][ld_D]; rot_dev is a prepared rotation.
+ * blob_bytes >= jolt_blob_bytes, ws_bytes >= jolt_encode_workspace_bytes.
+ * Asynchronous.  Errors: EINVAL, ENOSPACE, EHIP. */
+jolt_status jolt_encode(const jolt_shape* shape, const void* x_dev, jolt_choice choice,
+                        const float* U_T_dev, int32_t ld_T,
+                        const float* U_D_dev, int32_t ld_D,
+                        const void* rot_dev, uint64_t seed,
+                        void* blob_dev, size_t blob_bytes,
+                        void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Decode one record: X^_h = U_T G_h U_D^T + dequant(codes)_h Q, written to
+ * xhat_dev in shape->dtype.  shape/choice must describe the record (the
+ * device-side header is not read back).  Asynchronous. */
+jolt_status jolt_decode(const jolt_shape* shape, jolt_choice choice,
+                        const void* blob_dev, size_t blob_bytes,
+                        const void* rot_dev, void* xhat_dev,
+                        void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Group quantizer alone: rows x D fp32 rotated residual in y_dev ->
+ * scales bf16 [rows][D/32][2] and packed codes [rows][D/32][4*bits].
+ * The same arithmetic as the encode kernel's last stage. */
+jolt_status jolt_quantize(const float* y_dev, int64_t rows, int32_t D, int32_t bits,
+                          void* scales_dev, void* codes_dev, void* stream);
+
+/* ------------------------------------------------------ host-only helpers */
+
+/* The Lagrangian dual alone, on host spectra (no device access).
+ * spectra_T: [2*n_layers][len_T], spectra_D: [2*n_layers][D], frob2:
+ * [2*n_layers]; plan->choice must be allocated. */
+jolt_status jolt_plan_from_spectra(const jolt_alloc_req* req, const double* spectra_T,
+                                   int32_t len_T, const double* spectra_D,
+                                   const double* frob2, jolt_plan* plan);
+
+/* The rotation Q in fp64 on the host (D*D values, row-major). */
+jolt_status jolt_rotation_host(uint64_t seed, int32_t D, double* Q);
+
+/* Normal number `index` of the counter-based stream (seed, tag), fp64. */
+double jolt_rng_normal(uint64_t seed, uint64_t tag, uint64_t index);
+
+/* Parse a 64-byte record header. */
+jolt_status jolt_header_parse(const void* header, size_t bytes, jolt_shape* shape,
+                              jolt_choice* choice, uint64_t* seed);
+
+const char* jolt_status_str(jolt_status s);
+int32_t jolt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* JOLT_H */

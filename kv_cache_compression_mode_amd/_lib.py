@@ -1,0 +1,102 @@
+"""ctypes declarations of the C ABI in include/jolt.h (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libjolt.so")
+
+JOLT_OK, JOLT_EINVAL, JOLT_ENOSPACE, JOLT_EBUDGET = 0, -1, -2, -3
+JOLT_ERANGE, JOLT_EFORMAT, JOLT_EHIP, JOLT_ENODEV = -4, -5, -6, -7
+JOLT_BF16, JOLT_F32 = 0, 1
+JOLT_EXACT, JOLT_FLASH = 0, 1
+
+STATUS_NAMES = {0: "JOLT_OK", -1: "JOLT_EINVAL", -2: "JOLT_ENOSPACE", -3: "JOLT_EBUDGET",
+                -4: "JOLT_ERANGE", -5: "JOLT_EFORMAT", -6: "JOLT_EHIP", -7: "JOLT_ENODEV"}
+
+
+class Shape(C.Structure):
+    _fields_ = [("H", C.c_int32), ("T", C.c_int32), ("D", C.c_int32), ("dtype", C.c_int32)]
+
+
+class Choice(C.Structure):
+    _fields_ = [("r_T", C.c_int32), ("r_D", C.c_int32), ("bits", C.c_int32)]
+
+    def tuple(self):
+        return (self.r_T, self.r_D, self.bits)
+
+
+class AllocReq(C.Structure):
+    _fields_ = [("shape", Shape), ("n_layers", C.c_int32), ("group_layers", C.c_int32),
+                ("budget_ratio", C.c_double), ("bit_menu", C.c_int32 * 4), ("n_bits", C.c_int32),
+                ("method", C.c_int32), ("oversample", C.c_int32), ("power_iters", C.c_int32),
+                ("r_T_cap", C.c_int32), ("step_T", C.c_int32), ("step_D", C.c_int32),
+                ("seed", C.c_uint64)]
+
+
+class Plan(C.Structure):
+    _fields_ = [("choice", C.POINTER(Choice)), ("tensor_bytes", C.POINTER(C.c_uint64)),
+                ("spectra_T", C.POINTER(C.c_double)), ("spectra_D", C.POINTER(C.c_double)),
+                ("frob2", C.POINTER(C.c_double)), ("objective", C.c_double),
+                ("total_bytes", C.c_uint64), ("budget_bytes", C.c_uint64), ("r_T_cap", C.c_int32)]
+
+
+class JoltError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}")
+        self.status = status
+
+
+# name -> (restype, argtypes), in the order of include/jolt.h
+SIGNATURES = {
+    "jolt_blob_bytes": (C.c_size_t, [C.POINTER(Shape), Choice]),
+    "jolt_workspace_bytes": (C.c_size_t, [C.POINTER(AllocReq)]),
+    "jolt_spectrum_len": (C.c_int32, [C.POINTER(AllocReq)]),
+    "jolt_encode_workspace_bytes": (C.c_size_t, [C.POINTER(Shape), Choice]),
+    "jolt_decode_workspace_bytes": (C.c_size_t, [C.POINTER(Shape), Choice]),
+    "jolt_rotation_bytes": (C.c_size_t, [C.c_int32]),
+    "jolt_allocate": (C.c_int, [C.POINTER(AllocReq), C.POINTER(C.c_void_p), C.c_void_p, C.c_size_t,
+                                C.c_void_p, C.POINTER(Plan)]),
+    "jolt_factors": (C.c_int, [C.POINTER(AllocReq), C.c_void_p, C.c_int32, C.POINTER(C.c_void_p),
+                               C.POINTER(C.c_int32), C.POINTER(C.c_void_p)]),
+    "jolt_rotation": (C.c_int, [C.c_uint64, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "jolt_encode": (C.c_int, [C.POINTER(Shape), C.c_void_p, Choice, C.c_void_p, C.c_int32, C.c_void_p,
+                              C.c_int32, C.c_void_p, C.c_uint64, C.c_void_p, C.c_size_t, C.c_void_p,
+                              C.c_size_t, C.c_void_p]),
+    "jolt_decode": (C.c_int, [C.POINTER(Shape), Choice, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p,
+                              C.c_void_p, C.c_size_t, C.c_void_p]),
+    "jolt_quantize": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
+                                C.c_void_p]),
+    "jolt_plan_from_spectra": (C.c_int, [C.POINTER(AllocReq), C.POINTER(C.c_double), C.c_int32,
+                                         C.POINTER(C.c_double), C.POINTER(C.c_double), C.POINTER(Plan)]),
+    "jolt_rotation_host": (C.c_int, [C.c_uint64, C.c_int32, C.POINTER(C.c_double)]),
+    "jolt_rng_normal": (C.c_double, [C.c_uint64, C.c_uint64, C.c_uint64]),
+    "jolt_header_parse": (C.c_int, [C.c_void_p, C.c_size_t, C.POINTER(Shape), C.POINTER(Choice),
+                                    C.POINTER(C.c_uint64)]),
+    "jolt_status_str": (C.c_char_p, [C.c_int]),
+    "jolt_version": (C.c_int32, []),
+}
+
+_lib = None
+
+
+def lib():
+    """Load the in-tree libjolt.so; fail loudly if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m kv_cache_compression_mode_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def check(status: int, where: str) -> None:
+    if status != JOLT_OK:
+        raise JoltError(status, where)

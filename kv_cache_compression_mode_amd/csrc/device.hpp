@@ -1,0 +1,98 @@
+// Device-side helpers shared by the codec's HIP kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jolt {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return static_cast<uint16_t>(u >> 16);  // inf/nan
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Largest bf16 <= f: truncation rounds toward zero, so a negative inexact
+// value takes one more unit of magnitude.
+__device__ __forceinline__ uint16_t bf16_round_down(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t hi = u >> 16;
+  if ((u & 0xffffu) != 0u && (u >> 31) != 0u) hi += 1u;
+  return static_cast<uint16_t>(hi);
+}
+
+// Smallest bf16 >= f.
+__device__ __forceinline__ uint16_t bf16_round_up(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t hi = u >> 16;
+  if ((u & 0xffffu) != 0u && (u >> 31) == 0u) hi += 1u;
+  return static_cast<uint16_t>(hi);
+}
+
+template <typename T> __device__ __forceinline__ float load_as_f32(const T* p, int64_t i);
+template <> __device__ __forceinline__ float load_as_f32<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_bits_to_f32(p[i]);
+}
+
+// ----------------------------------------------------- counter-based RNG
+// SplitMix64 (Steele, Lea & Flood 2014): word i of the stream keyed by
+// key = mix64(seed ^ tag) is mix64(key + (i + 1) * GAMMA); normals come from
+// Box-Muller pairs of uniforms ((w >> 11) + 0.5) * 2^-53, in fp64.
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+__host__ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
+  z ^= z >> 30;
+  z *= 0xBF58476D1CE4E5B9ull;
+  z ^= z >> 27;
+  z *= 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return z;
+}
+
+__device__ __forceinline__ double rng_normal(uint64_t key, uint64_t i) {
+  const uint64_t k = i >> 1;
+  const uint64_t w1 = mix64(key + (2 * k + 1) * kGamma);
+  const uint64_t w2 = mix64(key + (2 * k + 2) * kGamma);
+  const double u1 = (static_cast<double>(w1 >> 11) + 0.5) * 0x1p-53;
+  const double u2 = (static_cast<double>(w2 >> 11) + 0.5) * 0x1p-53;
+  const double rad = sqrt(-2.0 * log(u1));
+  const double ang = 2.0 * 3.141592653589793 * u2;
+  return (i & 1) ? rad * sin(ang) : rad * cos(ang);
+}
+
+// ------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Round-robin ("circle method") pairing of n (even) slots: round r in
+// [0, n-1), pair i in [0, n/2).  Slot 0 stays, the others rotate.
+__host__ __device__ __forceinline__ int rr_slot(int k, int r, int n) {
+  return k == 0 ? 0 : 1 + (k - 1 + r) % (n - 1);
+}
+__host__ __device__ __forceinline__ void rr_pair(int i, int r, int n, int* p, int* q) {
+  *p = rr_slot(i, r, n);
+  *q = rr_slot(n - 1 - i, r, n);
+}
+
+}  // namespace jolt

@@ -1,0 +1,271 @@
+// Strided, batched fp32-accumulating GEMM on CDNA4 matrix cores, plus the
+// small streaming kernels the factor pipeline needs (sum of squares, casts,
+// Gaussian sketch, column gathers).
+//
+// The GEMM serves the codec's dense contractions whose operands are views of
+// a [H][T][D] tensor: the token unfolding X_(T)[t][h*D+d] and its transpose
+// are not plain strided matrices, so every dimension carries a two-level
+// ("segmented") stride: offset(i) = (i / len) * seg + (i % len) * stride.
+// Segment lengths are multiples of the tile edge, so a tile never straddles
+// a segment and the per-tile base is computed once.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace jolt {
+
+namespace {
+
+constexpr int BM = 64, BN = 64, BK = 16, PAD = 4;
+
+__device__ __forceinline__ int64_t dim_off(const GemmDim& d, int64_t i) {
+  return (i / d.len) * d.seg + (i % d.len) * d.stride;
+}
+
+template <typename T>
+__device__ __forceinline__ float ld(const void* p, int64_t i) {
+  return load_as_f32<T>(static_cast<const T*>(p), i);
+}
+
+// One 64x64 output tile per workgroup, 4 waves of 32x32, fp32 MFMA 32x32x2.
+template <typename TA, typename TB>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
+  __shared__ float As[BK][BM + PAD];
+  __shared__ float Bs[BK][BN + PAD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
+  const int64_t z = blockIdx.z;
+  const char* Ab = g.a_ptrs ? static_cast<const char*>(g.a_ptrs[z])
+                           : static_cast<const char*>(g.A) + z * g.a_batch * static_cast<int64_t>(sizeof(TA));
+  const char* Bb = g.b_ptrs ? static_cast<const char*>(g.b_ptrs[z])
+                           : static_cast<const char*>(g.B) + z * g.b_batch * static_cast<int64_t>(sizeof(TB));
+  const int64_t a_mbase = dim_off(g.am, m0);
+  const int64_t b_nbase = dim_off(g.bn, n0);
+  const bool a_mcontig = g.am.stride == 1;
+  const bool b_ncontig = g.bn.stride == 1;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  f32x16 acc = {};
+
+  for (int64_t k0 = 0; k0 < g.K; k0 += BK) {
+    const int64_t a_kbase = dim_off(g.ak, k0);
+    const int64_t b_kbase = dim_off(g.bk, k0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int mm, kk;
+      if (a_mcontig) { kk = tid >> 4; mm = ((tid & 15) << 2) + j; }
+      else           { mm = tid >> 2; kk = ((tid & 3) << 2) + j; }
+      float v = 0.f;
+      if (m0 + mm < g.M && k0 + kk < g.K)
+        v = ld<TA>(Ab, a_mbase + mm * g.am.stride + a_kbase + kk * g.ak.stride);
+      As[kk][mm] = v;
+      int nn, kb;
+      if (b_ncontig) { kb = tid >> 4; nn = ((tid & 15) << 2) + j; }
+      else           { nn = tid >> 2; kb = ((tid & 3) << 2) + j; }
+      float w = 0.f;
+      if (n0 + nn < g.N && k0 + kb < g.K)
+        w = ld<TB>(Bb, b_nbase + nn * g.bn.stride + b_kbase + kb * g.bk.stride);
+      Bs[kb][nn] = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 2) {
+      const float a = As[kk + (lane >> 5)][wm + (lane & 31)];
+      const float b = Bs[kk + (lane >> 5)][wn + (lane & 31)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  char* Cb = static_cast<char*>(g.C);
+  const int64_t cz = z * g.c_batch;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t m = m0 + wm + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+    const int64_t n = n0 + wn + (lane & 31);
+    if (m < g.M && n < g.N) {
+      float v = g.alpha * acc[i];
+      if (g.col_scale) v *= g.col_scale[z * g.col_scale_batch + n];
+      const int64_t off = cz + m * g.c_m + n * g.c_n;
+      if (g.c_dtype == kF32) {
+        float* C = reinterpret_cast<float*>(Cb);
+        if (g.beta != 0.f) v += g.beta * C[off];
+        C[off] = v;
+      } else {
+        uint16_t* C = reinterpret_cast<uint16_t*>(Cb);
+        C[off] = f32_to_bf16_rne(v);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- misc
+// Sum of squares in fp64, one accumulator per tensor (blockIdx.y).
+template <typename T>
+__global__ __launch_bounds__(256) void k_sumsq(const void* const* xs, int64_t n, double* out) {
+  const T* x = static_cast<const T*>(xs[blockIdx.y]);
+  double s = 0.0;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += 256ll * gridDim.x) {
+    const double v = load_as_f32<T>(x, i);
+    s += v * v;
+  }
+  s = wave_sum(s);
+  __shared__ double part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicAdd(out + blockIdx.y, part[0] + part[1] + part[2] + part[3]);
+}
+
+// Gaussian sketch: out[z][i][j] = N(seed, tag ^ (layer<<8|kind), i*cols + j), fp32.
+__global__ __launch_bounds__(256) void k_sketch(float* out, int64_t rows, int64_t cols,
+                                                 uint64_t seed, const uint64_t* tags) {
+  const int64_t n = rows * cols;
+  const uint64_t key = mix64(seed ^ tags[blockIdx.y]);
+  float* o = out + blockIdx.y * n;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += 256ll * gridDim.x)
+    o[i] = static_cast<float>(rng_normal(key, static_cast<uint64_t>(i)));
+}
+
+// fp32 [rows][ld_in] (first `cols` columns) -> bf16 [rows][cols], RNE.
+__global__ __launch_bounds__(256) void k_to_bf16(const float* in, int64_t ld_in, uint16_t* out,
+                                                  int64_t rows, int64_t cols) {
+  const int64_t n = rows * cols;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += 256ll * gridDim.x) {
+    const int64_t r = i / cols, c = i % cols;
+    out[i] = f32_to_bf16_rne(in[r * ld_in + c]);
+  }
+}
+
+// out[z][r + j*ld_out] = in[z][r*ld_in + idx[z][j]] (gather columns, emit column-major).
+__global__ __launch_bounds__(256) void k_gather_cols(const float* in, int64_t ld_in, int64_t in_batch,
+                                                      const int* idx, int64_t idx_batch,
+                                                      float* out, int64_t ld_out, int64_t out_batch,
+                                                      int64_t rows, int64_t ncols) {
+  const int64_t z = blockIdx.y;
+  const int64_t n = rows * ncols;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += 256ll * gridDim.x) {
+    const int64_t j = i / rows, r = i % rows;
+    out[z * out_batch + j * ld_out + r] = in[z * in_batch + r * ld_in + idx[z * idx_batch + j]];
+  }
+}
+
+// Sum of squares of each row of P [rows][cols] (fp64 accumulation).
+__global__ __launch_bounds__(256) void k_row_sumsq(const float* P, int64_t rows, int64_t cols,
+                                                    int64_t batch, double* out, int64_t out_batch) {
+  const int64_t z = blockIdx.y, r = blockIdx.x;
+  const float* p = P + z * batch + r * cols;
+  double s = 0.0;
+  for (int64_t c = threadIdx.x; c < cols; c += 256) { const double v = p[c]; s += v * v; }
+  s = wave_sum(s);
+  __shared__ double part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) out[z * out_batch + r] = part[0] + part[1] + part[2] + part[3];
+}
+
+// out[z][j] = sum_i A[z][j*ld + i] * B[z][j*ld + i] (column-major dots, fp64 accumulation).
+__global__ __launch_bounds__(256) void k_col_dot(const float* A, const float* B, int64_t m, int64_t ld,
+                                                  int64_t bs, double* out, int64_t out_batch) {
+  const int64_t z = blockIdx.y, j = blockIdx.x;
+  const float* a = A + z * bs + j * ld;
+  const float* b = B + z * bs + j * ld;
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < m; i += 256) s += static_cast<double>(a[i]) * b[i];
+  s = wave_sum(s);
+  __shared__ double part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) out[z * out_batch + j] = part[0] + part[1] + part[2] + part[3];
+}
+
+// Copy an n x n fp32 matrix into an n_pad x n_pad zero-padded one (batched).
+__global__ __launch_bounds__(256) void k_pad_copy(const float* in, int64_t n, int64_t in_batch,
+                                                   float* out, int64_t n_pad) {
+  const int64_t z = blockIdx.y, tot = n_pad * n_pad;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < tot; i += 256ll * gridDim.x) {
+    const int64_t r = i / n_pad, c = i % n_pad;
+    out[z * tot + i] = (r < n && c < n) ? in[z * in_batch + r * n + c] : 0.f;
+  }
+}
+
+// G_D = sum over heads of the D x D diagonal blocks of the dual Gram C (HD x HD).
+__global__ __launch_bounds__(256) void k_sum_diag_blocks(const float* C, int64_t H, int64_t D,
+                                                          float* GD) {
+  const int64_t z = blockIdx.y, HD = H * D;
+  const float* c = C + z * HD * HD;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < D * D; i += 256ll * gridDim.x) {
+    const int64_t r = i / D, k = i % D;
+    float s = 0.f;
+    for (int64_t h = 0; h < H; ++h) s += c[(h * D + r) * HD + h * D + k];
+    GD[z * D * D + i] = s;
+  }
+}
+
+int grid1(int64_t n, int cap = 4096) {
+  int64_t b = (n + 255) / 256;
+  return static_cast<int>(b < 1 ? 1 : (b > cap ? cap : b));
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& g, int batch, hipStream_t s) {
+  dim3 grid((g.M + BM - 1) / BM, (g.N + BN - 1) / BN, batch);
+  if (g.a_dtype == kBF16 && g.b_dtype == kBF16) k_gemm<uint16_t, uint16_t><<<grid, 256, 0, s>>>(g);
+  else if (g.a_dtype == kBF16) k_gemm<uint16_t, float><<<grid, 256, 0, s>>>(g);
+  else if (g.b_dtype == kBF16) k_gemm<float, uint16_t><<<grid, 256, 0, s>>>(g);
+  else k_gemm<float, float><<<grid, 256, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+hipError_t launch_sumsq(const void* const* xs_dev, int ntensors, int64_t n, int dtype, double* out,
+                        hipStream_t s) {
+  dim3 grid(grid1(n, 1024), ntensors);
+  if (dtype == kBF16) k_sumsq<uint16_t><<<grid, 256, 0, s>>>(xs_dev, n, out);
+  else k_sumsq<float><<<grid, 256, 0, s>>>(xs_dev, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sketch(float* out, int64_t rows, int64_t cols, uint64_t seed, const uint64_t* tags,
+                         int ntensors, hipStream_t s) {
+  k_sketch<<<dim3(grid1(rows * cols), ntensors), 256, 0, s>>>(out, rows, cols, seed, tags);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_bf16(const float* in, int64_t ld_in, uint16_t* out, int64_t rows, int64_t cols,
+                          hipStream_t s) {
+  k_to_bf16<<<grid1(rows * cols), 256, 0, s>>>(in, ld_in, out, rows, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_cols(const float* in, int64_t ld_in, int64_t in_batch, const int* idx,
+                              int64_t idx_batch, float* out, int64_t ld_out, int64_t out_batch,
+                              int64_t rows, int64_t ncols, int batch, hipStream_t s) {
+  k_gather_cols<<<dim3(grid1(rows * ncols), batch), 256, 0, s>>>(in, ld_in, in_batch, idx, idx_batch,
+                                                                 out, ld_out, out_batch, rows, ncols);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_sumsq(const float* P, int64_t rows, int64_t cols, int64_t batch_stride,
+                            int batch, double* out, int64_t out_batch, hipStream_t s) {
+  k_row_sumsq<<<dim3(rows, batch), 256, 0, s>>>(P, rows, cols, batch_stride, out, out_batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_col_dot(const float* A, const float* B, int64_t m, int64_t ncols, int64_t ld,
+                          int64_t batch_stride, int batch, double* out, int64_t out_batch, hipStream_t s) {
+  k_col_dot<<<dim3(ncols, batch), 256, 0, s>>>(A, B, m, ld, batch_stride, out, out_batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_copy(const float* in, int64_t n, int64_t in_batch, float* out, int64_t n_pad,
+                           int batch, hipStream_t s) {
+  k_pad_copy<<<dim3(grid1(n_pad * n_pad), batch), 256, 0, s>>>(in, n, in_batch, out, n_pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_diag_blocks(const float* C, int64_t H, int64_t D, float* GD, int batch,
+                                  hipStream_t s) {
+  k_sum_diag_blocks<<<dim3(grid1(D * D), batch), 256, 0, s>>>(C, H, D, GD);
+  return hipGetLastError();
+}
+
+}  // namespace jolt

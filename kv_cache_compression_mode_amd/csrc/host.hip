@@ -1,0 +1,870 @@
+// C ABI of the JoLT codec: argument checks, workspace layout, host algorithms
+// (counter-based RNG, Haar rotation, Lagrangian-dual allocation) and the
+// orchestration of the HIP kernels.  See include/jolt.h for the contract.
+#include "../../include/jolt.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "kernels.hpp"
+
+using namespace jolt;
+
+namespace {
+
+constexpr uint32_t kMagic = 0x544C4F4Au;      // "JOLT", little-endian
+constexpr uint32_t kVersion = 1;
+constexpr int kGroup = 32;
+constexpr int kD = 128;
+// E[(max - min)^2] of 32 iid N(0, 1), by numerical quadrature.
+constexpr double kKappa32 = 17.60642599755;
+constexpr uint64_t kTagRotation = 0x4A4F4C54524F5431ull;   // "JOLTROT1"
+constexpr uint64_t kTagSketch = 0x4A4F4C54534B5431ull;     // "JOLTSKT1"
+// Jacobi thresholds: rotate when |a_pq| > max(tau_abs_rel * trace, tau_rel * sqrt(|a_pp a_qq|)).
+constexpr float kTauRel = 4.8e-7f;
+constexpr float kTauAbsRel = 1e-7f;
+constexpr int kMaxSweeps = 30;
+
+struct HipFail {};
+inline void ck(hipError_t e) {
+  if (e != hipSuccess) throw HipFail{};
+}
+
+size_t a256(size_t n) { return (n + 255) / 256 * 256; }
+
+// ------------------------------------------------------------- host RNG
+uint64_t mix64h(uint64_t z) {
+  z ^= z >> 30;
+  z *= 0xBF58476D1CE4E5B9ull;
+  z ^= z >> 27;
+  z *= 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return z;
+}
+
+double normal_h(uint64_t key, uint64_t i) {
+  const uint64_t k = i >> 1;
+  const uint64_t w1 = mix64h(key + (2 * k + 1) * 0x9E3779B97F4A7C15ull);
+  const uint64_t w2 = mix64h(key + (2 * k + 2) * 0x9E3779B97F4A7C15ull);
+  const double u1 = (static_cast<double>(w1 >> 11) + 0.5) * 0x1p-53;
+  const double u2 = (static_cast<double>(w2 >> 11) + 0.5) * 0x1p-53;
+  const double rad = std::sqrt(-2.0 * std::log(u1));
+  const double ang = 2.0 * 3.141592653589793 * u2;
+  return (i & 1) ? rad * std::sin(ang) : rad * std::cos(ang);
+}
+
+// Haar rotation: Householder QR (fp64) of the seeded Gaussian matrix, Q with diag(R) > 0.
+void rotation_host(uint64_t seed, int D, double* Q) {
+  const uint64_t key = mix64h(seed ^ kTagRotation);
+  std::vector<double> A(static_cast<size_t>(D) * D), tau(D), sgn(D);
+  for (int i = 0; i < D * D; ++i) A[i] = normal_h(key, static_cast<uint64_t>(i));
+  auto at = [&](int r, int c) -> double& { return A[static_cast<size_t>(r) * D + c]; };
+  for (int j = 0; j < D; ++j) {
+    double sigma = 0.0;
+    for (int i = j + 1; i < D; ++i) sigma += at(i, j) * at(i, j);
+    const double alpha = at(j, j);
+    double beta = alpha, t = 0.0;
+    if (sigma > 0.0) {
+      const double nrm = std::sqrt(alpha * alpha + sigma);
+      beta = alpha >= 0.0 ? -nrm : nrm;
+      t = (beta - alpha) / beta;
+      const double sc = 1.0 / (alpha - beta);
+      for (int i = j + 1; i < D; ++i) at(i, j) *= sc;
+      for (int c = j + 1; c < D; ++c) {
+        double w = at(j, c);
+        for (int i = j + 1; i < D; ++i) w += at(i, j) * at(i, c);
+        at(j, c) -= t * w;
+        for (int i = j + 1; i < D; ++i) at(i, c) -= t * at(i, j) * w;
+      }
+    }
+    tau[j] = t;
+    sgn[j] = beta < 0.0 ? -1.0 : 1.0;
+    at(j, j) = beta;
+  }
+  // Q = H_0 ... H_{D-1}: apply reflectors back to front to the identity
+  std::vector<double> M(static_cast<size_t>(D) * D, 0.0);
+  for (int i = 0; i < D; ++i) M[static_cast<size_t>(i) * D + i] = 1.0;
+  for (int j = D - 1; j >= 0; --j) {
+    if (tau[j] == 0.0) continue;
+    for (int c = 0; c < D; ++c) {
+      double w = M[static_cast<size_t>(j) * D + c];
+      for (int i = j + 1; i < D; ++i) w += at(i, j) * M[static_cast<size_t>(i) * D + c];
+      M[static_cast<size_t>(j) * D + c] -= tau[j] * w;
+      for (int i = j + 1; i < D; ++i) M[static_cast<size_t>(i) * D + c] -= tau[j] * at(i, j) * w;
+    }
+  }
+  for (int r = 0; r < D; ++r)
+    for (int c = 0; c < D; ++c) Q[static_cast<size_t>(r) * D + c] = M[static_cast<size_t>(r) * D + c] * sgn[c];
+}
+
+// ------------------------------------------------------------ byte model
+struct BlobLayout {
+  size_t ut, ud, g, sc, cd, total;
+};
+BlobLayout blob_layout(int64_t H, int64_t T, int64_t D, jolt_choice c) {
+  const size_t groups = static_cast<size_t>(H * T * D / kGroup);
+  BlobLayout L{};
+  L.ut = 256;
+  L.ud = L.ut + a256(2ull * T * c.r_T);
+  L.g = L.ud + a256(2ull * D * c.r_D);
+  L.sc = L.g + a256(2ull * H * c.r_T * c.r_D);
+  L.cd = L.sc + a256(4ull * groups);
+  L.total = L.cd + a256(4ull * c.bits * groups);
+  return L;
+}
+
+bool shape_ok(const jolt_shape* s) {
+  return s && s->H >= 1 && s->T >= 1 && s->D == kD && (s->dtype == JOLT_BF16 || s->dtype == JOLT_F32);
+}
+bool choice_ok(const jolt_shape* s, jolt_choice c) {
+  if (c.bits < 1 || c.bits > 4) return false;
+  if (c.r_T == 0 && c.r_D == 0) return true;
+  const int64_t nT = std::min<int64_t>(s->T, static_cast<int64_t>(s->H) * s->D);
+  return c.r_T >= 1 && c.r_T <= nT && c.r_D >= 1 && c.r_D <= s->D;
+}
+
+// ---------------------------------------------------------- the dual
+int rank_cap_T(int64_t H, int64_t T, int64_t D, double ratio, int step) {
+  const double N = static_cast<double>(H * T * D);
+  const double bbar = 2.0 * N / ratio;
+  const int64_t q = static_cast<int64_t>(std::floor(bbar / (4.0 * static_cast<double>(T))));
+  return static_cast<int>(std::min<int64_t>(std::min<int64_t>(T, H * D), (q / step) * step));
+}
+int numerical_rank(const double* lam, int len, int64_t n) {
+  if (len <= 0 || !(lam[0] > 0.0)) return 0;
+  const double thr = static_cast<double>(n) * 0x1p-23 * lam[0];
+  int c = 0;
+  for (int i = 0; i < len; ++i) c += lam[i] > thr;
+  return c;
+}
+double tail(const double* lam, int len, double frob2, int r) {
+  double s = 0.0;
+  for (int i = 0; i < std::min(r, len); ++i) s += lam[i];
+  return std::max(0.0, frob2 - s);
+}
+double rho(int bits) {
+  const int L = (1 << bits) - 1;
+  return kKappa32 / (12.0 * static_cast<double>(L * L));
+}
+
+struct Pt {
+  int64_t bytes;
+  double dist;
+  int idx;
+};
+struct Seg {
+  double slope;
+  int unit;
+  int64_t start;
+  int k;
+};
+
+int steps_T(const jolt_alloc_req* r) { return r->step_T > 0 ? r->step_T : 32; }
+int steps_D(const jolt_alloc_req* r) { return r->step_D > 0 ? r->step_D : 16; }
+int cap_of(const jolt_alloc_req* r) {
+  const jolt_shape& s = r->shape;
+  return r->r_T_cap > 0 ? r->r_T_cap : rank_cap_T(s.H, s.T, s.D, r->budget_ratio, steps_T(r));
+}
+
+bool req_ok(const jolt_alloc_req* r) {
+  if (!r || !shape_ok(&r->shape) || r->n_layers < 1 || r->group_layers < 1) return false;
+  if (!(r->budget_ratio > 0.0) || !std::isfinite(r->budget_ratio)) return false;
+  if (r->n_bits < 1 || r->n_bits > 4) return false;
+  for (int i = 0; i < r->n_bits; ++i)
+    if (r->bit_menu[i] < 1 || r->bit_menu[i] > 4) return false;
+  if (r->method != JOLT_EXACT && r->method != JOLT_FLASH) return false;
+  if (r->method == JOLT_FLASH && (r->oversample < 0 || r->power_iters < 0)) return false;
+  const int64_t nT = std::min<int64_t>(r->shape.T, static_cast<int64_t>(r->shape.H) * r->shape.D);
+  const int cap = cap_of(r);
+  return cap >= 0 && cap <= nT && cap <= 2048;
+}
+
+jolt_status plan_dual(const jolt_alloc_req* req, const double* spT, int lenT, const double* spD,
+                      const double* frob2, jolt_plan* plan) {
+  const jolt_shape& s = req->shape;
+  const int L = req->n_layers, G = req->group_layers;
+  const int64_t N = static_cast<int64_t>(s.H) * s.T * s.D;
+  const int64_t n_total = N * 2 * L;
+  const int64_t budget = static_cast<int64_t>(std::floor(2.0 * static_cast<double>(n_total) / req->budget_ratio));
+  const int cap = cap_of(req);
+  const int64_t nT = std::min<int64_t>(s.T, static_cast<int64_t>(s.H) * s.D);
+  const int sT = steps_T(req), sD = steps_D(req);
+  const int n_groups = (L + G - 1) / G;
+  struct Unit {
+    int first, last;
+    std::vector<jolt_choice> menu;
+    std::vector<Pt> hull;
+  };
+  std::vector<Unit> units;
+  for (int g = 0; g < n_groups; ++g) {
+    for (int kind = 0; kind < 2; ++kind) {
+      Unit u;
+      u.first = g * G;
+      u.last = std::min(L, (g + 1) * G);
+      int RT = cap, RD = s.D;
+      for (int l = u.first; l < u.last; ++l) {
+        const int t = l * 2 + kind;
+        RT = std::min(RT, numerical_rank(spT + static_cast<size_t>(t) * lenT, lenT, nT));
+        RD = std::min(RD, numerical_rank(spD + static_cast<size_t>(t) * s.D, s.D, s.D));
+      }
+      for (int b = 0; b < req->n_bits; ++b) u.menu.push_back({0, 0, req->bit_menu[b]});
+      for (int rt = sT; rt <= RT; rt += sT)
+        for (int rd = sD; rd <= RD; rd += sD)
+          for (int b = 0; b < req->n_bits; ++b) u.menu.push_back({rt, rd, req->bit_menu[b]});
+      std::vector<Pt> pts;
+      for (int i = 0; i < static_cast<int>(u.menu.size()); ++i) {
+        const jolt_choice c = u.menu[i];
+        const int64_t nb = static_cast<int64_t>(u.last - u.first) *
+                           static_cast<int64_t>(blob_layout(s.H, s.T, s.D, c).total);
+        double dist = 0.0;
+        for (int l = u.first; l < u.last; ++l) {
+          const int t = l * 2 + kind;
+          const double f2 = frob2[t];
+          if (!(f2 > 0.0)) continue;
+          const double e = (tail(spT + static_cast<size_t>(t) * lenT, lenT, f2, c.r_T) +
+                            tail(spD + static_cast<size_t>(t) * s.D, s.D, f2, c.r_D)) / f2;
+          dist += rho(c.bits) * std::min(1.0, e);
+        }
+        pts.push_back({nb, dist, i});
+      }
+      std::sort(pts.begin(), pts.end(), [](const Pt& a, const Pt& b) {
+        if (a.bytes != b.bytes) return a.bytes < b.bytes;
+        if (a.dist != b.dist) return a.dist < b.dist;
+        return a.idx < b.idx;
+      });
+      for (const Pt& p : pts) {
+        if (!u.hull.empty() && p.dist >= u.hull.back().dist) continue;
+        while (u.hull.size() >= 2) {
+          const Pt& a = u.hull[u.hull.size() - 2];
+          const Pt& b = u.hull.back();
+          const double cross = static_cast<double>(b.bytes - a.bytes) * (p.dist - a.dist) -
+                               (b.dist - a.dist) * static_cast<double>(p.bytes - a.bytes);
+          if (cross <= 0.0) u.hull.pop_back();
+          else break;
+        }
+        u.hull.push_back(p);
+      }
+      units.push_back(std::move(u));
+    }
+  }
+  std::vector<int> pos(units.size(), 0);
+  int64_t total = 0;
+  for (const Unit& u : units) total += u.hull[0].bytes;
+  if (total > budget) return JOLT_EBUDGET;
+  std::vector<Seg> segs;
+  for (int ui = 0; ui < static_cast<int>(units.size()); ++ui) {
+    const auto& h = units[ui].hull;
+    for (int k = 0; k + 1 < static_cast<int>(h.size()); ++k) {
+      const double dB = static_cast<double>(h[k + 1].bytes - h[k].bytes);
+      const double dD = h[k].dist - h[k + 1].dist;
+      segs.push_back({dD / dB, ui, h[k].bytes, k});
+    }
+  }
+  std::sort(segs.begin(), segs.end(), [](const Seg& a, const Seg& b) {
+    if (a.slope != b.slope) return a.slope > b.slope;
+    if (a.unit != b.unit) return a.unit < b.unit;
+    return a.start < b.start;
+  });
+  for (const Seg& sg : segs) {
+    const auto& h = units[sg.unit].hull;
+    if (pos[sg.unit] != sg.k) break;   // cannot happen on a strictly convex hull
+    const int64_t step = h[sg.k + 1].bytes - h[sg.k].bytes;
+    if (total + step > budget) break;
+    total += step;
+    pos[sg.unit] = sg.k + 1;
+  }
+  double obj = 0.0;
+  for (int ui = 0; ui < static_cast<int>(units.size()); ++ui) {
+    const Unit& u = units[ui];
+    const Pt& p = u.hull[pos[ui]];
+    const jolt_choice c = u.menu[p.idx];
+    plan->choice[ui] = c;
+    obj += p.dist;
+    if (plan->tensor_bytes)
+      for (int l = u.first; l < u.last; ++l)
+        plan->tensor_bytes[l * 2 + (ui & 1)] = blob_layout(s.H, s.T, s.D, c).total;
+  }
+  plan->objective = obj;
+  plan->total_bytes = static_cast<uint64_t>(total);
+  plan->budget_bytes = static_cast<uint64_t>(budget);
+  plan->r_T_cap = cap;
+  return JOLT_OK;
+}
+
+// --------------------------------------------------- allocate workspace
+struct Carver {
+  size_t off = 0;
+  char* base = nullptr;
+  template <typename T> T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += a256(count * sizeof(T));
+    return p;
+  }
+};
+
+int64_t pad64(int64_t n) { return (n + 63) / 64 * 64; }
+
+struct AllocWS {
+  // persistent
+  float* UT; float* UD; double* lamT; double* lamD; double* frob2;
+  const void** xptrs; uint64_t* tags;
+  // scratch (chunk tensors)
+  float* G; float* V; float* J; int* active; int* rot; float* tauabs;
+  float* GD; float* GDc; float* VD;
+  int* order; float* Ucm; float* Vr; float* P; double* lam_tmp; float* qtau; int* perm; float* sgn;
+  float* Om; float* Y; float* Z; float* Bm; float* Wr; float* Wd;
+  size_t bytes;
+  int chunk;
+};
+
+struct Dims {
+  int64_t H, T, D, HD, nT, R, n_pad, ell, ell_pad;
+  bool dual, flash;
+};
+
+Dims dims_of(const jolt_alloc_req* r) {
+  Dims d{};
+  d.H = r->shape.H; d.T = r->shape.T; d.D = r->shape.D; d.HD = d.H * d.D;
+  d.nT = std::min(d.T, d.HD);
+  d.R = cap_of(r);
+  d.flash = r->method == JOLT_FLASH;
+  d.dual = d.T > d.HD;
+  d.n_pad = pad64(d.nT);
+  d.ell = std::min<int64_t>(d.R + r->oversample, d.nT);
+  d.ell_pad = pad64(d.ell);
+  return d;
+}
+
+AllocWS carve_alloc(const jolt_alloc_req* r, void* base) {
+  const Dims d = dims_of(r);
+  const int nt = 2 * r->n_layers;
+  AllocWS w{};
+  // scratch per tensor drives the chunk size (bounded by 4 GiB of scratch)
+  size_t per = 0;
+  if (!d.flash) per = 3 * static_cast<size_t>(d.n_pad) * d.n_pad * 4;
+  else per = static_cast<size_t>(d.T) * d.ell * 4 * 2 + static_cast<size_t>(d.HD) * d.ell * 12 +
+             static_cast<size_t>(d.ell_pad) * d.ell_pad * 12;
+  per += static_cast<size_t>(std::max(d.T, d.HD)) * std::max<int64_t>(d.R, 1) * 8 + (1 << 20);
+  int chunk = static_cast<int>(std::max<size_t>(1, std::min<size_t>(64, (4ull << 30) / per)));
+  chunk = std::min(chunk, nt);
+  w.chunk = chunk;
+  Carver c;
+  c.base = static_cast<char*>(base);
+  const int64_t R = std::max<int64_t>(d.R, 1);
+  w.UT = c.take<float>(static_cast<size_t>(nt) * d.T * R);
+  w.UD = c.take<float>(static_cast<size_t>(nt) * d.D * d.D);
+  w.lamT = c.take<double>(static_cast<size_t>(nt) * R);
+  w.lamD = c.take<double>(static_cast<size_t>(nt) * d.D);
+  w.frob2 = c.take<double>(nt);
+  w.xptrs = c.take<const void*>(chunk);
+  w.tags = c.take<uint64_t>(chunk);
+  const int64_t n = d.flash ? d.ell_pad : d.n_pad;
+  w.G = c.take<float>(static_cast<size_t>(chunk) * n * n);
+  w.V = c.take<float>(static_cast<size_t>(chunk) * n * n);
+  w.J = c.take<float>(static_cast<size_t>(chunk) * (n / 64) * 64 * 64);
+  w.active = c.take<int>(static_cast<size_t>(chunk) * (n / 64));
+  w.rot = c.take<int>(chunk);
+  w.tauabs = c.take<float>(chunk);
+  w.GD = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
+  w.GDc = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
+  w.VD = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
+  w.order = c.take<int>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
+  w.Ucm = c.take<float>(static_cast<size_t>(chunk) * d.T * R);
+  w.Vr = c.take<float>(static_cast<size_t>(chunk) * std::max(d.nT, d.D) * std::max<int64_t>(R, d.D));
+  w.P = c.take<float>(static_cast<size_t>(chunk) * R * d.HD);
+  w.lam_tmp = c.take<double>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
+  w.qtau = c.take<float>(static_cast<size_t>(chunk) * 2 * std::max<int64_t>(std::max(R, d.ell), d.D));
+  w.perm = c.take<int>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
+  w.sgn = c.take<float>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
+  if (d.flash) {
+    w.Om = c.take<float>(static_cast<size_t>(chunk) * d.HD * d.ell);
+    w.Y = c.take<float>(static_cast<size_t>(chunk) * d.T * d.ell);
+    w.Z = c.take<float>(static_cast<size_t>(chunk) * d.HD * d.ell);
+    w.Bm = c.take<float>(static_cast<size_t>(chunk) * d.ell * d.HD);
+    w.Wr = c.take<float>(static_cast<size_t>(chunk) * d.ell * R);
+  }
+  w.Wd = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
+  w.bytes = c.off;
+  return w;
+}
+
+// ------------------------------------------------- factor pipeline pieces
+GemmArgs gemm0() {
+  GemmArgs g{};
+  g.am = g.ak = g.bk = g.bn = plain(1);
+  g.alpha = 1.f;
+  g.a_dtype = g.b_dtype = g.c_dtype = kF32;
+  return g;
+}
+
+// Jacobi to convergence on `batch` n x n matrices in w.G (V -> w.V); host loop
+// over sweeps, stopping when a sweep applies no rotation.
+void run_jacobi(float* A, float* V, int64_t n, int batch, const AllocWS& w, hipStream_t s) {
+  JacobiWork jw{A, V, n, batch, w.J, w.active, w.rot, w.tauabs};
+  ck(jacobi_init(jw, kTauAbsRel, s));
+  const int nb = static_cast<int>(n / 32);
+  std::vector<int> cnt(batch);
+  for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
+    ck(hipMemsetAsync(w.rot, 0, sizeof(int) * batch, s));
+    for (int r = 0; r < nb - 1; ++r) ck(jacobi_round(jw, r, kTauRel, s));
+    ck(hipMemcpyAsync(cnt.data(), w.rot, sizeof(int) * batch, hipMemcpyDeviceToHost, s));
+    ck(hipStreamSynchronize(s));
+    bool any = false;
+    for (int v : cnt) any |= v != 0;
+    if (!any) break;
+  }
+}
+
+// Feature-mode factor of `batch` tensors from their D x D Grams in w.GD.
+void feature_factor(const Dims& d, int batch, int t0, const AllocWS& w, hipStream_t s) {
+  const int64_t D = d.D;
+  ck(hipMemcpyAsync(w.GDc, w.GD, sizeof(float) * batch * D * D, hipMemcpyDeviceToDevice, s));
+  ck(jacobi_small128(w.GD, w.VD, batch, kTauRel, kTauAbsRel, kMaxSweeps, s));
+  ck(topk_diag(w.GD, D, batch, static_cast<int>(D), w.order, s));
+  ck(launch_gather_cols(w.VD, D, D * D, w.order, D, w.Vr, D, D * D, D, D, batch, s));
+  ck(householder_qr(w.Vr, D, D, D, D * D, batch, w.qtau, s));
+  // Rayleigh quotients diag(U^T G U): W = G U (column-major), then column dots
+  GemmArgs g = gemm0();
+  g.M = D; g.N = D; g.K = D;
+  g.A = w.GDc; g.am = plain(D); g.ak = plain(1); g.a_batch = D * D;
+  g.B = w.Vr; g.bk = plain(1); g.bn = plain(D); g.b_batch = D * D;
+  g.C = w.Wd; g.c_m = 1; g.c_n = D; g.c_batch = D * D;
+  ck(launch_gemm(g, batch, s));
+  ck(launch_col_dot(w.Vr, w.Wd, D, D, D, D * D, batch, w.lam_tmp, D, s));
+  ck(finalize_factor_ws(w.Vr, D, D, D, D * D, w.lam_tmp, D, w.UD + static_cast<size_t>(t0) * D * D, D,
+                        D * D, w.lamD + static_cast<size_t>(t0) * D, D, batch, w.perm, w.sgn, s));
+}
+
+// Token-mode eigenvalues as Rayleigh quotients ||X_(T)^T u_j||^2 of the
+// orthonormal column-major U (T x R), then sort/sign/emit.
+void token_finalize(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, hipStream_t s) {
+  const int64_t T = d.T, HD = d.HD, D = d.D, R = d.R;
+  GemmArgs g = gemm0();
+  g.M = R; g.N = HD; g.K = T;
+  g.A = w.Ucm; g.am = plain(T); g.ak = plain(1); g.a_batch = T * R;
+  g.b_ptrs = reinterpret_cast<const void* const*>(w.xptrs); g.b_dtype = xdt;
+  g.bk = plain(D); g.bn = segmented(D, T * D, 1);
+  g.C = w.P; g.c_m = HD; g.c_n = 1; g.c_batch = R * HD;
+  ck(launch_gemm(g, batch, s));
+  ck(launch_row_sumsq(w.P, R, HD, R * HD, batch, w.lam_tmp, R, s));
+  ck(finalize_factor_ws(w.Ucm, T, R, T, T * R, w.lam_tmp, R, w.UT + static_cast<size_t>(t0) * T * R, R,
+                        T * R, w.lamT + static_cast<size_t>(t0) * R, R, batch, w.perm, w.sgn, s));
+}
+
+void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, hipStream_t s) {
+  const int64_t T = d.T, D = d.D, HD = d.HD, n = d.n_pad, R = d.R;
+  const void* const* xp = reinterpret_cast<const void* const*>(w.xptrs);
+  ck(hipMemsetAsync(w.G, 0, sizeof(float) * batch * n * n, s));
+  GemmArgs g = gemm0();
+  g.a_ptrs = xp; g.b_ptrs = xp; g.a_dtype = g.b_dtype = xdt;
+  if (d.dual) {   // C = X_(T)^T X_(T), HD x HD
+    g.M = HD; g.N = HD; g.K = T;
+    g.am = segmented(D, T * D, 1); g.ak = plain(D);
+    g.bk = plain(D); g.bn = segmented(D, T * D, 1);
+  } else {        // G_T = X_(T) X_(T)^T, T x T
+    g.M = T; g.N = T; g.K = HD;
+    g.am = plain(D); g.ak = segmented(D, T * D, 1);
+    g.bk = segmented(D, T * D, 1); g.bn = plain(D);
+  }
+  g.C = w.G; g.c_m = n; g.c_n = 1; g.c_batch = n * n;
+  ck(launch_gemm(g, batch, s));
+  if (d.dual) {
+    ck(launch_sum_diag_blocks(w.G, d.H, D, w.GD, batch, s));   // n == HD here
+  } else {
+    GemmArgs gd = gemm0();
+    gd.a_ptrs = xp; gd.b_ptrs = xp; gd.a_dtype = gd.b_dtype = xdt;
+    gd.M = D; gd.N = D; gd.K = d.H * T;
+    gd.am = plain(1); gd.ak = plain(D); gd.bk = plain(D); gd.bn = plain(1);
+    gd.C = w.GD; gd.c_m = D; gd.c_n = 1; gd.c_batch = D * D;
+    ck(launch_gemm(gd, batch, s));
+  }
+  feature_factor(d, batch, t0, w, s);
+  if (R == 0) return;
+  run_jacobi(w.G, w.V, n, batch, w, s);
+  ck(topk_diag(w.G, n, batch, static_cast<int>(R), w.order, s));
+  if (d.dual) {
+    // V_R (HD x R, column-major), then U' = X_(T) V_R (T x R, column-major)
+    ck(launch_gather_cols(w.V, n, n * n, w.order, R, w.Vr, HD, HD * R, HD, R, batch, s));
+    GemmArgs gu = gemm0();
+    gu.a_ptrs = xp; gu.a_dtype = xdt;
+    gu.M = T; gu.N = R; gu.K = HD;
+    gu.am = plain(D); gu.ak = segmented(D, T * D, 1);
+    gu.B = w.Vr; gu.bk = plain(1); gu.bn = plain(HD); gu.b_batch = HD * R;
+    gu.C = w.Ucm; gu.c_m = 1; gu.c_n = T; gu.c_batch = T * R;
+    ck(launch_gemm(gu, batch, s));
+  } else {
+    ck(launch_gather_cols(w.V, n, n * n, w.order, R, w.Ucm, T, T * R, T, R, batch, s));
+  }
+  ck(householder_qr(w.Ucm, T, R, T, T * R, batch, w.qtau, s));
+  token_finalize(d, batch, t0, w, xdt, s);
+}
+
+void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, int q, uint64_t seed,
+                   hipStream_t s) {
+  const int64_t T = d.T, D = d.D, HD = d.HD, R = d.R, ell = d.ell, ep = d.ell_pad;
+  const void* const* xp = reinterpret_cast<const void* const*>(w.xptrs);
+  // feature mode: exact Gram path (a sketch of width D spans all of R^D)
+  {
+    GemmArgs gd = gemm0();
+    gd.a_ptrs = xp; gd.b_ptrs = xp; gd.a_dtype = gd.b_dtype = xdt;
+    gd.M = D; gd.N = D; gd.K = d.H * T;
+    gd.am = plain(1); gd.ak = plain(D); gd.bk = plain(D); gd.bn = plain(1);
+    gd.C = w.GD; gd.c_m = D; gd.c_n = 1; gd.c_batch = D * D;
+    ck(launch_gemm(gd, batch, s));
+    feature_factor(d, batch, t0, w, s);
+  }
+  if (R == 0) return;
+  ck(launch_sketch(w.Om, HD, ell, seed, w.tags, batch, s));
+  auto AY = [&](const float* Bsrc, int64_t ldb, bool b_rowmajor, float* out) {
+    // out (T x ell, column-major) = X_(T) B, B is HD x ell
+    GemmArgs g = gemm0();
+    g.a_ptrs = xp; g.a_dtype = xdt;
+    g.M = T; g.N = ell; g.K = HD;
+    g.am = plain(D); g.ak = segmented(D, T * D, 1);
+    g.B = Bsrc;
+    if (b_rowmajor) { g.bk = plain(ldb); g.bn = plain(1); }
+    else { g.bk = plain(1); g.bn = plain(ldb); }
+    g.b_batch = HD * ell;
+    g.C = out; g.c_m = 1; g.c_n = T; g.c_batch = T * ell;
+    ck(launch_gemm(g, batch, s));
+  };
+  AY(w.Om, ell, true, w.Y);
+  ck(householder_qr(w.Y, T, ell, T, T * ell, batch, w.qtau, s));
+  for (int it = 0; it < q; ++it) {
+    GemmArgs g = gemm0();                       // Z = X_(T)^T Q (HD x ell, column-major)
+    g.a_ptrs = xp; g.a_dtype = xdt;
+    g.M = HD; g.N = ell; g.K = T;
+    g.am = segmented(D, T * D, 1); g.ak = plain(D);
+    g.B = w.Y; g.bk = plain(1); g.bn = plain(T); g.b_batch = T * ell;
+    g.C = w.Z; g.c_m = 1; g.c_n = HD; g.c_batch = HD * ell;
+    ck(launch_gemm(g, batch, s));
+    ck(householder_qr(w.Z, HD, ell, HD, HD * ell, batch, w.qtau, s));
+    AY(w.Z, HD, false, w.Y);
+    ck(householder_qr(w.Y, T, ell, T, T * ell, batch, w.qtau, s));
+  }
+  {
+    GemmArgs g = gemm0();                       // B = Q^T X_(T) (ell x HD, row-major)
+    g.M = ell; g.N = HD; g.K = T;
+    g.A = w.Y; g.am = plain(T); g.ak = plain(1); g.a_batch = T * ell;
+    g.b_ptrs = xp; g.b_dtype = xdt; g.bk = plain(D); g.bn = segmented(D, T * D, 1);
+    g.C = w.Bm; g.c_m = HD; g.c_n = 1; g.c_batch = ell * HD;
+    ck(launch_gemm(g, batch, s));
+  }
+  ck(hipMemsetAsync(w.G, 0, sizeof(float) * batch * ep * ep, s));
+  {
+    GemmArgs g = gemm0();                       // M = B B^T (ell x ell, padded)
+    g.M = ell; g.N = ell; g.K = HD;
+    g.A = w.Bm; g.am = plain(HD); g.ak = plain(1); g.a_batch = ell * HD;
+    g.B = w.Bm; g.bk = plain(1); g.bn = plain(HD); g.b_batch = ell * HD;
+    g.C = w.G; g.c_m = ep; g.c_n = 1; g.c_batch = ep * ep;
+    ck(launch_gemm(g, batch, s));
+  }
+  run_jacobi(w.G, w.V, ep, batch, w, s);
+  ck(topk_diag(w.G, ep, batch, static_cast<int>(R), w.order, s));
+  ck(launch_gather_cols(w.V, ep, ep * ep, w.order, R, w.Wr, ell, ell * R, ell, R, batch, s));
+  {
+    GemmArgs g = gemm0();                       // U = Q W_R (T x R, column-major)
+    g.M = T; g.N = R; g.K = ell;
+    g.A = w.Y; g.am = plain(1); g.ak = plain(T); g.a_batch = T * ell;
+    g.B = w.Wr; g.bk = plain(1); g.bn = plain(ell); g.b_batch = ell * R;
+    g.C = w.Ucm; g.c_m = 1; g.c_n = T; g.c_batch = T * R;
+    ck(launch_gemm(g, batch, s));
+  }
+  ck(householder_qr(w.Ucm, T, R, T, T * R, batch, w.qtau, s));
+  token_finalize(d, batch, t0, w, xdt, s);
+}
+
+template <typename F>
+jolt_status guard(F&& f) {
+  try {
+    return f();
+  } catch (const HipFail&) {
+    return JOLT_EHIP;
+  } catch (...) {
+    return JOLT_EHIP;
+  }
+}
+
+}  // namespace
+
+// ================================================================== ABI
+extern "C" {
+
+size_t jolt_blob_bytes(const jolt_shape* shape, jolt_choice choice) {
+  if (!shape_ok(shape) || !choice_ok(shape, choice)) return 0;
+  return blob_layout(shape->H, shape->T, shape->D, choice).total;
+}
+
+size_t jolt_workspace_bytes(const jolt_alloc_req* req) {
+  if (!req_ok(req)) return 0;
+  return carve_alloc(req, nullptr).bytes;
+}
+
+int32_t jolt_spectrum_len(const jolt_alloc_req* req) {
+  if (!req_ok(req)) return 0;
+  return cap_of(req);
+}
+
+size_t jolt_encode_workspace_bytes(const jolt_shape* shape, jolt_choice c) {
+  if (!shape_ok(shape) || !choice_ok(shape, c)) return 0;
+  return 2 * a256(4ull * shape->H * c.r_T * shape->D) + 256;
+}
+
+size_t jolt_decode_workspace_bytes(const jolt_shape* shape, jolt_choice c) {
+  if (!shape_ok(shape) || !choice_ok(shape, c)) return 0;
+  return a256(4ull * shape->H * c.r_T * shape->D) + 256;
+}
+
+size_t jolt_rotation_bytes(int32_t D) {
+  if (D != kD) return 0;
+  return a256(4ull * D * D) * 2 + a256(2ull * D * D);
+}
+
+jolt_status jolt_plan_from_spectra(const jolt_alloc_req* req, const double* spectra_T, int32_t len_T,
+                                   const double* spectra_D, const double* frob2, jolt_plan* plan) {
+  if (!req_ok(req) || !spectra_T || !spectra_D || !frob2 || !plan || !plan->choice) return JOLT_EINVAL;
+  if (len_T < cap_of(req)) return JOLT_EINVAL;
+  const int nt = 2 * req->n_layers;
+  for (int i = 0; i < nt; ++i)
+    if (!std::isfinite(frob2[i])) return JOLT_ERANGE;
+  return plan_dual(req, spectra_T, len_T, spectra_D, frob2, plan);
+}
+
+jolt_status jolt_rotation_host(uint64_t seed, int32_t D, double* Q) {
+  if (D < 1 || D > 4096 || !Q) return JOLT_EINVAL;
+  rotation_host(seed, D, Q);
+  return JOLT_OK;
+}
+
+double jolt_rng_normal(uint64_t seed, uint64_t tag, uint64_t index) {
+  return normal_h(mix64h(seed ^ tag), index);
+}
+
+jolt_status jolt_rotation(uint64_t seed, int32_t D, void* q_dev, size_t q_bytes, void* stream) {
+  if (D != kD || !q_dev) return JOLT_EINVAL;
+  if (q_bytes < jolt_rotation_bytes(D)) return JOLT_ENOSPACE;
+  return guard([&]() -> jolt_status {
+    std::vector<double> Q(static_cast<size_t>(D) * D);
+    rotation_host(seed, D, Q.data());
+    const size_t n = static_cast<size_t>(D) * D;
+    std::vector<float> buf(2 * n);
+    std::vector<uint16_t> b16(n);
+    for (size_t i = 0; i < n; ++i) {
+      const size_t r = i / D, c = i % D;
+      buf[i] = static_cast<float>(Q[i]);
+      buf[n + c * D + r] = static_cast<float>(Q[i]);       // Q^T
+      // bf16 nearest-even of the fp64 value via its fp32 rounding
+      float f = static_cast<float>(Q[i]);
+      uint32_t u;
+      std::memcpy(&u, &f, 4);
+      u += 0x7fffu + ((u >> 16) & 1u);
+      b16[i] = static_cast<uint16_t>(u >> 16);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* base = static_cast<char*>(q_dev);
+    ck(hipMemcpyAsync(base, buf.data(), 4 * n, hipMemcpyHostToDevice, s));
+    ck(hipMemcpyAsync(base + a256(4 * n), buf.data() + n, 4 * n, hipMemcpyHostToDevice, s));
+    ck(hipMemcpyAsync(base + 2 * a256(4 * n), b16.data(), 2 * n, hipMemcpyHostToDevice, s));
+    ck(hipStreamSynchronize(s));
+    return JOLT_OK;
+  });
+}
+
+jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, void* ws_dev,
+                          size_t ws_bytes, void* stream, jolt_plan* plan) {
+  if (!req_ok(req) || !x_dev || !ws_dev || !plan || !plan->choice) return JOLT_EINVAL;
+  const int nt = 2 * req->n_layers;
+  for (int i = 0; i < nt; ++i)
+    if (!x_dev[i]) return JOLT_EINVAL;
+  const AllocWS w = carve_alloc(req, ws_dev);
+  if (ws_bytes < w.bytes) return JOLT_ENOSPACE;
+  return guard([&]() -> jolt_status {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const Dims d = dims_of(req);
+    const int xdt = req->shape.dtype == JOLT_BF16 ? kBF16 : kF32;
+    const int64_t N = d.H * d.T * d.D;
+    ck(hipMemsetAsync(w.frob2, 0, sizeof(double) * nt, s));
+    for (int t0 = 0; t0 < nt; t0 += w.chunk) {
+      const int batch = std::min(w.chunk, nt - t0);
+      std::vector<const void*> ptrs(x_dev + t0, x_dev + t0 + batch);
+      std::vector<uint64_t> tags(batch);
+      for (int i = 0; i < batch; ++i) {
+        const int t = t0 + i;
+        tags[i] = kTagSketch ^ ((static_cast<uint64_t>(t / 2) << 8) | static_cast<uint64_t>(t % 2));
+      }
+      ck(hipMemcpyAsync(w.xptrs, ptrs.data(), sizeof(void*) * batch, hipMemcpyHostToDevice, s));
+      ck(hipMemcpyAsync(w.tags, tags.data(), sizeof(uint64_t) * batch, hipMemcpyHostToDevice, s));
+      ck(hipStreamSynchronize(s));
+      ck(launch_sumsq(reinterpret_cast<const void* const*>(w.xptrs), batch, N, xdt, w.frob2 + t0, s));
+      if (d.flash) analyze_flash(d, batch, t0, w, xdt, req->power_iters, req->seed, s);
+      else analyze_exact(d, batch, t0, w, xdt, s);
+    }
+    const int R = static_cast<int>(d.R);
+    std::vector<double> lt(static_cast<size_t>(nt) * std::max(R, 1)), ld(static_cast<size_t>(nt) * d.D), f2(nt);
+    if (R > 0) ck(hipMemcpyAsync(lt.data(), w.lamT, sizeof(double) * nt * R, hipMemcpyDeviceToHost, s));
+    ck(hipMemcpyAsync(ld.data(), w.lamD, sizeof(double) * nt * d.D, hipMemcpyDeviceToHost, s));
+    ck(hipMemcpyAsync(f2.data(), w.frob2, sizeof(double) * nt, hipMemcpyDeviceToHost, s));
+    ck(hipStreamSynchronize(s));
+    for (int i = 0; i < nt; ++i)
+      if (!std::isfinite(f2[i])) return JOLT_ERANGE;
+    if (plan->spectra_T && R > 0) std::memcpy(plan->spectra_T, lt.data(), sizeof(double) * nt * R);
+    if (plan->spectra_D) std::memcpy(plan->spectra_D, ld.data(), sizeof(double) * nt * d.D);
+    if (plan->frob2) std::memcpy(plan->frob2, f2.data(), sizeof(double) * nt);
+    return plan_dual(req, lt.data(), std::max(R, 1), ld.data(), f2.data(), plan);
+  });
+}
+
+jolt_status jolt_factors(const jolt_alloc_req* req, void* ws_dev, int32_t tensor, const float** U_T,
+                         int32_t* ld_T, const float** U_D) {
+  if (!req_ok(req) || !ws_dev || tensor < 0 || tensor >= 2 * req->n_layers) return JOLT_EINVAL;
+  const AllocWS w = carve_alloc(req, ws_dev);
+  const Dims d = dims_of(req);
+  const int64_t R = std::max<int64_t>(d.R, 1);
+  if (U_T) *U_T = w.UT + static_cast<size_t>(tensor) * d.T * R;
+  if (ld_T) *ld_T = static_cast<int32_t>(R);
+  if (U_D) *U_D = w.UD + static_cast<size_t>(tensor) * d.D * d.D;
+  return JOLT_OK;
+}
+
+jolt_status jolt_encode(const jolt_shape* shape, const void* x_dev, jolt_choice c, const float* U_T_dev,
+                        int32_t ld_T, const float* U_D_dev, int32_t ld_D, const void* rot_dev, uint64_t seed,
+                        void* blob_dev, size_t blob_bytes, void* ws_dev, size_t ws_bytes, void* stream) {
+  if (!shape_ok(shape) || !choice_ok(shape, c) || !x_dev || !rot_dev || !blob_dev) return JOLT_EINVAL;
+  const bool tucker = c.r_T > 0;
+  if (tucker && (!U_T_dev || !U_D_dev || ld_T < c.r_T || ld_D < c.r_D || !ws_dev)) return JOLT_EINVAL;
+  const BlobLayout L = blob_layout(shape->H, shape->T, shape->D, c);
+  if (blob_bytes < L.total) return JOLT_ENOSPACE;
+  if (tucker && ws_bytes < jolt_encode_workspace_bytes(shape, c)) return JOLT_ENOSPACE;
+  return guard([&]() -> jolt_status {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t H = shape->H, T = shape->T, D = shape->D, rT = c.r_T, rD = c.r_D;
+    const int xdt = shape->dtype == JOLT_BF16 ? kBF16 : kF32;
+    char* blob = static_cast<char*>(blob_dev);
+    uint16_t* Ut = reinterpret_cast<uint16_t*>(blob + L.ut);
+    uint16_t* Ud = reinterpret_cast<uint16_t*>(blob + L.ud);
+    uint16_t* G = reinterpret_cast<uint16_t*>(blob + L.g);
+    float* W = static_cast<float*>(ws_dev);
+    float* P = W + a256(4ull * H * rT * D) / 4;
+    const size_t n = static_cast<size_t>(D) * D;
+    const float* Qt = reinterpret_cast<const float*>(static_cast<const char*>(rot_dev) + a256(4 * n));
+    if (tucker) {
+      ck(launch_to_bf16(U_T_dev, ld_T, Ut, T, rT, s));
+      ck(launch_to_bf16(U_D_dev, ld_D, Ud, D, rD, s));
+      GemmArgs g = gemm0();                      // P_h = U~_T^T X_h  (r_T x D)
+      g.M = rT; g.N = D; g.K = T;
+      g.A = Ut; g.a_dtype = kBF16; g.am = plain(1); g.ak = plain(rT); g.a_batch = 0;
+      g.B = x_dev; g.b_dtype = xdt; g.bk = plain(D); g.bn = plain(1); g.b_batch = T * D;
+      g.C = P; g.c_m = D; g.c_n = 1; g.c_batch = rT * D;
+      ck(launch_gemm(g, static_cast<int>(H), s));
+      GemmArgs g2 = gemm0();                     // G~_h = bf16(P_h U~_D)  (r_T x r_D)
+      g2.M = rT; g2.N = rD; g2.K = D;
+      g2.A = P; g2.am = plain(D); g2.ak = plain(1); g2.a_batch = rT * D;
+      g2.B = Ud; g2.b_dtype = kBF16; g2.bk = plain(rD); g2.bn = plain(1); g2.b_batch = 0;
+      g2.C = G; g2.c_dtype = kBF16; g2.c_m = rD; g2.c_n = 1; g2.c_batch = rT * rD;
+      ck(launch_gemm(g2, static_cast<int>(H), s));
+      GemmArgs g3 = gemm0();                     // W_h = G~_h U~_D^T  (r_T x D)
+      g3.M = rT; g3.N = D; g3.K = rD;
+      g3.A = G; g3.a_dtype = kBF16; g3.am = plain(rD); g3.ak = plain(1); g3.a_batch = rT * rD;
+      g3.B = Ud; g3.b_dtype = kBF16; g3.bk = plain(1); g3.bn = plain(rD); g3.b_batch = 0;
+      g3.C = W; g3.c_m = D; g3.c_n = 1; g3.c_batch = rT * D;
+      ck(launch_gemm(g3, static_cast<int>(H), s));
+    }
+    EncodeArgs ea{};
+    ea.X = x_dev; ea.x_dtype = xdt; ea.H = H; ea.T = T;
+    ea.Ut = tucker ? Ut : nullptr; ea.W = W; ea.r_T = rT;
+    ea.Qt = Qt; ea.bits = c.bits;
+    ea.scales = reinterpret_cast<uint16_t*>(blob + L.sc);
+    ea.codes = reinterpret_cast<uint8_t*>(blob + L.cd);
+    ck(launch_encode_residual(ea, s));
+    const uint32_t hdr[16] = {kMagic, kVersion, static_cast<uint32_t>(H), static_cast<uint32_t>(T),
+                              static_cast<uint32_t>(D), static_cast<uint32_t>(shape->dtype),
+                              static_cast<uint32_t>(rT), static_cast<uint32_t>(rD),
+                              static_cast<uint32_t>(c.bits), static_cast<uint32_t>(kGroup),
+                              static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), 0, 0, 0, 0};
+    ck(launch_write_header(blob, hdr, s));
+    return JOLT_OK;
+  });
+}
+
+jolt_status jolt_decode(const jolt_shape* shape, jolt_choice c, const void* blob_dev, size_t blob_bytes,
+                        const void* rot_dev, void* xhat_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  if (!shape_ok(shape) || !choice_ok(shape, c) || !blob_dev || !rot_dev || !xhat_dev) return JOLT_EINVAL;
+  const bool tucker = c.r_T > 0;
+  const BlobLayout L = blob_layout(shape->H, shape->T, shape->D, c);
+  if (blob_bytes < L.total) return JOLT_ENOSPACE;
+  if (tucker && (!ws_dev || ws_bytes < jolt_decode_workspace_bytes(shape, c))) return JOLT_ENOSPACE;
+  return guard([&]() -> jolt_status {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t H = shape->H, T = shape->T, D = shape->D, rT = c.r_T, rD = c.r_D;
+    const char* blob = static_cast<const char*>(blob_dev);
+    const uint16_t* Ut = reinterpret_cast<const uint16_t*>(blob + L.ut);
+    const uint16_t* Ud = reinterpret_cast<const uint16_t*>(blob + L.ud);
+    const uint16_t* G = reinterpret_cast<const uint16_t*>(blob + L.g);
+    float* W = static_cast<float*>(ws_dev);
+    if (tucker) {
+      GemmArgs g3 = gemm0();                     // W_h = G~_h U~_D^T
+      g3.M = rT; g3.N = D; g3.K = rD;
+      g3.A = G; g3.a_dtype = kBF16; g3.am = plain(rD); g3.ak = plain(1); g3.a_batch = rT * rD;
+      g3.B = Ud; g3.b_dtype = kBF16; g3.bk = plain(1); g3.bn = plain(rD); g3.b_batch = 0;
+      g3.C = W; g3.c_m = D; g3.c_n = 1; g3.c_batch = rT * D;
+      ck(launch_gemm(g3, static_cast<int>(H), s));
+    }
+    DecodeArgs da{};
+    da.Ut = tucker ? Ut : nullptr; da.W = W; da.r_T = rT;
+    da.scales = reinterpret_cast<const uint16_t*>(blob + L.sc);
+    da.codes = reinterpret_cast<const uint8_t*>(blob + L.cd);
+    da.bits = c.bits;
+    da.Q = static_cast<const float*>(rot_dev);
+    da.H = H; da.T = T; da.Xh = xhat_dev;
+    da.out_dtype = shape->dtype == JOLT_BF16 ? kBF16 : kF32;
+    ck(launch_decode(da, s));
+    return JOLT_OK;
+  });
+}
+
+jolt_status jolt_quantize(const float* y_dev, int64_t rows, int32_t D, int32_t bits, void* scales_dev,
+                          void* codes_dev, void* stream) {
+  if (!y_dev || !scales_dev || !codes_dev || rows < 0 || D != kD || bits < 1 || bits > 4) return JOLT_EINVAL;
+  if (rows == 0) return JOLT_OK;
+  return guard([&]() -> jolt_status {
+    ck(launch_quantize(y_dev, rows, bits, static_cast<uint16_t*>(scales_dev),
+                       static_cast<uint8_t*>(codes_dev), static_cast<hipStream_t>(stream)));
+    return JOLT_OK;
+  });
+}
+
+jolt_status jolt_header_parse(const void* header, size_t bytes, jolt_shape* shape, jolt_choice* choice,
+                              uint64_t* seed) {
+  if (!header || bytes < 64) return JOLT_EINVAL;
+  uint32_t w[16];
+  std::memcpy(w, header, 64);
+  if (w[0] != kMagic || w[1] != kVersion || w[9] != static_cast<uint32_t>(kGroup)) return JOLT_EFORMAT;
+  jolt_shape s{static_cast<int32_t>(w[2]), static_cast<int32_t>(w[3]), static_cast<int32_t>(w[4]),
+               static_cast<int32_t>(w[5])};
+  jolt_choice c{static_cast<int32_t>(w[6]), static_cast<int32_t>(w[7]), static_cast<int32_t>(w[8])};
+  if (!shape_ok(&s) || !choice_ok(&s, c)) return JOLT_EFORMAT;
+  if (shape) *shape = s;
+  if (choice) *choice = c;
+  if (seed) *seed = static_cast<uint64_t>(w[10]) | (static_cast<uint64_t>(w[11]) << 32);
+  return JOLT_OK;
+}
+
+const char* jolt_status_str(jolt_status s) {
+  switch (s) {
+    case JOLT_OK: return "ok";
+    case JOLT_EINVAL: return "invalid argument";
+    case JOLT_ENOSPACE: return "buffer too small";
+    case JOLT_EBUDGET: return "byte budget below the cheapest plan";
+    case JOLT_ERANGE: return "non-finite input";
+    case JOLT_EFORMAT: return "bad record header";
+    case JOLT_EHIP: return "HIP runtime error";
+    case JOLT_ENODEV: return "no usable device";
+  }
+  return "unknown status";
+}
+
+int32_t jolt_version(void) { return static_cast<int32_t>(kVersion); }
+
+}  // extern "C"

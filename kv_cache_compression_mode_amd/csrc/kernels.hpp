@@ -1,0 +1,104 @@
+// Host-side launch interface of the codec's HIP kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jolt {
+
+enum { kBF16 = 0, kF32 = 1 };
+
+// offset(i) = (i / len) * seg + (i % len) * stride   (len = INT64_MAX: plain stride)
+struct GemmDim {
+  int64_t len, seg, stride;
+};
+inline GemmDim plain(int64_t stride) { return GemmDim{INT64_MAX, 0, stride}; }
+inline GemmDim segmented(int64_t len, int64_t seg, int64_t stride) { return GemmDim{len, seg, stride}; }
+
+// C[z](m, n) = alpha * sum_k A[z](m, k) B[z](k, n) * col_scale[z][n] + beta * C[z](m, n)
+struct GemmArgs {
+  int64_t M, N, K;
+  const void* A; int a_dtype; GemmDim am, ak; int64_t a_batch;
+  const void* B; int b_dtype; GemmDim bk, bn; int64_t b_batch;
+  const void* const* a_ptrs;   // optional device array: operand base per batch entry
+  const void* const* b_ptrs;
+  void* C; int c_dtype; int64_t c_m, c_n, c_batch;
+  float alpha, beta;
+  const float* col_scale; int64_t col_scale_batch;
+};
+
+hipError_t launch_gemm(const GemmArgs& g, int batch, hipStream_t s);
+hipError_t launch_sumsq(const void* const* xs_dev, int ntensors, int64_t n, int dtype, double* out,
+                        hipStream_t s);
+hipError_t launch_sketch(float* out, int64_t rows, int64_t cols, uint64_t seed, const uint64_t* tags,
+                         int ntensors, hipStream_t s);
+hipError_t launch_to_bf16(const float* in, int64_t ld_in, uint16_t* out, int64_t rows, int64_t cols,
+                          hipStream_t s);
+hipError_t launch_gather_cols(const float* in, int64_t ld_in, int64_t in_batch, const int* idx,
+                              int64_t idx_batch, float* out, int64_t ld_out, int64_t out_batch,
+                              int64_t rows, int64_t ncols, int batch, hipStream_t s);
+hipError_t launch_row_sumsq(const float* P, int64_t rows, int64_t cols, int64_t batch_stride,
+                            int batch, double* out, int64_t out_batch, hipStream_t s);
+hipError_t launch_col_dot(const float* A, const float* B, int64_t m, int64_t ncols, int64_t ld,
+                          int64_t batch_stride, int batch, double* out, int64_t out_batch, hipStream_t s);
+hipError_t launch_pad_copy(const float* in, int64_t n, int64_t in_batch, float* out, int64_t n_pad,
+                           int batch, hipStream_t s);
+hipError_t launch_sum_diag_blocks(const float* C, int64_t H, int64_t D, float* GD, int batch,
+                                  hipStream_t s);
+
+// ---- symmetric eigensolver (block Jacobi) ----
+// A: [batch][n][n] (n multiple of 64), V: [batch][n][n] (initialized by the solver).
+struct JacobiWork {
+  float* A; float* V; int64_t n; int batch;
+  float* J;          // [batch][n/64][64][64]
+  int* active;       // [batch][n/64]
+  int* rot_count;    // [batch]
+  float* tau_abs;    // [batch]
+};
+hipError_t jacobi_init(const JacobiWork& w, float tau_abs_rel, hipStream_t s);
+hipError_t jacobi_round(const JacobiWork& w, int round, float tau_rel, hipStream_t s);
+// Scalar Jacobi to convergence on 128 x 128 matrices (one workgroup each):
+// A -> diagonal (in place), V <- eigenvectors.
+hipError_t jacobi_small128(float* A, float* V, int batch, float tau_rel, float tau_abs_rel,
+                           int max_sweeps, hipStream_t s);
+// Indices of the R largest diagonal entries of each A, descending (ties: lower index).
+hipError_t topk_diag(const float* A, int64_t n, int batch, int R, int* idx, hipStream_t s);
+
+// ---- Householder QR, column-major panels [batch][k][ld] (column j at j*ld) ----
+// In place: on return the panel holds the explicit orthonormal Q (m x k) with
+// diag(R) >= 0.  tau_work: [batch][2k] floats.
+hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t batch_stride, int batch,
+                          float* tau_work, hipStream_t s);
+
+// Sort columns by lam descending (ties: lower index), sign-fix (largest |.| entry
+// positive, lowest index on ties) and emit row-major U_out [m][ld_out]; lam_out
+// sorted, fp64.  perm / sign: [batch][R] scratch.
+hipError_t finalize_factor_ws(const float* U_cm, int64_t m, int64_t R, int64_t ld_cm, int64_t cm_batch,
+                              const double* lam, int64_t lam_batch, float* U_out, int64_t ld_out,
+                              int64_t out_batch, double* lam_out, int64_t lam_out_batch, int batch,
+                              int* perm, float* sign, hipStream_t s);
+
+// ---- codec ----
+hipError_t launch_quantize(const float* Y, int64_t rows, int bits, uint16_t* scales, uint8_t* codes,
+                           hipStream_t s);
+// Fused residual -> rotation -> quantization for one tensor (D = 128).
+struct EncodeArgs {
+  const void* X; int x_dtype; int64_t H, T;
+  const uint16_t* Ut;  // bf16 [T][r_T] (NULL when r_T == 0)
+  const float* W;      // fp32 [H][r_T][128] = G~_h U~_D^T
+  int64_t r_T;
+  const float* Qt;     // fp32 [128][128], Qt[d][c] = Q[c][d]
+  int bits;
+  uint16_t* scales;    // [H][T][4][2]
+  uint8_t* codes;      // [H][T][4][4*bits]
+};
+hipError_t launch_encode_residual(const EncodeArgs& a, hipStream_t s);
+struct DecodeArgs {
+  const uint16_t* Ut; const float* W; int64_t r_T;
+  const uint16_t* scales; const uint8_t* codes; int bits;
+  const float* Q; int64_t H, T;
+  void* Xh; int out_dtype;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_write_header(void* blob, const uint32_t* words16, hipStream_t s);
+
+}  // namespace jolt

@@ -1,0 +1,238 @@
+"""Python binding of the JoLT codec C ABI (include/jolt.h).
+
+Argument marshalling only: every step of the codec runs in libjolt.so's HIP
+kernels and host code.  PyTorch provides device memory and the current HIP
+stream.  Names follow the C entry points: ``allocate``, ``factors``,
+``rotation``, ``encode``, ``decode``, ``quantize``, plus the host-only
+``plan_from_spectra`` and ``rotation_host``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import AllocReq, Choice, Plan, Shape, check, lib
+
+D_FEATURES = 128
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return _lib.JOLT_BF16
+    if dt == torch.float32:
+        return _lib.JOLT_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == _lib.JOLT_BF16 else torch.float32
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def make_shape(H: int, T: int, D: int, dtype) -> Shape:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return Shape(H, T, D, code)
+
+
+def make_req(H, T, D, dtype, n_layers, ratio, method="exact", bits=(1, 2, 3, 4), group_layers=4,
+             seed=0, oversample=10, power_iters=1, r_T_cap=0, step_T=0, step_D=0) -> AllocReq:
+    menu = (C.c_int32 * 4)(*(list(bits) + [0] * (4 - len(bits))))
+    m = _lib.JOLT_FLASH if method == "flash" else _lib.JOLT_EXACT
+    return AllocReq(make_shape(H, T, D, dtype), n_layers, group_layers, float(ratio), menu, len(bits), m,
+                    oversample, power_iters, r_T_cap, step_T, step_D, seed)
+
+
+# ----------------------------------------------------------------- sizes
+def blob_bytes(H, T, D, choice, dtype=torch.bfloat16) -> int:
+    return lib().jolt_blob_bytes(C.byref(make_shape(H, T, D, dtype)), Choice(*choice))
+
+
+def workspace_bytes(req: AllocReq) -> int:
+    return lib().jolt_workspace_bytes(C.byref(req))
+
+
+def spectrum_len(req: AllocReq) -> int:
+    return lib().jolt_spectrum_len(C.byref(req))
+
+
+# -------------------------------------------------------------- rotation
+def rotation(seed: int, D: int = D_FEATURES, device="cuda") -> torch.Tensor:
+    """Prepared rotation buffer (fp32 Q, fp32 Q^T, bf16 Q) on the device."""
+    n = lib().jolt_rotation_bytes(D)
+    buf = torch.empty(n, dtype=torch.uint8, device=device)
+    check(lib().jolt_rotation(seed, D, buf.data_ptr(), n, _stream(buf.device)), "jolt_rotation")
+    return buf
+
+
+def rotation_host(seed: int, D: int = D_FEATURES) -> np.ndarray:
+    out = np.empty((D, D), dtype=np.float64)
+    check(lib().jolt_rotation_host(seed, D, out.ctypes.data_as(C.POINTER(C.c_double))),
+          "jolt_rotation_host")
+    return out
+
+
+def rng_normal(seed: int, tag: int, index: int) -> float:
+    return lib().jolt_rng_normal(seed, tag, index)
+
+
+# -------------------------------------------------------------- allocate
+@dataclass
+class Allocation:
+    req: AllocReq
+    workspace: torch.Tensor
+    choice: dict           # (group, kind) -> (r_T, r_D, bits)
+    tensor_bytes: list
+    total_bytes: int
+    budget_bytes: int
+    objective: float
+    r_T_cap: int
+    spectra_T: np.ndarray | None
+    spectra_D: np.ndarray | None
+    frob2: np.ndarray | None
+
+    def choice_of(self, layer: int, kind: int):
+        return self.choice[(layer // self.req.group_layers, kind)]
+
+    def factors(self, tensor: int):
+        """(U_T [T, ld] fp32, U_D [D, D] fp32) views into the workspace."""
+        ut, ldt, ud = C.c_void_p(), C.c_int32(), C.c_void_p()
+        check(lib().jolt_factors(C.byref(self.req), self.workspace.data_ptr(), tensor, C.byref(ut),
+                                 C.byref(ldt), C.byref(ud)), "jolt_factors")
+        base = self.workspace.data_ptr()
+        T, D = self.req.shape.T, self.req.shape.D
+        w32 = self.workspace.view(torch.float32)
+        o1 = (ut.value - base) // 4
+        o2 = (ud.value - base) // 4
+        return (w32[o1:o1 + T * ldt.value].view(T, ldt.value), w32[o2:o2 + D * D].view(D, D))
+
+
+def _plan_arrays(req: AllocReq, spectra: bool):
+    L = req.n_layers
+    ng = (L + req.group_layers - 1) // req.group_layers
+    choice = (Choice * (2 * ng))()
+    tb = (C.c_uint64 * (2 * L))()
+    plan = Plan(choice, tb, None, None, None, 0.0, 0, 0, 0)
+    arrs = {}
+    if spectra:
+        lt = max(1, spectrum_len(req))
+        arrs["T"] = np.zeros((2 * L, lt))
+        arrs["D"] = np.zeros((2 * L, req.shape.D))
+        arrs["f"] = np.zeros(2 * L)
+        plan.spectra_T = arrs["T"].ctypes.data_as(C.POINTER(C.c_double))
+        plan.spectra_D = arrs["D"].ctypes.data_as(C.POINTER(C.c_double))
+        plan.frob2 = arrs["f"].ctypes.data_as(C.POINTER(C.c_double))
+    return plan, choice, tb, ng, arrs
+
+
+def _plan_dict(req, plan, choice, tb, ng):
+    ch = {(g, k): choice[2 * g + k].tuple() for g in range(ng) for k in (0, 1)}
+    return ch, [int(tb[i]) for i in range(2 * req.n_layers)]
+
+
+def allocate(tensors, ratio: float, method: str = "exact", bits=(1, 2, 3, 4), group_layers: int = 4,
+             seed: int = 0, oversample: int = 10, power_iters: int = 1, r_T_cap: int = 0,
+             step_T: int = 0, step_D: int = 0, spectra: bool = True) -> Allocation:
+    """Spectra, factors and the Lagrangian-dual plan of a cache.
+
+    tensors[layer] = (K, V), each a contiguous [H, T, 128] bf16/fp32 CUDA tensor.
+    """
+    L = len(tensors)
+    x0 = tensors[0][0]
+    H, T, D = x0.shape
+    req = make_req(H, T, D, x0.dtype, L, ratio, method, bits, group_layers, seed, oversample,
+                   power_iters, r_T_cap, step_T, step_D)
+    ptrs = (C.c_void_p * (2 * L))()
+    for l in range(L):
+        for k in (0, 1):
+            t = tensors[l][k]
+            if t.shape != x0.shape or t.dtype != x0.dtype or not t.is_contiguous():
+                raise ValueError("all tensors must be contiguous with one shape and dtype")
+            ptrs[2 * l + k] = t.data_ptr()
+    nws = workspace_bytes(req)
+    if nws == 0:
+        check(_lib.JOLT_EINVAL, "jolt_workspace_bytes")
+    ws = torch.empty(nws, dtype=torch.uint8, device=x0.device)
+    plan, choice, tb, ng, arrs = _plan_arrays(req, spectra)
+    check(lib().jolt_allocate(C.byref(req), ptrs, ws.data_ptr(), nws, _stream(x0.device), C.byref(plan)),
+          "jolt_allocate")
+    ch, tbl = _plan_dict(req, plan, choice, tb, ng)
+    return Allocation(req, ws, ch, tbl, plan.total_bytes, plan.budget_bytes, plan.objective,
+                      plan.r_T_cap, arrs.get("T"), arrs.get("D"), arrs.get("f"))
+
+
+def plan_from_spectra(req: AllocReq, spectra_T: np.ndarray, spectra_D: np.ndarray, frob2: np.ndarray):
+    """The Lagrangian dual alone on host spectra (no device)."""
+    sT = np.ascontiguousarray(spectra_T, dtype=np.float64)
+    sD = np.ascontiguousarray(spectra_D, dtype=np.float64)
+    f2 = np.ascontiguousarray(frob2, dtype=np.float64)
+    plan, choice, tb, ng, _ = _plan_arrays(req, False)
+    P = C.POINTER(C.c_double)
+    check(lib().jolt_plan_from_spectra(C.byref(req), sT.ctypes.data_as(P), sT.shape[1],
+                                       sD.ctypes.data_as(P), f2.ctypes.data_as(P), C.byref(plan)),
+          "jolt_plan_from_spectra")
+    ch, tbl = _plan_dict(req, plan, choice, tb, ng)
+    return dict(choice=ch, tensor_bytes=tbl, total_bytes=plan.total_bytes, budget=plan.budget_bytes,
+                objective=plan.objective, r_T_cap=plan.r_T_cap)
+
+
+# ------------------------------------------------------- encode / decode
+def encode(x: torch.Tensor, choice, U_T: torch.Tensor | None, U_D: torch.Tensor | None,
+           rot: torch.Tensor, seed: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Compress one [H, T, 128] tensor into a device record (uint8 tensor)."""
+    H, T, D = x.shape
+    shape = make_shape(H, T, D, x.dtype)
+    ch = Choice(*choice)
+    nb = lib().jolt_blob_bytes(C.byref(shape), ch)
+    if nb == 0:
+        check(_lib.JOLT_EINVAL, "jolt_blob_bytes")
+    blob = out if out is not None else torch.empty(nb, dtype=torch.uint8, device=x.device)
+    nws = lib().jolt_encode_workspace_bytes(C.byref(shape), ch)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
+    ut = U_T.data_ptr() if U_T is not None else None
+    ud = U_D.data_ptr() if U_D is not None else None
+    ldt = U_T.stride(0) if U_T is not None else 0
+    ldd = U_D.stride(0) if U_D is not None else 0
+    check(lib().jolt_encode(C.byref(shape), x.data_ptr(), ch, ut, ldt, ud, ldd, rot.data_ptr(), seed,
+                            blob.data_ptr(), blob.numel(), ws.data_ptr(), ws.numel(),
+                            _stream(x.device)), "jolt_encode")
+    return blob
+
+
+def decode(blob: torch.Tensor, H: int, T: int, choice, rot: torch.Tensor, dtype=torch.bfloat16,
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Reconstruct [H, T, 128] from a record."""
+    shape = make_shape(H, T, D_FEATURES, dtype)
+    ch = Choice(*choice)
+    xh = out if out is not None else torch.empty((H, T, D_FEATURES), dtype=dtype, device=blob.device)
+    nws = lib().jolt_decode_workspace_bytes(C.byref(shape), ch)
+    ws = workspace if workspace is not None else torch.empty(max(nws, 1), dtype=torch.uint8,
+                                                              device=blob.device)
+    check(lib().jolt_decode(C.byref(shape), ch, blob.data_ptr(), blob.numel(), rot.data_ptr(),
+                            xh.data_ptr(), ws.data_ptr(), ws.numel(), _stream(blob.device)), "jolt_decode")
+    return xh
+
+
+def quantize(y: torch.Tensor, bits: int):
+    """Group quantizer alone: y [rows, 128] fp32 -> (scales [rows, 4, 2] bf16 bits as int16,
+    codes [rows, 4, 4*bits] uint8)."""
+    rows, D = y.shape
+    sc = torch.empty((rows, D // 32, 2), dtype=torch.int16, device=y.device)
+    cd = torch.empty((rows, D // 32, 4 * bits), dtype=torch.uint8, device=y.device)
+    check(lib().jolt_quantize(y.data_ptr(), rows, D, bits, sc.data_ptr(), cd.data_ptr(),
+                              _stream(y.device)), "jolt_quantize")
+    return sc, cd
+
+
+def header_parse(header: bytes):
+    s, c, seed = Shape(), Choice(), C.c_uint64()
+    buf = C.create_string_buffer(bytes(header), len(header))
+    check(lib().jolt_header_parse(buf, len(header), C.byref(s), C.byref(c), C.byref(seed)),
+          "jolt_header_parse")
+    return (s.H, s.T, s.D, s.dtype), c.tuple(), seed.value

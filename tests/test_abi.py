@@ -1,0 +1,145 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and its host-only logic (counter RNG, rotation, byte model, Lagrangian dual,
+header parsing, argument validation) agrees with the oracle.  No GPU calls."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import alloc, rng, rotation
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jolt.h")
+
+jl = pytest.importorskip("kv_cache_compression_mode_amd._lib")
+
+
+@pytest.fixture(scope="module")
+def J():
+    from kv_cache_compression_mode_amd import jolt
+    jl.lib()
+    return jolt
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(jolt_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(J):
+    names = _declared()
+    assert len(names) >= 18
+    L = jl.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    # and the binding declares exactly the header's entry points
+    assert sorted(jl.SIGNATURES) == names
+
+
+def test_rng_normals_match_oracle(J):
+    for seed, tag in [(0, rng.TAG_ROTATION), (7, rng.tensor_tag(rng.TAG_SKETCH, 3, 1))]:
+        z = rng.normals(seed, tag, 50)
+        got = np.array([J.rng_normal(seed, tag, i) for i in range(50)])
+        np.testing.assert_allclose(got, z, rtol=4e-16, atol=4e-16)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 12345])
+def test_rotation_matches_oracle(J, seed):
+    np.testing.assert_allclose(J.rotation_host(seed), rotation.rotation(seed, 128), atol=1e-12)
+
+
+@pytest.mark.parametrize("H,T,choice", [(8, 1024, (256, 64, 2)), (8, 1024, (0, 0, 4)),
+                                         (40, 4096, (1280, 112, 3)), (2, 100, (32, 16, 1)),
+                                         (8, 32768, (160, 48, 3))])
+def test_blob_bytes_match_byte_model(J, H, T, choice):
+    assert J.blob_bytes(H, T, 128, choice) == alloc.blob_bytes(H, T, 128, *choice)
+
+
+def test_invalid_arguments_rejected(J):
+    assert J.blob_bytes(8, 1024, 64, (32, 16, 2)) == 0          # D must be 128
+    assert J.blob_bytes(8, 1024, 128, (32, 16, 5)) == 0         # bits in 1..4
+    assert J.blob_bytes(8, 1024, 128, (2000, 16, 2)) == 0       # r_T > min(T, HD)
+    assert J.blob_bytes(8, 1024, 128, (32, 0, 2)) == 0          # r_D = 0 with r_T > 0
+    req = J.make_req(8, 1024, 128, 0, 4, -1.0)
+    assert J.workspace_bytes(req) == 0
+    L = jl.lib()
+    assert L.jolt_rotation_bytes(64) == 0
+    assert L.jolt_quantize(None, 4, 128, 2, None, None, None) == jl.JOLT_EINVAL
+    assert L.jolt_encode(None, None, jl.Choice(0, 0, 2), None, 0, None, 0, None, 0, None, 0, None, 0,
+                         None) == jl.JOLT_EINVAL
+
+
+def test_header_parse(J):
+    w = np.array([0x544C4F4A, 1, 8, 1024, 128, 0, 256, 64, 2, 32, 5, 0, 0, 0, 0, 0], dtype=np.uint32)
+    shape, choice, seed = J.header_parse(w.tobytes())
+    assert shape == (8, 1024, 128, 0) and choice == (256, 64, 2) and seed == 5
+    bad = w.copy()
+    bad[0] = 0
+    with pytest.raises(jl.JoltError) as e:
+        J.header_parse(bad.tobytes())
+    assert e.value.status == jl.JOLT_EFORMAT
+    with pytest.raises(jl.JoltError) as e:
+        J.header_parse(w.tobytes()[:32])
+    assert e.value.status == jl.JOLT_EINVAL
+
+
+def _spectra(seed, L, T, D, H):
+    r = np.random.default_rng(seed)
+    nT = min(T, H * D)
+    sp = []
+    for l in range(L):
+        row = []
+        for k in (0, 1):
+            dt = r.uniform(0.85, 0.99)
+            lamT = np.sort(1e5 * dt ** np.arange(nT) + r.uniform(5, 40, nT))[::-1]
+            f2 = float(lamT.sum())
+            lamD = np.sort(r.uniform(0.7, 0.97) ** np.arange(D) + 0.002)[::-1]
+            lamD *= f2 / lamD.sum()
+            row.append((lamT, lamD, f2))
+        sp.append(row)
+    return sp
+
+
+@pytest.mark.parametrize("seed,L,T,H,ratio,bits,G", [
+    (0, 32, 4096, 8, 2.0, (1, 2, 3, 4), 4),
+    (1, 8, 1024, 8, 2.0, (1, 2, 3, 4), 4),
+    (2, 6, 1024, 8, 3.0, (2, 4), 4),          # last group shorter
+    (3, 4, 4096, 40, 2.0, (1, 2, 3, 4), 4),
+    (4, 5, 512, 8, 1.7, (3,), 2),
+])
+def test_dual_matches_oracle_on_identical_spectra(J, seed, L, T, H, ratio, bits, G):
+    D = 128
+    sp = _spectra(seed, L, T, D, H)
+    want = alloc.allocate(sp, L, H, T, D, ratio, bits, G)
+    req = J.make_req(H, T, D, 0, L, ratio, bits=bits, group_layers=G)
+    cap = alloc.rank_cap_T(H, T, D, ratio)
+    # the library reads the leading spectrum only; give it the full one and a truncated one
+    for lenT in (len(sp[0][0][0]), cap):
+        sT = np.stack([sp[l][k][0][:lenT] for l in range(L) for k in (0, 1)])
+        sD = np.stack([sp[l][k][1] for l in range(L) for k in (0, 1)])
+        f2 = np.array([sp[l][k][2] for l in range(L) for k in (0, 1)])
+        got = J.plan_from_spectra(req, sT, sD, f2)
+        assert got["choice"] == want["choice"]
+        assert got["total_bytes"] == want["total_bytes"]
+        assert got["budget"] == want["budget"]
+        assert got["objective"] == want["objective"]
+        assert got["tensor_bytes"] == [want["tensor_bytes"][(l, k)] for l in range(L) for k in (0, 1)]
+        assert got["r_T_cap"] == cap
+
+
+def test_dual_infeasible_budget(J):
+    sp = _spectra(5, 4, 1024, 128, 8)
+    req = J.make_req(8, 1024, 128, 0, 4, 40.0, bits=(1, 2))
+    sT = np.stack([sp[l][k][0] for l in range(4) for k in (0, 1)])
+    sD = np.stack([sp[l][k][1] for l in range(4) for k in (0, 1)])
+    f2 = np.array([sp[l][k][2] for l in range(4) for k in (0, 1)])
+    with pytest.raises(jl.JoltError) as e:
+        J.plan_from_spectra(req, sT, sD, f2)
+    assert e.value.status == jl.JOLT_EBUDGET
+    f2[3] = np.nan
+    with pytest.raises(jl.JoltError) as e:
+        J.plan_from_spectra(J.make_req(8, 1024, 128, 0, 4, 2.0), sT, sD, f2)
+    assert e.value.status == jl.JOLT_ERANGE

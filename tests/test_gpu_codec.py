@@ -1,0 +1,246 @@
+"""GPU parity of the HIP path against the fp64 CPU oracle, through the C ABI.
+
+Bars (from the codec's statement and its arithmetic):
+* quantization codes and scales bit-exact when the kernel is fed the oracle's
+  fp32 rotated residual;
+* relative Frobenius reconstruction error within 1e-4 of the oracle's;
+* factors: spectra within 2e-5 * lambda_1, orthonormal to 1e-5, principal-angle
+  sines <= 1e-3 at every cut the fp32 eigengaps resolve, captured energy within
+  1e-4 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kvgen
+from oracle import alloc, bf16, codec, flash, quant, rng, rotation, tucker
+
+from gpu_util import D, max_sine, parse_blob, resolvable_cuts, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def J():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from kv_cache_compression_mode_amd import jolt
+    return jolt
+
+
+@pytest.fixture(scope="module")
+def rot(J):
+    return J.rotation(0)
+
+
+@pytest.fixture(scope="module")
+def single():
+    cfg = kvgen.CONFIGS["single_k_t1024_f32"]
+    X = kvgen.config_tensor(cfg, 0, 0).astype(np.float64)
+    return X, codec.analyze(X, 256), rotation.rotation(0, 128)
+
+
+def _quant_ref(Y, bits):
+    m16, s16, c = quant.quantize(Y, bits)
+    return m16, s16, quant.pack(c, bits)
+
+
+def _gpu_quant(J, Y, bits):
+    rows = Y.shape[0]
+    sc, cd = J.quantize(torch.from_numpy(np.ascontiguousarray(Y, np.float32)).cuda(), bits)
+    torch.cuda.synchronize()
+    sc = sc.cpu().numpy().view(np.uint16).reshape(rows, 4, 2)
+    m16 = (sc[..., 0].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    s16 = (sc[..., 1].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return m16, s16, cd.cpu().numpy().reshape(rows, 4, 4 * bits)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_quantizer_bit_exact_on_oracle_residual(J, single, bits):
+    X, a, Q = single
+    Y = codec.encode_tensor(X, a["U_T"], a["U_D"], (256, 64, bits), Q)["Y"].reshape(-1, D)
+    m, s, p = _quant_ref(Y, bits)
+    gm, gs, gp = _gpu_quant(J, Y, bits)
+    np.testing.assert_array_equal(gm, m)
+    np.testing.assert_array_equal(gs, s)
+    np.testing.assert_array_equal(gp, p)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_quantizer_edge_cases(J, bits):
+    r = np.random.default_rng(100 + bits)
+    rows = 37                                            # ragged: not a multiple of the tile
+    Y = (r.standard_normal((rows, D)) * r.uniform(1e-3, 1e3, (rows, 1))).astype(np.float32)
+    Y[0] = 3.0                                           # constant row: zero step
+    Y[1, :32] = -2.5                                     # one constant group
+    Y[2] *= np.float32(1e-40)                            # subnormal values
+    Y[3] = -np.abs(Y[3])                                 # all negative
+    Y[4, ::2] = Y[4, 1::2]                               # exact ties in a row
+    Y[5] = np.arange(D, dtype=np.float32) * 0.5 - 31.75  # grid-aligned, midpoints
+    m, s, p = _quant_ref(Y, bits)
+    gm, gs, gp = _gpu_quant(J, Y, bits)
+    np.testing.assert_array_equal(gm, m)
+    np.testing.assert_array_equal(gs, s)
+    np.testing.assert_array_equal(gp, p)
+
+
+def test_quantizer_empty(J):
+    sc, cd = J.quantize(torch.empty((0, D), dtype=torch.float32, device="cuda"), 2)
+    assert sc.numel() == 0 and cd.numel() == 0
+
+
+def _oracle_from_blob(X, parts, choice, Q, H, T):
+    """The oracle's residual, rotation and quantizer applied to the GPU's stored parts."""
+    r_T = choice[0]
+    if r_T > 0:
+        R = X - tucker.reconstruct(parts["G"], parts["U_T"], parts["U_D"])
+    else:
+        R = X
+    Y = (R.reshape(-1, D) @ Q.T).astype(np.float32).reshape(H, T, D)
+    return Y
+
+
+def _check_codes(parts, Y, bits, H, T):
+    m16, s16, codes = quant.quantize(Y, bits)
+    same_scale = (parts["m16"] == m16) & (parts["s16"] == s16)
+    assert same_scale.mean() > 0.999
+    got = quant.unpack(parts["packed"], bits)
+    diff = (got != codes) & same_scale[..., None]
+    if diff.any():
+        # only where the oracle's (y - m16)/s16 sits at a rounding half-point
+        t = (Y.reshape(H, T, 4, 32).astype(np.float64) - m16[..., None]) / np.where(s16 == 0, 1, s16)[..., None]
+        frac = np.abs(t - np.floor(t) - 0.5)
+        assert np.all(frac[diff] < 1e-3)
+    assert diff.mean() < 1e-3
+
+
+@pytest.mark.parametrize("choice,xdt", [((256, 64, 2), "f32"), ((256, 64, 3), "bf16"),
+                                        ((128, 32, 4), "f32"), ((0, 0, 2), "f32"), ((96, 112, 1), "bf16")])
+def test_encode_decode_with_oracle_factors(J, rot, single, choice, xdt):
+    X0, a, Q = single
+    X = codec.round_to(X0, xdt)
+    H, T, _ = X.shape
+    r_T, r_D, bits = choice
+    # factors rounded to bf16 on the oracle side, so both sides store the same values
+    Ut = bf16.round_nearest(a["U_T"][:, :max(r_T, 1)])
+    Ud = bf16.round_nearest(a["U_D"][:, :max(r_D, 1)])
+    xd = to_dev(X, xdt)
+    blob = J.encode(xd, choice, torch.from_numpy(Ut.astype(np.float32)).cuda() if r_T else None,
+                    torch.from_numpy(Ud.astype(np.float32)).cuda() if r_T else None, rot, seed=0)
+    xh = J.decode(blob, H, T, choice, rot, dtype=xd.dtype)
+    torch.cuda.synchronize()
+    parts = parse_blob(blob, H, T, choice)
+    assert list(parts["header"][:10]) == [0x544C4F4A, 1, H, T, D, 1 if xdt == "f32" else 0,
+                                          r_T, r_D, bits, 32]
+    if r_T:
+        np.testing.assert_array_equal(parts["U_T"], Ut[:, :r_T])
+        np.testing.assert_array_equal(parts["U_D"], Ud[:, :r_D])
+        Go = bf16.round_nearest(tucker.core(X, Ut[:, :r_T], Ud[:, :r_D]))
+        mism = parts["G"] != Go
+        assert mism.mean() < 2e-3
+        ulp = np.spacing(np.abs(Go).astype(np.float32)).astype(np.float64) * 2 ** 16
+        assert np.all(np.abs(parts["G"] - Go)[mism] <= ulp[mism] * 1.01)
+    Y = _oracle_from_blob(X, parts, choice, Q, H, T)
+    _check_codes(parts, Y, bits, H, T)
+    # decode parity: the oracle decode of the GPU record, element by element
+    enc = dict(shape=(H, T, D), choice=choice, U_T=parts["U_T"], U_D=parts["U_D"], G=parts["G"],
+               m16=parts["m16"], s16=parts["s16"], codes=quant.unpack(parts["packed"], bits))
+    Xo = codec.decode_tensor(enc, Q, xdt)
+    Xg = xh.float().cpu().numpy().astype(np.float64)
+    scale = np.abs(X).max()
+    if xdt == "f32":
+        assert np.abs(Xg - Xo).max() <= 2e-5 * scale
+    else:
+        ulp = np.spacing(np.abs(Xo).astype(np.float32)).astype(np.float64) * 2 ** 16
+        assert np.all(np.abs(Xg - Xo) <= ulp * 1.01)
+    # end-to-end error against the oracle's own record
+    eo = codec.encode_tensor(X, Ut, Ud, choice, Q)
+    err_o = codec.rel_err(X, codec.decode_tensor(eo, Q, xdt))
+    assert abs(codec.rel_err(X, Xg) - err_o) < 1e-4
+
+
+def _alloc_single(J, X, xdt, method="exact"):
+    xd = to_dev(X, xdt)
+    return J.allocate([(xd, xd)], ratio=2.0, method=method), xd
+
+
+def test_gpu_factors_exact_direct(J, single):
+    X, a, Q = single
+    res, _ = _alloc_single(J, X, "f32")
+    torch.cuda.synchronize()
+    R = res.r_T_cap
+    assert R == 256
+    lam_o, lamD_o = a["lam_T"], a["lam_D"]
+    lam_g, lamD_g = res.spectra_T[0], res.spectra_D[0]
+    assert np.all(np.abs(lam_g - lam_o[:R]) <= 2e-5 * lam_o[0])
+    np.testing.assert_allclose(lam_g[:8], lam_o[:8], rtol=1e-5)
+    assert np.all(np.abs(lamD_g - lamD_o) <= 2e-5 * lamD_o[0])
+    assert abs(res.frob2[0] - a["frob2"]) <= 1e-12 * a["frob2"]
+    Ut, Ud = (t.cpu().numpy().astype(np.float64) for t in res.factors(0))
+    assert np.abs(Ut.T @ Ut - np.eye(R)).max() < 1e-5
+    assert np.abs(Ud.T @ Ud - np.eye(D)).max() < 1e-5
+    for k in resolvable_cuts(lam_o, R, len(lam_o)):
+        assert max_sine(Ut[:, :k], a["U_T"][:, :k]) <= 1e-3, k
+    for k in resolvable_cuts(lamD_o, D - 1, D):
+        assert max_sine(Ud[:, :k], a["U_D"][:, :k]) <= 1e-3, k
+    for r_T, r_D in [(256, 64), (96, 32), (32, 16)]:
+        eg = np.sum(tucker.core(X, Ut[:, :r_T], Ud[:, :r_D]) ** 2)
+        eo = np.sum(tucker.core(X, a["U_T"][:, :r_T], a["U_D"][:, :r_D]) ** 2)
+        assert abs(eg - eo) <= 1e-4 * eo
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_end_to_end_single_tensor(J, rot, single, bits):
+    X, a, Q = single
+    res, xd = _alloc_single(J, X, "f32")
+    Ut, Ud = res.factors(0)
+    choice = (256, 64, bits)
+    blob = J.encode(xd, choice, Ut, Ud, rot)
+    xh = J.decode(blob, 8, 1024, choice, rot, dtype=torch.float32)
+    err_g = codec.rel_err(X, xh.cpu().numpy())
+    err_o = codec.rel_err(X, codec.decode_tensor(codec.encode_tensor(X, a["U_T"], a["U_D"], choice, Q),
+                                                 Q, "f32"))
+    assert abs(err_g - err_o) < 1e-4
+
+
+def _cache(L, H, T, seed=0, dtype="bf16"):
+    return [[kvgen.tensor(H, T, D, seed=seed, layer=l, kind=k, decay=kvgen.decay_for(seed, l, k),
+                          outliers=True, dtype=dtype).astype(np.float64) for k in (0, 1)]
+            for l in range(L)]
+
+
+@pytest.mark.parametrize("method,L,H,T,ratio", [("exact", 4, 2, 512, 2.0),    # dual Gram (T > HD)
+                                                ("exact", 2, 4, 200, 2.0),    # direct, ragged T
+                                                ("flash", 4, 2, 512, 2.0),
+                                                ("flash", 2, 8, 384, 3.0)])
+def test_small_cache_end_to_end(J, rot, method, L, H, T, ratio):
+    tens = _cache(L, H, T)
+    dev = [(to_dev(tens[l][0], "bf16"), to_dev(tens[l][1], "bf16")) for l in range(L)]
+    res = J.allocate(dev, ratio=ratio, method=method, group_layers=2)
+    torch.cuda.synchronize()
+    orc = codec.encode_cache(tens, ratio, "bf16", method=method, group_layers=2)
+    R = res.r_T_cap
+    Q = orc["Q"]
+    # the library's plan equals the oracle dual run on the library's spectra
+    sp = [[(res.spectra_T[2 * l + k], res.spectra_D[2 * l + k], res.frob2[2 * l + k]) for k in (0, 1)]
+          for l in range(L)]
+    want = alloc.allocate(sp, L, H, T, D, ratio, (1, 2, 3, 4), 2)
+    assert res.choice == want["choice"] and res.total_bytes == want["total_bytes"]
+    assert res.total_bytes <= res.budget_bytes
+    for l in range(L):
+        for k in (0, 1):
+            t = 2 * l + k
+            X = tens[l][k]
+            an = orc["analysis"][l][k]
+            lam_o = an["lam_T"]
+            assert np.all(np.abs(res.spectra_T[t] - lam_o[:R]) <= 2e-5 * lam_o[0])
+            Ut, Ud = res.factors(t)
+            Utn = Ut.cpu().numpy().astype(np.float64)
+            assert np.abs(Utn.T @ Utn - np.eye(R)).max() < 1e-5
+            for kc in resolvable_cuts(lam_o, R, min(T, H * D)):
+                assert max_sine(Utn[:, :kc], an["U_T"][:, :kc]) <= 1e-3
+            # encode/decode with the library's own factors under the oracle's plan
+            ch = orc["plan"]["choice"][(l // 2, k)]
+            blob = J.encode(dev[l][k], ch, Ut, Ud, rot)
+            xh = J.decode(blob, H, T, ch, rot, dtype=torch.bfloat16)
+            err_g = codec.rel_err(X, xh.float().cpu().numpy())
+            assert abs(err_g - orc["rel_err"][l][k]) < 1e-4, (l, k, err_g, orc["rel_err"][l][k])
