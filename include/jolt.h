@@ -140,7 +140,8 @@ jolt_status jolt_factors(const jolt_alloc_req* req, void* ws_dev, int32_t tensor
 
 /* The seeded rotation Q (D x D, Haar: QR of a counter-based Gaussian matrix
  * with diag(R) > 0), prepared on the host in fp64 and uploaded to q_dev
- * (jolt_rotation_bytes(D) bytes: fp32 Q then bf16 Q).  Synchronizes `stream`.
+ * (jolt_rotation_bytes(D) bytes: fp32 Q, fp32 Q^T, bf16 Q, each section
+ * 256-aligned).  Synchronizes `stream`.
  * Source: JoLT abstract, "a random orthogonal rotation followed by low-bit
  * quantization". */
 jolt_status jolt_rotation(uint64_t seed, int32_t D, void* q_dev, size_t q_bytes,
@@ -168,7 +169,8 @@ jolt_status jolt_decode(const jolt_shape* shape, jolt_choice choice,
                         const void* rot_dev, void* xhat_dev,
                         void* ws_dev, size_t ws_bytes, void* stream);
 
-/* Group quantizer alone: rows x D fp32 rotated residual in y_dev ->
+/* Group quantizer alone (rows == 0 is a no-op; pointers may then be NULL):
+ * rows x D fp32 rotated residual in y_dev ->
  * scales bf16 [rows][D/32][2] and packed codes [rows][D/32][4*bits].
  * The same arithmetic as the encode kernel's last stage. */
 jolt_status jolt_quantize(const float* y_dev, int64_t rows, int32_t D, int32_t bits,

@@ -195,6 +195,9 @@ def encode(x: torch.Tensor, choice, U_T: torch.Tensor | None, U_D: torch.Tensor 
     blob = out if out is not None else torch.empty(nb, dtype=torch.uint8, device=x.device)
     nws = lib().jolt_encode_workspace_bytes(C.byref(shape), ch)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
+    for f in (U_T, U_D):
+        if f is not None and (f.dtype != torch.float32 or f.dim() != 2 or f.stride(1) != 1):
+            raise ValueError("factors must be fp32 [rows, ld] with unit column stride")
     ut = U_T.data_ptr() if U_T is not None else None
     ud = U_D.data_ptr() if U_D is not None else None
     ldt = U_T.stride(0) if U_T is not None else 0

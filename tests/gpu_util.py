@@ -61,3 +61,23 @@ def resolvable_cuts(lam: np.ndarray, rmax: int, n: int):
         if (lam[k - 1] - lam[k]) / lam[0] >= thr:
             out.append(k)
     return out
+
+
+def check_bf16_rounding(got: np.ndarray, exact: np.ndarray, abs_terms: np.ndarray, gamma: float,
+                        max_frac: float = 0.05):
+    """bf16 values computed in fp32 arithmetic vs the fp64 exact value rounded.
+
+    Where the two roundings differ, the stored value may be off the exact one
+    by at most half a bf16 ulp plus gamma * abs_terms (the fp32 accumulation
+    error bound from the sum of |terms|).
+    """
+    from oracle import bf16
+    want = bf16.round_nearest(exact)
+    mism = got != want
+    assert mism.mean() <= max_frac, mism.mean()
+    if mism.any():
+        g, e, t = got[mism], exact[mism], abs_terms[mism]
+        half_ulp = np.spacing(np.maximum(np.abs(g), np.abs(e)).astype(np.float32)).astype(np.float64) * 2 ** 15
+        excess = np.abs(g - e) - half_ulp
+        assert np.all(excess <= gamma * t + 1e-30), float(np.max(excess / (t + 1e-30)))
+    return float(mism.mean())
