@@ -208,6 +208,10 @@ def encode(x: torch.Tensor, choice, U_T: torch.Tensor | None, U_D: torch.Tensor 
     return blob
 
 
+def decode_workspace_bytes(H: int, T: int, choice, dtype=torch.bfloat16) -> int:
+    return lib().jolt_decode_workspace_bytes(C.byref(make_shape(H, T, D_FEATURES, dtype)), Choice(*choice))
+
+
 def decode(blob: torch.Tensor, H: int, T: int, choice, rot: torch.Tensor, dtype=torch.bfloat16,
            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Reconstruct [H, T, 128] from a record."""
