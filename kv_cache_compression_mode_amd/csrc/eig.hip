@@ -98,15 +98,16 @@ __global__ __launch_bounds__(256) void k_trace_init(float* A, float* V, int64_t 
   }
 }
 
-// Sub-problem solve: one workgroup per (pair, matrix).
-__global__ __launch_bounds__(256) void k_jac_solve(const float* A, int64_t n, float* J, int* active,
-                                                   int* rot_count, const float* tau_abs_g, int round,
-                                                   float tau_rel) {
+// Sub-problem solve: one workgroup per (pair, matrix).  The scalar rounds are
+// latency-bound (two barriers each), so four waves share every round.
+constexpr int ST = 256;
+__global__ __launch_bounds__(ST) void k_jac_solve(const float* A, int64_t n, float* J, int* active,
+                                                  int* rot_count, const float* tau_abs_g, int round,
+                                                  float tau_rel) {
   __shared__ float S[NS][LP];
   __shared__ float Jl[NS][LP];
   __shared__ float rc[NS / 2], rs[NS / 2];
   __shared__ int ru[NS / 2], rv[NS / 2];
-  __shared__ int flag;
   const int tid = threadIdx.x;
   const int nb = static_cast<int>(n / SB);
   const int pair = blockIdx.x;
@@ -114,36 +115,44 @@ __global__ __launch_bounds__(256) void k_jac_solve(const float* A, int64_t n, fl
   int p, q;
   rr_pair(pair, round, nb, &p, &q);
   const float* a = A + z * n * n;
-  for (int idx = tid; idx < NS * NS; idx += 256) {
-    const int u = idx / NS, v = idx % NS;
-    S[u][v] = a[slot_index(u, p, q) * n + slot_index(v, p, q)];
-    Jl[u][v] = (u == v) ? 1.f : 0.f;
+  // rows of the four 32 x 32 blocks, 16-byte loads
+  for (int idx = tid; idx < NS * (NS / 4); idx += ST) {
+    const int u = idx / (NS / 4), v4 = (idx % (NS / 4)) * 4;
+    const float4 x = *reinterpret_cast<const float4*>(a + static_cast<int64_t>(slot_index(u, p, q)) * n +
+                                                      slot_index(v4, p, q));
+    S[u][v4] = x.x; S[u][v4 + 1] = x.y; S[u][v4 + 2] = x.z; S[u][v4 + 3] = x.w;
   }
-  if (tid == 0) flag = 0;
+  for (int idx = tid; idx < NS * NS; idx += ST) Jl[idx / NS][idx % NS] = (idx / NS == idx % NS) ? 1.f : 0.f;
   __syncthreads();
   const float tau_abs = tau_abs_g[z];
-  // anything above threshold in this sub-problem?
   int any = 0;
-  for (int idx = tid; idx < NS * NS; idx += 256) {
+  for (int idx = tid; idx < NS * NS; idx += ST) {
     const int u = idx / NS, v = idx % NS;
     if (u < v) {
       const float apq = S[u][v];
       if (fabsf(apq) > tau_abs && fabsf(apq) > tau_rel * sqrtf(fabsf(S[u][u] * S[v][v]))) any = 1;
     }
   }
+  const int64_t aidx = z * (nb / 2) + pair;
+  __shared__ int flag;
+  if (tid == 0) flag = 0;
+  __syncthreads();
   if (any) atomicOr(&flag, 1);
   __syncthreads();
-  int64_t aidx = z * (nb / 2) + pair;
   if (!flag) {
     if (tid == 0) active[aidx] = 0;
     return;
   }
   int nrot = 0;
   for (int ir = 0; ir < NS - 1; ++ir)
-    nrot += jacobi_scalar_round<NS, LP, 256>(S, Jl, rc, rs, ru, rv, ir, tau_rel, tau_abs);
+    nrot += jacobi_scalar_round<NS, LP, ST>(S, Jl, rc, rs, ru, rv, ir, tau_rel, tau_abs);
   float* jo = J + aidx * NS * NS;
-  for (int idx = tid; idx < NS * NS; idx += 256) jo[idx] = Jl[idx / NS][idx % NS];
-  if (tid < NS / 2 && nrot) atomicAdd(rot_count + z, nrot);
+  for (int idx = tid; idx < NS * (NS / 4); idx += ST) {
+    const int u = idx / (NS / 4), v4 = (idx % (NS / 4)) * 4;
+    *reinterpret_cast<float4*>(jo + u * NS + v4) = make_float4(Jl[u][v4], Jl[u][v4 + 1], Jl[u][v4 + 2],
+                                                               Jl[u][v4 + 3]);
+  }
+  if (nrot) atomicAdd(rot_count + z, nrot);
   if (tid == 0) active[aidx] = 1;
 }
 
@@ -181,11 +190,17 @@ __global__ __launch_bounds__(256) void k_jac_update(float* A, float* V, int64_t 
     float* a = A + z * n * n;
     const float* Jpi = J + (z * np + i) * NS * NS;
     const float* Jpj = J + (z * np + j) * NS * NS;
-    for (int idx = tid; idx < NS * NS; idx += 256) {
-      const int u = idx / NS, v = idx % NS;
-      M[u][v] = a[slot_index(u, pi, qi) * n + slot_index(v, pj, qj)];
-      Ji[u][v] = ai ? Jpi[idx] : (u == v ? 1.f : 0.f);
-      Jj[u][v] = aj ? Jpj[idx] : (u == v ? 1.f : 0.f);
+    for (int idx = tid; idx < NS * (NS / 4); idx += 256) {
+      const int u = idx / (NS / 4), v4 = (idx % (NS / 4)) * 4;
+      const float4 x = *reinterpret_cast<const float4*>(a + static_cast<int64_t>(slot_index(u, pi, qi)) * n +
+                                                        slot_index(v4, pj, qj));
+      M[u][v4] = x.x; M[u][v4 + 1] = x.y; M[u][v4 + 2] = x.z; M[u][v4 + 3] = x.w;
+      const float4 ji = ai ? *reinterpret_cast<const float4*>(Jpi + u * NS + v4)
+                           : make_float4(u == v4, u == v4 + 1, u == v4 + 2, u == v4 + 3);
+      const float4 jj = aj ? *reinterpret_cast<const float4*>(Jpj + u * NS + v4)
+                           : make_float4(u == v4, u == v4 + 1, u == v4 + 2, u == v4 + 3);
+      Ji[u][v4] = ji.x; Ji[u][v4 + 1] = ji.y; Ji[u][v4 + 2] = ji.z; Ji[u][v4 + 3] = ji.w;
+      Jj[u][v4] = jj.x; Jj[u][v4 + 1] = jj.y; Jj[u][v4 + 2] = jj.z; Jj[u][v4 + 3] = jj.w;
     }
     __syncthreads();
     f32x16 acc = {};
@@ -213,9 +228,10 @@ __global__ __launch_bounds__(256) void k_jac_update(float* A, float* V, int64_t 
       }
       __syncthreads();
     }
-    for (int idx = tid; idx < NS * NS; idx += 256) {
-      const int u = idx / NS, v = idx % NS;
-      a[slot_index(u, pi, qi) * n + slot_index(v, pj, qj)] = M[u][v];
+    for (int idx = tid; idx < NS * (NS / 4); idx += 256) {
+      const int u = idx / (NS / 4), v4 = (idx % (NS / 4)) * 4;
+      *reinterpret_cast<float4*>(a + static_cast<int64_t>(slot_index(u, pi, qi)) * n + slot_index(v4, pj, qj)) =
+          make_float4(M[u][v4], M[u][v4 + 1], M[u][v4 + 2], M[u][v4 + 3]);
     }
     if (i != j) {
       for (int idx = tid; idx < NS * NS; idx += 256) {
@@ -232,10 +248,12 @@ __global__ __launch_bounds__(256) void k_jac_update(float* A, float* V, int64_t 
     rr_pair(i, round, nb, &pi, &qi);
     float* v = V + z * n * n;
     const float* Jpi = J + (z * np + i) * NS * NS;
-    for (int idx = tid; idx < NS * NS; idx += 256) {
-      const int u = idx / NS, w = idx % NS;
-      M[u][w] = v[(r0 + u) * n + slot_index(w, pi, qi)];
-      Ji[u][w] = Jpi[idx];
+    for (int idx = tid; idx < NS * (NS / 4); idx += 256) {
+      const int u = idx / (NS / 4), w4 = (idx % (NS / 4)) * 4;
+      const float4 x = *reinterpret_cast<const float4*>(v + (r0 + u) * n + slot_index(w4, pi, qi));
+      M[u][w4] = x.x; M[u][w4 + 1] = x.y; M[u][w4 + 2] = x.z; M[u][w4 + 3] = x.w;
+      const float4 ji = *reinterpret_cast<const float4*>(Jpi + u * NS + w4);
+      Ji[u][w4] = ji.x; Ji[u][w4 + 1] = ji.y; Ji[u][w4 + 2] = ji.z; Ji[u][w4 + 3] = ji.w;
     }
     __syncthreads();
     f32x16 acc = {};
@@ -337,8 +355,8 @@ hipError_t jacobi_init(const JacobiWork& w, float tau_abs_rel, hipStream_t s) {
 
 hipError_t jacobi_round(const JacobiWork& w, int round, float tau_rel, hipStream_t s) {
   const int nb = static_cast<int>(w.n / SB), np = nb / 2;
-  k_jac_solve<<<dim3(np, w.batch), 256, 0, s>>>(w.A, w.n, w.J, w.active, w.rot_count, w.tau_abs,
-                                                round, tau_rel);
+  k_jac_solve<<<dim3(np, w.batch), ST, 0, s>>>(w.A, w.n, w.J, w.active, w.rot_count, w.tau_abs,
+                                               round, tau_rel);
   const int nA = np * (np + 1) / 2;
   const int nV = np * static_cast<int>(w.n / NS);
   k_jac_update<<<dim3(nA + nV, w.batch), 256, 0, s>>>(w.A, w.V, w.n, w.J, w.active, round);

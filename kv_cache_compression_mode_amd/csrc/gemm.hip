@@ -34,7 +34,10 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
   const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
-  const int64_t z = blockIdx.z;
+  const int64_t zz = blockIdx.z;
+  const int64_t z = zz / g.ksplit, kz = zz % g.ksplit;
+  const int64_t kbeg = kz * g.kchunk;
+  const int64_t kend = (kbeg + g.kchunk < g.K) ? kbeg + g.kchunk : g.K;
   const char* Ab = g.a_ptrs ? static_cast<const char*>(g.a_ptrs[z])
                            : static_cast<const char*>(g.A) + z * g.a_batch * static_cast<int64_t>(sizeof(TA));
   const char* Bb = g.b_ptrs ? static_cast<const char*>(g.b_ptrs[z])
@@ -46,7 +49,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
   f32x16 acc = {};
 
-  for (int64_t k0 = 0; k0 < g.K; k0 += BK) {
+  for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
     const int64_t a_kbase = dim_off(g.ak, k0);
     const int64_t b_kbase = dim_off(g.bk, k0);
 #pragma unroll
@@ -55,14 +58,14 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
       if (a_mcontig) { kk = tid >> 4; mm = ((tid & 15) << 2) + j; }
       else           { mm = tid >> 2; kk = ((tid & 3) << 2) + j; }
       float v = 0.f;
-      if (m0 + mm < g.M && k0 + kk < g.K)
+      if (m0 + mm < g.M && k0 + kk < kend)
         v = ld<TA>(Ab, a_mbase + mm * g.am.stride + a_kbase + kk * g.ak.stride);
       As[kk][mm] = v;
       int nn, kb;
       if (b_ncontig) { kb = tid >> 4; nn = ((tid & 15) << 2) + j; }
       else           { nn = tid >> 2; kb = ((tid & 3) << 2) + j; }
       float w = 0.f;
-      if (n0 + nn < g.N && k0 + kb < g.K)
+      if (n0 + nn < g.N && k0 + kb < kend)
         w = ld<TB>(Bb, b_nbase + nn * g.bn.stride + b_kbase + kb * g.bk.stride);
       Bs[kb][nn] = w;
     }
@@ -76,6 +79,16 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     __syncthreads();
   }
 
+  if (g.ksplit > 1) {   // partial sums, reduced in a fixed order by k_splitk_reduce
+    float* Pp = g.partial + (z * g.ksplit + kz) * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t m = m0 + wm + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+      const int64_t n = n0 + wn + (lane & 31);
+      if (m < g.M && n < g.N) Pp[m * g.N + n] = acc[i];
+    }
+    return;
+  }
   char* Cb = static_cast<char*>(g.C);
   const int64_t cz = z * g.c_batch;
 #pragma unroll
@@ -94,6 +107,27 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
         uint16_t* C = reinterpret_cast<uint16_t*>(Cb);
         C[off] = f32_to_bf16_rne(v);
       }
+    }
+  }
+}
+
+// C = alpha * sum_kz partial[z][kz] (+ beta C), split order fixed: deterministic.
+__global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
+  const int64_t z = blockIdx.y, MN = g.M * g.N;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < MN; i += 256ll * gridDim.x) {
+    const float* p = g.partial + z * g.ksplit * MN + i;
+    float acc = 0.f;
+    for (int kz = 0; kz < g.ksplit; ++kz) acc += p[kz * MN];
+    const int64_t m = i / g.N, n = i % g.N;
+    float v = g.alpha * acc;
+    if (g.col_scale) v *= g.col_scale[z * g.col_scale_batch + n];
+    const int64_t off = z * g.c_batch + m * g.c_m + n * g.c_n;
+    if (g.c_dtype == kF32) {
+      float* C = static_cast<float*>(g.C);
+      if (g.beta != 0.f) v += g.beta * C[off];
+      C[off] = v;
+    } else {
+      static_cast<uint16_t*>(g.C)[off] = f32_to_bf16_rne(v);
     }
   }
 }
@@ -207,12 +241,19 @@ int grid1(int64_t n, int cap = 4096) {
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& g, int batch, hipStream_t s) {
-  dim3 grid((g.M + BM - 1) / BM, (g.N + BN - 1) / BN, batch);
+hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s) {
+  GemmArgs g = g0;
+  if (g.ksplit < 1 || !g.partial) g.ksplit = 1;
+  g.kchunk = (g.K + g.ksplit - 1) / g.ksplit;
+  g.kchunk = (g.kchunk + BK - 1) / BK * BK;            // chunks start on tile edges
+  dim3 grid((g.M + BM - 1) / BM, (g.N + BN - 1) / BN, batch * g.ksplit);
   if (g.a_dtype == kBF16 && g.b_dtype == kBF16) k_gemm<uint16_t, uint16_t><<<grid, 256, 0, s>>>(g);
   else if (g.a_dtype == kBF16) k_gemm<uint16_t, float><<<grid, 256, 0, s>>>(g);
   else if (g.b_dtype == kBF16) k_gemm<float, uint16_t><<<grid, 256, 0, s>>>(g);
   else k_gemm<float, float><<<grid, 256, 0, s>>>(g);
+  if (g.ksplit > 1) {
+    k_splitk_reduce<<<dim3(grid1(g.M * g.N), batch), 256, 0, s>>>(g);
+  }
   return hipGetLastError();
 }
 

@@ -377,7 +377,8 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base) {
   w.Vr = c.take<float>(static_cast<size_t>(chunk) * std::max(d.nT, d.D) * std::max<int64_t>(R, d.D));
   w.P = c.take<float>(static_cast<size_t>(chunk) * R * d.HD);
   w.lam_tmp = c.take<double>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
-  w.qtau = c.take<float>(static_cast<size_t>(chunk) * 2 * std::max<int64_t>(std::max(R, d.ell), d.D));
+  w.qtau = c.take<float>(householder_qr_work_floats(std::max(d.T, d.HD),
+                                                     std::max<int64_t>(std::max(R, d.ell), d.D), chunk));
   w.perm = c.take<int>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
   w.sgn = c.take<float>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
   if (d.flash) {
@@ -609,9 +610,12 @@ int32_t jolt_spectrum_len(const jolt_alloc_req* req) {
   return cap_of(req);
 }
 
+int encode_ksplit(int64_t T) { return static_cast<int>(std::min<int64_t>(16, std::max<int64_t>(1, T / 256))); }
+
 size_t jolt_encode_workspace_bytes(const jolt_shape* shape, jolt_choice c) {
   if (!shape_ok(shape) || !choice_ok(shape, c)) return 0;
-  return 2 * a256(4ull * shape->H * c.r_T * shape->D) + 256;
+  const size_t w = a256(4ull * shape->H * c.r_T * shape->D);
+  return 2 * w + a256(w * encode_ksplit(shape->T)) + 256;
 }
 
 size_t jolt_decode_workspace_bytes(const jolt_shape* shape, jolt_choice c) {
@@ -754,15 +758,19 @@ jolt_status jolt_encode(const jolt_shape* shape, const void* x_dev, jolt_choice 
     if (tucker) {
       ck(launch_to_bf16(U_T_dev, ld_T, Ut, T, rT, s));
       ck(launch_to_bf16(U_D_dev, ld_D, Ud, D, rD, s));
-      GemmArgs g = gemm0();                      // P_h = U~_T^T X_h  (r_T x D)
-      g.M = rT; g.N = D; g.K = T;
-      g.A = Ut; g.a_dtype = kBF16; g.am = plain(1); g.ak = plain(rT); g.a_batch = 0;
-      g.B = x_dev; g.b_dtype = xdt; g.bk = plain(D); g.bn = plain(1); g.b_batch = T * D;
-      g.C = P; g.c_m = D; g.c_n = 1; g.c_batch = rT * D;
-      ck(launch_gemm(g, static_cast<int>(H), s));
+      // P = U~_T^T X_(T): P[j][h*D + d] = (U~_T^T X_h)[j][d], all heads in one
+      // product (r_T x HD, K = T tokens), split along K for parallelism
+      GemmArgs g = gemm0();
+      g.M = rT; g.N = H * D; g.K = T;
+      g.A = Ut; g.a_dtype = kBF16; g.am = plain(1); g.ak = plain(rT);
+      g.B = x_dev; g.b_dtype = xdt; g.bk = plain(D); g.bn = segmented(D, T * D, 1);
+      g.C = P; g.c_m = H * D; g.c_n = 1;
+      g.ksplit = encode_ksplit(T);
+      g.partial = P + a256(4ull * H * rT * D) / 4;
+      ck(launch_gemm(g, 1, s));
       GemmArgs g2 = gemm0();                     // G~_h = bf16(P_h U~_D)  (r_T x r_D)
       g2.M = rT; g2.N = rD; g2.K = D;
-      g2.A = P; g2.am = plain(D); g2.ak = plain(1); g2.a_batch = rT * D;
+      g2.A = P; g2.am = plain(H * D); g2.ak = plain(1); g2.a_batch = D;
       g2.B = Ud; g2.b_dtype = kBF16; g2.bk = plain(rD); g2.bn = plain(1); g2.b_batch = 0;
       g2.C = G; g2.c_dtype = kBF16; g2.c_m = rD; g2.c_n = 1; g2.c_batch = rT * rD;
       ck(launch_gemm(g2, static_cast<int>(H), s));

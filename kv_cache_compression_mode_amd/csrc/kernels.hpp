@@ -24,6 +24,9 @@ struct GemmArgs {
   void* C; int c_dtype; int64_t c_m, c_n, c_batch;
   float alpha, beta;
   const float* col_scale; int64_t col_scale_batch;
+  // split-K: ksplit > 1 writes partial sums to `partial` ([batch][ksplit][M][N]
+  // floats) and reduces them in a fixed order (deterministic)
+  int ksplit; float* partial; int64_t kchunk;
 };
 
 hipError_t launch_gemm(const GemmArgs& g, int batch, hipStream_t s);
@@ -64,10 +67,11 @@ hipError_t jacobi_small128(float* A, float* V, int batch, float tau_rel, float t
 hipError_t topk_diag(const float* A, int64_t n, int batch, int R, int* idx, hipStream_t s);
 
 // ---- Householder QR, column-major panels [batch][k][ld] (column j at j*ld) ----
-// In place: on return the panel holds the explicit orthonormal Q (m x k) with
-// diag(R) >= 0.  tau_work: [batch][2k] floats.
+// In place: on return the panel holds the explicit orthonormal Q (m x k, m >= k)
+// with diag(R) >= 0.  work: householder_qr_work_floats(m, k, batch) floats.
+size_t householder_qr_work_floats(int64_t m, int64_t k, int batch);
 hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t batch_stride, int batch,
-                          float* tau_work, hipStream_t s);
+                          float* work, hipStream_t s);
 
 // Sort columns by lam descending (ties: lower index), sign-fix (largest |.| entry
 // positive, lowest index on ties) and emit row-major U_out [m][ld_out]; lam_out

@@ -8,10 +8,13 @@
 // Panel A (m x k, column j at A + j*ld, m >= k).  Factorization: for each
 // column j the reflector H_j = I - tau_j v_j v_j^T (v_j[j] = 1) maps
 // A[j:, j] to beta_j e_1 with beta_j = -sign(alpha) * ||A[j:, j]||; the
-// trailing columns are updated in chunks of 16 (one block reduction per
-// chunk).  Then Q = H_0 ... H_{k-1} [I; 0] is formed in place, back to front,
-// and column j is multiplied by sign(beta_j) so that diag(R) >= 0.
-// Threads run along rows, so every access is a coalesced column read.
+// panel columns are updated in chunks of 16 (one block reduction per chunk).
+// Blocked in panels of 32 columns (compact WY, I - V T V^T): a panel is
+// factored by one workgroup, the trailing columns are updated with two
+// matrix-core products, and Q = H_0 ... H_{k-1} [I; 0] is formed in place,
+// back to front, the same way; column j is then multiplied by sign(beta_j) so
+// that diag(R) >= 0.  Threads run along rows: every panel access is a
+// coalesced column read.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -66,84 +69,117 @@ __device__ __forceinline__ void chunk_dots(const float* a, int64_t m, int64_t ld
   __syncthreads();
 }
 
-__global__ __launch_bounds__(QT) void k_hqr(float* A, int64_t m, int64_t k, int64_t ld, int64_t bstride,
-                                            float* tau_g) {
+// Householder factorization of the panel columns [c0, c0 + nb) (rows c0..m-1),
+// one workgroup per matrix.  Reflector vectors stay below the diagonal of A
+// (beta on the diagonal); the explicit unit-lower V panel, the compact-WY
+// factor T (I - V T V^T = H_c0 ... H_{c0+nb-1}) and tau / sign(beta) are
+// written out for the blocked updates.
+__global__ __launch_bounds__(QT) void k_hqr_panel(float* A, int64_t m, int64_t k, int64_t ld,
+                                                  int64_t bstride, int64_t c0, int nb, float* Vp,
+                                                  int64_t vstride, float* Tp, int64_t tstride,
+                                                  float* taus_g) {
   __shared__ float red[QW][CH];
   __shared__ float red1[QW];
   __shared__ float bc;
   __shared__ float wsum[CH];
-  float* a = A + blockIdx.x * bstride;
-  float* taus = tau_g + blockIdx.x * 2 * k;       // [tau_j ..., sign(beta_j) ...]
-  // ---- factorization
-  for (int64_t j = 0; j < k; ++j) {
-    float* col = a + j * ld;
+  __shared__ float S[32][33];
+  __shared__ float Ts[32][33];
+  const int64_t z = blockIdx.x;
+  float* a = A + z * bstride;
+  float* taus = taus_g + z * 2 * k;
+  float* V = Vp + z * vstride;         // column-major m x 32 (this panel's slot)
+  float* T = Tp + z * tstride;         // row-major 32 x 32
+  for (int j = 0; j < nb; ++j) {
+    const int64_t r0 = c0 + j;
+    float* col = a + r0 * ld;
     float s = 0.f;
-    for (int64_t i = j + 1 + threadIdx.x; i < m; i += QT) s += col[i] * col[i];
+    for (int64_t i = r0 + 1 + threadIdx.x; i < m; i += QT) s += col[i] * col[i];
     const float sigma = block_sum(s, red1, &bc);
-    const float alpha = col[j];
+    const float alpha = col[r0];
     float tau = 0.f, beta = alpha;
     if (sigma > 0.f) {
       const float nrm = sqrtf(alpha * alpha + sigma);
       beta = alpha >= 0.f ? -nrm : nrm;
       tau = (beta - alpha) / beta;
       const float scale = 1.f / (alpha - beta);
-      for (int64_t i = j + 1 + threadIdx.x; i < m; i += QT) col[i] *= scale;
+      for (int64_t i = r0 + 1 + threadIdx.x; i < m; i += QT) col[i] *= scale;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-      col[j] = beta;
-      taus[j] = tau;
-      taus[k + j] = beta < 0.f ? -1.f : 1.f;
+      col[r0] = beta;
+      taus[r0] = tau;
+      taus[k + r0] = beta < 0.f ? -1.f : 1.f;
+      Ts[j][j] = tau;
     }
     __syncthreads();
     if (tau != 0.f) {
-      for (int64_t c0 = j + 1; c0 < k; c0 += CH) {
-        const int nc = static_cast<int>(k - c0 < CH ? k - c0 : CH);
-        chunk_dots(a, m, ld, j, c0, nc, 1.f, red, wsum);
-        // A[i][c] -= tau v_i w_c  (v_j = 1)
-        for (int64_t i = j + threadIdx.x; i < m; i += QT) {
-          const float vi = (i == j) ? 1.f : col[i];
+      for (int64_t cc = r0 + 1; cc < c0 + nb; cc += CH) {
+        const int nc = static_cast<int>(c0 + nb - cc < CH ? c0 + nb - cc : CH);
+        chunk_dots(a, m, ld, r0, cc, nc, 1.f, red, wsum);
+        for (int64_t i = r0 + threadIdx.x; i < m; i += QT) {
+          const float vi = (i == r0) ? 1.f : col[i];
 #pragma unroll
           for (int c = 0; c < CH; ++c)
-            if (c < nc) a[(c0 + c) * ld + i] -= tau * vi * wsum[c];
+            if (c < nc) a[(cc + c) * ld + i] -= tau * vi * wsum[c];
         }
         __syncthreads();
       }
     }
   }
-  // ---- form Q in place, back to front
-  for (int64_t j = k - 1; j >= 0; --j) {
-    const float tau = taus[j];
-    float* col = a + j * ld;
-    if (tau != 0.f) {
-      for (int64_t c0 = j + 1; c0 < k; c0 += CH) {
-        const int nc = static_cast<int>(k - c0 < CH ? k - c0 : CH);
-        // row j of the formed columns is zero here: w_c = sum_{i>j} v_i Q[i][c]
-        chunk_dots(a, m, ld, j, c0, nc, 0.f, red, wsum);
-        for (int64_t i = j + threadIdx.x; i < m; i += QT) {
-          const float vi = (i == j) ? 1.f : col[i];
-#pragma unroll
-          for (int c = 0; c < CH; ++c)
-            if (c < nc) a[(c0 + c) * ld + i] -= tau * vi * wsum[c];
-        }
-        __syncthreads();
-      }
+  // S[i][j] = v_i . v_j for i < j  (v_j starts at row c0 + j with a unit entry)
+  for (int j = 1; j < nb; ++j) {
+    for (int c0c = 0; c0c < j; c0c += CH) {
+      const int nc = j - c0c < CH ? j - c0c : CH;
+      chunk_dots(a, m, ld, c0 + j, c0 + c0c, nc, 1.f, red, wsum);
+      if (threadIdx.x < nc) S[c0c + threadIdx.x][j] = wsum[threadIdx.x];
+      __syncthreads();
     }
+  }
+  // T[0:j, j] = -tau_j T[0:j, 0:j] S[0:j, j]  (upper triangular, column by column)
+  if (threadIdx.x == 0) {
+    for (int j = 0; j < nb; ++j) {
+      for (int i = 0; i < j; ++i) {
+        float acc = 0.f;
+        for (int l = i; l < j; ++l) acc += Ts[i][l] * S[l][j];
+        Ts[i][j] = -Ts[j][j] * acc;
+      }
+      for (int i = j + 1; i < 32; ++i) Ts[i][j] = 0.f;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 32 * 32; idx += QT) {
+    const int r = idx / 32, c = idx % 32;
+    T[idx] = (r < nb && c < nb) ? Ts[r][c] : 0.f;
+  }
+  // explicit V panel (zeros above, unit diagonal); columns past nb are zero
+  for (int j = 0; j < 32; ++j) {
+    const float* col = a + (c0 + j) * ld;
     for (int64_t i = threadIdx.x; i < m; i += QT) {
-      float q;
-      if (i < j) q = 0.f;
-      else if (i == j) q = 1.f - tau;
-      else q = -tau * col[i];
-      col[i] = q;
+      float v = 0.f;
+      if (j < nb) v = i < c0 + j ? 0.f : (i == c0 + j ? 1.f : col[i]);
+      V[j * m + i] = v;
     }
-    __syncthreads();
   }
-  // ---- diag(R) >= 0
-  for (int64_t j = 0; j < k; ++j) {
-    if (taus[k + j] < 0.f) {
-      float* col = a + j * ld;
-      for (int64_t i = threadIdx.x; i < m; i += QT) col[i] = -col[i];
-    }
+}
+
+// Q[:, c0 .. c0+nb) <- columns of the identity (rows 0..m-1).
+__global__ __launch_bounds__(256) void k_eye_cols(float* A, int64_t m, int64_t ld, int64_t bstride,
+                                                   int64_t c0, int nb) {
+  float* a = A + blockIdx.y * bstride;
+  for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < m * nb; idx += 256ll * gridDim.x) {
+    const int64_t j = idx / m, i = idx % m;
+    a[(c0 + j) * ld + i] = (i == c0 + j) ? 1.f : 0.f;
+  }
+}
+
+// diag(R) >= 0: column j times sign(beta_j).
+__global__ __launch_bounds__(256) void k_col_signs(float* A, int64_t m, int64_t k, int64_t ld,
+                                                    int64_t bstride, const float* taus_g) {
+  float* a = A + blockIdx.y * bstride;
+  const float* sg = taus_g + blockIdx.y * 2 * k + k;
+  for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < m * k; idx += 256ll * gridDim.x) {
+    const int64_t j = idx / m, i = idx % m;
+    if (sg[j] < 0.f) a[j * ld + i] = -a[j * ld + i];
   }
 }
 
@@ -244,9 +280,82 @@ __global__ __launch_bounds__(256) void k_emit(const float* U, int64_t m, int64_t
 
 }  // namespace
 
-hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t batch_stride, int batch,
-                          float* tau_work, hipStream_t s) {
-  k_hqr<<<batch, QT, 0, s>>>(A, m, k, ld, batch_stride, tau_work);
+size_t householder_qr_work_floats(int64_t m, int64_t k, int batch) {
+  const int64_t P = (k + 31) / 32;
+  // V panels (m x 32 each), T factors (32 x 32 each), W / W2 (32 x k), tau + signs (2k)
+  return static_cast<size_t>(batch) * (P * m * 32 + P * 32 * 32 + 2 * 32 * k + 2 * k + 64);
+}
+
+hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t bstride, int batch,
+                          float* work, hipStream_t s) {
+  constexpr int NB = 32;
+  const int64_t P = (k + NB - 1) / NB;
+  float* Vall = work;                                        // [batch][P][m][32]
+  float* Tall = Vall + static_cast<size_t>(batch) * P * m * NB;   // [batch][P][32][32]
+  float* W = Tall + static_cast<size_t>(batch) * P * NB * NB;     // [batch][32][k]
+  float* W2 = W + static_cast<size_t>(batch) * NB * k;            // [batch][32][k]
+  float* taus = W2 + static_cast<size_t>(batch) * NB * k;         // [batch][2k]
+  const int64_t vstride = P * m * NB, tstride = P * NB * NB;
+  auto Vp = [&](int64_t p) { return Vall + p * m * NB; };
+  auto Tp = [&](int64_t p) { return Tall + p * NB * NB; };
+  auto gemm = [&](int64_t M, int64_t N, int64_t K, const float* Ab, GemmDim am, GemmDim ak, int64_t ab,
+                  const float* Bb, GemmDim bk, GemmDim bn, int64_t bb, float* Cb, int64_t cm, int64_t cn,
+                  int64_t cb, float alpha, float beta) -> hipError_t {
+    if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = Ab; g.a_dtype = kF32; g.am = am; g.ak = ak; g.a_batch = ab;
+    g.B = Bb; g.b_dtype = kF32; g.bk = bk; g.bn = bn; g.b_batch = bb;
+    g.C = Cb; g.c_dtype = kF32; g.c_m = cm; g.c_n = cn; g.c_batch = cb;
+    g.alpha = alpha; g.beta = beta;
+    return launch_gemm(g, batch, s);
+  };
+  hipError_t e;
+  // ---- factorization
+  for (int64_t p = 0; p < P; ++p) {
+    const int64_t c0 = p * NB;
+    const int nb = static_cast<int>(k - c0 < NB ? k - c0 : NB);
+    k_hqr_panel<<<batch, QT, 0, s>>>(A, m, k, ld, bstride, c0, nb, Vp(p), vstride, Tp(p), tstride, taus);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t n2 = k - c0 - nb, mr = m - c0;
+    if (n2 <= 0) continue;
+    // W = V^T A2  (nb x n2, K = m - c0)
+    if ((e = gemm(nb, n2, mr, Vp(p) + c0, plain(m), plain(1), vstride, A + (c0 + nb) * ld + c0, plain(1),
+                  plain(ld), bstride, W, k, 1, NB * k, 1.f, 0.f)) != hipSuccess) return e;
+    // W2 = T^T W
+    if ((e = gemm(nb, n2, nb, Tp(p), plain(1), plain(NB), tstride, W, plain(k), plain(1), NB * k, W2, k,
+                  1, NB * k, 1.f, 0.f)) != hipSuccess) return e;
+    // A2 -= V W2
+    if ((e = gemm(mr, n2, nb, Vp(p) + c0, plain(1), plain(m), vstride, W2, plain(k), plain(1), NB * k,
+                  A + (c0 + nb) * ld + c0, 1, ld, bstride, -1.f, 1.f)) != hipSuccess) return e;
+  }
+  // ---- explicit Q, back to front
+  for (int64_t p = P - 1; p >= 0; --p) {
+    const int64_t c0 = p * NB;
+    const int nb = static_cast<int>(k - c0 < NB ? k - c0 : NB);
+    const int64_t n2 = k - c0 - nb, mr = m - c0;
+    if (n2 > 0) {
+      // Q[c0:, right] -= V (T (V^T Q[c0:, right]))
+      if ((e = gemm(nb, n2, mr, Vp(p) + c0, plain(m), plain(1), vstride, A + (c0 + nb) * ld + c0,
+                    plain(1), plain(ld), bstride, W, k, 1, NB * k, 1.f, 0.f)) != hipSuccess) return e;
+      if ((e = gemm(nb, n2, nb, Tp(p), plain(NB), plain(1), tstride, W, plain(k), plain(1), NB * k, W2,
+                    k, 1, NB * k, 1.f, 0.f)) != hipSuccess) return e;
+      if ((e = gemm(mr, n2, nb, Vp(p) + c0, plain(1), plain(m), vstride, W2, plain(k), plain(1), NB * k,
+                    A + (c0 + nb) * ld + c0, 1, ld, bstride, -1.f, 1.f)) != hipSuccess) return e;
+    }
+    // panel columns: E - V (T V_top^T), V_top = rows c0 .. c0+nb of V
+    int64_t blocks = (m * nb + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    k_eye_cols<<<dim3(blocks, batch), 256, 0, s>>>(A, m, ld, bstride, c0, nb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = gemm(nb, nb, nb, Tp(p), plain(NB), plain(1), tstride, Vp(p) + c0, plain(m), plain(1), vstride,
+                  W2, k, 1, NB * k, 1.f, 0.f)) != hipSuccess) return e;
+    if ((e = gemm(mr, nb, nb, Vp(p) + c0, plain(1), plain(m), vstride, W2, plain(k), plain(1), NB * k,
+                  A + c0 * ld + c0, 1, ld, bstride, -1.f, 1.f)) != hipSuccess) return e;
+  }
+  int64_t blocks = (m * k + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  k_col_signs<<<dim3(blocks, batch), 256, 0, s>>>(A, m, k, ld, bstride, taus);
   return hipGetLastError();
 }
 
