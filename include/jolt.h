@@ -112,6 +112,8 @@ int32_t jolt_spectrum_len(const jolt_alloc_req* req);
 /* Device workspace of jolt_encode / jolt_decode for one tensor. */
 size_t jolt_encode_workspace_bytes(const jolt_shape* shape, jolt_choice choice);
 size_t jolt_decode_workspace_bytes(const jolt_shape* shape, jolt_choice choice);
+size_t jolt_decode_many_workspace_bytes(int32_t n, const jolt_shape* shape,
+                                        const jolt_choice* choices);
 
 /* Bytes of a prepared rotation (jolt_rotation). */
 size_t jolt_rotation_bytes(int32_t D);
@@ -140,7 +142,7 @@ jolt_status jolt_factors(const jolt_alloc_req* req, void* ws_dev, int32_t tensor
 
 /* The seeded rotation Q (D x D, Haar: QR of a counter-based Gaussian matrix
  * with diag(R) > 0), prepared on the host in fp64 and uploaded to q_dev
- * (jolt_rotation_bytes(D) bytes: fp32 Q, fp32 Q^T, bf16 Q, each section
+ * (jolt_rotation_bytes(D) bytes: fp32 Q, fp32 Q^T, bf16 Q^T, each section
  * 256-aligned).  Synchronizes `stream`.
  * Source: JoLT abstract, "a random orthogonal rotation followed by low-bit
  * quantization". */
@@ -163,11 +165,24 @@ jolt_status jolt_encode(const jolt_shape* shape, const void* x_dev, jolt_choice 
 
 /* Decode one record: X^_h = U_T G_h U_D^T + dequant(codes)_h Q, written to
  * xhat_dev in shape->dtype.  shape/choice must describe the record (the
- * device-side header is not read back).  Asynchronous. */
+ * device-side header is not read back).  ws_bytes >=
+ * jolt_decode_workspace_bytes.  Asynchronous.
+ * Arithmetic: bf16 matrix cores with fp32 accumulation; W = G_h U_D^T is
+ * carried as a hi + lo bf16 pair, the dequantized residual and Q in bf16. */
 jolt_status jolt_decode(const jolt_shape* shape, jolt_choice choice,
                         const void* blob_dev, size_t blob_bytes,
                         const void* rot_dev, void* xhat_dev,
                         void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Decode n records of one shape in few launches (up to 32 records each):
+ * record i (choices[i], blobs[i] of blob_bytes[i]) into outs[i].  Same
+ * arithmetic as jolt_decode.  ws_bytes >= jolt_decode_many_workspace_bytes.
+ * Source: JoLT abstract (reconstruction of the whole cache, whose error the
+ * paper reports as relative Frobenius error). */
+jolt_status jolt_decode_many(int32_t n, const jolt_shape* shape, const jolt_choice* choices,
+                             const void* const* blobs, const size_t* blob_bytes,
+                             const void* rot_dev, void* const* outs,
+                             void* ws_dev, size_t ws_bytes, void* stream);
 
 /* Group quantizer alone (rows == 0 is a no-op; pointers may then be NULL):
  * rows x D fp32 rotated residual in y_dev ->

@@ -55,6 +55,7 @@ SIGNATURES = {
     "jolt_spectrum_len": (C.c_int32, [C.POINTER(AllocReq)]),
     "jolt_encode_workspace_bytes": (C.c_size_t, [C.POINTER(Shape), Choice]),
     "jolt_decode_workspace_bytes": (C.c_size_t, [C.POINTER(Shape), Choice]),
+    "jolt_decode_many_workspace_bytes": (C.c_size_t, [C.c_int32, C.POINTER(Shape), C.POINTER(Choice)]),
     "jolt_rotation_bytes": (C.c_size_t, [C.c_int32]),
     "jolt_allocate": (C.c_int, [C.POINTER(AllocReq), C.POINTER(C.c_void_p), C.c_void_p, C.c_size_t,
                                 C.c_void_p, C.POINTER(Plan)]),
@@ -66,6 +67,9 @@ SIGNATURES = {
                               C.c_size_t, C.c_void_p]),
     "jolt_decode": (C.c_int, [C.POINTER(Shape), Choice, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_size_t, C.c_void_p]),
+    "jolt_decode_many": (C.c_int, [C.c_int32, C.POINTER(Shape), C.POINTER(Choice), C.POINTER(C.c_void_p),
+                                   C.POINTER(C.c_size_t), C.c_void_p, C.POINTER(C.c_void_p), C.c_void_p,
+                                   C.c_size_t, C.c_void_p]),
     "jolt_quantize": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                 C.c_void_p]),
     "jolt_plan_from_spectra": (C.c_int, [C.POINTER(AllocReq), C.POINTER(C.c_double), C.c_int32,

@@ -151,53 +151,167 @@ __global__ __launch_bounds__(256) void k_encode_residual(EncodeArgs a) {
   }
 }
 
-// Decode: X^ = Ut W + Yhat Q for a 32-row tile of head h.
-template <typename TO>
-__global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
-  __shared__ float Us[KC][TM + 1];
-  __shared__ float Ys[TM][D + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t h = blockIdx.y, t0 = static_cast<int64_t>(blockIdx.x) * TM;
-  f32x16 acc = {};
-  if (a.r_T > 0) recon_tile(acc, a.Ut, a.W + h * a.r_T * D, a.r_T, a.T, t0, Us);
-  // dequantize the tile: 32 rows x 4 groups, one (row, group) per half-wave pass
-  const uint32_t* sc = reinterpret_cast<const uint32_t*>(a.scales);
-  const uint32_t* cd = reinterpret_cast<const uint32_t*>(a.codes);
-  const int bits = a.bits;
-  for (int idx = tid; idx < TM * D; idx += 256) {
-    const int m = idx / D, c = idx % D;
-    const int64_t t = t0 + m;
-    float v = 0.f;
-    if (t < a.T) {
-      const int64_t g = (h * a.T + t) * 4 + c / 32;
-      const uint32_t s = sc[g];
-      const float m16 = bf16_bits_to_f32(static_cast<uint16_t>(s & 0xffffu));
-      const float s16 = bf16_bits_to_f32(static_cast<uint16_t>(s >> 16));
-      const int pos = (c & 31) * bits;
-      const uint32_t* w = cd + g * bits;
-      uint32_t q = w[pos >> 5] >> (pos & 31);
-      if ((pos & 31) + bits > 32) q |= w[(pos >> 5) + 1] << (32 - (pos & 31));
-      q &= (1u << bits) - 1u;
-      v = fmaf(static_cast<float>(q), s16, m16);
-    }
-    Ys[m][c] = v;
-  }
-  __syncthreads();
-#pragma unroll 8
-  for (int kk = 0; kk < D; kk += 2) {
-    const int d = kk + (lane >> 5);
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Ys[lane & 31][d], a.Q[d * D + wave * 32 + (lane & 31)],
-                                               acc, 0, 0, 0);
-  }
-  TO* out = static_cast<TO*>(a.Xh);
+// ------------------------------------------------------------------ decode
+// bf16 matrix cores (32x32x16, fp32 accumulate).  Stored factors and core are
+// bf16, so U~_T x W is exact per product once W = G~_h U~_D^T is carried as a
+// hi + lo pair of bf16 (relative error 2^-17); the dequantized residual and Q
+// enter in bf16 (relative 2^-9 each, far below the quantization error they
+// ride on).  Every MFMA operand is one 16-byte load per lane: lane l holds
+// row l%32 and k = 8*(l/32) .. +8 of A, column l%32 and the same k of B.
+
+__device__ __forceinline__ bf16x8 load8_bf16(const uint16_t* base, int64_t idx, int64_t limit,
+                                             bool aligned) {
+  bf16x8 v;
+  if (aligned && idx + 8 <= limit) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(base + idx);
+    v = *reinterpret_cast<const bf16x8*>(&raw);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int m = (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-    const int64_t t = t0 + m;
-    if (t < a.T) {
-      const int64_t off = (h * a.T + t) * D + wave * 32 + (lane & 31);
-      if constexpr (sizeof(TO) == 2) out[off] = f32_to_bf16_rne(acc[i]);
-      else out[off] = acc[i];
+    for (int i = 0; i < 8; ++i) {
+      const uint16_t b = idx + i < limit ? base[idx + i] : static_cast<uint16_t>(0);
+      v[i] = __builtin_bit_cast(__bf16, b);
+    }
+  }
+  return v;
+}
+
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0));
+  return v;
+}
+
+// W_h^T = (G~_h U~_D^T)^T as bf16 hi + lo, [h][d][k] with row stride r_Tp.
+// One wave per (record, head, 32 rows of r_T).
+__global__ __launch_bounds__(256) void k_make_w(DecBatch b) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tile = blockIdx.x * 4 + wave;
+  if (tile >= b.wtiles_total) return;
+  int ri = 0;
+  while (ri + 1 < b.n && b.rec[ri + 1].wtile0 <= tile) ++ri;
+  const DecRec& R = b.rec[ri];
+  const int local = tile - R.wtile0;
+  const int ktiles = R.r_Tp / 32;
+  const int h = local / ktiles, k0 = (local % ktiles) * 32;
+  const int r = lane & 31, half = lane >> 5;
+  f32x16 acc[4] = {};
+  const int k = k0 + r;
+  const bool arow = k < R.r_T;
+  const bool ga = (R.r_D % 8) == 0;
+  for (int j0 = 0; j0 < R.r_D; j0 += 16) {
+    const int jj = j0 + 8 * half;
+    const bf16x8 a = arow ? load8_bf16(R.G + (static_cast<int64_t>(h) * R.r_T + k) * R.r_D, jj, R.r_D, ga)
+                          : zero8();
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const bf16x8 bb = load8_bf16(R.Ud + static_cast<int64_t>(32 * ct + r) * R.r_D, jj, R.r_D, ga);
+      acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc[ct], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = (i >> 2) * 8 + half * 4 + (i & 3);
+      const int d = 32 * ct + r;
+      const float w = acc[ct][i];
+      const uint16_t hi = f32_to_bf16_rne(w);
+      const uint16_t lo = f32_to_bf16_rne(w - bf16_bits_to_f32(hi));
+      const int64_t off = (static_cast<int64_t>(h) * D + d) * R.r_Tp + k0 + m;
+      R.Whi[off] = hi;
+      R.Wlo[off] = lo;
+    }
+  }
+}
+
+// One wave per (record, head, 64 rows): X^ rows = U~_T W (hi + lo) + Yhat Q.
+template <typename TO>
+__global__ __launch_bounds__(256) void k_decode(DecBatch b) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tile = blockIdx.x * 4 + wave;
+  if (tile >= b.tiles_total) return;
+  int ri = 0;
+  while (ri + 1 < b.n && b.rec[ri + 1].tile0 <= tile) ++ri;
+  const DecRec& R = b.rec[ri];
+  const int local = tile - R.tile0;
+  const int tilesT = (b.T + 63) / 64;
+  const int64_t h = local / tilesT, t0 = static_cast<int64_t>(local % tilesT) * 64;
+  const int r = lane & 31, half = lane >> 5;
+  f32x16 acc[2][4] = {};
+  const bool ua = (R.r_T % 8) == 0;
+  for (int k0 = 0; k0 < R.r_Tp; k0 += 16) {
+    const int kk = k0 + 8 * half;
+    bf16x8 a[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int64_t t = t0 + 32 * rt + r;
+      a[rt] = t < b.T ? load8_bf16(R.Ut + t * R.r_T, kk, R.r_T, ua) : zero8();
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int64_t wo = (h * D + 32 * ct + r) * R.r_Tp + kk;
+      const uint4 rh = *reinterpret_cast<const uint4*>(R.Whi + wo);
+      const uint4 rl = *reinterpret_cast<const uint4*>(R.Wlo + wo);
+      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&rh);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&rl);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rt], bh, acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rt], bl, acc[rt][ct], 0, 0, 0);
+      }
+    }
+  }
+  const int bits = R.bits;
+  const uint32_t qmask = (1u << bits) - 1u;
+  for (int d0 = 0; d0 < D; d0 += 16) {
+    const int dd = d0 + 8 * half;               // this lane's 8 features
+    const int g = dd >> 5, bitpos = (dd & 31) * bits;
+    bf16x8 y[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int64_t t = t0 + 32 * rt + r;
+      if (t < b.T) {
+        const int64_t gi = (h * b.T + t) * 4 + g;
+        const uint32_t sw = R.scales[gi];
+        const float m16 = bf16_bits_to_f32(static_cast<uint16_t>(sw & 0xffffu));
+        const float s16 = bf16_bits_to_f32(static_cast<uint16_t>(sw >> 16));
+        const uint32_t* cw = R.codes + gi * bits;
+        uint64_t stream = cw[bitpos >> 5];
+        if ((bitpos & 31) + 8 * bits > 32) stream |= static_cast<uint64_t>(cw[(bitpos >> 5) + 1]) << 32;
+        stream >>= (bitpos & 31);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t q = static_cast<uint32_t>(stream >> (i * bits)) & qmask;
+          y[rt][i] = static_cast<__bf16>(fmaf(static_cast<float>(q), s16, m16));
+        }
+      } else {
+        y[rt] = zero8();
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const uint4 rq = *reinterpret_cast<const uint4*>(b.Qt16 + (32 * ct + r) * D + dd);
+      const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&rq);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(y[rt], bq, acc[rt][ct], 0, 0, 0);
+    }
+  }
+  TO* out = static_cast<TO*>(R.out);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t t = t0 + 32 * rt + (i >> 2) * 8 + half * 4 + (i & 3);
+        if (t < b.T) {
+          const int64_t off = (h * b.T + t) * D + 32 * ct + r;
+          if constexpr (sizeof(TO) == 2) out[off] = f32_to_bf16_rne(acc[rt][ct][i]);
+          else out[off] = acc[rt][ct][i];
+        }
+      }
     }
   }
 }
@@ -226,10 +340,14 @@ hipError_t launch_encode_residual(const EncodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid((a.T + TM - 1) / TM, a.H);
-  if (a.out_dtype == kBF16) k_decode<uint16_t><<<grid, 256, 0, s>>>(a);
-  else k_decode<float><<<grid, 256, 0, s>>>(a);
+hipError_t launch_decode_batch(const DecBatch& b, hipStream_t s) {
+  if (b.wtiles_total > 0) {
+    k_make_w<<<(b.wtiles_total + 3) / 4, 256, 0, s>>>(b);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (b.out_dtype == kBF16) k_decode<uint16_t><<<(b.tiles_total + 3) / 4, 256, 0, s>>>(b);
+  else k_decode<float><<<(b.tiles_total + 3) / 4, 256, 0, s>>>(b);
   return hipGetLastError();
 }
 

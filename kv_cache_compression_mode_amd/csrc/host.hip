@@ -579,6 +579,56 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   token_finalize(d, batch, t0, w, xdt, s);
 }
 
+int64_t rtp_of(int r_T) { return (static_cast<int64_t>(r_T) + 31) / 32 * 32; }
+
+size_t decode_ws_one(const jolt_shape* s, jolt_choice c) {
+  if (c.r_T == 0) return 0;
+  return 2 * a256(2ull * s->H * s->D * rtp_of(c.r_T));
+}
+
+// Decode n records of one shape, kDecBatch per launch pair (W prologue + decode).
+void decode_records(int n, const jolt_shape* shape, const jolt_choice* ch, const void* const* blobs,
+                    const void* rot_dev, void* const* outs, void* ws, hipStream_t s) {
+  const int64_t H = shape->H, T = shape->T, D = shape->D;
+  const size_t n2 = static_cast<size_t>(D) * D;
+  const uint16_t* Qt16 = reinterpret_cast<const uint16_t*>(static_cast<const char*>(rot_dev) + 2 * a256(4 * n2));
+  char* wsp = static_cast<char*>(ws);
+  const int64_t tilesT = (T + 63) / 64;
+  for (int i0 = 0; i0 < n; i0 += kDecBatch) {
+    DecBatch b{};
+    b.n = std::min(kDecBatch, n - i0);
+    b.T = static_cast<int32_t>(T);
+    b.out_dtype = shape->dtype == JOLT_BF16 ? kBF16 : kF32;
+    b.Qt16 = Qt16;
+    int tiles = 0, wtiles = 0;
+    for (int j = 0; j < b.n; ++j) {
+      const jolt_choice c = ch[i0 + j];
+      const BlobLayout L = blob_layout(H, T, D, c);
+      const char* blob = static_cast<const char*>(blobs[i0 + j]);
+      DecRec& R = b.rec[j];
+      R.Ut = reinterpret_cast<const uint16_t*>(blob + L.ut);
+      R.Ud = reinterpret_cast<const uint16_t*>(blob + L.ud);
+      R.G = reinterpret_cast<const uint16_t*>(blob + L.g);
+      R.scales = reinterpret_cast<const uint32_t*>(blob + L.sc);
+      R.codes = reinterpret_cast<const uint32_t*>(blob + L.cd);
+      R.out = outs[i0 + j];
+      R.r_T = c.r_T; R.r_D = c.r_D; R.bits = c.bits;
+      R.r_Tp = static_cast<int32_t>(rtp_of(c.r_T));
+      const size_t wb = a256(2ull * H * D * R.r_Tp);
+      R.Whi = reinterpret_cast<uint16_t*>(wsp);
+      R.Wlo = reinterpret_cast<uint16_t*>(wsp + (c.r_T ? wb : 0));
+      wsp += c.r_T ? 2 * wb : 0;
+      R.tile0 = tiles;
+      R.wtile0 = wtiles;
+      tiles += static_cast<int>(H * tilesT);
+      wtiles += static_cast<int>(H * (R.r_Tp / 32));
+    }
+    b.tiles_total = tiles;
+    b.wtiles_total = wtiles;
+    ck(launch_decode_batch(b, s));
+  }
+}
+
 template <typename F>
 jolt_status guard(F&& f) {
   try {
@@ -620,7 +670,17 @@ size_t jolt_encode_workspace_bytes(const jolt_shape* shape, jolt_choice c) {
 
 size_t jolt_decode_workspace_bytes(const jolt_shape* shape, jolt_choice c) {
   if (!shape_ok(shape) || !choice_ok(shape, c)) return 0;
-  return a256(4ull * shape->H * c.r_T * shape->D) + 256;
+  return decode_ws_one(shape, c);
+}
+
+size_t jolt_decode_many_workspace_bytes(int32_t n, const jolt_shape* shape, const jolt_choice* choices) {
+  if (n < 0 || !shape_ok(shape) || (n > 0 && !choices)) return 0;
+  size_t tot = 256;
+  for (int i = 0; i < n; ++i) {
+    if (!choice_ok(shape, choices[i])) return 0;
+    tot += decode_ws_one(shape, choices[i]);
+  }
+  return tot;
 }
 
 size_t jolt_rotation_bytes(int32_t D) {
@@ -661,12 +721,12 @@ jolt_status jolt_rotation(uint64_t seed, int32_t D, void* q_dev, size_t q_bytes,
       const size_t r = i / D, c = i % D;
       buf[i] = static_cast<float>(Q[i]);
       buf[n + c * D + r] = static_cast<float>(Q[i]);       // Q^T
-      // bf16 nearest-even of the fp64 value via its fp32 rounding
+      // bf16 (nearest-even, via the fp32 value) of Q^T: b16[c][r] = Q[r][c]
       float f = static_cast<float>(Q[i]);
       uint32_t u;
       std::memcpy(&u, &f, 4);
       u += 0x7fffu + ((u >> 16) & 1u);
-      b16[i] = static_cast<uint16_t>(u >> 16);
+      b16[c * D + r] = static_cast<uint16_t>(u >> 16);
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* base = static_cast<char*>(q_dev);
@@ -801,35 +861,29 @@ jolt_status jolt_encode(const jolt_shape* shape, const void* x_dev, jolt_choice 
 jolt_status jolt_decode(const jolt_shape* shape, jolt_choice c, const void* blob_dev, size_t blob_bytes,
                         const void* rot_dev, void* xhat_dev, void* ws_dev, size_t ws_bytes, void* stream) {
   if (!shape_ok(shape) || !choice_ok(shape, c) || !blob_dev || !rot_dev || !xhat_dev) return JOLT_EINVAL;
-  const bool tucker = c.r_T > 0;
-  const BlobLayout L = blob_layout(shape->H, shape->T, shape->D, c);
-  if (blob_bytes < L.total) return JOLT_ENOSPACE;
-  if (tucker && (!ws_dev || ws_bytes < jolt_decode_workspace_bytes(shape, c))) return JOLT_ENOSPACE;
+  if (blob_bytes < blob_layout(shape->H, shape->T, shape->D, c).total) return JOLT_ENOSPACE;
+  const size_t need = decode_ws_one(shape, c);
+  if (need > 0 && (!ws_dev || ws_bytes < need)) return JOLT_ENOSPACE;
   return guard([&]() -> jolt_status {
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t H = shape->H, T = shape->T, D = shape->D, rT = c.r_T, rD = c.r_D;
-    const char* blob = static_cast<const char*>(blob_dev);
-    const uint16_t* Ut = reinterpret_cast<const uint16_t*>(blob + L.ut);
-    const uint16_t* Ud = reinterpret_cast<const uint16_t*>(blob + L.ud);
-    const uint16_t* G = reinterpret_cast<const uint16_t*>(blob + L.g);
-    float* W = static_cast<float*>(ws_dev);
-    if (tucker) {
-      GemmArgs g3 = gemm0();                     // W_h = G~_h U~_D^T
-      g3.M = rT; g3.N = D; g3.K = rD;
-      g3.A = G; g3.a_dtype = kBF16; g3.am = plain(rD); g3.ak = plain(1); g3.a_batch = rT * rD;
-      g3.B = Ud; g3.b_dtype = kBF16; g3.bk = plain(1); g3.bn = plain(rD); g3.b_batch = 0;
-      g3.C = W; g3.c_m = D; g3.c_n = 1; g3.c_batch = rT * D;
-      ck(launch_gemm(g3, static_cast<int>(H), s));
-    }
-    DecodeArgs da{};
-    da.Ut = tucker ? Ut : nullptr; da.W = W; da.r_T = rT;
-    da.scales = reinterpret_cast<const uint16_t*>(blob + L.sc);
-    da.codes = reinterpret_cast<const uint8_t*>(blob + L.cd);
-    da.bits = c.bits;
-    da.Q = static_cast<const float*>(rot_dev);
-    da.H = H; da.T = T; da.Xh = xhat_dev;
-    da.out_dtype = shape->dtype == JOLT_BF16 ? kBF16 : kF32;
-    ck(launch_decode(da, s));
+    decode_records(1, shape, &c, &blob_dev, rot_dev, &xhat_dev, ws_dev, static_cast<hipStream_t>(stream));
+    return JOLT_OK;
+  });
+}
+
+jolt_status jolt_decode_many(int32_t n, const jolt_shape* shape, const jolt_choice* choices,
+                             const void* const* blobs, const size_t* blob_bytes, const void* rot_dev,
+                             void* const* outs, void* ws_dev, size_t ws_bytes, void* stream) {
+  if (n < 0 || !shape_ok(shape) || !rot_dev) return JOLT_EINVAL;
+  if (n == 0) return JOLT_OK;
+  if (!choices || !blobs || !blob_bytes || !outs) return JOLT_EINVAL;
+  for (int i = 0; i < n; ++i) {
+    if (!choice_ok(shape, choices[i]) || !blobs[i] || !outs[i]) return JOLT_EINVAL;
+    if (blob_bytes[i] < blob_layout(shape->H, shape->T, shape->D, choices[i]).total) return JOLT_ENOSPACE;
+  }
+  const size_t need = jolt_decode_many_workspace_bytes(n, shape, choices);
+  if (!ws_dev || ws_bytes < need) return JOLT_ENOSPACE;
+  return guard([&]() -> jolt_status {
+    decode_records(n, shape, choices, blobs, rot_dev, outs, ws_dev, static_cast<hipStream_t>(stream));
     return JOLT_OK;
   });
 }

@@ -96,13 +96,26 @@ struct EncodeArgs {
   uint8_t* codes;      // [H][T][4][4*bits]
 };
 hipError_t launch_encode_residual(const EncodeArgs& a, hipStream_t s);
-struct DecodeArgs {
-  const uint16_t* Ut; const float* W; int64_t r_T;
-  const uint16_t* scales; const uint8_t* codes; int bits;
-  const float* Q; int64_t H, T;
-  void* Xh; int out_dtype;
+// Batched decode: up to kDecBatch records of one shape (H, T, D = 128).
+constexpr int kDecBatch = 32;
+struct DecRec {
+  const uint16_t* Ut;      // bf16 [T][r_T]
+  const uint16_t* Ud;      // bf16 [D][r_D]
+  const uint16_t* G;       // bf16 [H][r_T][r_D]
+  const uint32_t* scales;  // [H][T][4] words (offset | step << 16)
+  const uint32_t* codes;   // [H][T][4][bits] words
+  uint16_t* Whi;           // workspace: bf16 [H][D][r_Tp]
+  uint16_t* Wlo;
+  void* out;               // [H][T][D]
+  int32_t r_T, r_D, r_Tp, bits;
+  int32_t tile0, wtile0;   // first decode tile / W tile of this record
 };
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+struct DecBatch {
+  DecRec rec[kDecBatch];
+  int32_t n, T, out_dtype, tiles_total, wtiles_total;
+  const uint16_t* Qt16;    // bf16 [D][D], Qt16[c][d] = Q[d][c]
+};
+hipError_t launch_decode_batch(const DecBatch& b, hipStream_t s);
 hipError_t launch_write_header(void* blob, const uint32_t* words16, hipStream_t s);
 
 }  // namespace jolt

@@ -64,7 +64,7 @@ def spectrum_len(req: AllocReq) -> int:
 
 # -------------------------------------------------------------- rotation
 def rotation(seed: int, D: int = D_FEATURES, device="cuda") -> torch.Tensor:
-    """Prepared rotation buffer (fp32 Q, fp32 Q^T, bf16 Q) on the device."""
+    """Prepared rotation buffer (fp32 Q, fp32 Q^T, bf16 Q^T) on the device."""
     n = lib().jolt_rotation_bytes(D)
     buf = torch.empty(n, dtype=torch.uint8, device=device)
     check(lib().jolt_rotation(seed, D, buf.data_ptr(), n, _stream(buf.device)), "jolt_rotation")
@@ -224,6 +224,24 @@ def decode(blob: torch.Tensor, H: int, T: int, choice, rot: torch.Tensor, dtype=
     check(lib().jolt_decode(C.byref(shape), ch, blob.data_ptr(), blob.numel(), rot.data_ptr(),
                             xh.data_ptr(), ws.data_ptr(), ws.numel(), _stream(blob.device)), "jolt_decode")
     return xh
+
+
+def decode_many_workspace_bytes(H: int, T: int, choices, dtype=torch.bfloat16) -> int:
+    arr = (Choice * len(choices))(*[Choice(*c) for c in choices])
+    return lib().jolt_decode_many_workspace_bytes(len(choices), C.byref(make_shape(H, T, D_FEATURES, dtype)), arr)
+
+
+def decode_many(blobs, H: int, T: int, choices, rot: torch.Tensor, outs, workspace: torch.Tensor,
+                dtype=torch.bfloat16) -> None:
+    """Reconstruct several records of one shape into the given output tensors."""
+    n = len(blobs)
+    shape = make_shape(H, T, D_FEATURES, dtype)
+    ch = (Choice * n)(*[Choice(*c) for c in choices])
+    bp = (C.c_void_p * n)(*[b.data_ptr() for b in blobs])
+    bb = (C.c_size_t * n)(*[b.numel() for b in blobs])
+    op = (C.c_void_p * n)(*[o.data_ptr() for o in outs])
+    check(lib().jolt_decode_many(n, C.byref(shape), ch, bp, bb, rot.data_ptr(), op, workspace.data_ptr(),
+                                 workspace.numel(), _stream(workspace.device)), "jolt_decode_many")
 
 
 def quantize(y: torch.Tensor, bits: int):

@@ -186,12 +186,19 @@ def test_encode_decode_with_oracle_factors(J, rot, single, choice, xdt):
     if r_T:
         exact = exact + tucker.reconstruct(enc["G"], enc["U_T"], enc["U_D"])
         terms = terms + tucker.reconstruct(np.abs(enc["G"]), np.abs(enc["U_T"]), np.abs(enc["U_D"]))
-    gamma = (r_T + r_D + D + 4) * 2.0 ** -24
+    # decode arithmetic: bf16 matrix cores, fp32 accumulation; W = G~ U~_D^T as a
+    # hi + lo bf16 pair (relative 2^-17 after an fp32 product over r_D), the
+    # dequantized residual and Q each rounded to bf16 (relative 2^-9 each)
+    rot_terms = (np.abs(Yh).reshape(-1, D) @ np.abs(Q)).reshape(H, T, D)
+    rec_terms = terms - rot_terms
+    bound = (r_T + r_D + D + 8) * 2.0 ** -24 * terms + 2.0 ** -15 * rec_terms + 2.0 ** -8 * rot_terms
     if xdt == "f32":
         ulp = np.spacing(np.abs(exact).astype(np.float32)).astype(np.float64)
-        assert np.all(np.abs(Xg - exact) <= gamma * terms + ulp)
+        assert np.all(np.abs(Xg - exact) <= bound + ulp)
     else:
-        check_bf16_rounding(Xg, exact, terms, gamma)
+        # the per-element bound is the check; roundings may flip wherever the
+        # bf16-operand error reaches a midpoint, which at 1 bit/element is often
+        check_bf16_rounding(Xg, exact, bound, 1.0, max_frac=0.25)
     # end-to-end error against the oracle's own record
     eo = codec.encode_tensor(X, Ut, Ud, choice, Q)
     err_o = codec.rel_err(X, codec.decode_tensor(eo, Q, xdt))
@@ -288,3 +295,25 @@ def test_small_cache_end_to_end(J, rot, method, L, H, T, ratio):
             xh = J.decode(blob, H, T, ch, rot, dtype=torch.bfloat16)
             err_g = codec.rel_err(X, xh.float().cpu().numpy())
             assert abs(err_g - orc["rel_err"][l][k]) < 1e-4, (l, k, err_g, orc["rel_err"][l][k])
+
+
+def test_decode_many_matches_single_records(J, rot, single):
+    """One batched call (mixed ranks and bit-widths, a no-Tucker record, more
+    records than one launch takes) reproduces the single-record decodes bit
+    for bit."""
+    X0, a, Q = single
+    X = codec.round_to(X0, "bf16")
+    H, T, _ = X.shape
+    xd = to_dev(X, "bf16")
+    Ut32 = torch.from_numpy(np.ascontiguousarray(a["U_T"], dtype=np.float32)).cuda()
+    Ud32 = torch.from_numpy(np.ascontiguousarray(a["U_D"], dtype=np.float32)).cuda()
+    base = [(256, 64, 2), (96, 112, 3), (0, 0, 4), (32, 16, 1), (224, 128, 4)]
+    choices = [base[i % len(base)] for i in range(37)]           # 37 > one launch (32)
+    blobs = [J.encode(xd, c, Ut32 if c[0] else None, Ud32 if c[0] else None, rot) for c in choices]
+    outs = [torch.empty((H, T, D), dtype=torch.bfloat16, device="cuda") for _ in choices]
+    ws = torch.empty(J.decode_many_workspace_bytes(H, T, choices), dtype=torch.uint8, device="cuda")
+    J.decode_many(blobs, H, T, choices, rot, outs, ws)
+    for b, c, o in zip(blobs, choices, outs):
+        single_out = J.decode(b, H, T, c, rot)
+        assert torch.equal(single_out, o)
+    torch.cuda.synchronize()
