@@ -4,7 +4,10 @@
 #include "../../include/jolt.h"
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -404,19 +407,36 @@ GemmArgs gemm0() {
 
 // Jacobi to convergence on `batch` n x n matrices in w.G (V -> w.V); host loop
 // over sweeps, stopping when a sweep applies no rotation.
+bool trace_on() {
+  static const bool on = [] {
+    const char* e = std::getenv("JOLT_TRACE");
+    return e && e[0] && e[0] != '0';
+  }();
+  return on;
+}
+
 void run_jacobi(float* A, float* V, int64_t n, int batch, const AllocWS& w, hipStream_t s) {
   JacobiWork jw{A, V, n, batch, w.J, w.active, w.rot, w.tauabs};
   ck(jacobi_init(jw, kTauAbsRel, s));
   const int nb = static_cast<int>(n / 32);
   std::vector<int> cnt(batch);
+  auto t_prev = std::chrono::steady_clock::now();
   for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
     ck(hipMemsetAsync(w.rot, 0, sizeof(int) * batch, s));
     for (int r = 0; r < nb - 1; ++r) ck(jacobi_round(jw, r, kTauRel, s));
     ck(hipMemcpyAsync(cnt.data(), w.rot, sizeof(int) * batch, hipMemcpyDeviceToHost, s));
     ck(hipStreamSynchronize(s));
-    bool any = false;
-    for (int v : cnt) any |= v != 0;
-    if (!any) break;
+    int64_t tot = 0;
+    int busy = 0;
+    for (int v : cnt) { tot += v; busy += v != 0; }
+    if (trace_on()) {
+      const auto now = std::chrono::steady_clock::now();
+      std::fprintf(stderr, "[jolt] jacobi n=%lld batch=%d sweep %d: %lld rotations, %d matrices busy, %.3f ms\n",
+                   static_cast<long long>(n), batch, sweep, static_cast<long long>(tot), busy,
+                   std::chrono::duration<double, std::milli>(now - t_prev).count());
+      t_prev = now;
+    }
+    if (!tot) break;
   }
 }
 
