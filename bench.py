@@ -32,14 +32,23 @@ def parse():
     p.add_argument("--warmup", type=int, default=1)
     p.add_argument("--config", default="mistral7b_t4096_2x")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tensors", type=int, default=2)
+    p.add_argument("--cpu-sample-tensors", type=int, default=24)
     p.add_argument("--profile-step", action="store_true",
-                   help="run warmup + one step only (for rocprofv3 runs)")
+                   help="run warmup + one step, then a plain copy of a known size (rocprofv3 runs)")
+    p.add_argument("--copy-mib", type=int, default=1024,
+                   help="size of the calibration copy in --profile-step mode")
+    p.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="turn the counter_collection.csv files of two rocprofv3 --pmc runs of "
+                        "--profile-step (FETCH_SIZE, then WRITE_SIZE) into the traffic record "
+                        "the roofline reads, and exit")
     return p.parse_args()
 
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic, args.copy_mib << 20)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this codec benchmark runs on one GPU only: the path has no "
                                    "cross-GPU step (tensors shard by layer with no collective); "
@@ -95,17 +104,39 @@ def main():
     torch.cuda.synchronize()
     K = 1 if args.profile_step else args.steps
     evs = []
+    # per-launch HIP events on the launch stream, and device counters of the
+    # work the Jacobi update performed, over the timed region (that kernel only)
+    if not args.profile_step:
+        jolt.profile_enable("jacobi_update")
     t0 = time.perf_counter()
     for _ in range(K):
         step(evs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    kstats = {}
+    if not args.profile_step:
+        jac = jolt.profile_query("jacobi_update")
+        # per-kernel breakdown from one more step with every kernel bracketed
+        # by events (outside the timed region: the extra events cost time)
+        jolt.profile_enable("*")
+        step()
+        torch.cuda.synchronize()
+        kstats = {name: jolt.profile_query(name) for name in KERNELS}
+        jolt.profile_enable(None)
     ms_alloc = np.mean([a.elapsed_time(b) for a, b, c, d in evs])
     ms_enc = np.mean([b.elapsed_time(c) for a, b, c, d in evs])
     ms_dec = np.mean([c.elapsed_time(d) for a, b, c, d in evs])
     ms_step = wall * 1e3 / K
     if args.profile_step:
-        print(json.dumps({"profile_step_ms": ms_step}), flush=True)
+        # a plain copy of known size (read n bytes, write n bytes), against
+        # which the FETCH_SIZE / WRITE_SIZE counters are scaled
+        n = args.copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_step_ms": ms_step, "copy_bytes": n}), flush=True)
         return
 
     res, blobs, choices = state["res"], state["blobs"], state["choices"]
@@ -157,16 +188,114 @@ def main():
         "plan_bytes": int(res.total_bytes), "budget_bytes": int(res.budget_bytes),
         "rel_err_K_mean": round(float(errs[:, 0].mean()), 6),
         "rel_err_V_mean": round(float(errs[:, 1].mean()), 6),
-        "roofline": {"kernel": "jolt_decode_many (k_make_w + k_decode, whole cache)", "bound": "hbm",
-                     "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "algorithmic_bytes_per_call": int(dec_bytes),
-                     "avg_call_ms": round(dec_ms, 5)},
+        "roofline": roofline_jacobi(jac),
+        "roofline_decode": {"kernel": "jolt_decode_many (k_make_w + k_decode, whole cache)",
+                            "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                            "algorithmic_bytes_per_call": int(dec_bytes),
+                            "avg_call_ms": round(dec_ms, 5)},
+        "kernel_ms_per_step": {k: round(v["total_ms"], 3) for k, v in kstats.items()},
+        "kernel_launches_per_step": {k: v["launches"] for k, v in kstats.items()},
     }
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, host, args.cpu_sample_tensors)
     print(json.dumps(line), flush=True)
+
+
+KERNELS = ("jacobi_update", "jacobi_solve", "jacobi128", "qr_panel", "gemm", "encode_residual",
+           "decode_w", "decode")
+RIDGE_FP32 = MFMA_FP32_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)   # flop/B
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_jac_update_mistral7b_t4096_2x.json")
+JACOBI_SOURCES = tuple(os.path.join(ROOT, "kv_cache_compression_mode_amd", "csrc", f)
+                       for f in ("eig.hip", "device.hpp"))
+
+
+def sources_sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(source_paths, record_path):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE runs,
+    or None when the kernel's source has changed since they were taken."""
+    if not os.path.exists(record_path):
+        return None
+    with open(record_path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != sources_sha256(source_paths):
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
+def _pmc_means(path, counter):
+    """Mean counter value (KiB per dispatch) of the Jacobi update and of the
+    calibration copy (the last elementwise dispatch: the copies follow the
+    fill that allocates their source)."""
+    import csv
+    jac, copy = [], []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            if "k_jac_update" in r["Kernel_Name"]:
+                jac.append(float(r["Counter_Value"]))
+            elif "elementwise" in r["Kernel_Name"]:
+                copy.append(float(r["Counter_Value"]))
+    if not jac or len(copy) < 2:
+        raise SystemExit(f"{path}: no k_jac_update or calibration-copy dispatches of {counter}")
+    return sum(jac) / len(jac), copy[-1], len(jac)
+
+
+def record_traffic(fetch_csv, write_csv, copy_bytes, record_path=None, source_paths=JACOBI_SOURCES):
+    jf, cf, n = _pmc_means(fetch_csv, "FETCH_SIZE")
+    jw, cw, _ = _pmc_means(write_csv, "WRITE_SIZE")
+    kib = copy_bytes / 1024.0
+    f_scale, w_scale = kib / cf, kib / cw      # known bytes / counted KiB of a plain copy
+    rec = {"kernel": "k_jac_update", "workload": "mistral7b_t4096_2x (one step, 64 tensors, n = 1024)",
+           "dispatches": n,
+           "fetch_kib_per_dispatch": round(jf, 3), "write_kib_per_dispatch": round(jw, 3),
+           "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_scale": round(f_scale, 6), "write_scale": round(w_scale, 6),
+           "traffic_bytes_per_launch": round((jf * f_scale + jw * w_scale) * 1024.0),
+           "sources": [os.path.relpath(p, ROOT) for p in source_paths],
+           "source_sha256": sources_sha256(source_paths)}
+    record_path = record_path or TRAFFIC_FILE
+    os.makedirs(os.path.dirname(record_path), exist_ok=True)
+    with open(record_path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+def roofline_jacobi(st):
+    """Roofline of the block-Jacobi update (A <- J^T A J on the touched
+    super-blocks, V <- V J): algorithmic bytes and flops counted on the device
+    by every active workgroup, time from HIP events around every launch."""
+    launches = max(st["launches"], 1)
+    avg_ms = st["total_ms"] / launches
+    bytes_l = st["bytes"] / launches
+    flops_l = st["flops"] / launches
+    ai = flops_l / max(bytes_l, 1.0)
+    gbps = bytes_l / (avg_ms * 1e-3) / 1e9
+    tflops = flops_l / (avg_ms * 1e-3) / 1e12
+    if ai < RIDGE_FP32:
+        bound, achieved, peak, unit = "hbm", gbps, HBM_PEAK_GBPS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", tflops, MFMA_FP32_PEAK_TFLOPS, "TFLOP/s"
+    return {"kernel": "k_jac_update (block-Jacobi rotation of A and V, fp32 MFMA)",
+            "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(JACOBI_SOURCES, TRAFFIC_FILE),
+            "algorithmic_bytes_per_launch": round(bytes_l),
+            "algorithmic_flops_per_launch": round(flops_l),
+            "arithmetic_intensity": round(ai, 2), "ridge_fp32": round(RIDGE_FP32, 2),
+            "GBps": round(gbps, 1), "TFLOPs": round(tflops, 2),
+            "avg_launch_ms": round(avg_ms, 5), "launches": st["launches"]}
 
 
 def cpu_baseline(cfg, host, n_tensors):

@@ -213,6 +213,34 @@ jolt_status jolt_header_parse(const void* header, size_t bytes, jolt_shape* shap
 const char* jolt_status_str(jolt_status s);
 int32_t jolt_version(void);
 
+/* ------------------------------------------------------------ profiling */
+
+/* Per-kernel statistics of the calls made while profiling was on: launches,
+ * summed HIP-event time of those launches on their streams, and the
+ * algorithmic HBM bytes and flops of the work they performed (for the Jacobi
+ * update: counted on the device, active blocks only). */
+typedef struct {
+  int64_t launches;
+  double total_ms;
+  double bytes;
+  double flops;
+} jolt_kernel_stats;
+
+/* Select the kernels to profile: a comma-separated list of names, "*" for
+ * all, NULL or "" to turn profiling off.  Every call synchronizes the device
+ * and clears the records.  While on, the library records two HIP events
+ * around each launch of a selected kernel on its stream; for "jacobi_update"
+ * it also allocates 16 bytes of device counters per workgroup of the largest
+ * grid seen (the only device memory the library allocates by itself; freed
+ * by the next call).  Not safe with concurrent hot-path calls on other
+ * streams.  Kernel names: "jacobi_update", "jacobi_solve", "jacobi128",
+ * "qr_panel", "gemm", "encode_residual", "decode_w", "decode". */
+jolt_status jolt_profile_enable(const char* kernels);
+
+/* Synchronizes the device, then reports the statistics of one kernel name
+ * (zeros if it never ran). */
+jolt_status jolt_profile_query(const char* kernel, jolt_kernel_stats* out);
+
 #ifdef __cplusplus
 }
 #endif

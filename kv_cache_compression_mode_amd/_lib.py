@@ -42,6 +42,11 @@ class Plan(C.Structure):
                 ("total_bytes", C.c_uint64), ("budget_bytes", C.c_uint64), ("r_T_cap", C.c_int32)]
 
 
+class KernelStats(C.Structure):
+    _fields_ = [("launches", C.c_int64), ("total_ms", C.c_double), ("bytes", C.c_double),
+                ("flops", C.c_double)]
+
+
 class JoltError(RuntimeError):
     def __init__(self, status: int, where: str):
         super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}")
@@ -80,6 +85,8 @@ SIGNATURES = {
                                     C.POINTER(C.c_uint64)]),
     "jolt_status_str": (C.c_char_p, [C.c_int]),
     "jolt_version": (C.c_int32, []),
+    "jolt_profile_enable": (C.c_int, [C.c_char_p]),
+    "jolt_profile_query": (C.c_int, [C.c_char_p, C.POINTER(KernelStats)]),
 }
 
 _lib = None

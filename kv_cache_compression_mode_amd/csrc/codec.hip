@@ -335,6 +335,7 @@ hipError_t launch_quantize(const float* Y, int64_t rows, int bits, uint16_t* sca
 
 hipError_t launch_encode_residual(const EncodeArgs& a, hipStream_t s) {
   dim3 grid((a.T + TM - 1) / TM, a.H);
+  ProfScope ps("encode_residual", s);
   if (a.x_dtype == kBF16) k_encode_residual<uint16_t><<<grid, 256, 0, s>>>(a);
   else k_encode_residual<float><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
@@ -342,10 +343,12 @@ hipError_t launch_encode_residual(const EncodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_batch(const DecBatch& b, hipStream_t s) {
   if (b.wtiles_total > 0) {
+    ProfScope ps("decode_w", s);
     k_make_w<<<(b.wtiles_total + 3) / 4, 256, 0, s>>>(b);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  ProfScope ps("decode", s);
   if (b.out_dtype == kBF16) k_decode<uint16_t><<<(b.tiles_total + 3) / 4, 256, 0, s>>>(b);
   else k_decode<float><<<(b.tiles_total + 3) / 4, 256, 0, s>>>(b);
   return hipGetLastError();

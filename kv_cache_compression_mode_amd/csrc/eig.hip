@@ -167,7 +167,8 @@ __global__ __launch_bounds__(ST) void k_jac_solve(const float* A, int64_t n, flo
 
 // Apply the round's rotations: A super-blocks (i <= j) then V row chunks.
 __global__ __launch_bounds__(256) void k_jac_update(float* A, float* V, int64_t n, const float* J,
-                                                    const int* active, int round) {
+                                                    const int* active, int round,
+                                                    unsigned long long* work) {
   __shared__ float M[NS][LP];
   __shared__ float Ji[NS][LP];
   __shared__ float Jj[NS][LP];
@@ -184,6 +185,11 @@ __global__ __launch_bounds__(256) void k_jac_update(float* A, float* V, int64_t 
     const int j = i + rem;
     const int ai = act[i], aj = act[j];
     if (!ai && !aj) return;
+    if (work && tid == 0) {   // bytes of A moved (mirror write off the diagonal), MFMA flops
+      unsigned long long* w = work + 2 * (blockIdx.y * gridDim.x + blockIdx.x);
+      w[0] += static_cast<unsigned long long>(NS * NS * 4 * (i == j ? 2 : 3));
+      w[1] += static_cast<unsigned long long>(4 * NS * NS * NS);
+    }
     int pi, qi, pj, qj;
     rr_pair(i, round, nb, &pi, &qi);
     rr_pair(j, round, nb, &pj, &qj);
@@ -244,6 +250,11 @@ __global__ __launch_bounds__(256) void k_jac_update(float* A, float* V, int64_t 
     const int i = idx0 % np;
     const int64_t r0 = static_cast<int64_t>(idx0 / np) * NS;
     if (!act[i]) return;
+    if (work && tid == 0) {   // the V block read and written, one product
+      unsigned long long* w = work + 2 * (blockIdx.y * gridDim.x + blockIdx.x);
+      w[0] += static_cast<unsigned long long>(NS * NS * 4 * 2);
+      w[1] += static_cast<unsigned long long>(2 * NS * NS * NS);
+    }
     int pi, qi;
     rr_pair(i, round, nb, &pi, &qi);
     float* v = V + z * n * n;
@@ -355,11 +366,18 @@ hipError_t jacobi_init(const JacobiWork& w, float tau_abs_rel, hipStream_t s) {
 
 hipError_t jacobi_round(const JacobiWork& w, int round, float tau_rel, hipStream_t s) {
   const int nb = static_cast<int>(w.n / SB), np = nb / 2;
-  k_jac_solve<<<dim3(np, w.batch), ST, 0, s>>>(w.A, w.n, w.J, w.active, w.rot_count, w.tau_abs,
-                                               round, tau_rel);
+  {
+    ProfScope ps("jacobi_solve", s);
+    k_jac_solve<<<dim3(np, w.batch), ST, 0, s>>>(w.A, w.n, w.J, w.active, w.rot_count, w.tau_abs,
+                                                 round, tau_rel);
+  }
   const int nA = np * (np + 1) / 2;
   const int nV = np * static_cast<int>(w.n / NS);
-  k_jac_update<<<dim3(nA + nV, w.batch), 256, 0, s>>>(w.A, w.V, w.n, w.J, w.active, round);
+  {
+    unsigned long long* work = prof_slots("jacobi_update", static_cast<int64_t>(nA + nV) * w.batch);
+    ProfScope ps("jacobi_update", s);
+    k_jac_update<<<dim3(nA + nV, w.batch), 256, 0, s>>>(w.A, w.V, w.n, w.J, w.active, round, work);
+  }
   return hipGetLastError();
 }
 
@@ -373,6 +391,7 @@ hipError_t jacobi_small128(float* A, float* V, int batch, float tau_rel, float t
     if (e != hipSuccess) return e;
     attr = true;
   }
+  ProfScope ps("jacobi128", s);
   k_jacobi128<<<batch, 512, lds, s>>>(A, V, tau_rel, tau_abs_rel, max_sweeps);
   return hipGetLastError();
 }

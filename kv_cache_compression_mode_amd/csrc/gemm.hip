@@ -247,6 +247,14 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s) {
   g.kchunk = (g.K + g.ksplit - 1) / g.ksplit;
   g.kchunk = (g.kchunk + BK - 1) / BK * BK;            // chunks start on tile edges
   dim3 grid((g.M + BM - 1) / BM, (g.N + BN - 1) / BN, batch * g.ksplit);
+  ProfScope ps("gemm", s);
+  if (prof_enabled("gemm")) {   // dense flops; operands once, C written (and read when beta != 0) once
+    const double ea = g.a_dtype == kBF16 ? 2 : 4, eb = g.b_dtype == kBF16 ? 2 : 4;
+    const double ec = g.c_dtype == kBF16 ? 2 : 4;
+    prof_add_work("gemm",
+                  batch * (g.M * g.K * ea + g.K * g.N * eb + g.M * g.N * ec * (g.beta != 0.f ? 2 : 1)),
+                  2.0 * g.M * g.N * g.K * batch);
+  }
   if (g.a_dtype == kBF16 && g.b_dtype == kBF16) k_gemm<uint16_t, uint16_t><<<grid, 256, 0, s>>>(g);
   else if (g.a_dtype == kBF16) k_gemm<uint16_t, float><<<grid, 256, 0, s>>>(g);
   else if (g.b_dtype == kBF16) k_gemm<float, uint16_t><<<grid, 256, 0, s>>>(g);

@@ -9,11 +9,89 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
 #include <vector>
 
 #include "kernels.hpp"
 
 using namespace jolt;
+
+// ------------------------------------------------------------- profiling
+namespace jolt {
+namespace {
+struct ProfRec {
+  std::vector<std::pair<int, int>> ev;   // indices into the event pool
+  double bytes = 0, flops = 0;           // host-side accounting
+  std::vector<std::pair<unsigned long long*, int64_t>> slots;   // device [count][2] counters
+};
+std::mutex g_prof_mu;
+std::string g_prof_sel;                  // "" off, "*" every kernel, else ",name,name,"
+std::map<std::string, ProfRec> g_prof;
+std::vector<hipEvent_t> g_pool;          // created once, reused after every enable
+size_t g_pool_used = 0;
+
+int pool_event() {
+  if (g_pool_used == g_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return -1;
+    g_pool.push_back(e);
+  }
+  return static_cast<int>(g_pool_used++);
+}
+
+void prof_release() {
+  for (auto& kv : g_prof)
+    for (auto& sl : kv.second.slots) (void)hipFree(sl.first);
+  g_prof.clear();
+  g_pool_used = 0;
+}
+}  // namespace
+
+bool prof_enabled(const char* name) {
+  if (g_prof_sel.empty()) return false;
+  return g_prof_sel == "*" || g_prof_sel.find("," + std::string(name) + ",") != std::string::npos;
+}
+
+unsigned long long* prof_slots(const char* name, int64_t count) {
+  if (!prof_enabled(name) || count <= 0) return nullptr;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRec& r = g_prof[name];
+  if (r.slots.empty() || r.slots.back().second < count) {
+    unsigned long long* p = nullptr;
+    const size_t bytes = static_cast<size_t>(count) * 2 * sizeof(unsigned long long);
+    if (hipMalloc(&p, bytes) != hipSuccess) return nullptr;
+    if (hipMemset(p, 0, bytes) != hipSuccess) { (void)hipFree(p); return nullptr; }
+    r.slots.emplace_back(p, count);
+  }
+  return r.slots.back().first;
+}
+
+void prof_add_work(const char* name, double bytes, double flops) {
+  if (!prof_enabled(name)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRec& r = g_prof[name];
+  r.bytes += bytes;
+  r.flops += flops;
+}
+
+ProfScope::ProfScope(const char* n, hipStream_t s) : name(n), stream(s), e0(-1), e1(-1) {
+  if (!prof_enabled(name)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  e0 = pool_event();
+  e1 = pool_event();
+  if (e0 < 0 || e1 < 0) { e0 = e1 = -1; return; }
+  (void)hipEventRecord(g_pool[e0], stream);
+}
+
+ProfScope::~ProfScope() {
+  if (e0 < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  (void)hipEventRecord(g_pool[e1], stream);
+  g_prof[name].ev.emplace_back(e0, e1);
+}
+}  // namespace jolt
 
 namespace {
 
@@ -951,5 +1029,51 @@ const char* jolt_status_str(jolt_status s) {
 }
 
 int32_t jolt_version(void) { return static_cast<int32_t>(kVersion); }
+
+jolt_status jolt_profile_enable(const char* kernels) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (hipDeviceSynchronize() != hipSuccess) return JOLT_EHIP;   // no recorded event in flight
+  prof_release();
+  if (!kernels || !*kernels) {
+    g_prof_sel.clear();
+  } else if (std::strcmp(kernels, "*") == 0) {
+    g_prof_sel = "*";
+  } else {
+    g_prof_sel = std::string(",") + kernels + ",";
+    g_prof_sel.erase(std::remove(g_prof_sel.begin(), g_prof_sel.end(), ' '), g_prof_sel.end());
+  }
+  return JOLT_OK;
+}
+
+jolt_status jolt_profile_query(const char* kernel, jolt_kernel_stats* out) {
+  if (!kernel || !out) return JOLT_EINVAL;
+  if (hipDeviceSynchronize() != hipSuccess) return JOLT_EHIP;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  auto it = g_prof.find(kernel);
+  jolt_kernel_stats st{0, 0.0, 0.0, 0.0};
+  if (it != g_prof.end()) {
+    const ProfRec& r = it->second;
+    st.launches = static_cast<int64_t>(r.ev.size());
+    for (const auto& e : r.ev) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, g_pool[e.first], g_pool[e.second]) != hipSuccess) return JOLT_EHIP;
+      st.total_ms += ms;
+    }
+    st.bytes = r.bytes;
+    st.flops = r.flops;
+    for (const auto& sl : r.slots) {
+      std::vector<unsigned long long> c(static_cast<size_t>(sl.second) * 2);
+      if (hipMemcpy(c.data(), sl.first, c.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost) !=
+          hipSuccess)
+        return JOLT_EHIP;
+      for (size_t i = 0; i < c.size(); i += 2) {
+        st.bytes += static_cast<double>(c[i]);
+        st.flops += static_cast<double>(c[i + 1]);
+      }
+    }
+  }
+  *out = st;
+  return JOLT_OK;
+}
 
 }  // extern "C"

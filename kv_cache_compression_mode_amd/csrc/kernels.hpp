@@ -7,6 +7,22 @@ namespace jolt {
 
 enum { kBF16 = 0, kF32 = 1 };
 
+// ---- opt-in profiling (jolt_profile_enable): HIP events around launches of a
+// selected kernel on its stream, plus device counters (bytes, flops) that a
+// kernel fills with the work it actually performed: one [2] slot per
+// workgroup, each added to only by the workgroup of that grid position, so
+// launches serialized on one stream accumulate without atomics.
+bool prof_enabled(const char* name);
+unsigned long long* prof_slots(const char* name, int64_t count);   // nullptr when off
+void prof_add_work(const char* name, double bytes, double flops);
+struct ProfScope {
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+  const char* name;
+  hipStream_t stream;
+  int e0, e1;   // event-pool slots, -1 when not recording
+};
+
 // offset(i) = (i / len) * seg + (i % len) * stride   (len = INT64_MAX: plain stride)
 struct GemmDim {
   int64_t len, seg, stride;

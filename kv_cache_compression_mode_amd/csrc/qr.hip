@@ -315,7 +315,10 @@ hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t bs
   for (int64_t p = 0; p < P; ++p) {
     const int64_t c0 = p * NB;
     const int nb = static_cast<int>(k - c0 < NB ? k - c0 : NB);
-    k_hqr_panel<<<batch, QT, 0, s>>>(A, m, k, ld, bstride, c0, nb, Vp(p), vstride, Tp(p), tstride, taus);
+    {
+      ProfScope ps("qr_panel", s);
+      k_hqr_panel<<<batch, QT, 0, s>>>(A, m, k, ld, bstride, c0, nb, Vp(p), vstride, Tp(p), tstride, taus);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t n2 = k - c0 - nb, mr = m - c0;
     if (n2 <= 0) continue;

@@ -261,3 +261,15 @@ def header_parse(header: bytes):
     check(lib().jolt_header_parse(buf, len(header), C.byref(s), C.byref(c), C.byref(seed)),
           "jolt_header_parse")
     return (s.H, s.T, s.D, s.dtype), c.tuple(), seed.value
+
+
+# -------------------------------------------------------------- profiling
+def profile_enable(kernels: str | None = "*") -> None:
+    """Profile the named kernels ("a,b", "*" for all); None or "" turns it off."""
+    check(lib().jolt_profile_enable(kernels.encode() if kernels else None), "jolt_profile_enable")
+
+
+def profile_query(kernel: str) -> dict:
+    st = _lib.KernelStats()
+    check(lib().jolt_profile_query(kernel.encode(), C.byref(st)), "jolt_profile_query")
+    return dict(launches=st.launches, total_ms=st.total_ms, bytes=st.bytes, flops=st.flops)
