@@ -277,6 +277,32 @@ __global__ __launch_bounds__(256) void k_jac_update(float* A, float* V, int64_t 
   }
 }
 
+// Off-diagonal and diagonal sums of squares, rows strided over kOffBlocks
+// workgroups per matrix; one partial pair per workgroup (no atomics).
+__global__ __launch_bounds__(256) void k_offnorm(const float* A, int64_t n, double* part) {
+  const int64_t z = blockIdx.y;
+  const float* a = A + z * n * n;
+  double off = 0.0, dia = 0.0;
+  for (int64_t i = blockIdx.x; i < n; i += kOffBlocks) {
+    const float* row = a + i * n;
+    for (int64_t j = threadIdx.x; j < n; j += 256) {
+      const double v = row[j];
+      if (j == i) dia += v * v;
+      else off += v * v;
+    }
+  }
+  off = wave_sum(off);
+  dia = wave_sum(dia);
+  __shared__ double po[4], pd[4];
+  if ((threadIdx.x & 63) == 0) { po[threadIdx.x >> 6] = off; pd[threadIdx.x >> 6] = dia; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double* p = part + (z * kOffBlocks + blockIdx.x) * 2;
+    p[0] = (po[0] + po[1]) + (po[2] + po[3]);
+    p[1] = (pd[0] + pd[1]) + (pd[2] + pd[3]);
+  }
+}
+
 // Scalar cyclic Jacobi to convergence on one 128 x 128 matrix per workgroup.
 __global__ __launch_bounds__(512) void k_jacobi128(float* A, float* V, float tau_rel,
                                                    float tau_abs_rel, int max_sweeps) {
@@ -378,6 +404,11 @@ hipError_t jacobi_round(const JacobiWork& w, int round, float tau_rel, hipStream
     ProfScope ps("jacobi_update", s);
     k_jac_update<<<dim3(nA + nV, w.batch), 256, 0, s>>>(w.A, w.V, w.n, w.J, w.active, round, work);
   }
+  return hipGetLastError();
+}
+
+hipError_t jacobi_offnorm(const float* A, int64_t n, int batch, double* part, hipStream_t s) {
+  k_offnorm<<<dim3(kOffBlocks, batch), 256, 0, s>>>(A, n, part);
   return hipGetLastError();
 }
 

@@ -109,6 +109,15 @@ constexpr uint64_t kTagSketch = 0x4A4F4C54534B5431ull;     // "JOLTSKT1"
 constexpr float kTauRel = 2e-6f;
 constexpr float kTauAbsRel = 1e-9f;
 constexpr int kMaxSweeps = 30;
+// A matrix of the block-Jacobi batch is done once its relative off-diagonal
+// Frobenius mass off/fro is below 2^-19, or once it has stopped falling (a
+// sweep removes less than 10% of it) after reaching 2^-12: what is left then
+// sits in entries below the rotation thresholds (about n * kTauAbsRel * trace
+// in total), and further sweeps only rotate pairs at the threshold, which no
+// longer moves the leading invariant subspaces or their captured energy.
+constexpr double kOffRel = 1.0 / (1 << 19);
+constexpr double kOffStall = 1.0 / (1 << 12);
+constexpr double kOffStallRatio = 0.9;
 
 struct HipFail {};
 inline void ck(hipError_t e) {
@@ -394,7 +403,7 @@ struct AllocWS {
   float* UT; float* UD; double* lamT; double* lamD; double* frob2;
   const void** xptrs; uint64_t* tags;
   // scratch (chunk tensors)
-  float* G; float* V; float* J; int* active; int* rot; float* tauabs;
+  float* G; float* V; float* J; int* active; int* rot; float* tauabs; double* offp;
   float* GD; float* GDc; float* VD;
   int* order; float* Ucm; float* Vr; float* P; double* lam_tmp; float* qtau; int* perm; float* sgn;
   float* Om; float* Y; float* Z; float* Bm; float* Wr; float* Wd;
@@ -450,6 +459,7 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base) {
   w.active = c.take<int>(static_cast<size_t>(chunk) * (n / 64));
   w.rot = c.take<int>(chunk);
   w.tauabs = c.take<float>(chunk);
+  w.offp = c.take<double>(static_cast<size_t>(chunk) * kOffBlocks * 2);
   w.GD = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
   w.GDc = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
   w.VD = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
@@ -498,23 +508,51 @@ void run_jacobi(float* A, float* V, int64_t n, int batch, const AllocWS& w, hipS
   ck(jacobi_init(jw, kTauAbsRel, s));
   const int nb = static_cast<int>(n / 32);
   std::vector<int> cnt(batch);
+  std::vector<float> tau(batch);
+  std::vector<double> part(static_cast<size_t>(batch) * kOffBlocks * 2);
+  std::vector<char> done(batch, 0);
+  std::vector<double> prev(batch, INFINITY);
+  ck(hipMemcpyAsync(tau.data(), w.tauabs, sizeof(float) * batch, hipMemcpyDeviceToHost, s));
   auto t_prev = std::chrono::steady_clock::now();
   for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
     ck(hipMemsetAsync(w.rot, 0, sizeof(int) * batch, s));
     for (int r = 0; r < nb - 1; ++r) ck(jacobi_round(jw, r, kTauRel, s));
+    ck(jacobi_offnorm(A, n, batch, w.offp, s));
     ck(hipMemcpyAsync(cnt.data(), w.rot, sizeof(int) * batch, hipMemcpyDeviceToHost, s));
+    ck(hipMemcpyAsync(part.data(), w.offp, sizeof(double) * part.size(), hipMemcpyDeviceToHost, s));
     ck(hipStreamSynchronize(s));
     int64_t tot = 0;
-    int busy = 0;
-    for (int v : cnt) { tot += v; busy += v != 0; }
+    int busy = 0, newly = 0;
+    double worst = 0.0;
+    for (int z = 0; z < batch; ++z) {
+      tot += cnt[z];
+      busy += cnt[z] != 0;
+      double off2 = 0.0, dia2 = 0.0;
+      for (int b = 0; b < kOffBlocks; ++b) {
+        off2 += part[(static_cast<size_t>(z) * kOffBlocks + b) * 2];
+        dia2 += part[(static_cast<size_t>(z) * kOffBlocks + b) * 2 + 1];
+      }
+      const double rel = off2 > 0.0 ? std::sqrt(off2 / (off2 + dia2)) : 0.0;
+      worst = std::max(worst, rel);
+      const bool stalled = rel <= kOffStall && rel >= kOffStallRatio * prev[z];
+      prev[z] = rel;
+      if (!done[z] && (rel <= kOffRel || stalled)) {
+        done[z] = 1;
+        tau[z] = INFINITY;          // no pair of this matrix rotates again
+        ++newly;
+      }
+    }
     if (trace_on()) {
       const auto now = std::chrono::steady_clock::now();
-      std::fprintf(stderr, "[jolt] jacobi n=%lld batch=%d sweep %d: %lld rotations, %d matrices busy, %.3f ms\n",
-                   static_cast<long long>(n), batch, sweep, static_cast<long long>(tot), busy,
+      std::fprintf(stderr,
+                   "[jolt] jacobi n=%lld batch=%d sweep %d: %lld rotations, %d matrices busy, "
+                   "max off/fro %.3e, %.3f ms\n",
+                   static_cast<long long>(n), batch, sweep, static_cast<long long>(tot), busy, worst,
                    std::chrono::duration<double, std::milli>(now - t_prev).count());
       t_prev = now;
     }
-    if (!tot) break;
+    if (!tot || std::all_of(done.begin(), done.end(), [](char c) { return c != 0; })) break;
+    if (newly) ck(hipMemcpyAsync(w.tauabs, tau.data(), sizeof(float) * batch, hipMemcpyHostToDevice, s));
   }
 }
 

@@ -75,6 +75,10 @@ struct JacobiWork {
 };
 hipError_t jacobi_init(const JacobiWork& w, float tau_abs_rel, hipStream_t s);
 hipError_t jacobi_round(const JacobiWork& w, int round, float tau_rel, hipStream_t s);
+// Per matrix, kOffBlocks partial sums (off-diagonal squares, diagonal squares)
+// in fp64: part[z][block][2].  The host adds them in a fixed order.
+constexpr int kOffBlocks = 64;
+hipError_t jacobi_offnorm(const float* A, int64_t n, int batch, double* part, hipStream_t s);
 // Scalar Jacobi to convergence on 128 x 128 matrices (one workgroup each):
 // A -> diagonal (in place), V <- eigenvectors.
 hipError_t jacobi_small128(float* A, float* V, int batch, float tau_rel, float tau_abs_rel,
