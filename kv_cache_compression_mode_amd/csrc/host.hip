@@ -226,7 +226,7 @@ int rank_cap_T(int64_t H, int64_t T, int64_t D, double ratio, int step) {
 }
 int numerical_rank(const double* lam, int len, int64_t n) {
   if (len <= 0 || !(lam[0] > 0.0)) return 0;
-  const double thr = static_cast<double>(n) * 0x1p-23 * lam[0];
+  const double thr = static_cast<double>(n) * 0x1p-52 * lam[0];
   int c = 0;
   for (int i = 0; i < len; ++i) c += lam[i] > thr;
   return c;

@@ -19,8 +19,11 @@ T, HD, floor(Bbar / (4 T)) rounded down to a multiple of s_T (Bbar = 2N/ratio,
 the average per-tensor budget: U_T alone may take at most half of it) and the
 numerical rank of every layer's token spectrum; R_D is the smallest of D and
 the layers' feature numerical ranks.  Numerical rank counts eigenvalues above
-n * 2^-23 * lambda_1 (fp32 working precision, n = the Gram's dimension,
-min(T, HD) or D).  Only the leading R_T token eigenvalues are ever read, so a
+n * 2^-52 * lambda_1 (n = the Gram's dimension, min(T, HD) or D): it only
+drops directions that carry no energy at the precision of the fp64 spectra
+the dual reads.  (A cap at fp32 resolution, n * 2^-23 * lambda_1, would cut
+the whole noise bulk of a cache, whose eigenvalues sit near 1e-6 lambda_1 yet
+hold most of the truncation energy, and leave only no-Tucker plans.)  Only the leading R_T token eigenvalues are ever read, so a
 spectrum truncated after them gives the same plan.
 
 Bytes.  The compressed record size (see ``blob_bytes``); the budget is
@@ -89,11 +92,11 @@ def rank_cap_T(H: int, T: int, D: int, ratio: float, step: int = 32) -> int:
 
 
 def numerical_rank(lam, n: int) -> int:
-    """Count of eigenvalues above n * 2^-23 * lambda_1 (n = Gram dimension)."""
+    """Count of eigenvalues above n * 2^-52 * lambda_1 (n = Gram dimension)."""
     lam = [float(v) for v in lam]
     if not lam or lam[0] <= 0.0:
         return 0
-    thr = float(n) * (2.0 ** -23) * lam[0]
+    thr = float(n) * (2.0 ** -52) * lam[0]
     return sum(1 for v in lam if v > thr)
 
 

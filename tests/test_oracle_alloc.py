@@ -51,8 +51,8 @@ def test_rank_cap(H, T, ratio, want):
 
 def test_numerical_rank_and_tail():
     lam = [10.0, 1.0, 1e-9, 0.0]
-    assert alloc.numerical_rank(lam, 4) == 2
-    assert alloc.numerical_rank(lam, 10 ** 6) == 1      # threshold 1.19 > 1.0
+    assert alloc.numerical_rank(lam, 4) == 3            # threshold 8.9e-15 < 1e-9
+    assert alloc.numerical_rank(lam, 10 ** 7) == 2      # threshold 2.2e-8 > 1e-9
     assert alloc.tail(lam, 11.0, 0) == 11.0
     assert alloc.tail(lam, 11.0, 1) == 1.0
     assert alloc.tail(lam, 11.0, 4) == 0.0
