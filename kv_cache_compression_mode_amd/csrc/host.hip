@@ -404,6 +404,7 @@ struct AllocWS {
   const void** xptrs; uint64_t* tags;
   // scratch (chunk tensors)
   float* G; float* V; float* J; int* active; int* rot; float* tauabs; double* offp;
+  float* GDpart;
   float* GD; float* GDc; float* VD;
   int* order; float* Ucm; float* Vr; float* P; double* lam_tmp; float* qtau; int* perm; float* sgn;
   float* Om; float* Y; float* Z; float* Bm; float* Wr; float* Wd;
@@ -415,6 +416,16 @@ struct Dims {
   int64_t H, T, D, HD, nT, R, n_pad, ell, ell_pad;
   bool dual, flash;
 };
+
+// Split-K factor of the feature Gram sum_h X_h^T X_h when it is one product
+// over K = H * T rows (direct and randomized paths): chunks of about 4096
+// rows keep every fp32 accumulation short, and the partial sums are added in
+// a fixed order.  The dual path gets it from the token Gram's diagonal blocks.
+int gram_d_ksplit(const Dims& d) {
+  if (d.dual && !d.flash) return 1;
+  const int64_t K = d.H * d.T;
+  return static_cast<int>(std::min<int64_t>(32, std::max<int64_t>(1, (K + 4095) / 4096)));
+}
 
 Dims dims_of(const jolt_alloc_req* r) {
   Dims d{};
@@ -439,6 +450,7 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base) {
   else per = static_cast<size_t>(d.T) * d.ell * 4 * 2 + static_cast<size_t>(d.HD) * d.ell * 12 +
              static_cast<size_t>(d.ell_pad) * d.ell_pad * 12;
   per += static_cast<size_t>(std::max(d.T, d.HD)) * std::max<int64_t>(d.R, 1) * 8 + (1 << 20);
+  per += static_cast<size_t>(gram_d_ksplit(d)) * d.D * d.D * 4;
   int chunk = static_cast<int>(std::max<size_t>(1, std::min<size_t>(64, (4ull << 30) / per)));
   chunk = std::min(chunk, nt);
   w.chunk = chunk;
@@ -460,6 +472,7 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base) {
   w.rot = c.take<int>(chunk);
   w.tauabs = c.take<float>(chunk);
   w.offp = c.take<double>(static_cast<size_t>(chunk) * kOffBlocks * 2);
+  w.GDpart = c.take<float>(static_cast<size_t>(chunk) * gram_d_ksplit(d) * d.D * d.D);
   w.GD = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
   w.GDc = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
   w.VD = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
@@ -617,6 +630,7 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     gd.M = D; gd.N = D; gd.K = d.H * T;
     gd.am = plain(1); gd.ak = plain(D); gd.bk = plain(D); gd.bn = plain(1);
     gd.C = w.GD; gd.c_m = D; gd.c_n = 1; gd.c_batch = D * D;
+    gd.ksplit = gram_d_ksplit(d); gd.partial = w.GDpart;
     ck(launch_gemm(gd, batch, s));
   }
   feature_factor(d, batch, t0, w, s);
@@ -651,6 +665,7 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     gd.M = D; gd.N = D; gd.K = d.H * T;
     gd.am = plain(1); gd.ak = plain(D); gd.bk = plain(D); gd.bn = plain(1);
     gd.C = w.GD; gd.c_m = D; gd.c_n = 1; gd.c_batch = D * D;
+    gd.ksplit = gram_d_ksplit(d); gd.partial = w.GDpart;
     ck(launch_gemm(gd, batch, s));
     feature_factor(d, batch, t0, w, s);
   }

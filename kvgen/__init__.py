@@ -127,3 +127,34 @@ def config_tensor(cfg: CacheConfig, layer: int, kind: int, T: int | None = None)
     out = (kind == 0 and "K" in cfg.outliers) or (kind == 1 and "V" in cfg.outliers)
     return tensor(cfg.H, cfg.T if T is None else T, cfg.D, seed=cfg.seed, layer=layer,
                   kind=kind, decay=decay, outliers=out, dtype=cfg.dtype)
+
+
+def _config_item(args):
+    name, layer, kind = args
+    return layer, kind, config_tensor(CONFIGS[name], layer, kind)
+
+
+def generate(cfg: CacheConfig, items, workers: int = 8):
+    """Yield (layer, kind, tensor) for every (layer, kind) in ``items``, made by
+    ``workers`` spawned processes (completion order).  Spawned, not forked, so
+    the caller may already hold a GPU context."""
+    import multiprocessing as mp
+    items = [(cfg.name, int(l), int(k)) for l, k in items]
+    if workers <= 1 or len(items) <= 1:
+        for it in items:
+            yield _config_item(it)
+        return
+    import os
+    keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {k: os.environ.get(k) for k in keys}
+    os.environ.update({k: "1" for k in keys})      # one BLAS thread per worker
+    try:
+        pool = mp.get_context("spawn").Pool(min(workers, len(items)))
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    with pool:
+        yield from pool.imap_unordered(_config_item, items)

@@ -81,3 +81,110 @@ def check_bf16_rounding(got: np.ndarray, exact: np.ndarray, abs_terms: np.ndarra
         excess = np.abs(g - e) - half_ulp
         assert np.all(excess <= gamma * t + 1e-30), float(np.max(excess / (t + 1e-30)))
     return float(mism.mean())
+
+
+# ---------------------------------------------------------------------------
+# Row-sampled parity at full size: the oracle's arithmetic applied to chosen
+# (head, token) rows of a GPU record, so that caches far too large for the
+# oracle as a whole are still checked element by element on a sample.
+
+def sample_rows(H: int, T: int, n: int, seed: int = 0):
+    """(heads, tokens) of n rows: the four corners plus uniform draws."""
+    rng = np.random.default_rng(seed)
+    hs = np.concatenate([[0, 0, H - 1, H - 1], rng.integers(0, H, n - 4)])
+    ts = np.concatenate([[0, T - 1, 0, T - 1], rng.integers(0, T, n - 4)])
+    return hs.astype(np.int64), ts.astype(np.int64)
+
+
+def oracle_rows(X_rows: np.ndarray, parts: dict, choice, Q: np.ndarray, hs, ts):
+    """Y = fp32((X - U~_T G~_h U~_D^T) Q^T) on the rows, and the per-element
+    bound on the kernel's fp32 error (as in the whole-tensor check)."""
+    r_T, r_D, _ = choice
+    Xr = np.asarray(X_rows, dtype=np.float64)
+    absQ = np.abs(Q)
+    if r_T > 0:
+        Ut = parts["U_T"][ts]                        # [n, r_T]
+        G = parts["G"][hs]                           # [n, r_T, r_D]
+        Ud = parts["U_D"]                            # [D, r_D]
+        recon = np.einsum("nr,nrs,ds->nd", Ut, G, Ud, optimize=True)
+        terms = np.einsum("nr,nrs,ds->nd", np.abs(Ut), np.abs(G), np.abs(Ud), optimize=True)
+        R = Xr - recon
+        bR = (r_T + r_D + 4) * 2.0 ** -24 * terms
+    else:
+        R, recon, terms = Xr, 0.0 * Xr, 0.0 * Xr
+        bR = np.zeros_like(Xr)
+    bR = bR + 2.0 ** -24 * np.abs(Xr)
+    Y = (R @ Q.T).astype(np.float32)
+    bY = bR @ absQ.T + (D + 4) * 2.0 ** -24 * (np.abs(R) @ absQ.T)
+    return Y, bY
+
+
+def record_rows(parts: dict, hs, ts, bits: int):
+    from oracle import quant
+    return (parts["m16"][hs, ts], parts["s16"][hs, ts],
+            quant.unpack(parts["packed"][hs, ts], bits))
+
+
+def check_codes(m16_g, s16_g, codes_g, Y, bY, bits):
+    """Scales and codes from the GPU vs the oracle quantizer on the oracle's Y
+    (any leading shape, groups of 32 along the last axis of Y).
+
+    They may differ only where the fp32 error bound bY lets a decision flip: a
+    group minimum (or step) within the bound of a bf16 rounding boundary, a
+    code where (y - m16)/s16 is within bound/s16 of a half-integer."""
+    from oracle import bf16, quant
+    m16, s16, codes = quant.quantize(Y, bits)
+    m16, s16 = m16.reshape(-1, 4), s16.reshape(-1, 4)
+    codes = codes.reshape(-1, 4, 32)
+    gm, gs = np.asarray(m16_g).reshape(-1, 4), np.asarray(s16_g).reshape(-1, 4)
+    got = np.asarray(codes_g).reshape(-1, 4, 32)
+    L = 2 ** bits - 1
+    g = np.asarray(Y).reshape(-1, 4, 32).astype(np.float64)
+    b = np.asarray(bY).reshape(-1, 4, 32)
+    bmax = b.max(-1)
+    same = (gm == m16) & (gs == s16)
+    assert same.mean() > 0.98, same.mean()
+    if (~same).any():
+        mn = g.min(-1)
+        lo = bf16.round_down((mn - bmax).astype(np.float32))
+        hi = bf16.round_down((mn + bmax).astype(np.float32))
+        assert np.all(((gm >= lo) & (gm <= hi))[~same])
+        mx = g.max(-1)
+        s_lo = bf16.round_up((((mx - bmax) - hi) / L).astype(np.float32))
+        s_hi = bf16.round_up((((mx + bmax) - lo) / L).astype(np.float32) * np.float32(1 + 2 ** -22))
+        assert np.all(((gs >= s_lo) & (gs <= s_hi))[~same])
+    diff = (got != codes) & same[..., None]
+    if diff.any():
+        t = (g - m16[..., None]) / np.where(s16 == 0, 1, s16)[..., None]
+        frac = np.abs(t - np.floor(t) - 0.5)
+        tol = b / np.where(s16 == 0, 1, s16)[..., None] + 1e-6
+        assert np.all(frac[diff] <= tol[diff])
+        assert np.all(np.abs(got.astype(int) - codes.astype(int))[diff] == 1)
+    assert diff.mean() < 1e-2, diff.mean()
+    return float((~same).mean()), float(diff.mean())
+
+
+def check_decode_rows(out_rows, parts: dict, choice, Q: np.ndarray, hs, ts, out_dtype: str):
+    """GPU decode rows vs the exact decode of the GPU record, within the
+    kernel's error bound: bf16 matrix cores with fp32 accumulation, W = G~ U~_D^T
+    as a hi + lo bf16 pair (relative 2^-17 after an fp32 product over r_D), the
+    dequantized residual and Q each rounded to bf16 (relative 2^-9 each)."""
+    from oracle import quant
+    r_T, r_D, bits = choice
+    m16, s16, codes = record_rows(parts, hs, ts, bits)
+    Yh = quant.dequantize(m16, s16, codes).reshape(-1, D)
+    exact = Yh @ Q
+    rot_terms = np.abs(Yh) @ np.abs(Q)
+    rec_terms = np.zeros_like(exact)
+    if r_T > 0:
+        Ut, G, Ud = parts["U_T"][ts], parts["G"][hs], parts["U_D"]
+        exact = exact + np.einsum("nr,nrs,ds->nd", Ut, G, Ud, optimize=True)
+        rec_terms = np.einsum("nr,nrs,ds->nd", np.abs(Ut), np.abs(G), np.abs(Ud), optimize=True)
+    terms = rot_terms + rec_terms
+    bound = (r_T + r_D + D + 8) * 2.0 ** -24 * terms + 2.0 ** -15 * rec_terms + 2.0 ** -8 * rot_terms
+    got = np.asarray(out_rows, dtype=np.float64)
+    if out_dtype == "f32":
+        ulp = np.spacing(np.abs(exact).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(got - exact) <= bound + ulp)
+        return 0.0
+    return check_bf16_rounding(got, exact, bound, 1.0, max_frac=0.25)

@@ -15,7 +15,7 @@ import torch
 import kvgen
 from oracle import alloc, bf16, codec, flash, quant, rng, rotation, tucker
 
-from gpu_util import D, check_bf16_rounding, max_sine, parse_blob, resolvable_cuts, to_dev
+from gpu_util import D, check_bf16_rounding, check_codes, max_sine, parse_blob, resolvable_cuts, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -112,39 +112,7 @@ def _oracle_from_blob(X, parts, choice, Q, H, T):
 
 
 def _check_codes(parts, Y, bY, bits, H, T):
-    """Scales and codes of the GPU record vs the oracle quantizer on the oracle's Y.
-
-    They may differ only where the fp32 error bound bY lets a decision flip: a
-    group minimum (or step) within the bound of a bf16 rounding boundary, a
-    code where (y - m16)/s16 is within bound/s16 of a half-integer."""
-    m16, s16, codes = quant.quantize(Y, bits)
-    L = 2 ** bits - 1
-    g = Y.reshape(H, T, 4, 32).astype(np.float64)
-    b = bY.reshape(H, T, 4, 32)
-    bmax = b.max(-1)
-    same = (parts["m16"] == m16) & (parts["s16"] == s16)
-    assert same.mean() > 0.98, same.mean()
-    if (~same).any():
-        mn = g.min(-1)
-        lo = bf16.round_down((mn - bmax).astype(np.float32))
-        hi = bf16.round_down((mn + bmax).astype(np.float32))
-        gm = parts["m16"]
-        assert np.all(((gm >= lo) & (gm <= hi))[~same])
-        mx = g.max(-1)
-        s_lo = bf16.round_up((((mx - bmax) - hi) / L).astype(np.float32))
-        s_hi = bf16.round_up((((mx + bmax) - lo) / L).astype(np.float32) * np.float32(1 + 2 ** -22))
-        gs = parts["s16"]
-        assert np.all(((gs >= s_lo) & (gs <= s_hi))[~same])
-    got = quant.unpack(parts["packed"], bits)
-    diff = (got != codes) & same[..., None]
-    if diff.any():
-        t = (g - m16[..., None]) / np.where(s16 == 0, 1, s16)[..., None]
-        frac = np.abs(t - np.floor(t) - 0.5)
-        tol = b / np.where(s16 == 0, 1, s16)[..., None] + 1e-6
-        assert np.all(frac[diff] <= tol[diff])
-        assert np.all(np.abs(got.astype(int) - codes.astype(int))[diff] == 1)
-    assert diff.mean() < 1e-2, diff.mean()
-    return float((~same).mean()), float(diff.mean())
+    return check_codes(parts["m16"], parts["s16"], quant.unpack(parts["packed"], bits), Y, bY, bits)
 
 
 @pytest.mark.parametrize("choice,xdt", [((256, 64, 2), "f32"), ((256, 64, 3), "bf16"),
