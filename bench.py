@@ -2,9 +2,14 @@
 
 One step = the whole path over one synthetic cache: spectra, factors and the
 Lagrangian-dual allocation of all layers x {K, V} (jolt_allocate), encode of
-every tensor (jolt_encode), decode of every tensor (jolt_decode).  The default
-workload is the Mistral-7B-v0.3-shaped GQA cache: 32 layers x {K, V},
+every tensor (jolt_encode), decode of every tensor (jolt_decode_many).  The
+default workload is the Mistral-7B-v0.3-shaped GQA cache: 32 layers x {K, V},
 8 KV heads, T = 4096, D = 128, bf16, 2x byte budget, exact Gram factors.
+``--config`` selects another cache workload: the LLaMA-2-13B-shaped MHA cache
+(40 heads), the T = 1024 FlashJoLT comparison (the exact path is timed too;
+the encode-time ratio and the error delta are reported) or the T = 32768 3x
+long context (randomized factors; decode streams one layer at a time into
+two reused output buffers).
 
 Prints one JSON line.  ``value`` is cache tokens per second of the full step
 (T tokens of the whole cache through allocate + encode + decode); the encode
@@ -32,7 +37,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=1)
     p.add_argument("--config", default="mistral7b_t4096_2x")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tensors", type=int, default=24)
+    p.add_argument("--cpu-sample-tensors", type=int, default=0,
+                   help="tensors the oracle runs on (0: a per-workload default of about 10-30 s)")
     p.add_argument("--profile-step", action="store_true",
                    help="run warmup + one step, then a plain copy of a known size (rocprofv3 runs)")
     p.add_argument("--copy-mib", type=int, default=1024,
@@ -61,72 +67,104 @@ def main():
     from kv_cache_compression_mode_amd import jolt
 
     cfg = kvgen.CONFIGS[args.config]
+    if cfg.ratio <= 0:
+        print(json.dumps({"error": f"{cfg.name} has a fixed choice and no byte budget: it is a parity "
+                                   "case, not a benchmark workload"}))
+        sys.exit(2)
     L, H, T, D = cfg.n_layers, cfg.H, cfg.T, cfg.D
+    streaming = cfg.name in STREAMING       # decode one layer at a time into reused buffers
+    compare = cfg.name in COMPARE_EXACT     # also time the exact path on the same inputs
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating {L}x2 tensors [{H},{T},{D}] {cfg.dtype}", file=sys.stderr, flush=True)
-    host = [[kvgen.config_tensor(cfg, l, k) for k in (0, 1)] for l in range(L)]
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
-    xs = [tuple(torch.from_numpy(host[l][k]).to(tdt).to(dev) for k in (0, 1)) for l in range(L)]
+    xs = [[None, None] for _ in range(L)]
+    for l, k, x in kvgen.generate(cfg, [(l, k) for l in range(L) for k in (0, 1)], workers=8):
+        xs[l][k] = torch.from_numpy(x).to(tdt).to(dev)
+    xs = [tuple(p) for p in xs]
     flat = [xs[l][k] for l in range(L) for k in (0, 1)]
     rot = jolt.rotation(cfg.seed)
-    out = torch.empty((H, T, D), dtype=tdt, device=dev)
-    outs = [torch.empty((H, T, D), dtype=tdt, device=dev) for _ in range(2 * L)]
+    n_out = 2 if streaming else 2 * L
+    outs = [torch.empty((H, T, D), dtype=tdt, device=dev) for _ in range(n_out)]
     stream = torch.cuda.current_stream(dev)
+    print("[bench] inputs resident", file=sys.stderr, flush=True)
+
+    def decode_all(blobs, choices, dws):
+        if streaming:
+            for l in range(L):
+                jolt.decode_many(blobs[2 * l:2 * l + 2], H, T, choices[2 * l:2 * l + 2], rot, outs, dws,
+                                 dtype=tdt)
+        else:
+            jolt.decode_many(blobs, H, T, choices, rot, outs, dws, dtype=tdt)
+
+    def decode_ws_bytes(choices):
+        if streaming:
+            return max(jolt.decode_many_workspace_bytes(H, T, choices[2 * l:2 * l + 2], tdt) for l in range(L))
+        return jolt.decode_many_workspace_bytes(H, T, choices, tdt)
 
     state = {}
 
-    def step(record=None):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e2 = torch.cuda.Event(enable_timing=True)
-        e3 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        res = jolt.allocate(xs, ratio=cfg.ratio, method=cfg.method, bits=cfg.bits, seed=cfg.seed)
-        e1.record(stream)
+    def step(method, record=None):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record(stream)
+        res = jolt.allocate(xs, ratio=cfg.ratio, method=method, bits=cfg.bits, seed=cfg.seed)
+        ev[1].record(stream)
         blobs, choices = [], []
         for i, x in enumerate(flat):
             ch = res.choice_of(i // 2, i % 2)
             Ut, Ud = res.factors(i)
             blobs.append(jolt.encode(x, ch, Ut, Ud, rot, seed=cfg.seed))
             choices.append(ch)
-        e2.record(stream)
-        dws = torch.empty(jolt.decode_many_workspace_bytes(H, T, choices, tdt), dtype=torch.uint8,
-                          device=dev)
-        jolt.decode_many(blobs, H, T, choices, rot, outs, dws, dtype=tdt)
-        e3.record(stream)
-        state.update(res=res, blobs=blobs, choices=choices, ev=(e0, e1, e2, e3))
+        ev[2].record(stream)
+        dws = torch.empty(decode_ws_bytes(choices), dtype=torch.uint8, device=dev)
+        decode_all(blobs, choices, dws)
+        ev[3].record(stream)
+        state.update(res=res, blobs=blobs, choices=choices)
         if record is not None:
-            record.append(state["ev"])
+            record.append(ev)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    K = 1 if args.profile_step else args.steps
-    evs = []
-    # per-launch HIP events on the launch stream, and device counters of the
-    # work the Jacobi update performed, over the timed region (that kernel only)
-    if not args.profile_step:
-        jolt.profile_enable("jacobi_update")
-    t0 = time.perf_counter()
-    for _ in range(K):
-        step(evs)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kstats = {}
-    if not args.profile_step:
-        jac = jolt.profile_query("jacobi_update")
-        # per-kernel breakdown from one more step with every kernel bracketed
-        # by events (outside the timed region: the extra events cost time)
-        jolt.profile_enable("*")
-        step()
+    def run(method, K, profile):
+        for _ in range(args.warmup):
+            step(method)
         torch.cuda.synchronize()
-        kstats = {name: jolt.profile_query(name) for name in KERNELS}
-        jolt.profile_enable(None)
-    ms_alloc = np.mean([a.elapsed_time(b) for a, b, c, d in evs])
-    ms_enc = np.mean([b.elapsed_time(c) for a, b, c, d in evs])
-    ms_dec = np.mean([c.elapsed_time(d) for a, b, c, d in evs])
-    ms_step = wall * 1e3 / K
+        evs = []
+        # per-launch HIP events on the launch stream, and device counters of
+        # the work the Jacobi update performed, over the timed region
+        if profile:
+            jolt.profile_enable("jacobi_update")
+        t0 = time.perf_counter()
+        for _ in range(K):
+            step(method, evs)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        jac = None
+        if profile:
+            jac = jolt.profile_query("jacobi_update")
+            jolt.profile_enable(None)
+        ph = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(3)]
+        return wall * 1e3 / K, ph, jac
+
+    def errors():
+        """Relative Frobenius error of every tensor (outside the timed region)."""
+        blobs, choices = state["blobs"], state["choices"]
+        dws = torch.empty(decode_ws_bytes(choices), dtype=torch.uint8, device=dev)
+        errs = []
+        for l in range(L):
+            if streaming:
+                jolt.decode_many(blobs[2 * l:2 * l + 2], H, T, choices[2 * l:2 * l + 2], rot, outs, dws,
+                                 dtype=tdt)
+                pair = outs
+            else:
+                pair = outs[2 * l:2 * l + 2]
+            if not streaming and l == 0:
+                decode_all(blobs, choices, dws)
+            for k in (0, 1):
+                xd = xs[l][k].double()
+                errs.append(float(torch.linalg.vector_norm(xd - pair[k].double()) / torch.linalg.vector_norm(xd)))
+        return np.array(errs).reshape(L, 2)
+
+    K = 1 if args.profile_step else args.steps
+    ms_step, (ms_alloc, ms_enc, ms_dec), jac = run(cfg.method, K, not args.profile_step)
     if args.profile_step:
         # a plain copy of known size (read n bytes, write n bytes), against
         # which the FETCH_SIZE / WRITE_SIZE counters are scaled
@@ -139,33 +177,36 @@ def main():
         print(json.dumps({"profile_step_ms": ms_step, "copy_bytes": n}), flush=True)
         return
 
+    # per-kernel breakdown from one more step with every kernel bracketed by
+    # events (outside the timed region: the extra events cost time)
+    jolt.profile_enable("*")
+    step(cfg.method)
+    torch.cuda.synchronize()
+    kstats = {name: jolt.profile_query(name) for name in KERNELS}
+    jolt.profile_enable(None)
+
     res, blobs, choices = state["res"], state["blobs"], state["choices"]
     blob_total = sum(b.numel() for b in blobs)
     in_bytes = sum(x.numel() * x.element_size() for x in flat)
 
     # decode roofline: algorithmic bytes = every record read once + every output
-    # written once, over the batched decode of the whole cache, timed live with
-    # HIP events on the launch stream
-    dws = torch.empty(jolt.decode_many_workspace_bytes(H, T, choices, tdt), dtype=torch.uint8, device=dev)
+    # written once, over the decode of the whole cache (one batched call, or the
+    # layer-by-layer stream), timed live with HIP events on the launch stream
+    dws = torch.empty(decode_ws_bytes(choices), dtype=torch.uint8, device=dev)
     reps = 5
     de0, de1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     de0.record(stream)
     for _ in range(reps):
-        jolt.decode_many(blobs, H, T, choices, rot, outs, dws, dtype=tdt)
+        decode_all(blobs, choices, dws)
     de1.record(stream)
     torch.cuda.synchronize()
     dec_ms = de0.elapsed_time(de1) / reps
     dec_bytes = (blob_total - 256 * len(flat)) + in_bytes
     dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+    errs = errors()
 
-    # quality on every tensor (outside the timed region)
-    errs = []
-    for i, x in enumerate(flat):
-        xh = outs[i]
-        xd = x.double()
-        errs.append(float(torch.linalg.vector_norm(xd - xh.double()) / torch.linalg.vector_norm(xd)))
-    errs = np.array(errs).reshape(L, 2)
-
+    dec_kernel = ("jolt_decode_many per layer (K + V) into two reused buffers, all layers" if streaming
+                  else "jolt_decode_many (k_make_w + k_decode, whole cache)")
     line = {
         "metric": "JoLT encode tokens/s + decode GB/s, Mistral-7B KV shape, 2x budget, 1 GPU",
         "value": round(T / (ms_step * 1e-3), 2),
@@ -177,19 +218,19 @@ def main():
         "data": "synthetic (seeded low-rank + noise + outlier channels, model cache shapes)",
         "config": {"workload": cfg.name, "layers": L, "kv_heads": H, "tokens": T, "head_dim": D,
                    "input_dtype": cfg.dtype, "budget_ratio": cfg.ratio, "method": cfg.method,
-                   "tensors": 2 * L},
+                   "tensors": 2 * L, "decode": "streamed per layer" if streaming else "one batched call"},
         "phases_ms": {"allocate": round(ms_alloc, 3), "encode": round(ms_enc, 3),
                       "decode": round(ms_dec, 3)},
         "encode_tokens_per_s": round(T / ((ms_alloc + ms_enc) * 1e-3), 2),
         "decode_GBps": round(dec_gbps, 1),
         "decode_ms": round(dec_ms, 4),
-        "decode_output_GBps": round(in_bytes / (ms_dec * 1e-3) / 1e9, 1),
+        "decode_output_GBps": round(in_bytes / (dec_ms * 1e-3) / 1e9, 1),
         "compression_ratio_vs_bf16": round(in_bytes * (2 / flat[0].element_size()) / blob_total, 4),
         "plan_bytes": int(res.total_bytes), "budget_bytes": int(res.budget_bytes),
         "rel_err_K_mean": round(float(errs[:, 0].mean()), 6),
         "rel_err_V_mean": round(float(errs[:, 1].mean()), 6),
-        "roofline": roofline_jacobi(jac),
-        "roofline_decode": {"kernel": "jolt_decode_many (k_make_w + k_decode, whole cache)",
+        "roofline": roofline_jacobi(jac) if jac and jac["launches"] else None,
+        "roofline_decode": {"kernel": dec_kernel,
                             "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                             "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                             "algorithmic_bytes_per_call": int(dec_bytes),
@@ -197,11 +238,33 @@ def main():
         "kernel_ms_per_step": {k: round(v["total_ms"], 3) for k, v in kstats.items()},
         "kernel_launches_per_step": {k: v["launches"] for k, v in kstats.items()},
     }
+    if compare:
+        # the exact Gram path on the same inputs, same budget, its own plan
+        ex_step, (ex_alloc, ex_enc, _), _ = run("exact", K, False)
+        ex_errs = errors()
+        line["exact_path"] = {
+            "ms_per_step": round(ex_step, 3),
+            "encode_ms": round(ex_alloc + ex_enc, 3),
+            "rel_err_K_mean": round(float(ex_errs[:, 0].mean()), 6),
+            "rel_err_V_mean": round(float(ex_errs[:, 1].mean()), 6)}
+        line["encode_time_ratio_exact_over_flash"] = round((ex_alloc + ex_enc) / (ms_alloc + ms_enc), 3)
+        line["rel_err_delta_flash_minus_exact"] = {
+            "K": round(float(errs[:, 0].mean() - ex_errs[:, 0].mean()), 7),
+            "V": round(float(errs[:, 1].mean() - ex_errs[:, 1].mean()), 7)}
 
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, host, args.cpu_sample_tensors)
+        n_cpu = args.cpu_sample_tensors if args.cpu_sample_tensors > 0 else CPU_SAMPLE.get(cfg.name, 2)
+        line["cpu_baseline"] = cpu_baseline(cfg, n_cpu)
     print(json.dumps(line), flush=True)
 
+
+# workloads whose decode streams one layer (K + V) at a time into two reused
+# output buffers, and workloads that also time the exact path (FlashJoLT
+# comparison); oracle sample sizes that take about 10-30 s on the host
+STREAMING = {"mistral7b_t32768_3x"}
+COMPARE_EXACT = {"mistral7b_t1024_flash"}
+CPU_SAMPLE = {"mistral7b_t4096_2x": 24, "mistral7b_t1024_flash": 64, "llama13b_t4096_2x": 2,
+              "mistral7b_t32768_3x": 4}
 
 KERNELS = ("jacobi_update", "jacobi_solve", "jacobi128", "qr_panel", "gemm", "encode_residual",
            "decode_w", "decode")
@@ -298,10 +361,11 @@ def roofline_jacobi(st):
             "avg_launch_ms": round(avg_ms, 5), "launches": st["launches"]}
 
 
-def cpu_baseline(cfg, host, n_tensors):
+def cpu_baseline(cfg, n_tensors):
     """The fp64 oracle on a bounded sample of the same workload (host cores)."""
     import numpy as np
 
+    import kvgen
     from oracle import alloc, codec, rotation
     try:
         from threadpoolctl import threadpool_info
@@ -310,21 +374,22 @@ def cpu_baseline(cfg, host, n_tensors):
         cores = len(os.sched_getaffinity(0))
     cap = alloc.rank_cap_T(cfg.H, cfg.T, cfg.D, cfg.ratio)
     Q = rotation.rotation(cfg.seed, cfg.D)
-    t0 = time.perf_counter()
+    dt = 0.0
     done = 0
     for i in range(n_tensors):
         l, k = i // 2, i % 2
-        X = host[l][k].astype(np.float64)
+        X = kvgen.config_tensor(cfg, l, k).astype(np.float64)   # input generation is not timed
+        t0 = time.perf_counter()
         a = codec.analyze(X, cap, cfg.method, cfg.seed, l, k)
         e = codec.encode_tensor(X, a["U_T"], a["U_D"], (cap, 64, 2), Q)
         codec.decode_tensor(e, Q, cfg.dtype)
+        dt += time.perf_counter() - t0
         done += 1
-    dt = time.perf_counter() - t0
     frac = done / (2 * cfg.n_layers)
     return {"value": round(cfg.T * frac / dt, 2), "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{done} of {2 * cfg.n_layers} tensors (layers 0..{(done - 1) // 2}): analyze "
-                      f"(exact fp64 factors) + encode at (r_T={cap}, r_D=64, b=2) + decode; "
+                      f"({cfg.method} fp64 factors) + encode at (r_T={cap}, r_D=64, b=2) + decode; "
                       f"the dual allocation over the whole cache (milliseconds) is not included; "
                       f"tokens/s scaled by the sampled fraction of the cache, {dt:.1f} s"}
 
