@@ -162,6 +162,339 @@ __global__ __launch_bounds__(QT) void k_hqr_panel(float* A, int64_t m, int64_t k
   }
 }
 
+// ---- LDS-resident panels and tall-skinny QR (TSQR) with Householder
+// reconstruction.  A panel block of up to kLeaf rows x 32 columns lives in
+// LDS (128 KB) and is factored there with one row per thread.  Taller panels
+// are split into row leaves factored independently; their stacked R factors
+// are factored once more (the TSQR tree), the panel's orthonormal factor is
+// assembled as diag(Q_i) Q_top, and the compact-WY form I - V T V^T of the
+// panel is recovered from it by a sign-chosen LU of Q - S (Ballard, Demmel,
+// Grigori, Jacobsen, Knight, Nguyen, "Reconstructing Householder vectors from
+// tall-skinny QR", 2015): V = L, T = -U S L_1^{-T}, and the Householder R is
+// S R, so sign(beta_j) = s_j when diag(R) >= 0.  The blocked updates that
+// follow use V and T exactly as for a panel factored in place.
+constexpr int kLeaf = 1024;      // rows of one LDS block (one per thread)
+constexpr int LT = 1024;         // threads of the LDS kernels
+constexpr int LW = LT / 64;      // waves
+constexpr int kStack = 32 * 32 * 32;   // per matrix: up to 32 leaves x 32 rows x 32 (Rs, Qt)
+
+// Wave sums of 32 per-lane values at once (a halving butterfly): lane l ends
+// with the total of value l >> 1.
+__device__ __forceinline__ float reduce32(float (&v)[32], int lane) {
+#pragma unroll
+  for (int cnt = 32, off = 32; cnt > 1; cnt >>= 1, off >>= 1) {
+    const int h = cnt >> 1;
+    const bool up = (lane & off) != 0;
+#pragma unroll
+    for (int q = 0; q < h; ++q) {
+      const float send = up ? v[q] : v[q + h];
+      const float keep = up ? v[q + h] : v[q];
+      v[q] = keep + __shfl_xor(send, off);
+    }
+  }
+  return v[0] + __shfl_xor(v[0], 1);
+}
+
+struct LdsQr {
+  float Ts[32][33];    // compact-WY T
+  float Mt[32][33];    // T V_1^T (explicit Q)
+  float red[LW][32];
+  float dots[32];
+  float sgn[32];
+  float bc;
+};
+
+// Householder QR of the mr x nb block P (column-major, column stride kLeaf,
+// mr <= kLeaf, nb <= 32), one row per thread.  On return the upper triangle
+// holds R (beta_j on the diagonal), the strict lower part the vectors v_j
+// (unit leading entry implied), L.Ts the factor T with I - V T V^T =
+// H_0 ... H_{nb-1}, L.sgn[j] = sign(beta_j).  Per column: the norm below the
+// diagonal, then one fused pass of dot products of v_j with every other
+// column: against later columns they drive the update, against earlier
+// reflectors they give column j of T (T[0:j, j] = -tau_j T[0:j, 0:j] V^T v_j).
+__device__ void lds_householder(float* P, int mr, int nb, LdsQr& L) {
+  const int i = threadIdx.x, lane = i & 63, wave = i >> 6;
+  for (int j = 0; j < nb; ++j) {
+    const float x = (i > j && i < mr) ? P[j * kLeaf + i] : 0.f;
+    float ss = wave_sum(x * x);
+    if (lane == 0) L.red[wave][0] = ss;
+    __syncthreads();
+    if (i == 0) {
+      float t = 0.f;
+      for (int w = 0; w < LW; ++w) t += L.red[w][0];
+      L.bc = t;
+    }
+    __syncthreads();
+    const float sigma = L.bc;
+    const float alpha = P[j * kLeaf + j];
+    float tau = 0.f, beta = alpha, scale = 0.f;
+    if (sigma > 0.f) {
+      const float nrm = sqrtf(alpha * alpha + sigma);
+      beta = alpha >= 0.f ? -nrm : nrm;
+      tau = (beta - alpha) / beta;
+      scale = 1.f / (alpha - beta);
+    }
+    const float v = (i == j) ? 1.f : (i > j && i < mr ? x * scale : 0.f);
+    float part[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c)
+      part[c] = (c < nb && c != j && i >= j && i < mr) ? P[c * kLeaf + i] * v : 0.f;
+    const float tot = reduce32(part, lane);
+    if ((lane & 1) == 0) L.red[wave][lane >> 1] = tot;
+    __syncthreads();
+    if (i < 32) {
+      float t = 0.f;
+      for (int w = 0; w < LW; ++w) t += L.red[w][i];
+      L.dots[i] = t;
+    }
+    __syncthreads();
+    if (i > j && i < mr) P[j * kLeaf + i] = v;
+    if (i == j) P[j * kLeaf + j] = beta;
+    if (tau != 0.f && i >= j && i < mr) {
+      for (int c = j + 1; c < nb; ++c) P[c * kLeaf + i] -= tau * v * L.dots[c];
+    }
+    if (i < 32) {
+      float t = 0.f;
+      if (i < j) {
+        for (int l = i; l < j; ++l) t += L.Ts[i][l] * L.dots[l];
+        t *= -tau;
+      } else if (i == j) {
+        t = tau;
+      }
+      L.Ts[i][j] = t;
+    }
+    if (i == 0) L.sgn[j] = beta < 0.f ? -1.f : 1.f;
+    __syncthreads();
+  }
+  for (int idx = i; idx < 32 * 32; idx += LT) {
+    const int r = idx / 32, c = idx % 32;
+    if (r >= nb || c >= nb) L.Ts[r][c] = 0.f;
+  }
+  __syncthreads();
+}
+
+// Row i of the explicit Q = (I - V T V^T)[:, :nb] of a factored block.
+__device__ void lds_explicit_q_row(const float* P, int nb, LdsQr& L, float (&q)[32]) {
+  const int i = threadIdx.x;
+  // Mt = T V_1^T (V_1: top nb rows, unit lower)
+  {
+    const int a = i / 32, c = i % 32;
+    float t = 0.f;
+    if (a < nb && c < nb) {
+      for (int b = a; b <= c && b < nb; ++b) {           // T upper, V_1[c][b] = 0 for b > c
+        const float vcb = (b == c) ? 1.f : P[b * kLeaf + c];
+        t += L.Ts[a][b] * vcb;
+      }
+    }
+    L.Mt[a][c] = t;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < 32; ++c) q[c] = (i == c) ? 1.f : 0.f;
+  for (int a = 0; a < nb; ++a) {
+    const float via = (i == a) ? 1.f : (i > a ? P[a * kLeaf + i] : 0.f);
+    if (via != 0.f) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) q[c] -= via * L.Mt[a][c];
+    }
+  }
+}
+
+// mode 0: the whole panel (m - c0 <= kLeaf rows): explicit V (zero above
+//         row c0) -> Vp, T -> Tp, tau / sign(beta) -> taus.
+// mode 1: leaf blockIdx.x of a tall panel (nl leaves of rl rows): explicit
+//         Q_i -> Qb (column-major, (m - c0) x 32), R_i -> Rs rows 32 i ...
+// mode 2: the stacked R factors (nl * 32 rows) -> explicit Q_top -> Qt
+//         (row-major, 32 wide), columns signed so that diag(R) >= 0.
+__global__ __launch_bounds__(LT) void k_qr_block(const float* A, int64_t m, int64_t ld, int64_t bstride,
+                                                 int64_t c0, int nb, int mode, int nl, int64_t rl,
+                                                 float* Vp, int64_t vstride, float* Tp, int64_t tstride,
+                                                 float* taus_g, int64_t k, float* Qb, float* Rs, float* Qt,
+                                                 int64_t aux_stride) {
+  extern __shared__ float P[];                 // [32][kLeaf]
+  __shared__ LdsQr L;
+  const int i = threadIdx.x;
+  const int64_t z = blockIdx.y;
+  const int64_t mp = m - c0;
+  int64_t row0 = 0;
+  int mr;
+  if (mode == 0) {
+    mr = static_cast<int>(mp);
+  } else if (mode == 1) {
+    row0 = blockIdx.x * rl;
+    mr = static_cast<int>(mp - row0 < rl ? mp - row0 : rl);
+  } else {
+    mr = nl * 32;
+  }
+  for (int c = 0; c < 32; ++c) {
+    float v = 0.f;
+    if (c < nb && i < mr) {
+      if (mode == 2) v = Rs[z * kStack + static_cast<int64_t>(i) * 32 + c];
+      else v = A[z * bstride + (c0 + c) * ld + c0 + row0 + i];
+    }
+    P[c * kLeaf + i] = v;
+  }
+  __syncthreads();
+  lds_householder(P, mr, nb, L);
+  if (mode == 0) {
+    float* V = Vp + z * vstride;
+    for (int c = 0; c < 32; ++c) {
+      for (int64_t r = i; r < m; r += LT) {
+        float v = 0.f;
+        if (c < nb) {
+          const int64_t rr = r - c0;
+          v = rr < c ? 0.f : (rr == c ? 1.f : P[c * kLeaf + rr]);
+        }
+        V[c * m + r] = v;
+      }
+    }
+    Tp[z * tstride + i] = L.Ts[i / 32][i % 32];
+    if (i < nb) {
+      taus_g[z * 2 * k + c0 + i] = L.Ts[i][i];
+      taus_g[z * 2 * k + k + c0 + i] = L.sgn[i];
+    }
+    return;
+  }
+  float q[32];
+  lds_explicit_q_row(P, nb, L, q);
+  if (mode == 1) {
+    if (i < mr) {
+      float* qb = Qb + z * aux_stride;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) qb[c * mp + row0 + i] = q[c];
+    }
+    // R_i: rows 32 * leaf .. +32 of the stack (zero below nb)
+    const int a = i / 32, c = i % 32;
+    Rs[z * kStack + (blockIdx.x * 32 + a) * 32 + c] = (a < nb && c < nb && a <= c) ? P[c * kLeaf + a] : 0.f;
+  } else {
+    if (i < mr) {
+      float* qt = Qt + z * kStack;
+#pragma unroll
+      for (int c = 0; c < 32; ++c) {
+        const float sg = c < nb ? L.sgn[c] : 1.f;     // beta_c = R_cc: flip so diag(R) >= 0
+        qt[static_cast<int64_t>(i) * 32 + c] = sg * q[c];
+      }
+    }
+  }
+}
+
+// Top block of the panel's Q (leaf 0's first nb rows times Q_top's first
+// block), its sign-chosen LU, and T = -U S L_1^{-T}; U and L_1 -> UL for the
+// tall part.
+__global__ __launch_bounds__(LT) void k_hr_lu(int64_t m, int64_t c0, int nb, const float* Qb, const float* Qt,
+                                              int64_t aux_stride, float* Tp, int64_t tstride, float* taus_g,
+                                              int64_t k, float* UL) {
+  __shared__ float B[32][33];
+  __shared__ float Xi[32][33];
+  __shared__ float sg[32];
+  const int i = threadIdx.x, r = i / 32, c = i % 32;
+  const int64_t z = blockIdx.x;
+  const int64_t mp = m - c0;
+  {
+    float t = 0.f;
+    if (r < nb && c < nb) {
+      const float* qb = Qb + z * aux_stride;
+      const float* qt = Qt + z * kStack;
+      for (int a = 0; a < nb; ++a) t += qb[a * mp + r] * qt[a * 32 + c];
+    }
+    B[r][c] = t;
+  }
+  __syncthreads();
+  for (int j = 0; j < nb; ++j) {
+    if (i == 0) {
+      const float s = B[j][j] >= 0.f ? -1.f : 1.f;
+      sg[j] = s;
+      B[j][j] -= s;
+    }
+    __syncthreads();
+    if (c == 0 && r > j && r < nb) B[r][j] /= B[j][j];
+    __syncthreads();
+    if (r > j && r < nb && c > j && c < nb) B[r][c] -= B[r][j] * B[j][c];
+    __syncthreads();
+  }
+  // Xi = L_1^{-1} (unit lower), one column per thread
+  if (i < 32) {
+    for (int rr = 0; rr < 32; ++rr) Xi[rr][i] = 0.f;
+    if (i < nb) {
+      Xi[i][i] = 1.f;
+      for (int rr = i + 1; rr < nb; ++rr) {
+        float t = 0.f;
+        for (int qq = i; qq < rr; ++qq) t += B[rr][qq] * Xi[qq][i];
+        Xi[rr][i] = -t;
+      }
+    }
+  }
+  __syncthreads();
+  // T[r][c] = -sum_q U[r][q] s_q Xi[c][q]
+  float t = 0.f;
+  if (r < nb && c < nb && r <= c) {
+    for (int qq = r; qq <= c; ++qq) t -= B[r][qq] * sg[qq] * Xi[c][qq];
+  }
+  Tp[z * tstride + i] = t;
+  if (i < nb) {
+    float d = 0.f;
+    for (int qq = i; qq <= i; ++qq) d -= B[i][qq] * sg[qq] * Xi[i][qq];
+    taus_g[z * 2 * k + c0 + i] = d;
+    taus_g[z * 2 * k + k + c0 + i] = sg[i];
+  }
+  UL[z * 1024 + i] = (r < nb && c < nb) ? B[r][c] : 0.f;      // U upper, L_1 strict lower
+}
+
+// Explicit V of a tall panel: rows above c0 are zero, the top nb rows are
+// L_1, every other row is (Q_i row . Q_top block) U^{-1}.
+__global__ __launch_bounds__(256) void k_hr_tall(int64_t m, int64_t c0, int nb, int64_t rl, const float* Qb,
+                                                 const float* Qt, int64_t aux_stride, const float* UL,
+                                                 float* Vp, int64_t vstride) {
+  __shared__ float U[32][33];          // U on and above the diagonal, L_1 below
+  __shared__ float Qs[2][32][33];
+  const int64_t z = blockIdx.y;
+  const int64_t g0 = blockIdx.x * 256ll;
+  const int64_t mp = m - c0;
+  for (int idx = threadIdx.x; idx < 1024; idx += 256) U[idx / 32][idx % 32] = UL[z * 1024 + idx];
+  const int64_t lo = g0 - c0 > 0 ? g0 - c0 : 0;
+  const int64_t leaf0 = lo / rl;
+  for (int idx = threadIdx.x; idx < 2048; idx += 256) {
+    const int s = idx / 1024, a = (idx % 1024) / 32, c = idx % 32;
+    const int64_t leaf = leaf0 + s;
+    float v = 0.f;
+    if (leaf * rl < mp) v = Qt[z * kStack + (leaf * 32 + a) * 32 + c];
+    Qs[s][a][c] = v;
+  }
+  __syncthreads();
+  const int64_t g = g0 + threadIdx.x;
+  if (g >= m) return;
+  float* V = Vp + z * vstride;
+  const int64_t r = g - c0;
+  float x[32];
+#pragma unroll
+  for (int c = 0; c < 32; ++c) x[c] = 0.f;
+  if (r >= 0 && r < nb) {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) x[c] = c < r ? U[r][c] : (c == r ? 1.f : 0.f);
+  } else if (r >= nb) {
+    const int s = static_cast<int>(r / rl - leaf0);
+    const float* qb = Qb + z * aux_stride;
+    float q[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c) q[c] = 0.f;
+    for (int a = 0; a < nb; ++a) {
+      const float qa = qb[a * mp + r];
+#pragma unroll
+      for (int c = 0; c < 32; ++c) q[c] += qa * Qs[s][a][c];
+    }
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      if (c < nb) {
+        float t = q[c];
+        for (int a = 0; a < c; ++a) t -= x[a] * U[a][c];
+        x[c] = t / U[c][c];
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 32; ++c) V[c * m + g] = x[c];
+}
+
 // Q[:, c0 .. c0+nb) <- columns of the identity (rows 0..m-1).
 __global__ __launch_bounds__(256) void k_eye_cols(float* A, int64_t m, int64_t ld, int64_t bstride,
                                                    int64_t c0, int nb) {
@@ -280,11 +613,22 @@ __global__ __launch_bounds__(256) void k_emit(const float* U, int64_t m, int64_t
 
 }  // namespace
 
+constexpr int kQrSplit = 16;     // split-K of the long products V^T A (K = rows below the panel)
+
 size_t householder_qr_work_floats(int64_t m, int64_t k, int batch) {
   const int64_t P = (k + 31) / 32;
-  // V panels (m x 32 each), T factors (32 x 32 each), W / W2 (32 x k), tau + signs (2k)
-  return static_cast<size_t>(batch) * (P * m * 32 + P * 32 * 32 + 2 * 32 * k + 2 * k + 64);
+  // V panels (m x 32 each), T factors (32 x 32 each), W / W2 (32 x k), tau + signs (2k),
+  // TSQR: leaf Q (m x 32), stacked R and Q_top (kStack each), LU (32 x 32); split-K partials
+  return static_cast<size_t>(batch) * (P * m * 32 + P * 32 * 32 + 2 * 32 * k + 2 * k + 64 + m * 32 +
+                                       2 * kStack + 1024 + static_cast<int64_t>(kQrSplit) * 32 * k);
 }
+
+namespace {
+int qr_ksplit(int64_t K) {
+  const int64_t s = K / 2048;
+  return static_cast<int>(s < 1 ? 1 : (s > kQrSplit ? kQrSplit : s));
+}
+}  // namespace
 
 hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t bstride, int batch,
                           float* work, hipStream_t s) {
@@ -295,12 +639,25 @@ hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t bs
   float* W = Tall + static_cast<size_t>(batch) * P * NB * NB;     // [batch][32][k]
   float* W2 = W + static_cast<size_t>(batch) * NB * k;            // [batch][32][k]
   float* taus = W2 + static_cast<size_t>(batch) * NB * k;         // [batch][2k]
+  float* Qb = taus + static_cast<size_t>(batch) * (2 * k + 64);    // [batch][m][32]
+  float* Rs = Qb + static_cast<size_t>(batch) * m * 32;           // [batch][kStack]
+  float* Qt = Rs + static_cast<size_t>(batch) * kStack;           // [batch][kStack]
+  float* UL = Qt + static_cast<size_t>(batch) * kStack;           // [batch][1024]
+  float* part = UL + static_cast<size_t>(batch) * 1024;           // [batch][kQrSplit][32][k]
+  static bool lds_attr = false;
+  if (!lds_attr) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_qr_block),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(32 * kLeaf * sizeof(float)));
+    if (e != hipSuccess) return e;
+    lds_attr = true;
+  }
   const int64_t vstride = P * m * NB, tstride = P * NB * NB;
   auto Vp = [&](int64_t p) { return Vall + p * m * NB; };
   auto Tp = [&](int64_t p) { return Tall + p * NB * NB; };
   auto gemm = [&](int64_t M, int64_t N, int64_t K, const float* Ab, GemmDim am, GemmDim ak, int64_t ab,
                   const float* Bb, GemmDim bk, GemmDim bn, int64_t bb, float* Cb, int64_t cm, int64_t cn,
-                  int64_t cb, float alpha, float beta) -> hipError_t {
+                  int64_t cb, float alpha, float beta, int ksplit = 1) -> hipError_t {
     if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
     GemmArgs g{};
     g.M = M; g.N = N; g.K = K;
@@ -308,6 +665,7 @@ hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t bs
     g.B = Bb; g.b_dtype = kF32; g.bk = bk; g.bn = bn; g.b_batch = bb;
     g.C = Cb; g.c_dtype = kF32; g.c_m = cm; g.c_n = cn; g.c_batch = cb;
     g.alpha = alpha; g.beta = beta;
+    if (ksplit > 1 && M <= NB && N <= k) { g.ksplit = ksplit; g.partial = part; }
     return launch_gemm(g, batch, s);
   };
   hipError_t e;
@@ -317,14 +675,35 @@ hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t bs
     const int nb = static_cast<int>(k - c0 < NB ? k - c0 : NB);
     {
       ProfScope ps("qr_panel", s);
-      k_hqr_panel<<<batch, QT, 0, s>>>(A, m, k, ld, bstride, c0, nb, Vp(p), vstride, Tp(p), tstride, taus);
+      const int64_t mp = m - c0;
+      const int64_t nl = (mp + kLeaf - 1) / kLeaf;
+      const size_t lds = 32 * kLeaf * sizeof(float);
+      if (nl <= 1) {
+        k_qr_block<<<dim3(1, batch), LT, lds, s>>>(A, m, ld, bstride, c0, nb, 0, 1, mp, Vp(p), vstride, Tp(p),
+                                                   tstride, taus, k, Qb, Rs, Qt, m * 32);
+      } else if (nl <= 32) {
+        const int64_t rl = (mp + nl - 1) / nl;
+        k_qr_block<<<dim3(static_cast<unsigned>(nl), batch), LT, lds, s>>>(
+            A, m, ld, bstride, c0, nb, 1, static_cast<int>(nl), rl, Vp(p), vstride, Tp(p), tstride, taus, k, Qb,
+            Rs, Qt, m * 32);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        k_qr_block<<<dim3(1, batch), LT, lds, s>>>(A, m, ld, bstride, c0, nb, 2, static_cast<int>(nl), rl,
+                                                   Vp(p), vstride, Tp(p), tstride, taus, k, Qb, Rs, Qt, m * 32);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        k_hr_lu<<<batch, LT, 0, s>>>(m, c0, nb, Qb, Qt, m * 32, Tp(p), tstride, taus, k, UL);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        k_hr_tall<<<dim3(static_cast<unsigned>((m + 255) / 256), batch), 256, 0, s>>>(
+            m, c0, nb, rl, Qb, Qt, m * 32, UL, Vp(p), vstride);
+      } else {
+        k_hqr_panel<<<batch, QT, 0, s>>>(A, m, k, ld, bstride, c0, nb, Vp(p), vstride, Tp(p), tstride, taus);
+      }
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t n2 = k - c0 - nb, mr = m - c0;
     if (n2 <= 0) continue;
     // W = V^T A2  (nb x n2, K = m - c0)
     if ((e = gemm(nb, n2, mr, Vp(p) + c0, plain(m), plain(1), vstride, A + (c0 + nb) * ld + c0, plain(1),
-                  plain(ld), bstride, W, k, 1, NB * k, 1.f, 0.f)) != hipSuccess) return e;
+                  plain(ld), bstride, W, k, 1, NB * k, 1.f, 0.f, qr_ksplit(mr))) != hipSuccess) return e;
     // W2 = T^T W
     if ((e = gemm(nb, n2, nb, Tp(p), plain(1), plain(NB), tstride, W, plain(k), plain(1), NB * k, W2, k,
                   1, NB * k, 1.f, 0.f)) != hipSuccess) return e;
@@ -340,7 +719,8 @@ hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t bs
     if (n2 > 0) {
       // Q[c0:, right] -= V (T (V^T Q[c0:, right]))
       if ((e = gemm(nb, n2, mr, Vp(p) + c0, plain(m), plain(1), vstride, A + (c0 + nb) * ld + c0,
-                    plain(1), plain(ld), bstride, W, k, 1, NB * k, 1.f, 0.f)) != hipSuccess) return e;
+                    plain(1), plain(ld), bstride, W, k, 1, NB * k, 1.f, 0.f, qr_ksplit(mr))) != hipSuccess)
+        return e;
       if ((e = gemm(nb, n2, nb, Tp(p), plain(NB), plain(1), tstride, W, plain(k), plain(1), NB * k, W2,
                     k, 1, NB * k, 1.f, 0.f)) != hipSuccess) return e;
       if ((e = gemm(mr, n2, nb, Vp(p) + c0, plain(1), plain(m), vstride, W2, plain(k), plain(1), NB * k,
