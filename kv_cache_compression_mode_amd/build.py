@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libjolt.so")
-SOURCES = ["gemm.hip", "eig.hip", "qr.hip", "codec.hip", "host.hip"]
+SOURCES = ["gemm.hip", "eig.hip", "qr.hip", "tridiag.hip", "codec.hip", "host.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

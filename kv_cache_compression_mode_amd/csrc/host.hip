@@ -405,6 +405,7 @@ struct AllocWS {
   // scratch (chunk tensors)
   float* G; float* V; float* J; int* active; int* rot; float* tauabs; double* offp;
   float* GDpart;
+  void* syev;
   float* GD; float* GDc; float* VD;
   int* order; float* Ucm; float* Vr; float* P; double* lam_tmp; float* qtau; int* perm; float* sgn;
   float* Om; float* Y; float* Z; float* Bm; float* Wr; float* Wd;
@@ -451,6 +452,7 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base) {
              static_cast<size_t>(d.ell_pad) * d.ell_pad * 12;
   per += static_cast<size_t>(std::max(d.T, d.HD)) * std::max<int64_t>(d.R, 1) * 8 + (1 << 20);
   per += static_cast<size_t>(gram_d_ksplit(d)) * d.D * d.D * 4;
+  if (!d.flash && d.R > 0) per += syev_top_work_bytes(d.n_pad, static_cast<int>(d.R), 1);
   int chunk = static_cast<int>(std::max<size_t>(1, std::min<size_t>(64, (4ull << 30) / per)));
   chunk = std::min(chunk, nt);
   w.chunk = chunk;
@@ -473,6 +475,9 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base) {
   w.tauabs = c.take<float>(chunk);
   w.offp = c.take<double>(static_cast<size_t>(chunk) * kOffBlocks * 2);
   w.GDpart = c.take<float>(static_cast<size_t>(chunk) * gram_d_ksplit(d) * d.D * d.D);
+  w.syev = (!d.flash && d.R > 0)
+               ? static_cast<void*>(c.take<char>(syev_top_work_bytes(d.n_pad, static_cast<int>(d.R), chunk)))
+               : nullptr;
   w.GD = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
   w.GDc = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
   w.VD = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
@@ -508,6 +513,16 @@ GemmArgs gemm0() {
 
 // Jacobi to convergence on `batch` n x n matrices in w.G (V -> w.V); host loop
 // over sweeps, stopping when a sweep applies no rotation.
+// The token Gram's eigensolver: two-stage tridiagonal reduction by default,
+// block Jacobi with JOLT_EIG=jacobi.
+bool eig_jacobi() {
+  static const bool on = [] {
+    const char* e = std::getenv("JOLT_EIG");
+    return e && std::strcmp(e, "jacobi") == 0;
+  }();
+  return on;
+}
+
 bool trace_on() {
   static const bool on = [] {
     const char* e = std::getenv("JOLT_TRACE");
@@ -635,20 +650,36 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   }
   feature_factor(d, batch, t0, w, s);
   if (R == 0) return;
-  run_jacobi(w.G, w.V, n, batch, w, s);
-  ck(topk_diag(w.G, n, batch, static_cast<int>(R), w.order, s));
-  if (d.dual) {
-    // V_R (HD x R, column-major), then U' = X_(T) V_R (T x R, column-major)
-    ck(launch_gather_cols(w.V, n, n * n, w.order, R, w.Vr, HD, HD * R, HD, R, batch, s));
+  // leading eigenvectors V_R of the token Gram, column-major with leading dimension ldv
+  const float* VR;
+  int64_t ldv, vr_batch;
+  bool in_ucm = false;
+  if (eig_jacobi()) {
+    run_jacobi(w.G, w.V, n, batch, w, s);
+    ck(topk_diag(w.G, n, batch, static_cast<int>(R), w.order, s));
+    if (d.dual) {     // n == HD
+      ck(launch_gather_cols(w.V, n, n * n, w.order, R, w.Vr, HD, HD * R, HD, R, batch, s));
+    } else {
+      ck(launch_gather_cols(w.V, n, n * n, w.order, R, w.Ucm, T, T * R, T, R, batch, s));
+      in_ucm = true;
+    }
+    VR = w.Vr; ldv = HD; vr_batch = HD * R;
+  } else {
+    ck(syev_top(w.G, n, batch, static_cast<int>(R), w.V, nullptr, w.syev, s));
+    VR = w.V; ldv = n; vr_batch = n * n;
+  }
+  if (in_ucm) {
+  } else if (d.dual) {
+    // U' = X_(T) V_R (T x R, column-major)
     GemmArgs gu = gemm0();
     gu.a_ptrs = xp; gu.a_dtype = xdt;
     gu.M = T; gu.N = R; gu.K = HD;
     gu.am = plain(D); gu.ak = segmented(D, T * D, 1);
-    gu.B = w.Vr; gu.bk = plain(1); gu.bn = plain(HD); gu.b_batch = HD * R;
+    gu.B = VR; gu.bk = plain(1); gu.bn = plain(ldv); gu.b_batch = vr_batch;
     gu.C = w.Ucm; gu.c_m = 1; gu.c_n = T; gu.c_batch = T * R;
     ck(launch_gemm(gu, batch, s));
   } else {
-    ck(launch_gather_cols(w.V, n, n * n, w.order, R, w.Ucm, T, T * R, T, R, batch, s));
+    ck(copy_cols(VR, ldv, vr_batch, w.Ucm, T, T * R, T, R, batch, s));
   }
   ck(householder_qr(w.Ucm, T, R, T, T * R, batch, w.qtau, s));
   token_finalize(d, batch, t0, w, xdt, s);

@@ -90,6 +90,25 @@ hipError_t topk_diag(const float* A, int64_t n, int batch, int R, int* idx, hipS
 // In place: on return the panel holds the explicit orthonormal Q (m x k, m >= k)
 // with diag(R) >= 0.  work: householder_qr_work_floats(m, k, batch) floats.
 size_t householder_qr_work_floats(int64_t m, int64_t k, int batch);
+// Householder factorization of the panel columns [c0, c0 + nb) (nb <= 32) of
+// column-major m x k matrices (rows c0 .. m-1): explicit unit-lower V
+// (m x 32, zero above row c0) -> Vp, compact-WY T (32 x 32 row-major) -> Tp,
+// tau / sign(beta_j) -> taus[j] / taus[k + j] (per matrix 2k floats).  The
+// panel's own columns in A are left as they were (the R factor is not
+// written).  scratch: panel_factor_scratch_floats(m, batch) floats.
+size_t panel_factor_scratch_floats(int64_t m, int batch);
+// Top R eigenpairs of `batch` symmetric n x n matrices A (row-major = column-
+// major; n a multiple of 32; A is destroyed) by two-stage tridiagonal
+// reduction: Z [batch][n][n] receives the eigenvectors as the first R
+// columns (column-major, ld n), eigenvalue-descending; lam (optional, fp64
+// [batch][R]) the eigenvalues.  work: syev_top_work_bytes(n, R, batch).
+size_t syev_top_work_bytes(int64_t n, int R, int batch);
+hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam, void* work, hipStream_t s);
+hipError_t copy_cols(const float* in, int64_t ld_in, int64_t in_batch, float* out, int64_t ld_out,
+                     int64_t out_batch, int64_t rows, int64_t cols, int batch, hipStream_t s);
+hipError_t panel_factor(float* A, int64_t m, int64_t ld, int64_t bstride, int64_t c0, int nb, int batch,
+                        float* Vp, int64_t vstride, float* Tp, int64_t tstride, float* taus, int64_t k,
+                        float* scratch, hipStream_t s);
 hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t batch_stride, int batch,
                           float* work, hipStream_t s);
 

@@ -630,6 +630,52 @@ int qr_ksplit(int64_t K) {
 }
 }  // namespace
 
+size_t panel_factor_scratch_floats(int64_t m, int batch) {
+  return static_cast<size_t>(batch) * (m * 32 + 2 * kStack + 1024);
+}
+
+hipError_t panel_factor(float* A, int64_t m, int64_t ld, int64_t bstride, int64_t c0, int nb, int batch,
+                        float* Vp, int64_t vstride, float* Tp, int64_t tstride, float* taus, int64_t k,
+                        float* scratch, hipStream_t s) {
+  static bool lds_attr = false;
+  if (!lds_attr) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_qr_block),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(32 * kLeaf * sizeof(float)));
+    if (e != hipSuccess) return e;
+    lds_attr = true;
+  }
+  float* Qb = scratch;                                            // [batch][m][32]
+  float* Rs = Qb + static_cast<size_t>(batch) * m * 32;           // [batch][kStack]
+  float* Qt = Rs + static_cast<size_t>(batch) * kStack;           // [batch][kStack]
+  float* UL = Qt + static_cast<size_t>(batch) * kStack;           // [batch][1024]
+  ProfScope ps("qr_panel", s);
+  const int64_t mp = m - c0;
+  const int64_t nl = (mp + kLeaf - 1) / kLeaf;
+  const size_t lds = 32 * kLeaf * sizeof(float);
+  hipError_t e;
+  if (nl <= 1) {
+    k_qr_block<<<dim3(1, batch), LT, lds, s>>>(A, m, ld, bstride, c0, nb, 0, 1, mp, Vp, vstride, Tp, tstride,
+                                               taus, k, Qb, Rs, Qt, m * 32);
+  } else if (nl <= 32) {
+    const int64_t rl = (mp + nl - 1) / nl;
+    k_qr_block<<<dim3(static_cast<unsigned>(nl), batch), LT, lds, s>>>(
+        A, m, ld, bstride, c0, nb, 1, static_cast<int>(nl), rl, Vp, vstride, Tp, tstride, taus, k, Qb, Rs, Qt,
+        m * 32);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_qr_block<<<dim3(1, batch), LT, lds, s>>>(A, m, ld, bstride, c0, nb, 2, static_cast<int>(nl), rl, Vp,
+                                               vstride, Tp, tstride, taus, k, Qb, Rs, Qt, m * 32);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_hr_lu<<<batch, LT, 0, s>>>(m, c0, nb, Qb, Qt, m * 32, Tp, tstride, taus, k, UL);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_hr_tall<<<dim3(static_cast<unsigned>((m + 255) / 256), batch), 256, 0, s>>>(m, c0, nb, rl, Qb, Qt, m * 32,
+                                                                                  UL, Vp, vstride);
+  } else {
+    k_hqr_panel<<<batch, QT, 0, s>>>(A, m, k, ld, bstride, c0, nb, Vp, vstride, Tp, tstride, taus);
+  }
+  return hipGetLastError();
+}
+
 hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t bstride, int batch,
                           float* work, hipStream_t s) {
   constexpr int NB = 32;
@@ -640,18 +686,7 @@ hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t bs
   float* W2 = W + static_cast<size_t>(batch) * NB * k;            // [batch][32][k]
   float* taus = W2 + static_cast<size_t>(batch) * NB * k;         // [batch][2k]
   float* Qb = taus + static_cast<size_t>(batch) * (2 * k + 64);    // [batch][m][32]
-  float* Rs = Qb + static_cast<size_t>(batch) * m * 32;           // [batch][kStack]
-  float* Qt = Rs + static_cast<size_t>(batch) * kStack;           // [batch][kStack]
-  float* UL = Qt + static_cast<size_t>(batch) * kStack;           // [batch][1024]
-  float* part = UL + static_cast<size_t>(batch) * 1024;           // [batch][kQrSplit][32][k]
-  static bool lds_attr = false;
-  if (!lds_attr) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_qr_block),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(32 * kLeaf * sizeof(float)));
-    if (e != hipSuccess) return e;
-    lds_attr = true;
-  }
+  float* part = Qb + panel_factor_scratch_floats(m, batch);       // [batch][kQrSplit][32][k]
   const int64_t vstride = P * m * NB, tstride = P * NB * NB;
   auto Vp = [&](int64_t p) { return Vall + p * m * NB; };
   auto Tp = [&](int64_t p) { return Tall + p * NB * NB; };
@@ -673,31 +708,9 @@ hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t bs
   for (int64_t p = 0; p < P; ++p) {
     const int64_t c0 = p * NB;
     const int nb = static_cast<int>(k - c0 < NB ? k - c0 : NB);
-    {
-      ProfScope ps("qr_panel", s);
-      const int64_t mp = m - c0;
-      const int64_t nl = (mp + kLeaf - 1) / kLeaf;
-      const size_t lds = 32 * kLeaf * sizeof(float);
-      if (nl <= 1) {
-        k_qr_block<<<dim3(1, batch), LT, lds, s>>>(A, m, ld, bstride, c0, nb, 0, 1, mp, Vp(p), vstride, Tp(p),
-                                                   tstride, taus, k, Qb, Rs, Qt, m * 32);
-      } else if (nl <= 32) {
-        const int64_t rl = (mp + nl - 1) / nl;
-        k_qr_block<<<dim3(static_cast<unsigned>(nl), batch), LT, lds, s>>>(
-            A, m, ld, bstride, c0, nb, 1, static_cast<int>(nl), rl, Vp(p), vstride, Tp(p), tstride, taus, k, Qb,
-            Rs, Qt, m * 32);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_qr_block<<<dim3(1, batch), LT, lds, s>>>(A, m, ld, bstride, c0, nb, 2, static_cast<int>(nl), rl,
-                                                   Vp(p), vstride, Tp(p), tstride, taus, k, Qb, Rs, Qt, m * 32);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_hr_lu<<<batch, LT, 0, s>>>(m, c0, nb, Qb, Qt, m * 32, Tp(p), tstride, taus, k, UL);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_hr_tall<<<dim3(static_cast<unsigned>((m + 255) / 256), batch), 256, 0, s>>>(
-            m, c0, nb, rl, Qb, Qt, m * 32, UL, Vp(p), vstride);
-      } else {
-        k_hqr_panel<<<batch, QT, 0, s>>>(A, m, k, ld, bstride, c0, nb, Vp(p), vstride, Tp(p), tstride, taus);
-      }
-    }
+    if ((e = panel_factor(A, m, ld, bstride, c0, nb, batch, Vp(p), vstride, Tp(p), tstride, taus, k, Qb, s)) !=
+        hipSuccess)
+      return e;
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t n2 = k - c0 - nb, mr = m - c0;
     if (n2 <= 0) continue;

@@ -1,0 +1,593 @@
+// Leading eigenpairs of a batch of symmetric n x n matrices (the token Gram)
+// by two-stage tridiagonal reduction:
+//
+//  1. dense -> band (half-bandwidth 32): per 32-column panel, a Householder
+//     QR of the panel below the band (the LDS / TSQR panel kernels) and the
+//     two-sided update A22 <- H^T A22 H as matrix-core products,
+//     H = I - V T V^T:  X = A22 V T,  W = X - V (T^T V^T X) / 2,
+//     A22 <- A22 - V W^T - W V^T;
+//  2. band -> tridiagonal by bulge chasing: sweep j annihilates column j
+//     below the subdiagonal with a reflector of length <= 32 and chases the
+//     bulge it creates down the band one 32-row block per step; sweeps are
+//     pipelined (sweep j step s runs at tick S j + s, one wave per sweep in
+//     flight, S >= 3 keeps the blocks of concurrent steps disjoint);
+//  3. the top R eigenvalues of the tridiagonal by bisection on Sturm counts
+//     and their eigenvectors by inverse iteration on T - lambda I = L D L^T,
+//     both in fp64;
+//  4. back-transformation: the chase reflectors in reverse order, one sweep
+//     at a time (the reflectors of one sweep touch disjoint rows), then the
+//     panel reflectors as matrix-core products.
+//
+// The factors the codec needs are the leading eigenvectors of the Gram
+// (JoLT abstract: Tucker factors from the leading singular vectors of the
+// mode unfoldings); every Householder step is the textbook one (beta =
+// -sign(alpha) ||x||, tau = (beta - alpha) / beta).
+#include "device.hpp"
+#include "kernels.hpp"
+
+#include <cfloat>
+#include <vector>
+
+namespace jolt {
+namespace {
+
+constexpr int SBW = 32;           // half-bandwidth after stage 1 (= panel width)
+constexpr int BWS = 2 * SBW;      // band storage width: the bulge stays within 2b - 1
+constexpr int RFS = SBW + 1;      // stored floats per chase reflector: v[0..31], tau
+constexpr int SW = 8;             // waves of the chase kernel (sweeps in flight)
+
+__host__ __device__ inline int64_t sweep_steps(int64_t n, int64_t j) {
+  return (n - 1 - j < 2) ? 0 : (n - 3 - j) / SBW + 1;
+}
+__host__ __device__ inline int64_t floor_sum(int64_t M) {       // sum_{m=0}^{M} floor(m / SBW)
+  if (M < 0) return 0;
+  const int64_t q = M / SBW, r = M % SBW;
+  return SBW * q * (q - 1) / 2 + q * (r + 1);
+}
+// index of the first reflector of sweep j (sweeps in order, steps in order)
+__host__ __device__ inline int64_t sweep_offset(int64_t n, int64_t j) {
+  if (j > n - 2) j = n - 2;
+  if (j <= 0) return 0;
+  return j + floor_sum(n - 3) - floor_sum(n - 3 - j);
+}
+
+// Band storage: Bw[i * BWS + k] = A[i][i - k], 0 <= k < BWS.
+__global__ __launch_bounds__(256) void k_band_init(const float* A, int64_t n, float* Bw) {
+  const int64_t z = blockIdx.y;
+  const float* a = A + z * n * n;
+  float* b = Bw + z * n * BWS;
+  for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < n * BWS; idx += 256ll * gridDim.x) {
+    const int64_t i = idx / BWS, k = idx % BWS;
+    b[idx] = (k <= SBW && i - k >= 0) ? a[(i - k) * n + i] : 0.f;   // column-major (row i, column i - k)
+  }
+}
+
+// n <= 32768, so every band offset fits in 32 bits
+__device__ __forceinline__ int bidx(int r, int c) { return r * BWS + (r - c); }
+
+// Stage 2: one workgroup of SW waves per matrix.
+__global__ __launch_bounds__(SW * 64) void k_chase(float* Bw_g, int64_t n, float* Rf_g, int64_t rf_stride,
+                                                  int S) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  float* Bw = Bw_g + blockIdx.x * n * BWS;
+  float* Rf = Rf_g + blockIdx.x * rf_stride;
+  const int64_t last = n - 3;                       // last sweep with work
+  const int64_t ticks = last >= 0 ? S * last + sweep_steps(n, last) : 0;
+  float xn = 0.f;                                   // the next step's column (lanes 0..31)
+  for (int64_t t = 0; t < ticks; ++t) {
+    int64_t j = -1, s = -1;
+    const int64_t q = t / S;
+    if (q >= wave) {
+      const int64_t jj = q - ((q - wave) % SW);     // latest sweep of this wave that has started
+      if (jj <= last) {
+        const int64_t ss = t - S * jj;
+        if (ss < sweep_steps(n, jj)) { j = jj; s = ss; }
+      }
+    }
+    if (j >= 0) {
+      const int nn = static_cast<int>(n), jj = static_cast<int>(j), ss = static_cast<int>(s);
+      int r0, c, L;
+      if (ss == 0) { r0 = jj + 1; c = jj; L = nn - 1 - jj < SBW ? nn - 1 - jj : SBW; }
+      else { r0 = jj + 1 + ss * SBW; c = r0 - SBW; L = nn - r0 < SBW ? nn - r0 : SBW; }
+      const int r1 = r0 + L;
+      const int hi = (r1 + SBW < nn) ? r1 + SBW : nn;
+      float x = 0.f;
+      if (ss == 0) x = (lane < L) ? Bw[bidx(r0 + lane, jj)] : 0.f;
+      else x = (lane < L) ? xn : 0.f;
+      // every block this step reads, loaded up front (the blocks are disjoint)
+      float ai[16], dv[16], bv[16];
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) {
+        const int i = h * 16 + ii;
+        ai[ii] = (ss > 0 && i < L) ? Bw[bidx(r0 + i, c + l32)] : 0.f;                  // block left of D
+        const int a = l32, bb = h * 16 + ii;
+        float d = 0.f;
+        if (a < L && bb < L) d = a >= bb ? Bw[bidx(r0 + a, r0 + bb)] : Bw[bidx(r0 + bb, r0 + a)];
+        dv[ii] = d;
+        const int row = r1 + l32;
+        bv[ii] = (row < hi && bb < L) ? Bw[bidx(row, r0 + bb)] : 0.f;                    // block below D
+      }
+      // reflector (I - tau v v^T) x = beta e_1
+      const float alpha = __shfl(x, 0);
+      const float sigma = wave_sum((lane >= 1 && lane < L) ? x * x : 0.f);
+      float tau = 0.f, beta = alpha, scale = 0.f;
+      if (sigma > 0.f) {
+        const float nrm = sqrtf(alpha * alpha + sigma);
+        beta = alpha >= 0.f ? -nrm : nrm;
+        tau = (beta - alpha) / beta;
+        scale = 1.f / (alpha - beta);
+      }
+      const float v = (lane == 0) ? 1.f : ((lane < L) ? x * scale : 0.f);   // lanes >= 32: 0
+      const int64_t ridx = sweep_offset(n, j) + s;
+      if (lane < SBW) Rf[ridx * RFS + lane] = v;
+      if (lane == 0) Rf[ridx * RFS + SBW] = tau;
+      float vv[16];
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) vv[ii] = __shfl(v, h * 16 + ii);
+      const float va = __shfl(v, l32);
+      if (tau != 0.f) {
+        // left block: rows r0.., columns c..r0-1 (for s == 0 only column j)
+        if (ss == 0) {
+          if (lane < L) Bw[bidx(r0 + lane, jj)] = lane == 0 ? beta : 0.f;
+        } else {
+          float y = 0.f;
+#pragma unroll
+          for (int ii = 0; ii < 16; ++ii) y += vv[ii] * ai[ii];
+          y += __shfl_xor(y, 32);
+#pragma unroll
+          for (int ii = 0; ii < 16; ++ii) {
+            const int i = h * 16 + ii;
+            if (i < L) {
+              const float nv = (l32 == 0) ? (i == 0 ? beta : 0.f) : ai[ii] - tau * vv[ii] * y;
+              Bw[bidx(r0 + i, c + l32)] = nv;
+            }
+          }
+        }
+        // D <- H D H = D - tau (v w^T + w v^T) + tau^2 (v^T w) v v^T, w = D v
+        float w = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) w += dv[ii] * vv[ii];
+        w += __shfl_xor(w, 32);                           // w_a, a = l32, in both halves
+        const float gam = wave_sum(lane < 32 ? va * w : 0.f);
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+          const int bb = h * 16 + ii;
+          const float wb = __shfl(w, bb);
+          if (l32 < L && bb < L && bb <= l32) {
+            const float nd = dv[ii] - tau * (va * wb + w * vv[ii]) + tau * tau * gam * va * vv[ii];
+            Bw[bidx(r0 + l32, r0 + bb)] = nd;
+          }
+        }
+        // block below D: rows r1.., columns r0..r1-1, from the right
+        float zr = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) zr += bv[ii] * vv[ii];
+        zr += __shfl_xor(zr, 32);
+        const int row = r1 + l32;
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+          const int bb = h * 16 + ii;
+          if (row < hi && bb < L) {
+            const float nb = bv[ii] - tau * zr * vv[ii];
+            Bw[bidx(row, r0 + bb)] = nb;
+            bv[ii] = nb;
+          }
+        }
+      }
+      // the next step's column: column r0 of the block below, rows r1 .. hi-1
+      xn = __shfl(bv[0], l32);                             // lanes with h == 0 hold column r0
+      if (!(lane < 32 && r1 + lane < hi)) xn = 0.f;
+    }
+    __syncthreads();
+  }
+}
+
+// d[i] = T[i][i], e[i] = T[i+1][i] (fp64), from the band after the chase.
+__global__ __launch_bounds__(256) void k_tri_out(const float* Bw, int64_t n, double* d, double* e) {
+  const int64_t z = blockIdx.y;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += 256ll * gridDim.x) {
+    d[z * n + i] = Bw[z * n * BWS + i * BWS];
+    e[z * n + i] = (i + 1 < n) ? Bw[z * n * BWS + (i + 1) * BWS + 1] : 0.0;
+  }
+}
+
+// Number of eigenvalues of the tridiagonal (d, e2 = e^2) below x (Sturm count).
+__device__ __forceinline__ int sturm_count(const double* d, const double* e2, int64_t n, double x,
+                                           double pivmin) {
+  int cnt = 0;
+  double q = d[0] - x;
+  if (fabs(q) < pivmin) q = -pivmin;
+  cnt += q < 0.0;
+  for (int64_t i = 1; i < n; ++i) {
+    q = (d[i] - x) - e2[i - 1] / q;
+    if (fabs(q) < pivmin) q = -pivmin;
+    cnt += q < 0.0;
+  }
+  return cnt;
+}
+
+// Top R eigenvalues, descending: lam[q] is the (n-1-q)-th smallest, by
+// bisection to fp64 resolution inside the Gershgorin interval.
+__global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double* e_g, int64_t n, int R,
+                                               double* lam) {
+  extern __shared__ double sh[];
+  double* d = sh;
+  double* e2 = sh + n;
+  __shared__ double gl_s, gu_s, piv_s;
+  const int64_t z = blockIdx.y;
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    d[i] = d_g[z * n + i];
+    const double ei = (i + 1 < n) ? e_g[z * n + i] : 0.0;
+    e2[i] = ei * ei;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double gl = INFINITY, gu = -INFINITY, emax = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+      const double el = i > 0 ? fabs(e_g[z * n + i - 1]) : 0.0;
+      const double er = i + 1 < n ? fabs(e_g[z * n + i]) : 0.0;
+      gl = fmin(gl, d[i] - el - er);
+      gu = fmax(gu, d[i] + el + er);
+      emax = fmax(emax, e2[i]);
+    }
+    const double span = fmax(fabs(gl), fabs(gu));
+    gl_s = gl - 2.0 * DBL_EPSILON * span - DBL_MIN;
+    gu_s = gu + 2.0 * DBL_EPSILON * span + DBL_MIN;
+    piv_s = DBL_MIN * fmax(1.0, emax);
+  }
+  __syncthreads();
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= R) return;
+  const int64_t k = n - 1 - q;                    // wanted: the k-th smallest (0-based)
+  double lo = gl_s, hi = gu_s;
+  for (int it = 0; it < 200; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    if (hi - lo <= 2.0 * DBL_EPSILON * fmax(fabs(lo), fabs(hi)) + piv_s) break;
+    if (sturm_count(d, e2, n, mid, piv_s) > k) hi = mid;
+    else lo = mid;
+  }
+  lam[z * R + q] = 0.5 * (lo + hi);
+}
+
+// Eigenvector of eigenvalue lam[q] by inverse iteration (three solves with
+// T - lam I = L D L^T from a fixed pseudo-random start), normalized, fp32
+// out as column q of Z (column-major, ld n).  Scratch dp / y: [i][q]
+// interleaved (coalesced across q).
+__global__ __launch_bounds__(256) void k_invit(const double* d_g, const double* e_g, int64_t n, int R,
+                                              const double* lam, double* dp_g, double* y_g, float* Z,
+                                              int64_t z_batch) {
+  const int64_t z = blockIdx.y;
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= R) return;
+  const double* d = d_g + z * n;
+  const double* e = e_g + z * n;
+  double* dp = dp_g + z * n * R;
+  double* y = y_g + z * n * R;
+  const double lm = lam[z * R + q];
+  double tnorm = 0.0;
+  for (int64_t i = 0; i < n; ++i) tnorm = fmax(tnorm, fabs(d[i]) + fabs(e[i]) + (i ? fabs(e[i - 1]) : 0.0));
+  const double tiny = fmax(tnorm, DBL_MIN) * DBL_EPSILON;
+  // L D L^T of T - lam I
+  double prev = d[0] - lm;
+  if (fabs(prev) < tiny) prev = tiny;
+  dp[q] = prev;
+  for (int64_t i = 1; i < n; ++i) {
+    double di = (d[i] - lm) - e[i - 1] * e[i - 1] / prev;
+    if (fabs(di) < tiny) di = tiny;
+    dp[i * R + q] = di;
+    prev = di;
+  }
+  // start: uniform in [0.5, 1.5) from a counter hash of (q, i)
+  for (int64_t i = 0; i < n; ++i) {
+    const uint64_t hsh = mix64(0x9E3779B97F4A7C15ull * static_cast<uint64_t>(q + 1) + static_cast<uint64_t>(i));
+    y[i * R + q] = 0.5 + static_cast<double>(hsh >> 11) * 0x1p-53;
+  }
+  for (int it = 0; it < 3; ++it) {
+    // forward: L u = y
+    double u = y[q];
+    for (int64_t i = 1; i < n; ++i) {
+      const double li = e[i - 1] / dp[(i - 1) * R + q];
+      u = y[i * R + q] - li * u;
+      y[i * R + q] = u;
+    }
+    // D L^T x = u  (backward), then normalize
+    double xs = y[(n - 1) * R + q] / dp[(n - 1) * R + q];
+    y[(n - 1) * R + q] = xs;
+    double mx = fabs(xs);
+    for (int64_t i = n - 2; i >= 0; --i) {
+      const double li = e[i] / dp[i * R + q];
+      xs = y[i * R + q] / dp[i * R + q] - li * xs;
+      y[i * R + q] = xs;
+      mx = fmax(mx, fabs(xs));
+    }
+    double s2 = 0.0;
+    const double inv = mx > 0.0 ? 1.0 / mx : 1.0;
+    for (int64_t i = 0; i < n; ++i) {
+      const double t = y[i * R + q] * inv;
+      y[i * R + q] = t;
+      s2 += t * t;
+    }
+    const double sc = 1.0 / sqrt(s2);
+    for (int64_t i = 0; i < n; ++i) y[i * R + q] *= sc;
+  }
+  float* zc = Z + z * z_batch + static_cast<int64_t>(q) * n;
+  for (int64_t i = 0; i < n; ++i) zc[i] = static_cast<float>(y[i * R + q]);
+}
+
+// Stage 2 back-transformation of a tile of CT eigenvector columns held in
+// LDS: sweeps in reverse order; the reflectors of one sweep act on disjoint
+// 32-row blocks and run in parallel, one (reflector, column) per thread.
+__global__ __launch_bounds__(1024) void k_chase_back(float* Z, int64_t n, int R, int64_t z_batch, int CT,
+                                                    const float* Rf_g, int64_t rf_stride) {
+  extern __shared__ float Zt[];                   // [CT][n]
+  const int64_t z = blockIdx.y;
+  const int c0 = blockIdx.x * CT;
+  const int nc = (R - c0 < CT) ? R - c0 : CT;
+  float* zb = Z + z * z_batch;
+  const float* Rf = Rf_g + z * rf_stride;
+  for (int64_t idx = threadIdx.x; idx < static_cast<int64_t>(CT) * n; idx += 1024) {
+    const int cc = static_cast<int>(idx / n);
+    const int64_t i = idx % n;
+    Zt[idx] = cc < nc ? zb[static_cast<int64_t>(c0 + cc) * n + i] : 0.f;
+  }
+  __syncthreads();
+  for (int64_t j = n - 3; j >= 0; --j) {
+    const int64_t K = sweep_steps(n, j);
+    const int64_t base = sweep_offset(n, j);
+    const int64_t pairs = K * CT;
+    for (int64_t p = threadIdx.x; p < pairs; p += 1024) {
+      const int64_t s = p / CT;
+      const int cc = static_cast<int>(p % CT);
+      int64_t r0;
+      int L;
+      if (s == 0) { r0 = j + 1; L = static_cast<int>(n - 1 - j < SBW ? n - 1 - j : SBW); }
+      else { r0 = j + 1 + s * SBW; L = static_cast<int>(n - r0 < SBW ? n - r0 : SBW); }
+      const float* rf = Rf + (base + s) * RFS;
+      const float tau = rf[SBW];
+      if (tau == 0.f || cc >= nc) continue;
+      float* col = Zt + static_cast<int64_t>(cc) * n + r0;
+      float yv = 0.f;
+      for (int i = 0; i < L; ++i) yv += rf[i] * col[i];
+      yv *= tau;
+      for (int i = 0; i < L; ++i) col[i] -= rf[i] * yv;
+    }
+    __syncthreads();
+  }
+  for (int64_t idx = threadIdx.x; idx < static_cast<int64_t>(nc) * n; idx += 1024) {
+    const int cc = static_cast<int>(idx / n);
+    const int64_t i = idx % n;
+    zb[static_cast<int64_t>(c0 + cc) * n + i] = Zt[idx];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_copy_cols(const float* in, int64_t ld_in, int64_t in_batch, float* out,
+                                                  int64_t ld_out, int64_t out_batch, int64_t rows, int64_t cols) {
+  const int64_t z = blockIdx.y;
+  for (int64_t idx = blockIdx.x * 256ll + threadIdx.x; idx < rows * cols; idx += 256ll * gridDim.x) {
+    const int64_t c = idx / rows, r = idx % rows;
+    out[z * out_batch + c * ld_out + r] = in[z * in_batch + c * ld_in + r];
+  }
+}
+
+struct SyevLayout {
+  int64_t P, vtot, nref;
+  size_t v_off, t_off, tau_off, y_off, x_off, s1_off, s2_off, s3_off, wb_off, wb2_off, part_off, pscr_off,
+      bw_off, rf_off, d_off, e_off, lam_off, dp_off, yv_off, total;
+};
+
+SyevLayout syev_layout(int64_t n, int R, int batch) {
+  SyevLayout L{};
+  L.P = n / SBW - 1;
+  L.vtot = 0;
+  for (int64_t p = 0; p < L.P; ++p) L.vtot += (n - (p + 1) * SBW) * SBW;
+  L.nref = sweep_offset(n, n - 2);
+  const size_t B = static_cast<size_t>(batch);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  };
+  const int64_t Rm = R > SBW ? R : SBW;
+  L.v_off = take(B * L.vtot * 4);
+  L.t_off = take(B * (L.P > 0 ? L.P : 1) * 1024 * 4);
+  L.tau_off = take(B * 2 * SBW * 4);
+  L.y_off = take(B * n * SBW * 4);
+  L.x_off = take(B * n * SBW * 4);
+  L.s1_off = take(B * 1024 * 4);
+  L.s2_off = take(B * 1024 * 4);
+  L.s3_off = take(B * 1024 * 4);
+  L.wb_off = take(B * SBW * Rm * 4);
+  L.wb2_off = take(B * SBW * Rm * 4);
+  L.part_off = take(B * 16 * SBW * Rm * 4);
+  L.pscr_off = take(panel_factor_scratch_floats(n, batch) * 4);
+  L.bw_off = take(B * n * BWS * 4);
+  L.rf_off = take(B * (L.nref > 0 ? L.nref : 1) * RFS * 4);
+  L.d_off = take(B * n * 8);
+  L.e_off = take(B * n * 8);
+  L.lam_off = take(B * R * 8);
+  L.dp_off = take(B * n * R * 8);
+  L.yv_off = take(B * n * R * 8);
+  L.total = off;
+  return L;
+}
+
+int ksplit_for(int64_t K) {
+  const int64_t s = K / 2048;
+  return static_cast<int>(s < 1 ? 1 : (s > 16 ? 16 : s));
+}
+
+}  // namespace
+
+size_t syev_top_work_bytes(int64_t n, int R, int batch) { return syev_layout(n, R, batch).total; }
+
+hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam_out, void* work,
+                    hipStream_t s) {
+  if (n % SBW != 0 || R < 1 || R > n) return hipErrorInvalidValue;
+  const SyevLayout Lw = syev_layout(n, R, batch);
+  char* wb = static_cast<char*>(work);
+  float* Vst = reinterpret_cast<float*>(wb + Lw.v_off);
+  float* Tst = reinterpret_cast<float*>(wb + Lw.t_off);
+  float* taus = reinterpret_cast<float*>(wb + Lw.tau_off);
+  float* Yb = reinterpret_cast<float*>(wb + Lw.y_off);
+  float* Xb = reinterpret_cast<float*>(wb + Lw.x_off);
+  float* S1 = reinterpret_cast<float*>(wb + Lw.s1_off);
+  float* S2 = reinterpret_cast<float*>(wb + Lw.s2_off);
+  float* Wb = reinterpret_cast<float*>(wb + Lw.wb_off);
+  float* Wb2 = reinterpret_cast<float*>(wb + Lw.wb2_off);
+  float* part = reinterpret_cast<float*>(wb + Lw.part_off);
+  float* pscr = reinterpret_cast<float*>(wb + Lw.pscr_off);
+  float* Bw = reinterpret_cast<float*>(wb + Lw.bw_off);
+  float* Rf = reinterpret_cast<float*>(wb + Lw.rf_off);
+  double* dd = reinterpret_cast<double*>(wb + Lw.d_off);
+  double* ee = reinterpret_cast<double*>(wb + Lw.e_off);
+  double* lam = reinterpret_cast<double*>(wb + Lw.lam_off);
+  double* dp = reinterpret_cast<double*>(wb + Lw.dp_off);
+  double* yv = reinterpret_cast<double*>(wb + Lw.yv_off);
+  const int64_t nn = n * n;
+  hipError_t e;
+  auto gemm = [&](int64_t M, int64_t N, int64_t K, const float* Ab, GemmDim am, GemmDim ak, int64_t ab,
+                  const float* Bb, GemmDim bk, GemmDim bn, int64_t bb, float* Cb, int64_t cm, int64_t cn,
+                  int64_t cb, float alpha, float beta, int ksplit = 1) -> hipError_t {
+    if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = Ab; g.a_dtype = kF32; g.am = am; g.ak = ak; g.a_batch = ab;
+    g.B = Bb; g.b_dtype = kF32; g.bk = bk; g.bn = bn; g.b_batch = bb;
+    g.C = Cb; g.c_dtype = kF32; g.c_m = cm; g.c_n = cn; g.c_batch = cb;
+    g.alpha = alpha; g.beta = beta;
+    if (ksplit > 1) { g.ksplit = ksplit; g.partial = part; }
+    return launch_gemm(g, batch, s);
+  };
+  // ---- stage 1: dense -> band
+  std::vector<int64_t> voff(Lw.P > 0 ? Lw.P : 1);
+  {
+    int64_t o = 0;
+    for (int64_t p = 0; p < Lw.P; ++p) { voff[p] = o; o += (n - (p + 1) * SBW) * SBW; }
+  }
+  for (int64_t p = 0; p < Lw.P; ++p) {
+    const int64_t c = p * SBW, r = c + SBW, mp = n - r;
+    float* panel = A + c * n + r;                  // column-major mp x 32 (ld n)
+    float* V = Vst + voff[p];
+    float* T = Tst + p * 1024;
+    const int64_t vs = Lw.vtot, ts = Lw.P * 1024;
+    if ((e = panel_factor(panel, mp, n, nn, 0, SBW, batch, V, vs, T, ts, taus, SBW, pscr, s)) != hipSuccess)
+      return e;
+    // R = top rows of H^T panel: panel_top -= V_top (T^T (V^T panel))
+    if ((e = gemm(SBW, SBW, mp, V, plain(mp), plain(1), vs, panel, plain(1), plain(n), nn, S1, SBW, 1, 1024, 1.f,
+                  0.f, ksplit_for(mp))) != hipSuccess) return e;
+    if ((e = gemm(SBW, SBW, SBW, T, plain(1), plain(SBW), ts, S1, plain(SBW), plain(1), 1024, S2, SBW, 1, 1024,
+                  1.f, 0.f)) != hipSuccess) return e;
+    if ((e = gemm(SBW, SBW, SBW, V, plain(1), plain(mp), vs, S2, plain(SBW), plain(1), 1024, panel, 1, n, nn,
+                  -1.f, 1.f)) != hipSuccess) return e;
+    float* A22 = A + r * n + r;
+    // X = A22 V T
+    if ((e = gemm(mp, SBW, mp, A22, plain(1), plain(n), nn, V, plain(1), plain(mp), vs, Yb, 1, mp, n * SBW, 1.f,
+                  0.f)) != hipSuccess) return e;
+    if ((e = gemm(mp, SBW, SBW, Yb, plain(1), plain(mp), n * SBW, T, plain(SBW), plain(1), ts, Xb, 1, mp,
+                  n * SBW, 1.f, 0.f)) != hipSuccess) return e;
+    // W = X - V (T^T (V^T X)) / 2, in place in X
+    if ((e = gemm(SBW, SBW, mp, V, plain(mp), plain(1), vs, Xb, plain(1), plain(mp), n * SBW, S1, SBW, 1, 1024,
+                  1.f, 0.f, ksplit_for(mp))) != hipSuccess) return e;
+    if ((e = gemm(SBW, SBW, SBW, T, plain(1), plain(SBW), ts, S1, plain(SBW), plain(1), 1024, S2, SBW, 1, 1024,
+                  1.f, 0.f)) != hipSuccess) return e;
+    if ((e = gemm(mp, SBW, SBW, V, plain(1), plain(mp), vs, S2, plain(SBW), plain(1), 1024, Xb, 1, mp, n * SBW,
+                  -0.5f, 1.f)) != hipSuccess) return e;
+    // A22 -= V W^T + W V^T
+    if ((e = gemm(mp, mp, SBW, V, plain(1), plain(mp), vs, Xb, plain(mp), plain(1), n * SBW, A22, 1, n, nn,
+                  -1.f, 1.f)) != hipSuccess) return e;
+    if ((e = gemm(mp, mp, SBW, Xb, plain(1), plain(mp), n * SBW, V, plain(mp), plain(1), vs, A22, 1, n, nn,
+                  -1.f, 1.f)) != hipSuccess) return e;
+  }
+  // ---- stage 2: band -> tridiagonal
+  {
+    int64_t blocks = (n * BWS + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    k_band_init<<<dim3(static_cast<unsigned>(blocks), batch), 256, 0, s>>>(A, n, Bw);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t K0 = sweep_steps(n, 0);
+    int S = static_cast<int>((K0 + SW - 1) / SW);
+    if (S < 3) S = 3;
+    {
+      ProfScope ps("chase", s);
+      k_chase<<<batch, SW * 64, 0, s>>>(Bw, n, Rf, Lw.nref * RFS, S);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    int64_t tb = (n + 255) / 256;
+    k_tri_out<<<dim3(static_cast<unsigned>(tb), batch), 256, 0, s>>>(Bw, n, dd, ee);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // ---- stage 3: top R eigenpairs of the tridiagonal (fp64)
+  {
+    const size_t lds = static_cast<size_t>(2 * n) * sizeof(double);
+    static bool attr = false;
+    if (!attr) {
+      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bisect),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, 65536)) != hipSuccess)
+        return e;
+      attr = true;
+    }
+    if (lds > 65536) return hipErrorInvalidValue;
+    const unsigned gx = static_cast<unsigned>((R + 255) / 256);
+    {
+      ProfScope ps("tri_eig", s);
+      k_bisect<<<dim3(gx, batch), 256, lds, s>>>(dd, ee, n, R, lam);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      k_invit<<<dim3(gx, batch), 256, 0, s>>>(dd, ee, n, R, lam, dp, yv, Z, n * n);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (lam_out) {
+      if ((e = hipMemcpyAsync(lam_out, lam, sizeof(double) * batch * R, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return e;
+    }
+  }
+  // ---- stage 4: back-transformation (chase reflectors, then panel reflectors)
+  {
+    int CT = static_cast<int>(32768 / n);
+    if (CT > 32) CT = 32;
+    if (CT < 1) return hipErrorInvalidValue;
+    const size_t lds = static_cast<size_t>(CT) * n * sizeof(float);
+    static bool attr = false;
+    if (!attr) {
+      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chase_back),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, 131072)) != hipSuccess)
+        return e;
+      attr = true;
+    }
+    if (lds > 131072) return hipErrorInvalidValue;
+    {
+      ProfScope ps("chase_back", s);
+      k_chase_back<<<dim3(static_cast<unsigned>((R + CT - 1) / CT), batch), 1024, lds, s>>>(
+          Z, n, R, n * n, CT, Rf, Lw.nref * RFS);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    for (int64_t p = Lw.P - 1; p >= 0; --p) {
+      const int64_t r = (p + 1) * SBW, mp = n - r;
+      const float* V = Vst + voff[p];
+      const float* T = Tst + p * 1024;
+      const int64_t vs = Lw.vtot, ts = Lw.P * 1024;
+      float* Zr = Z + r;
+      // Zr -= V (T (V^T Zr))
+      if ((e = gemm(SBW, R, mp, V, plain(mp), plain(1), vs, Zr, plain(1), plain(n), nn, Wb, R, 1, SBW * R, 1.f,
+                    0.f, ksplit_for(mp))) != hipSuccess) return e;
+      if ((e = gemm(SBW, R, SBW, T, plain(SBW), plain(1), ts, Wb, plain(R), plain(1), SBW * R, Wb2, R, 1,
+                    SBW * R, 1.f, 0.f)) != hipSuccess) return e;
+      if ((e = gemm(mp, R, SBW, V, plain(1), plain(mp), vs, Wb2, plain(R), plain(1), SBW * R, Zr, 1, n, nn, -1.f,
+                    1.f)) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+hipError_t copy_cols(const float* in, int64_t ld_in, int64_t in_batch, float* out, int64_t ld_out,
+                     int64_t out_batch, int64_t rows, int64_t cols, int batch, hipStream_t s) {
+  int64_t blocks = (rows * cols + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  k_copy_cols<<<dim3(static_cast<unsigned>(blocks), batch), 256, 0, s>>>(in, ld_in, in_batch, out, ld_out,
+                                                                       out_batch, rows, cols);
+  return hipGetLastError();
+}
+
+}  // namespace jolt
