@@ -266,8 +266,8 @@ COMPARE_EXACT = {"mistral7b_t1024_flash"}
 CPU_SAMPLE = {"mistral7b_t4096_2x": 24, "mistral7b_t1024_flash": 64, "llama13b_t4096_2x": 2,
               "mistral7b_t32768_3x": 4}
 
-KERNELS = ("jacobi_update", "jacobi_solve", "jacobi128", "qr_panel", "gemm", "encode_residual",
-           "decode_w", "decode")
+KERNELS = ("jacobi_update", "jacobi_solve", "jacobi128", "qr_panel", "gemm", "band", "chase", "tri_eig",
+           "chase_back", "band_back", "encode_residual", "decode_w", "decode")
 RIDGE_FP32 = MFMA_FP32_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)   # flop/B
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_jac_update_mistral7b_t4096_2x.json")
 JACOBI_SOURCES = tuple(os.path.join(ROOT, "kv_cache_compression_mode_amd", "csrc", f)

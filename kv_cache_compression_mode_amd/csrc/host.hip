@@ -453,7 +453,9 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base) {
   per += static_cast<size_t>(std::max(d.T, d.HD)) * std::max<int64_t>(d.R, 1) * 8 + (1 << 20);
   per += static_cast<size_t>(gram_d_ksplit(d)) * d.D * d.D * 4;
   if (!d.flash && d.R > 0) per += syev_top_work_bytes(d.n_pad, static_cast<int>(d.R), 1);
-  int chunk = static_cast<int>(std::max<size_t>(1, std::min<size_t>(64, (4ull << 30) / per)));
+  // up to 64 tensors (24 GiB of scratch) per chunk: the eigensolver's chase
+  // runs one workgroup per tensor, so wide chunks keep more of the chip busy
+  int chunk = static_cast<int>(std::max<size_t>(1, std::min<size_t>(64, (24ull << 30) / per)));
   chunk = std::min(chunk, nt);
   w.chunk = chunk;
   Carver c;

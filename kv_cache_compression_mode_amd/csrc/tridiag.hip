@@ -317,11 +317,16 @@ __global__ __launch_bounds__(256) void k_invit(const double* d_g, const double* 
 }
 
 // Stage 2 back-transformation of a tile of CT eigenvector columns held in
-// LDS: sweeps in reverse order; the reflectors of one sweep act on disjoint
-// 32-row blocks and run in parallel, one (reflector, column) per thread.
+// LDS (column stride n + 1, so the columns of one reflector's threads fall in
+// different banks): sweeps in reverse order; a sweep's reflectors are staged
+// in LDS, act on disjoint 32-row blocks and run in parallel, one (reflector,
+// column) per thread.
 __global__ __launch_bounds__(1024) void k_chase_back(float* Z, int64_t n, int R, int64_t z_batch, int CT,
                                                     const float* Rf_g, int64_t rf_stride) {
-  extern __shared__ float Zt[];                   // [CT][n]
+  extern __shared__ float sm[];
+  const int ldz = static_cast<int>(n) + 1;
+  float* Zt = sm;                                 // [CT][n + 1]
+  float* Rl = sm + static_cast<int64_t>(CT) * ldz;   // [steps][RFS]
   const int64_t z = blockIdx.y;
   const int c0 = blockIdx.x * CT;
   const int nc = (R - c0 < CT) ? R - c0 : CT;
@@ -329,36 +334,43 @@ __global__ __launch_bounds__(1024) void k_chase_back(float* Z, int64_t n, int R,
   const float* Rf = Rf_g + z * rf_stride;
   for (int64_t idx = threadIdx.x; idx < static_cast<int64_t>(CT) * n; idx += 1024) {
     const int cc = static_cast<int>(idx / n);
-    const int64_t i = idx % n;
-    Zt[idx] = cc < nc ? zb[static_cast<int64_t>(c0 + cc) * n + i] : 0.f;
+    const int i = static_cast<int>(idx % n);
+    Zt[cc * ldz + i] = cc < nc ? zb[static_cast<int64_t>(c0 + cc) * n + i] : 0.f;
   }
-  __syncthreads();
   for (int64_t j = n - 3; j >= 0; --j) {
-    const int64_t K = sweep_steps(n, j);
-    const int64_t base = sweep_offset(n, j);
-    const int64_t pairs = K * CT;
-    for (int64_t p = threadIdx.x; p < pairs; p += 1024) {
-      const int64_t s = p / CT;
-      const int cc = static_cast<int>(p % CT);
-      int64_t r0;
-      int L;
-      if (s == 0) { r0 = j + 1; L = static_cast<int>(n - 1 - j < SBW ? n - 1 - j : SBW); }
-      else { r0 = j + 1 + s * SBW; L = static_cast<int>(n - r0 < SBW ? n - r0 : SBW); }
-      const float* rf = Rf + (base + s) * RFS;
+    const int K = static_cast<int>(sweep_steps(n, j));
+    const float* rs = Rf + sweep_offset(n, j) * RFS;
+    __syncthreads();                              // previous sweep done with Rl
+    for (int idx = threadIdx.x; idx < K * RFS; idx += 1024) Rl[idx] = rs[idx];
+    __syncthreads();
+    for (int p = threadIdx.x; p < K * CT; p += 1024) {
+      const int s = p / CT, cc = p % CT;
+      const float* rf = Rl + s * RFS;
       const float tau = rf[SBW];
       if (tau == 0.f || cc >= nc) continue;
-      float* col = Zt + static_cast<int64_t>(cc) * n + r0;
-      float yv = 0.f;
-      for (int i = 0; i < L; ++i) yv += rf[i] * col[i];
-      yv *= tau;
-      for (int i = 0; i < L; ++i) col[i] -= rf[i] * yv;
+      const int r0 = (s == 0) ? static_cast<int>(j) + 1 : static_cast<int>(j) + 1 + s * SBW;
+      float* col = Zt + cc * ldz + r0;
+      if (r0 + SBW <= n) {                        // v is zero past its length
+        float yv = 0.f;
+#pragma unroll
+        for (int i = 0; i < SBW; ++i) yv += rf[i] * col[i];
+        yv *= tau;
+#pragma unroll
+        for (int i = 0; i < SBW; ++i) col[i] -= rf[i] * yv;
+      } else {
+        const int L = static_cast<int>(n) - r0;
+        float yv = 0.f;
+        for (int i = 0; i < L; ++i) yv += rf[i] * col[i];
+        yv *= tau;
+        for (int i = 0; i < L; ++i) col[i] -= rf[i] * yv;
+      }
     }
-    __syncthreads();
   }
+  __syncthreads();
   for (int64_t idx = threadIdx.x; idx < static_cast<int64_t>(nc) * n; idx += 1024) {
     const int cc = static_cast<int>(idx / n);
-    const int64_t i = idx % n;
-    zb[static_cast<int64_t>(c0 + cc) * n + i] = Zt[idx];
+    const int i = static_cast<int>(idx % n);
+    zb[static_cast<int64_t>(c0 + cc) * n + i] = Zt[cc * ldz + i];
   }
 }
 
@@ -467,6 +479,8 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     int64_t o = 0;
     for (int64_t p = 0; p < Lw.P; ++p) { voff[p] = o; o += (n - (p + 1) * SBW) * SBW; }
   }
+  {
+  ProfScope ps_band("band", s);
   for (int64_t p = 0; p < Lw.P; ++p) {
     const int64_t c = p * SBW, r = c + SBW, mp = n - r;
     float* panel = A + c * n + r;                  // column-major mp x 32 (ld n)
@@ -500,6 +514,7 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
                   -1.f, 1.f)) != hipSuccess) return e;
     if ((e = gemm(mp, mp, SBW, Xb, plain(1), plain(mp), n * SBW, V, plain(mp), plain(1), vs, A22, 1, n, nn,
                   -1.f, 1.f)) != hipSuccess) return e;
+  }
   }
   // ---- stage 2: band -> tridiagonal
   {
@@ -548,21 +563,24 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     int CT = static_cast<int>(32768 / n);
     if (CT > 32) CT = 32;
     if (CT < 1) return hipErrorInvalidValue;
-    const size_t lds = static_cast<size_t>(CT) * n * sizeof(float);
+    const size_t lds = (static_cast<size_t>(CT) * (n + 1) + static_cast<size_t>(sweep_steps(n, 0)) * RFS) *
+                       sizeof(float);
+    constexpr int kMaxLds = 160 * 1024;
     static bool attr = false;
     if (!attr) {
       if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chase_back),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, 131072)) != hipSuccess)
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds)) != hipSuccess)
         return e;
       attr = true;
     }
-    if (lds > 131072) return hipErrorInvalidValue;
+    if (lds > static_cast<size_t>(kMaxLds)) return hipErrorInvalidValue;
     {
       ProfScope ps("chase_back", s);
       k_chase_back<<<dim3(static_cast<unsigned>((R + CT - 1) / CT), batch), 1024, lds, s>>>(
           Z, n, R, n * n, CT, Rf, Lw.nref * RFS);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    ProfScope ps_bb("band_back", s);
     for (int64_t p = Lw.P - 1; p >= 0; --p) {
       const int64_t r = (p + 1) * SBW, mp = n - r;
       const float* V = Vst + voff[p];
