@@ -43,6 +43,7 @@ def parse():
                    help="run warmup + one step, then a plain copy of a known size (rocprofv3 runs)")
     p.add_argument("--copy-mib", type=int, default=1024,
                    help="size of the calibration copy in --profile-step mode")
+    p.add_argument("--traffic-kernel", default="gemm", help="kernel of the --record-traffic record")
     p.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="turn the counter_collection.csv files of two rocprofv3 --pmc runs of "
                         "--profile-step (FETCH_SIZE, then WRITE_SIZE) into the traffic record "
@@ -53,7 +54,7 @@ def parse():
 def main():
     args = parse()
     if args.record_traffic:
-        record_traffic(*args.record_traffic, args.copy_mib << 20)
+        record_traffic(*args.record_traffic, args.copy_mib << 20, args.traffic_kernel, args.config)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this codec benchmark runs on one GPU only: the path has no "
@@ -128,21 +129,21 @@ def main():
             step(method)
         torch.cuda.synchronize()
         evs = []
-        # per-launch HIP events on the launch stream, and device counters of
-        # the work the Jacobi update performed, over the timed region
+        # per-launch HIP events on the launch stream around the dominant
+        # kernel, with its algorithmic work, over the timed region
         if profile:
-            jolt.profile_enable("jacobi_update")
+            jolt.profile_enable(profile)
         t0 = time.perf_counter()
         for _ in range(K):
             step(method, evs)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        jac = None
+        dom = None
         if profile:
-            jac = jolt.profile_query("jacobi_update")
+            dom = jolt.profile_query(profile)
             jolt.profile_enable(None)
         ph = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(3)]
-        return wall * 1e3 / K, ph, jac
+        return wall * 1e3 / K, ph, dom
 
     def errors():
         """Relative Frobenius error of every tensor (outside the timed region)."""
@@ -164,7 +165,22 @@ def main():
         return np.array(errs).reshape(L, 2)
 
     K = 1 if args.profile_step else args.steps
-    ms_step, (ms_alloc, ms_enc, ms_dec), jac = run(cfg.method, K, not args.profile_step)
+    kstats = {}
+    dominant = None
+    if not args.profile_step:
+        # per-kernel breakdown from one step with every kernel bracketed by
+        # events (outside the timed region: the extra events cost time); the
+        # dominant kernel among those that account their algorithmic work is
+        # then timed inside the timed region
+        step(cfg.method)
+        jolt.profile_enable("*")
+        step(cfg.method)
+        torch.cuda.synchronize()
+        kstats = {name: jolt.profile_query(name) for name in KERNELS}
+        jolt.profile_enable(None)
+        cands = [k for k in ROOF if kstats[k]["launches"] and kstats[k]["bytes"] > 0]
+        dominant = max(cands, key=lambda k: kstats[k]["total_ms"]) if cands else None
+    ms_step, (ms_alloc, ms_enc, ms_dec), dom = run(cfg.method, K, dominant)
     if args.profile_step:
         # a plain copy of known size (read n bytes, write n bytes), against
         # which the FETCH_SIZE / WRITE_SIZE counters are scaled
@@ -176,14 +192,6 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"profile_step_ms": ms_step, "copy_bytes": n}), flush=True)
         return
-
-    # per-kernel breakdown from one more step with every kernel bracketed by
-    # events (outside the timed region: the extra events cost time)
-    jolt.profile_enable("*")
-    step(cfg.method)
-    torch.cuda.synchronize()
-    kstats = {name: jolt.profile_query(name) for name in KERNELS}
-    jolt.profile_enable(None)
 
     res, blobs, choices = state["res"], state["blobs"], state["choices"]
     blob_total = sum(b.numel() for b in blobs)
@@ -229,7 +237,7 @@ def main():
         "plan_bytes": int(res.total_bytes), "budget_bytes": int(res.budget_bytes),
         "rel_err_K_mean": round(float(errs[:, 0].mean()), 6),
         "rel_err_V_mean": round(float(errs[:, 1].mean()), 6),
-        "roofline": roofline_jacobi(jac) if jac and jac["launches"] else None,
+        "roofline": roofline_for(dominant, dom, cfg.name) if dom and dom["launches"] else None,
         "roofline_decode": {"kernel": dec_kernel,
                             "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                             "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
@@ -269,9 +277,24 @@ CPU_SAMPLE = {"mistral7b_t4096_2x": 24, "mistral7b_t1024_flash": 64, "llama13b_t
 KERNELS = ("jacobi_update", "jacobi_solve", "jacobi128", "qr_panel", "gemm", "band", "chase", "tri_eig",
            "chase_back", "band_back", "encode_residual", "decode_w", "decode")
 RIDGE_FP32 = MFMA_FP32_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)   # flop/B
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_jac_update_mistral7b_t4096_2x.json")
-JACOBI_SOURCES = tuple(os.path.join(ROOT, "kv_cache_compression_mode_amd", "csrc", f)
-                       for f in ("eig.hip", "device.hpp"))
+CSRC = os.path.join(ROOT, "kv_cache_compression_mode_amd", "csrc")
+# kernels whose launches account their algorithmic work (bytes, flops):
+# name -> (description, symbol in profiler traces, sources of the kernel)
+ROOF = {
+    "gemm": ("k_gemm: strided batched GEMM on fp32 matrix cores (all launches of the step: Grams, "
+             "band reduction, back-transformation, factor recovery, core products)",
+             "k_gemm", ("gemm.hip", "device.hpp")),
+    "jacobi_update": ("k_jac_update: block-Jacobi rotation of A and V, fp32 matrix cores",
+                      "k_jac_update", ("eig.hip", "device.hpp")),
+}
+
+
+def traffic_file(symbol, workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{symbol}_{workload}.json")
+
+
+def kernel_sources(name):
+    return tuple(os.path.join(CSRC, f) for f in ROOF[name][2])
 
 
 def sources_sha256(paths):
@@ -295,39 +318,41 @@ def measured_traffic(source_paths, record_path):
     return rec["traffic_bytes_per_launch"]
 
 
-def _pmc_means(path, counter):
-    """Mean counter value (KiB per dispatch) of the Jacobi update and of the
+def _pmc_means(path, counter, symbol):
+    """Mean counter value (KiB per dispatch) of one kernel and of the
     calibration copy (the last elementwise dispatch: the copies follow the
     fill that allocates their source)."""
     import csv
-    jac, copy = [], []
+    ker, copy = [], []
     with open(path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter:
                 continue
-            if "k_jac_update" in r["Kernel_Name"]:
-                jac.append(float(r["Counter_Value"]))
+            if symbol in r["Kernel_Name"]:
+                ker.append(float(r["Counter_Value"]))
             elif "elementwise" in r["Kernel_Name"]:
                 copy.append(float(r["Counter_Value"]))
-    if not jac or len(copy) < 2:
-        raise SystemExit(f"{path}: no k_jac_update or calibration-copy dispatches of {counter}")
-    return sum(jac) / len(jac), copy[-1], len(jac)
+    if not ker or len(copy) < 2:
+        raise SystemExit(f"{path}: no {symbol} or calibration-copy dispatches of {counter}")
+    return sum(ker) / len(ker), copy[-1], len(ker)
 
 
-def record_traffic(fetch_csv, write_csv, copy_bytes, record_path=None, source_paths=JACOBI_SOURCES):
-    jf, cf, n = _pmc_means(fetch_csv, "FETCH_SIZE")
-    jw, cw, _ = _pmc_means(write_csv, "WRITE_SIZE")
+def record_traffic(fetch_csv, write_csv, copy_bytes, name="gemm", workload="mistral7b_t4096_2x",
+                   record_path=None, source_paths=None):
+    symbol = ROOF[name][1]
+    source_paths = source_paths or kernel_sources(name)
+    jf, cf, n = _pmc_means(fetch_csv, "FETCH_SIZE", symbol)
+    jw, cw, _ = _pmc_means(write_csv, "WRITE_SIZE", symbol)
     kib = copy_bytes / 1024.0
     f_scale, w_scale = kib / cf, kib / cw      # known bytes / counted KiB of a plain copy
-    rec = {"kernel": "k_jac_update", "workload": "mistral7b_t4096_2x (one step, 64 tensors, n = 1024)",
-           "dispatches": n,
+    rec = {"kernel": symbol, "workload": f"{workload} (one step)", "dispatches": n,
            "fetch_kib_per_dispatch": round(jf, 3), "write_kib_per_dispatch": round(jw, 3),
            "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_scale": round(f_scale, 6), "write_scale": round(w_scale, 6),
            "traffic_bytes_per_launch": round((jf * f_scale + jw * w_scale) * 1024.0),
            "sources": [os.path.relpath(p, ROOT) for p in source_paths],
            "source_sha256": sources_sha256(source_paths)}
-    record_path = record_path or TRAFFIC_FILE
+    record_path = record_path or traffic_file(symbol, workload)
     os.makedirs(os.path.dirname(record_path), exist_ok=True)
     with open(record_path, "w") as f:
         json.dump(rec, f, indent=1)
@@ -335,10 +360,12 @@ def record_traffic(fetch_csv, write_csv, copy_bytes, record_path=None, source_pa
     print(json.dumps(rec))
 
 
-def roofline_jacobi(st):
-    """Roofline of the block-Jacobi update (A <- J^T A J on the touched
-    super-blocks, V <- V J): algorithmic bytes and flops counted on the device
-    by every active workgroup, time from HIP events around every launch."""
+def roofline_for(name, st, workload):
+    """Roofline of a kernel from its launches in the timed steps: time from HIP
+    events around every launch on its stream, algorithmic bytes and flops as
+    the launches account them (the GEMM: operands read once and the output
+    written once, 2 M N K flops; the Jacobi update: counted on the device by
+    every workgroup that does work)."""
     launches = max(st["launches"], 1)
     avg_ms = st["total_ms"] / launches
     bytes_l = st["bytes"] / launches
@@ -350,10 +377,10 @@ def roofline_jacobi(st):
         bound, achieved, peak, unit = "hbm", gbps, HBM_PEAK_GBPS, "GB/s"
     else:
         bound, achieved, peak, unit = "mfma", tflops, MFMA_FP32_PEAK_TFLOPS, "TFLOP/s"
-    return {"kernel": "k_jac_update (block-Jacobi rotation of A and V, fp32 MFMA)",
-            "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+    desc, symbol, _ = ROOF[name]
+    return {"kernel": desc, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(JACOBI_SOURCES, TRAFFIC_FILE),
+            "traffic": measured_traffic(kernel_sources(name), traffic_file(symbol, workload)),
             "algorithmic_bytes_per_launch": round(bytes_l),
             "algorithmic_flops_per_launch": round(flops_l),
             "arithmetic_intensity": round(ai, 2), "ridge_fp32": round(RIDGE_FP32, 2),

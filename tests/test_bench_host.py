@@ -2,8 +2,11 @@
 --pmc CSVs (scaled by a plain copy of known size) and its invalidation when
 the kernel's source changes.  No GPU."""
 import csv
+import glob
 import json
 import os
+
+import pytest
 
 import bench
 
@@ -34,7 +37,8 @@ def test_record_and_invalidate(tmp_path):
     src = tmp_path / "k.hip"
     src.write_text("kernel v1")
     rec_path = str(tmp_path / "traffic.json")
-    bench.record_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), copy, rec_path, (str(src),))
+    bench.record_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), copy, "jacobi_update",
+                         "test_workload", rec_path, (str(src),))
     rec = json.load(open(rec_path))
     assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
     assert rec["traffic_bytes_per_launch"] == (200.0 * 2 + 100.0) * 1024
@@ -44,10 +48,8 @@ def test_record_and_invalidate(tmp_path):
     assert bench.measured_traffic((str(src),), str(tmp_path / "missing.json")) is None
 
 
-def test_committed_record_matches_layout():
-    path = bench.TRAFFIC_FILE
-    if not os.path.exists(path):
-        return
+@pytest.mark.parametrize("path", sorted(glob.glob(os.path.join(bench.ROOT, "profiles", "traffic_*.json"))))
+def test_committed_record_matches_layout(path):
     rec = json.load(open(path))
     for k in ("fetch_kib_per_dispatch", "write_kib_per_dispatch", "fetch_scale", "write_scale",
               "traffic_bytes_per_launch", "source_sha256"):
@@ -59,12 +61,12 @@ def test_committed_record_matches_layout():
 
 def test_roofline_bound_choice():
     st = dict(launches=2, total_ms=2.0, bytes=2e9, flops=2e9 * 30)   # intensity 30 > fp32 ridge
-    r = bench.roofline_jacobi(st)
+    r = bench.roofline_for("gemm", st, "no_such_workload")
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
     # per launch: 1 ms, 1 GB, 30 GFLOP -> 30 TFLOP/s
     assert abs(r["achieved"] - 30.0) < 1e-9 and r["frac"] == round(30.0 / 157.3, 4)
     st = dict(launches=2, total_ms=2.0, bytes=2e9, flops=2e9)
-    r = bench.roofline_jacobi(st)
+    r = bench.roofline_for("gemm", st, "no_such_workload")
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and abs(r["achieved"] - 1000.0) < 1e-9
 
 
