@@ -111,6 +111,119 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   }
 }
 
+// Both operands bf16: bf16 matrix cores (32x32x16, fp32 accumulation).  A
+// product of two bf16 values is exact in fp32, so the result carries the same
+// fp32 accumulation as the fp32 path.  LDS holds the tiles k-contiguous per
+// row (As[m][k], Bs[n][k]) so that an MFMA operand (8 consecutive k of one
+// row) is one 16-byte read; tiles are filled with 16-byte global loads along
+// whichever dimension is contiguous.
+constexpr int BK16 = 32, KP = BK16 + 8;
+
+__device__ __forceinline__ void fill_tile_bf16(uint16_t (*S)[KP], const uint16_t* base, int64_t rbase,
+                                               int64_t rstride, bool rcontig, int64_t kbase, int64_t kstride,
+                                               bool kcontig, int64_t r0, int64_t rlim, int64_t k0, int64_t klim,
+                                               int tid) {
+  // 64 rows x 32 k = 2048 elements, 8 per thread
+  if (kcontig) {
+    const int r = tid >> 2, kq = (tid & 3) * 8;
+    const uint16_t* p = base + rbase + r * rstride + kbase + kq;
+    uint16_t v[8];
+    if (r0 + r < rlim && k0 + kq + 8 <= klim && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(p);
+      *reinterpret_cast<uint4*>(v) = raw;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (r0 + r < rlim && k0 + kq + i < klim) ? p[i] : static_cast<uint16_t>(0);
+    }
+    *reinterpret_cast<uint4*>(&S[r][kq]) = *reinterpret_cast<uint4*>(v);
+  } else if (rcontig) {
+    const int k = tid >> 3, rq = (tid & 7) * 8;
+    const uint16_t* p = base + rbase + rq + kbase + k * kstride;
+    uint16_t v[8];
+    if (r0 + rq + 8 <= rlim && k0 + k < klim && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(p);
+      *reinterpret_cast<uint4*>(v) = raw;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (r0 + rq + i < rlim && k0 + k < klim) ? p[i] : static_cast<uint16_t>(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) S[rq + i][k] = v[i];
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = tid * 8 + j, r = e >> 5, k = e & 31;
+      S[r][k] = (r0 + r < rlim && k0 + k < klim) ? base[rbase + r * rstride + kbase + k * kstride]
+                                                 : static_cast<uint16_t>(0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM][KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN][KP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
+  const int64_t zz = blockIdx.z;
+  const int64_t z = zz / g.ksplit, kz = zz % g.ksplit;
+  const int64_t kbeg = kz * g.kchunk;
+  const int64_t kend = (kbeg + g.kchunk < g.K) ? kbeg + g.kchunk : g.K;
+  const uint16_t* Ab = g.a_ptrs ? static_cast<const uint16_t*>(g.a_ptrs[z])
+                                : static_cast<const uint16_t*>(g.A) + z * g.a_batch;
+  const uint16_t* Bb = g.b_ptrs ? static_cast<const uint16_t*>(g.b_ptrs[z])
+                                : static_cast<const uint16_t*>(g.B) + z * g.b_batch;
+  const int64_t a_mbase = dim_off(g.am, m0);
+  const int64_t b_nbase = dim_off(g.bn, n0);
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const int r = lane & 31, half = lane >> 5;
+  f32x16 acc = {};
+  for (int64_t k0 = kbeg; k0 < kend; k0 += BK16) {
+    fill_tile_bf16(As, Ab, a_mbase, g.am.stride, g.am.stride == 1, dim_off(g.ak, k0), g.ak.stride,
+                   g.ak.stride == 1, m0, g.M, k0, kend, tid);
+    fill_tile_bf16(Bs, Bb, b_nbase, g.bn.stride, g.bn.stride == 1, dim_off(g.bk, k0), g.bk.stride,
+                   g.bk.stride == 1, n0, g.N, k0, kend, tid);
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK16; kk += 16) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&As[wm + r][kk + 8 * half]);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&Bs[wn + r][kk + 8 * half]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  if (g.ksplit > 1) {
+    float* Pp = g.partial + (z * g.ksplit + kz) * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t m = m0 + wm + (i >> 2) * 8 + half * 4 + (i & 3);
+      const int64_t n = n0 + wn + r;
+      if (m < g.M && n < g.N) Pp[m * g.N + n] = acc[i];
+    }
+    return;
+  }
+  char* Cb = static_cast<char*>(g.C);
+  const int64_t cz = z * g.c_batch;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t m = m0 + wm + (i >> 2) * 8 + half * 4 + (i & 3);
+    const int64_t n = n0 + wn + r;
+    if (m < g.M && n < g.N) {
+      float v = g.alpha * acc[i];
+      if (g.col_scale) v *= g.col_scale[z * g.col_scale_batch + n];
+      const int64_t off = cz + m * g.c_m + n * g.c_n;
+      if (g.c_dtype == kF32) {
+        float* C = reinterpret_cast<float*>(Cb);
+        if (g.beta != 0.f) v += g.beta * C[off];
+        C[off] = v;
+      } else {
+        uint16_t* C = reinterpret_cast<uint16_t*>(Cb);
+        C[off] = f32_to_bf16_rne(v);
+      }
+    }
+  }
+}
+
 // C = alpha * sum_kz partial[z][kz] (+ beta C), split order fixed: deterministic.
 __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
   const int64_t z = blockIdx.y, MN = g.M * g.N;
@@ -244,8 +357,14 @@ int grid1(int64_t n, int cap = 4096) {
 hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s) {
   GemmArgs g = g0;
   if (g.ksplit < 1 || !g.partial) g.ksplit = 1;
+  // bf16 x bf16 on bf16 matrix cores when every segmented dimension keeps a
+  // 32-wide k tile inside one segment
+  auto seg_ok = [](const GemmDim& d) { return d.len == INT64_MAX || d.len % BK16 == 0; };
+  const bool bf = g.a_dtype == kBF16 && g.b_dtype == kBF16 && seg_ok(g.ak) && seg_ok(g.bk) && seg_ok(g.am) &&
+                  seg_ok(g.bn);
+  const int kt = bf ? BK16 : BK;
   g.kchunk = (g.K + g.ksplit - 1) / g.ksplit;
-  g.kchunk = (g.kchunk + BK - 1) / BK * BK;            // chunks start on tile edges
+  g.kchunk = (g.kchunk + kt - 1) / kt * kt;            // chunks start on tile edges
   dim3 grid((g.M + BM - 1) / BM, (g.N + BN - 1) / BN, batch * g.ksplit);
   ProfScope ps("gemm", s);
   if (prof_enabled("gemm")) {   // dense flops; operands once, C written (and read when beta != 0) once
@@ -255,7 +374,8 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s) {
                   batch * (g.M * g.K * ea + g.K * g.N * eb + g.M * g.N * ec * (g.beta != 0.f ? 2 : 1)),
                   2.0 * g.M * g.N * g.K * batch);
   }
-  if (g.a_dtype == kBF16 && g.b_dtype == kBF16) k_gemm<uint16_t, uint16_t><<<grid, 256, 0, s>>>(g);
+  if (bf) k_gemm_bf16<<<grid, 256, 0, s>>>(g);
+  else if (g.a_dtype == kBF16 && g.b_dtype == kBF16) k_gemm<uint16_t, uint16_t><<<grid, 256, 0, s>>>(g);
   else if (g.a_dtype == kBF16) k_gemm<uint16_t, float><<<grid, 256, 0, s>>>(g);
   else if (g.b_dtype == kBF16) k_gemm<float, uint16_t><<<grid, 256, 0, s>>>(g);
   else k_gemm<float, float><<<grid, 256, 0, s>>>(g);

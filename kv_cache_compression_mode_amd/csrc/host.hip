@@ -406,6 +406,7 @@ struct AllocWS {
   float* G; float* V; float* J; int* active; int* rot; float* tauabs; double* offp;
   float* GDpart;
   void* syev;
+  void* syevD;
   float* GD; float* GDc; float* VD;
   int* order; float* Ucm; float* Vr; float* P; double* lam_tmp; float* qtau; int* perm; float* sgn;
   float* Om; float* Y; float* Z; float* Bm; float* Wr; float* Wd;
@@ -452,6 +453,7 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base) {
              static_cast<size_t>(d.ell_pad) * d.ell_pad * 12;
   per += static_cast<size_t>(std::max(d.T, d.HD)) * std::max<int64_t>(d.R, 1) * 8 + (1 << 20);
   per += static_cast<size_t>(gram_d_ksplit(d)) * d.D * d.D * 4;
+  per += syev_top_work_bytes(d.D, static_cast<int>(d.D), 1);
   if (!d.flash && d.R > 0) per += syev_top_work_bytes(d.n_pad, static_cast<int>(d.R), 1);
   // up to 64 tensors (24 GiB of scratch) per chunk: the eigensolver's chase
   // runs one workgroup per tensor, so wide chunks keep more of the chip busy
@@ -477,6 +479,7 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base) {
   w.tauabs = c.take<float>(chunk);
   w.offp = c.take<double>(static_cast<size_t>(chunk) * kOffBlocks * 2);
   w.GDpart = c.take<float>(static_cast<size_t>(chunk) * gram_d_ksplit(d) * d.D * d.D);
+  w.syevD = c.take<char>(syev_top_work_bytes(d.D, static_cast<int>(d.D), chunk));
   w.syev = (!d.flash && d.R > 0)
                ? static_cast<void*>(c.take<char>(syev_top_work_bytes(d.n_pad, static_cast<int>(d.R), chunk)))
                : nullptr;
@@ -590,9 +593,13 @@ void run_jacobi(float* A, float* V, int64_t n, int batch, const AllocWS& w, hipS
 void feature_factor(const Dims& d, int batch, int t0, const AllocWS& w, hipStream_t s) {
   const int64_t D = d.D;
   ck(hipMemcpyAsync(w.GDc, w.GD, sizeof(float) * batch * D * D, hipMemcpyDeviceToDevice, s));
-  ck(jacobi_small128(w.GD, w.VD, batch, kTauRel, kTauAbsRel, kMaxSweeps, s));
-  ck(topk_diag(w.GD, D, batch, static_cast<int>(D), w.order, s));
-  ck(launch_gather_cols(w.VD, D, D * D, w.order, D, w.Vr, D, D * D, D, D, batch, s));
+  if (eig_jacobi()) {
+    ck(jacobi_small128(w.GD, w.VD, batch, kTauRel, kTauAbsRel, kMaxSweeps, s));
+    ck(topk_diag(w.GD, D, batch, static_cast<int>(D), w.order, s));
+    ck(launch_gather_cols(w.VD, D, D * D, w.order, D, w.Vr, D, D * D, D, D, batch, s));
+  } else {
+    ck(syev_top(w.GD, D, batch, static_cast<int>(D), w.Vr, nullptr, w.syevD, s));
+  }
   ck(householder_qr(w.Vr, D, D, D, D * D, batch, w.qtau, s));
   // Rayleigh quotients diag(U^T G U): W = G U (column-major), then column dots
   GemmArgs g = gemm0();
