@@ -48,6 +48,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   const bool b_ncontig = g.bn.stride == 1;
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
   f32x16 acc = {};
+  if (g.c_lower && m0 + BM <= n0) return;          // tile wholly above the diagonal
 
   for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
     const int64_t a_kbase = dim_off(g.ak, k0);
@@ -58,8 +59,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
       if (a_mcontig) { kk = tid >> 4; mm = ((tid & 15) << 2) + j; }
       else           { mm = tid >> 2; kk = ((tid & 3) << 2) + j; }
       float v = 0.f;
-      if (m0 + mm < g.M && k0 + kk < kend)
-        v = ld<TA>(Ab, a_mbase + mm * g.am.stride + a_kbase + kk * g.ak.stride);
+      if (m0 + mm < g.M && k0 + kk < kend) {
+        if (g.a_sym && m0 + mm < k0 + kk)
+          v = ld<TA>(Ab, (k0 + kk) * g.am.stride + (m0 + mm) * g.ak.stride);
+        else
+          v = ld<TA>(Ab, a_mbase + mm * g.am.stride + a_kbase + kk * g.ak.stride);
+      }
       As[kk][mm] = v;
       int nn, kb;
       if (b_ncontig) { kb = tid >> 4; nn = ((tid & 15) << 2) + j; }
@@ -95,7 +100,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   for (int i = 0; i < 16; ++i) {
     const int64_t m = m0 + wm + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
     const int64_t n = n0 + wn + (lane & 31);
-    if (m < g.M && n < g.N) {
+    if (m < g.M && n < g.N && (!g.c_lower || m >= n)) {
       float v = g.alpha * acc[i];
       if (g.col_scale) v *= g.col_scale[z * g.col_scale_batch + n];
       const int64_t off = cz + m * g.c_m + n * g.c_n;
@@ -232,6 +237,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
     float acc = 0.f;
     for (int kz = 0; kz < g.ksplit; ++kz) acc += p[kz * MN];
     const int64_t m = i / g.N, n = i % g.N;
+    if (g.c_lower && m < n) continue;
     float v = g.alpha * acc;
     if (g.col_scale) v *= g.col_scale[z * g.col_scale_batch + n];
     const int64_t off = z * g.c_batch + m * g.c_m + n * g.c_n;
@@ -361,7 +367,7 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s) {
   // 32-wide k tile inside one segment
   auto seg_ok = [](const GemmDim& d) { return d.len == INT64_MAX || d.len % BK16 == 0; };
   const bool bf = g.a_dtype == kBF16 && g.b_dtype == kBF16 && seg_ok(g.ak) && seg_ok(g.bk) && seg_ok(g.am) &&
-                  seg_ok(g.bn);
+                  seg_ok(g.bn) && !g.a_sym && !g.c_lower;
   const int kt = bf ? BK16 : BK;
   g.kchunk = (g.K + g.ksplit - 1) / g.ksplit;
   g.kchunk = (g.kchunk + kt - 1) / kt * kt;            // chunks start on tile edges

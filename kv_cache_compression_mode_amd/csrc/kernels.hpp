@@ -43,6 +43,10 @@ struct GemmArgs {
   // split-K: ksplit > 1 writes partial sums to `partial` ([batch][ksplit][M][N]
   // floats) and reduces them in a fixed order (deterministic)
   int ksplit; float* partial; int64_t kchunk;
+  // symmetric operands stored as their lower triangle (fp32 path, plain
+  // dimensions only): a_sym reads A(m, k) with m < k from A(k, m); c_lower
+  // computes and writes only C(m, n) with m >= n
+  int a_sym, c_lower;
 };
 
 hipError_t launch_gemm(const GemmArgs& g, int batch, hipStream_t s);

@@ -407,7 +407,7 @@ SyevLayout syev_layout(int64_t n, int R, int batch) {
   L.t_off = take(B * (L.P > 0 ? L.P : 1) * 1024 * 4);
   L.tau_off = take(B * 2 * SBW * 4);
   L.y_off = take(B * n * SBW * 4);
-  L.x_off = take(B * n * SBW * 4);
+  L.x_off = take(B * n * 2 * SBW * 4);
   L.s1_off = take(B * 1024 * 4);
   L.s2_off = take(B * 1024 * 4);
   L.s3_off = take(B * 1024 * 4);
@@ -444,7 +444,7 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
   float* Tst = reinterpret_cast<float*>(wb + Lw.t_off);
   float* taus = reinterpret_cast<float*>(wb + Lw.tau_off);
   float* Yb = reinterpret_cast<float*>(wb + Lw.y_off);
-  float* Xb = reinterpret_cast<float*>(wb + Lw.x_off);
+  float* VW = reinterpret_cast<float*>(wb + Lw.x_off);     // [V | W], mp x 64 column-major
   float* S1 = reinterpret_cast<float*>(wb + Lw.s1_off);
   float* S2 = reinterpret_cast<float*>(wb + Lw.s2_off);
   float* Wb = reinterpret_cast<float*>(wb + Lw.wb_off);
@@ -462,9 +462,11 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
   hipError_t e;
   auto gemm = [&](int64_t M, int64_t N, int64_t K, const float* Ab, GemmDim am, GemmDim ak, int64_t ab,
                   const float* Bb, GemmDim bk, GemmDim bn, int64_t bb, float* Cb, int64_t cm, int64_t cn,
-                  int64_t cb, float alpha, float beta, int ksplit = 1) -> hipError_t {
+                  int64_t cb, float alpha, float beta, int ksplit = 1, int a_sym = 0,
+                  int c_lower = 0) -> hipError_t {
     if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
     GemmArgs g{};
+    g.a_sym = a_sym; g.c_lower = c_lower;
     g.M = M; g.N = N; g.K = K;
     g.A = Ab; g.a_dtype = kF32; g.am = am; g.ak = ak; g.a_batch = ab;
     g.B = Bb; g.b_dtype = kF32; g.bk = bk; g.bn = bn; g.b_batch = bb;
@@ -497,23 +499,24 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     if ((e = gemm(SBW, SBW, SBW, V, plain(1), plain(mp), vs, S2, plain(SBW), plain(1), 1024, panel, 1, n, nn,
                   -1.f, 1.f)) != hipSuccess) return e;
     float* A22 = A + r * n + r;
-    // X = A22 V T
+    // X = A22 V T, into the W half of VW
+    const int64_t vwb = n * 2 * SBW;
+    float* Xb = VW + SBW * mp;
     if ((e = gemm(mp, SBW, mp, A22, plain(1), plain(n), nn, V, plain(1), plain(mp), vs, Yb, 1, mp, n * SBW, 1.f,
-                  0.f)) != hipSuccess) return e;
-    if ((e = gemm(mp, SBW, SBW, Yb, plain(1), plain(mp), n * SBW, T, plain(SBW), plain(1), ts, Xb, 1, mp,
-                  n * SBW, 1.f, 0.f)) != hipSuccess) return e;
+                  0.f, 1, /*a_sym=*/1)) != hipSuccess) return e;
+    if ((e = gemm(mp, SBW, SBW, Yb, plain(1), plain(mp), n * SBW, T, plain(SBW), plain(1), ts, Xb, 1, mp, vwb,
+                  1.f, 0.f)) != hipSuccess) return e;
     // W = X - V (T^T (V^T X)) / 2, in place in X
-    if ((e = gemm(SBW, SBW, mp, V, plain(mp), plain(1), vs, Xb, plain(1), plain(mp), n * SBW, S1, SBW, 1, 1024,
+    if ((e = gemm(SBW, SBW, mp, V, plain(mp), plain(1), vs, Xb, plain(1), plain(mp), vwb, S1, SBW, 1, 1024,
                   1.f, 0.f, ksplit_for(mp))) != hipSuccess) return e;
     if ((e = gemm(SBW, SBW, SBW, T, plain(1), plain(SBW), ts, S1, plain(SBW), plain(1), 1024, S2, SBW, 1, 1024,
                   1.f, 0.f)) != hipSuccess) return e;
-    if ((e = gemm(mp, SBW, SBW, V, plain(1), plain(mp), vs, S2, plain(SBW), plain(1), 1024, Xb, 1, mp, n * SBW,
+    if ((e = gemm(mp, SBW, SBW, V, plain(1), plain(mp), vs, S2, plain(SBW), plain(1), 1024, Xb, 1, mp, vwb,
                   -0.5f, 1.f)) != hipSuccess) return e;
-    // A22 -= V W^T + W V^T
-    if ((e = gemm(mp, mp, SBW, V, plain(1), plain(mp), vs, Xb, plain(mp), plain(1), n * SBW, A22, 1, n, nn,
-                  -1.f, 1.f)) != hipSuccess) return e;
-    if ((e = gemm(mp, mp, SBW, Xb, plain(1), plain(mp), n * SBW, V, plain(mp), plain(1), vs, A22, 1, n, nn,
-                  -1.f, 1.f)) != hipSuccess) return e;
+    // A22 -= V W^T + W V^T as one product of K = 64: [V W] [W V]^T
+    if ((e = copy_cols(V, mp, vs, VW, mp, vwb, mp, SBW, batch, s)) != hipSuccess) return e;
+    if ((e = gemm(mp, mp, 2 * SBW, VW, plain(1), plain(mp), vwb, Xb, segmented(SBW, -SBW * mp, mp), plain(1), vwb,
+                  A22, 1, n, nn, -1.f, 1.f, 1, 0, /*c_lower=*/1)) != hipSuccess) return e;
   }
   }
   // ---- stage 2: band -> tridiagonal
