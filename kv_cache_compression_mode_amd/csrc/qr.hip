@@ -215,17 +215,18 @@ struct LdsQr {
 __device__ void lds_householder(float* P, int mr, int nb, LdsQr& L) {
   const int i = threadIdx.x, lane = i & 63, wave = i >> 6;
   for (int j = 0; j < nb; ++j) {
+    // one reduction per column: slot c != j gets sum_{i > j} P[c][i] x_i, slot j
+    // gets sigma = sum_{i > j} x_i^2 (x = column j below the diagonal)
     const float x = (i > j && i < mr) ? P[j * kLeaf + i] : 0.f;
-    float ss = wave_sum(x * x);
-    if (lane == 0) L.red[wave][0] = ss;
+    float part[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c)
+      part[c] = (c < nb && i > j && i < mr) ? (c == j ? x : P[c * kLeaf + i]) * x : 0.f;
+    const float tot = reduce32(part, lane);
+    if ((lane & 1) == 0) L.red[wave][lane >> 1] = tot;
     __syncthreads();
-    if (i == 0) {
-      float t = 0.f;
-      for (int w = 0; w < LW; ++w) t += L.red[w][0];
-      L.bc = t;
-    }
-    __syncthreads();
-    const float sigma = L.bc;
+    float sigma = 0.f;
+    for (int w = 0; w < LW; ++w) sigma += L.red[w][j];
     const float alpha = P[j * kLeaf + j];
     float tau = 0.f, beta = alpha, scale = 0.f;
     if (sigma > 0.f) {
@@ -234,20 +235,14 @@ __device__ void lds_householder(float* P, int mr, int nb, LdsQr& L) {
       tau = (beta - alpha) / beta;
       scale = 1.f / (alpha - beta);
     }
-    const float v = (i == j) ? 1.f : (i > j && i < mr ? x * scale : 0.f);
-    float part[32];
-#pragma unroll
-    for (int c = 0; c < 32; ++c)
-      part[c] = (c < nb && c != j && i >= j && i < mr) ? P[c * kLeaf + i] * v : 0.f;
-    const float tot = reduce32(part, lane);
-    if ((lane & 1) == 0) L.red[wave][lane >> 1] = tot;
-    __syncthreads();
+    // v_j = (1, x * scale); dots d_c = v_c^T v_j (c < j) or v_j^T P[c] (c > j)
     if (i < 32) {
       float t = 0.f;
       for (int w = 0; w < LW; ++w) t += L.red[w][i];
-      L.dots[i] = t;
+      L.dots[i] = (i < nb && i != j) ? P[i * kLeaf + j] + scale * t : 0.f;
     }
     __syncthreads();
+    const float v = (i == j) ? 1.f : (i > j && i < mr ? x * scale : 0.f);
     if (i > j && i < mr) P[j * kLeaf + i] = v;
     if (i == j) P[j * kLeaf + j] = beta;
     if (tau != 0.f && i >= j && i < mr) {

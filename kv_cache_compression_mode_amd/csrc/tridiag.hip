@@ -237,83 +237,109 @@ __global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double*
     piv_s = DBL_MIN * fmax(1.0, emax);
   }
   __syncthreads();
-  const int q = blockIdx.x * 256 + threadIdx.x;
-  if (q >= R) return;
+  // four threads per eigenvalue (multisection): each evaluates one of four
+  // interior points of the bracket, which then shrinks to one fifth
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int q = gid >> 2, sub = gid & 3;
+  if (q >= R) return;                             // whole groups leave together
   const int64_t k = n - 1 - q;                    // wanted: the k-th smallest (0-based)
   double lo = gl_s, hi = gu_s;
-  for (int it = 0; it < 200; ++it) {
-    const double mid = 0.5 * (lo + hi);
-    if (mid <= lo || mid >= hi) break;
+  for (int it = 0; it < 100; ++it) {
     if (hi - lo <= 2.0 * DBL_EPSILON * fmax(fabs(lo), fabs(hi)) + piv_s) break;
-    if (sturm_count(d, e2, n, mid, piv_s) > k) hi = mid;
-    else lo = mid;
+    const double w = hi - lo;
+    const double x = lo + w * (sub + 1) * 0.2;
+    const int cnt = sturm_count(d, e2, n, x, piv_s);
+    double nlo = lo, nhi = hi;
+    bool found = false;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int ct = __shfl(cnt, (threadIdx.x & 63 & ~3) + t);
+      const double xt = lo + w * (t + 1) * 0.2;
+      if (!found) {
+        if (ct > k) { nhi = xt; found = true; }
+        else nlo = xt;
+      }
+    }
+    if (!(nlo > lo || nhi < hi)) break;           // no progress at fp64 resolution
+    lo = nlo;
+    hi = nhi;
   }
-  lam[z * R + q] = 0.5 * (lo + hi);
+  if (sub == 0) lam[z * R + q] = 0.5 * (lo + hi);
 }
 
 // Eigenvector of eigenvalue lam[q] by inverse iteration (three solves with
 // T - lam I = L D L^T from a fixed pseudo-random start), normalized, fp32
-// out as column q of Z (column-major, ld n).  Scratch dp / y: [i][q]
-// interleaved (coalesced across q).
+// out as column q of Z (column-major, ld n).  The factorization keeps the
+// reciprocal pivots, so each solve is multiply-only; intermediate vectors
+// are rescaled on the fly.  Scratch rp / y: [i][q] interleaved (coalesced
+// across q).
 __global__ __launch_bounds__(256) void k_invit(const double* d_g, const double* e_g, int64_t n, int R,
-                                              const double* lam, double* dp_g, double* y_g, float* Z,
+                                              const double* lam, double* rp_g, double* y_g, float* Z,
                                               int64_t z_batch) {
+  __shared__ double red[4];
   const int64_t z = blockIdx.y;
-  const int q = blockIdx.x * 256 + threadIdx.x;
-  if (q >= R) return;
   const double* d = d_g + z * n;
   const double* e = e_g + z * n;
-  double* dp = dp_g + z * n * R;
+  double tn = 0.0;                                  // infinity norm of T (whole block)
+  for (int64_t i = threadIdx.x; i < n; i += 256)
+    tn = fmax(tn, fabs(d[i]) + fabs(e[i]) + (i ? fabs(e[i - 1]) : 0.0));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tn = fmax(tn, __shfl_xor(tn, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = tn;
+  __syncthreads();
+  const double tnorm = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= R) return;
+  double* rp = rp_g + z * n * R;
   double* y = y_g + z * n * R;
   const double lm = lam[z * R + q];
-  double tnorm = 0.0;
-  for (int64_t i = 0; i < n; ++i) tnorm = fmax(tnorm, fabs(d[i]) + fabs(e[i]) + (i ? fabs(e[i - 1]) : 0.0));
   const double tiny = fmax(tnorm, DBL_MIN) * DBL_EPSILON;
-  // L D L^T of T - lam I
-  double prev = d[0] - lm;
-  if (fabs(prev) < tiny) prev = tiny;
-  dp[q] = prev;
-  for (int64_t i = 1; i < n; ++i) {
-    double di = (d[i] - lm) - e[i - 1] * e[i - 1] / prev;
-    if (fabs(di) < tiny) di = tiny;
-    dp[i * R + q] = di;
-    prev = di;
+  // L D L^T of T - lam I: pivots p_i = (d_i - lam) - e_{i-1}^2 / p_{i-1}, kept as 1 / p_i
+  {
+    double p = d[0] - lm;
+    if (fabs(p) < tiny) p = tiny;
+    double r = 1.0 / p;
+    rp[q] = r;
+    for (int64_t i = 1; i < n; ++i) {
+      p = (d[i] - lm) - e[i - 1] * e[i - 1] * r;
+      if (fabs(p) < tiny) p = tiny;
+      r = 1.0 / p;
+      rp[i * R + q] = r;
+    }
   }
   // start: uniform in [0.5, 1.5) from a counter hash of (q, i)
   for (int64_t i = 0; i < n; ++i) {
     const uint64_t hsh = mix64(0x9E3779B97F4A7C15ull * static_cast<uint64_t>(q + 1) + static_cast<uint64_t>(i));
     y[i * R + q] = 0.5 + static_cast<double>(hsh >> 11) * 0x1p-53;
   }
+  double sc = 1.0;
   for (int it = 0; it < 3; ++it) {
-    // forward: L u = y
-    double u = y[q];
+    // forward: L u = sc * y   (L unit lower, l_i = e_{i-1} / p_{i-1})
+    double u = y[q] * sc;
+    y[q] = u;
     for (int64_t i = 1; i < n; ++i) {
-      const double li = e[i - 1] / dp[(i - 1) * R + q];
-      u = y[i * R + q] - li * u;
+      u = y[i * R + q] * sc - e[i - 1] * rp[(i - 1) * R + q] * u;
       y[i * R + q] = u;
     }
-    // D L^T x = u  (backward), then normalize
-    double xs = y[(n - 1) * R + q] / dp[(n - 1) * R + q];
+    // D L^T x = u:  x_i = (u_i - e_i x_{i+1}) / p_i
+    double xs = y[(n - 1) * R + q] * rp[(n - 1) * R + q];
     y[(n - 1) * R + q] = xs;
     double mx = fabs(xs);
     for (int64_t i = n - 2; i >= 0; --i) {
-      const double li = e[i] / dp[i * R + q];
-      xs = y[i * R + q] / dp[i * R + q] - li * xs;
+      xs = (y[i * R + q] - e[i] * xs) * rp[i * R + q];
       y[i * R + q] = xs;
       mx = fmax(mx, fabs(xs));
     }
-    double s2 = 0.0;
-    const double inv = mx > 0.0 ? 1.0 / mx : 1.0;
-    for (int64_t i = 0; i < n; ++i) {
-      const double t = y[i * R + q] * inv;
-      y[i * R + q] = t;
-      s2 += t * t;
-    }
-    const double sc = 1.0 / sqrt(s2);
-    for (int64_t i = 0; i < n; ++i) y[i * R + q] *= sc;
+    sc = mx > 0.0 ? 1.0 / mx : 1.0;
   }
+  double s2 = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    const double t = y[i * R + q] * sc;
+    s2 += t * t;
+  }
+  const double nrm = sc / sqrt(s2);
   float* zc = Z + z * z_batch + static_cast<int64_t>(q) * n;
-  for (int64_t i = 0; i < n; ++i) zc[i] = static_cast<float>(y[i * R + q]);
+  for (int64_t i = 0; i < n; ++i) zc[i] = static_cast<float>(y[i * R + q] * nrm);
 }
 
 // Stage 2 back-transformation of a tile of CT eigenvector columns held in
@@ -551,7 +577,7 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     const unsigned gx = static_cast<unsigned>((R + 255) / 256);
     {
       ProfScope ps("tri_eig", s);
-      k_bisect<<<dim3(gx, batch), 256, lds, s>>>(dd, ee, n, R, lam);
+      k_bisect<<<dim3(static_cast<unsigned>((4 * R + 255) / 256), batch), 256, lds, s>>>(dd, ee, n, R, lam);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       k_invit<<<dim3(gx, batch), 256, 0, s>>>(dd, ee, n, R, lam, dp, yv, Z, n * n);
     }
