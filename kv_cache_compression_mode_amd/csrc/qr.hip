@@ -619,8 +619,8 @@ size_t householder_qr_work_floats(int64_t m, int64_t k, int batch) {
 }
 
 namespace {
-int qr_ksplit(int64_t K) {
-  const int64_t s = K / 2048;
+int qr_ksplit(int64_t K) {        // chunks of at least 256 rows
+  const int64_t s = K / 256;
   return static_cast<int>(s < 1 ? 1 : (s > kQrSplit ? kQrSplit : s));
 }
 }  // namespace

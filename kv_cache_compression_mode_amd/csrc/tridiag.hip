@@ -452,8 +452,10 @@ SyevLayout syev_layout(int64_t n, int R, int batch) {
   return L;
 }
 
+// split-K for the products with a 32-row output and a long K (a workgroup per
+// output tile would otherwise walk K alone): chunks of at least 256
 int ksplit_for(int64_t K) {
-  const int64_t s = K / 2048;
+  const int64_t s = K / 256;
   return static_cast<int>(s < 1 ? 1 : (s > 16 ? 16 : s));
 }
 
