@@ -10,7 +10,8 @@
 //     below the subdiagonal with a reflector of length <= 32 and chases the
 //     bulge it creates down the band one 32-row block per step; sweeps are
 //     pipelined (sweep j step s runs at tick S j + s, one wave per sweep in
-//     flight, S >= 3 keeps the blocks of concurrent steps disjoint);
+//     flight; S >= 4 keeps the rows of concurrent steps, and of each step and
+//     the next step's prefetch, disjoint);
 //  3. the top R eigenvalues of the tridiagonal by bisection on Sturm counts
 //     and their eigenvectors by inverse iteration on T - lambda I = L D L^T,
 //     both in fp64;
@@ -34,7 +35,6 @@ namespace {
 constexpr int SBW = 32;           // half-bandwidth after stage 1 (= panel width)
 constexpr int BWS = 2 * SBW;      // band storage width: the bulge stays within 2b - 1
 constexpr int RFS = SBW + 1;      // stored floats per chase reflector: v[0..31], tau
-constexpr int SW = 8;             // waves of the chase kernel (sweeps in flight)
 
 __host__ __device__ inline int64_t sweep_steps(int64_t n, int64_t j) {
   return (n - 1 - j < 2) ? 0 : (n - 3 - j) / SBW + 1;
@@ -65,119 +65,240 @@ __global__ __launch_bounds__(256) void k_band_init(const float* A, int64_t n, fl
 // n <= 32768, so every band offset fits in 32 bits
 __device__ __forceinline__ int bidx(int r, int c) { return r * BWS + (r - c); }
 
-// Stage 2: one workgroup of SW waves per matrix.
-__global__ __launch_bounds__(SW * 64) void k_chase(float* Bw_g, int64_t n, float* Rf_g, int64_t rf_stride,
-                                                  int S) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Stage 2: one workgroup of NW waves per matrix; sweep j runs on wave j % NW.
+// Every block of a step moves between the band and registers along its rows
+// (row r of the band holds A[r][r - k], k = 0..63, contiguous), so each
+// access of a wave covers two 128-byte row segments; a wave's private LDS
+// tiles provide the transposed views the step needs.  Per wave:
+//  * the below block of step s is kept in LDS: it is the left block of step
+//    s + 1 of the same sweep, which writes it back to the band (the last step
+//    of a sweep writes it itself);
+//  * the diagonal block, the below block and (step 0) the column being
+//    annihilated of the wave's next step are loaded one tick ahead, into
+//    registers.
+// With S >= 4 ticks between consecutive sweeps every value a prefetch reads
+// was written at least two ticks earlier, and no concurrent step touches it.
+// The band is addressed through a buffer resource of the matrix's n rows:
+// rows past the last read as zero and writes to them are dropped, which
+// covers the ragged last block of every sweep without per-row masks.
+constexpr int TLD = SBW + 1;      // LDS tile row stride (conflict-free transposes)
+constexpr uint32_t kOut = 0x80000000u;   // a byte offset past any band (n <= 32768)
+struct ChaseLds {
+  float tile[2][SBW * TLD];       // ping-pong: carried left block / staged below block
+  float x[SBW];                   // the column annihilated by the next step
+  float w[SBW];
+};
+struct ChaseStep {
+  int j, s, r0, L, r1, hi;
+  bool last;
+};
+// sweeps of one wave: j = wave, wave + nw, ...; sweep j runs its steps at
+// ticks S j .. S j + steps(j) - 1 (S nw >= steps(0), so they never overlap)
+struct ChaseClock {
+  int j, start, K;
+  __device__ void init(int wave, int S, int n) {
+    j = wave; start = S * j; K = static_cast<int>(sweep_steps(n, j));
+  }
+  // the step at tick t (ticks visited in increasing order)
+  __device__ bool at(int t, int nw, int S, int n, ChaseStep& g) {
+    if (t - start >= K && K > 0) { j += nw; start = S * j; K = static_cast<int>(sweep_steps(n, j)); }
+    const int s = t - start;
+    if (s < 0 || s >= K) return false;
+    g.j = j; g.s = s; g.last = (s == K - 1);
+    g.r0 = j + 1 + s * SBW;
+    g.L = min(n - g.r0, SBW);
+    g.r1 = g.r0 + g.L;
+    g.hi = min(g.r1 + SBW, n);
+    return true;
+  }
+};
+// orders one wave's LDS accesses (LDS executes a wave's operations in order)
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+__device__ __forceinline__ float bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
+}
+__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(off), 0, 0);
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void k_chase(float* Bw_g, int n, float* Rf_g, int64_t rf_stride, int S) {
+  extern __shared__ float chase_lds_raw[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, l32 = lane & 31;
-  float* Bw = Bw_g + blockIdx.x * n * BWS;
+  ChaseLds& sm = reinterpret_cast<ChaseLds*>(chase_lds_raw)[wave];
+  float* Bw = Bw_g + static_cast<int64_t>(blockIdx.x) * n * BWS;
+  const __amdgpu_buffer_rsrc_t band = __builtin_amdgcn_make_buffer_rsrc(Bw, 0, n * BWS * 4, 0x00020000);
   float* Rf = Rf_g + blockIdx.x * rf_stride;
-  const int64_t last = n - 3;                       // last sweep with work
-  const int64_t ticks = last >= 0 ? S * last + sweep_steps(n, last) : 0;
-  float xn = 0.f;                                   // the next step's column (lanes 0..31)
-  for (int64_t t = 0; t < ticks; ++t) {
-    int64_t j = -1, s = -1;
-    const int64_t q = t / S;
-    if (q >= wave) {
-      const int64_t jj = q - ((q - wave) % SW);     // latest sweep of this wave that has started
-      if (jj <= last) {
-        const int64_t ss = t - S * jj;
-        if (ss < sweep_steps(n, jj)) { j = jj; s = ss; }
-      }
+  const int last = n - 3;
+  const int ticks = last >= 0 ? S * last + static_cast<int>(sweep_steps(n, last)) : 0;
+  // byte offsets of this lane's element in row h * 16 of a block; row ii adds 65 floats
+  constexpr uint32_t RS = 4 * (BWS + 1);
+  float pd[16], pb[16], px = 0.f;   // next step: diagonal block rows, below block rows, column
+  auto prefetch = [&](const ChaseStep& q) {
+    const uint32_t od = 4u * static_cast<uint32_t>(q.r0 * BWS + h * 16 * (BWS + 1) - l32);  // (r0 + a, r0 + l32)
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) pd[ii] = bload(band, od + ii * RS);
+    if (q.r1 < q.hi) {
+      const uint32_t ob = 4u * static_cast<uint32_t>(q.r1 * BWS + h * 16 * (BWS + 1) + q.L - l32);  // (r1 + a, r0 + l32)
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) pb[ii] = bload(band, ob + ii * RS);
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) pb[ii] = 0.f;
     }
-    if (j >= 0) {
-      const int nn = static_cast<int>(n), jj = static_cast<int>(j), ss = static_cast<int>(s);
-      int r0, c, L;
-      if (ss == 0) { r0 = jj + 1; c = jj; L = nn - 1 - jj < SBW ? nn - 1 - jj : SBW; }
-      else { r0 = jj + 1 + ss * SBW; c = r0 - SBW; L = nn - r0 < SBW ? nn - r0 : SBW; }
-      const int r1 = r0 + L;
-      const int hi = (r1 + SBW < nn) ? r1 + SBW : nn;
-      float x = 0.f;
-      if (ss == 0) x = (lane < L) ? Bw[bidx(r0 + lane, jj)] : 0.f;
-      else x = (lane < L) ? xn : 0.f;
-      // every block this step reads, loaded up front (the blocks are disjoint)
-      float ai[16], dv[16], bv[16];
+    if (q.s == 0) px = bload(band, 4u * static_cast<uint32_t>(q.r0 * BWS + 1 + l32 * (BWS + 1)));  // (r0 + l32, j)
+  };
+  ChaseClock ck, ckn;
+  ck.init(wave, S, n);
+  ckn.init(wave, S, n);
+  {
+    ChaseStep g0;
+    if (ckn.at(0, NW, S, n, g0)) prefetch(g0);
+  }
+  int cur = 0;                      // tile holding the carried left block
+  for (int t = 0; t < ticks; ++t) {
+    ChaseStep g, gn;
+    const bool act = ck.at(t, NW, S, n, g);
+    const bool actn = ckn.at(t + 1, NW, S, n, gn);
+    float* Lt = sm.tile[cur];
+    float* Ft = sm.tile[cur ^ 1];
+    float dcur[16];
+    if (act) {
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) {
-        const int i = h * 16 + ii;
-        ai[ii] = (ss > 0 && i < L) ? Bw[bidx(r0 + i, c + l32)] : 0.f;                  // block left of D
-        const int a = l32, bb = h * 16 + ii;
-        float d = 0.f;
-        if (a < L && bb < L) d = a >= bb ? Bw[bidx(r0 + a, r0 + bb)] : Bw[bidx(r0 + bb, r0 + a)];
-        dv[ii] = d;
-        const int row = r1 + l32;
-        bv[ii] = (row < hi && bb < L) ? Bw[bidx(row, r0 + bb)] : 0.f;                    // block below D
+        dcur[ii] = pd[ii];
+        Ft[(h * 16 + ii) * TLD + l32] = pb[ii];     // below block, row-major
       }
-      // reflector (I - tau v v^T) x = beta e_1
-      const float alpha = __shfl(x, 0);
-      const float sigma = wave_sum((lane >= 1 && lane < L) ? x * x : 0.f);
+      if (g.s == 0 && lane < SBW) sm.x[lane] = px;
+    }
+    if (actn) prefetch(gn);
+    if (act) {
+      const int L = g.L, r0 = g.r0;
+      wave_lds_sync();
+      // reflector (I - tau v v^T) x = beta e_1 from x = sm.x (zero past L)
+      float xh[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 x4 = *reinterpret_cast<const float4*>(&sm.x[h * 16 + 4 * q4]);
+        xh[4 * q4] = x4.x; xh[4 * q4 + 1] = x4.y; xh[4 * q4 + 2] = x4.z; xh[4 * q4 + 3] = x4.w;
+      }
+      const float xo = sm.x[l32];
+      const float alpha = sm.x[0];
+      float sig = h ? xh[0] * xh[0] : 0.f;
+#pragma unroll
+      for (int ii = 1; ii < 16; ++ii) sig += xh[ii] * xh[ii];
+      sig += __shfl_xor(sig, 32);                  // same sum in both halves (commutative)
       float tau = 0.f, beta = alpha, scale = 0.f;
-      if (sigma > 0.f) {
-        const float nrm = sqrtf(alpha * alpha + sigma);
+      if (sig > 0.f) {
+        const float nrm = sqrtf(alpha * alpha + sig);
         beta = alpha >= 0.f ? -nrm : nrm;
         tau = (beta - alpha) / beta;
         scale = 1.f / (alpha - beta);
       }
-      const float v = (lane == 0) ? 1.f : ((lane < L) ? x * scale : 0.f);   // lanes >= 32: 0
-      const int64_t ridx = sweep_offset(n, j) + s;
-      if (lane < SBW) Rf[ridx * RFS + lane] = v;
+      float vh[16];                                // v_i, i = h * 16 + ii
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) vh[ii] = xh[ii] * scale;
+      if (h == 0) vh[0] = 1.f;
+      const float vo = (l32 == 0) ? 1.f : xo * scale;   // v_{l32}
+      const int64_t ridx = sweep_offset(n, g.j) + g.s;
+      if (lane < SBW) Rf[ridx * RFS + lane] = vo;
       if (lane == 0) Rf[ridx * RFS + SBW] = tau;
-      float vv[16];
+      // left block (rows r0.., columns r0-32 .. r0-1) from the left; written back
+      if (g.s == 0) {
+        if (h == 0) bstore(band, 4u * static_cast<uint32_t>(r0 * BWS + 1 + l32 * (BWS + 1)),
+                           l32 == 0 ? beta : 0.f);
+      } else {
+        float li[16];
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) vv[ii] = __shfl(v, h * 16 + ii);
-      const float va = __shfl(v, l32);
-      if (tau != 0.f) {
-        // left block: rows r0.., columns c..r0-1 (for s == 0 only column j)
-        if (ss == 0) {
-          if (lane < L) Bw[bidx(r0 + lane, jj)] = lane == 0 ? beta : 0.f;
-        } else {
-          float y = 0.f;
+        for (int ii = 0; ii < 16; ++ii) li[ii] = Lt[(h * 16 + ii) * TLD + l32];
+        float y = 0.f;
 #pragma unroll
-          for (int ii = 0; ii < 16; ++ii) y += vv[ii] * ai[ii];
-          y += __shfl_xor(y, 32);
-#pragma unroll
-          for (int ii = 0; ii < 16; ++ii) {
-            const int i = h * 16 + ii;
-            if (i < L) {
-              const float nv = (l32 == 0) ? (i == 0 ? beta : 0.f) : ai[ii] - tau * vv[ii] * y;
-              Bw[bidx(r0 + i, c + l32)] = nv;
-            }
-          }
-        }
-        // D <- H D H = D - tau (v w^T + w v^T) + tau^2 (v^T w) v v^T, w = D v
-        float w = 0.f;
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) w += dv[ii] * vv[ii];
-        w += __shfl_xor(w, 32);                           // w_a, a = l32, in both halves
-        const float gam = wave_sum(lane < 32 ? va * w : 0.f);
+        for (int ii = 0; ii < 16; ++ii) y += vh[ii] * li[ii];
+        y += __shfl_xor(y, 32);
+        const uint32_t ol = 4u * static_cast<uint32_t>(r0 * BWS + h * 16 * (BWS + 1) + SBW - l32);
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) {
-          const int bb = h * 16 + ii;
-          const float wb = __shfl(w, bb);
-          if (l32 < L && bb < L && bb <= l32) {
-            const float nd = dv[ii] - tau * (va * wb + w * vv[ii]) + tau * tau * gam * va * vv[ii];
-            Bw[bidx(r0 + l32, r0 + bb)] = nd;
-          }
-        }
-        // block below D: rows r1.., columns r0..r1-1, from the right
-        float zr = 0.f;
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) zr += bv[ii] * vv[ii];
-        zr += __shfl_xor(zr, 32);
-        const int row = r1 + l32;
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) {
-          const int bb = h * 16 + ii;
-          if (row < hi && bb < L) {
-            const float nb = bv[ii] - tau * zr * vv[ii];
-            Bw[bidx(row, r0 + bb)] = nb;
-            bv[ii] = nb;
-          }
+          float nv = li[ii] - tau * vh[ii] * y;
+          if (l32 == 0) nv = (h == 0 && ii == 0) ? beta : 0.f;
+          bstore(band, ol + ii * RS, nv);
         }
       }
-      // the next step's column: column r0 of the block below, rows r1 .. hi-1
-      xn = __shfl(bv[0], l32);                             // lanes with h == 0 hold column r0
-      if (!(lane < 32 && r1 + lane < hi)) xn = 0.f;
+      if (tau != 0.f) {
+        // diagonal block, symmetric, into the left block's tile
+        float* Ds = Lt;
+        wave_lds_sync();
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+          const int a = h * 16 + ii;
+          Ds[a * TLD + l32] = (l32 <= a) ? dcur[ii] : 0.f;
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+          const int a = h * 16 + ii;
+          if (l32 < a) Ds[l32 * TLD + a] = dcur[ii];
+        }
+        wave_lds_sync();
+        // w = D v (lane: row l32)
+        float wo = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) wo += Ds[l32 * TLD + h * 16 + ii] * vh[ii];
+        wo += __shfl_xor(wo, 32);
+        if (lane < SBW) sm.w[lane] = wo;
+        wave_lds_sync();
+        float wh[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 w4 = *reinterpret_cast<const float4*>(&sm.w[h * 16 + 4 * q4]);
+          wh[4 * q4] = w4.x; wh[4 * q4 + 1] = w4.y; wh[4 * q4 + 2] = w4.z; wh[4 * q4 + 3] = w4.w;
+        }
+        float gam = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) gam += vh[ii] * wh[ii];
+        gam += __shfl_xor(gam, 32);
+        // D <- H D H = D - tau (v w^T + w v^T) + tau^2 (v^T w) v v^T  (lane: column l32)
+        const float tgv = tau * tau * gam * vo;
+        const uint32_t od = 4u * static_cast<uint32_t>(r0 * BWS + h * 16 * (BWS + 1) - l32);
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+          const int a = h * 16 + ii;
+          const float nd = dcur[ii] - tau * (vh[ii] * wo + wh[ii] * vo) + tgv * vh[ii];
+          bstore(band, l32 <= a ? od + ii * RS : kOut, nd);
+        }
+      }
+      if (g.r1 < g.hi) {
+        // below block (rows r1 .., columns r0 .. r1-1) from the right (lane: row l32)
+        float bi[16];
+        wave_lds_sync();
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) bi[ii] = Ft[l32 * TLD + h * 16 + ii];
+        if (tau != 0.f) {
+          float zr = 0.f;
+#pragma unroll
+          for (int ii = 0; ii < 16; ++ii) zr += bi[ii] * vh[ii];
+          zr += __shfl_xor(zr, 32);
+          const float tz = tau * zr;
+#pragma unroll
+          for (int ii = 0; ii < 16; ++ii) {
+            bi[ii] -= tz * vh[ii];
+            Ft[l32 * TLD + h * 16 + ii] = bi[ii];
+          }
+        }
+        if (h == 0) sm.x[l32] = bi[0];             // the next step's column (zero past hi)
+        if (g.last) {
+          wave_lds_sync();
+          const uint32_t ob = 4u * static_cast<uint32_t>(g.r1 * BWS + h * 16 * (BWS + 1) + SBW - l32);
+#pragma unroll
+          for (int ii = 0; ii < 16; ++ii) bstore(band, ob + ii * RS, Ft[(h * 16 + ii) * TLD + l32]);
+        }
+      }
+      cur ^= 1;
     }
     __syncthreads();
   }
@@ -465,7 +586,7 @@ size_t syev_top_work_bytes(int64_t n, int R, int batch) { return syev_layout(n, 
 
 hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam_out, void* work,
                     hipStream_t s) {
-  if (n % SBW != 0 || R < 1 || R > n) return hipErrorInvalidValue;
+  if (n % SBW != 0 || n > 32768 || R < 1 || R > n) return hipErrorInvalidValue;
   const SyevLayout Lw = syev_layout(n, R, batch);
   char* wb = static_cast<char*>(work);
   float* Vst = reinterpret_cast<float*>(wb + Lw.v_off);
@@ -553,12 +674,26 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     if (blocks > 4096) blocks = 4096;
     k_band_init<<<dim3(static_cast<unsigned>(blocks), batch), 256, 0, s>>>(A, n, Bw);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    // sweeps in flight: 8 waves up to 32 steps per sweep (n <= 1026), else 16
     const int64_t K0 = sweep_steps(n, 0);
-    int S = static_cast<int>((K0 + SW - 1) / SW);
-    if (S < 3) S = 3;
+    const int nw = K0 > 32 ? 16 : 8;
+    int S = static_cast<int>((K0 + nw - 1) / nw);
+    if (S < 4) S = 4;
+    const size_t lds = static_cast<size_t>(nw) * sizeof(ChaseLds);
+    static bool attr = false;
+    if (!attr) {
+      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chase<8>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, 16 * sizeof(ChaseLds))) != hipSuccess)
+        return e;
+      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chase<16>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, 16 * sizeof(ChaseLds))) != hipSuccess)
+        return e;
+      attr = true;
+    }
     {
       ProfScope ps("chase", s);
-      k_chase<<<batch, SW * 64, 0, s>>>(Bw, n, Rf, Lw.nref * RFS, S);
+      if (nw == 8) k_chase<8><<<batch, 8 * 64, lds, s>>>(Bw, static_cast<int>(n), Rf, Lw.nref * RFS, S);
+      else k_chase<16><<<batch, 16 * 64, lds, s>>>(Bw, static_cast<int>(n), Rf, Lw.nref * RFS, S);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     int64_t tb = (n + 255) / 256;
