@@ -11,6 +11,8 @@
 #include "device.hpp"
 #include "kernels.hpp"
 
+#include <utility>
+
 namespace jolt {
 
 namespace {
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
     float acc = 0.f;
     for (int kz = 0; kz < g.ksplit; ++kz) acc += p[kz * MN];
     const int64_t m = i / g.N, n = i % g.N;
-    if (g.c_lower && m < n) continue;
+    if (g.c_lower > 0 ? m < n : (g.c_lower < 0 && m > n)) continue;
     float v = g.alpha * acc;
     if (g.col_scale) v *= g.col_scale[z * g.col_scale_batch + n];
     const int64_t off = z * g.c_batch + m * g.c_m + n * g.c_n;
@@ -249,6 +251,222 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
       static_cast<uint16_t*>(g.C)[off] = f32_to_bf16_rne(v);
     }
   }
+}
+
+// ---------------------------------------------------------------- 128 x 128 tiles
+// Large products on bf16 matrix cores: 128 x 128 output tiles, K tiles of 64,
+// four waves of 64 x 64 (2 x 2 blocks of MFMA 32x32x16).  LDS keeps each
+// operand tile k-contiguous per row ([row][k], 144-byte rows) with the
+// 16-byte chunk index XOR-swizzled by (row / 8) % 8, which keeps the fragment
+// reads (one chunk per lane) and the transposing writes free of bank
+// conflicts.  Operands in memory:
+//   kOpBfK   bf16, k contiguous: 16-byte loads along k;
+//   kOpBfM   bf16, rows contiguous: 16-byte loads along the rows, transposed
+//            in registers (four k by eight rows per thread) on the way to LDS;
+//   kOpF32K  fp32, k contiguous: split into bf16 planes hi = rne(x),
+//            lo = rne(x - hi), so x = hi + lo to 2^-17 relative; the product
+//            takes hi B + lo B (or A hi + A lo): exact bf16 products summed in
+//            fp32, ~2^-17 relative error per term (fp32 operands: 2^-24).
+// The next K tile's global loads are issued before the current tile's MFMAs.
+constexpr int XT = 128, XK = 64, XKP = XK + 8;
+enum { kOpBfK = 0, kOpBfM = 1, kOpF32K = 2 };
+
+__device__ __forceinline__ int xswz(int row, int chunk) { return chunk ^ ((row >> 3) & 7); }
+
+template <int MODE> struct XRegs { uint4 v[4]; };
+template <> struct XRegs<kOpF32K> { float4 v[8]; };
+
+// one operand's per-thread addressing (rows: M for A, N for B)
+struct XAddr {
+  const char* base;
+  int64_t roff[8];     // kOpBfK / kOpF32K: element offset of each row of this thread, -1 outside
+  int64_t rbase;       // kOpBfM: element offset of this thread's eight rows, -1 outside
+};
+
+template <int MODE>
+__device__ __forceinline__ void x_addr(XAddr& a, const char* base, const GemmDim& rd, int64_t r0, int64_t rows,
+                                       int tid) {
+  a.base = base;
+  if constexpr (MODE == kOpBfM) {
+    const int64_t r = r0 + 8 * (tid & 15);
+    a.rbase = r < rows ? dim_off(rd, r0) + 8 * (tid & 15) : -1;
+  } else {
+    constexpr int NR = MODE == kOpBfK ? 4 : 8, SH = MODE == kOpBfK ? 3 : 4;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int64_t r = r0 + (tid >> SH) + (XT / NR) * i;
+      a.roff[i] = r < rows ? dim_off(rd, r) : -1;
+    }
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void x_load(XRegs<MODE>& R, const XAddr& a, const GemmDim& kd, int64_t k0, int tid) {
+  if constexpr (MODE == kOpBfK) {
+    const int64_t kb = dim_off(kd, k0) + 8 * (tid & 7);
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(a.base);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      R.v[i] = a.roff[i] >= 0 ? *reinterpret_cast<const uint4*>(p + a.roff[i] + kb) : make_uint4(0, 0, 0, 0);
+  } else if constexpr (MODE == kOpBfM) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(a.base);
+    const int64_t kk = k0 + 4 * (tid >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      R.v[i] = a.rbase >= 0 ? *reinterpret_cast<const uint4*>(p + a.rbase + dim_off(kd, kk + i))
+                            : make_uint4(0, 0, 0, 0);
+  } else {
+    const int64_t kb = dim_off(kd, k0) + 4 * (tid & 15);
+    const float* p = reinterpret_cast<const float*>(a.base);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      R.v[i] = a.roff[i] >= 0 ? *reinterpret_cast<const float4*>(p + a.roff[i] + kb) : make_float4(0, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ uint32_t x_half(const uint4& v, int e) {    // 16-bit element e of eight
+  const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+__device__ __forceinline__ void x_split(float x, uint32_t& hi, uint32_t& lo) {
+  const uint16_t h = f32_to_bf16_rne(x);
+  hi = h;
+  lo = f32_to_bf16_rne(x - bf16_bits_to_f32(h));
+}
+
+template <int MODE>
+__device__ __forceinline__ void x_store(const XRegs<MODE>& R, uint16_t (*Sh)[XKP], uint16_t (*Sl)[XKP], int tid) {
+  if constexpr (MODE == kOpBfK) {
+    const int kc = tid & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (tid >> 3) + 32 * i;
+      *reinterpret_cast<uint4*>(&Sh[row][xswz(row, kc) * 8]) = R.v[i];
+    }
+  } else if constexpr (MODE == kOpBfM) {
+    const int mc = tid & 15, kg = tid >> 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = 8 * mc + e;
+      uint2 w;
+      w.x = x_half(R.v[0], e) | (x_half(R.v[1], e) << 16);
+      w.y = x_half(R.v[2], e) | (x_half(R.v[3], e) << 16);
+      *reinterpret_cast<uint2*>(&Sh[row][xswz(row, kg >> 1) * 8 + (kg & 1) * 4]) = w;
+    }
+  } else {
+    const int kc4 = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = (tid >> 4) + 16 * i;
+      uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+      x_split(R.v[i].x, h0, l0); x_split(R.v[i].y, h1, l1);
+      x_split(R.v[i].z, h2, l2); x_split(R.v[i].w, h3, l3);
+      const int col = xswz(row, kc4 >> 1) * 8 + (kc4 & 1) * 4;
+      *reinterpret_cast<uint2*>(&Sh[row][col]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+      *reinterpret_cast<uint2*>(&Sl[row][col]) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+    }
+  }
+}
+
+template <int AM, int BMODE>
+__global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
+  constexpr bool AS = AM == kOpF32K, BS = BMODE == kOpF32K;
+  __shared__ __attribute__((aligned(16))) uint16_t As[AS ? 2 : 1][XT][XKP];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BS ? 2 : 1][XT][XKP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * XT;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * XT;
+  // tile wholly outside the kept triangle (c_lower > 0: m >= n; < 0: m <= n)
+  if (g.c_lower > 0 ? m0 + XT <= n0 : (g.c_lower < 0 && n0 + XT <= m0)) return;
+  const int64_t zz = blockIdx.z;
+  const int64_t z = zz / g.ksplit, kz = zz % g.ksplit;
+  const int64_t kbeg = kz * g.kchunk;
+  const int64_t kend = (kbeg + g.kchunk < g.K) ? kbeg + g.kchunk : g.K;
+  const size_t ea = AS ? 4 : 2, eb = BS ? 4 : 2;
+  const char* Ab = g.a_ptrs ? static_cast<const char*>(g.a_ptrs[z])
+                            : static_cast<const char*>(g.A) + z * g.a_batch * static_cast<int64_t>(ea);
+  const char* Bb = g.b_ptrs ? static_cast<const char*>(g.b_ptrs[z])
+                            : static_cast<const char*>(g.B) + z * g.b_batch * static_cast<int64_t>(eb);
+  XAddr pa, pb;
+  x_addr<AM>(pa, Ab, g.am, m0, g.M, tid);
+  x_addr<BMODE>(pb, Bb, g.bn, n0, g.N, tid);
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int r = lane & 31, half = lane >> 5;
+  f32x16 acc[2][2] = {};
+  XRegs<AM> ra;
+  XRegs<BMODE> rb;
+  if (kbeg < kend) {
+    x_load<AM>(ra, pa, g.ak, kbeg, tid);
+    x_load<BMODE>(rb, pb, g.bk, kbeg, tid);
+  }
+  for (int64_t k0 = kbeg; k0 < kend; k0 += XK) {
+    x_store<AM>(ra, As[0], As[AS ? 1 : 0], tid);
+    x_store<BMODE>(rb, Bs[0], Bs[BS ? 1 : 0], tid);
+    __syncthreads();
+    if (k0 + XK < kend) {
+      x_load<AM>(ra, pa, g.ak, k0 + XK, tid);
+      x_load<BMODE>(rb, pb, g.bk, k0 + XK, tid);
+    }
+#pragma unroll
+    for (int kk = 0; kk < XK / 16; ++kk) {
+      const int ch = 2 * kk + half;
+      bf16x8 a[2], b[2], al[2], bl[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int ra_ = wm + 32 * i + r, rb_ = wn + 32 * i + r;
+        a[i] = *reinterpret_cast<const bf16x8*>(&As[0][ra_][xswz(ra_, ch) * 8]);
+        b[i] = *reinterpret_cast<const bf16x8*>(&Bs[0][rb_][xswz(rb_, ch) * 8]);
+        if constexpr (AS) al[i] = *reinterpret_cast<const bf16x8*>(&As[AS ? 1 : 0][ra_][xswz(ra_, ch) * 8]);
+        if constexpr (BS) bl[i] = *reinterpret_cast<const bf16x8*>(&Bs[BS ? 1 : 0][rb_][xswz(rb_, ch) * 8]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          if constexpr (AS) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], b[j], acc[i][j], 0, 0, 0);
+          if constexpr (BS) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bl[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+  }
+  if (g.ksplit > 1) {   // partial sums, reduced in a fixed order by k_splitk_reduce
+    float* Pp = g.partial + (z * g.ksplit + kz) * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t m = m0 + wm + 32 * i + (e >> 2) * 8 + half * 4 + (e & 3);
+          const int64_t n = n0 + wn + 32 * j + r;
+          if (m < g.M && n < g.N) Pp[m * g.N + n] = acc[i][j][e];
+        }
+    return;
+  }
+  char* Cb = static_cast<char*>(g.C);
+  const int64_t cz = z * g.c_batch;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + wm + 32 * i + (e >> 2) * 8 + half * 4 + (e & 3);
+        const int64_t n = n0 + wn + 32 * j + r;
+        if (m < g.M && n < g.N && (g.c_lower == 0 || (g.c_lower > 0 ? m >= n : m <= n))) {
+          float v = g.alpha * acc[i][j][e];
+          if (g.col_scale) v *= g.col_scale[z * g.col_scale_batch + n];
+          const int64_t off = cz + m * g.c_m + n * g.c_n;
+          if (g.c_dtype == kF32) {
+            float* C = reinterpret_cast<float*>(Cb);
+            if (g.beta != 0.f) v += g.beta * C[off];
+            C[off] = v;
+          } else {
+            reinterpret_cast<uint16_t*>(Cb)[off] = f32_to_bf16_rne(v);
+          }
+        }
+      }
 }
 
 // ---------------------------------------------------------------- misc
@@ -340,15 +558,16 @@ __global__ __launch_bounds__(256) void k_pad_copy(const float* in, int64_t n, in
   }
 }
 
-// G_D = sum over heads of the D x D diagonal blocks of the dual Gram C (HD x HD).
+// G_D = sum over heads of the D x D diagonal blocks of the dual Gram C (HD x HD,
+// symmetric, column-major; only its lower triangle is read).
 __global__ __launch_bounds__(256) void k_sum_diag_blocks(const float* C, int64_t H, int64_t D,
                                                           float* GD) {
   const int64_t z = blockIdx.y, HD = H * D;
   const float* c = C + z * HD * HD;
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < D * D; i += 256ll * gridDim.x) {
-    const int64_t r = i / D, k = i % D;
+    const int64_t r = i / D, k = i % D, lo = r < k ? r : k, hi = r < k ? k : r;
     float s = 0.f;
-    for (int64_t h = 0; h < H; ++h) s += c[(h * D + r) * HD + h * D + k];
+    for (int64_t h = 0; h < H; ++h) s += c[(h * D + lo) * HD + h * D + hi];
     GD[z * D * D + i] = s;
   }
 }
@@ -358,11 +577,67 @@ int grid1(int64_t n, int cap = 4096) {
   return static_cast<int>(b < 1 ? 1 : (b > cap ? cap : b));
 }
 
+// Operand mode for the 128 x 128 kernel (rows rd, contraction kd), or -1.
+int x_mode(int dtype, const GemmDim& rd, const GemmDim& kd, int64_t rows, bool use_ptrs, bool ptrs_aligned,
+           const void* base, int64_t batch_stride) {
+  const int64_t q = dtype == kBF16 ? 8 : 4;     // elements per 16 bytes
+  auto mult = [](int64_t v, int64_t m) { return v % m == 0; };
+  auto within = [](const GemmDim& d, int64_t t) { return d.len == INT64_MAX || d.len % t == 0; };
+  auto seg16 = [&](const GemmDim& d) { return d.len == INT64_MAX || mult(d.seg, q); };
+  if (use_ptrs ? !ptrs_aligned : ((reinterpret_cast<uintptr_t>(base) & 15) != 0 || !mult(batch_stride, q)))
+    return -1;
+  if (kd.stride == 1 && within(kd, XK) && seg16(kd) && mult(rd.stride, q) && seg16(rd))
+    return dtype == kBF16 ? kOpBfK : kOpF32K;
+  if (dtype == kBF16 && rd.stride == 1 && within(rd, XT) && seg16(rd) && mult(rows, 8) && within(kd, XK) &&
+      mult(kd.stride, q) && seg16(kd))
+    return kOpBfM;
+  return -1;
+}
+
+template <int AM>
+void launch_x_b(const GemmArgs& g, int xb, dim3 grid, hipStream_t s) {
+  if (xb == kOpBfK) k_gemm_x<AM, kOpBfK><<<grid, 256, 0, s>>>(g);
+  else if (xb == kOpBfM) k_gemm_x<AM, kOpBfM><<<grid, 256, 0, s>>>(g);
+  else if constexpr (AM != kOpF32K) k_gemm_x<AM, kOpF32K><<<grid, 256, 0, s>>>(g);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s) {
   GemmArgs g = g0;
   if (g.ksplit < 1 || !g.partial) g.ksplit = 1;
+  ProfScope ps("gemm", s);
+  if (prof_enabled("gemm")) {   // dense flops; operands once, C written (and read when beta != 0) once
+    const double ea = g.a_dtype == kBF16 ? 2 : 4, eb = g.b_dtype == kBF16 ? 2 : 4;
+    const double ec = g.c_dtype == kBF16 ? 2 : 4;
+    prof_add_work("gemm",
+                  batch * (g.M * g.K * ea + g.K * g.N * eb + g.M * g.N * ec * (g.beta != 0.f ? 2 : 1)),
+                  2.0 * g.M * g.N * g.K * batch);
+  }
+  // 128 x 128 bf16 matrix-core tiles when the operands allow 16-byte loads
+  // (at least one of them bf16); a column-major C is produced as the
+  // row-major C^T = B^T A^T so that its stores run along rows
+  if (!g.a_sym && g.K % XK == 0 && (g.a_dtype == kBF16 || g.b_dtype == kBF16)) {
+    GemmArgs x = g;
+    if (x.c_m == 1 && x.c_n != 1 && !x.col_scale) {
+      std::swap(x.M, x.N); std::swap(x.A, x.B); std::swap(x.a_dtype, x.b_dtype);
+      std::swap(x.am, x.bn); std::swap(x.ak, x.bk); std::swap(x.a_batch, x.b_batch);
+      std::swap(x.a_ptrs, x.b_ptrs); std::swap(x.c_m, x.c_n);
+      x.c_lower = -x.c_lower;                          // m >= n of C is m <= n of C^T
+    }
+    const int xa = x_mode(x.a_dtype, x.am, x.ak, x.M, x.a_ptrs != nullptr, x.ptr_align16 != 0, x.A, x.a_batch);
+    const int xb = x_mode(x.b_dtype, x.bn, x.bk, x.N, x.b_ptrs != nullptr, x.ptr_align16 != 0, x.B, x.b_batch);
+    if (xa >= 0 && xb >= 0 && !(xa == kOpF32K && xb == kOpF32K)) {
+      x.kchunk = (x.K + x.ksplit - 1) / x.ksplit;
+      x.kchunk = (x.kchunk + XK - 1) / XK * XK;
+      dim3 grid((x.M + XT - 1) / XT, (x.N + XT - 1) / XT, batch * x.ksplit);
+      if (xa == kOpBfK) launch_x_b<kOpBfK>(x, xb, grid, s);
+      else if (xa == kOpBfM) launch_x_b<kOpBfM>(x, xb, grid, s);
+      else launch_x_b<kOpF32K>(x, xb, grid, s);
+      if (x.ksplit > 1) k_splitk_reduce<<<dim3(grid1(x.M * x.N), batch), 256, 0, s>>>(x);
+      return hipGetLastError();
+    }
+  }
   // bf16 x bf16 on bf16 matrix cores when every segmented dimension keeps a
   // 32-wide k tile inside one segment
   auto seg_ok = [](const GemmDim& d) { return d.len == INT64_MAX || d.len % BK16 == 0; };
@@ -372,14 +647,6 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s) {
   g.kchunk = (g.K + g.ksplit - 1) / g.ksplit;
   g.kchunk = (g.kchunk + kt - 1) / kt * kt;            // chunks start on tile edges
   dim3 grid((g.M + BM - 1) / BM, (g.N + BN - 1) / BN, batch * g.ksplit);
-  ProfScope ps("gemm", s);
-  if (prof_enabled("gemm")) {   // dense flops; operands once, C written (and read when beta != 0) once
-    const double ea = g.a_dtype == kBF16 ? 2 : 4, eb = g.b_dtype == kBF16 ? 2 : 4;
-    const double ec = g.c_dtype == kBF16 ? 2 : 4;
-    prof_add_work("gemm",
-                  batch * (g.M * g.K * ea + g.K * g.N * eb + g.M * g.N * ec * (g.beta != 0.f ? 2 : 1)),
-                  2.0 * g.M * g.N * g.K * batch);
-  }
   if (bf) k_gemm_bf16<<<grid, 256, 0, s>>>(g);
   else if (g.a_dtype == kBF16 && g.b_dtype == kBF16) k_gemm<uint16_t, uint16_t><<<grid, 256, 0, s>>>(g);
   else if (g.a_dtype == kBF16) k_gemm<uint16_t, float><<<grid, 256, 0, s>>>(g);

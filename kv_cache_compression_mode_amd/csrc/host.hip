@@ -402,6 +402,7 @@ struct AllocWS {
   // persistent
   float* UT; float* UD; double* lamT; double* lamD; double* frob2;
   const void** xptrs; uint64_t* tags;
+  bool x16;            // every input tensor is 16-byte aligned
   // scratch (chunk tensors)
   float* G; float* V; float* J; int* active; int* rot; float* tauabs; double* offp;
   float* GDpart;
@@ -620,7 +621,7 @@ void token_finalize(const Dims& d, int batch, int t0, const AllocWS& w, int xdt,
   GemmArgs g = gemm0();
   g.M = R; g.N = HD; g.K = T;
   g.A = w.Ucm; g.am = plain(T); g.ak = plain(1); g.a_batch = T * R;
-  g.b_ptrs = reinterpret_cast<const void* const*>(w.xptrs); g.b_dtype = xdt;
+  g.b_ptrs = reinterpret_cast<const void* const*>(w.xptrs); g.b_dtype = xdt; g.ptr_align16 = w.x16;
   g.bk = plain(D); g.bn = segmented(D, T * D, 1);
   g.C = w.P; g.c_m = HD; g.c_n = 1; g.c_batch = R * HD;
   ck(launch_gemm(g, batch, s));
@@ -634,7 +635,7 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   const void* const* xp = reinterpret_cast<const void* const*>(w.xptrs);
   ck(hipMemsetAsync(w.G, 0, sizeof(float) * batch * n * n, s));
   GemmArgs g = gemm0();
-  g.a_ptrs = xp; g.b_ptrs = xp; g.a_dtype = g.b_dtype = xdt;
+  g.a_ptrs = xp; g.b_ptrs = xp; g.a_dtype = g.b_dtype = xdt; g.ptr_align16 = w.x16;
   if (d.dual) {   // C = X_(T)^T X_(T), HD x HD
     g.M = HD; g.N = HD; g.K = T;
     g.am = segmented(D, T * D, 1); g.ak = plain(D);
@@ -644,13 +645,15 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     g.am = plain(D); g.ak = segmented(D, T * D, 1);
     g.bk = segmented(D, T * D, 1); g.bn = plain(D);
   }
-  g.C = w.G; g.c_m = n; g.c_n = 1; g.c_batch = n * n;
+  // column-major; the tridiagonal path reads the lower triangle only
+  g.C = w.G; g.c_m = 1; g.c_n = n; g.c_batch = n * n;
+  g.c_lower = eig_jacobi() ? 0 : 1;
   ck(launch_gemm(g, batch, s));
   if (d.dual) {
     ck(launch_sum_diag_blocks(w.G, d.H, D, w.GD, batch, s));   // n == HD here
   } else {
     GemmArgs gd = gemm0();
-    gd.a_ptrs = xp; gd.b_ptrs = xp; gd.a_dtype = gd.b_dtype = xdt;
+    gd.a_ptrs = xp; gd.b_ptrs = xp; gd.a_dtype = gd.b_dtype = xdt; gd.ptr_align16 = w.x16;
     gd.M = D; gd.N = D; gd.K = d.H * T;
     gd.am = plain(1); gd.ak = plain(D); gd.bk = plain(D); gd.bn = plain(1);
     gd.C = w.GD; gd.c_m = D; gd.c_n = 1; gd.c_batch = D * D;
@@ -681,7 +684,7 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   } else if (d.dual) {
     // U' = X_(T) V_R (T x R, column-major)
     GemmArgs gu = gemm0();
-    gu.a_ptrs = xp; gu.a_dtype = xdt;
+    gu.a_ptrs = xp; gu.a_dtype = xdt; gu.ptr_align16 = w.x16;
     gu.M = T; gu.N = R; gu.K = HD;
     gu.am = plain(D); gu.ak = segmented(D, T * D, 1);
     gu.B = VR; gu.bk = plain(1); gu.bn = plain(ldv); gu.b_batch = vr_batch;
@@ -701,7 +704,7 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   // feature mode: exact Gram path (a sketch of width D spans all of R^D)
   {
     GemmArgs gd = gemm0();
-    gd.a_ptrs = xp; gd.b_ptrs = xp; gd.a_dtype = gd.b_dtype = xdt;
+    gd.a_ptrs = xp; gd.b_ptrs = xp; gd.a_dtype = gd.b_dtype = xdt; gd.ptr_align16 = w.x16;
     gd.M = D; gd.N = D; gd.K = d.H * T;
     gd.am = plain(1); gd.ak = plain(D); gd.bk = plain(D); gd.bn = plain(1);
     gd.C = w.GD; gd.c_m = D; gd.c_n = 1; gd.c_batch = D * D;
@@ -714,7 +717,7 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   auto AY = [&](const float* Bsrc, int64_t ldb, bool b_rowmajor, float* out) {
     // out (T x ell, column-major) = X_(T) B, B is HD x ell
     GemmArgs g = gemm0();
-    g.a_ptrs = xp; g.a_dtype = xdt;
+    g.a_ptrs = xp; g.a_dtype = xdt; g.ptr_align16 = w.x16;
     g.M = T; g.N = ell; g.K = HD;
     g.am = plain(D); g.ak = segmented(D, T * D, 1);
     g.B = Bsrc;
@@ -728,7 +731,7 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   ck(householder_qr(w.Y, T, ell, T, T * ell, batch, w.qtau, s));
   for (int it = 0; it < q; ++it) {
     GemmArgs g = gemm0();                       // Z = X_(T)^T Q (HD x ell, column-major)
-    g.a_ptrs = xp; g.a_dtype = xdt;
+    g.a_ptrs = xp; g.a_dtype = xdt; g.ptr_align16 = w.x16;
     g.M = HD; g.N = ell; g.K = T;
     g.am = segmented(D, T * D, 1); g.ak = plain(D);
     g.B = w.Y; g.bk = plain(1); g.bn = plain(T); g.b_batch = T * ell;
@@ -742,7 +745,7 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     GemmArgs g = gemm0();                       // B = Q^T X_(T) (ell x HD, row-major)
     g.M = ell; g.N = HD; g.K = T;
     g.A = w.Y; g.am = plain(T); g.ak = plain(1); g.a_batch = T * ell;
-    g.b_ptrs = xp; g.b_dtype = xdt; g.bk = plain(D); g.bn = segmented(D, T * D, 1);
+    g.b_ptrs = xp; g.b_dtype = xdt; g.bk = plain(D); g.bn = segmented(D, T * D, 1); g.ptr_align16 = w.x16;
     g.C = w.Bm; g.c_m = HD; g.c_n = 1; g.c_batch = ell * HD;
     ck(launch_gemm(g, batch, s));
   }
@@ -935,8 +938,10 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, v
   const int nt = 2 * req->n_layers;
   for (int i = 0; i < nt; ++i)
     if (!x_dev[i]) return JOLT_EINVAL;
-  const AllocWS w = carve_alloc(req, ws_dev);
+  AllocWS w = carve_alloc(req, ws_dev);
   if (ws_bytes < w.bytes) return JOLT_ENOSPACE;
+  w.x16 = true;
+  for (int i = 0; i < nt; ++i) w.x16 = w.x16 && (reinterpret_cast<uintptr_t>(x_dev[i]) & 15) == 0;
   return guard([&]() -> jolt_status {
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Dims d = dims_of(req);

@@ -45,8 +45,11 @@ struct GemmArgs {
   int ksplit; float* partial; int64_t kchunk;
   // symmetric operands stored as their lower triangle (fp32 path, plain
   // dimensions only): a_sym reads A(m, k) with m < k from A(k, m); c_lower
-  // computes and writes only C(m, n) with m >= n
+  // computes and writes only C(m, n) with m >= n (the launcher may pass -1,
+  // m <= n, to a kernel computing the transposed product)
   int a_sym, c_lower;
+  // the a_ptrs / b_ptrs entries are 16-byte aligned
+  int ptr_align16;
 };
 
 hipError_t launch_gemm(const GemmArgs& g, int batch, hipStream_t s);
