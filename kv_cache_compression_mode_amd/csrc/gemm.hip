@@ -276,51 +276,67 @@ __device__ __forceinline__ int xswz(int row, int chunk) { return chunk ^ ((row >
 template <int MODE> struct XRegs { uint4 v[4]; };
 template <> struct XRegs<kOpF32K> { float4 v[8]; };
 
-// one operand's per-thread addressing (rows: M for A, N for B)
+// One operand's addressing: a buffer resource on its batch entry, this
+// thread's byte offsets (rows and in-tile k; kXOut for rows past the end,
+// which read as zero) and the K tile's byte offset, advanced per tile with
+// scalar segment counters.  Every offset fits in 31 bits (checked at launch).
+constexpr uint32_t kXOut = 0x80000000u;
 struct XAddr {
-  const char* base;
-  int64_t roff[8];     // kOpBfK / kOpF32K: element offset of each row of this thread, -1 outside
-  int64_t rbase;       // kOpBfM: element offset of this thread's eight rows, -1 outside
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t vo[8];
+  int64_t kseg, kin;
 };
 
+__device__ __forceinline__ int64_t x_koff(const GemmDim& kd, const XAddr& a) {
+  return a.kseg * kd.seg + a.kin * kd.stride;
+}
+
 template <int MODE>
-__device__ __forceinline__ void x_addr(XAddr& a, const char* base, const GemmDim& rd, int64_t r0, int64_t rows,
-                                       int tid) {
-  a.base = base;
+__device__ __forceinline__ void x_addr(XAddr& a, const char* base, const GemmDim& rd, const GemmDim& kd,
+                                       int64_t r0, int64_t rows, int64_t kbeg, int tid) {
+  a.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, static_cast<int>(kXOut), 0x00020000);
+  if (kd.len == INT64_MAX) { a.kseg = 0; a.kin = kbeg; }
+  else { a.kseg = kbeg / kd.len; a.kin = kbeg % kd.len; }
   if constexpr (MODE == kOpBfM) {
     const int64_t r = r0 + 8 * (tid & 15);
-    a.rbase = r < rows ? dim_off(rd, r0) + 8 * (tid & 15) : -1;
+    const int64_t rb = dim_off(rd, r0) + 8 * (tid & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a.vo[i] = r < rows ? static_cast<uint32_t>(2 * (rb + (4 * (tid >> 4) + i) * kd.stride)) : kXOut;
   } else {
     constexpr int NR = MODE == kOpBfK ? 4 : 8, SH = MODE == kOpBfK ? 3 : 4;
+    constexpr int64_t E = MODE == kOpBfK ? 2 : 4;
+    const int64_t kl = MODE == kOpBfK ? 8 * (tid & 7) : 4 * (tid & 15);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int64_t r = r0 + (tid >> SH) + (XT / NR) * i;
-      a.roff[i] = r < rows ? dim_off(rd, r) : -1;
+      a.vo[i] = r < rows ? static_cast<uint32_t>(E * (dim_off(rd, r) + kl)) : kXOut;
     }
   }
 }
 
+__device__ __forceinline__ void x_next(XAddr& a, const GemmDim& kd) {
+  a.kin += XK;
+  if (a.kin == kd.len) { a.kin = 0; ++a.kseg; }
+}
+
 template <int MODE>
-__device__ __forceinline__ void x_load(XRegs<MODE>& R, const XAddr& a, const GemmDim& kd, int64_t k0, int tid) {
-  if constexpr (MODE == kOpBfK) {
-    const int64_t kb = dim_off(kd, k0) + 8 * (tid & 7);
-    const uint16_t* p = reinterpret_cast<const uint16_t*>(a.base);
+__device__ __forceinline__ void x_load(XRegs<MODE>& R, const XAddr& a, const GemmDim& kd) {
+  constexpr int64_t E = MODE == kOpF32K ? 4 : 2;
+  const int so = static_cast<int>(E * x_koff(kd, a));
+  if constexpr (MODE == kOpF32K) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      R.v[i] = a.roff[i] >= 0 ? *reinterpret_cast<const uint4*>(p + a.roff[i] + kb) : make_uint4(0, 0, 0, 0);
-  } else if constexpr (MODE == kOpBfM) {
-    const uint16_t* p = reinterpret_cast<const uint16_t*>(a.base);
-    const int64_t kk = k0 + 4 * (tid >> 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      R.v[i] = a.rbase >= 0 ? *reinterpret_cast<const uint4*>(p + a.rbase + dim_off(kd, kk + i))
-                            : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(a.rs, static_cast<int>(a.vo[i]), so, 0);
+      R.v[i] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                           __uint_as_float(v[3]));
+    }
   } else {
-    const int64_t kb = dim_off(kd, k0) + 4 * (tid & 15);
-    const float* p = reinterpret_cast<const float*>(a.base);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      R.v[i] = a.roff[i] >= 0 ? *reinterpret_cast<const float4*>(p + a.roff[i] + kb) : make_float4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(a.rs, static_cast<int>(a.vo[i]), so, 0);
+      R.v[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
   }
 }
 
@@ -388,24 +404,26 @@ __global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
   const char* Bb = g.b_ptrs ? static_cast<const char*>(g.b_ptrs[z])
                             : static_cast<const char*>(g.B) + z * g.b_batch * static_cast<int64_t>(eb);
   XAddr pa, pb;
-  x_addr<AM>(pa, Ab, g.am, m0, g.M, tid);
-  x_addr<BMODE>(pb, Bb, g.bn, n0, g.N, tid);
+  x_addr<AM>(pa, Ab, g.am, g.ak, m0, g.M, kbeg, tid);
+  x_addr<BMODE>(pb, Bb, g.bn, g.bk, n0, g.N, kbeg, tid);
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   const int r = lane & 31, half = lane >> 5;
   f32x16 acc[2][2] = {};
   XRegs<AM> ra;
   XRegs<BMODE> rb;
   if (kbeg < kend) {
-    x_load<AM>(ra, pa, g.ak, kbeg, tid);
-    x_load<BMODE>(rb, pb, g.bk, kbeg, tid);
+    x_load<AM>(ra, pa, g.ak);
+    x_load<BMODE>(rb, pb, g.bk);
   }
   for (int64_t k0 = kbeg; k0 < kend; k0 += XK) {
     x_store<AM>(ra, As[0], As[AS ? 1 : 0], tid);
     x_store<BMODE>(rb, Bs[0], Bs[BS ? 1 : 0], tid);
     __syncthreads();
     if (k0 + XK < kend) {
-      x_load<AM>(ra, pa, g.ak, k0 + XK, tid);
-      x_load<BMODE>(rb, pb, g.bk, k0 + XK, tid);
+      x_next(pa, g.ak);
+      x_next(pb, g.bk);
+      x_load<AM>(ra, pa, g.ak);
+      x_load<BMODE>(rb, pb, g.bk);
     }
 #pragma unroll
     for (int kk = 0; kk < XK / 16; ++kk) {
@@ -578,13 +596,22 @@ int grid1(int64_t n, int cap = 4096) {
 }
 
 // Operand mode for the 128 x 128 kernel (rows rd, contraction kd), or -1.
-int x_mode(int dtype, const GemmDim& rd, const GemmDim& kd, int64_t rows, bool use_ptrs, bool ptrs_aligned,
-           const void* base, int64_t batch_stride) {
+int x_mode(int dtype, const GemmDim& rd, const GemmDim& kd, int64_t rows, int64_t kext, bool use_ptrs,
+           bool ptrs_aligned, const void* base, int64_t batch_stride) {
   const int64_t q = dtype == kBF16 ? 8 : 4;     // elements per 16 bytes
   auto mult = [](int64_t v, int64_t m) { return v % m == 0; };
   auto within = [](const GemmDim& d, int64_t t) { return d.len == INT64_MAX || d.len % t == 0; };
   auto seg16 = [&](const GemmDim& d) { return d.len == INT64_MAX || mult(d.seg, q); };
   if (use_ptrs ? !ptrs_aligned : ((reinterpret_cast<uintptr_t>(base) & 15) != 0 || !mult(batch_stride, q)))
+    return -1;
+  // every byte offset inside one batch entry below 2^31 (buffer addressing)
+  auto span = [](const GemmDim& d, int64_t n) {
+    if (n <= 0) return int64_t{0};
+    const int64_t i = n - 1;
+    return d.len == INT64_MAX ? i * d.stride : (i / d.len) * d.seg + (i % d.len) * d.stride;
+  };
+  if (rd.stride < 0 || kd.stride < 0 || rd.seg < 0 || kd.seg < 0 ||
+      (span(rd, rows + XT) + span(kd, kext) + 8) * (dtype == kBF16 ? 2 : 4) >= (int64_t{1} << 31))
     return -1;
   if (kd.stride == 1 && within(kd, XK) && seg16(kd) && mult(rd.stride, q) && seg16(rd))
     return dtype == kBF16 ? kOpBfK : kOpF32K;
@@ -625,8 +652,8 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s) {
       std::swap(x.a_ptrs, x.b_ptrs); std::swap(x.c_m, x.c_n);
       x.c_lower = -x.c_lower;                          // m >= n of C is m <= n of C^T
     }
-    const int xa = x_mode(x.a_dtype, x.am, x.ak, x.M, x.a_ptrs != nullptr, x.ptr_align16 != 0, x.A, x.a_batch);
-    const int xb = x_mode(x.b_dtype, x.bn, x.bk, x.N, x.b_ptrs != nullptr, x.ptr_align16 != 0, x.B, x.b_batch);
+    const int xa = x_mode(x.a_dtype, x.am, x.ak, x.M, x.K, x.a_ptrs != nullptr, x.ptr_align16 != 0, x.A, x.a_batch);
+    const int xb = x_mode(x.b_dtype, x.bn, x.bk, x.N, x.K, x.b_ptrs != nullptr, x.ptr_align16 != 0, x.B, x.b_batch);
     if (xa >= 0 && xb >= 0 && !(xa == kOpF32K && xb == kOpF32K)) {
       x.kchunk = (x.K + x.ksplit - 1) / x.ksplit;
       x.kchunk = (x.kchunk + XK - 1) / XK * XK;
