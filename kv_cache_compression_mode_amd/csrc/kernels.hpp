@@ -113,9 +113,12 @@ size_t syev_top_work_bytes(int64_t n, int R, int batch);
 hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam, void* work, hipStream_t s);
 hipError_t copy_cols(const float* in, int64_t ld_in, int64_t in_batch, float* out, int64_t ld_out,
                      int64_t out_batch, int64_t rows, int64_t cols, int batch, hipStream_t s);
+// write_r: when the panel fits one block (m - c0 <= panel_block_rows()), R
+// (upper triangle) is also written into the panel's top nb rows.
+int64_t panel_block_rows();
 hipError_t panel_factor(float* A, int64_t m, int64_t ld, int64_t bstride, int64_t c0, int nb, int batch,
                         float* Vp, int64_t vstride, float* Tp, int64_t tstride, float* taus, int64_t k,
-                        float* scratch, hipStream_t s);
+                        float* scratch, hipStream_t s, int write_r = 0);
 hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t batch_stride, int batch,
                           float* work, hipStream_t s);
 

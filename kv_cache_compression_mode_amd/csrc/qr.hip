@@ -179,16 +179,20 @@ constexpr int LW = LT / 64;      // waves
 constexpr int kStack = 32 * 32 * 32;   // per matrix: up to 32 leaves x 32 rows x 32 (Rs, Qt)
 
 // Wave sums of 32 per-lane values at once (a halving butterfly): lane l ends
-// with the total of value l >> 1.
-__device__ __forceinline__ float reduce32(float (&v)[32], int lane) {
+// with the total of value l >> 1.  The values travel as one 32-wide vector:
+// with a plain array the compiler turns the two-way pick of each stage into
+// an indexed access, which it then expands into compare/select ladders.
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+__device__ __forceinline__ float reduce32(f32x32 v, int lane) {
 #pragma unroll
   for (int cnt = 32, off = 32; cnt > 1; cnt >>= 1, off >>= 1) {
     const int h = cnt >> 1;
     const bool up = (lane & off) != 0;
 #pragma unroll
     for (int q = 0; q < h; ++q) {
-      const float send = up ? v[q] : v[q + h];
-      const float keep = up ? v[q + h] : v[q];
+      const float lo = v[q], hi = v[q + h];
+      const float send = up ? lo : hi;
+      const float keep = up ? hi : lo;
       v[q] = keep + __shfl_xor(send, off);
     }
   }
@@ -218,7 +222,7 @@ __device__ void lds_householder(float* P, int mr, int nb, LdsQr& L) {
     // one reduction per column: slot c != j gets sum_{i > j} P[c][i] x_i, slot j
     // gets sigma = sum_{i > j} x_i^2 (x = column j below the diagonal)
     const float x = (i > j && i < mr) ? P[j * kLeaf + i] : 0.f;
-    float part[32];
+    f32x32 part;
 #pragma unroll
     for (int c = 0; c < 32; ++c)
       part[c] = (c < nb && i > j && i < mr) ? (c == j ? x : P[c * kLeaf + i]) * x : 0.f;
@@ -369,6 +373,113 @@ __global__ __launch_bounds__(LT) void k_qr_block(const float* A, int64_t m, int6
         const float sg = c < nb ? L.sgn[c] : 1.f;     // beta_c = R_cc: flip so diag(R) >= 0
         qt[static_cast<int64_t>(i) * 32 + c] = sg * q[c];
       }
+    }
+  }
+}
+
+// Householder QR of one panel (mp = m - c0 <= kLeaf rows, nb <= 32 columns),
+// the panel's rows in registers (thread t holds rows t and t + RT).  Column
+// j: thread j publishes row j, one fused 32-slot reduction gives sigma (slot
+// j) and the raw dots sum_{i > j} P[c][i] x_i of every other column, and
+// every thread then forms tau, beta and d_c = P[c][j] + scale * raw_c itself:
+// the update of the later columns and column j of T (T[0:j, j] = -tau_j
+// T[0:j, 0:j] d), as in the LDS kernel, with two barriers per column.
+// Outputs are those of k_qr_block mode 0, plus (write_r) R in the panel's top
+// rows.
+constexpr int RT = kLeaf / 2, RW = RT / 64;
+__global__ __launch_bounds__(RT) void k_qr_reg(float* A, int64_t m, int64_t ld, int64_t bstride, int64_t c0,
+                                               int nb, float* Vp, int64_t vstride, float* Tp, int64_t tstride,
+                                               float* taus_g, int64_t k, int write_r) {
+  __shared__ float red[RW][32];
+  __shared__ __attribute__((aligned(16))) float raw[32];
+  __shared__ __attribute__((aligned(16))) float rowj[2][32];
+  __shared__ float Ts[32][33];
+  __shared__ float sgn[32];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int i0 = t, i1 = t + RT;
+  const int64_t z = blockIdx.y;
+  const int mr = static_cast<int>(m - c0);
+  float* Az = A + z * bstride;
+  float p0[32], p1[32];
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    p0[c] = (c < nb && i0 < mr) ? Az[(c0 + c) * ld + c0 + i0] : 0.f;
+    p1[c] = (c < nb && i1 < mr) ? Az[(c0 + c) * ld + c0 + i1] : 0.f;
+  }
+  for (int idx = t; idx < 32 * 33; idx += RT) (&Ts[0][0])[idx] = 0.f;
+  // fully unrolled (register indices must be compile-time); columns past nb skipped
+#pragma clang loop unroll(full)
+  for (int j = 0; j < 32; ++j) {
+    if (j >= nb) continue;
+    float* rj = rowj[j & 1];
+    if (t == j) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) rj[c] = p0[c];
+    }
+    const bool b0 = i0 > j && i0 < mr, b1 = i1 < mr;     // i1 >= RT > j
+    const float x0 = b0 ? p0[j] : 0.f, x1 = b1 ? p1[j] : 0.f;
+    f32x32 part;
+#pragma unroll
+    for (int c = 0; c < 32; ++c)
+      part[c] = c < nb ? (c == j ? x0 : p0[c]) * x0 + (c == j ? x1 : p1[c]) * x1 : 0.f;
+    const float tot = reduce32(part, lane);
+    if ((lane & 1) == 0) red[wave][lane >> 1] = tot;
+    __syncthreads();
+    if (t < 32) {
+      float u = 0.f;
+      for (int w = 0; w < RW; ++w) u += red[w][t];
+      raw[t] = u;
+    }
+    __syncthreads();
+    const float sigma = raw[j], alpha = rj[j];
+    float tau = 0.f, beta = alpha, scale = 0.f;
+    if (sigma > 0.f) {
+      const float nrm = sqrtf(alpha * alpha + sigma);
+      beta = alpha >= 0.f ? -nrm : nrm;
+      tau = (beta - alpha) / beta;
+      scale = 1.f / (alpha - beta);
+    }
+    const float v0 = (t == j) ? 1.f : (b0 ? x0 * scale : 0.f), v1 = b1 ? x1 * scale : 0.f;
+    if (tau != 0.f) {
+#pragma unroll
+      for (int c = j + 1; c < 32; ++c) {
+        if (c < nb) {
+          const float d = tau * (rj[c] + scale * raw[c]);
+          p0[c] -= v0 * d;
+          p1[c] -= v1 * d;
+        }
+      }
+    }
+    if (b0) p0[j] = v0;
+    if (t == j) p0[j] = beta;
+    if (b1) p1[j] = v1;
+    if (t < j) {
+      float u = 0.f;
+      for (int l = t; l < j; ++l) u += Ts[t][l] * (rj[l] + scale * raw[l]);
+      Ts[t][j] = -tau * u;
+    } else if (t == j) {
+      Ts[j][j] = tau;
+      sgn[j] = beta < 0.f ? -1.f : 1.f;
+    }
+  }
+  __syncthreads();
+  // V (explicit, zero above row c0, unit diagonal), T, tau / sign(beta)
+  float* V = Vp + z * vstride;
+  for (int64_t r = t; r < c0; r += RT)
+    for (int c = 0; c < 32; ++c) V[c * m + r] = 0.f;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    if (i0 < mr) V[c * m + c0 + i0] = (c >= nb || i0 < c) ? 0.f : (i0 == c ? 1.f : p0[c]);
+    if (i1 < mr) V[c * m + c0 + i1] = c >= nb ? 0.f : p1[c];
+  }
+  for (int idx = t; idx < 1024; idx += RT) Tp[z * tstride + idx] = Ts[idx / 32][idx % 32];
+  if (t < nb) {
+    taus_g[z * 2 * k + c0 + t] = Ts[t][t];
+    taus_g[z * 2 * k + k + c0 + t] = sgn[t];
+    if (write_r && t < mr) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        if (c >= t && c < nb) Az[(c0 + c) * ld + c0 + t] = p0[c];
     }
   }
 }
@@ -629,9 +740,11 @@ size_t panel_factor_scratch_floats(int64_t m, int batch) {
   return static_cast<size_t>(batch) * (m * 32 + 2 * kStack + 1024);
 }
 
+int64_t panel_block_rows() { return kLeaf; }
+
 hipError_t panel_factor(float* A, int64_t m, int64_t ld, int64_t bstride, int64_t c0, int nb, int batch,
                         float* Vp, int64_t vstride, float* Tp, int64_t tstride, float* taus, int64_t k,
-                        float* scratch, hipStream_t s) {
+                        float* scratch, hipStream_t s, int write_r) {
   static bool lds_attr = false;
   if (!lds_attr) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_qr_block),
@@ -650,8 +763,7 @@ hipError_t panel_factor(float* A, int64_t m, int64_t ld, int64_t bstride, int64_
   const size_t lds = 32 * kLeaf * sizeof(float);
   hipError_t e;
   if (nl <= 1) {
-    k_qr_block<<<dim3(1, batch), LT, lds, s>>>(A, m, ld, bstride, c0, nb, 0, 1, mp, Vp, vstride, Tp, tstride,
-                                               taus, k, Qb, Rs, Qt, m * 32);
+    k_qr_reg<<<dim3(1, batch), RT, 0, s>>>(A, m, ld, bstride, c0, nb, Vp, vstride, Tp, tstride, taus, k, write_r);
   } else if (nl <= 32) {
     const int64_t rl = (mp + nl - 1) / nl;
     k_qr_block<<<dim3(static_cast<unsigned>(nl), batch), LT, lds, s>>>(

@@ -638,15 +638,20 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     float* V = Vst + voff[p];
     float* T = Tst + p * 1024;
     const int64_t vs = Lw.vtot, ts = Lw.P * 1024;
-    if ((e = panel_factor(panel, mp, n, nn, 0, SBW, batch, V, vs, T, ts, taus, SBW, pscr, s)) != hipSuccess)
+    // R into the panel's top rows: by the panel kernel when the panel is one
+    // block, else as panel_top -= V_top (T^T (V^T panel))
+    const bool r_in = mp <= panel_block_rows();
+    if ((e = panel_factor(panel, mp, n, nn, 0, SBW, batch, V, vs, T, ts, taus, SBW, pscr, s, r_in ? 1 : 0)) !=
+        hipSuccess)
       return e;
-    // R = top rows of H^T panel: panel_top -= V_top (T^T (V^T panel))
-    if ((e = gemm(SBW, SBW, mp, V, plain(mp), plain(1), vs, panel, plain(1), plain(n), nn, S1, SBW, 1, 1024, 1.f,
-                  0.f, ksplit_for(mp))) != hipSuccess) return e;
-    if ((e = gemm(SBW, SBW, SBW, T, plain(1), plain(SBW), ts, S1, plain(SBW), plain(1), 1024, S2, SBW, 1, 1024,
-                  1.f, 0.f)) != hipSuccess) return e;
-    if ((e = gemm(SBW, SBW, SBW, V, plain(1), plain(mp), vs, S2, plain(SBW), plain(1), 1024, panel, 1, n, nn,
-                  -1.f, 1.f)) != hipSuccess) return e;
+    if (!r_in) {
+      if ((e = gemm(SBW, SBW, mp, V, plain(mp), plain(1), vs, panel, plain(1), plain(n), nn, S1, SBW, 1, 1024, 1.f,
+                    0.f, ksplit_for(mp))) != hipSuccess) return e;
+      if ((e = gemm(SBW, SBW, SBW, T, plain(1), plain(SBW), ts, S1, plain(SBW), plain(1), 1024, S2, SBW, 1, 1024,
+                    1.f, 0.f)) != hipSuccess) return e;
+      if ((e = gemm(SBW, SBW, SBW, V, plain(1), plain(mp), vs, S2, plain(SBW), plain(1), 1024, panel, 1, n, nn,
+                    -1.f, 1.f)) != hipSuccess) return e;
+    }
     float* A22 = A + r * n + r;
     // X = A22 V T, into the W half of VW
     const int64_t vwb = n * 2 * SBW;
