@@ -378,14 +378,16 @@ __global__ __launch_bounds__(LT) void k_qr_block(const float* A, int64_t m, int6
 }
 
 // Householder QR of one panel (mp = m - c0 <= kLeaf rows, nb <= 32 columns),
-// the panel's rows in registers (thread t holds rows t and t + RT).  Column
-// j: thread j publishes row j, one fused 32-slot reduction gives sigma (slot
-// j) and the raw dots sum_{i > j} P[c][i] x_i of every other column, and
-// every thread then forms tau, beta and d_c = P[c][j] + scale * raw_c itself:
-// the update of the later columns and column j of T (T[0:j, j] = -tau_j
-// T[0:j, 0:j] d), as in the LDS kernel, with two barriers per column.
-// Outputs are those of k_qr_block mode 0, plus (write_r) R in the panel's top
-// rows.
+// the panel's rows in registers (thread t holds rows 2t and 2t + 1).  Column
+// j: the thread holding row j publishes it, one fused 32-slot reduction gives
+// sigma (slot j) and the raw dots sum_{i > j} P[c][i] x_i of every other
+// column, and every thread then forms tau, beta and d_c = P[c][j] + scale *
+// raw_c itself, updating the later columns; d_c for c < j is v_c^T v_j,
+// kept for T.  Two barriers per column; waves whose rows all lie past the
+// panel skip the arithmetic.  T follows the factorization: row t of T by
+// thread t, T[t][j] = -tau_j sum_{t <= l < j} T[t][l] (v_l^T v_j), T[j][j] =
+// tau_j.  Outputs are those of k_qr_block mode 0, plus (write_r) R in the
+// panel's top rows.
 constexpr int RT = kLeaf / 2, RW = RT / 64;
 __global__ __launch_bounds__(RT) void k_qr_reg(float* A, int64_t m, int64_t ld, int64_t bstride, int64_t c0,
                                                int nb, float* Vp, int64_t vstride, float* Tp, int64_t tstride,
@@ -393,12 +395,13 @@ __global__ __launch_bounds__(RT) void k_qr_reg(float* A, int64_t m, int64_t ld, 
   __shared__ float red[RW][32];
   __shared__ __attribute__((aligned(16))) float raw[32];
   __shared__ __attribute__((aligned(16))) float rowj[2][32];
-  __shared__ float Ts[32][33];
-  __shared__ float sgn[32];
+  __shared__ __attribute__((aligned(16))) float St[32][36];   // St[j][l] = v_l^T v_j (l < j)
+  __shared__ float tau_s[32], sgn[32];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int i0 = t, i1 = t + RT;
+  const int i0 = 2 * t, i1 = 2 * t + 1;
   const int64_t z = blockIdx.y;
   const int mr = static_cast<int>(m - c0);
+  const bool live = 128 * wave < mr;                 // this wave holds rows of the panel
   float* Az = A + z * bstride;
   float p0[32], p1[32];
 #pragma unroll
@@ -406,28 +409,30 @@ __global__ __launch_bounds__(RT) void k_qr_reg(float* A, int64_t m, int64_t ld, 
     p0[c] = (c < nb && i0 < mr) ? Az[(c0 + c) * ld + c0 + i0] : 0.f;
     p1[c] = (c < nb && i1 < mr) ? Az[(c0 + c) * ld + c0 + i1] : 0.f;
   }
-  for (int idx = t; idx < 32 * 33; idx += RT) (&Ts[0][0])[idx] = 0.f;
   // fully unrolled (register indices must be compile-time); columns past nb skipped
 #pragma clang loop unroll(full)
   for (int j = 0; j < 32; ++j) {
     if (j >= nb) continue;
     float* rj = rowj[j & 1];
-    if (t == j) {
+    if (t == (j >> 1)) {
 #pragma unroll
-      for (int c = 0; c < 32; ++c) rj[c] = p0[c];
+      for (int c = 0; c < 32; ++c) rj[c] = (j & 1) ? p1[c] : p0[c];
     }
-    const bool b0 = i0 > j && i0 < mr, b1 = i1 < mr;     // i1 >= RT > j
+    const bool b0 = i0 > j && i0 < mr, b1 = i1 > j && i1 < mr;
     const float x0 = b0 ? p0[j] : 0.f, x1 = b1 ? p1[j] : 0.f;
-    f32x32 part;
+    if (live) {
+      f32x32 part;
 #pragma unroll
-    for (int c = 0; c < 32; ++c)
-      part[c] = c < nb ? (c == j ? x0 : p0[c]) * x0 + (c == j ? x1 : p1[c]) * x1 : 0.f;
-    const float tot = reduce32(part, lane);
-    if ((lane & 1) == 0) red[wave][lane >> 1] = tot;
+      for (int c = 0; c < 32; ++c)
+        part[c] = c < nb ? (c == j ? x0 : p0[c]) * x0 + (c == j ? x1 : p1[c]) * x1 : 0.f;
+      const float tot = reduce32(part, lane);
+      if ((lane & 1) == 0) red[wave][lane >> 1] = tot;
+    }
     __syncthreads();
     if (t < 32) {
       float u = 0.f;
-      for (int w = 0; w < RW; ++w) u += red[w][t];
+      for (int w = 0; w < RW; ++w)
+        if (128 * w < mr) u += red[w][t];
       raw[t] = u;
     }
     __syncthreads();
@@ -439,8 +444,9 @@ __global__ __launch_bounds__(RT) void k_qr_reg(float* A, int64_t m, int64_t ld, 
       tau = (beta - alpha) / beta;
       scale = 1.f / (alpha - beta);
     }
-    const float v0 = (t == j) ? 1.f : (b0 ? x0 * scale : 0.f), v1 = b1 ? x1 * scale : 0.f;
-    if (tau != 0.f) {
+    const bool d0 = i0 == j, d1 = i1 == j;           // the diagonal row
+    const float v0 = d0 ? 1.f : (b0 ? x0 * scale : 0.f), v1 = d1 ? 1.f : (b1 ? x1 * scale : 0.f);
+    if (tau != 0.f && live) {
 #pragma unroll
       for (int c = j + 1; c < 32; ++c) {
         if (c < nb) {
@@ -451,35 +457,47 @@ __global__ __launch_bounds__(RT) void k_qr_reg(float* A, int64_t m, int64_t ld, 
       }
     }
     if (b0) p0[j] = v0;
-    if (t == j) p0[j] = beta;
     if (b1) p1[j] = v1;
-    if (t < j) {
-      float u = 0.f;
-      for (int l = t; l < j; ++l) u += Ts[t][l] * (rj[l] + scale * raw[l]);
-      Ts[t][j] = -tau * u;
-    } else if (t == j) {
-      Ts[j][j] = tau;
+    if (d0) p0[j] = beta;
+    if (d1) p1[j] = beta;
+    if (t < j) St[j][t] = rj[t] + scale * raw[t];
+    if (t == j) {
+      tau_s[j] = tau;
       sgn[j] = beta < 0.f ? -1.f : 1.f;
     }
   }
   __syncthreads();
-  // V (explicit, zero above row c0, unit diagonal), T, tau / sign(beta)
+  if (t < 32) {                                      // row t of T
+    float tr[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      float u = 0.f;
+#pragma unroll
+      for (int l = 0; l < j; ++l)
+        if (l >= t) u += tr[l] * St[j][l];
+      tr[j] = (j >= nb || j < t) ? 0.f : (j == t ? tau_s[j] : -tau_s[j] * u);
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) Tp[z * tstride + t * 32 + j] = tr[j];
+  }
+  // V (explicit, zero above row c0, unit diagonal), tau / sign(beta)
   float* V = Vp + z * vstride;
   for (int64_t r = t; r < c0; r += RT)
     for (int c = 0; c < 32; ++c) V[c * m + r] = 0.f;
 #pragma unroll
   for (int c = 0; c < 32; ++c) {
     if (i0 < mr) V[c * m + c0 + i0] = (c >= nb || i0 < c) ? 0.f : (i0 == c ? 1.f : p0[c]);
-    if (i1 < mr) V[c * m + c0 + i1] = c >= nb ? 0.f : p1[c];
+    if (i1 < mr) V[c * m + c0 + i1] = (c >= nb || i1 < c) ? 0.f : (i1 == c ? 1.f : p1[c]);
   }
-  for (int idx = t; idx < 1024; idx += RT) Tp[z * tstride + idx] = Ts[idx / 32][idx % 32];
   if (t < nb) {
-    taus_g[z * 2 * k + c0 + t] = Ts[t][t];
+    taus_g[z * 2 * k + c0 + t] = tau_s[t];
     taus_g[z * 2 * k + k + c0 + t] = sgn[t];
-    if (write_r && t < mr) {
+  }
+  if (write_r) {                                     // R: rows 2t, 2t + 1 < nb, upper triangle
 #pragma unroll
-      for (int c = 0; c < 32; ++c)
-        if (c >= t && c < nb) Az[(c0 + c) * ld + c0 + t] = p0[c];
+    for (int c = 0; c < 32; ++c) {
+      if (c < nb && i0 < mr && i0 <= c) Az[(c0 + c) * ld + c0 + i0] = p0[c];
+      if (c < nb && i1 < mr && i1 <= c) Az[(c0 + c) * ld + c0 + i1] = p1[c];
     }
   }
 }
