@@ -27,12 +27,19 @@ template <typename T>
 __device__ __forceinline__ float ld(const void* p, int64_t i) {
   return load_as_f32<T>(static_cast<const T*>(p), i);
 }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint16_t h) { return bf16_bits_to_f32(h); }
 
-// One 64x64 output tile per workgroup, 4 waves of 32x32, fp32 MFMA 32x32x2.
+// One 64x64 output tile per workgroup, 4 waves of 32x32, fp32 MFMA 32x32x2,
+// K tiles of 32.  Each thread loads fixed positions of every tile (four rows
+// by two k, or one row by eight k, along whichever dimension is contiguous);
+// the next tile's loads are issued before the current tile's MFMAs, and the
+// K position advances with segment counters (no divisions in the loop).
+constexpr int FK = 32;
 template <typename TA, typename TB>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
-  __shared__ float As[BK][BM + PAD];
-  __shared__ float Bs[BK][BN + PAD];
+  __shared__ float As[FK][BM + PAD];
+  __shared__ float Bs[FK][BN + PAD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
   const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
@@ -40,45 +47,65 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   const int64_t z = zz / g.ksplit, kz = zz % g.ksplit;
   const int64_t kbeg = kz * g.kchunk;
   const int64_t kend = (kbeg + g.kchunk < g.K) ? kbeg + g.kchunk : g.K;
+  if (g.c_lower && m0 + BM <= n0) return;          // tile wholly above the diagonal
   const char* Ab = g.a_ptrs ? static_cast<const char*>(g.a_ptrs[z])
                            : static_cast<const char*>(g.A) + z * g.a_batch * static_cast<int64_t>(sizeof(TA));
   const char* Bb = g.b_ptrs ? static_cast<const char*>(g.b_ptrs[z])
                            : static_cast<const char*>(g.B) + z * g.b_batch * static_cast<int64_t>(sizeof(TB));
-  const int64_t a_mbase = dim_off(g.am, m0);
-  const int64_t b_nbase = dim_off(g.bn, n0);
   const bool a_mcontig = g.am.stride == 1;
   const bool b_ncontig = g.bn.stride == 1;
+  // this thread's tile positions: element e = 0..7 at row pr(e), k pk(e), four
+  // rows by two k along a contiguous row dimension, else one row by eight k
+  auto pr = [&](bool rc, int e) { return rc ? ((tid & 15) << 2) + (e & 3) : tid >> 2; };
+  auto pk = [&](bool rc, int e) { return rc ? (tid >> 4) + 16 * (e >> 2) : ((tid & 3) << 3) + e; };
+  // element offsets inside one batch entry fit in 32 bits (checked at launch)
+  const TA* Ap = reinterpret_cast<const TA*>(Ab);
+  const TB* Bp = reinterpret_cast<const TB*>(Bb);
+  const int a_mbase = static_cast<int>(dim_off(g.am, m0));
+  const int b_nbase = static_cast<int>(dim_off(g.bn, n0));
+  const int ams = static_cast<int>(g.am.stride), aks = static_cast<int>(g.ak.stride);
+  const int bns = static_cast<int>(g.bn.stride), bks = static_cast<int>(g.bk.stride);
+  int64_t a_kseg = 0, a_kin = kbeg, b_kseg = 0, b_kin = kbeg;
+  if (g.ak.len != INT64_MAX) { a_kseg = kbeg / g.ak.len; a_kin = kbeg % g.ak.len; }
+  if (g.bk.len != INT64_MAX) { b_kseg = kbeg / g.bk.len; b_kin = kbeg % g.bk.len; }
+  float ra[8], rb[8];
+  auto load = [&](int64_t k0) {
+    const int a_kbase = static_cast<int>(a_kseg * g.ak.seg + a_kin * g.ak.stride);
+    const int b_kbase = static_cast<int>(b_kseg * g.bk.seg + b_kin * g.bk.stride);
+    const int kl = static_cast<int>(kend - k0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ar = pr(a_mcontig, e), ak = pk(a_mcontig, e);
+      const int64_t m = m0 + ar;
+      float v = 0.f;
+      if (m < g.M && ak < kl) {
+        if (g.a_sym && m < k0 + ak)
+          v = to_f32(Ap[static_cast<int>(k0 + ak) * ams + static_cast<int>(m) * aks]);
+        else
+          v = to_f32(Ap[a_mbase + ar * ams + a_kbase + ak * aks]);
+      }
+      ra[e] = v;
+      const int br = pr(b_ncontig, e), bk = pk(b_ncontig, e);
+      rb[e] = (n0 + br < g.N && bk < kl) ? to_f32(Bp[b_nbase + br * bns + b_kbase + bk * bks]) : 0.f;
+    }
+  };
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
   f32x16 acc = {};
-  if (g.c_lower && m0 + BM <= n0) return;          // tile wholly above the diagonal
-
-  for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
-    const int64_t a_kbase = dim_off(g.ak, k0);
-    const int64_t b_kbase = dim_off(g.bk, k0);
+  if (kbeg < kend) load(kbeg);
+  for (int64_t k0 = kbeg; k0 < kend; k0 += FK) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int mm, kk;
-      if (a_mcontig) { kk = tid >> 4; mm = ((tid & 15) << 2) + j; }
-      else           { mm = tid >> 2; kk = ((tid & 3) << 2) + j; }
-      float v = 0.f;
-      if (m0 + mm < g.M && k0 + kk < kend) {
-        if (g.a_sym && m0 + mm < k0 + kk)
-          v = ld<TA>(Ab, (k0 + kk) * g.am.stride + (m0 + mm) * g.ak.stride);
-        else
-          v = ld<TA>(Ab, a_mbase + mm * g.am.stride + a_kbase + kk * g.ak.stride);
-      }
-      As[kk][mm] = v;
-      int nn, kb;
-      if (b_ncontig) { kb = tid >> 4; nn = ((tid & 15) << 2) + j; }
-      else           { nn = tid >> 2; kb = ((tid & 3) << 2) + j; }
-      float w = 0.f;
-      if (n0 + nn < g.N && k0 + kb < kend)
-        w = ld<TB>(Bb, b_nbase + nn * g.bn.stride + b_kbase + kb * g.bk.stride);
-      Bs[kb][nn] = w;
+    for (int e = 0; e < 8; ++e) {
+      As[pk(a_mcontig, e)][pr(a_mcontig, e)] = ra[e];
+      Bs[pk(b_ncontig, e)][pr(b_ncontig, e)] = rb[e];
     }
     __syncthreads();
+    if (k0 + FK < kend) {
+      a_kin += FK; if (a_kin == g.ak.len) { a_kin = 0; ++a_kseg; }
+      b_kin += FK; if (b_kin == g.bk.len) { b_kin = 0; ++b_kseg; }
+      load(k0 + FK);
+    }
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 2) {
+    for (int kk = 0; kk < FK; kk += 2) {
       const float a = As[kk + (lane >> 5)][wm + (lane & 31)];
       const float b = Bs[kk + (lane >> 5)][wn + (lane & 31)];
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
@@ -595,6 +622,21 @@ int grid1(int64_t n, int cap = 4096) {
   return static_cast<int>(b < 1 ? 1 : (b > cap ? cap : b));
 }
 
+// Largest element offset of indices [0, n) along d (strides non-negative).
+int64_t dim_span(const GemmDim& d, int64_t n) {
+  if (n <= 0) return 0;
+  const int64_t i = n - 1;
+  return d.len == INT64_MAX ? i * d.stride : (i / d.len) * d.seg + (i % d.len) * d.stride;
+}
+// Largest |offset| of indices [0, n) along d (any signs).
+int64_t dim_reach(const GemmDim& d, int64_t n) {
+  if (n <= 0) return 0;
+  auto ab = [](int64_t v) { return v < 0 ? -v : v; };
+  if (d.len == INT64_MAX) return ab((n - 1) * d.stride);
+  const int64_t nseg = (n + d.len - 1) / d.len, inner = (n < d.len ? n : d.len) - 1;
+  return ab((nseg - 1) * d.seg) + ab(inner * d.stride);
+}
+
 // Operand mode for the 128 x 128 kernel (rows rd, contraction kd), or -1.
 int x_mode(int dtype, const GemmDim& rd, const GemmDim& kd, int64_t rows, int64_t kext, bool use_ptrs,
            bool ptrs_aligned, const void* base, int64_t batch_stride) {
@@ -605,13 +647,8 @@ int x_mode(int dtype, const GemmDim& rd, const GemmDim& kd, int64_t rows, int64_
   if (use_ptrs ? !ptrs_aligned : ((reinterpret_cast<uintptr_t>(base) & 15) != 0 || !mult(batch_stride, q)))
     return -1;
   // every byte offset inside one batch entry below 2^31 (buffer addressing)
-  auto span = [](const GemmDim& d, int64_t n) {
-    if (n <= 0) return int64_t{0};
-    const int64_t i = n - 1;
-    return d.len == INT64_MAX ? i * d.stride : (i / d.len) * d.seg + (i % d.len) * d.stride;
-  };
   if (rd.stride < 0 || kd.stride < 0 || rd.seg < 0 || kd.seg < 0 ||
-      (span(rd, rows + XT) + span(kd, kext) + 8) * (dtype == kBF16 ? 2 : 4) >= (int64_t{1} << 31))
+      (dim_span(rd, rows + XT) + dim_span(kd, kext) + 8) * (dtype == kBF16 ? 2 : 4) >= (int64_t{1} << 31))
     return -1;
   if (kd.stride == 1 && within(kd, XK) && seg16(kd) && mult(rd.stride, q) && seg16(rd))
     return dtype == kBF16 ? kOpBfK : kOpF32K;
@@ -665,12 +702,21 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s) {
       return hipGetLastError();
     }
   }
+  // the 64 x 64 kernels address each batch entry with 32-bit element offsets
+  {
+    const int64_t lim = int64_t{1} << 31;
+    auto ab = [](int64_t v) { return v < 0 ? -v : v; };
+    const int64_t sa = dim_reach(g.am, g.M + BM) + dim_reach(g.ak, g.K + BK16);
+    const int64_t ssym = g.a_sym ? ab((g.K + FK) * g.am.stride) + ab((g.M + BM) * g.ak.stride) : 0;
+    const int64_t sb = dim_reach(g.bn, g.N + BN) + dim_reach(g.bk, g.K + BK16);
+    if (sa >= lim || ssym >= lim || sb >= lim) return hipErrorInvalidValue;
+  }
   // bf16 x bf16 on bf16 matrix cores when every segmented dimension keeps a
   // 32-wide k tile inside one segment
   auto seg_ok = [](const GemmDim& d) { return d.len == INT64_MAX || d.len % BK16 == 0; };
   const bool bf = g.a_dtype == kBF16 && g.b_dtype == kBF16 && seg_ok(g.ak) && seg_ok(g.bk) && seg_ok(g.am) &&
                   seg_ok(g.bn) && !g.a_sym && !g.c_lower;
-  const int kt = bf ? BK16 : BK;
+  const int kt = bf ? BK16 : FK;
   g.kchunk = (g.K + g.ksplit - 1) / g.ksplit;
   g.kchunk = (g.kchunk + kt - 1) / kt * kt;            // chunks start on tile edges
   dim3 grid((g.M + BM - 1) / BM, (g.N + BN - 1) / BN, batch * g.ksplit);
