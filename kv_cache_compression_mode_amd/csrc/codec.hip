@@ -11,7 +11,7 @@
 // correctly rounded divide, packed as a little-endian bit stream (code k at
 // bits [k*b, (k+1)*b) of the group's 4b bytes).
 //
-// Layout of one workgroup (256 threads, 4 waves) over a 32-row tile: wave w
+// Layout of one workgroup (256 threads, 4 waves) over a 64-row tile: wave w
 // owns features [32w, 32w + 32) = quantization group w.  In the 32x32 fp32
 // matrix-core accumulator, register i of lane l holds row
 // (i/4)*8 + (l/32)*4 + i%4 and column l%32, so one register across a
@@ -24,8 +24,6 @@ namespace jolt {
 namespace {
 
 constexpr int D = 128;
-constexpr int TM = 32;        // rows per tile
-constexpr int KC = 64;        // K chunk of the reconstruction product
 
 __device__ __forceinline__ float half_min(float v) {
 #pragma unroll
@@ -36,6 +34,45 @@ __device__ __forceinline__ float half_max(float v) {
 #pragma unroll
   for (int o = 16; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
+}
+
+// Bit interleaves: bit i of x moves to bit 2i (16 bits), 4i (8 bits), 3i (12 bits).
+__device__ __forceinline__ uint32_t spread2_16(uint32_t x) {
+  x &= 0xFFFFu;
+  x = (x | (x << 8)) & 0x00FF00FFu;
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  return (x | (x << 1)) & 0x55555555u;
+}
+__device__ __forceinline__ uint32_t spread4_8(uint32_t x) {
+  x &= 0xFFu;
+  x = (x | (x << 12)) & 0x000F000Fu;
+  x = (x | (x << 6)) & 0x03030303u;
+  return (x | (x << 3)) & 0x11111111u;
+}
+__device__ __forceinline__ uint64_t spread3_12(uint64_t x) {
+  x &= 0xFFFull;
+  x = (x | (x << 16)) & 0x00000000FF0000FFull;
+  x = (x | (x << 8)) & 0x000000F00F00F00Full;
+  x = (x | (x << 4)) & 0x00000C30C30C30C3ull;
+  return (x | (x << 2)) & 0x0000249249249249ull;
+}
+// Word k (k < bits) of a group's code stream (stream bit s = bit s % bits of
+// code s / bits, word k = stream bits [32k, 32k + 32)) from the per-bit masks
+// m[j] (bit c = bit j of code c).
+__device__ __forceinline__ uint32_t pack_word(const uint32_t (&m)[4], int bits, int k) {
+  switch (bits) {
+    case 1: return m[0];
+    case 2: return spread2_16(m[0] >> (16 * k)) | (spread2_16(m[1] >> (16 * k)) << 1);
+    case 3: {   // codes c0 .. c0 + 11 cover the word; c0 = floor(32k / 3)
+      const int c0 = (32 * k) / 3, sh = 32 * k - 3 * c0;
+      const uint64_t w = spread3_12(m[0] >> c0) | (spread3_12(m[1] >> c0) << 1) | (spread3_12(m[2] >> c0) << 2);
+      return static_cast<uint32_t>(w >> sh);
+    }
+    default:
+      return spread4_8(m[0] >> (8 * k)) | (spread4_8(m[1] >> (8 * k)) << 1) |
+             (spread4_8(m[2] >> (8 * k)) << 2) | (spread4_8(m[3] >> (8 * k)) << 3);
+  }
 }
 
 // Quantize the group held by this half-wave (one value per lane) and write
@@ -65,16 +102,7 @@ __device__ __forceinline__ void quantize_group(float y, int bits, bool valid, ui
   }
   if (!valid) return;
   if (k == 0) *scale_word = static_cast<uint32_t>(m16b) | (static_cast<uint32_t>(s16b) << 16);
-  if (k < bits) {
-    // word k holds stream bits 32k .. 32k+31; stream bit s = bit (s % bits) of code s / bits
-    uint32_t w = 0;
-    for (int i = 0; i < 32; ++i) {
-      const int s = 32 * k + i;
-      const int cidx = s / bits, bj = s - cidx * bits;
-      w |= ((mask[bj] >> cidx) & 1u) << i;
-    }
-    code_words[k] = w;
-  }
+  if (k < bits) code_words[k] = pack_word(mask, bits, k);
 }
 
 // Standalone quantizer: one group per half-wave, 8 groups per workgroup.
@@ -91,63 +119,108 @@ __device__ __forceinline__ float load_x(const void* X, int64_t i) {
   return load_as_f32<TX>(static_cast<const TX*>(X), i);
 }
 
-// acc += Ut[t0 .. t0+32)[0 .. r_T) * W[0 .. r_T)[32w .. 32w+32), fp32 matrix cores.
-__device__ __forceinline__ void recon_tile(f32x16& acc, const uint16_t* Ut, const float* W, int64_t r_T,
-                                           int64_t T, int64_t t0, float (*Us)[TM + 1]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int64_t k0 = 0; k0 < r_T; k0 += KC) {
-    __syncthreads();
-    for (int idx = tid; idx < KC * TM; idx += 256) {
-      const int m = idx / KC, kk = idx % KC;
-      const int64_t t = t0 + m, k = k0 + kk;
-      Us[kk][m] = (t < T && k < r_T) ? bf16_bits_to_f32(Ut[t * r_T + k]) : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int kk = 0; kk < KC; kk += 2) {
-      const int kr = kk + (lane >> 5);
-      const int64_t k = k0 + kr;
-      const float a = Us[kr][lane & 31];
-      const float b = k < r_T ? W[k * D + wave * 32 + (lane & 31)] : 0.f;
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
-    }
-  }
-}
+// One workgroup per 64-row tile of one head (two 32-row blocks).  The
+// reconstruction Ut[t0 .. t0+64) W_h and the rotation R Q^T run on fp32
+// matrix cores (32x32x2, k in increasing order), their B operands (W_h, then
+// Q^T) staged through LDS in chunks of 32 k with the next chunk's loads issued
+// before the current chunk's MFMAs; wave w keeps the two 32x32 blocks of
+// features [32w, 32w + 32), i.e. quantization group w of every row.
+constexpr int ER = 64;        // rows per workgroup
+constexpr int EK = 32;        // K chunk
+constexpr int EWP = D + 4;    // LDS row stride of a staged B chunk (16-byte rows)
 
 template <typename TX>
-__global__ __launch_bounds__(256) void k_encode_residual(EncodeArgs a) {
-  __shared__ float Us[KC][TM + 1];
-  __shared__ float Rs[TM][D + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t h = blockIdx.y, t0 = static_cast<int64_t>(blockIdx.x) * TM;
-  f32x16 acc = {};
-  if (a.r_T > 0) recon_tile(acc, a.Ut, a.W + h * a.r_T * D, a.r_T, a.T, t0, Us);
+__global__ __launch_bounds__(256, 2) void k_encode_residual(EncodeArgs a) {
+  __shared__ float Us[EK][ER + 1];                               // Ut chunk, [k][row]
+  __shared__ __attribute__((aligned(16))) float Bs[EK][EWP];     // W_h or Q^T chunk, [k][feature]
+  __shared__ float Rs[ER][D + 1];                                // residual rows
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, half = lane >> 5;
+  const int64_t h = blockIdx.y, t0 = static_cast<int64_t>(blockIdx.x) * ER;
+  const int col = wave * 32 + rl;
+  // B chunk loader: 32 rows x 128 floats, rows kb = (tid >> 5) + 8 i, float4 column 4 (tid & 31)
+  const int bk = tid >> 5, bc = 4 * (tid & 31);
+  float4 rb[4];
+  auto load_b = [&](const float* src, int64_t k0, int64_t kmax) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t k = k0 + bk + 8 * i;
+      rb[i] = k < kmax ? *reinterpret_cast<const float4*>(src + k * D + bc) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto store_b = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(&Bs[bk + 8 * i][bc]) = rb[i];
+  };
+  f32x16 acc0 = {}, acc1 = {};
+  if (a.r_T > 0) {
+    const float* Wh = a.W + h * a.r_T * D;
+    // Ut chunk loader: row ur = tid >> 2, k = 8 (tid & 3) .. +8
+    const int ur = tid >> 2, uk = 8 * (tid & 3);
+    const int64_t ut = t0 + ur;
+    float ru[8];
+    auto load_u = [&](int64_t k0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t k = k0 + uk + i;
+        ru[i] = (ut < a.T && k < a.r_T) ? bf16_bits_to_f32(a.Ut[ut * a.r_T + k]) : 0.f;
+      }
+    };
+    load_u(0);
+    load_b(Wh, 0, a.r_T);
+    for (int64_t k0 = 0; k0 < a.r_T; k0 += EK) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Us[uk + i][ur] = ru[i];
+      store_b();
+      __syncthreads();
+      if (k0 + EK < a.r_T) {
+        load_u(k0 + EK);
+        load_b(Wh, k0 + EK, a.r_T);
+      }
+#pragma unroll
+      for (int kk = 0; kk < EK; kk += 2) {
+        const int k = kk + half;
+        const float b = Bs[k][col];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(Us[k][rl], b, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(Us[k][32 + rl], b, acc1, 0, 0, 0);
+      }
+      __syncthreads();
+    }
+  }
   // residual R = X - recon, staged in LDS as [row][feature]
+  load_b(a.Qt, 0, D);                            // first Q^T chunk, in flight meanwhile
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int m = (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-    const int c = wave * 32 + (lane & 31);
-    const int64_t t = t0 + m;
-    const float x = t < a.T ? load_x<TX>(a.X, (h * a.T + t) * D + c) : 0.f;
-    Rs[m][c] = x - acc[i];
+    const int m = (i >> 2) * 8 + half * 4 + (i & 3);
+    const int64_t ta = t0 + m, tb = t0 + 32 + m;
+    const float xa = ta < a.T ? load_x<TX>(a.X, (h * a.T + ta) * D + col) : 0.f;
+    const float xb = tb < a.T ? load_x<TX>(a.X, (h * a.T + tb) * D + col) : 0.f;
+    Rs[m][col] = xa - acc0[i];
+    Rs[32 + m][col] = xb - acc1[i];
   }
-  __syncthreads();
-  // Y = R Q^T: Y[m][c] = sum_d R[m][d] Q[c][d] = sum_d R[m][d] Qt[d][c]
-  f32x16 y = {};
-#pragma unroll 8
-  for (int kk = 0; kk < D; kk += 2) {
-    const int d = kk + (lane >> 5);
-    y = __builtin_amdgcn_mfma_f32_32x32x2f32(Rs[lane & 31][d], a.Qt[d * D + wave * 32 + (lane & 31)], y,
-                                             0, 0, 0);
+  // Y = R Q^T: Y[m][c] = sum_d R[m][d] Qt[d][c]
+  f32x16 y0 = {}, y1 = {};
+  for (int d0 = 0; d0 < D; d0 += EK) {
+    store_b();
+    __syncthreads();
+    if (d0 + EK < D) load_b(a.Qt, d0 + EK, D);
+#pragma unroll
+    for (int kk = 0; kk < EK; kk += 2) {
+      const int k = kk + half;
+      const float b = Bs[k][col];
+      y0 = __builtin_amdgcn_mfma_f32_32x32x2f32(Rs[rl][d0 + k], b, y0, 0, 0, 0);
+      y1 = __builtin_amdgcn_mfma_f32_32x32x2f32(Rs[32 + rl][d0 + k], b, y1, 0, 0, 0);
+    }
+    __syncthreads();
   }
   uint32_t* sc = reinterpret_cast<uint32_t*>(a.scales);
   uint32_t* cd = reinterpret_cast<uint32_t*>(a.codes);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int m = (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-    const int64_t t = t0 + m;
-    const int64_t g = (h * a.T + t) * 4 + wave;          // group index
-    quantize_group(y[i], a.bits, t < a.T, sc + g, cd + g * a.bits);
+    const int m = (i >> 2) * 8 + half * 4 + (i & 3);
+    const int64_t ta = t0 + m, tb = t0 + 32 + m;
+    const int64_t ga = (h * a.T + ta) * 4 + wave, gb = (h * a.T + tb) * 4 + wave;   // group indices
+    quantize_group(y0[i], a.bits, ta < a.T, sc + ga, cd + ga * a.bits);
+    quantize_group(y1[i], a.bits, tb < a.T, sc + gb, cd + gb * a.bits);
   }
 }
 
@@ -334,7 +407,7 @@ hipError_t launch_quantize(const float* Y, int64_t rows, int bits, uint16_t* sca
 }
 
 hipError_t launch_encode_residual(const EncodeArgs& a, hipStream_t s) {
-  dim3 grid((a.T + TM - 1) / TM, a.H);
+  dim3 grid((a.T + ER - 1) / ER, a.H);
   ProfScope ps("encode_residual", s);
   if (a.x_dtype == kBF16) k_encode_residual<uint16_t><<<grid, 256, 0, s>>>(a);
   else k_encode_residual<float><<<grid, 256, 0, s>>>(a);
