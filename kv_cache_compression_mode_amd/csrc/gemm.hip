@@ -47,7 +47,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   const int64_t z = zz / g.ksplit, kz = zz % g.ksplit;
   const int64_t kbeg = kz * g.kchunk;
   const int64_t kend = (kbeg + g.kchunk < g.K) ? kbeg + g.kchunk : g.K;
-  if (g.c_lower && m0 + BM <= n0) return;          // tile wholly above the diagonal
+  // tile wholly outside the kept triangle (c_lower > 0: m >= n; < 0: m <= n)
+  if (g.c_lower > 0 ? m0 + BM <= n0 : (g.c_lower < 0 && n0 + BN <= m0)) return;
   const char* Ab = g.a_ptrs ? static_cast<const char*>(g.a_ptrs[z])
                            : static_cast<const char*>(g.A) + z * g.a_batch * static_cast<int64_t>(sizeof(TA));
   const char* Bb = g.b_ptrs ? static_cast<const char*>(g.b_ptrs[z])
@@ -91,6 +92,20 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   };
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
   f32x16 acc = {};
+  // C (when accumulated, beta != 0) is read before the K loop
+  char* Cb = static_cast<char*>(g.C);
+  const int64_t cz = z * g.c_batch;
+  auto kept = [&](int64_t m, int64_t n) {
+    return m < g.M && n < g.N && (g.c_lower == 0 || (g.c_lower > 0 ? m >= n : m <= n));
+  };
+  float cold[16];
+  const bool rd_c = g.ksplit == 1 && g.beta != 0.f && g.c_dtype == kF32;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t m = m0 + wm + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+    const int64_t n = n0 + wn + (lane & 31);
+    cold[i] = (rd_c && kept(m, n)) ? reinterpret_cast<const float*>(Cb)[cz + m * g.c_m + n * g.c_n] : 0.f;
+  }
   if (kbeg < kend) load(kbeg);
   for (int64_t k0 = kbeg; k0 < kend; k0 += FK) {
 #pragma unroll
@@ -123,23 +138,19 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     }
     return;
   }
-  char* Cb = static_cast<char*>(g.C);
-  const int64_t cz = z * g.c_batch;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t m = m0 + wm + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
     const int64_t n = n0 + wn + (lane & 31);
-    if (m < g.M && n < g.N && (!g.c_lower || m >= n)) {
+    if (kept(m, n)) {
       float v = g.alpha * acc[i];
       if (g.col_scale) v *= g.col_scale[z * g.col_scale_batch + n];
       const int64_t off = cz + m * g.c_m + n * g.c_n;
       if (g.c_dtype == kF32) {
-        float* C = reinterpret_cast<float*>(Cb);
-        if (g.beta != 0.f) v += g.beta * C[off];
-        C[off] = v;
+        if (rd_c) v += g.beta * cold[i];
+        reinterpret_cast<float*>(Cb)[off] = v;
       } else {
-        uint16_t* C = reinterpret_cast<uint16_t*>(Cb);
-        C[off] = f32_to_bf16_rne(v);
+        reinterpret_cast<uint16_t*>(Cb)[off] = f32_to_bf16_rne(v);
       }
     }
   }
@@ -717,6 +728,13 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s) {
   const bool bf = g.a_dtype == kBF16 && g.b_dtype == kBF16 && seg_ok(g.ak) && seg_ok(g.bk) && seg_ok(g.am) &&
                   seg_ok(g.bn) && !g.a_sym && !g.c_lower;
   const int kt = bf ? BK16 : FK;
+  if (!bf && !g.a_sym && g.c_m == 1 && g.c_n != 1 && !g.col_scale) {
+    // column-major C as the row-major C^T = B^T A^T: stores and the C read run along rows
+    std::swap(g.M, g.N); std::swap(g.A, g.B); std::swap(g.a_dtype, g.b_dtype);
+    std::swap(g.am, g.bn); std::swap(g.ak, g.bk); std::swap(g.a_batch, g.b_batch);
+    std::swap(g.a_ptrs, g.b_ptrs); std::swap(g.c_m, g.c_n);
+    g.c_lower = -g.c_lower;
+  }
   g.kchunk = (g.K + g.ksplit - 1) / g.ksplit;
   g.kchunk = (g.kchunk + kt - 1) / kt * kt;            // chunks start on tile edges
   dim3 grid((g.M + BM - 1) / BM, (g.N + BN - 1) / BN, batch * g.ksplit);
