@@ -15,9 +15,10 @@
 //  3. the top R eigenvalues of the tridiagonal by bisection on Sturm counts
 //     and their eigenvectors by inverse iteration on T - lambda I = L D L^T,
 //     both in fp64;
-//  4. back-transformation: the chase reflectors in reverse order, one sweep
-//     at a time (the reflectors of one sweep touch disjoint rows), then the
-//     panel reflectors as matrix-core products.
+//  4. back-transformation: the chase reflectors in reverse order, grouped
+//     into blocks of 32 sweeps at one step (compact WY, matrix cores) applied
+//     in a wavefront of launches, then the panel reflectors as matrix-core
+//     products.
 //
 // The factors the codec needs are the leading eigenvectors of the Gram
 // (JoLT abstract: Tucker factors from the leading singular vectors of the
@@ -463,61 +464,145 @@ __global__ __launch_bounds__(256) void k_invit(const double* d_g, const double* 
   for (int64_t i = 0; i < n; ++i) zc[i] = static_cast<float>(y[i * R + q] * nrm);
 }
 
-// Stage 2 back-transformation of a tile of CT eigenvector columns held in
-// LDS (column stride n + 1, so the columns of one reflector's threads fall in
-// different banks): sweeps in reverse order; a sweep's reflectors are staged
-// in LDS, act on disjoint 32-row blocks and run in parallel, one (reflector,
-// column) per thread.
-__global__ __launch_bounds__(1024) void k_chase_back(float* Z, int64_t n, int R, int64_t z_batch, int CT,
-                                                    const float* Rf_g, int64_t rf_stride) {
-  extern __shared__ float sm[];
-  const int ldz = static_cast<int>(n) + 1;
-  float* Zt = sm;                                 // [CT][n + 1]
-  float* Rl = sm + static_cast<int64_t>(CT) * ldz;   // [steps][RFS]
+// Stage 2 back-transformation in blocks.  Block (G, s) gathers the step-s
+// reflectors of the 32 sweeps j = 32G .. 32G + 31: reflector i acts on rows
+// rb + i .. rb + i + 31 (rb = 32G + 1 + 32s), so the block is I - V T V^T
+// with V a 63 x 32 staircase and T the upper-triangular factor of the
+// product H_{32G} ... H_{32G+31} (forward accumulation: T[i][i] = tau_i,
+// T[0:i, i] = -tau_i T[0:i, 0:i] V[:, 0:i]^T v_i).  Applying the sweeps in
+// reverse order equals applying, for the groups in reverse order, their
+// blocks in increasing s: a block only overlaps its neighbours in s within
+// its group and blocks of adjacent groups, which the wavefront t = 2 g' + s
+// (g' = 0 for the last group) orders; blocks of one t touch disjoint rows.
+constexpr int CBR = 2 * SBW;      // staircase rows (63) padded to 64
+
+// T of every block: one wave per (G, s).
+__global__ __launch_bounds__(64) void k_cb_tfac(const float* Rf_g, int64_t rf_stride, int n, int K0, float* Tg,
+                                                int64_t t_stride) {
+  __shared__ float Vs[SBW][SBW + 1];     // Vs[i][r] = v_i[r]
+  __shared__ float S[SBW][SBW + 1];      // S[l][i] = v_l^T v_i (l < i)
+  __shared__ float Ts[SBW][SBW + 1];
+  __shared__ float tau[SBW];
+  const int lane = threadIdx.x, blk = blockIdx.x, G = blk / K0, s = blk % K0;
   const int64_t z = blockIdx.y;
-  const int c0 = blockIdx.x * CT;
-  const int nc = (R - c0 < CT) ? R - c0 : CT;
-  float* zb = Z + z * z_batch;
   const float* Rf = Rf_g + z * rf_stride;
-  for (int64_t idx = threadIdx.x; idx < static_cast<int64_t>(CT) * n; idx += 1024) {
-    const int cc = static_cast<int>(idx / n);
-    const int i = static_cast<int>(idx % n);
-    Zt[cc * ldz + i] = cc < nc ? zb[static_cast<int64_t>(c0 + cc) * n + i] : 0.f;
+  const int jg = G * SBW, last = n - 3;
+  for (int idx = lane; idx < SBW * SBW; idx += 64) {
+    const int i = idx / SBW, r = idx % SBW, j = jg + i;
+    const bool ex = j <= last && s < sweep_steps(n, j);
+    Vs[i][r] = ex ? Rf[(sweep_offset(n, j) + s) * RFS + r] : 0.f;
+    if (r == 0) tau[i] = ex ? Rf[(sweep_offset(n, j) + s) * RFS + SBW] : 0.f;
+    Ts[i][r] = 0.f;
   }
-  for (int64_t j = n - 3; j >= 0; --j) {
-    const int K = static_cast<int>(sweep_steps(n, j));
-    const float* rs = Rf + sweep_offset(n, j) * RFS;
-    __syncthreads();                              // previous sweep done with Rl
-    for (int idx = threadIdx.x; idx < K * RFS; idx += 1024) Rl[idx] = rs[idx];
-    __syncthreads();
-    for (int p = threadIdx.x; p < K * CT; p += 1024) {
-      const int s = p / CT, cc = p % CT;
-      const float* rf = Rl + s * RFS;
-      const float tau = rf[SBW];
-      if (tau == 0.f || cc >= nc) continue;
-      const int r0 = (s == 0) ? static_cast<int>(j) + 1 : static_cast<int>(j) + 1 + s * SBW;
-      float* col = Zt + cc * ldz + r0;
-      if (r0 + SBW <= n) {                        // v is zero past its length
-        float yv = 0.f;
-#pragma unroll
-        for (int i = 0; i < SBW; ++i) yv += rf[i] * col[i];
-        yv *= tau;
-#pragma unroll
-        for (int i = 0; i < SBW; ++i) col[i] -= rf[i] * yv;
-      } else {
-        const int L = static_cast<int>(n) - r0;
-        float yv = 0.f;
-        for (int i = 0; i < L; ++i) yv += rf[i] * col[i];
-        yv *= tau;
-        for (int i = 0; i < L; ++i) col[i] -= rf[i] * yv;
-      }
+  __syncthreads();
+  for (int idx = lane; idx < SBW * SBW; idx += 64) {
+    const int l = idx / SBW, i = idx % SBW;
+    float a = 0.f;
+    if (l < i)
+      for (int r = i; r < l + SBW; ++r) a += Vs[l][r - l] * Vs[i][r - i];   // common rows i .. l + 31
+    S[l][i] = a;
+  }
+  __syncthreads();
+  // row `lane` of T is written only by this lane
+  for (int i = 0; i < SBW; ++i) {
+    if (lane < i) {
+      float a = 0.f;
+      for (int p = lane; p < i; ++p) a += Ts[lane][p] * S[p][i];
+      Ts[lane][i] = -tau[i] * a;
+    } else if (lane == i) {
+      Ts[i][i] = tau[i];
     }
   }
   __syncthreads();
-  for (int64_t idx = threadIdx.x; idx < static_cast<int64_t>(nc) * n; idx += 1024) {
-    const int cc = static_cast<int>(idx / n);
-    const int i = static_cast<int>(idx % n);
-    zb[static_cast<int64_t>(c0 + cc) * n + i] = Zt[cc * ldz + i];
+  float* Tb = Tg + z * t_stride + static_cast<int64_t>(blk) * SBW * SBW;
+  for (int idx = lane; idx < SBW * SBW; idx += 64) Tb[idx] = Ts[idx / SBW][idx % SBW];
+}
+
+// The blocks of wavefront step t, one workgroup per (block, 64 columns of Z):
+// W = V^T Z_rows (K split over two wave pairs), W2 = T W, Z_rows -= V W2, on
+// fp32 matrix cores (32x32x2) from LDS.
+__global__ __launch_bounds__(256) void k_cb_apply(int t, int glo, int nchunk, float* Z, int n, int R,
+                                                  int64_t z_batch, const float* Rf_g, int64_t rf_stride,
+                                                  const float* Tg, int64_t t_stride, int ng, int K0) {
+  __shared__ float Vs[CBR][SBW + 1];     // staircase V[r][i]
+  __shared__ float Ts[SBW][SBW + 1];
+  __shared__ float Zs[CBR][65];          // Z rows x 64 columns
+  __shared__ float Wp[2][SBW][65];       // W partial sums, then W2
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
+  const int bi = blockIdx.x / nchunk, ch = blockIdx.x % nchunk;
+  const int gp = glo + bi, s = t - 2 * gp, G = ng - 1 - gp, jg = G * SBW;
+  if (gp >= ng || s < 0 || s >= K0 || s >= sweep_steps(n, jg)) return;
+  const int rb = jg + 1 + s * SBW;
+  if (rb >= n) return;
+  const int rows = min(CBR - 1, n - rb);
+  const int c0 = ch * 64, nc = min(64, R - c0);
+  const int64_t z = blockIdx.y;
+  const float* Rf = Rf_g + z * rf_stride;
+  float* Zz = Z + z * z_batch;
+  const int last = n - 3;
+  for (int idx = tid; idx < CBR * (SBW + 1); idx += 256) (&Vs[0][0])[idx] = 0.f;
+  for (int idx = tid; idx < SBW * SBW; idx += 256) {
+    const int r = idx / SBW, c = idx % SBW;
+    Ts[r][c] = Tg[z * t_stride + (static_cast<int64_t>(G) * K0 + s) * SBW * SBW + idx];
+  }
+  for (int idx = tid; idx < CBR * 64; idx += 256) {
+    const int c = idx / CBR, r = idx % CBR;
+    Zs[r][c] = (r < rows && c < nc) ? Zz[static_cast<int64_t>(c0 + c) * n + rb + r] : 0.f;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < SBW * SBW; idx += 256) {
+    const int i = idx / SBW, r = idx % SBW, j = jg + i;
+    if (j <= last && s < sweep_steps(n, j)) Vs[i + r][i] = Rf[(sweep_offset(n, j) + s) * RFS + r];
+  }
+  __syncthreads();
+  // W = V^T Z: wave w -> columns 32 (w & 1) .., rows of V 32 (w >> 1) ..
+  {
+    const int cb = 32 * (wave & 1), kb = 32 * (wave >> 1);
+    f32x16 acc = {};
+#pragma unroll
+    for (int kk = 0; kk < SBW; kk += 2) {
+      const int k = kb + kk + hf;
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[k][rl], Zs[k][cb + rl], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Wp[wave >> 1][(e >> 2) * 8 + hf * 4 + (e & 3)][cb + rl] = acc[e];
+  }
+  __syncthreads();
+  // W2 = T W (T upper), waves 0 and 1; W2 overwrites Wp[0] after the barrier
+  f32x16 w2 = {};
+  if (wave < 2) {
+    const int cb = 32 * wave;
+#pragma unroll
+    for (int kk = 0; kk < SBW; kk += 2) {
+      const int k = kk + hf;
+      w2 = __builtin_amdgcn_mfma_f32_32x32x2f32(Ts[rl][k], Wp[0][k][cb + rl] + Wp[1][k][cb + rl], w2, 0, 0, 0);
+    }
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Wp[0][(e >> 2) * 8 + hf * 4 + (e & 3)][32 * wave + rl] = w2[e];
+  }
+  __syncthreads();
+  // Z_rows -= V W2: wave w -> rows 32 (w >> 1) .., columns 32 (w & 1) ..
+  {
+    const int rbk = 32 * (wave >> 1), cb = 32 * (wave & 1);
+    f32x16 acc = {};
+#pragma unroll
+    for (int kk = 0; kk < SBW; kk += 2) {
+      const int k = kk + hf;
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[rbk + rl][k], Wp[0][k][cb + rl], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = rbk + (e >> 2) * 8 + hf * 4 + (e & 3);
+      Zs[r][cb + rl] -= acc[e];
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < CBR * 64; idx += 256) {
+    const int c = idx / CBR, r = idx % CBR;
+    if (r < rows && c < nc) Zz[static_cast<int64_t>(c0 + c) * n + rb + r] = Zs[r][c];
   }
 }
 
@@ -533,7 +618,8 @@ __global__ __launch_bounds__(256) void k_copy_cols(const float* in, int64_t ld_i
 struct SyevLayout {
   int64_t P, vtot, nref;
   size_t v_off, t_off, tau_off, y_off, x_off, s1_off, s2_off, s3_off, wb_off, wb2_off, part_off, pscr_off,
-      bw_off, rf_off, d_off, e_off, lam_off, dp_off, yv_off, total;
+      bw_off, rf_off, d_off, e_off, lam_off, dp_off, yv_off, cbt_off, total;
+  int64_t ng, K0;                 // chase groups of 32 sweeps, steps of sweep 0
 };
 
 SyevLayout syev_layout(int64_t n, int R, int batch) {
@@ -569,6 +655,9 @@ SyevLayout syev_layout(int64_t n, int R, int batch) {
   L.lam_off = take(B * R * 8);
   L.dp_off = take(B * n * R * 8);
   L.yv_off = take(B * n * R * 8);
+  L.ng = (n - 2 + SBW - 1) / SBW;
+  L.K0 = sweep_steps(n, 0);
+  L.cbt_off = take(B * (L.ng > 0 ? L.ng : 1) * (L.K0 > 0 ? L.K0 : 1) * SBW * SBW * 4);
   L.total = off;
   return L;
 }
@@ -729,28 +818,27 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
         return e;
     }
   }
-  // ---- stage 4: back-transformation (chase reflectors, then panel reflectors)
+  // ---- stage 4: back-transformation (chase reflectors in blocks, then panel reflectors)
   {
-    int CT = static_cast<int>(32768 / n);
-    if (CT > 32) CT = 32;
-    if (CT < 1) return hipErrorInvalidValue;
-    const size_t lds = (static_cast<size_t>(CT) * (n + 1) + static_cast<size_t>(sweep_steps(n, 0)) * RFS) *
-                       sizeof(float);
-    constexpr int kMaxLds = 160 * 1024;
-    static bool attr = false;
-    if (!attr) {
-      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chase_back),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds)) != hipSuccess)
-        return e;
-      attr = true;
-    }
-    if (lds > static_cast<size_t>(kMaxLds)) return hipErrorInvalidValue;
-    {
+    float* Tcb = reinterpret_cast<float*>(wb + Lw.cbt_off);
+    const int ng = static_cast<int>(Lw.ng), K0 = static_cast<int>(Lw.K0);
+    const int64_t tstr = Lw.ng * Lw.K0 * SBW * SBW;
+    if (ng > 0 && K0 > 0) {
       ProfScope ps("chase_back", s);
-      k_chase_back<<<dim3(static_cast<unsigned>((R + CT - 1) / CT), batch), 1024, lds, s>>>(
-          Z, n, R, n * n, CT, Rf, Lw.nref * RFS);
+      k_cb_tfac<<<dim3(static_cast<unsigned>(ng * K0), batch), 64, 0, s>>>(Rf, Lw.nref * RFS, static_cast<int>(n),
+                                                                         K0, Tcb, tstr);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      const int nchunk = (R + 63) / 64;
+      const int tmax = 2 * (ng - 1) + K0 - 1;
+      for (int t = 0; t <= tmax; ++t) {
+        const int glo = t - K0 + 1 > 0 ? (t - K0 + 2) / 2 : 0;
+        const int ghi = t / 2 < ng - 1 ? t / 2 : ng - 1;
+        if (ghi < glo) continue;
+        k_cb_apply<<<dim3(static_cast<unsigned>((ghi - glo + 1) * nchunk), batch), 256, 0, s>>>(
+            t, glo, nchunk, Z, static_cast<int>(n), R, n * n, Rf, Lw.nref * RFS, Tcb, tstr, ng, K0);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     ProfScope ps_bb("band_back", s);
     for (int64_t p = Lw.P - 1; p >= 0; --p) {
       const int64_t r = (p + 1) * SBW, mp = n - r;
