@@ -476,46 +476,52 @@ __global__ __launch_bounds__(256) void k_invit(const double* d_g, const double* 
 // (g' = 0 for the last group) orders; blocks of one t touch disjoint rows.
 constexpr int CBR = 2 * SBW;      // staircase rows (63) padded to 64
 
-// T of every block: one wave per (G, s).
+// T of every block: one wave per (G, s).  S = V^T V on fp32 matrix cores
+// (the 64 x 32 staircase), then the recurrence with row `lane` of T in
+// registers (lanes 0..31), unrolled so that every S read is independent.
 __global__ __launch_bounds__(64) void k_cb_tfac(const float* Rf_g, int64_t rf_stride, int n, int K0, float* Tg,
                                                 int64_t t_stride) {
-  __shared__ float Vs[SBW][SBW + 1];     // Vs[i][r] = v_i[r]
-  __shared__ float S[SBW][SBW + 1];      // S[l][i] = v_l^T v_i (l < i)
-  __shared__ float Ts[SBW][SBW + 1];
+  __shared__ float Vs[CBR][SBW + 1];     // staircase V[r][i]
+  __shared__ float S[SBW][SBW + 1];      // S[l][i] = v_l^T v_i
   __shared__ float tau[SBW];
-  const int lane = threadIdx.x, blk = blockIdx.x, G = blk / K0, s = blk % K0;
+  const int lane = threadIdx.x, rl = lane & 31, hf = lane >> 5, blk = blockIdx.x, G = blk / K0, s = blk % K0;
   const int64_t z = blockIdx.y;
   const float* Rf = Rf_g + z * rf_stride;
   const int jg = G * SBW, last = n - 3;
+  for (int idx = lane; idx < CBR * (SBW + 1); idx += 64) (&Vs[0][0])[idx] = 0.f;
+  if (lane < SBW) {
+    const int j = jg + lane;
+    tau[lane] = (j <= last && s < sweep_steps(n, j)) ? Rf[(sweep_offset(n, j) + s) * RFS + SBW] : 0.f;
+  }
+  __syncthreads();
   for (int idx = lane; idx < SBW * SBW; idx += 64) {
     const int i = idx / SBW, r = idx % SBW, j = jg + i;
-    const bool ex = j <= last && s < sweep_steps(n, j);
-    Vs[i][r] = ex ? Rf[(sweep_offset(n, j) + s) * RFS + r] : 0.f;
-    if (r == 0) tau[i] = ex ? Rf[(sweep_offset(n, j) + s) * RFS + SBW] : 0.f;
-    Ts[i][r] = 0.f;
+    if (j <= last && s < sweep_steps(n, j)) Vs[i + r][i] = Rf[(sweep_offset(n, j) + s) * RFS + r];
   }
   __syncthreads();
-  for (int idx = lane; idx < SBW * SBW; idx += 64) {
-    const int l = idx / SBW, i = idx % SBW;
-    float a = 0.f;
-    if (l < i)
-      for (int r = i; r < l + SBW; ++r) a += Vs[l][r - l] * Vs[i][r - i];   // common rows i .. l + 31
-    S[l][i] = a;
+  f32x16 acc = {};
+#pragma unroll
+  for (int kk = 0; kk < CBR; kk += 2) {
+    const int k = kk + hf;
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[k][rl], Vs[k][rl], acc, 0, 0, 0);
   }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) S[(e >> 2) * 8 + hf * 4 + (e & 3)][rl] = acc[e];
   __syncthreads();
-  // row `lane` of T is written only by this lane
-  for (int i = 0; i < SBW; ++i) {
-    if (lane < i) {
-      float a = 0.f;
-      for (int p = lane; p < i; ++p) a += Ts[lane][p] * S[p][i];
-      Ts[lane][i] = -tau[i] * a;
-    } else if (lane == i) {
-      Ts[i][i] = tau[i];
+  if (lane < SBW) {
+    float tr[SBW];
+#pragma unroll
+    for (int i = 0; i < SBW; ++i) {
+      float u = 0.f;
+#pragma unroll
+      for (int p = 0; p < i; ++p)
+        if (p >= lane) u += tr[p] * S[p][i];
+      tr[i] = i < lane ? 0.f : (i == lane ? tau[i] : -tau[i] * u);
     }
+    float* Tb = Tg + z * t_stride + static_cast<int64_t>(blk) * SBW * SBW + lane * SBW;
+#pragma unroll
+    for (int i = 0; i < SBW; ++i) Tb[i] = tr[i];
   }
-  __syncthreads();
-  float* Tb = Tg + z * t_stride + static_cast<int64_t>(blk) * SBW * SBW;
-  for (int idx = lane; idx < SBW * SBW; idx += 64) Tb[idx] = Ts[idx / SBW][idx % SBW];
 }
 
 // The blocks of wavefront step t, one workgroup per (block, 64 columns of Z):
