@@ -395,73 +395,128 @@ __global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double*
 // reciprocal pivots, so each solve is multiply-only; intermediate vectors
 // are rescaled on the fly.  Scratch rp / y: [i][q] interleaved (coalesced
 // across q).
-__global__ __launch_bounds__(256) void k_invit(const double* d_g, const double* e_g, int64_t n, int R,
-                                              const double* lam, double* rp_g, double* y_g, float* Z,
-                                              int64_t z_batch) {
-  __shared__ double red[4];
+constexpr int IVW = 64;          // threads (eigenvectors) per inverse-iteration workgroup
+constexpr int IVC = 16;          // solve steps per register chunk (n is a multiple of 32)
+__device__ __forceinline__ double invit_start(int q, int64_t i) {   // uniform in [0.5, 1.5)
+  const uint64_t hsh = mix64(0x9E3779B97F4A7C15ull * static_cast<uint64_t>(q + 1) + static_cast<uint64_t>(i));
+  return 0.5 + static_cast<double>(hsh >> 11) * 0x1p-53;
+}
+// One thread per eigenvector: the solves run over [i][q] scratch (coalesced
+// over the eigenvectors) in chunks of IVC steps whose loads are issued
+// together; the normalized vector is written by k_invit_out.
+__global__ __launch_bounds__(IVW) void k_invit(const double* d_g, const double* e_g, int64_t n, int R,
+                                              const double* lam, double* rp_g, double* y_g, double* nrm_g) {
   const int64_t z = blockIdx.y;
   const double* d = d_g + z * n;
   const double* e = e_g + z * n;
-  double tn = 0.0;                                  // infinity norm of T (whole block)
-  for (int64_t i = threadIdx.x; i < n; i += 256)
+  double tn = 0.0;                                  // infinity norm of T
+  for (int64_t i = threadIdx.x; i < n; i += IVW)
     tn = fmax(tn, fabs(d[i]) + fabs(e[i]) + (i ? fabs(e[i - 1]) : 0.0));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) tn = fmax(tn, __shfl_xor(tn, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = tn;
-  __syncthreads();
-  const double tnorm = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
-  const int q = blockIdx.x * 256 + threadIdx.x;
+  const int q = blockIdx.x * IVW + threadIdx.x;
   if (q >= R) return;
   double* rp = rp_g + z * n * R;
   double* y = y_g + z * n * R;
   const double lm = lam[z * R + q];
-  const double tiny = fmax(tnorm, DBL_MIN) * DBL_EPSILON;
+  const double tiny = fmax(tn, DBL_MIN) * DBL_EPSILON;
   // L D L^T of T - lam I: pivots p_i = (d_i - lam) - e_{i-1}^2 / p_{i-1}, kept as 1 / p_i
   {
-    double p = d[0] - lm;
-    if (fabs(p) < tiny) p = tiny;
-    double r = 1.0 / p;
-    rp[q] = r;
-    for (int64_t i = 1; i < n; ++i) {
-      p = (d[i] - lm) - e[i - 1] * e[i - 1] * r;
-      if (fabs(p) < tiny) p = tiny;
-      r = 1.0 / p;
-      rp[i * R + q] = r;
+    double r = 0.0;
+    for (int64_t i0 = 0; i0 < n; i0 += IVC) {
+      double rr[IVC];
+#pragma unroll
+      for (int c = 0; c < IVC; ++c) {
+        const int64_t i = i0 + c;
+        double p = (d[i] - lm) - (i ? e[i - 1] * e[i - 1] * r : 0.0);
+        if (fabs(p) < tiny) p = tiny;
+        r = 1.0 / p;
+        rr[c] = r;
+      }
+#pragma unroll
+      for (int c = 0; c < IVC; ++c) rp[(i0 + c) * R + q] = rr[c];
     }
-  }
-  // start: uniform in [0.5, 1.5) from a counter hash of (q, i)
-  for (int64_t i = 0; i < n; ++i) {
-    const uint64_t hsh = mix64(0x9E3779B97F4A7C15ull * static_cast<uint64_t>(q + 1) + static_cast<uint64_t>(i));
-    y[i * R + q] = 0.5 + static_cast<double>(hsh >> 11) * 0x1p-53;
   }
   double sc = 1.0;
   for (int it = 0; it < 3; ++it) {
     // forward: L u = sc * y   (L unit lower, l_i = e_{i-1} / p_{i-1})
-    double u = y[q] * sc;
-    y[q] = u;
-    for (int64_t i = 1; i < n; ++i) {
-      u = y[i * R + q] * sc - e[i - 1] * rp[(i - 1) * R + q] * u;
-      y[i * R + q] = u;
+    double u = 0.0, rprev = 0.0;
+    for (int64_t i0 = 0; i0 < n; i0 += IVC) {
+      double yy[IVC], rr[IVC];
+#pragma unroll
+      for (int c = 0; c < IVC; ++c) {
+        const int64_t i = i0 + c;
+        yy[c] = it == 0 ? invit_start(q, i) : y[i * R + q];
+        rr[c] = rp[i * R + q];
+      }
+#pragma unroll
+      for (int c = 0; c < IVC; ++c) {
+        const int64_t i = i0 + c;
+        u = yy[c] * sc - (i ? e[i - 1] * rprev * u : 0.0);
+        yy[c] = u;
+        rprev = rr[c];
+      }
+#pragma unroll
+      for (int c = 0; c < IVC; ++c) y[(i0 + c) * R + q] = yy[c];
     }
     // D L^T x = u:  x_i = (u_i - e_i x_{i+1}) / p_i
-    double xs = y[(n - 1) * R + q] * rp[(n - 1) * R + q];
-    y[(n - 1) * R + q] = xs;
-    double mx = fabs(xs);
-    for (int64_t i = n - 2; i >= 0; --i) {
-      xs = (y[i * R + q] - e[i] * xs) * rp[i * R + q];
-      y[i * R + q] = xs;
-      mx = fmax(mx, fabs(xs));
+    double xs = 0.0, mx = 0.0;
+    for (int64_t i0 = n - IVC; i0 >= 0; i0 -= IVC) {
+      double yy[IVC], rr[IVC];
+#pragma unroll
+      for (int c = 0; c < IVC; ++c) {
+        yy[c] = y[(i0 + c) * R + q];
+        rr[c] = rp[(i0 + c) * R + q];
+      }
+#pragma unroll
+      for (int c = IVC - 1; c >= 0; --c) {
+        const int64_t i = i0 + c;
+        xs = (yy[c] - (i + 1 < n ? e[i] * xs : 0.0)) * rr[c];
+        yy[c] = xs;
+        mx = fmax(mx, fabs(xs));
+      }
+#pragma unroll
+      for (int c = 0; c < IVC; ++c) y[(i0 + c) * R + q] = yy[c];
     }
     sc = mx > 0.0 ? 1.0 / mx : 1.0;
   }
   double s2 = 0.0;
-  for (int64_t i = 0; i < n; ++i) {
-    const double t = y[i * R + q] * sc;
-    s2 += t * t;
+  for (int64_t i0 = 0; i0 < n; i0 += IVC) {
+    double yy[IVC];
+#pragma unroll
+    for (int c = 0; c < IVC; ++c) yy[c] = y[(i0 + c) * R + q];
+#pragma unroll
+    for (int c = 0; c < IVC; ++c) {
+      const double t = yy[c] * sc;
+      s2 += t * t;
+    }
   }
-  const double nrm = sc / sqrt(s2);
-  float* zc = Z + z * z_batch + static_cast<int64_t>(q) * n;
-  for (int64_t i = 0; i < n; ++i) zc[i] = static_cast<float>(y[i * R + q] * nrm);
+  nrm_g[z * R + q] = sc / sqrt(s2);
+}
+
+// Z[:, q] = y[:, q] * nrm[q] as fp32, through a 32 x 32 LDS transpose ([i][q]
+// scratch to column-major Z).
+__global__ __launch_bounds__(256) void k_invit_out(const double* y_g, const double* nrm_g, int64_t n, int R,
+                                                   float* Z, int64_t z_batch) {
+  __shared__ float tile[32][33];
+  const int64_t z = blockIdx.z;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 32;
+  const int q0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const double* y = y_g + z * n * R;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t i = i0 + ty + 8 * k;
+    const int q = q0 + tx;
+    tile[ty + 8 * k][tx] = (i < n && q < R) ? static_cast<float>(y[i * R + q] * nrm_g[z * R + q]) : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int q = q0 + ty + 8 * k;
+    const int64_t i = i0 + tx;
+    if (i < n && q < R) Z[z * z_batch + static_cast<int64_t>(q) * n + i] = tile[tx][ty + 8 * k];
+  }
 }
 
 // Stage 2 back-transformation in blocks.  Block (G, s) gathers the step-s
@@ -624,7 +679,7 @@ __global__ __launch_bounds__(256) void k_copy_cols(const float* in, int64_t ld_i
 struct SyevLayout {
   int64_t P, vtot, nref;
   size_t v_off, t_off, tau_off, y_off, x_off, s1_off, s2_off, s3_off, wb_off, wb2_off, part_off, pscr_off,
-      bw_off, rf_off, d_off, e_off, lam_off, dp_off, yv_off, cbt_off, total;
+      bw_off, rf_off, d_off, e_off, lam_off, dp_off, yv_off, nrm_off, cbt_off, total;
   int64_t ng, K0;                 // chase groups of 32 sweeps, steps of sweep 0
 };
 
@@ -661,6 +716,7 @@ SyevLayout syev_layout(int64_t n, int R, int batch) {
   L.lam_off = take(B * R * 8);
   L.dp_off = take(B * n * R * 8);
   L.yv_off = take(B * n * R * 8);
+  L.nrm_off = take(B * R * 8);
   L.ng = (n - 2 + SBW - 1) / SBW;
   L.K0 = sweep_steps(n, 0);
   L.cbt_off = take(B * (L.ng > 0 ? L.ng : 1) * (L.K0 > 0 ? L.K0 : 1) * SBW * SBW * 4);
@@ -811,12 +867,16 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
       attr = true;
     }
     if (lds > 65536) return hipErrorInvalidValue;
-    const unsigned gx = static_cast<unsigned>((R + 255) / 256);
+    const unsigned gx = static_cast<unsigned>((R + IVW - 1) / IVW);
+    double* nrm = reinterpret_cast<double*>(wb + Lw.nrm_off);
     {
       ProfScope ps("tri_eig", s);
       k_bisect<<<dim3(static_cast<unsigned>((4 * R + 255) / 256), batch), 256, lds, s>>>(dd, ee, n, R, lam);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      k_invit<<<dim3(gx, batch), 256, 0, s>>>(dd, ee, n, R, lam, dp, yv, Z, n * n);
+      k_invit<<<dim3(gx, batch), IVW, 0, s>>>(dd, ee, n, R, lam, dp, yv, nrm);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      k_invit_out<<<dim3(static_cast<unsigned>((n + 31) / 32), static_cast<unsigned>((R + 31) / 32), batch), 256, 0,
+                    s>>>(yv, nrm, n, R, Z, n * n);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (lam_out) {
