@@ -322,7 +322,13 @@ __device__ __forceinline__ int sturm_count(const double* d, const double* e2, in
   if (fabs(q) < pivmin) q = -pivmin;
   cnt += q < 0.0;
   for (int64_t i = 1; i < n; ++i) {
-    q = (d[i] - x) - e2[i - 1] / q;
+    // e2 / q through the hardware reciprocal refined by two Newton steps (a
+    // few ulps, as the count needs only the pivot signs); |q| >= pivmin
+    // keeps the reciprocal finite
+    double r = __builtin_amdgcn_rcp(q);
+    r = __builtin_fma(__builtin_fma(-q, r, 1.0), r, r);
+    r = __builtin_fma(__builtin_fma(-q, r, 1.0), r, r);
+    q = (d[i] - x) - e2[i - 1] * r;
     if (fabs(q) < pivmin) q = -pivmin;
     cnt += q < 0.0;
   }
@@ -430,7 +436,9 @@ __global__ __launch_bounds__(IVW) void k_invit(const double* d_g, const double* 
         const int64_t i = i0 + c;
         double p = (d[i] - lm) - (i ? e[i - 1] * e[i - 1] * r : 0.0);
         if (fabs(p) < tiny) p = tiny;
-        r = 1.0 / p;
+        r = __builtin_amdgcn_rcp(p);                 // 1 / p: reciprocal + two Newton steps
+        r = __builtin_fma(__builtin_fma(-p, r, 1.0), r, r);
+        r = __builtin_fma(__builtin_fma(-p, r, 1.0), r, r);
         rr[c] = r;
       }
 #pragma unroll
