@@ -243,6 +243,10 @@ def main():
                             "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                             "algorithmic_bytes_per_call": int(dec_bytes),
                             "avg_call_ms": round(dec_ms, 5)},
+        # the other kernels that account their work, from the per-kernel
+        # breakdown step (events around every launch, outside the timed steps)
+        "roofline_more": {k: roofline_for(k, kstats[k], cfg.name) for k in ROOF
+                          if k != dominant and k in kstats and kstats[k]["launches"] and kstats[k]["bytes"] > 0},
         "kernel_ms_per_step": {k: round(v["total_ms"], 3) for k, v in kstats.items()},
         "kernel_launches_per_step": {k: v["launches"] for k, v in kstats.items()},
     }
@@ -274,18 +278,23 @@ COMPARE_EXACT = {"mistral7b_t1024_flash"}
 CPU_SAMPLE = {"mistral7b_t4096_2x": 24, "mistral7b_t1024_flash": 64, "llama13b_t4096_2x": 2,
               "mistral7b_t32768_3x": 4}
 
-KERNELS = ("jacobi_update", "jacobi_solve", "jacobi128", "qr_panel", "gemm", "band", "chase", "tri_eig",
-           "chase_back", "band_back", "encode_residual", "decode_w", "decode")
-RIDGE_FP32 = MFMA_FP32_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)   # flop/B
+KERNELS = ("jacobi_update", "jacobi_solve", "jacobi128", "qr_panel", "gemm", "gemm_bf16", "band", "chase",
+           "tri_eig", "chase_back", "band_back", "encode_residual", "decode_w", "decode")
 CSRC = os.path.join(ROOT, "kv_cache_compression_mode_amd", "csrc")
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 # kernels whose launches account their algorithmic work (bytes, flops):
-# name -> (description, symbol in profiler traces, sources of the kernel)
+# name -> (description, symbol, pattern of its kernel names in profiler
+#          traces, sources of the kernel, peak of the matrix cores it runs on
+#          in TFLOP/s)
 ROOF = {
-    "gemm": ("k_gemm: strided batched GEMM on fp32 matrix cores (all launches of the step: Grams, "
-             "band reduction, back-transformation, factor recovery, core products)",
-             "k_gemm", ("gemm.hip", "device.hpp")),
+    "gemm": ("k_gemm: strided batched 64x64-tile GEMM on fp32 matrix cores (the fp32 products of a step: "
+             "band reduction, panel back-transformation, QR trailing updates, small products)",
+             "k_gemm", r"k_gemm(<|_bf16\b)", ("gemm.hip", "device.hpp"), MFMA_FP32_PEAK_TFLOPS),
+    "gemm_bf16": ("k_gemm_x: 128x128-tile GEMM on bf16 matrix cores (token and feature Grams, factor recovery, "
+                  "Rayleigh and core products; fp32 operands enter as bf16 hi + lo)",
+                  "k_gemm_x", r"k_gemm_x<", ("gemm.hip", "device.hpp"), MFMA_BF16_PEAK_TFLOPS),
     "jacobi_update": ("k_jac_update: block-Jacobi rotation of A and V, fp32 matrix cores",
-                      "k_jac_update", ("eig.hip", "device.hpp")),
+                      "k_jac_update", r"k_jac_update\b", ("eig.hip", "device.hpp"), MFMA_FP32_PEAK_TFLOPS),
 }
 
 
@@ -294,7 +303,7 @@ def traffic_file(symbol, workload):
 
 
 def kernel_sources(name):
-    return tuple(os.path.join(CSRC, f) for f in ROOF[name][2])
+    return tuple(os.path.join(CSRC, f) for f in ROOF[name][3])
 
 
 def sources_sha256(paths):
@@ -318,17 +327,18 @@ def measured_traffic(source_paths, record_path):
     return rec["traffic_bytes_per_launch"]
 
 
-def _pmc_means(path, counter, symbol):
-    """Mean counter value (KiB per dispatch) of one kernel and of the
-    calibration copy (the last elementwise dispatch: the copies follow the
-    fill that allocates their source)."""
+def _pmc_means(path, counter, symbol, pattern):
+    """Mean counter value (KiB per dispatch) of one kernel (trace names
+    matching `pattern`) and of the calibration copy (the last elementwise
+    dispatch: the copies follow the fill that allocates their source)."""
     import csv
+    import re
     ker, copy = [], []
     with open(path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter:
                 continue
-            if symbol in r["Kernel_Name"]:
+            if re.search(pattern, r["Kernel_Name"]):
                 ker.append(float(r["Counter_Value"]))
             elif "elementwise" in r["Kernel_Name"]:
                 copy.append(float(r["Counter_Value"]))
@@ -339,10 +349,10 @@ def _pmc_means(path, counter, symbol):
 
 def record_traffic(fetch_csv, write_csv, copy_bytes, name="gemm", workload="mistral7b_t4096_2x",
                    record_path=None, source_paths=None):
-    symbol = ROOF[name][1]
+    symbol, pattern = ROOF[name][1], ROOF[name][2]
     source_paths = source_paths or kernel_sources(name)
-    jf, cf, n = _pmc_means(fetch_csv, "FETCH_SIZE", symbol)
-    jw, cw, _ = _pmc_means(write_csv, "WRITE_SIZE", symbol)
+    jf, cf, n = _pmc_means(fetch_csv, "FETCH_SIZE", symbol, pattern)
+    jw, cw, _ = _pmc_means(write_csv, "WRITE_SIZE", symbol, pattern)
     kib = copy_bytes / 1024.0
     f_scale, w_scale = kib / cf, kib / cw      # known bytes / counted KiB of a plain copy
     rec = {"kernel": symbol, "workload": f"{workload} (one step)", "dispatches": n,
@@ -373,17 +383,19 @@ def roofline_for(name, st, workload):
     ai = flops_l / max(bytes_l, 1.0)
     gbps = bytes_l / (avg_ms * 1e-3) / 1e9
     tflops = flops_l / (avg_ms * 1e-3) / 1e12
-    if ai < RIDGE_FP32:
+    peak_tf = ROOF[name][4]
+    ridge = peak_tf * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if ai < ridge:
         bound, achieved, peak, unit = "hbm", gbps, HBM_PEAK_GBPS, "GB/s"
     else:
-        bound, achieved, peak, unit = "mfma", tflops, MFMA_FP32_PEAK_TFLOPS, "TFLOP/s"
-    desc, symbol, _ = ROOF[name]
+        bound, achieved, peak, unit = "mfma", tflops, peak_tf, "TFLOP/s"
+    desc, symbol = ROOF[name][0], ROOF[name][1]
     return {"kernel": desc, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4),
             "traffic": measured_traffic(kernel_sources(name), traffic_file(symbol, workload)),
             "algorithmic_bytes_per_launch": round(bytes_l),
             "algorithmic_flops_per_launch": round(flops_l),
-            "arithmetic_intensity": round(ai, 2), "ridge_fp32": round(RIDGE_FP32, 2),
+            "arithmetic_intensity": round(ai, 2), "ridge": round(ridge, 2),
             "GBps": round(gbps, 1), "TFLOPs": round(tflops, 2),
             "avg_launch_ms": round(avg_ms, 5), "launches": st["launches"]}
 

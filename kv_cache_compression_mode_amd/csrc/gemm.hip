@@ -681,14 +681,14 @@ void launch_x_b(const GemmArgs& g, int xb, dim3 grid, hipStream_t s) {
 hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s) {
   GemmArgs g = g0;
   if (g.ksplit < 1 || !g.partial) g.ksplit = 1;
-  ProfScope ps("gemm", s);
-  if (prof_enabled("gemm")) {   // dense flops; operands once, C written (and read when beta != 0) once
+  // algorithmic work: dense flops; operands read once, C written (and read when beta != 0) once
+  auto account = [&](const char* name) {
+    if (!prof_enabled(name)) return;
     const double ea = g.a_dtype == kBF16 ? 2 : 4, eb = g.b_dtype == kBF16 ? 2 : 4;
     const double ec = g.c_dtype == kBF16 ? 2 : 4;
-    prof_add_work("gemm",
-                  batch * (g.M * g.K * ea + g.K * g.N * eb + g.M * g.N * ec * (g.beta != 0.f ? 2 : 1)),
+    prof_add_work(name, batch * (g.M * g.K * ea + g.K * g.N * eb + g.M * g.N * ec * (g.beta != 0.f ? 2 : 1)),
                   2.0 * g.M * g.N * g.K * batch);
-  }
+  };
   // 128 x 128 bf16 matrix-core tiles when the operands allow 16-byte loads
   // (at least one of them bf16); a column-major C is produced as the
   // row-major C^T = B^T A^T so that its stores run along rows
@@ -706,6 +706,8 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s) {
       x.kchunk = (x.K + x.ksplit - 1) / x.ksplit;
       x.kchunk = (x.kchunk + XK - 1) / XK * XK;
       dim3 grid((x.M + XT - 1) / XT, (x.N + XT - 1) / XT, batch * x.ksplit);
+      ProfScope ps("gemm_bf16", s);
+      account("gemm_bf16");
       if (xa == kOpBfK) launch_x_b<kOpBfK>(x, xb, grid, s);
       else if (xa == kOpBfM) launch_x_b<kOpBfM>(x, xb, grid, s);
       else launch_x_b<kOpF32K>(x, xb, grid, s);
@@ -738,6 +740,8 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s) {
   g.kchunk = (g.K + g.ksplit - 1) / g.ksplit;
   g.kchunk = (g.kchunk + kt - 1) / kt * kt;            // chunks start on tile edges
   dim3 grid((g.M + BM - 1) / BM, (g.N + BN - 1) / BN, batch * g.ksplit);
+  ProfScope ps("gemm", s);
+  account("gemm");
   if (bf) k_gemm_bf16<<<grid, 256, 0, s>>>(g);
   else if (g.a_dtype == kBF16 && g.b_dtype == kBF16) k_gemm<uint16_t, uint16_t><<<grid, 256, 0, s>>>(g);
   else if (g.a_dtype == kBF16) k_gemm<uint16_t, float><<<grid, 256, 0, s>>>(g);

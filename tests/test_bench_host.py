@@ -48,6 +48,33 @@ def test_record_and_invalidate(tmp_path):
     assert bench.measured_traffic((str(src),), str(tmp_path / "missing.json")) is None
 
 
+def test_gemm_records_keep_their_kernels(tmp_path):
+    """The fp32 GEMM record counts k_gemm<...> and k_gemm_bf16, the bf16
+    matrix-core record only k_gemm_x<...> (one name is a prefix of the other)."""
+    copy = 1 << 30
+    kib = copy / 1024
+    names = {"jolt::(anonymous namespace)::k_gemm<float, float>(jolt::GemmArgs)": 10.0,
+             "jolt::(anonymous namespace)::k_gemm_bf16(jolt::GemmArgs)": 30.0,
+             "void jolt::(anonymous namespace)::k_gemm_x<2, 1>(jolt::GemmArgs)": 1000.0}
+    for counter, fname, cval in (("FETCH_SIZE", "f.csv", kib / 2), ("WRITE_SIZE", "w.csv", kib)):
+        with open(tmp_path / fname, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Correlation_Id", "Dispatch_Id", "Counter_Name", "Counter_Value",
+                                              "Kernel_Name"])
+            w.writeheader()
+            rows = list(names.items()) + [("void at::native::vectorized_elementwise_k", cval)] * 2
+            for i, (kn, v) in enumerate(rows):
+                w.writerow(dict(Correlation_Id=i, Dispatch_Id=i, Counter_Name=counter, Counter_Value=v,
+                                Kernel_Name=kn))
+    src = tmp_path / "k.hip"
+    src.write_text("kernel")
+    for name, want in (("gemm", 20.0), ("gemm_bf16", 1000.0)):
+        rec_path = str(tmp_path / f"{name}.json")
+        bench.record_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), copy, name, "w", rec_path,
+                             (str(src),))
+        rec = json.load(open(rec_path))
+        assert rec["fetch_kib_per_dispatch"] == want and rec["write_kib_per_dispatch"] == want
+
+
 @pytest.mark.parametrize("path", sorted(glob.glob(os.path.join(bench.ROOT, "profiles", "traffic_*.json"))))
 def test_committed_record_matches_layout(path):
     rec = json.load(open(path))
@@ -68,6 +95,13 @@ def test_roofline_bound_choice():
     st = dict(launches=2, total_ms=2.0, bytes=2e9, flops=2e9)
     r = bench.roofline_for("gemm", st, "no_such_workload")
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and abs(r["achieved"] - 1000.0) < 1e-9
+    # the bf16 matrix-core GEMM: ridge 2500 / 8 = 312.5 flop/B
+    st = dict(launches=2, total_ms=2.0, bytes=2e9, flops=2e9 * 30)
+    r = bench.roofline_for("gemm_bf16", st, "no_such_workload")
+    assert r["bound"] == "hbm" and abs(r["ridge"] - 312.5) < 1e-9
+    st = dict(launches=2, total_ms=2.0, bytes=2e9, flops=2e9 * 400)
+    r = bench.roofline_for("gemm_bf16", st, "no_such_workload")
+    assert r["bound"] == "mfma" and r["peak"] == 2500.0 and r["frac"] == round(400.0 / 2500.0, 4)
 
 
 def test_multi_gpu_refused():
