@@ -411,6 +411,8 @@ struct AllocWS {
   float* GD; float* GDc; float* VD;
   int* order; float* Ucm; float* Vr; float* P; double* lam_tmp; float* qtau; int* perm; float* sgn;
   float* Om; float* Y; float* Z; float* Bm; float* Wr; float* Wd;
+  // the feature-mode factor's own scratch (it runs beside the token path)
+  float* qtauD; double* lamDt; int* permD; float* sgnD;
   size_t bytes;
   int chunk;
 };
@@ -504,6 +506,10 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base) {
     w.Wr = c.take<float>(static_cast<size_t>(chunk) * d.ell * R);
   }
   w.Wd = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
+  w.qtauD = c.take<float>(householder_qr_work_floats(d.D, d.D, chunk));
+  w.lamDt = c.take<double>(static_cast<size_t>(chunk) * d.D);
+  w.permD = c.take<int>(static_cast<size_t>(chunk) * d.D);
+  w.sgnD = c.take<float>(static_cast<size_t>(chunk) * d.D);
   w.bytes = c.off;
   return w;
 }
@@ -590,6 +596,49 @@ void run_jacobi(float* A, float* V, int64_t n, int batch, const AllocWS& w, hipS
   }
 }
 
+// A second stream per device (default priority) for the feature-mode factor,
+// which depends only on the feature Gram and runs beside the token path; fork
+// and join through events.  Created on first use, kept for the process.
+struct AuxStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+AuxStream& aux_stream() {
+  static std::vector<AuxStream> per_dev;
+  int dev = 0;
+  ck(hipGetDevice(&dev));
+  if (static_cast<int>(per_dev.size()) <= dev) per_dev.resize(dev + 1);
+  AuxStream& a = per_dev[dev];
+  if (!a.s) {
+    ck(hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking));
+    ck(hipEventCreateWithFlags(&a.fork, hipEventDisableTiming));
+    ck(hipEventCreateWithFlags(&a.join, hipEventDisableTiming));
+  }
+  return a;
+}
+// Runs the feature-mode factor on the auxiliary stream after the work queued
+// on s so far (the tridiagonal path; the Jacobi path shares scratch and stays
+// on s); join() makes s wait for it.
+struct FeatureFork {
+  AuxStream* a = nullptr;
+  hipStream_t s;
+  explicit FeatureFork(hipStream_t s_) : s(s_) {}
+  hipStream_t start() {
+    if (eig_jacobi()) return s;
+    a = &aux_stream();
+    ck(hipEventRecord(a->fork, s));
+    ck(hipStreamWaitEvent(a->s, a->fork, 0));
+    return a->s;
+  }
+  void done() {
+    if (a) ck(hipEventRecord(a->join, a->s));
+  }
+  void join() {
+    if (a) ck(hipStreamWaitEvent(s, a->join, 0));
+    a = nullptr;
+  }
+};
+
 // Feature-mode factor of `batch` tensors from their D x D Grams in w.GD.
 void feature_factor(const Dims& d, int batch, int t0, const AllocWS& w, hipStream_t s) {
   const int64_t D = d.D;
@@ -601,7 +650,7 @@ void feature_factor(const Dims& d, int batch, int t0, const AllocWS& w, hipStrea
   } else {
     ck(syev_top(w.GD, D, batch, static_cast<int>(D), w.Vr, nullptr, w.syevD, s));
   }
-  ck(householder_qr(w.Vr, D, D, D, D * D, batch, w.qtau, s));
+  ck(householder_qr(w.Vr, D, D, D, D * D, batch, w.qtauD, s));
   // Rayleigh quotients diag(U^T G U): W = G U (column-major), then column dots
   GemmArgs g = gemm0();
   g.M = D; g.N = D; g.K = D;
@@ -609,9 +658,9 @@ void feature_factor(const Dims& d, int batch, int t0, const AllocWS& w, hipStrea
   g.B = w.Vr; g.bk = plain(1); g.bn = plain(D); g.b_batch = D * D;
   g.C = w.Wd; g.c_m = 1; g.c_n = D; g.c_batch = D * D;
   ck(launch_gemm(g, batch, s));
-  ck(launch_col_dot(w.Vr, w.Wd, D, D, D, D * D, batch, w.lam_tmp, D, s));
-  ck(finalize_factor_ws(w.Vr, D, D, D, D * D, w.lam_tmp, D, w.UD + static_cast<size_t>(t0) * D * D, D,
-                        D * D, w.lamD + static_cast<size_t>(t0) * D, D, batch, w.perm, w.sgn, s));
+  ck(launch_col_dot(w.Vr, w.Wd, D, D, D, D * D, batch, w.lamDt, D, s));
+  ck(finalize_factor_ws(w.Vr, D, D, D, D * D, w.lamDt, D, w.UD + static_cast<size_t>(t0) * D * D, D,
+                        D * D, w.lamD + static_cast<size_t>(t0) * D, D, batch, w.permD, w.sgnD, s));
 }
 
 // Token-mode eigenvalues as Rayleigh quotients ||X_(T)^T u_j||^2 of the
@@ -660,8 +709,13 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     gd.ksplit = gram_d_ksplit(d); gd.partial = w.GDpart;
     ck(launch_gemm(gd, batch, s));
   }
-  feature_factor(d, batch, t0, w, s);
-  if (R == 0) return;
+  FeatureFork ff(s);
+  feature_factor(d, batch, t0, w, ff.start());
+  ff.done();
+  if (R == 0) {
+    ff.join();
+    return;
+  }
   // leading eigenvectors V_R of the token Gram, column-major with leading dimension ldv
   const float* VR;
   int64_t ldv, vr_batch;
@@ -695,6 +749,7 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   }
   ck(householder_qr(w.Ucm, T, R, T, T * R, batch, w.qtau, s));
   token_finalize(d, batch, t0, w, xdt, s);
+  ff.join();
 }
 
 void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, int q, uint64_t seed,
@@ -710,9 +765,14 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     gd.C = w.GD; gd.c_m = D; gd.c_n = 1; gd.c_batch = D * D;
     gd.ksplit = gram_d_ksplit(d); gd.partial = w.GDpart;
     ck(launch_gemm(gd, batch, s));
-    feature_factor(d, batch, t0, w, s);
   }
-  if (R == 0) return;
+  FeatureFork ff(s);
+  feature_factor(d, batch, t0, w, ff.start());
+  ff.done();
+  if (R == 0) {
+    ff.join();
+    return;
+  }
   ck(launch_sketch(w.Om, HD, ell, seed, w.tags, batch, s));
   auto AY = [&](const float* Bsrc, int64_t ldb, bool b_rowmajor, float* out) {
     // out (T x ell, column-major) = X_(T) B, B is HD x ell
@@ -771,6 +831,7 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   }
   ck(householder_qr(w.Ucm, T, R, T, T * R, batch, w.qtau, s));
   token_finalize(d, batch, t0, w, xdt, s);
+  ff.join();
 }
 
 int64_t rtp_of(int r_T) { return (static_cast<int64_t>(r_T) + 31) / 32 * 32; }
