@@ -2,7 +2,7 @@
 
 One step = the whole path over one synthetic cache: spectra, factors and the
 Lagrangian-dual allocation of all layers x {K, V} (jolt_allocate), encode of
-every tensor (jolt_encode), decode of every tensor (jolt_decode_many).  The
+every tensor (jolt_encode_many), decode of every tensor (jolt_decode_many).  The
 default workload is the Mistral-7B-v0.3-shaped GQA cache: 32 layers x {K, V},
 8 KV heads, T = 4096, D = 128, bf16, 2x byte budget, exact Gram factors.
 ``--config`` selects another cache workload: the LLaMA-2-13B-shaped MHA cache
@@ -110,12 +110,9 @@ def main():
         ev[0].record(stream)
         res = jolt.allocate(xs, ratio=cfg.ratio, method=method, bits=cfg.bits, seed=cfg.seed)
         ev[1].record(stream)
-        blobs, choices = [], []
-        for i, x in enumerate(flat):
-            ch = res.choice_of(i // 2, i % 2)
-            Ut, Ud = res.factors(i)
-            blobs.append(jolt.encode(x, ch, Ut, Ud, rot, seed=cfg.seed))
-            choices.append(ch)
+        choices = [res.choice_of(i // 2, i % 2) for i in range(len(flat))]
+        factors = [res.factors(i) for i in range(len(flat))]
+        blobs = jolt.encode_many(flat, choices, factors, rot, seed=cfg.seed)
         ev[2].record(stream)
         dws = torch.empty(decode_ws_bytes(choices), dtype=torch.uint8, device=dev)
         decode_all(blobs, choices, dws)

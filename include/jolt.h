@@ -114,6 +114,9 @@ size_t jolt_encode_workspace_bytes(const jolt_shape* shape, jolt_choice choice);
 size_t jolt_decode_workspace_bytes(const jolt_shape* shape, jolt_choice choice);
 size_t jolt_decode_many_workspace_bytes(int32_t n, const jolt_shape* shape,
                                         const jolt_choice* choices);
+/* Device workspace of jolt_encode_many (0 if the arguments are invalid). */
+size_t jolt_encode_many_workspace_bytes(int32_t n, const jolt_shape* shape,
+                                        const jolt_choice* choices);
 
 /* Bytes of a prepared rotation (jolt_rotation). */
 size_t jolt_rotation_bytes(int32_t D);
@@ -162,6 +165,26 @@ jolt_status jolt_encode(const jolt_shape* shape, const void* x_dev, jolt_choice 
                         const void* rot_dev, uint64_t seed,
                         void* blob_dev, size_t blob_bytes,
                         void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Encode n tensors of one shape: record i from x_dev[i] with choices[i] and
+ * the factors U_T_dev[i] (fp32 [T][ld_T[i]]) and U_D_dev[i] (fp32
+ * [D][ld_D[i]]) into blob_dev[i] (blob_bytes[i] >= jolt_blob_bytes).  The
+ * records are those jolt_encode writes, byte for byte (the same kernels and
+ * arithmetic, batched over the tensors of each (r_T, r_D) and over all
+ * tensors for the residual, rotation and quantization); the factor arrays
+ * may be NULL when no choice has r_T > 0.  All arrays are host arrays of
+ * length n; the device pointers must stay valid until the stream reaches the
+ * end of the call's work.  ws_bytes >= jolt_encode_many_workspace_bytes.
+ * Synchronizes `stream` once (uploading the pointer tables), then
+ * asynchronous.  Errors: EINVAL, ENOSPACE, EHIP.
+ * Source: JoLT abstract (the compressed cache: Tucker parts plus the
+ * JL-rotated, quantized residual of every layer's K and V). */
+jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choice* choices,
+                             const void* const* x_dev, const float* const* U_T_dev,
+                             const int32_t* ld_T, const float* const* U_D_dev,
+                             const int32_t* ld_D, const void* rot_dev, uint64_t seed,
+                             void* const* blob_dev, const size_t* blob_bytes,
+                             void* ws_dev, size_t ws_bytes, void* stream);
 
 /* Decode one record: X^_h = U_T G_h U_D^T + dequant(codes)_h Q, written to
  * xhat_dev in shape->dtype.  shape/choice must describe the record (the

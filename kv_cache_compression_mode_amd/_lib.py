@@ -61,6 +61,7 @@ SIGNATURES = {
     "jolt_encode_workspace_bytes": (C.c_size_t, [C.POINTER(Shape), Choice]),
     "jolt_decode_workspace_bytes": (C.c_size_t, [C.POINTER(Shape), Choice]),
     "jolt_decode_many_workspace_bytes": (C.c_size_t, [C.c_int32, C.POINTER(Shape), C.POINTER(Choice)]),
+    "jolt_encode_many_workspace_bytes": (C.c_size_t, [C.c_int32, C.POINTER(Shape), C.POINTER(Choice)]),
     "jolt_rotation_bytes": (C.c_size_t, [C.c_int32]),
     "jolt_allocate": (C.c_int, [C.POINTER(AllocReq), C.POINTER(C.c_void_p), C.c_void_p, C.c_size_t,
                                 C.c_void_p, C.POINTER(Plan)]),
@@ -70,6 +71,10 @@ SIGNATURES = {
     "jolt_encode": (C.c_int, [C.POINTER(Shape), C.c_void_p, Choice, C.c_void_p, C.c_int32, C.c_void_p,
                               C.c_int32, C.c_void_p, C.c_uint64, C.c_void_p, C.c_size_t, C.c_void_p,
                               C.c_size_t, C.c_void_p]),
+    "jolt_encode_many": (C.c_int, [C.c_int32, C.POINTER(Shape), C.POINTER(Choice), C.POINTER(C.c_void_p),
+                                   C.POINTER(C.c_void_p), C.POINTER(C.c_int32), C.POINTER(C.c_void_p),
+                                   C.POINTER(C.c_int32), C.c_void_p, C.c_uint64, C.POINTER(C.c_void_p),
+                                   C.POINTER(C.c_size_t), C.c_void_p, C.c_size_t, C.c_void_p]),
     "jolt_decode": (C.c_int, [C.POINTER(Shape), Choice, C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_size_t, C.c_void_p]),
     "jolt_decode_many": (C.c_int, [C.c_int32, C.POINTER(Shape), C.POINTER(Choice), C.POINTER(C.c_void_p),

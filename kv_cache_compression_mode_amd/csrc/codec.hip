@@ -130,7 +130,7 @@ constexpr int EK = 32;        // K chunk
 constexpr int EWP = D + 4;    // LDS row stride of a staged B chunk (16-byte rows)
 
 template <typename TX>
-__global__ __launch_bounds__(256, 2) void k_encode_residual(EncodeArgs a) {
+__device__ __forceinline__ void encode_tile(const EncodeArgs& a) {
   __shared__ float Us[EK][ER + 1];                               // Ut chunk, [k][row]
   __shared__ __attribute__((aligned(16))) float Bs[EK][EWP];     // W_h or Q^T chunk, [k][feature]
   __shared__ float Rs[ER][D + 1];                                // residual rows
@@ -222,6 +222,17 @@ __global__ __launch_bounds__(256, 2) void k_encode_residual(EncodeArgs a) {
     quantize_group(y0[i], a.bits, ta < a.T, sc + ga, cd + ga * a.bits);
     quantize_group(y1[i], a.bits, tb < a.T, sc + gb, cd + gb * a.bits);
   }
+}
+
+template <typename TX>
+__global__ __launch_bounds__(256, 2) void k_encode_residual(EncodeArgs a) {
+  encode_tile<TX>(a);
+}
+// Tensors of one shape in one launch: blockIdx.z selects the tensor's arguments.
+template <typename TX>
+__global__ __launch_bounds__(256, 2) void k_encode_residual_many(const EncodeArgs* list) {
+  const EncodeArgs a = list[blockIdx.z];
+  encode_tile<TX>(a);
 }
 
 // ------------------------------------------------------------------ decode
@@ -414,6 +425,16 @@ hipError_t launch_encode_residual(const EncodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_encode_residual_many(const EncodeArgs* list_dev, int n, int64_t H, int64_t T, int x_dtype,
+                                       hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid((T + ER - 1) / ER, H, n);
+  ProfScope ps("encode_residual", s);
+  if (x_dtype == kBF16) k_encode_residual_many<uint16_t><<<grid, 256, 0, s>>>(list_dev);
+  else k_encode_residual_many<float><<<grid, 256, 0, s>>>(list_dev);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_batch(const DecBatch& b, hipStream_t s) {
   if (b.wtiles_total > 0) {
     ProfScope ps("decode_w", s);
@@ -427,6 +448,14 @@ hipError_t launch_decode_batch(const DecBatch& b, hipStream_t s) {
   return hipGetLastError();
 }
 
+__global__ void k_header_many(uint32_t* const* blobs, const uint32_t* words) {
+  if (threadIdx.x < 16) blobs[blockIdx.x][threadIdx.x] = words[blockIdx.x * 16 + threadIdx.x];
+}
+hipError_t launch_write_headers(uint32_t* const* blobs_dev, const uint32_t* words_dev, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_header_many<<<n, 64, 0, s>>>(blobs_dev, words_dev);
+  return hipGetLastError();
+}
 hipError_t launch_write_header(void* blob, const uint32_t* w, hipStream_t s) {
   k_header<<<1, 64, 0, s>>>(static_cast<uint32_t*>(blob), w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7],
                             w[8], w[9], w[10], w[11], w[12], w[13], w[14], w[15]);

@@ -93,8 +93,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
   f32x16 acc = {};
   // C (when accumulated, beta != 0) is read before the K loop
-  char* Cb = static_cast<char*>(g.C);
-  const int64_t cz = z * g.c_batch;
+  char* Cb = g.c_ptrs ? static_cast<char*>(g.c_ptrs[z]) : static_cast<char*>(g.C);
+  const int64_t cz = g.c_ptrs ? 0 : z * g.c_batch;
   auto kept = [&](int64_t m, int64_t n) {
     return m < g.M && n < g.N && (g.c_lower == 0 || (g.c_lower > 0 ? m >= n : m <= n));
   };
@@ -247,8 +247,8 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
     }
     return;
   }
-  char* Cb = static_cast<char*>(g.C);
-  const int64_t cz = z * g.c_batch;
+  char* Cb = g.c_ptrs ? static_cast<char*>(g.c_ptrs[z]) : static_cast<char*>(g.C);
+  const int64_t cz = g.c_ptrs ? 0 : z * g.c_batch;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t m = m0 + wm + (i >> 2) * 8 + half * 4 + (i & 3);
@@ -280,13 +280,14 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
     if (g.c_lower > 0 ? m < n : (g.c_lower < 0 && m > n)) continue;
     float v = g.alpha * acc;
     if (g.col_scale) v *= g.col_scale[z * g.col_scale_batch + n];
-    const int64_t off = z * g.c_batch + m * g.c_m + n * g.c_n;
+    void* Cz = g.c_ptrs ? g.c_ptrs[z] : g.C;
+    const int64_t off = (g.c_ptrs ? 0 : z * g.c_batch) + m * g.c_m + n * g.c_n;
     if (g.c_dtype == kF32) {
-      float* C = static_cast<float*>(g.C);
+      float* C = static_cast<float*>(Cz);
       if (g.beta != 0.f) v += g.beta * C[off];
       C[off] = v;
     } else {
-      static_cast<uint16_t*>(g.C)[off] = f32_to_bf16_rne(v);
+      static_cast<uint16_t*>(Cz)[off] = f32_to_bf16_rne(v);
     }
   }
 }
@@ -500,8 +501,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
         }
     return;
   }
-  char* Cb = static_cast<char*>(g.C);
-  const int64_t cz = z * g.c_batch;
+  char* Cb = g.c_ptrs ? static_cast<char*>(g.c_ptrs[z]) : static_cast<char*>(g.C);
+  const int64_t cz = g.c_ptrs ? 0 : z * g.c_batch;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -555,6 +556,18 @@ __global__ __launch_bounds__(256) void k_sketch(float* out, int64_t rows, int64_
 // fp32 [rows][ld_in] (first `cols` columns) -> bf16 [rows][cols], RNE.
 __global__ __launch_bounds__(256) void k_to_bf16(const float* in, int64_t ld_in, uint16_t* out,
                                                   int64_t rows, int64_t cols) {
+  const int64_t n = rows * cols;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += 256ll * gridDim.x) {
+    const int64_t r = i / cols, c = i % cols;
+    out[i] = f32_to_bf16_rne(in[r * ld_in + c]);
+  }
+}
+
+// out[z] = bf16(in[z]) for rows x cols of row stride ld_in, per-tensor pointers.
+__global__ __launch_bounds__(256) void k_to_bf16_many(const float* const* ins, int64_t ld_in, uint16_t* const* outs,
+                                                       int64_t rows, int64_t cols) {
+  const float* in = ins[blockIdx.y];
+  uint16_t* out = outs[blockIdx.y];
   const int64_t n = rows * cols;
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += 256ll * gridDim.x) {
     const int64_t r = i / cols, c = i % cols;
@@ -770,6 +783,13 @@ hipError_t launch_sketch(float* out, int64_t rows, int64_t cols, uint64_t seed, 
 hipError_t launch_to_bf16(const float* in, int64_t ld_in, uint16_t* out, int64_t rows, int64_t cols,
                           hipStream_t s) {
   k_to_bf16<<<grid1(rows * cols), 256, 0, s>>>(in, ld_in, out, rows, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_bf16_many(const float* const* ins_dev, int64_t ld_in, uint16_t* const* outs_dev, int64_t rows,
+                               int64_t cols, int n, hipStream_t s) {
+  if (n <= 0 || rows * cols <= 0) return hipSuccess;
+  k_to_bf16_many<<<dim3(grid1(rows * cols), n), 256, 0, s>>>(ins_dev, ld_in, outs_dev, rows, cols);
   return hipGetLastError();
 }
 

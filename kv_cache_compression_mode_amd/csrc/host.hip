@@ -898,6 +898,53 @@ jolt_status guard(F&& f) {
 }  // namespace
 
 // ================================================================== ABI
+// split-K of the encode's U~_T^T X product (K = T tokens)
+int encode_ksplit(int64_t T) { return static_cast<int>(std::min<int64_t>(16, std::max<int64_t>(1, T / 256))); }
+
+// ---- encode of many tensors of one shape: the per-tensor steps of jolt_encode,
+// batched over the tensors of each (r_T, r_D) and over all tensors for the
+// residual kernel and the headers (the same kernels and arithmetic).
+struct EncManyLayout {
+  std::vector<int> order;                  // Tucker tensors grouped by (r_T, r_D), input order kept
+  std::vector<std::pair<int, int>> groups; // [begin, end) into order
+  std::vector<size_t> w_off, p_off, part_off;   // per group, bytes into the workspace
+  size_t arr_off, total;
+  size_t n_ptrs;                           // pointer slots
+};
+EncManyLayout enc_many_layout(int n, const jolt_shape* shape, const jolt_choice* ch) {
+  EncManyLayout L;
+  const int64_t H = shape->H, T = shape->T, D = shape->D, HD = H * D;
+  std::vector<int> idx;
+  for (int i = 0; i < n; ++i)
+    if (ch[i].r_T > 0) idx.push_back(i);
+  std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) {
+    return ch[a].r_T != ch[b].r_T ? ch[a].r_T < ch[b].r_T : ch[a].r_D < ch[b].r_D;
+  });
+  L.order = idx;
+  size_t off = 0;
+  for (size_t b = 0; b < idx.size();) {
+    size_t e = b;
+    while (e < idx.size() && ch[idx[e]].r_T == ch[idx[b]].r_T && ch[idx[e]].r_D == ch[idx[b]].r_D) ++e;
+    const size_t m = e - b, rT = ch[idx[b]].r_T;
+    L.groups.emplace_back(static_cast<int>(b), static_cast<int>(e));
+    L.w_off.push_back(off);
+    off += a256(4ull * m * H * rT * D);
+    L.p_off.push_back(off);
+    off += a256(4ull * m * rT * HD);
+    L.part_off.push_back(off);
+    off += a256(4ull * m * rT * HD * encode_ksplit(T));
+    b = e;
+  }
+  // pointers: casts 4 per Tucker tensor, P 2 per, G2 3 and G3 2 per (tensor, head);
+  // blobs 1 per tensor
+  const size_t nt = idx.size();
+  L.n_ptrs = 4 * nt + 2 * nt + 5 * nt * H + static_cast<size_t>(n);
+  L.arr_off = off;
+  off += a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n) + a256(4ull * 16 * n);
+  L.total = off + 256;
+  return L;
+}
+
 extern "C" {
 
 size_t jolt_blob_bytes(const jolt_shape* shape, jolt_choice choice) {
@@ -915,7 +962,6 @@ int32_t jolt_spectrum_len(const jolt_alloc_req* req) {
   return cap_of(req);
 }
 
-int encode_ksplit(int64_t T) { return static_cast<int>(std::min<int64_t>(16, std::max<int64_t>(1, T / 256))); }
 
 size_t jolt_encode_workspace_bytes(const jolt_shape* shape, jolt_choice c) {
   if (!shape_ok(shape) || !choice_ok(shape, c)) return 0;
@@ -1111,6 +1157,174 @@ jolt_status jolt_encode(const jolt_shape* shape, const void* x_dev, jolt_choice 
                               static_cast<uint32_t>(c.bits), static_cast<uint32_t>(kGroup),
                               static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), 0, 0, 0, 0};
     ck(launch_write_header(blob, hdr, s));
+    return JOLT_OK;
+  });
+}
+
+size_t jolt_encode_many_workspace_bytes(int32_t n, const jolt_shape* shape, const jolt_choice* choices) {
+  if (n < 0 || !shape_ok(shape) || (n > 0 && !choices)) return 0;
+  for (int i = 0; i < n; ++i)
+    if (!choice_ok(shape, choices[i])) return 0;
+  return enc_many_layout(n, shape, choices).total;
+}
+
+jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choice* choices,
+                             const void* const* x_dev, const float* const* U_T_dev, const int32_t* ld_T,
+                             const float* const* U_D_dev, const int32_t* ld_D, const void* rot_dev, uint64_t seed,
+                             void* const* blob_dev, const size_t* blob_bytes, void* ws_dev, size_t ws_bytes,
+                             void* stream) {
+  if (n < 0 || !shape_ok(shape) || !rot_dev) return JOLT_EINVAL;
+  if (n == 0) return JOLT_OK;
+  if (!choices || !x_dev || !blob_dev || !blob_bytes) return JOLT_EINVAL;
+  for (int i = 0; i < n; ++i) {
+    const jolt_choice c = choices[i];
+    if (!choice_ok(shape, c) || !x_dev[i] || !blob_dev[i]) return JOLT_EINVAL;
+    if (c.r_T > 0 && (!U_T_dev || !U_D_dev || !ld_T || !ld_D || !U_T_dev[i] || !U_D_dev[i] || ld_T[i] < c.r_T ||
+                      ld_D[i] < c.r_D))
+      return JOLT_EINVAL;
+    if (blob_bytes[i] < blob_layout(shape->H, shape->T, shape->D, c).total) return JOLT_ENOSPACE;
+  }
+  const EncManyLayout L = enc_many_layout(n, shape, choices);
+  if (!ws_dev || ws_bytes < L.total) return JOLT_ENOSPACE;
+  return guard([&]() -> jolt_status {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t H = shape->H, T = shape->T, D = shape->D, HD = H * D;
+    const int xdt = shape->dtype == JOLT_BF16 ? kBF16 : kF32;
+    char* ws = static_cast<char*>(ws_dev);
+    const size_t nq = static_cast<size_t>(D) * D;
+    const float* Qt = reinterpret_cast<const float*>(static_cast<const char*>(rot_dev) + a256(4 * nq));
+    bool al16 = true;
+    for (int i = 0; i < n; ++i)
+      al16 = al16 && (reinterpret_cast<uintptr_t>(x_dev[i]) & 15) == 0 && (reinterpret_cast<uintptr_t>(blob_dev[i]) & 15) == 0;
+    auto blob = [&](int i) { return static_cast<char*>(blob_dev[i]); };
+    auto lay = [&](int i) { return blob_layout(H, T, D, choices[i]); };
+    // host images of the pointer arrays, the residual arguments and the header words
+    std::vector<const void*> ptr(L.n_ptrs, nullptr);
+    std::vector<EncodeArgs> args(n);
+    std::vector<uint32_t> words(static_cast<size_t>(16) * n);
+    void** dptr = reinterpret_cast<void**>(ws + L.arr_off);
+    EncodeArgs* dargs = reinterpret_cast<EncodeArgs*>(ws + L.arr_off + a256(8 * L.n_ptrs));
+    uint32_t* dwords = reinterpret_cast<uint32_t*>(ws + L.arr_off + a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n));
+    size_t np = 0;
+    auto slots = [&](size_t k) { const size_t o = np; np += k; return o; };
+    struct GroupPtrs { size_t ut_in, ut_out, ud_in, ud_out, pa, pb, g2a, g2b, g2c, g3a, g3b; };
+    std::vector<GroupPtrs> gp(L.groups.size());
+    std::vector<float*> Wslot(n, nullptr);
+    for (size_t g = 0; g < L.groups.size(); ++g) {
+      const int b0 = L.groups[g].first, e0 = L.groups[g].second, m = e0 - b0;
+      const jolt_choice c = choices[L.order[b0]];
+      const int64_t rT = c.r_T, rD = c.r_D;
+      GroupPtrs& q = gp[g];
+      q.ut_in = slots(m); q.ut_out = slots(m); q.ud_in = slots(m); q.ud_out = slots(m);
+      q.pa = slots(m); q.pb = slots(m);
+      q.g2a = slots(m * H); q.g2b = slots(m * H); q.g2c = slots(m * H);
+      q.g3a = slots(m * H); q.g3b = slots(m * H);
+      float* P = reinterpret_cast<float*>(ws + L.p_off[g]);
+      float* W = reinterpret_cast<float*>(ws + L.w_off[g]);
+      for (int j = 0; j < m; ++j) {
+        const int i = L.order[b0 + j];
+        const BlobLayout B = lay(i);
+        ptr[q.ut_in + j] = U_T_dev[i];
+        ptr[q.ut_out + j] = blob(i) + B.ut;
+        ptr[q.ud_in + j] = U_D_dev[i];
+        ptr[q.ud_out + j] = blob(i) + B.ud;
+        ptr[q.pa + j] = blob(i) + B.ut;
+        ptr[q.pb + j] = x_dev[i];
+        for (int64_t h = 0; h < H; ++h) {
+          const size_t k = static_cast<size_t>(j) * H + h;
+          ptr[q.g2a + k] = P + static_cast<size_t>(j) * rT * HD + h * D;
+          ptr[q.g2b + k] = blob(i) + B.ud;
+          ptr[q.g2c + k] = blob(i) + B.g + 2ull * h * rT * rD;
+          ptr[q.g3a + k] = blob(i) + B.g + 2ull * h * rT * rD;
+          ptr[q.g3b + k] = blob(i) + B.ud;
+        }
+        Wslot[i] = W + static_cast<size_t>(j) * H * rT * D;
+      }
+    }
+    const size_t blob_slot = slots(n);
+    for (int i = 0; i < n; ++i) {
+      const jolt_choice c = choices[i];
+      const BlobLayout B = lay(i);
+      ptr[blob_slot + i] = blob(i);
+      EncodeArgs& ea = args[i];
+      ea = EncodeArgs{};
+      ea.X = x_dev[i]; ea.x_dtype = xdt; ea.H = H; ea.T = T;
+      ea.Ut = c.r_T > 0 ? reinterpret_cast<const uint16_t*>(blob(i) + B.ut) : nullptr;
+      ea.W = Wslot[i]; ea.r_T = c.r_T;
+      ea.Qt = Qt; ea.bits = c.bits;
+      ea.scales = reinterpret_cast<uint16_t*>(blob(i) + B.sc);
+      ea.codes = reinterpret_cast<uint8_t*>(blob(i) + B.cd);
+      const uint32_t hdr[16] = {kMagic, kVersion, static_cast<uint32_t>(H), static_cast<uint32_t>(T),
+                                static_cast<uint32_t>(D), static_cast<uint32_t>(shape->dtype),
+                                static_cast<uint32_t>(c.r_T), static_cast<uint32_t>(c.r_D),
+                                static_cast<uint32_t>(c.bits), static_cast<uint32_t>(kGroup),
+                                static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), 0, 0, 0, 0};
+      std::memcpy(&words[static_cast<size_t>(16) * i], hdr, sizeof(hdr));
+    }
+    // one upload of the host images (pageable memory: the call copies before returning)
+    {
+      std::vector<char> img(a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n) + a256(4ull * 16 * n), 0);
+      std::memcpy(img.data(), ptr.data(), 8 * L.n_ptrs);
+      std::memcpy(img.data() + a256(8 * L.n_ptrs), args.data(), sizeof(EncodeArgs) * n);
+      std::memcpy(img.data() + a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n), words.data(), 4ull * 16 * n);
+      ck(hipMemcpyAsync(dptr, img.data(), img.size(), hipMemcpyHostToDevice, s));
+      ck(hipStreamSynchronize(s));
+    }
+    auto dp = [&](size_t slot) { return dptr + slot; };
+    for (size_t g = 0; g < L.groups.size(); ++g) {
+      const int b0 = L.groups[g].first, e0 = L.groups[g].second, m = e0 - b0;
+      const int i0 = L.order[b0];
+      const jolt_choice c = choices[i0];
+      const int64_t rT = c.r_T, rD = c.r_D;
+      const GroupPtrs& q = gp[g];
+      // one ld per group is required by the batched casts: tensors of a group share it or go one by one
+      bool same_ld = true;
+      for (int j = 0; j < m; ++j)
+        same_ld = same_ld && ld_T[L.order[b0 + j]] == ld_T[i0] && ld_D[L.order[b0 + j]] == ld_D[i0];
+      if (same_ld) {
+        ck(launch_to_bf16_many(reinterpret_cast<const float* const*>(dp(q.ut_in)), ld_T[i0],
+                               reinterpret_cast<uint16_t* const*>(dp(q.ut_out)), T, rT, m, s));
+        ck(launch_to_bf16_many(reinterpret_cast<const float* const*>(dp(q.ud_in)), ld_D[i0],
+                               reinterpret_cast<uint16_t* const*>(dp(q.ud_out)), D, rD, m, s));
+      } else {
+        for (int j = 0; j < m; ++j) {
+          const int i = L.order[b0 + j];
+          ck(launch_to_bf16(U_T_dev[i], ld_T[i], reinterpret_cast<uint16_t*>(blob(i) + lay(i).ut), T, rT, s));
+          ck(launch_to_bf16(U_D_dev[i], ld_D[i], reinterpret_cast<uint16_t*>(blob(i) + lay(i).ud), D, rD, s));
+        }
+      }
+      float* P = reinterpret_cast<float*>(ws + L.p_off[g]);
+      GemmArgs g1 = gemm0();                    // P = U~_T^T X_(T) per tensor (as in jolt_encode)
+      g1.M = rT; g1.N = HD; g1.K = T;
+      g1.a_ptrs = reinterpret_cast<const void* const*>(dp(q.pa)); g1.a_dtype = kBF16;
+      g1.am = plain(1); g1.ak = plain(rT);
+      g1.b_ptrs = reinterpret_cast<const void* const*>(dp(q.pb)); g1.b_dtype = xdt;
+      g1.bk = plain(D); g1.bn = segmented(D, T * D, 1);
+      g1.ptr_align16 = al16 ? 1 : 0;
+      g1.C = P; g1.c_m = HD; g1.c_n = 1; g1.c_batch = rT * HD;
+      g1.ksplit = encode_ksplit(T);
+      g1.partial = reinterpret_cast<float*>(ws + L.part_off[g]);
+      ck(launch_gemm(g1, m, s));
+      GemmArgs g2 = gemm0();                    // G~_h = bf16(P_h U~_D) per (tensor, head)
+      g2.M = rT; g2.N = rD; g2.K = D;
+      g2.a_ptrs = reinterpret_cast<const void* const*>(dp(q.g2a)); g2.am = plain(HD); g2.ak = plain(1);
+      g2.b_ptrs = reinterpret_cast<const void* const*>(dp(q.g2b)); g2.b_dtype = kBF16;
+      g2.bk = plain(rD); g2.bn = plain(1);
+      g2.c_ptrs = reinterpret_cast<void* const*>(dp(q.g2c)); g2.c_dtype = kBF16; g2.c_m = rD; g2.c_n = 1;
+      g2.ptr_align16 = al16 ? 1 : 0;
+      ck(launch_gemm(g2, static_cast<int>(m * H), s));
+      GemmArgs g3 = gemm0();                    // W_h = G~_h U~_D^T per (tensor, head)
+      g3.M = rT; g3.N = D; g3.K = rD;
+      g3.a_ptrs = reinterpret_cast<const void* const*>(dp(q.g3a)); g3.a_dtype = kBF16;
+      g3.am = plain(rD); g3.ak = plain(1);
+      g3.b_ptrs = reinterpret_cast<const void* const*>(dp(q.g3b)); g3.b_dtype = kBF16;
+      g3.bk = plain(1); g3.bn = plain(rD);
+      g3.C = ws + L.w_off[g]; g3.c_m = D; g3.c_n = 1; g3.c_batch = rT * D;
+      g3.ptr_align16 = al16 ? 1 : 0;
+      ck(launch_gemm(g3, static_cast<int>(m * H), s));
+    }
+    ck(launch_encode_residual_many(dargs, n, H, T, xdt, s));
+    ck(launch_write_headers(reinterpret_cast<uint32_t* const*>(dp(blob_slot)), dwords, n, s));
     return JOLT_OK;
   });
 }

@@ -38,6 +38,7 @@ struct GemmArgs {
   const void* const* a_ptrs;   // optional device array: operand base per batch entry
   const void* const* b_ptrs;
   void* C; int c_dtype; int64_t c_m, c_n, c_batch;
+  void* const* c_ptrs;         // optional device array: output base per batch entry
   float alpha, beta;
   const float* col_scale; int64_t col_scale_batch;
   // split-K: ksplit > 1 writes partial sums to `partial` ([batch][ksplit][M][N]
@@ -59,6 +60,8 @@ hipError_t launch_sketch(float* out, int64_t rows, int64_t cols, uint64_t seed, 
                          int ntensors, hipStream_t s);
 hipError_t launch_to_bf16(const float* in, int64_t ld_in, uint16_t* out, int64_t rows, int64_t cols,
                           hipStream_t s);
+hipError_t launch_to_bf16_many(const float* const* ins_dev, int64_t ld_in, uint16_t* const* outs_dev, int64_t rows,
+                               int64_t cols, int n, hipStream_t s);
 hipError_t launch_gather_cols(const float* in, int64_t ld_in, int64_t in_batch, const int* idx,
                               int64_t idx_batch, float* out, int64_t ld_out, int64_t out_batch,
                               int64_t rows, int64_t ncols, int batch, hipStream_t s);
@@ -145,6 +148,9 @@ struct EncodeArgs {
   uint8_t* codes;      // [H][T][4][4*bits]
 };
 hipError_t launch_encode_residual(const EncodeArgs& a, hipStream_t s);
+// n tensors of one shape (H, T), arguments in a device array
+hipError_t launch_encode_residual_many(const EncodeArgs* list_dev, int n, int64_t H, int64_t T, int x_dtype,
+                                       hipStream_t s);
 // Batched decode: up to kDecBatch records of one shape (H, T, D = 128).
 constexpr int kDecBatch = 32;
 struct DecRec {
@@ -166,5 +172,7 @@ struct DecBatch {
 };
 hipError_t launch_decode_batch(const DecBatch& b, hipStream_t s);
 hipError_t launch_write_header(void* blob, const uint32_t* words16, hipStream_t s);
+// 16 words words_dev[i * 16 ..] into the header of blobs_dev[i], i < n
+hipError_t launch_write_headers(uint32_t* const* blobs_dev, const uint32_t* words_dev, int n, hipStream_t s);
 
 }  // namespace jolt

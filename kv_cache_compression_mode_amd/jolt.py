@@ -208,6 +208,43 @@ def encode(x: torch.Tensor, choice, U_T: torch.Tensor | None, U_D: torch.Tensor 
     return blob
 
 
+def encode_many(xs, choices, factors, rot: torch.Tensor, seed: int = 0, outs=None):
+    """Compress several [H, T, 128] tensors of one shape and dtype into device
+    records (the same bytes as encode() per tensor, in batched launches).
+    factors[i] = (U_T, U_D) fp32 [rows, ld] with unit column stride (or
+    (None, None) for a choice with r_T == 0)."""
+    n = len(xs)
+    if n == 0:
+        return []
+    x0 = xs[0]
+    H, T, D = x0.shape
+    shape = make_shape(H, T, D, x0.dtype)
+    ch = (Choice * n)(*[Choice(*c) for c in choices])
+    for x in xs:
+        if x.shape != x0.shape or x.dtype != x0.dtype or not x.is_contiguous():
+            raise ValueError("all tensors must be contiguous with one shape and dtype")
+    blobs = outs if outs is not None else [
+        torch.empty(lib().jolt_blob_bytes(C.byref(shape), ch[i]), dtype=torch.uint8, device=x0.device)
+        for i in range(n)]
+    for f in (f for pair in factors for f in pair):
+        if f is not None and (f.dtype != torch.float32 or f.dim() != 2 or f.stride(1) != 1):
+            raise ValueError("factors must be fp32 [rows, ld] with unit column stride")
+    xp = (C.c_void_p * n)(*[x.data_ptr() for x in xs])
+    utp = (C.c_void_p * n)(*[f[0].data_ptr() if f[0] is not None else None for f in factors])
+    udp = (C.c_void_p * n)(*[f[1].data_ptr() if f[1] is not None else None for f in factors])
+    ldt = (C.c_int32 * n)(*[f[0].stride(0) if f[0] is not None else 0 for f in factors])
+    ldd = (C.c_int32 * n)(*[f[1].stride(0) if f[1] is not None else 0 for f in factors])
+    bp = (C.c_void_p * n)(*[b.data_ptr() for b in blobs])
+    bb = (C.c_size_t * n)(*[b.numel() for b in blobs])
+    nws = lib().jolt_encode_many_workspace_bytes(n, C.byref(shape), ch)
+    if nws == 0:
+        check(_lib.JOLT_EINVAL, "jolt_encode_many_workspace_bytes")
+    ws = torch.empty(nws, dtype=torch.uint8, device=x0.device)
+    check(lib().jolt_encode_many(n, C.byref(shape), ch, xp, utp, ldt, udp, ldd, rot.data_ptr(), seed, bp, bb,
+                                 ws.data_ptr(), ws.numel(), _stream(x0.device)), "jolt_encode_many")
+    return blobs
+
+
 def decode_workspace_bytes(H: int, T: int, choice, dtype=torch.bfloat16) -> int:
     return lib().jolt_decode_workspace_bytes(C.byref(make_shape(H, T, D_FEATURES, dtype)), Choice(*choice))
 
