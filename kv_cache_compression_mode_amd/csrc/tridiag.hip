@@ -675,6 +675,110 @@ __global__ __launch_bounds__(256) void k_cb_apply(int t, int glo, int nchunk, fl
   }
 }
 
+// Panel back-transformation, one launch per panel: Z_r <- (I - V T V^T) Z_r
+// for rows r .. n-1 of the eigenvector block, one workgroup per 64 columns of
+// Z and matrix.  Pass 1 accumulates W = V^T Z_r (32 x 64) over 64-row chunks,
+// W2 = T W, pass 2 streams the chunks again and subtracts V W2; both on fp32
+// matrix cores, the next chunk loaded into registers during the current one.
+__global__ __launch_bounds__(256) void k_apply_wy(float* Z, int64_t n, int64_t z_batch, int64_t r0, int64_t mp,
+                                                  int R, const float* V_g, int64_t v_batch, const float* T_g,
+                                                  int64_t t_batch) {
+  __shared__ float Vs[64][SBW + 1];      // V rows of a chunk
+  __shared__ float Zs[64][65];           // Z rows of a chunk x 64 columns
+  __shared__ float Wp[2][SBW][65];       // W partial sums (two row halves), then W2
+  __shared__ float Ts[SBW][SBW + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
+  const int64_t z = blockIdx.y;
+  const int c0 = blockIdx.x * 64, nc = min(64, R - c0);
+  float* Zr = Z + z * z_batch + r0;
+  const float* V = V_g + z * v_batch;
+  for (int idx = tid; idx < SBW * SBW; idx += 256) Ts[idx / SBW][idx % SBW] = T_g[z * t_batch + idx];
+  // chunk loader: Z 64 rows x 64 columns (16 per thread), V 64 rows x 32 (8 per thread)
+  float rz[16], rv[8];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = tid + 256 * q, c = idx >> 6, rr = idx & 63;
+      rz[q] = (k0 + rr < mp && c < nc) ? Zr[static_cast<int64_t>(c0 + c) * n + k0 + rr] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int idx = tid + 256 * q, c = idx >> 6, rr = idx & 63;
+      rv[q] = k0 + rr < mp ? V[static_cast<int64_t>(c) * mp + k0 + rr] : 0.f;
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = tid + 256 * q;
+      Zs[idx & 63][idx >> 6] = rz[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int idx = tid + 256 * q;
+      Vs[idx & 63][idx >> 6] = rv[q];
+    }
+  };
+  // pass 1: W = V^T Z_r; wave w: columns 32 (w & 1) .., chunk rows 32 (w >> 1) ..
+  const int cb = 32 * (wave & 1), kb = 32 * (wave >> 1);
+  f32x16 acc = {};
+  load(0);
+  for (int64_t k0 = 0; k0 < mp; k0 += 64) {
+    store();
+    __syncthreads();
+    if (k0 + 64 < mp) load(k0 + 64);
+#pragma unroll
+    for (int kk = 0; kk < SBW; kk += 2) {
+      const int k = kb + kk + hf;
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[k][rl], Zs[k][cb + rl], acc, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) Wp[wave >> 1][(e >> 2) * 8 + hf * 4 + (e & 3)][cb + rl] = acc[e];
+  __syncthreads();
+  // W2 = T W (waves 0, 1), into Wp[0] after the barrier
+  f32x16 w2 = {};
+  if (wave < 2) {
+#pragma unroll
+    for (int kk = 0; kk < SBW; kk += 2) {
+      const int k = kk + hf;
+      w2 = __builtin_amdgcn_mfma_f32_32x32x2f32(Ts[rl][k], Wp[0][k][32 * wave + rl] + Wp[1][k][32 * wave + rl], w2,
+                                                 0, 0, 0);
+    }
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Wp[0][(e >> 2) * 8 + hf * 4 + (e & 3)][32 * wave + rl] = w2[e];
+  }
+  // pass 2: Z_r -= V W2; wave w: chunk rows 32 (w >> 1) .., columns 32 (w & 1) ..
+  load(0);
+  for (int64_t k0 = 0; k0 < mp; k0 += 64) {
+    __syncthreads();                      // W2 visible; previous chunk's Zs / Vs reads done
+    store();
+    __syncthreads();
+    if (k0 + 64 < mp) load(k0 + 64);
+    f32x16 d = {};
+#pragma unroll
+    for (int kk = 0; kk < SBW; kk += 2) {
+      const int k = kk + hf;
+      d = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[kb + rl][k], Wp[0][k][cb + rl], d, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rr = kb + (e >> 2) * 8 + hf * 4 + (e & 3);
+      Zs[rr][cb + rl] -= d[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = tid + 256 * q, c = idx >> 6, rr = idx & 63;
+      if (k0 + rr < mp && c < nc) Zr[static_cast<int64_t>(c0 + c) * n + k0 + rr] = Zs[rr][c];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_copy_cols(const float* in, int64_t ld_in, int64_t in_batch, float* out,
                                                   int64_t ld_out, int64_t out_batch, int64_t rows, int64_t cols) {
   const int64_t z = blockIdx.y;
@@ -916,17 +1020,10 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     ProfScope ps_bb("band_back", s);
     for (int64_t p = Lw.P - 1; p >= 0; --p) {
       const int64_t r = (p + 1) * SBW, mp = n - r;
-      const float* V = Vst + voff[p];
-      const float* T = Tst + p * 1024;
-      const int64_t vs = Lw.vtot, ts = Lw.P * 1024;
-      float* Zr = Z + r;
-      // Zr -= V (T (V^T Zr))
-      if ((e = gemm(SBW, R, mp, V, plain(mp), plain(1), vs, Zr, plain(1), plain(n), nn, Wb, R, 1, SBW * R, 1.f,
-                    0.f, ksplit_for(mp))) != hipSuccess) return e;
-      if ((e = gemm(SBW, R, SBW, T, plain(SBW), plain(1), ts, Wb, plain(R), plain(1), SBW * R, Wb2, R, 1,
-                    SBW * R, 1.f, 0.f)) != hipSuccess) return e;
-      if ((e = gemm(mp, R, SBW, V, plain(1), plain(mp), vs, Wb2, plain(R), plain(1), SBW * R, Zr, 1, n, nn, -1.f,
-                    1.f)) != hipSuccess) return e;
+      // Z rows r.. <- (I - V T V^T) Z rows r..
+      k_apply_wy<<<dim3(static_cast<unsigned>((R + 63) / 64), batch), 256, 0, s>>>(
+          Z, n, nn, r, mp, R, Vst + voff[p], Lw.vtot, Tst + p * 1024, Lw.P * 1024);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
   return hipSuccess;
