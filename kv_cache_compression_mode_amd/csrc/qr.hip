@@ -377,66 +377,120 @@ __global__ __launch_bounds__(LT) void k_qr_block(const float* A, int64_t m, int6
   }
 }
 
-// Householder QR of one panel (mp = m - c0 <= kLeaf rows, nb <= 32 columns),
-// the panel's rows in registers (thread t holds rows 2t and 2t + 1).  Column
-// j: the thread holding row j publishes it, one fused 32-slot reduction gives
-// sigma (slot j) and the raw dots sum_{i > j} P[c][i] x_i of every other
-// column, and every thread then forms tau, beta and d_c = P[c][j] + scale *
-// raw_c itself, updating the later columns; d_c for c < j is v_c^T v_j,
-// kept for T.  Two barriers per column; waves whose rows all lie past the
-// panel skip the arithmetic.  T follows the factorization: row t of T by
-// thread t, T[t][j] = -tau_j sum_{t <= l < j} T[t][l] (v_l^T v_j), T[j][j] =
-// tau_j.  Outputs are those of k_qr_block mode 0, plus (write_r) R in the
+// Householder QR of one panel (mp = m - c0 <= kLeaf rows, nb <= 32 columns)
+// in registers: thread t holds column c = t & 31, rows 64 g .. 64 g + 63 with
+// g = t >> 5, so a wave holds 128 rows of all 32 columns.  Column j: the
+// threads of column j publish it below the diagonal (x) and the threads of
+// row block 0 publish row j; every thread forms its column's dot x^T P[:, c]
+// over its 64 rows, the two row blocks of a wave are added by one lane swap
+// and the eight waves through LDS, and every thread then has sigma = x^T x,
+// alpha = P[j][j], tau, beta and d_c = v^T P[:, c] = P[j][c] + scale x^T
+// P[:, c] for its own column.  Columns right of j take P -= tau v d^T; column
+// j keeps x below the diagonal (v = scale_j x, scaled when V is written) and
+// beta on it, so for c < j, v_c^T v_j = scale_c d_c is kept for T.  Two barriers per column; waves whose rows all lie past the panel
+// skip the arithmetic.  T follows the factorization by the forward
+// recurrence, T[t][j] = -tau_j sum_{t <= l < j} T[t][l] (v_l^T v_j), T[j][j]
+// = tau_j.  Outputs are those of k_qr_block mode 0, plus (write_r) R in the
 // panel's top rows.
 constexpr int RT = kLeaf / 2, RW = RT / 64;
 __global__ __launch_bounds__(RT) void k_qr_reg(float* A, int64_t m, int64_t ld, int64_t bstride, int64_t c0,
                                                int nb, float* Vp, int64_t vstride, float* Tp, int64_t tstride,
                                                float* taus_g, int64_t k, int write_r) {
+  __shared__ __attribute__((aligned(16))) float xs[kLeaf];     // column j, rows > j
+  __shared__ float rowj[2][32];                                // row j, by the parity of j
   __shared__ float red[RW][32];
-  __shared__ __attribute__((aligned(16))) float raw[32];
-  __shared__ __attribute__((aligned(16))) float rowj[2][32];
-  __shared__ __attribute__((aligned(16))) float St[32][36];   // St[j][l] = v_l^T v_j (l < j)
+  __shared__ float St[32][33];                                 // St[j][l] = v_l^T v_j (l < j)
+  __shared__ float Tl[32][33];
+  __shared__ float Rl[32][33];                                 // rows of R
   __shared__ float tau_s[32], sgn[32];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int i0 = 2 * t, i1 = 2 * t + 1;
+  const int c = t & 31, g = t >> 5, rb = 64 * g;               // column, first row
   const int64_t z = blockIdx.y;
   const int mr = static_cast<int>(m - c0);
-  const bool live = 128 * wave < mr;                 // this wave holds rows of the panel
+  const bool live = 128 * wave < mr;                           // this wave holds rows of the panel
   float* Az = A + z * bstride;
-  float p0[32], p1[32];
+  // The panel (columns c0.., rows c0.., column stride ld) through a buffer
+  // resource; offsets of rows past the panel or columns past nb start at 2^31
+  // (past any panel: ld <= 32768), which reads 0 and drops stores.
+  constexpr uint32_t kOff = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t pr =
+      __builtin_amdgcn_make_buffer_rsrc(Az + c0 * ld + c0, 0, static_cast<int>(((nb - 1) * ld + mr) * 4), 0x00020000);
+  const uint32_t cb = static_cast<uint32_t>(c) * static_cast<uint32_t>(ld) * 4u + 4u * rb;
+  auto off = [&](int r) -> int {
+    return static_cast<int>(c < nb && rb + r < mr ? cb + 4u * r : kOff);
+  };
+  // 16-byte loads where the thread's 64 rows all lie in the panel, single
+  // words in the block that straddles its end
+  float p[64];
+  const bool full = rb + 64 <= mr;
+  if (full) {
 #pragma unroll
-  for (int c = 0; c < 32; ++c) {
-    p0[c] = (c < nb && i0 < mr) ? Az[(c0 + c) * ld + c0 + i0] : 0.f;
-    p1[c] = (c < nb && i1 < mr) ? Az[(c0 + c) * ld + c0 + i1] : 0.f;
+    for (int q = 0; q < 16; ++q) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(pr, off(4 * q), 0, 0);
+      p[4 * q] = __uint_as_float(v[0]);
+      p[4 * q + 1] = __uint_as_float(v[1]);
+      p[4 * q + 2] = __uint_as_float(v[2]);
+      p[4 * q + 3] = __uint_as_float(v[3]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 64; ++r) p[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pr, off(r), 0, 0));
   }
-  // fully unrolled (register indices must be compile-time); columns past nb skipped
-#pragma clang loop unroll(full)
-  for (int j = 0; j < 32; ++j) {
-    if (j >= nb) continue;
-    float* rj = rowj[j & 1];
-    if (t == (j >> 1)) {
+  if (!live && lane < 32) red[wave][c] = 0.f;                  // waves past the panel add nothing
+  float vscale = 0.f;                                          // scale of this column's reflector
+#pragma clang loop unroll(disable)
+  for (int j = 0; j < nb; ++j) {
+    const int par = j & 1;
+    if (c == j) {                                              // publish column j
 #pragma unroll
-      for (int c = 0; c < 32; ++c) rj[c] = (j & 1) ? p1[c] : p0[c];
+      for (int r = 0; r < 64; r += 4)
+        *reinterpret_cast<float4*>(&xs[rb + r]) = make_float4(p[r], p[r + 1], p[r + 2], p[r + 3]);
     }
-    const bool b0 = i0 > j && i0 < mr, b1 = i1 > j && i1 < mr;
-    const float x0 = b0 ? p0[j] : 0.f, x1 = b1 ? p1[j] : 0.f;
+    // rows <= j of x are zero: written by lanes 0 .. j of wave 0 after the
+    // publishing lane j of the same wave (one wave's LDS writes land in order)
+    if (t <= j) xs[t] = 0.f;
+    if (g == 0) {                                              // publish row j (row block 0)
+      float a[16];                                             // p[j] by the bits of j (j < 32)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {               // values first: a select of two loads keeps p in registers
+        const float lo = p[2 * q], hi = p[2 * q + 1];
+        a[q] = (j & 1) ? hi : lo;
+      }
+#pragma unroll
+      for (int w = 2, n2 = 8; n2 >= 1; w <<= 1, n2 >>= 1) {
+#pragma unroll
+        for (int q = 0; q < n2; ++q) {
+          const float lo = a[2 * q], hi = a[2 * q + 1];
+          a[q] = (j & w) ? hi : lo;
+        }
+      }
+      rowj[par][c] = a[0];
+    }
+    __syncthreads();
+    float x[64];
     if (live) {
-      f32x32 part;
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-      for (int c = 0; c < 32; ++c)
-        part[c] = c < nb ? (c == j ? x0 : p0[c]) * x0 + (c == j ? x1 : p1[c]) * x1 : 0.f;
-      const float tot = reduce32(part, lane);
-      if ((lane & 1) == 0) red[wave][lane >> 1] = tot;
+      for (int r = 0; r < 64; r += 4) {
+        const float4 q = *reinterpret_cast<const float4*>(&xs[rb + r]);
+        x[r] = q.x; x[r + 1] = q.y; x[r + 2] = q.z; x[r + 3] = q.w;
+        s0 += q.x * p[r];
+        s1 += q.y * p[r + 1];
+        s2 += q.z * p[r + 2];
+        s3 += q.w * p[r + 3];
+      }
+      float part = (s0 + s1) + (s2 + s3);
+      part += __shfl_xor(part, 32);
+      if (lane < 32) red[wave][c] = part;
     }
     __syncthreads();
-    if (t < 32) {
-      float u = 0.f;
-      for (int w = 0; w < RW; ++w)
-        if (128 * w < mr) u += red[w][t];
-      raw[t] = u;
+    float raw = 0.f, sigma = 0.f;
+#pragma unroll
+    for (int w = 0; w < RW; ++w) {
+      raw += red[w][c];
+      sigma += red[w][j];
     }
-    __syncthreads();
-    const float sigma = raw[j], alpha = rj[j];
+    const float alpha = rowj[par][j];
     float tau = 0.f, beta = alpha, scale = 0.f;
     if (sigma > 0.f) {
       const float nrm = sqrtf(alpha * alpha + sigma);
@@ -444,62 +498,80 @@ __global__ __launch_bounds__(RT) void k_qr_reg(float* A, int64_t m, int64_t ld, 
       tau = (beta - alpha) / beta;
       scale = 1.f / (alpha - beta);
     }
-    const bool d0 = i0 == j, d1 = i1 == j;           // the diagonal row
-    const float v0 = d0 ? 1.f : (b0 ? x0 * scale : 0.f), v1 = d1 ? 1.f : (b1 ? x1 * scale : 0.f);
-    if (tau != 0.f && live) {
+    const float d = rowj[par][c] + scale * raw;                // v^T P[:, c]
+    if (c == j) vscale = scale;
+    // rows > j right of j: P -= x (scale tau d)
+    const float e = c > j ? scale * tau * d : 0.f;
+    if (live) {
 #pragma unroll
-      for (int c = j + 1; c < 32; ++c) {
-        if (c < nb) {
-          const float d = tau * (rj[c] + scale * raw[c]);
-          p0[c] -= v0 * d;
-          p1[c] -= v1 * d;
-        }
-      }
+      for (int r = 0; r < 64; ++r) p[r] -= x[r] * e;
     }
-    if (b0) p0[j] = v0;
-    if (b1) p1[j] = v1;
-    if (d0) p0[j] = beta;
-    if (d1) p1[j] = beta;
-    if (t < j) St[j][t] = rj[t] + scale * raw[t];
-    if (t == j) {
-      tau_s[j] = tau;
-      sgn[j] = beta < 0.f ? -1.f : 1.f;
+    // Row j is final after this step and only R reads it: it goes to LDS,
+    // its registers keep a stale value that later steps multiply by x = 0.
+    if (g == 0) {
+      Rl[j][c] = c == j ? beta : (c > j ? rowj[par][c] - tau * d : 0.f);
+      if (c < j) St[j][c] = vscale * d;
+      if (c == j) {
+        tau_s[j] = tau;
+        sgn[j] = beta < 0.f ? -1.f : 1.f;
+      }
     }
   }
   __syncthreads();
-  if (t < 32) {                                      // row t of T
-    float tr[32];
+  if (t < 32) {                                                // row t of T, in registers
+    float tr[32];                                              // tr[l] = 0 for l < t
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      float u = 0.f;
+      float u0 = 0.f, u1 = 0.f;
 #pragma unroll
-      for (int l = 0; l < j; ++l)
-        if (l >= t) u += tr[l] * St[j][l];
-      tr[j] = (j >= nb || j < t) ? 0.f : (j == t ? tau_s[j] : -tau_s[j] * u);
+      for (int l = 0; l + 1 < j; l += 2) {
+        u0 += tr[l] * St[j][l];
+        u1 += tr[l + 1] * St[j][l + 1];
+      }
+      if (j & 1) u0 += tr[j - 1] * St[j][j - 1];
+      const float tj = tau_s[j];
+      tr[j] = (j >= nb || j < t) ? 0.f : (j == t ? tj : -tj * (u0 + u1));
+      Tl[t][j] = tr[j];
     }
-#pragma unroll
-    for (int j = 0; j < 32; ++j) Tp[z * tstride + t * 32 + j] = tr[j];
   }
   // V (explicit, zero above row c0, unit diagonal), tau / sign(beta)
   float* V = Vp + z * vstride;
   for (int64_t r = t; r < c0; r += RT)
-    for (int c = 0; c < 32; ++c) V[c * m + r] = 0.f;
 #pragma unroll
-  for (int c = 0; c < 32; ++c) {
-    if (i0 < mr) V[c * m + c0 + i0] = (c >= nb || i0 < c) ? 0.f : (i0 == c ? 1.f : p0[c]);
-    if (i1 < mr) V[c * m + c0 + i1] = (c >= nb || i1 < c) ? 0.f : (i1 == c ? 1.f : p1[c]);
+    for (int q = 0; q < 32; ++q) V[q * m + r] = 0.f;
+  const __amdgpu_buffer_rsrc_t vr =
+      __builtin_amdgcn_make_buffer_rsrc(V + c0, 0, static_cast<int>((31 * m + mr) * 4), 0x00020000);
+  const uint32_t vb = static_cast<uint32_t>(c) * static_cast<uint32_t>(m) * 4u + 4u * rb;
+  auto vval = [&](int r) -> float {
+    const int i = rb + r;
+    return (c >= nb || i < c) ? 0.f : (i == c ? 1.f : vscale * p[r]);
+  };
+  if (full) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const float w0 = vval(4 * q), w1 = vval(4 * q + 1), w2 = vval(4 * q + 2), w3 = vval(4 * q + 3);
+      const __attribute__((ext_vector_type(4))) uint32_t w = {__float_as_uint(w0), __float_as_uint(w1),
+                                                               __float_as_uint(w2), __float_as_uint(w3)};
+      __builtin_amdgcn_raw_buffer_store_b128(w, vr, static_cast<int>(vb + 16u * q), 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 64; ++r)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vval(r)), vr,
+                                            static_cast<int>(rb + r < mr ? vb + 4u * r : kOff), 0, 0);
   }
   if (t < nb) {
     taus_g[z * 2 * k + c0 + t] = tau_s[t];
     taus_g[z * 2 * k + k + c0 + t] = sgn[t];
   }
-  if (write_r) {                                     // R: rows 2t, 2t + 1 < nb, upper triangle
+  if (write_r && g == 0) {                                     // R: rows <= c of row block 0
 #pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      if (c < nb && i0 < mr && i0 <= c) Az[(c0 + c) * ld + c0 + i0] = p0[c];
-      if (c < nb && i1 < mr && i1 <= c) Az[(c0 + c) * ld + c0 + i1] = p1[c];
-    }
+    for (int r = 0; r < 32; ++r)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Rl[r][c]), pr, r <= c && r < nb ? off(r) : static_cast<int>(kOff),
+                                            0, 0);
   }
+  __syncthreads();
+  for (int idx = t; idx < 1024; idx += RT) Tp[z * tstride + idx] = Tl[idx >> 5][idx & 31];
 }
 
 // Top block of the panel's Q (leaf 0's first nb rows times Q_top's first
