@@ -779,6 +779,271 @@ __global__ __launch_bounds__(256) void k_apply_wy(float* Z, int64_t n, int64_t z
   }
 }
 
+// ---- stage 1 of the band reduction: one panel's two-sided update
+//
+// With the panel's reflectors I - V T V^T (V: mp x 32, column-major, leading
+// dimension mp) and the trailing block A22 (mp x mp, the lower triangle is
+// stored, column-major with leading dimension n):
+//   Y = A22 V, X = Y T, S = V^T X, W = X - V (T^T S) / 2,
+//   A22 <- A22 - V W^T - W V^T (lower triangle).
+// k_symm_v forms Y for 64 rows of A22 per workgroup, streaming A22 in 64 x
+// 64 chunks read from the stored triangle (mirrored right of the diagonal),
+// then X = Y T for its rows and its rows' share of S; k_w_form sums the
+// shares and writes [V W]; k_syr2k updates one 64 x 64 tile of the lower
+// triangle from [V W] [W V]^T.  Rows and columns are multiples of 4, so
+// 16-byte accesses never straddle the end of a column.
+constexpr int SY = 64;    // rows of a stage-1 block
+
+__global__ __launch_bounds__(256) void k_symm_v(const float* A, int64_t n, int64_t a_batch, int mp,
+                                                const float* V_g, int64_t v_batch, const float* T_g,
+                                                int64_t t_batch, float* VW_g, int64_t vw_batch, float* SP) {
+  __shared__ float Ls[SY][SY + 1];       // chunk of A22 as stored: Ls[c][r] = column c, row r
+  __shared__ float Vs[SBW][SY + 1];      // rows of V: Vs[col][row]
+  __shared__ float Ys[SY][SBW + 1];      // Y, then X (row-major)
+  __shared__ float Ts[SBW][SBW + 1];
+  __shared__ float Vb[SBW][SY + 1];      // V rows of this block
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
+  const int64_t z = blockIdx.y;
+  const int ib = blockIdx.x, i0 = SY * ib, nb = (mp + SY - 1) / SY;
+  const float* a = A + z * a_batch;
+  const float* V = V_g + z * v_batch;
+  for (int idx = tid; idx < SBW * SBW; idx += 256) Ts[idx >> 5][idx & 31] = T_g[z * t_batch + idx];
+  float4 ra[4], rv[2];
+  auto load = [&](int jc) {
+    const int j0 = SY * jc;
+    const int rs = jc > ib ? j0 : i0, cs = jc > ib ? i0 : j0;   // stored block: rows rs.., columns cs..
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q, c = idx >> 4, r4 = (idx & 15) * 4;
+      ra[q] = (rs + r4 < mp && cs + c < mp)
+                  ? *reinterpret_cast<const float4*>(a + static_cast<int64_t>(cs + c) * n + rs + r4)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 256 * q, c = idx >> 4, r4 = (idx & 15) * 4;
+      rv[q] = j0 + r4 < mp ? *reinterpret_cast<const float4*>(V + static_cast<int64_t>(c) * mp + j0 + r4)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  const int wi = wave & 1, kh = wave >> 1;
+  f32x16 acc = {};
+  load(0);
+  for (int jc = 0; jc < nb; ++jc) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q, c = idx >> 4, r4 = (idx & 15) * 4;
+      Ls[c][r4] = ra[q].x; Ls[c][r4 + 1] = ra[q].y; Ls[c][r4 + 2] = ra[q].z; Ls[c][r4 + 3] = ra[q].w;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int idx = tid + 256 * q, c = idx >> 4, r4 = (idx & 15) * 4;
+      Vs[c][r4] = rv[q].x; Vs[c][r4 + 1] = rv[q].y; Vs[c][r4 + 2] = rv[q].z; Vs[c][r4 + 3] = rv[q].w;
+      if (jc == ib) { Vb[c][r4] = rv[q].x; Vb[c][r4 + 1] = rv[q].y; Vb[c][r4 + 2] = rv[q].z; Vb[c][r4 + 3] = rv[q].w; }
+    }
+    __syncthreads();
+    if (jc + 1 < nb) load(jc + 1);
+    const int i = SY / 2 * wi + rl;
+    if (jc < ib) {                       // A(i, k) = Ls[k][i]
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int k = 32 * kh + 2 * s + hf;
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Ls[k][i], Vs[rl][k], acc, 0, 0, 0);
+      }
+    } else if (jc > ib) {                // A(i, k) = Ls[i][k]
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int k = 32 * kh + 2 * s + hf;
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Ls[i][k], Vs[rl][k], acc, 0, 0, 0);
+      }
+    } else {                             // diagonal chunk: the lower triangle, mirrored
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int k = 32 * kh + 2 * s + hf;
+        const float lo = Ls[k][i], up = Ls[i][k];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(i >= k ? lo : up, Vs[rl][k], acc, 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  // Y = the two k halves
+  if (kh == 1) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Ys[SY / 2 * wi + (e >> 2) * 8 + hf * 4 + (e & 3)][rl] = acc[e];
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Ys[SY / 2 * wi + (e >> 2) * 8 + hf * 4 + (e & 3)][rl] += acc[e];
+  }
+  __syncthreads();
+  // X = Y T (waves 0, 1: 32 rows each)
+  f32x16 xa = {};
+  if (wave < 2) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int k = 2 * s + hf;
+      xa = __builtin_amdgcn_mfma_f32_32x32x2f32(Ys[32 * wave + rl][k], Ts[k][rl], xa, 0, 0, 0);
+    }
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Ys[32 * wave + (e >> 2) * 8 + hf * 4 + (e & 3)][rl] = xa[e];
+  }
+  __syncthreads();
+  // X -> the W half of [V W] (column-major, leading dimension mp)
+  float* Wd = VW_g + z * vw_batch + static_cast<int64_t>(SBW) * mp;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int idx = tid + 256 * q, c = idx >> 4, r4 = (idx & 15) * 4;
+    if (i0 + r4 < mp)
+      *reinterpret_cast<float4*>(Wd + static_cast<int64_t>(c) * mp + i0 + r4) =
+          make_float4(Ys[r4][c], Ys[r4 + 1][c], Ys[r4 + 2][c], Ys[r4 + 3][c]);
+  }
+  // this block's share of S = V^T X (wave 0, K = 64 rows)
+  if (wave == 0) {
+    f32x16 sa = {};
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      const int k = 2 * s + hf;
+      sa = __builtin_amdgcn_mfma_f32_32x32x2f32(Vb[rl][k], Ys[k][rl], sa, 0, 0, 0);
+    }
+    float* sp = SP + (z * nb + ib) * 1024;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sp[((e >> 2) * 8 + hf * 4 + (e & 3)) * 32 + rl] = sa[e];
+  }
+}
+
+// [V W] for 64 rows: S = sum of the blocks' shares, S2 = T^T S, W = X - V S2 / 2
+__global__ __launch_bounds__(256) void k_w_form(int mp, const float* V_g, int64_t v_batch, const float* T_g,
+                                                int64_t t_batch, float* VW_g, int64_t vw_batch, const float* SP) {
+  __shared__ float Ss[SBW][SBW + 1], Ts[SBW][SBW + 1], S2[SBW][SBW + 1];
+  __shared__ float Vr[SY][SBW + 1];
+  const int tid = threadIdx.x;
+  const int64_t z = blockIdx.y;
+  const int ib = blockIdx.x, i0 = SY * ib, nb = (mp + SY - 1) / SY;
+  const float* V = V_g + z * v_batch;
+  float* VW = VW_g + z * vw_batch;
+  const float* sp = SP + z * nb * 1024;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid + 256 * q;
+    float u = 0.f;
+    for (int b = 0; b < nb; ++b) u += sp[b * 1024 + e];
+    Ss[e >> 5][e & 31] = u;
+    Ts[e >> 5][e & 31] = T_g[z * t_batch + e];
+  }
+  // V rows of this block: to LDS and to the V half of [V W]
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int idx = tid + 256 * q, c = idx >> 4, r4 = (idx & 15) * 4;
+    if (i0 + r4 < mp) {
+      const float4 v = *reinterpret_cast<const float4*>(V + static_cast<int64_t>(c) * mp + i0 + r4);
+      *reinterpret_cast<float4*>(VW + static_cast<int64_t>(c) * mp + i0 + r4) = v;
+      Vr[r4][c] = v.x; Vr[r4 + 1][c] = v.y; Vr[r4 + 2][c] = v.z; Vr[r4 + 3][c] = v.w;
+    } else {
+      Vr[r4][c] = 0.f; Vr[r4 + 1][c] = 0.f; Vr[r4 + 2][c] = 0.f; Vr[r4 + 3][c] = 0.f;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {                  // S2 = T^T S
+    const int e = tid + 256 * q, a = e >> 5, b = e & 31;
+    float u = 0.f;
+#pragma unroll
+    for (int m = 0; m < SBW; ++m) u += Ts[m][a] * Ss[m][b];
+    S2[a][b] = 0.5f * u;
+  }
+  __syncthreads();
+  float* Wd = VW + static_cast<int64_t>(SBW) * mp;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int idx = tid + 256 * q, c = idx >> 4, r4 = (idx & 15) * 4;
+    if (i0 + r4 < mp) {
+      float* w = Wd + static_cast<int64_t>(c) * mp + i0 + r4;
+      float4 x = *reinterpret_cast<const float4*>(w);
+      float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+#pragma unroll
+      for (int a2 = 0; a2 < SBW; ++a2) {
+        const float s2 = S2[a2][c];
+        d0 += Vr[r4][a2] * s2;
+        d1 += Vr[r4 + 1][a2] * s2;
+        d2 += Vr[r4 + 2][a2] * s2;
+        d3 += Vr[r4 + 3][a2] * s2;
+      }
+      x.x -= d0; x.y -= d1; x.z -= d2; x.w -= d3;
+      *reinterpret_cast<float4*>(w) = x;
+    }
+  }
+}
+
+// A22 -= [V W] [W V]^T on the 64 x 64 tile (bi, bj), bi >= bj, of the lower
+// triangle; the diagonal tiles keep their upper part.
+__global__ __launch_bounds__(256) void k_syr2k(float* A, int64_t n, int64_t a_batch, int mp, const float* VW_g,
+                                               int64_t vw_batch) {
+  __shared__ float As[2 * SBW][SY + 1];  // [V W] rows of the tile's rows: As[k][r]
+  __shared__ float Bs[2 * SBW][SY + 1];  // [W V] rows of the tile's columns: Bs[k][r]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
+  const int64_t z = blockIdx.y;
+  // tile (bi, bj) from the linear index x = bi (bi + 1) / 2 + bj
+  const int x = blockIdx.x;
+  int bi = static_cast<int>((sqrtf(8.f * x + 1.f) - 1.f) * 0.5f);
+  while (bi * (bi + 1) / 2 > x) --bi;
+  while ((bi + 1) * (bi + 2) / 2 <= x) ++bi;
+  const int bj = x - bi * (bi + 1) / 2;
+  const int i0 = SY * bi, j0 = SY * bj;
+  float* a = A + z * a_batch;
+  const float* VW = VW_g + z * vw_batch;
+  float4 rc[4], ra[4], rb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = tid + 256 * q, c = idx >> 4, r4 = (idx & 15) * 4;
+    rc[q] = (i0 + r4 < mp && j0 + c < mp)
+                ? *reinterpret_cast<const float4*>(a + static_cast<int64_t>(j0 + c) * n + i0 + r4)
+                : make_float4(0.f, 0.f, 0.f, 0.f);
+    // operand column k = c: [V W] column c at rows i0.., [W V] column c = [V W] column c ^ 32 at rows j0..
+    ra[q] = i0 + r4 < mp ? *reinterpret_cast<const float4*>(VW + static_cast<int64_t>(c) * mp + i0 + r4)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    rb[q] = j0 + r4 < mp ? *reinterpret_cast<const float4*>(VW + static_cast<int64_t>(c ^ SBW) * mp + j0 + r4)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = tid + 256 * q, c = idx >> 4, r4 = (idx & 15) * 4;
+    As[c][r4] = ra[q].x; As[c][r4 + 1] = ra[q].y; As[c][r4 + 2] = ra[q].z; As[c][r4 + 3] = ra[q].w;
+    Bs[c][r4] = rb[q].x; Bs[c][r4 + 1] = rb[q].y; Bs[c][r4 + 2] = rb[q].z; Bs[c][r4 + 3] = rb[q].w;
+  }
+  __syncthreads();
+  const int wi = wave & 1, wj = wave >> 1;
+  f32x16 acc = {};
+  if (!(bi == bj && wi < wj)) {          // sub-blocks above the diagonal are not needed
+#pragma unroll
+    for (int s = 0; s < SBW; ++s) {
+      const int k = 2 * s + hf;
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[k][32 * wi + rl], Bs[k][32 * wj + rl], acc, 0, 0, 0);
+    }
+  }
+  __syncthreads();
+  // the product, column-major through LDS (As reused: As[c][r] = product at row r, column c)
+#pragma unroll
+  for (int e = 0; e < 16; ++e) As[32 * wj + rl][32 * wi + (e >> 2) * 8 + hf * 4 + (e & 3)] = acc[e];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = tid + 256 * q, c = idx >> 4, r4 = (idx & 15) * 4;
+    if (i0 + r4 < mp && j0 + c < mp) {
+      const int gc = j0 + c;
+      float4 v = rc[q];
+      if (i0 + r4 >= gc) v.x -= As[c][r4];
+      if (i0 + r4 + 1 >= gc) v.y -= As[c][r4 + 1];
+      if (i0 + r4 + 2 >= gc) v.z -= As[c][r4 + 2];
+      if (i0 + r4 + 3 >= gc) v.w -= As[c][r4 + 3];
+      *reinterpret_cast<float4*>(a + static_cast<int64_t>(gc) * n + i0 + r4) = v;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void k_copy_cols(const float* in, int64_t ld_in, int64_t in_batch, float* out,
                                                   int64_t ld_out, int64_t out_batch, int64_t rows, int64_t cols) {
   const int64_t z = blockIdx.y;
@@ -791,7 +1056,7 @@ __global__ __launch_bounds__(256) void k_copy_cols(const float* in, int64_t ld_i
 struct SyevLayout {
   int64_t P, vtot, nref;
   size_t v_off, t_off, tau_off, y_off, x_off, s1_off, s2_off, s3_off, wb_off, wb2_off, part_off, pscr_off,
-      bw_off, rf_off, d_off, e_off, lam_off, dp_off, yv_off, nrm_off, cbt_off, total;
+      bw_off, rf_off, d_off, e_off, lam_off, dp_off, yv_off, nrm_off, cbt_off, sp_off, total;
   int64_t ng, K0;                 // chase groups of 32 sweeps, steps of sweep 0
 };
 
@@ -832,6 +1097,7 @@ SyevLayout syev_layout(int64_t n, int R, int batch) {
   L.ng = (n - 2 + SBW - 1) / SBW;
   L.K0 = sweep_steps(n, 0);
   L.cbt_off = take(B * (L.ng > 0 ? L.ng : 1) * (L.K0 > 0 ? L.K0 : 1) * SBW * SBW * 4);
+  L.sp_off = take(B * ((n + SY - 1) / SY) * 1024 * 4);
   L.total = off;
   return L;
 }
@@ -863,6 +1129,7 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
   float* Wb2 = reinterpret_cast<float*>(wb + Lw.wb2_off);
   float* part = reinterpret_cast<float*>(wb + Lw.part_off);
   float* pscr = reinterpret_cast<float*>(wb + Lw.pscr_off);
+  float* SP = reinterpret_cast<float*>(wb + Lw.sp_off);
   float* Bw = reinterpret_cast<float*>(wb + Lw.bw_off);
   float* Rf = reinterpret_cast<float*>(wb + Lw.rf_off);
   double* dd = reinterpret_cast<double*>(wb + Lw.d_off);
@@ -915,25 +1182,17 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
       if ((e = gemm(SBW, SBW, SBW, V, plain(1), plain(mp), vs, S2, plain(SBW), plain(1), 1024, panel, 1, n, nn,
                     -1.f, 1.f)) != hipSuccess) return e;
     }
+    // Y = A22 V, X = Y T and the shares of V^T X; [V W]; A22 -= [V W] [W V]^T
     float* A22 = A + r * n + r;
-    // X = A22 V T, into the W half of VW
     const int64_t vwb = n * 2 * SBW;
-    float* Xb = VW + SBW * mp;
-    if ((e = gemm(mp, SBW, mp, A22, plain(1), plain(n), nn, V, plain(1), plain(mp), vs, Yb, 1, mp, n * SBW, 1.f,
-                  0.f, 1, /*a_sym=*/1)) != hipSuccess) return e;
-    if ((e = gemm(mp, SBW, SBW, Yb, plain(1), plain(mp), n * SBW, T, plain(SBW), plain(1), ts, Xb, 1, mp, vwb,
-                  1.f, 0.f)) != hipSuccess) return e;
-    // W = X - V (T^T (V^T X)) / 2, in place in X
-    if ((e = gemm(SBW, SBW, mp, V, plain(mp), plain(1), vs, Xb, plain(1), plain(mp), vwb, S1, SBW, 1, 1024,
-                  1.f, 0.f, ksplit_for(mp))) != hipSuccess) return e;
-    if ((e = gemm(SBW, SBW, SBW, T, plain(1), plain(SBW), ts, S1, plain(SBW), plain(1), 1024, S2, SBW, 1, 1024,
-                  1.f, 0.f)) != hipSuccess) return e;
-    if ((e = gemm(mp, SBW, SBW, V, plain(1), plain(mp), vs, S2, plain(SBW), plain(1), 1024, Xb, 1, mp, vwb,
-                  -0.5f, 1.f)) != hipSuccess) return e;
-    // A22 -= V W^T + W V^T as one product of K = 64: [V W] [W V]^T
-    if ((e = copy_cols(V, mp, vs, VW, mp, vwb, mp, SBW, batch, s)) != hipSuccess) return e;
-    if ((e = gemm(mp, mp, 2 * SBW, VW, plain(1), plain(mp), vwb, Xb, segmented(SBW, -SBW * mp, mp), plain(1), vwb,
-                  A22, 1, n, nn, -1.f, 1.f, 1, 0, /*c_lower=*/1)) != hipSuccess) return e;
+    const int nbk = static_cast<int>((mp + SY - 1) / SY);
+    k_symm_v<<<dim3(nbk, batch), 256, 0, s>>>(A22, n, nn, static_cast<int>(mp), V, vs, T, ts, VW, vwb, SP);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_w_form<<<dim3(nbk, batch), 256, 0, s>>>(static_cast<int>(mp), V, vs, T, ts, VW, vwb, SP);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_syr2k<<<dim3(static_cast<unsigned>(nbk * (nbk + 1) / 2), batch), 256, 0, s>>>(A22, n, nn,
+                                                                                  static_cast<int>(mp), VW, vwb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   }
   // ---- stage 2: band -> tridiagonal
