@@ -275,7 +275,7 @@ COMPARE_EXACT = {"mistral7b_t1024_flash"}
 CPU_SAMPLE = {"mistral7b_t4096_2x": 24, "mistral7b_t1024_flash": 64, "llama13b_t4096_2x": 2,
               "mistral7b_t32768_3x": 4}
 
-KERNELS = ("jacobi_update", "jacobi_solve", "jacobi128", "qr_panel", "gemm", "gemm_bf16", "band", "chase",
+KERNELS = ("jacobi_update", "jacobi_solve", "jacobi128", "qr_panel", "qr_update", "gemm", "gemm_bf16", "band", "chase",
            "tri_eig", "chase_back", "band_back", "encode_residual", "decode_w", "decode")
 CSRC = os.path.join(ROOT, "kv_cache_compression_mode_amd", "csrc")
 MFMA_BF16_PEAK_TFLOPS = 2500.0

@@ -257,8 +257,9 @@ typedef struct {
  * grid seen (the only device memory the library allocates by itself; freed
  * by the next call).  Not safe with concurrent hot-path calls on other
  * streams.  Kernel names: "jacobi_update", "jacobi_solve", "jacobi128",
- * "qr_panel", "gemm" (fp32 matrix-core products), "gemm_bf16" (bf16
- * matrix-core products), "band", "chase", "tri_eig", "chase_back",
+ * "qr_panel", "qr_update" (block reflectors applied to tall blocks), "gemm"
+ * (fp32 matrix-core products), "gemm_bf16" (bf16 matrix-core products),
+ * "band", "chase", "tri_eig", "chase_back",
  * "band_back" (the eigensolver stages), "encode_residual", "decode_w",
  * "decode".  "gemm" and "gemm_bf16" also account their algorithmic bytes and
  * flops. */

@@ -574,6 +574,161 @@ __global__ __launch_bounds__(RT) void k_qr_reg(float* A, int64_t m, int64_t ld, 
   for (int idx = t; idx < 1024; idx += RT) Tp[z * tstride + idx] = Tl[idx >> 5][idx & 31];
 }
 
+// Block reflector on a tall block: Z <- (I - V op(T) V^T) Z, Z mr x nc
+// (column-major, leading dimension ldz), V mr x 32 (leading dimension ldv,
+// rows aligned with Z's), op(T) = T or T^T.  The rows split into chunks of
+// rch rows (a multiple of 64) and the columns into tiles of 64:
+// k_wy_part: W_c = V_c^T Z_c for row chunk c and one column tile;
+// k_wy_mid: W2 = op(T) (sum over c of W_c), summed in chunk order;
+// k_wy_upd: Z_c -= V_c W2.
+// Inside a chunk the rows stream in blocks of 64, the next block loaded into
+// registers while the current one is multiplied on the fp32 matrix cores.
+struct WyTile {
+  float Zs[64][65];
+  float Vs[64][33];
+};
+
+__device__ __forceinline__ void wy_load(const float* Z, int64_t ldz, int64_t mr, int nc, int j0, const float* V,
+                                        int64_t ldv, int64_t r0, float (&rz)[16], float (&rv)[8]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int idx = tid + 256 * q, c = idx >> 6, rr = idx & 63;
+    rz[q] = (r0 + rr < mr && j0 + c < nc) ? Z[static_cast<int64_t>(j0 + c) * ldz + r0 + rr] : 0.f;
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int idx = tid + 256 * q, c = idx >> 6, rr = idx & 63;
+    rv[q] = r0 + rr < mr ? V[static_cast<int64_t>(c) * ldv + r0 + rr] : 0.f;
+  }
+}
+
+__device__ __forceinline__ void wy_store(WyTile& L, const float (&rz)[16], const float (&rv)[8]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int idx = tid + 256 * q;
+    L.Zs[idx & 63][idx >> 6] = rz[q];
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int idx = tid + 256 * q;
+    L.Vs[idx & 63][idx >> 6] = rv[q];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_wy_part(const float* Z_g, int64_t ldz, int64_t z_batch, int64_t mr, int nc,
+                                                 const float* V_g, int64_t ldv, int64_t v_batch, int64_t rch,
+                                                 float* Wp) {
+  __shared__ WyTile L;
+  __shared__ float Wh[2][32][65];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
+  const int64_t z = blockIdx.z;
+  const int ch = blockIdx.x, nch = gridDim.x, j0 = 64 * blockIdx.y;
+  const float* Z = Z_g + z * z_batch;
+  const float* V = V_g + z * v_batch;
+  const int64_t rbeg = ch * rch, rend = rbeg + rch < mr ? rbeg + rch : mr;
+  const int cb = 32 * (wave & 1), kb = 32 * (wave >> 1);
+  float rz[16], rv[8];
+  f32x16 acc = {};
+  if (rbeg < rend) wy_load(Z, ldz, rend, nc, j0, V, ldv, rbeg, rz, rv);
+  for (int64_t r0 = rbeg; r0 < rend; r0 += 64) {
+    wy_store(L, rz, rv);
+    __syncthreads();
+    if (r0 + 64 < rend) wy_load(Z, ldz, rend, nc, j0, V, ldv, r0 + 64, rz, rv);
+#pragma unroll
+    for (int kk = 0; kk < 32; kk += 2) {
+      const int k = kb + kk + hf;
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(L.Vs[k][rl], L.Zs[k][cb + rl], acc, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) Wh[wave >> 1][(e >> 2) * 8 + hf * 4 + (e & 3)][cb + rl] = acc[e];
+  __syncthreads();
+  float* wp = Wp + (z * nch + ch) * 32 * static_cast<int64_t>(nc);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int idx = tid + 256 * q, a = idx >> 6, j = idx & 63;
+    if (j0 + j < nc) wp[a * static_cast<int64_t>(nc) + j0 + j] = Wh[0][a][j] + Wh[1][a][j];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_wy_mid(int nc, int nch, const float* Wp, const float* T_g, int64_t t_batch,
+                                                int trans, float* W2) {
+  __shared__ float Ws[32][65];
+  __shared__ float Ts[32][33];
+  const int tid = threadIdx.x;
+  const int64_t z = blockIdx.y;
+  const int j0 = 64 * blockIdx.x;
+  for (int idx = tid; idx < 1024; idx += 256) {
+    const float t = T_g[z * t_batch + idx];
+    if (trans) Ts[idx & 31][idx >> 5] = t;
+    else Ts[idx >> 5][idx & 31] = t;
+  }
+  const float* wp = Wp + z * nch * 32 * static_cast<int64_t>(nc);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int idx = tid + 256 * q, a = idx >> 6, j = idx & 63;
+    float u = 0.f;
+    if (j0 + j < nc)
+      for (int c = 0; c < nch; ++c) u += wp[(c * 32 + a) * static_cast<int64_t>(nc) + j0 + j];
+    Ws[a][j] = u;
+  }
+  __syncthreads();
+  float* w2 = W2 + z * 32 * static_cast<int64_t>(nc);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int idx = tid + 256 * q, a = idx >> 6, j = idx & 63;
+    float u = 0.f;
+#pragma unroll
+    for (int m = 0; m < 32; ++m) u += Ts[a][m] * Ws[m][j];
+    if (j0 + j < nc) w2[a * static_cast<int64_t>(nc) + j0 + j] = u;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_wy_upd(float* Z_g, int64_t ldz, int64_t z_batch, int64_t mr, int nc,
+                                                const float* V_g, int64_t ldv, int64_t v_batch, int64_t rch,
+                                                const float* W2) {
+  __shared__ WyTile L;
+  __shared__ float Ws[32][65];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
+  const int64_t z = blockIdx.z;
+  const int ch = blockIdx.x, j0 = 64 * blockIdx.y;
+  float* Z = Z_g + z * z_batch;
+  const float* V = V_g + z * v_batch;
+  const int64_t rbeg = ch * rch, rend = rbeg + rch < mr ? rbeg + rch : mr;
+  const float* w2 = W2 + z * 32 * static_cast<int64_t>(nc);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int idx = tid + 256 * q, a = idx >> 6, j = idx & 63;
+    Ws[a][j] = j0 + j < nc ? w2[a * static_cast<int64_t>(nc) + j0 + j] : 0.f;
+  }
+  const int cb = 32 * (wave & 1), kb = 32 * (wave >> 1);
+  float rz[16], rv[8];
+  if (rbeg < rend) wy_load(Z, ldz, rend, nc, j0, V, ldv, rbeg, rz, rv);
+  for (int64_t r0 = rbeg; r0 < rend; r0 += 64) {
+    __syncthreads();                     // W2 visible; the previous block's Zs / Vs reads done
+    wy_store(L, rz, rv);
+    __syncthreads();
+    if (r0 + 64 < rend) wy_load(Z, ldz, rend, nc, j0, V, ldv, r0 + 64, rz, rv);
+    f32x16 d = {};
+#pragma unroll
+    for (int kk = 0; kk < 32; kk += 2) {
+      const int k = kk + hf;
+      d = __builtin_amdgcn_mfma_f32_32x32x2f32(L.Vs[kb + rl][k], Ws[k][cb + rl], d, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) L.Zs[kb + (e >> 2) * 8 + hf * 4 + (e & 3)][cb + rl] -= d[e];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = tid + 256 * q, c = idx >> 6, rr = idx & 63;
+      if (r0 + rr < rend && j0 + c < nc) Z[static_cast<int64_t>(j0 + c) * ldz + r0 + rr] = L.Zs[rr][c];
+    }
+  }
+}
+
 // Top block of the panel's Q (leaf 0's first nb rows times Q_top's first
 // block), its sign-chosen LU, and T = -U S L_1^{-T}; U and L_1 -> UL for the
 // tall part.
@@ -873,33 +1028,37 @@ hipError_t panel_factor(float* A, int64_t m, int64_t ld, int64_t bstride, int64_
   return hipGetLastError();
 }
 
+hipError_t apply_wy_tall(float* Z, int64_t ldz, int64_t z_batch, int64_t mr, int nc, const float* V, int64_t ldv,
+                         int64_t v_batch, const float* T, int64_t t_batch, int trans, int batch, float* Wp,
+                         float* W2, hipStream_t s) {
+  if (mr <= 0 || nc <= 0) return hipSuccess;
+  ProfScope ps("qr_update", s);
+  const int64_t blocks = (mr + 63) / 64;
+  const int nch = static_cast<int>(blocks < kQrSplit ? blocks : kQrSplit);
+  const int64_t rch = 64 * ((blocks + nch - 1) / nch);
+  const int nct = (nc + 63) / 64;
+  k_wy_part<<<dim3(nch, nct, batch), 256, 0, s>>>(Z, ldz, z_batch, mr, nc, V, ldv, v_batch, rch, Wp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_wy_mid<<<dim3(nct, batch), 256, 0, s>>>(nc, nch, Wp, T, t_batch, trans, W2);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  k_wy_upd<<<dim3(nch, nct, batch), 256, 0, s>>>(Z, ldz, z_batch, mr, nc, V, ldv, v_batch, rch, W2);
+  return hipGetLastError();
+}
+
 hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t bstride, int batch,
                           float* work, hipStream_t s) {
   constexpr int NB = 32;
   const int64_t P = (k + NB - 1) / NB;
   float* Vall = work;                                        // [batch][P][m][32]
   float* Tall = Vall + static_cast<size_t>(batch) * P * m * NB;   // [batch][P][32][32]
-  float* W = Tall + static_cast<size_t>(batch) * P * NB * NB;     // [batch][32][k]
-  float* W2 = W + static_cast<size_t>(batch) * NB * k;            // [batch][32][k]
-  float* taus = W2 + static_cast<size_t>(batch) * NB * k;         // [batch][2k]
+  float* W2 = Tall + static_cast<size_t>(batch) * P * NB * NB;    // [batch][32][k] (two such slots)
+  float* taus = W2 + static_cast<size_t>(batch) * 2 * NB * k;     // [batch][2k]
   float* Qb = taus + static_cast<size_t>(batch) * (2 * k + 64);    // [batch][m][32]
   float* part = Qb + panel_factor_scratch_floats(m, batch);       // [batch][kQrSplit][32][k]
   const int64_t vstride = P * m * NB, tstride = P * NB * NB;
   auto Vp = [&](int64_t p) { return Vall + p * m * NB; };
   auto Tp = [&](int64_t p) { return Tall + p * NB * NB; };
-  auto gemm = [&](int64_t M, int64_t N, int64_t K, const float* Ab, GemmDim am, GemmDim ak, int64_t ab,
-                  const float* Bb, GemmDim bk, GemmDim bn, int64_t bb, float* Cb, int64_t cm, int64_t cn,
-                  int64_t cb, float alpha, float beta, int ksplit = 1) -> hipError_t {
-    if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
-    GemmArgs g{};
-    g.M = M; g.N = N; g.K = K;
-    g.A = Ab; g.a_dtype = kF32; g.am = am; g.ak = ak; g.a_batch = ab;
-    g.B = Bb; g.b_dtype = kF32; g.bk = bk; g.bn = bn; g.b_batch = bb;
-    g.C = Cb; g.c_dtype = kF32; g.c_m = cm; g.c_n = cn; g.c_batch = cb;
-    g.alpha = alpha; g.beta = beta;
-    if (ksplit > 1 && M <= NB && N <= k) { g.ksplit = ksplit; g.partial = part; }
-    return launch_gemm(g, batch, s);
-  };
   hipError_t e;
   // ---- factorization
   for (int64_t p = 0; p < P; ++p) {
@@ -911,40 +1070,23 @@ hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t bs
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t n2 = k - c0 - nb, mr = m - c0;
     if (n2 <= 0) continue;
-    // W = V^T A2  (nb x n2, K = m - c0)
-    if ((e = gemm(nb, n2, mr, Vp(p) + c0, plain(m), plain(1), vstride, A + (c0 + nb) * ld + c0, plain(1),
-                  plain(ld), bstride, W, k, 1, NB * k, 1.f, 0.f, qr_ksplit(mr))) != hipSuccess) return e;
-    // W2 = T^T W
-    if ((e = gemm(nb, n2, nb, Tp(p), plain(1), plain(NB), tstride, W, plain(k), plain(1), NB * k, W2, k,
-                  1, NB * k, 1.f, 0.f)) != hipSuccess) return e;
-    // A2 -= V W2
-    if ((e = gemm(mr, n2, nb, Vp(p) + c0, plain(1), plain(m), vstride, W2, plain(k), plain(1), NB * k,
-                  A + (c0 + nb) * ld + c0, 1, ld, bstride, -1.f, 1.f)) != hipSuccess) return e;
+    // A2 <- (I - V T^T V^T) A2 (rows c0.., the columns right of the panel)
+    if ((e = apply_wy_tall(A + (c0 + nb) * ld + c0, ld, bstride, mr, static_cast<int>(n2), Vp(p) + c0, m,
+                           vstride, Tp(p), tstride, 1, batch, part, W2, s)) != hipSuccess)
+      return e;
   }
-  // ---- explicit Q, back to front
+  // ---- explicit Q, back to front: the panel's columns start as identity
+  // columns, then Q[c0:, c0:] <- (I - V T V^T) Q[c0:, c0:]
   for (int64_t p = P - 1; p >= 0; --p) {
     const int64_t c0 = p * NB;
     const int nb = static_cast<int>(k - c0 < NB ? k - c0 : NB);
-    const int64_t n2 = k - c0 - nb, mr = m - c0;
-    if (n2 > 0) {
-      // Q[c0:, right] -= V (T (V^T Q[c0:, right]))
-      if ((e = gemm(nb, n2, mr, Vp(p) + c0, plain(m), plain(1), vstride, A + (c0 + nb) * ld + c0,
-                    plain(1), plain(ld), bstride, W, k, 1, NB * k, 1.f, 0.f, qr_ksplit(mr))) != hipSuccess)
-        return e;
-      if ((e = gemm(nb, n2, nb, Tp(p), plain(NB), plain(1), tstride, W, plain(k), plain(1), NB * k, W2,
-                    k, 1, NB * k, 1.f, 0.f)) != hipSuccess) return e;
-      if ((e = gemm(mr, n2, nb, Vp(p) + c0, plain(1), plain(m), vstride, W2, plain(k), plain(1), NB * k,
-                    A + (c0 + nb) * ld + c0, 1, ld, bstride, -1.f, 1.f)) != hipSuccess) return e;
-    }
-    // panel columns: E - V (T V_top^T), V_top = rows c0 .. c0+nb of V
     int64_t blocks = (m * nb + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     k_eye_cols<<<dim3(blocks, batch), 256, 0, s>>>(A, m, ld, bstride, c0, nb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = gemm(nb, nb, nb, Tp(p), plain(NB), plain(1), tstride, Vp(p) + c0, plain(m), plain(1), vstride,
-                  W2, k, 1, NB * k, 1.f, 0.f)) != hipSuccess) return e;
-    if ((e = gemm(mr, nb, nb, Vp(p) + c0, plain(1), plain(m), vstride, W2, plain(k), plain(1), NB * k,
-                  A + c0 * ld + c0, 1, ld, bstride, -1.f, 1.f)) != hipSuccess) return e;
+    if ((e = apply_wy_tall(A + c0 * ld + c0, ld, bstride, m - c0, static_cast<int>(k - c0), Vp(p) + c0, m, vstride,
+                           Tp(p), tstride, 0, batch, part, W2, s)) != hipSuccess)
+      return e;
   }
   int64_t blocks = (m * k + 255) / 256;
   if (blocks > 8192) blocks = 8192;
