@@ -574,6 +574,8 @@ __global__ __launch_bounds__(RT) void k_qr_reg(float* A, int64_t m, int64_t ld, 
   for (int idx = t; idx < 1024; idx += RT) Tp[z * tstride + idx] = Tl[idx >> 5][idx & 31];
 }
 
+constexpr int kQrSplit = 16;     // row chunks of a tall block-reflector application
+
 // Block reflector on a tall block: Z <- (I - V op(T) V^T) Z, Z mr x nc
 // (column-major, leading dimension ldz), V mr x 32 (leading dimension ldv,
 // rows aligned with Z's), op(T) = T or T^T.  The rows split into chunks of
@@ -670,9 +672,14 @@ __global__ __launch_bounds__(256) void k_wy_mid(int nc, int nch, const float* Wp
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int idx = tid + 256 * q, a = idx >> 6, j = idx & 63;
+    // the chunks' shares added in chunk order, all loads in flight (nch <= kQrSplit)
+    float v[kQrSplit];
+#pragma unroll
+    for (int c = 0; c < kQrSplit; ++c)
+      v[c] = (c < nch && j0 + j < nc) ? wp[(c * 32 + a) * static_cast<int64_t>(nc) + j0 + j] : 0.f;
     float u = 0.f;
-    if (j0 + j < nc)
-      for (int c = 0; c < nch; ++c) u += wp[(c * 32 + a) * static_cast<int64_t>(nc) + j0 + j];
+#pragma unroll
+    for (int c = 0; c < kQrSplit; ++c) u += v[c];
     Ws[a][j] = u;
   }
   __syncthreads();
@@ -964,7 +971,6 @@ __global__ __launch_bounds__(256) void k_emit(const float* U, int64_t m, int64_t
 
 }  // namespace
 
-constexpr int kQrSplit = 16;     // split-K of the long products V^T A (K = rows below the panel)
 
 size_t householder_qr_work_floats(int64_t m, int64_t k, int batch) {
   const int64_t P = (k + 31) / 32;
@@ -974,12 +980,6 @@ size_t householder_qr_work_floats(int64_t m, int64_t k, int batch) {
                                        2 * kStack + 1024 + static_cast<int64_t>(kQrSplit) * 32 * k);
 }
 
-namespace {
-int qr_ksplit(int64_t K) {        // chunks of at least 256 rows
-  const int64_t s = K / 256;
-  return static_cast<int>(s < 1 ? 1 : (s > kQrSplit ? kQrSplit : s));
-}
-}  // namespace
 
 size_t panel_factor_scratch_floats(int64_t m, int batch) {
   return static_cast<size_t>(batch) * (m * 32 + 2 * kStack + 1024);

@@ -596,7 +596,7 @@ __global__ __launch_bounds__(256) void k_cb_apply(int t, int glo, int nchunk, fl
   __shared__ float Vs[CBR][SBW + 1];     // staircase V[r][i]
   __shared__ float Ts[SBW][SBW + 1];
   __shared__ float Zs[CBR][65];          // Z rows x 64 columns
-  __shared__ float Wp[2][SBW][65];       // W partial sums, then W2
+  __shared__ float Wp[2][SBW][65];       // W partial sums, then W2 = T W (in Wp[0])
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
   const int bi = blockIdx.x / nchunk, ch = blockIdx.x % nchunk;
   const int gp = glo + bi, s = t - 2 * gp, G = ng - 1 - gp, jg = G * SBW;
@@ -609,7 +609,8 @@ __global__ __launch_bounds__(256) void k_cb_apply(int t, int glo, int nchunk, fl
   const float* Rf = Rf_g + z * rf_stride;
   float* Zz = Z + z * z_batch;
   const int last = n - 3;
-  for (int idx = tid; idx < CBR * (SBW + 1); idx += 256) (&Vs[0][0])[idx] = 0.f;
+  // one phase of loads: T, Z, the staircase V[i + r][i] = v_r of sweep jg + i
+  // and zeros off the staircase (disjoint positions)
   for (int idx = tid; idx < SBW * SBW; idx += 256) {
     const int r = idx / SBW, c = idx % SBW;
     Ts[r][c] = Tg[z * t_stride + (static_cast<int64_t>(G) * K0 + s) * SBW * SBW + idx];
@@ -618,10 +619,13 @@ __global__ __launch_bounds__(256) void k_cb_apply(int t, int glo, int nchunk, fl
     const int c = idx / CBR, r = idx % CBR;
     Zs[r][c] = (r < rows && c < nc) ? Zz[static_cast<int64_t>(c0 + c) * n + rb + r] : 0.f;
   }
-  __syncthreads();
   for (int idx = tid; idx < SBW * SBW; idx += 256) {
     const int i = idx / SBW, r = idx % SBW, j = jg + i;
-    if (j <= last && s < sweep_steps(n, j)) Vs[i + r][i] = Rf[(sweep_offset(n, j) + s) * RFS + r];
+    Vs[i + r][i] = (j <= last && s < sweep_steps(n, j)) ? Rf[(sweep_offset(n, j) + s) * RFS + r] : 0.f;
+  }
+  for (int idx = tid; idx < CBR * SBW; idx += 256) {
+    const int row = idx / SBW, i = idx % SBW;
+    if (row < i || row >= i + SBW) Vs[row][i] = 0.f;
   }
   __syncthreads();
   // W = V^T Z: wave w -> columns 32 (w & 1) .., rows of V 32 (w >> 1) ..
@@ -926,13 +930,22 @@ __global__ __launch_bounds__(256) void k_w_form(int mp, const float* V_g, int64_
   const float* V = V_g + z * v_batch;
   float* VW = VW_g + z * vw_batch;
   const float* sp = SP + z * nb * 1024;
+  {
+    // elements 4 tid .. 4 tid + 3, the shares added in block order, eight loads in flight
+    const int e = 4 * tid;
+    float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int b0 = 0; b0 < nb; b0 += 8) {
+      float4 v[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = tid + 256 * q;
-    float u = 0.f;
-    for (int b = 0; b < nb; ++b) u += sp[b * 1024 + e];
-    Ss[e >> 5][e & 31] = u;
-    Ts[e >> 5][e & 31] = T_g[z * t_batch + e];
+      for (int q = 0; q < 8; ++q)
+        v[q] = b0 + q < nb ? *reinterpret_cast<const float4*>(sp + (b0 + q) * 1024 + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) { u.x += v[q].x; u.y += v[q].y; u.z += v[q].z; u.w += v[q].w; }
+    }
+    const float4 t4 = *reinterpret_cast<const float4*>(T_g + z * t_batch + e);
+    const int a = e >> 5, b = e & 31;
+    Ss[a][b] = u.x; Ss[a][b + 1] = u.y; Ss[a][b + 2] = u.z; Ss[a][b + 3] = u.w;
+    Ts[a][b] = t4.x; Ts[a][b + 1] = t4.y; Ts[a][b + 2] = t4.z; Ts[a][b + 3] = t4.w;
   }
   // V rows of this block: to LDS and to the V half of [V W]
 #pragma unroll
@@ -947,7 +960,7 @@ __global__ __launch_bounds__(256) void k_w_form(int mp, const float* V_g, int64_
     }
   }
   __syncthreads();
-#pragma unroll
+#pragma unroll 1
   for (int q = 0; q < 4; ++q) {                  // S2 = T^T S
     const int e = tid + 256 * q, a = e >> 5, b = e & 31;
     float u = 0.f;
@@ -964,7 +977,7 @@ __global__ __launch_bounds__(256) void k_w_form(int mp, const float* V_g, int64_
       float* w = Wd + static_cast<int64_t>(c) * mp + i0 + r4;
       float4 x = *reinterpret_cast<const float4*>(w);
       float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
-#pragma unroll
+#pragma unroll 4
       for (int a2 = 0; a2 < SBW; ++a2) {
         const float s2 = S2[a2][c];
         d0 += Vr[r4][a2] * s2;
