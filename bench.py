@@ -279,19 +279,37 @@ KERNELS = ("jacobi_update", "jacobi_solve", "jacobi128", "qr_panel", "qr_update"
            "tri_eig", "chase_back", "band_back", "encode_residual", "decode_w", "decode")
 CSRC = os.path.join(ROOT, "kv_cache_compression_mode_amd", "csrc")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# fp32 vector arithmetic without packed instructions (which the build turns
+# off): 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz
+VALU_FP32_PEAK_TFLOPS = 78.6
 # kernels whose launches account their algorithmic work (bytes, flops):
 # name -> (description, symbol, pattern of its kernel names in profiler
 #          traces, sources of the kernel, peak of the matrix cores it runs on
 #          in TFLOP/s)
 ROOF = {
-    "gemm": ("k_gemm: strided batched 64x64-tile GEMM on fp32 matrix cores (the fp32 products of a step: "
-             "band reduction, panel back-transformation, QR trailing updates, small products)",
-             "k_gemm", r"k_gemm(<|_bf16\b)", ("gemm.hip", "device.hpp"), MFMA_FP32_PEAK_TFLOPS),
+    "chase": ("k_chase: bulge chasing, band to tridiagonal, one workgroup per matrix, sweeps pipelined over its "
+              "waves (fp32 vector arithmetic)",
+              "k_chase", r"k_chase<", ("tridiag.hip", "device.hpp"), VALU_FP32_PEAK_TFLOPS, "alu"),
+    "chase_back": ("k_cb_tfac + k_cb_apply: the chase reflectors applied to the eigenvectors in compact-WY "
+                   "blocks of 32 sweeps (fp32 matrix cores)",
+                   "k_cb_apply", r"k_cb_(apply|tfac)\b", ("tridiag.hip", "device.hpp"), MFMA_FP32_PEAK_TFLOPS,
+                   "mfma"),
+    "band": ("k_qr_reg + k_symm_v + k_w_form + k_syr2k: dense to band, per panel a register QR, the symmetric "
+             "product, W, and the lower-triangle rank-64 update (fp32 matrix cores)",
+             "k_syr2k", r"k_(qr_reg|symm_v|w_form|syr2k)\b", ("tridiag.hip", "qr.hip", "device.hpp"),
+             MFMA_FP32_PEAK_TFLOPS, "mfma"),
+    "band_back": ("k_apply_wy: the panel reflectors applied to the eigenvectors (fp32 matrix cores)",
+                  "k_apply_wy", r"k_apply_wy\b", ("tridiag.hip", "device.hpp"), MFMA_FP32_PEAK_TFLOPS, "mfma"),
+    "qr_update": ("k_wy_part + k_wy_mid + k_wy_upd: block reflectors applied to tall blocks in the Householder "
+                  "QR of the token factor (fp32 matrix cores)",
+                  "k_wy_upd", r"k_wy_(part|mid|upd)\b", ("qr.hip", "device.hpp"), MFMA_FP32_PEAK_TFLOPS, "mfma"),
+    "gemm": ("k_gemm: strided batched 64x64-tile GEMM on fp32 matrix cores (small products)",
+             "k_gemm", r"k_gemm(<|_bf16\b)", ("gemm.hip", "device.hpp"), MFMA_FP32_PEAK_TFLOPS, "mfma"),
     "gemm_bf16": ("k_gemm_x: 128x128-tile GEMM on bf16 matrix cores (token and feature Grams, factor recovery, "
                   "Rayleigh and core products; fp32 operands enter as bf16 hi + lo)",
-                  "k_gemm_x", r"k_gemm_x<", ("gemm.hip", "device.hpp"), MFMA_BF16_PEAK_TFLOPS),
+                  "k_gemm_x", r"k_gemm_x<", ("gemm.hip", "device.hpp"), MFMA_BF16_PEAK_TFLOPS, "mfma"),
     "jacobi_update": ("k_jac_update: block-Jacobi rotation of A and V, fp32 matrix cores",
-                      "k_jac_update", r"k_jac_update\b", ("eig.hip", "device.hpp"), MFMA_FP32_PEAK_TFLOPS),
+                      "k_jac_update", r"k_jac_update\b", ("eig.hip", "device.hpp"), MFMA_FP32_PEAK_TFLOPS, "mfma"),
 }
 
 
@@ -380,12 +398,12 @@ def roofline_for(name, st, workload):
     ai = flops_l / max(bytes_l, 1.0)
     gbps = bytes_l / (avg_ms * 1e-3) / 1e9
     tflops = flops_l / (avg_ms * 1e-3) / 1e12
-    peak_tf = ROOF[name][4]
+    peak_tf, kind = ROOF[name][4], ROOF[name][5]
     ridge = peak_tf * 1e12 / (HBM_PEAK_GBPS * 1e9)
     if ai < ridge:
         bound, achieved, peak, unit = "hbm", gbps, HBM_PEAK_GBPS, "GB/s"
     else:
-        bound, achieved, peak, unit = "mfma", tflops, peak_tf, "TFLOP/s"
+        bound, achieved, peak, unit = kind, tflops, peak_tf, "TFLOP/s"
     desc, symbol = ROOF[name][0], ROOF[name][1]
     return {"kernel": desc, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4),

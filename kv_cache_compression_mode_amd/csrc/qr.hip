@@ -1033,6 +1033,10 @@ hipError_t apply_wy_tall(float* Z, int64_t ldz, int64_t z_batch, int64_t mr, int
                          float* W2, hipStream_t s) {
   if (mr <= 0 || nc <= 0) return hipSuccess;
   ProfScope ps("qr_update", s);
+  // algorithmic work: Z read and written once, V read once; 4 mr nc 32 flops
+  // (V^T Z and V W2) + 2 32^2 nc (op(T) W)
+  prof_add_work("qr_update", static_cast<double>(batch) * 4.0 * (2.0 * mr * nc + mr * 32.0),
+                static_cast<double>(batch) * (4.0 * mr * nc * 32.0 + 2.0 * 1024.0 * nc));
   const int64_t blocks = (mr + 63) / 64;
   const int nch = static_cast<int>(blocks < kQrSplit ? blocks : kQrSplit);
   const int64_t rch = 64 * ((blocks + nch - 1) / nch);

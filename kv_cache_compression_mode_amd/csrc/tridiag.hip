@@ -1175,6 +1175,19 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
   }
   {
   ProfScope ps_band("band", s);
+  {
+    // algorithmic work per panel: the lower triangle of A22 read by the
+    // symmetric product and read and written by the rank-64 update (3 passes),
+    // the panel read and written; 2 mp^2 b (A22 V) + 2 mp^2 (2 b) / 2 (the
+    // lower half of [V W][W V]^T) + 4 mp b^2 (panel QR) flops
+    double by = 0.0, fl = 0.0;
+    for (int64_t p = 0; p < Lw.P; ++p) {
+      const double mp = static_cast<double>(n - (p + 1) * SBW);
+      by += 3.0 * 4.0 * mp * (mp + 1) / 2 + 2.0 * 4.0 * mp * SBW;
+      fl += 2.0 * mp * mp * SBW + 2.0 * mp * mp * SBW + 4.0 * mp * SBW * SBW;
+    }
+    prof_add_work("band", batch * by, batch * fl);
+  }
   for (int64_t p = 0; p < Lw.P; ++p) {
     const int64_t c = p * SBW, r = c + SBW, mp = n - r;
     float* panel = A + c * n + r;                  // column-major mp x 32 (ld n)
@@ -1234,6 +1247,13 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
       ProfScope ps("chase", s);
       if (nw == 8) k_chase<8><<<batch, 8 * 64, lds, s>>>(Bw, static_cast<int>(n), Rf, Lw.nref * RFS, S);
       else k_chase<16><<<batch, 16 * 64, lds, s>>>(Bw, static_cast<int>(n), Rf, Lw.nref * RFS, S);
+      // algorithmic work: the band read and written once, every reflector
+      // written once; per step (b = 32) the reflector's two-sided action on the
+      // diagonal block (w = D v, D - v w^T - w v^T + c v v^T: 5 b^2 flops), its
+      // left action on the left block (4 b^2) and right action on the block
+      // below (4 b^2)
+      prof_add_work("chase", static_cast<double>(batch) * (2.0 * n * BWS * 4 + Lw.nref * RFS * 4.0),
+                    static_cast<double>(batch) * Lw.nref * 13.0 * SBW * SBW);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     int64_t tb = (n + 255) / 256;
@@ -1275,6 +1295,10 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     const int64_t tstr = Lw.ng * Lw.K0 * SBW * SBW;
     if (ng > 0 && K0 > 0) {
       ProfScope ps("chase_back", s);
+      // algorithmic work: Z (n x R) read and written once, every reflector
+      // read once; each 32-long reflector applied to R columns (4 b R flops)
+      prof_add_work("chase_back", static_cast<double>(batch) * (2.0 * n * R * 4 + Lw.nref * RFS * 4.0),
+                    static_cast<double>(batch) * Lw.nref * 4.0 * SBW * R);
       k_cb_tfac<<<dim3(static_cast<unsigned>(ng * K0), batch), 64, 0, s>>>(Rf, Lw.nref * RFS, static_cast<int>(n),
                                                                          K0, Tcb, tstr);
       if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1290,6 +1314,17 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
       }
     }
     ProfScope ps_bb("band_back", s);
+    {
+      // algorithmic work: per panel, Z rows r.. (mp x R) read and written,
+      // V read; 4 mp b R flops
+      double by = 0.0, fl = 0.0;
+      for (int64_t p = 0; p < Lw.P; ++p) {
+        const double mp = static_cast<double>(n - (p + 1) * SBW);
+        by += 4.0 * (2.0 * mp * R + mp * SBW);
+        fl += 4.0 * mp * SBW * R;
+      }
+      prof_add_work("band_back", batch * by, batch * fl);
+    }
     for (int64_t p = Lw.P - 1; p >= 0; --p) {
       const int64_t r = (p + 1) * SBW, mp = n - r;
       // Z rows r.. <- (I - V T V^T) Z rows r..
