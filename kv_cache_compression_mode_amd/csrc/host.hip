@@ -415,6 +415,8 @@ struct AllocWS {
   float* qtauD; double* lamDt; int* permD; float* sgnD;
   size_t bytes;
   int chunk;
+  int nlanes;          // scratch sets, one per stream (chunks alternate between them)
+  hipEvent_t band_done;  // recorded once the token eigensolver's band reduction is queued
 };
 
 struct Dims {
@@ -445,7 +447,13 @@ Dims dims_of(const jolt_alloc_req* r) {
   return d;
 }
 
-AllocWS carve_alloc(const jolt_alloc_req* r, void* base) {
+bool eig_jacobi();
+
+// Persistent outputs, the pointer and tag arrays of every tensor, then one
+// or two sets of chunk scratch (lanes): with two, consecutive chunks of half
+// the size alternate between two streams, so one chunk's single-CU-per-tensor
+// chase overlaps the other's matrix-core stages.
+AllocWS carve_alloc(const jolt_alloc_req* r, void* base, AllocWS* lane1 = nullptr) {
   const Dims d = dims_of(r);
   const int nt = 2 * r->n_layers;
   AllocWS w{};
@@ -458,11 +466,17 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base) {
   per += static_cast<size_t>(gram_d_ksplit(d)) * d.D * d.D * 4;
   per += syev_top_work_bytes(d.D, static_cast<int>(d.D), 1);
   if (!d.flash && d.R > 0) per += syev_top_work_bytes(d.n_pad, static_cast<int>(d.R), 1);
-  // up to 64 tensors (24 GiB of scratch) per chunk: the eigensolver's chase
-  // runs one workgroup per tensor, so wide chunks keep more of the chip busy
+  // up to 64 tensors (24 GiB of scratch) in flight.  Token eigenproblems of
+  // n >= 2048 go in two lanes of half chunks: there the stages around the
+  // chase are throughput-bound and overlap it; at smaller n they are
+  // latency-bound, and halving the batch only doubles their count (the
+  // Jacobi and randomized paths keep one lane).
   int chunk = static_cast<int>(std::max<size_t>(1, std::min<size_t>(64, (24ull << 30) / per)));
   chunk = std::min(chunk, nt);
+  const int nlanes = (chunk >= 2 && !eig_jacobi() && !d.flash && d.R > 0 && d.n_pad >= 2048) ? 2 : 1;
+  chunk = (chunk + nlanes - 1) / nlanes;
   w.chunk = chunk;
+  w.nlanes = nlanes;
   Carver c;
   c.base = static_cast<char*>(base);
   const int64_t R = std::max<int64_t>(d.R, 1);
@@ -471,46 +485,55 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base) {
   w.lamT = c.take<double>(static_cast<size_t>(nt) * R);
   w.lamD = c.take<double>(static_cast<size_t>(nt) * d.D);
   w.frob2 = c.take<double>(nt);
-  w.xptrs = c.take<const void*>(chunk);
-  w.tags = c.take<uint64_t>(chunk);
+  w.xptrs = c.take<const void*>(nt);
+  w.tags = c.take<uint64_t>(nt);
   const int64_t n = d.flash ? d.ell_pad : d.n_pad;
-  w.G = c.take<float>(static_cast<size_t>(chunk) * n * n);
-  w.V = c.take<float>(static_cast<size_t>(chunk) * n * n);
-  w.J = c.take<float>(static_cast<size_t>(chunk) * (n / 64) * 64 * 64);
-  w.active = c.take<int>(static_cast<size_t>(chunk) * (n / 64));
-  w.rot = c.take<int>(chunk);
-  w.tauabs = c.take<float>(chunk);
-  w.offp = c.take<double>(static_cast<size_t>(chunk) * kOffBlocks * 2);
-  w.GDpart = c.take<float>(static_cast<size_t>(chunk) * gram_d_ksplit(d) * d.D * d.D);
-  w.syevD = c.take<char>(syev_top_work_bytes(d.D, static_cast<int>(d.D), chunk));
-  w.syev = (!d.flash && d.R > 0)
-               ? static_cast<void*>(c.take<char>(syev_top_work_bytes(d.n_pad, static_cast<int>(d.R), chunk)))
-               : nullptr;
-  w.GD = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
-  w.GDc = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
-  w.VD = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
-  w.order = c.take<int>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
-  w.Ucm = c.take<float>(static_cast<size_t>(chunk) * d.T * R);
-  w.Vr = c.take<float>(static_cast<size_t>(chunk) * std::max(d.nT, d.D) * std::max<int64_t>(R, d.D));
-  w.P = c.take<float>(static_cast<size_t>(chunk) * R * d.HD);
-  w.lam_tmp = c.take<double>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
-  w.qtau = c.take<float>(householder_qr_work_floats(std::max(d.T, d.HD),
-                                                     std::max<int64_t>(std::max(R, d.ell), d.D), chunk));
-  w.perm = c.take<int>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
-  w.sgn = c.take<float>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
-  if (d.flash) {
-    w.Om = c.take<float>(static_cast<size_t>(chunk) * d.HD * d.ell);
-    w.Y = c.take<float>(static_cast<size_t>(chunk) * d.T * d.ell);
-    w.Z = c.take<float>(static_cast<size_t>(chunk) * d.HD * d.ell);
-    w.Bm = c.take<float>(static_cast<size_t>(chunk) * d.ell * d.HD);
-    w.Wr = c.take<float>(static_cast<size_t>(chunk) * d.ell * R);
+  auto scratch = [&](AllocWS& w) {
+    w.G = c.take<float>(static_cast<size_t>(chunk) * n * n);
+    w.V = c.take<float>(static_cast<size_t>(chunk) * n * n);
+    w.J = c.take<float>(static_cast<size_t>(chunk) * (n / 64) * 64 * 64);
+    w.active = c.take<int>(static_cast<size_t>(chunk) * (n / 64));
+    w.rot = c.take<int>(chunk);
+    w.tauabs = c.take<float>(chunk);
+    w.offp = c.take<double>(static_cast<size_t>(chunk) * kOffBlocks * 2);
+    w.GDpart = c.take<float>(static_cast<size_t>(chunk) * gram_d_ksplit(d) * d.D * d.D);
+    w.syevD = c.take<char>(syev_top_work_bytes(d.D, static_cast<int>(d.D), chunk));
+    w.syev = (!d.flash && d.R > 0)
+                 ? static_cast<void*>(c.take<char>(syev_top_work_bytes(d.n_pad, static_cast<int>(d.R), chunk)))
+                 : nullptr;
+    w.GD = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
+    w.GDc = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
+    w.VD = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
+    w.order = c.take<int>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
+    w.Ucm = c.take<float>(static_cast<size_t>(chunk) * d.T * R);
+    w.Vr = c.take<float>(static_cast<size_t>(chunk) * std::max(d.nT, d.D) * std::max<int64_t>(R, d.D));
+    w.P = c.take<float>(static_cast<size_t>(chunk) * R * d.HD);
+    w.lam_tmp = c.take<double>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
+    w.qtau = c.take<float>(householder_qr_work_floats(std::max(d.T, d.HD),
+                                                       std::max<int64_t>(std::max(R, d.ell), d.D), chunk));
+    w.perm = c.take<int>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
+    w.sgn = c.take<float>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
+    if (d.flash) {
+      w.Om = c.take<float>(static_cast<size_t>(chunk) * d.HD * d.ell);
+      w.Y = c.take<float>(static_cast<size_t>(chunk) * d.T * d.ell);
+      w.Z = c.take<float>(static_cast<size_t>(chunk) * d.HD * d.ell);
+      w.Bm = c.take<float>(static_cast<size_t>(chunk) * d.ell * d.HD);
+      w.Wr = c.take<float>(static_cast<size_t>(chunk) * d.ell * R);
+    }
+    w.Wd = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
+    w.qtauD = c.take<float>(householder_qr_work_floats(d.D, d.D, chunk));
+    w.lamDt = c.take<double>(static_cast<size_t>(chunk) * d.D);
+    w.permD = c.take<int>(static_cast<size_t>(chunk) * d.D);
+    w.sgnD = c.take<float>(static_cast<size_t>(chunk) * d.D);
+  };
+  scratch(w);
+  if (nlanes > 1) {
+    AllocWS w1 = w;
+    scratch(w1);
+    if (lane1) *lane1 = w1;
   }
-  w.Wd = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
-  w.qtauD = c.take<float>(householder_qr_work_floats(d.D, d.D, chunk));
-  w.lamDt = c.take<double>(static_cast<size_t>(chunk) * d.D);
-  w.permD = c.take<int>(static_cast<size_t>(chunk) * d.D);
-  w.sgnD = c.take<float>(static_cast<size_t>(chunk) * d.D);
   w.bytes = c.off;
+  if (lane1) lane1->bytes = c.off;
   return w;
 }
 
@@ -615,6 +638,34 @@ AuxStream& aux_stream() {
     ck(hipEventCreateWithFlags(&a.join, hipEventDisableTiming));
   }
   return a;
+}
+// The second lane's stream (non-blocking, default priority) and its fork / join events.
+AuxStream& lane_stream() {
+  static std::vector<AuxStream> per_dev;
+  int dev = 0;
+  ck(hipGetDevice(&dev));
+  if (static_cast<int>(per_dev.size()) <= dev) per_dev.resize(dev + 1);
+  AuxStream& a = per_dev[dev];
+  if (!a.s) {
+    ck(hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking));
+    ck(hipEventCreateWithFlags(&a.fork, hipEventDisableTiming));
+    ck(hipEventCreateWithFlags(&a.join, hipEventDisableTiming));
+  }
+  return a;
+}
+// Events marking each chunk's band reduction (grown on demand, kept per device).
+hipEvent_t* lane_marks(int count) {
+  static std::vector<std::vector<hipEvent_t>> per_dev;
+  int dev = 0;
+  ck(hipGetDevice(&dev));
+  if (static_cast<int>(per_dev.size()) <= dev) per_dev.resize(dev + 1);
+  std::vector<hipEvent_t>& v = per_dev[dev];
+  while (static_cast<int>(v.size()) < count) {
+    hipEvent_t e;
+    ck(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    v.push_back(e);
+  }
+  return v.data();
 }
 // Runs the feature-mode factor on the auxiliary stream after the work queued
 // on s so far (the tridiagonal path; the Jacobi path shares scratch and stays
@@ -731,7 +782,7 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     }
     VR = w.Vr; ldv = HD; vr_batch = HD * R;
   } else {
-    ck(syev_top(w.G, n, batch, static_cast<int>(R), w.V, nullptr, w.syev, s));
+    ck(syev_top(w.G, n, batch, static_cast<int>(R), w.V, nullptr, w.syev, s, w.band_done));
     VR = w.V; ldv = n; vr_batch = n * n;
   }
   if (in_ucm) {
@@ -1045,30 +1096,54 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, v
   const int nt = 2 * req->n_layers;
   for (int i = 0; i < nt; ++i)
     if (!x_dev[i]) return JOLT_EINVAL;
-  AllocWS w = carve_alloc(req, ws_dev);
+  AllocWS w1{};
+  AllocWS w = carve_alloc(req, ws_dev, &w1);
   if (ws_bytes < w.bytes) return JOLT_ENOSPACE;
   w.x16 = true;
   for (int i = 0; i < nt; ++i) w.x16 = w.x16 && (reinterpret_cast<uintptr_t>(x_dev[i]) & 15) == 0;
+  w1.x16 = w.x16;
   return guard([&]() -> jolt_status {
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Dims d = dims_of(req);
     const int xdt = req->shape.dtype == JOLT_BF16 ? kBF16 : kF32;
     const int64_t N = d.H * d.T * d.D;
     ck(hipMemsetAsync(w.frob2, 0, sizeof(double) * nt, s));
-    for (int t0 = 0; t0 < nt; t0 += w.chunk) {
+    // every tensor's pointer and sketch tag, uploaded once
+    std::vector<const void*> ptrs(x_dev, x_dev + nt);
+    std::vector<uint64_t> tags(nt);
+    for (int t = 0; t < nt; ++t)
+      tags[t] = kTagSketch ^ ((static_cast<uint64_t>(t / 2) << 8) | static_cast<uint64_t>(t % 2));
+    ck(hipMemcpyAsync(w.xptrs, ptrs.data(), sizeof(void*) * nt, hipMemcpyHostToDevice, s));
+    ck(hipMemcpyAsync(w.tags, tags.data(), sizeof(uint64_t) * nt, hipMemcpyHostToDevice, s));
+    ck(hipStreamSynchronize(s));
+    // chunks alternate between the lanes: lane 0 on s, lane 1 on a second
+    // stream forked from s and joined back into it
+    AuxStream* ls = nullptr;
+    if (w.nlanes > 1 && nt > w.chunk) {
+      ls = &lane_stream();
+      ck(hipEventRecord(ls->fork, s));
+      ck(hipStreamWaitEvent(ls->s, ls->fork, 0));
+    }
+    // a chunk on the second lane starts once the previous chunk's band
+    // reduction is queued ahead of it, so that chunk's chase (one CU per
+    // tensor) runs beside this chunk's matrix-core stages
+    hipEvent_t* marks = ls ? lane_marks(nt / w.chunk + 1) : nullptr;
+    for (int t0 = 0, c = 0; t0 < nt; t0 += w.chunk, ++c) {
       const int batch = std::min(w.chunk, nt - t0);
-      std::vector<const void*> ptrs(x_dev + t0, x_dev + t0 + batch);
-      std::vector<uint64_t> tags(batch);
-      for (int i = 0; i < batch; ++i) {
-        const int t = t0 + i;
-        tags[i] = kTagSketch ^ ((static_cast<uint64_t>(t / 2) << 8) | static_cast<uint64_t>(t % 2));
-      }
-      ck(hipMemcpyAsync(w.xptrs, ptrs.data(), sizeof(void*) * batch, hipMemcpyHostToDevice, s));
-      ck(hipMemcpyAsync(w.tags, tags.data(), sizeof(uint64_t) * batch, hipMemcpyHostToDevice, s));
-      ck(hipStreamSynchronize(s));
-      ck(launch_sumsq(reinterpret_cast<const void* const*>(w.xptrs), batch, N, xdt, w.frob2 + t0, s));
-      if (d.flash) analyze_flash(d, batch, t0, w, xdt, req->power_iters, req->seed, s);
-      else analyze_exact(d, batch, t0, w, xdt, s);
+      const bool second = ls && (c & 1);
+      AllocWS wl = second ? w1 : w;
+      hipStream_t sl = second ? ls->s : s;
+      wl.xptrs = w.xptrs + t0;
+      wl.tags = w.tags + t0;
+      wl.band_done = marks ? marks[c] : nullptr;
+      if (marks && c > 0) ck(hipStreamWaitEvent(sl, marks[c - 1], 0));
+      ck(launch_sumsq(reinterpret_cast<const void* const*>(wl.xptrs), batch, N, xdt, w.frob2 + t0, sl));
+      if (d.flash) analyze_flash(d, batch, t0, wl, xdt, req->power_iters, req->seed, sl);
+      else analyze_exact(d, batch, t0, wl, xdt, sl);
+    }
+    if (ls) {
+      ck(hipEventRecord(ls->join, ls->s));
+      ck(hipStreamWaitEvent(s, ls->join, 0));
     }
     const int R = static_cast<int>(d.R);
     std::vector<double> lt(static_cast<size_t>(nt) * std::max(R, 1)), ld(static_cast<size_t>(nt) * d.D), f2(nt);

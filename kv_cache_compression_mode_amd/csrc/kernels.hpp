@@ -113,7 +113,9 @@ size_t panel_factor_scratch_floats(int64_t m, int batch);
 // columns (column-major, ld n), eigenvalue-descending; lam (optional, fp64
 // [batch][R]) the eigenvalues.  work: syev_top_work_bytes(n, R, batch).
 size_t syev_top_work_bytes(int64_t n, int R, int batch);
-hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam, void* work, hipStream_t s);
+// band_done, when given, is recorded on s once the band reduction is queued
+hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam, void* work, hipStream_t s,
+                    hipEvent_t band_done = nullptr);
 hipError_t copy_cols(const float* in, int64_t ld_in, int64_t in_batch, float* out, int64_t ld_out,
                      int64_t out_batch, int64_t rows, int64_t cols, int batch, hipStream_t s);
 // write_r: when the panel fits one block (m - c0 <= panel_block_rows()), R

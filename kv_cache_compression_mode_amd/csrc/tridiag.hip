@@ -1127,7 +1127,7 @@ int ksplit_for(int64_t K) {
 size_t syev_top_work_bytes(int64_t n, int R, int batch) { return syev_layout(n, R, batch).total; }
 
 hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam_out, void* work,
-                    hipStream_t s) {
+                    hipStream_t s, hipEvent_t band_done) {
   if (n % SBW != 0 || n > 32768 || R < 1 || R > n) return hipErrorInvalidValue;
   const SyevLayout Lw = syev_layout(n, R, batch);
   char* wb = static_cast<char*>(work);
@@ -1221,6 +1221,7 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   }
+  if (band_done && (e = hipEventRecord(band_done, s)) != hipSuccess) return e;
   // ---- stage 2: band -> tridiagonal
   {
     int64_t blocks = (n * BWS + 255) / 256;
