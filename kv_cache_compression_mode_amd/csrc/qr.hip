@@ -377,6 +377,127 @@ __global__ __launch_bounds__(LT) void k_qr_block(const float* A, int64_t m, int6
   }
 }
 
+constexpr int RT = kLeaf / 2, RW = RT / 64;
+struct QrRegLds {
+  float xs[kLeaf] __attribute__((aligned(16)));   // column j, rows > j
+  float rowj[2][32];                              // row j, by the parity of j
+  float red[RW][32];
+  float St[32][33];                               // St[j][l] = v_l^T v_j (l < j)
+  float Tl[32][33];
+  float Rl[32][33];                               // rows of R
+  float tau_s[32], sgn[32];
+};
+
+// The column loop of the register panel QR below on the thread's column
+// c = t & 31, rows 64 (t >> 5) .. + 63 in p (mr rows, nb columns); leaves
+// column c's unscaled x below the diagonal in p and returns its scale, R in
+// L.Rl, v_l^T v_j in L.St, tau and sign(beta) in L.tau_s / L.sgn, and T in
+// L.Tl (rows written by threads t < 32; visible after a barrier).
+__device__ float qr_reg_factor(float (&p)[64], int mr, int nb, QrRegLds& L) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int c = t & 31, g = t >> 5, rb = 64 * g;
+  const bool live = 128 * wave < mr;
+  if (!live && lane < 32) L.red[wave][c] = 0.f;                  // waves past the panel add nothing
+  float vscale = 0.f;                                          // scale of this column's reflector
+#pragma clang loop unroll(disable)
+  for (int j = 0; j < nb; ++j) {
+    const int par = j & 1;
+    if (c == j) {                                              // publish column j
+#pragma unroll
+      for (int r = 0; r < 64; r += 4)
+        *reinterpret_cast<float4*>(&L.xs[rb + r]) = make_float4(p[r], p[r + 1], p[r + 2], p[r + 3]);
+    }
+    // rows <= j of x are zero: written by lanes 0 .. j of wave 0 after the
+    // publishing lane j of the same wave (one wave's LDS writes land in order)
+    if (t <= j) L.xs[t] = 0.f;
+    if (g == 0) {                                              // publish row j (row block 0)
+      float a[16];                                             // p[j] by the bits of j (j < 32)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {               // values first: a select of two loads keeps p in registers
+        const float lo = p[2 * q], hi = p[2 * q + 1];
+        a[q] = (j & 1) ? hi : lo;
+      }
+#pragma unroll
+      for (int w = 2, n2 = 8; n2 >= 1; w <<= 1, n2 >>= 1) {
+#pragma unroll
+        for (int q = 0; q < n2; ++q) {
+          const float lo = a[2 * q], hi = a[2 * q + 1];
+          a[q] = (j & w) ? hi : lo;
+        }
+      }
+      L.rowj[par][c] = a[0];
+    }
+    __syncthreads();
+    float x[64];
+    if (live) {
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+      for (int r = 0; r < 64; r += 4) {
+        const float4 q = *reinterpret_cast<const float4*>(&L.xs[rb + r]);
+        x[r] = q.x; x[r + 1] = q.y; x[r + 2] = q.z; x[r + 3] = q.w;
+        s0 += q.x * p[r];
+        s1 += q.y * p[r + 1];
+        s2 += q.z * p[r + 2];
+        s3 += q.w * p[r + 3];
+      }
+      float part = (s0 + s1) + (s2 + s3);
+      part += __shfl_xor(part, 32);
+      if (lane < 32) L.red[wave][c] = part;
+    }
+    __syncthreads();
+    float raw = 0.f, sigma = 0.f;
+#pragma unroll
+    for (int w = 0; w < RW; ++w) {
+      raw += L.red[w][c];
+      sigma += L.red[w][j];
+    }
+    const float alpha = L.rowj[par][j];
+    float tau = 0.f, beta = alpha, scale = 0.f;
+    if (sigma > 0.f) {
+      const float nrm = sqrtf(alpha * alpha + sigma);
+      beta = alpha >= 0.f ? -nrm : nrm;
+      tau = (beta - alpha) / beta;
+      scale = 1.f / (alpha - beta);
+    }
+    const float d = L.rowj[par][c] + scale * raw;                // v^T P[:, c]
+    if (c == j) vscale = scale;
+    // rows > j right of j: P -= x (scale tau d)
+    const float e = c > j ? scale * tau * d : 0.f;
+    if (live) {
+#pragma unroll
+      for (int r = 0; r < 64; ++r) p[r] -= x[r] * e;
+    }
+    // Row j is final after this step and only R reads it: it goes to LDS,
+    // its registers keep a stale value that later steps multiply by x = 0.
+    if (g == 0) {
+      L.Rl[j][c] = c == j ? beta : (c > j ? L.rowj[par][c] - tau * d : 0.f);
+      if (c < j) L.St[j][c] = vscale * d;
+      if (c == j) {
+        L.tau_s[j] = tau;
+        L.sgn[j] = beta < 0.f ? -1.f : 1.f;
+      }
+    }
+  }
+  __syncthreads();
+  if (t < 32) {                                                // row t of T, in registers
+    float tr[32];                                              // tr[l] = 0 for l < t
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      float u0 = 0.f, u1 = 0.f;
+#pragma unroll
+      for (int l = 0; l + 1 < j; l += 2) {
+        u0 += tr[l] * L.St[j][l];
+        u1 += tr[l + 1] * L.St[j][l + 1];
+      }
+      if (j & 1) u0 += tr[j - 1] * L.St[j][j - 1];
+      const float tj = L.tau_s[j];
+      tr[j] = (j >= nb || j < t) ? 0.f : (j == t ? tj : -tj * (u0 + u1));
+      L.Tl[t][j] = tr[j];
+    }
+  }
+  return vscale;
+}
+
 // Householder QR of one panel (mp = m - c0 <= kLeaf rows, nb <= 32 columns)
 // in registers: thread t holds column c = t & 31, rows 64 g .. 64 g + 63 with
 // g = t >> 5, so a wave holds 128 rows of all 32 columns.  Column j: the
@@ -392,22 +513,14 @@ __global__ __launch_bounds__(LT) void k_qr_block(const float* A, int64_t m, int6
 // recurrence, T[t][j] = -tau_j sum_{t <= l < j} T[t][l] (v_l^T v_j), T[j][j]
 // = tau_j.  Outputs are those of k_qr_block mode 0, plus (write_r) R in the
 // panel's top rows.
-constexpr int RT = kLeaf / 2, RW = RT / 64;
 __global__ __launch_bounds__(RT) void k_qr_reg(float* A, int64_t m, int64_t ld, int64_t bstride, int64_t c0,
                                                int nb, float* Vp, int64_t vstride, float* Tp, int64_t tstride,
                                                float* taus_g, int64_t k, int write_r) {
-  __shared__ __attribute__((aligned(16))) float xs[kLeaf];     // column j, rows > j
-  __shared__ float rowj[2][32];                                // row j, by the parity of j
-  __shared__ float red[RW][32];
-  __shared__ float St[32][33];                                 // St[j][l] = v_l^T v_j (l < j)
-  __shared__ float Tl[32][33];
-  __shared__ float Rl[32][33];                                 // rows of R
-  __shared__ float tau_s[32], sgn[32];
+  __shared__ QrRegLds L;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int c = t & 31, g = t >> 5, rb = 64 * g;               // column, first row
   const int64_t z = blockIdx.y;
   const int mr = static_cast<int>(m - c0);
-  const bool live = 128 * wave < mr;                           // this wave holds rows of the panel
   float* Az = A + z * bstride;
   // The panel (columns c0.., rows c0.., column stride ld) through a buffer
   // resource; offsets of rows past the panel or columns past nb start at 2^31
@@ -436,104 +549,7 @@ __global__ __launch_bounds__(RT) void k_qr_reg(float* A, int64_t m, int64_t ld, 
 #pragma unroll
     for (int r = 0; r < 64; ++r) p[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pr, off(r), 0, 0));
   }
-  if (!live && lane < 32) red[wave][c] = 0.f;                  // waves past the panel add nothing
-  float vscale = 0.f;                                          // scale of this column's reflector
-#pragma clang loop unroll(disable)
-  for (int j = 0; j < nb; ++j) {
-    const int par = j & 1;
-    if (c == j) {                                              // publish column j
-#pragma unroll
-      for (int r = 0; r < 64; r += 4)
-        *reinterpret_cast<float4*>(&xs[rb + r]) = make_float4(p[r], p[r + 1], p[r + 2], p[r + 3]);
-    }
-    // rows <= j of x are zero: written by lanes 0 .. j of wave 0 after the
-    // publishing lane j of the same wave (one wave's LDS writes land in order)
-    if (t <= j) xs[t] = 0.f;
-    if (g == 0) {                                              // publish row j (row block 0)
-      float a[16];                                             // p[j] by the bits of j (j < 32)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {               // values first: a select of two loads keeps p in registers
-        const float lo = p[2 * q], hi = p[2 * q + 1];
-        a[q] = (j & 1) ? hi : lo;
-      }
-#pragma unroll
-      for (int w = 2, n2 = 8; n2 >= 1; w <<= 1, n2 >>= 1) {
-#pragma unroll
-        for (int q = 0; q < n2; ++q) {
-          const float lo = a[2 * q], hi = a[2 * q + 1];
-          a[q] = (j & w) ? hi : lo;
-        }
-      }
-      rowj[par][c] = a[0];
-    }
-    __syncthreads();
-    float x[64];
-    if (live) {
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-      for (int r = 0; r < 64; r += 4) {
-        const float4 q = *reinterpret_cast<const float4*>(&xs[rb + r]);
-        x[r] = q.x; x[r + 1] = q.y; x[r + 2] = q.z; x[r + 3] = q.w;
-        s0 += q.x * p[r];
-        s1 += q.y * p[r + 1];
-        s2 += q.z * p[r + 2];
-        s3 += q.w * p[r + 3];
-      }
-      float part = (s0 + s1) + (s2 + s3);
-      part += __shfl_xor(part, 32);
-      if (lane < 32) red[wave][c] = part;
-    }
-    __syncthreads();
-    float raw = 0.f, sigma = 0.f;
-#pragma unroll
-    for (int w = 0; w < RW; ++w) {
-      raw += red[w][c];
-      sigma += red[w][j];
-    }
-    const float alpha = rowj[par][j];
-    float tau = 0.f, beta = alpha, scale = 0.f;
-    if (sigma > 0.f) {
-      const float nrm = sqrtf(alpha * alpha + sigma);
-      beta = alpha >= 0.f ? -nrm : nrm;
-      tau = (beta - alpha) / beta;
-      scale = 1.f / (alpha - beta);
-    }
-    const float d = rowj[par][c] + scale * raw;                // v^T P[:, c]
-    if (c == j) vscale = scale;
-    // rows > j right of j: P -= x (scale tau d)
-    const float e = c > j ? scale * tau * d : 0.f;
-    if (live) {
-#pragma unroll
-      for (int r = 0; r < 64; ++r) p[r] -= x[r] * e;
-    }
-    // Row j is final after this step and only R reads it: it goes to LDS,
-    // its registers keep a stale value that later steps multiply by x = 0.
-    if (g == 0) {
-      Rl[j][c] = c == j ? beta : (c > j ? rowj[par][c] - tau * d : 0.f);
-      if (c < j) St[j][c] = vscale * d;
-      if (c == j) {
-        tau_s[j] = tau;
-        sgn[j] = beta < 0.f ? -1.f : 1.f;
-      }
-    }
-  }
-  __syncthreads();
-  if (t < 32) {                                                // row t of T, in registers
-    float tr[32];                                              // tr[l] = 0 for l < t
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      float u0 = 0.f, u1 = 0.f;
-#pragma unroll
-      for (int l = 0; l + 1 < j; l += 2) {
-        u0 += tr[l] * St[j][l];
-        u1 += tr[l + 1] * St[j][l + 1];
-      }
-      if (j & 1) u0 += tr[j - 1] * St[j][j - 1];
-      const float tj = tau_s[j];
-      tr[j] = (j >= nb || j < t) ? 0.f : (j == t ? tj : -tj * (u0 + u1));
-      Tl[t][j] = tr[j];
-    }
-  }
+  const float vscale = qr_reg_factor(p, mr, nb, L);
   // V (explicit, zero above row c0, unit diagonal), tau / sign(beta)
   float* V = Vp + z * vstride;
   for (int64_t r = t; r < c0; r += RT)
@@ -561,17 +577,115 @@ __global__ __launch_bounds__(RT) void k_qr_reg(float* A, int64_t m, int64_t ld, 
                                             static_cast<int>(rb + r < mr ? vb + 4u * r : kOff), 0, 0);
   }
   if (t < nb) {
-    taus_g[z * 2 * k + c0 + t] = tau_s[t];
-    taus_g[z * 2 * k + k + c0 + t] = sgn[t];
+    taus_g[z * 2 * k + c0 + t] = L.tau_s[t];
+    taus_g[z * 2 * k + k + c0 + t] = L.sgn[t];
   }
   if (write_r && g == 0) {                                     // R: rows <= c of row block 0
 #pragma unroll
     for (int r = 0; r < 32; ++r)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Rl[r][c]), pr, r <= c && r < nb ? off(r) : static_cast<int>(kOff),
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(L.Rl[r][c]), pr, r <= c && r < nb ? off(r) : static_cast<int>(kOff),
                                             0, 0);
   }
   __syncthreads();
-  for (int idx = t; idx < 1024; idx += RT) Tp[z * tstride + idx] = Tl[idx >> 5][idx & 31];
+  for (int idx = t; idx < 1024; idx += RT) Tp[z * tstride + idx] = L.Tl[idx >> 5][idx & 31];
+}
+
+// TSQR leaves and top level in registers, the factorization of k_qr_reg
+// followed by the explicit Q = E - V (T V_1^T) (V_1: the first 32 rows of
+// V).  Mode 1: leaf blockIdx.x (rows row0 .. row0 + rl of the panel) ->
+// Q_i into Qb (column-major, leading dimension m - c0) and R_i into rows
+// 32 i .. 32 i + 31 of the stack Rs (row-major, zero below the diagonal).
+// Mode 2: the stack (nl * 32 rows, row-major) -> Q_top into Qt (row-major,
+// 32 wide), column j times sign(beta_j) so that diag(R) >= 0.  Q's rows
+// are formed on the fp32 matrix cores, each wave transposing its own rows
+// of V through a private LDS tile, 64 rows at a time.
+__global__ __launch_bounds__(RT) void k_qr_leaf(const float* A, int64_t m, int64_t ld, int64_t bstride,
+                                                int64_t c0, int nb, int mode, int nl, int64_t rl, float* Qb,
+                                                float* Rs, float* Qt, int64_t aux_stride) {
+  __shared__ QrRegLds L;
+  __shared__ float Ms[32][33];                                 // M = T V_1^T
+  extern __shared__ float leaf_vw[];                           // [RW][64][33]: per-wave V rows
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, rl32 = lane & 31, hf = lane >> 5;
+  const int c = t & 31, g = t >> 5, rb = 64 * g;
+  const int64_t z = blockIdx.y;
+  const int64_t mp = m - c0;
+  const int64_t row0 = mode == 1 ? blockIdx.x * rl : 0;
+  const int mr = mode == 1 ? static_cast<int>(mp - row0 < rl ? mp - row0 : rl) : nl * 32;
+  float p[64];
+  if (mode == 1) {
+    const float* a = A + z * bstride + (c0 + c) * ld + c0 + row0;
+#pragma unroll
+    for (int r = 0; r < 64; ++r) p[r] = (c < nb && rb + r < mr) ? a[rb + r] : 0.f;
+  } else {
+    const float* rs = Rs + z * kStack;
+#pragma unroll
+    for (int r = 0; r < 64; ++r) p[r] = (c < nb && rb + r < mr) ? rs[(rb + r) * 32 + c] : 0.f;
+  }
+  const float vscale = qr_reg_factor(p, mr, nb, L);
+  auto vval = [&](int r) -> float {                            // V at row rb + r, column c
+    const int i = rb + r;
+    return (c >= nb || i < c) ? 0.f : (i == c ? 1.f : vscale * p[r]);
+  };
+  __syncthreads();                                             // T complete
+  if (g == 0) {
+#pragma unroll
+    for (int r = 0; r < 32; ++r) L.St[r][c] = vval(r);         // V_1 (St is free after T)
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {                                // M[a][b] = sum_k T[a][k] V_1[b][k]
+    const int e = t + RT * q, a = e >> 5, b = e & 31;
+    float u = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) u += L.Tl[a][kk] * L.St[b][kk];
+    Ms[a][b] = u;
+  }
+  if (mode == 1) {                                             // R_i into the stack
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = t + RT * q, a = e >> 5, b = e & 31;
+      Rs[z * kStack + (blockIdx.x * 32 + a) * 32 + b] = (a < nb && b < nb && a <= b) ? L.Rl[a][b] : 0.f;
+    }
+  }
+  __syncthreads();
+  if (128 * wave >= mr) return;                                // no rows of the panel in this wave
+  float* vw = leaf_vw + wave * 64 * 33;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int base = 128 * wave + 64 * h2;                     // this round's rows
+    if (hf == h2) {
+#pragma unroll
+      for (int r = 0; r < 64; ++r) vw[r * 33 + c] = vval(r);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int kk = 0; kk < 32; kk += 2) {
+        const int k = kk + hf;
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(vw[(32 * blk + rl32) * 33 + k], Ms[k][rl32], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int i = base + 32 * blk + (e >> 2) * 8 + hf * 4 + (e & 3);
+        if (i < mr) {
+          const float qv = (i == rl32 ? 1.f : 0.f) - acc[e];
+          if (mode == 1) {
+            Qb[z * aux_stride + static_cast<int64_t>(rl32) * mp + row0 + i] = qv;
+          } else {
+            const float sg = rl32 < nb ? L.sgn[rl32] : 1.f;   // beta_c = R_cc: flip so diag(R) >= 0
+            Qt[z * kStack + static_cast<int64_t>(i) * 32 + rl32] = sg * qv;
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 }
 
 constexpr int kQrSplit = 16;     // row chunks of a tall block-reflector application
@@ -992,9 +1106,12 @@ hipError_t panel_factor(float* A, int64_t m, int64_t ld, int64_t bstride, int64_
                         float* scratch, hipStream_t s, int write_r) {
   static bool lds_attr = false;
   if (!lds_attr) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_qr_block),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(32 * kLeaf * sizeof(float)));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_qr_block),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(32 * kLeaf * sizeof(float)));
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_qr_leaf), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(RW * 64 * 33 * sizeof(float)));
     if (e != hipSuccess) return e;
     lds_attr = true;
   }
@@ -1011,12 +1128,13 @@ hipError_t panel_factor(float* A, int64_t m, int64_t ld, int64_t bstride, int64_
     k_qr_reg<<<dim3(1, batch), RT, 0, s>>>(A, m, ld, bstride, c0, nb, Vp, vstride, Tp, tstride, taus, k, write_r);
   } else if (nl <= 32) {
     const int64_t rl = (mp + nl - 1) / nl;
-    k_qr_block<<<dim3(static_cast<unsigned>(nl), batch), LT, lds, s>>>(
-        A, m, ld, bstride, c0, nb, 1, static_cast<int>(nl), rl, Vp, vstride, Tp, tstride, taus, k, Qb, Rs, Qt,
-        m * 32);
+    const size_t vw_lds = static_cast<size_t>(RW) * 64 * 33 * sizeof(float);
+    k_qr_leaf<<<dim3(static_cast<unsigned>(nl), batch), RT, vw_lds, s>>>(A, m, ld, bstride, c0, nb, 1,
+                                                                         static_cast<int>(nl), rl, Qb, Rs, Qt,
+                                                                         m * 32);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    k_qr_block<<<dim3(1, batch), LT, lds, s>>>(A, m, ld, bstride, c0, nb, 2, static_cast<int>(nl), rl, Vp,
-                                               vstride, Tp, tstride, taus, k, Qb, Rs, Qt, m * 32);
+    k_qr_leaf<<<dim3(1, batch), RT, vw_lds, s>>>(A, m, ld, bstride, c0, nb, 2, static_cast<int>(nl), rl, Qb, Rs,
+                                                 Qt, m * 32);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     k_hr_lu<<<batch, LT, 0, s>>>(m, c0, nb, Qb, Qt, m * 32, Tp, tstride, taus, k, UL);
     if ((e = hipGetLastError()) != hipSuccess) return e;
