@@ -162,10 +162,11 @@ __global__ __launch_bounds__(QT) void k_hqr_panel(float* A, int64_t m, int64_t k
   }
 }
 
-// ---- LDS-resident panels and tall-skinny QR (TSQR) with Householder
+// ---- Register panels and tall-skinny QR (TSQR) with Householder
 // reconstruction.  A panel block of up to kLeaf rows x 32 columns lives in
-// LDS (128 KB) and is factored there with one row per thread.  Taller panels
-// are split into row leaves factored independently; their stacked R factors
+// the registers of one workgroup (64 rows of one column per thread) and is
+// factored there.  Taller panels are split into row leaves factored
+// independently; their stacked R factors
 // are factored once more (the TSQR tree), the panel's orthonormal factor is
 // assembled as diag(Q_i) Q_top, and the compact-WY form I - V T V^T of the
 // panel is recovered from it by a sign-chosen LU of Q - S (Ballard, Demmel,
@@ -173,209 +174,9 @@ __global__ __launch_bounds__(QT) void k_hqr_panel(float* A, int64_t m, int64_t k
 // tall-skinny QR", 2015): V = L, T = -U S L_1^{-T}, and the Householder R is
 // S R, so sign(beta_j) = s_j when diag(R) >= 0.  The blocked updates that
 // follow use V and T exactly as for a panel factored in place.
-constexpr int kLeaf = 1024;      // rows of one LDS block (one per thread)
-constexpr int LT = 1024;         // threads of the LDS kernels
-constexpr int LW = LT / 64;      // waves
+constexpr int kLeaf = 1024;      // rows of one register panel
+constexpr int LT = 1024;         // threads of the reconstruction's LU kernel
 constexpr int kStack = 32 * 32 * 32;   // per matrix: up to 32 leaves x 32 rows x 32 (Rs, Qt)
-
-// Wave sums of 32 per-lane values at once (a halving butterfly): lane l ends
-// with the total of value l >> 1.  The values travel as one 32-wide vector:
-// with a plain array the compiler turns the two-way pick of each stage into
-// an indexed access, which it then expands into compare/select ladders.
-typedef float f32x32 __attribute__((ext_vector_type(32)));
-__device__ __forceinline__ float reduce32(f32x32 v, int lane) {
-#pragma unroll
-  for (int cnt = 32, off = 32; cnt > 1; cnt >>= 1, off >>= 1) {
-    const int h = cnt >> 1;
-    const bool up = (lane & off) != 0;
-#pragma unroll
-    for (int q = 0; q < h; ++q) {
-      const float lo = v[q], hi = v[q + h];
-      const float send = up ? lo : hi;
-      const float keep = up ? hi : lo;
-      v[q] = keep + __shfl_xor(send, off);
-    }
-  }
-  return v[0] + __shfl_xor(v[0], 1);
-}
-
-struct LdsQr {
-  float Ts[32][33];    // compact-WY T
-  float Mt[32][33];    // T V_1^T (explicit Q)
-  float red[LW][32];
-  float dots[32];
-  float sgn[32];
-  float bc;
-};
-
-// Householder QR of the mr x nb block P (column-major, column stride kLeaf,
-// mr <= kLeaf, nb <= 32), one row per thread.  On return the upper triangle
-// holds R (beta_j on the diagonal), the strict lower part the vectors v_j
-// (unit leading entry implied), L.Ts the factor T with I - V T V^T =
-// H_0 ... H_{nb-1}, L.sgn[j] = sign(beta_j).  Per column: the norm below the
-// diagonal, then one fused pass of dot products of v_j with every other
-// column: against later columns they drive the update, against earlier
-// reflectors they give column j of T (T[0:j, j] = -tau_j T[0:j, 0:j] V^T v_j).
-__device__ void lds_householder(float* P, int mr, int nb, LdsQr& L) {
-  const int i = threadIdx.x, lane = i & 63, wave = i >> 6;
-  for (int j = 0; j < nb; ++j) {
-    // one reduction per column: slot c != j gets sum_{i > j} P[c][i] x_i, slot j
-    // gets sigma = sum_{i > j} x_i^2 (x = column j below the diagonal)
-    const float x = (i > j && i < mr) ? P[j * kLeaf + i] : 0.f;
-    f32x32 part;
-#pragma unroll
-    for (int c = 0; c < 32; ++c)
-      part[c] = (c < nb && i > j && i < mr) ? (c == j ? x : P[c * kLeaf + i]) * x : 0.f;
-    const float tot = reduce32(part, lane);
-    if ((lane & 1) == 0) L.red[wave][lane >> 1] = tot;
-    __syncthreads();
-    float sigma = 0.f;
-    for (int w = 0; w < LW; ++w) sigma += L.red[w][j];
-    const float alpha = P[j * kLeaf + j];
-    float tau = 0.f, beta = alpha, scale = 0.f;
-    if (sigma > 0.f) {
-      const float nrm = sqrtf(alpha * alpha + sigma);
-      beta = alpha >= 0.f ? -nrm : nrm;
-      tau = (beta - alpha) / beta;
-      scale = 1.f / (alpha - beta);
-    }
-    // v_j = (1, x * scale); dots d_c = v_c^T v_j (c < j) or v_j^T P[c] (c > j)
-    if (i < 32) {
-      float t = 0.f;
-      for (int w = 0; w < LW; ++w) t += L.red[w][i];
-      L.dots[i] = (i < nb && i != j) ? P[i * kLeaf + j] + scale * t : 0.f;
-    }
-    __syncthreads();
-    const float v = (i == j) ? 1.f : (i > j && i < mr ? x * scale : 0.f);
-    if (i > j && i < mr) P[j * kLeaf + i] = v;
-    if (i == j) P[j * kLeaf + j] = beta;
-    if (tau != 0.f && i >= j && i < mr) {
-      for (int c = j + 1; c < nb; ++c) P[c * kLeaf + i] -= tau * v * L.dots[c];
-    }
-    if (i < 32) {
-      float t = 0.f;
-      if (i < j) {
-        for (int l = i; l < j; ++l) t += L.Ts[i][l] * L.dots[l];
-        t *= -tau;
-      } else if (i == j) {
-        t = tau;
-      }
-      L.Ts[i][j] = t;
-    }
-    if (i == 0) L.sgn[j] = beta < 0.f ? -1.f : 1.f;
-    __syncthreads();
-  }
-  for (int idx = i; idx < 32 * 32; idx += LT) {
-    const int r = idx / 32, c = idx % 32;
-    if (r >= nb || c >= nb) L.Ts[r][c] = 0.f;
-  }
-  __syncthreads();
-}
-
-// Row i of the explicit Q = (I - V T V^T)[:, :nb] of a factored block.
-__device__ void lds_explicit_q_row(const float* P, int nb, LdsQr& L, float (&q)[32]) {
-  const int i = threadIdx.x;
-  // Mt = T V_1^T (V_1: top nb rows, unit lower)
-  {
-    const int a = i / 32, c = i % 32;
-    float t = 0.f;
-    if (a < nb && c < nb) {
-      for (int b = a; b <= c && b < nb; ++b) {           // T upper, V_1[c][b] = 0 for b > c
-        const float vcb = (b == c) ? 1.f : P[b * kLeaf + c];
-        t += L.Ts[a][b] * vcb;
-      }
-    }
-    L.Mt[a][c] = t;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int c = 0; c < 32; ++c) q[c] = (i == c) ? 1.f : 0.f;
-  for (int a = 0; a < nb; ++a) {
-    const float via = (i == a) ? 1.f : (i > a ? P[a * kLeaf + i] : 0.f);
-    if (via != 0.f) {
-#pragma unroll
-      for (int c = 0; c < 32; ++c) q[c] -= via * L.Mt[a][c];
-    }
-  }
-}
-
-// mode 0: the whole panel (m - c0 <= kLeaf rows): explicit V (zero above
-//         row c0) -> Vp, T -> Tp, tau / sign(beta) -> taus.
-// mode 1: leaf blockIdx.x of a tall panel (nl leaves of rl rows): explicit
-//         Q_i -> Qb (column-major, (m - c0) x 32), R_i -> Rs rows 32 i ...
-// mode 2: the stacked R factors (nl * 32 rows) -> explicit Q_top -> Qt
-//         (row-major, 32 wide), columns signed so that diag(R) >= 0.
-__global__ __launch_bounds__(LT) void k_qr_block(const float* A, int64_t m, int64_t ld, int64_t bstride,
-                                                 int64_t c0, int nb, int mode, int nl, int64_t rl,
-                                                 float* Vp, int64_t vstride, float* Tp, int64_t tstride,
-                                                 float* taus_g, int64_t k, float* Qb, float* Rs, float* Qt,
-                                                 int64_t aux_stride) {
-  extern __shared__ float P[];                 // [32][kLeaf]
-  __shared__ LdsQr L;
-  const int i = threadIdx.x;
-  const int64_t z = blockIdx.y;
-  const int64_t mp = m - c0;
-  int64_t row0 = 0;
-  int mr;
-  if (mode == 0) {
-    mr = static_cast<int>(mp);
-  } else if (mode == 1) {
-    row0 = blockIdx.x * rl;
-    mr = static_cast<int>(mp - row0 < rl ? mp - row0 : rl);
-  } else {
-    mr = nl * 32;
-  }
-  for (int c = 0; c < 32; ++c) {
-    float v = 0.f;
-    if (c < nb && i < mr) {
-      if (mode == 2) v = Rs[z * kStack + static_cast<int64_t>(i) * 32 + c];
-      else v = A[z * bstride + (c0 + c) * ld + c0 + row0 + i];
-    }
-    P[c * kLeaf + i] = v;
-  }
-  __syncthreads();
-  lds_householder(P, mr, nb, L);
-  if (mode == 0) {
-    float* V = Vp + z * vstride;
-    for (int c = 0; c < 32; ++c) {
-      for (int64_t r = i; r < m; r += LT) {
-        float v = 0.f;
-        if (c < nb) {
-          const int64_t rr = r - c0;
-          v = rr < c ? 0.f : (rr == c ? 1.f : P[c * kLeaf + rr]);
-        }
-        V[c * m + r] = v;
-      }
-    }
-    Tp[z * tstride + i] = L.Ts[i / 32][i % 32];
-    if (i < nb) {
-      taus_g[z * 2 * k + c0 + i] = L.Ts[i][i];
-      taus_g[z * 2 * k + k + c0 + i] = L.sgn[i];
-    }
-    return;
-  }
-  float q[32];
-  lds_explicit_q_row(P, nb, L, q);
-  if (mode == 1) {
-    if (i < mr) {
-      float* qb = Qb + z * aux_stride;
-#pragma unroll
-      for (int c = 0; c < 32; ++c) qb[c * mp + row0 + i] = q[c];
-    }
-    // R_i: rows 32 * leaf .. +32 of the stack (zero below nb)
-    const int a = i / 32, c = i % 32;
-    Rs[z * kStack + (blockIdx.x * 32 + a) * 32 + c] = (a < nb && c < nb && a <= c) ? P[c * kLeaf + a] : 0.f;
-  } else {
-    if (i < mr) {
-      float* qt = Qt + z * kStack;
-#pragma unroll
-      for (int c = 0; c < 32; ++c) {
-        const float sg = c < nb ? L.sgn[c] : 1.f;     // beta_c = R_cc: flip so diag(R) >= 0
-        qt[static_cast<int64_t>(i) * 32 + c] = sg * q[c];
-      }
-    }
-  }
-}
 
 constexpr int RT = kLeaf / 2, RW = RT / 64;
 struct QrRegLds {
@@ -1106,11 +907,7 @@ hipError_t panel_factor(float* A, int64_t m, int64_t ld, int64_t bstride, int64_
                         float* scratch, hipStream_t s, int write_r) {
   static bool lds_attr = false;
   if (!lds_attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_qr_block),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(32 * kLeaf * sizeof(float)));
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_qr_leaf), hipFuncAttributeMaxDynamicSharedMemorySize,
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_qr_leaf), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(RW * 64 * 33 * sizeof(float)));
     if (e != hipSuccess) return e;
     lds_attr = true;
@@ -1122,7 +919,6 @@ hipError_t panel_factor(float* A, int64_t m, int64_t ld, int64_t bstride, int64_
   ProfScope ps("qr_panel", s);
   const int64_t mp = m - c0;
   const int64_t nl = (mp + kLeaf - 1) / kLeaf;
-  const size_t lds = 32 * kLeaf * sizeof(float);
   hipError_t e;
   if (nl <= 1) {
     k_qr_reg<<<dim3(1, batch), RT, 0, s>>>(A, m, ld, bstride, c0, nb, Vp, vstride, Tp, tstride, taus, k, write_r);
