@@ -578,10 +578,16 @@ __global__ __launch_bounds__(256) void k_wy_mid(int nc, int nch, const float* Wp
   const int tid = threadIdx.x;
   const int64_t z = blockIdx.y;
   const int j0 = 64 * blockIdx.x;
-  for (int idx = tid; idx < 1024; idx += 256) {
-    const float t = T_g[z * t_batch + idx];
-    if (trans) Ts[idx & 31][idx >> 5] = t;
-    else Ts[idx >> 5][idx & 31] = t;
+  {
+    float rt[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rt[q] = T_g[z * t_batch + tid + 256 * q];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q;
+      if (trans) Ts[idx & 31][idx >> 5] = rt[q];
+      else Ts[idx >> 5][idx & 31] = rt[q];
+    }
   }
   const float* wp = Wp + z * nch * 32 * static_cast<int64_t>(nc);
 #pragma unroll
@@ -723,15 +729,29 @@ __global__ __launch_bounds__(256) void k_hr_tall(int64_t m, int64_t c0, int nb, 
   const int64_t z = blockIdx.y;
   const int64_t g0 = blockIdx.x * 256ll;
   const int64_t mp = m - c0;
-  for (int idx = threadIdx.x; idx < 1024; idx += 256) U[idx / 32][idx % 32] = UL[z * 1024 + idx];
   const int64_t lo = g0 - c0 > 0 ? g0 - c0 : 0;
   const int64_t leaf0 = lo / rl;
-  for (int idx = threadIdx.x; idx < 2048; idx += 256) {
-    const int s = idx / 1024, a = (idx % 1024) / 32, c = idx % 32;
-    const int64_t leaf = leaf0 + s;
-    float v = 0.f;
-    if (leaf * rl < mp) v = Qt[z * kStack + (leaf * 32 + a) * 32 + c];
-    Qs[s][a][c] = v;
+  {
+    // every load in flight before the LDS writes
+    float ru[4], rq[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ru[q] = UL[z * 1024 + threadIdx.x + 256 * q];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int idx = threadIdx.x + 256 * q, s = idx / 1024, a = (idx % 1024) / 32, c = idx % 32;
+      const int64_t leaf = leaf0 + s;
+      rq[q] = leaf * rl < mp ? Qt[z * kStack + (leaf * 32 + a) * 32 + c] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = threadIdx.x + 256 * q;
+      U[idx / 32][idx % 32] = ru[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int idx = threadIdx.x + 256 * q, s = idx / 1024, a = (idx % 1024) / 32, c = idx % 32;
+      Qs[s][a][c] = rq[q];
+    }
   }
   __syncthreads();
   const int64_t g = g0 + threadIdx.x;

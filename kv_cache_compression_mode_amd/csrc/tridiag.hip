@@ -551,16 +551,28 @@ __global__ __launch_bounds__(64) void k_cb_tfac(const float* Rf_g, int64_t rf_st
   const int64_t z = blockIdx.y;
   const float* Rf = Rf_g + z * rf_stride;
   const int jg = G * SBW, last = n - 3;
-  for (int idx = lane; idx < CBR * (SBW + 1); idx += 64) (&Vs[0][0])[idx] = 0.f;
+  // every load in flight before the LDS writes; zeros off the staircase
+  float rv[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int idx = lane + 64 * q, i = idx / SBW, r = idx % SBW, j = jg + i;
+    rv[q] = (j <= last && s < sweep_steps(n, j)) ? Rf[(sweep_offset(n, j) + s) * RFS + r] : 0.f;
+  }
+  float tl = 0.f;
   if (lane < SBW) {
     const int j = jg + lane;
-    tau[lane] = (j <= last && s < sweep_steps(n, j)) ? Rf[(sweep_offset(n, j) + s) * RFS + SBW] : 0.f;
+    tl = (j <= last && s < sweep_steps(n, j)) ? Rf[(sweep_offset(n, j) + s) * RFS + SBW] : 0.f;
   }
-  __syncthreads();
-  for (int idx = lane; idx < SBW * SBW; idx += 64) {
-    const int i = idx / SBW, r = idx % SBW, j = jg + i;
-    if (j <= last && s < sweep_steps(n, j)) Vs[i + r][i] = Rf[(sweep_offset(n, j) + s) * RFS + r];
+  for (int idx = lane; idx < CBR * SBW; idx += 64) {
+    const int row = idx / SBW, i = idx % SBW;
+    if (row < i || row >= i + SBW) Vs[row][i] = 0.f;
   }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int idx = lane + 64 * q, i = idx / SBW, r = idx % SBW;
+    Vs[i + r][i] = rv[q];
+  }
+  if (lane < SBW) tau[lane] = tl;
   __syncthreads();
   f32x16 acc = {};
 #pragma unroll
@@ -609,23 +621,38 @@ __global__ __launch_bounds__(256) void k_cb_apply(int t, int glo, int nchunk, fl
   const float* Rf = Rf_g + z * rf_stride;
   float* Zz = Z + z * z_batch;
   const int last = n - 3;
-  // one phase of loads: T, Z, the staircase V[i + r][i] = v_r of sweep jg + i
-  // and zeros off the staircase (disjoint positions)
-  for (int idx = tid; idx < SBW * SBW; idx += 256) {
-    const int r = idx / SBW, c = idx % SBW;
-    Ts[r][c] = Tg[z * t_stride + (static_cast<int64_t>(G) * K0 + s) * SBW * SBW + idx];
+  // one phase of loads, every load in flight before the first LDS write: T,
+  // Z, the staircase V[i + r][i] = v_r of sweep jg + i; zeros off the
+  // staircase (disjoint positions)
+  float rt[4], rz[16], rv[4];
+  const float* tb = Tg + z * t_stride + (static_cast<int64_t>(G) * K0 + s) * SBW * SBW;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) rt[q] = tb[tid + 256 * q];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int idx = tid + 256 * q, c = idx / CBR, r = idx % CBR;
+    rz[q] = (r < rows && c < nc) ? Zz[static_cast<int64_t>(c0 + c) * n + rb + r] : 0.f;
   }
-  for (int idx = tid; idx < CBR * 64; idx += 256) {
-    const int c = idx / CBR, r = idx % CBR;
-    Zs[r][c] = (r < rows && c < nc) ? Zz[static_cast<int64_t>(c0 + c) * n + rb + r] : 0.f;
-  }
-  for (int idx = tid; idx < SBW * SBW; idx += 256) {
-    const int i = idx / SBW, r = idx % SBW, j = jg + i;
-    Vs[i + r][i] = (j <= last && s < sweep_steps(n, j)) ? Rf[(sweep_offset(n, j) + s) * RFS + r] : 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = tid + 256 * q, i = idx / SBW, r = idx % SBW, j = jg + i;
+    rv[q] = (j <= last && s < sweep_steps(n, j)) ? Rf[(sweep_offset(n, j) + s) * RFS + r] : 0.f;
   }
   for (int idx = tid; idx < CBR * SBW; idx += 256) {
     const int row = idx / SBW, i = idx % SBW;
     if (row < i || row >= i + SBW) Vs[row][i] = 0.f;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = tid + 256 * q;
+    Ts[idx / SBW][idx % SBW] = rt[q];
+    const int i = idx / SBW, r = idx % SBW;
+    Vs[i + r][i] = rv[q];
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int idx = tid + 256 * q;
+    Zs[idx % CBR][idx / CBR] = rz[q];
   }
   __syncthreads();
   // W = V^T Z: wave w -> columns 32 (w & 1) .., rows of V 32 (w >> 1) ..
@@ -673,9 +700,15 @@ __global__ __launch_bounds__(256) void k_cb_apply(int t, int glo, int nchunk, fl
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < CBR * 64; idx += 256) {
-    const int c = idx / CBR, r = idx % CBR;
-    if (r < rows && c < nc) Zz[static_cast<int64_t>(c0 + c) * n + rb + r] = Zs[r][c];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int idx = tid + 256 * q, c = idx / CBR, r = idx % CBR;
+    rz[q] = Zs[r][c];
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int idx = tid + 256 * q, c = idx / CBR, r = idx % CBR;
+    if (r < rows && c < nc) Zz[static_cast<int64_t>(c0 + c) * n + rb + r] = rz[q];
   }
 }
 
@@ -696,7 +729,13 @@ __global__ __launch_bounds__(256) void k_apply_wy(float* Z, int64_t n, int64_t z
   const int c0 = blockIdx.x * 64, nc = min(64, R - c0);
   float* Zr = Z + z * z_batch + r0;
   const float* V = V_g + z * v_batch;
-  for (int idx = tid; idx < SBW * SBW; idx += 256) Ts[idx / SBW][idx % SBW] = T_g[z * t_batch + idx];
+  {
+    float rt[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rt[q] = T_g[z * t_batch + tid + 256 * q];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Ts[(tid + 256 * q) / SBW][(tid + 256 * q) % SBW] = rt[q];
+  }
   // chunk loader: Z 64 rows x 64 columns (16 per thread), V 64 rows x 32 (8 per thread)
   float rz[16], rv[8];
   auto load = [&](int64_t k0) {
@@ -811,7 +850,13 @@ __global__ __launch_bounds__(256) void k_symm_v(const float* A, int64_t n, int64
   const int ib = blockIdx.x, i0 = SY * ib, nb = (mp + SY - 1) / SY;
   const float* a = A + z * a_batch;
   const float* V = V_g + z * v_batch;
-  for (int idx = tid; idx < SBW * SBW; idx += 256) Ts[idx >> 5][idx & 31] = T_g[z * t_batch + idx];
+  {
+    float rt[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rt[q] = T_g[z * t_batch + tid + 256 * q];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Ts[(tid + 256 * q) >> 5][(tid + 256 * q) & 31] = rt[q];
+  }
   float4 ra[4], rv[2];
   auto load = [&](int jc) {
     const int j0 = SY * jc;
