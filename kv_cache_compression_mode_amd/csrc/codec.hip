@@ -324,9 +324,10 @@ __global__ __launch_bounds__(256) void k_decode(DecBatch b) {
   const int r = lane & 31, half = lane >> 5;
   f32x16 acc[2][4] = {};
   const bool ua = (R.r_T % 8) == 0;
-  for (int k0 = 0; k0 < R.r_Tp; k0 += 16) {
+  // operands of one k step (16 of r_T), the next step's loaded during this one's MFMAs
+  bf16x8 a[2], bh[4], bl[4];
+  auto load_k = [&](int k0) {
     const int kk = k0 + 8 * half;
-    bf16x8 a[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const int64_t t = t0 + 32 * rt + r;
@@ -336,13 +337,22 @@ __global__ __launch_bounds__(256) void k_decode(DecBatch b) {
     for (int ct = 0; ct < 4; ++ct) {
       const int64_t wo = (h * D + 32 * ct + r) * R.r_Tp + kk;
       const uint4 rh = *reinterpret_cast<const uint4*>(R.Whi + wo);
-      const uint4 rl = *reinterpret_cast<const uint4*>(R.Wlo + wo);
-      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&rh);
-      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&rl);
+      const uint4 rlo = *reinterpret_cast<const uint4*>(R.Wlo + wo);
+      bh[ct] = *reinterpret_cast<const bf16x8*>(&rh);
+      bl[ct] = *reinterpret_cast<const bf16x8*>(&rlo);
+    }
+  };
+  if (R.r_Tp > 0) load_k(0);
+  for (int k0 = 0; k0 < R.r_Tp; k0 += 16) {
+    const bf16x8 ca[2] = {a[0], a[1]};
+    const bf16x8 ch[4] = {bh[0], bh[1], bh[2], bh[3]}, cl[4] = {bl[0], bl[1], bl[2], bl[3]};
+    if (k0 + 16 < R.r_Tp) load_k(k0 + 16);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rt], bh, acc[rt][ct], 0, 0, 0);
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rt], bl, acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[rt], ch[ct], acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[rt], cl[ct], acc[rt][ct], 0, 0, 0);
       }
     }
   }
