@@ -272,8 +272,14 @@ __global__ __launch_bounds__(256) void k_make_w(DecBatch b) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tile = blockIdx.x * 4 + wave;
   if (tile >= b.wtiles_total) return;
+  // the record holding this tile: the last with first tile <= tile (records
+  // are in order, so a binary search)
   int ri = 0;
-  while (ri + 1 < b.n && b.rec[ri + 1].wtile0 <= tile) ++ri;
+  for (int hi = b.n - 1; ri < hi;) {
+    const int mid = (ri + hi + 1) >> 1;
+    if (b.rec[mid].wtile0 <= tile) ri = mid;
+    else hi = mid - 1;
+  }
   const DecRec& R = b.rec[ri];
   const int local = tile - R.wtile0;
   const int ktiles = R.r_Tp / 32;
@@ -311,12 +317,18 @@ __global__ __launch_bounds__(256) void k_make_w(DecBatch b) {
 
 // One wave per (record, head, 64 rows): X^ rows = U~_T W (hi + lo) + Yhat Q.
 template <typename TO>
-__global__ __launch_bounds__(256) void k_decode(DecBatch b) {
+__global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tile = blockIdx.x * 4 + wave;
   if (tile >= b.tiles_total) return;
+  // the record holding this tile: the last with first tile <= tile (records
+  // are in order, so a binary search)
   int ri = 0;
-  while (ri + 1 < b.n && b.rec[ri + 1].tile0 <= tile) ++ri;
+  for (int hi = b.n - 1; ri < hi;) {
+    const int mid = (ri + hi + 1) >> 1;
+    if (b.rec[mid].tile0 <= tile) ri = mid;
+    else hi = mid - 1;
+  }
   const DecRec& R = b.rec[ri];
   const int local = tile - R.tile0;
   const int tilesT = (b.T + 63) / 64;
@@ -324,8 +336,10 @@ __global__ __launch_bounds__(256) void k_decode(DecBatch b) {
   const int r = lane & 31, half = lane >> 5;
   f32x16 acc[2][4] = {};
   const bool ua = (R.r_T % 8) == 0;
-  // operands of one k step (16 of r_T), the next step's loaded during this one's MFMAs
-  bf16x8 a[2], bh[4], bl[4];
+  // U~_T rows of one k step (16 of r_T) streamed from memory, the next
+  // step's loaded during this one's MFMAs; W (hi, lo) is shared by all row
+  // tiles of the head and stays in cache
+  bf16x8 a[2];
   auto load_k = [&](int k0) {
     const int kk = k0 + 8 * half;
 #pragma unroll
@@ -333,19 +347,20 @@ __global__ __launch_bounds__(256) void k_decode(DecBatch b) {
       const int64_t t = t0 + 32 * rt + r;
       a[rt] = t < b.T ? load8_bf16(R.Ut + t * R.r_T, kk, R.r_T, ua) : zero8();
     }
+  };
+  if (R.r_Tp > 0) load_k(0);
+  for (int k0 = 0; k0 < R.r_Tp; k0 += 16) {
+    const int kk = k0 + 8 * half;
+    const bf16x8 ca[2] = {a[0], a[1]};
+    bf16x8 ch[4], cl[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       const int64_t wo = (h * D + 32 * ct + r) * R.r_Tp + kk;
       const uint4 rh = *reinterpret_cast<const uint4*>(R.Whi + wo);
       const uint4 rlo = *reinterpret_cast<const uint4*>(R.Wlo + wo);
-      bh[ct] = *reinterpret_cast<const bf16x8*>(&rh);
-      bl[ct] = *reinterpret_cast<const bf16x8*>(&rlo);
+      ch[ct] = *reinterpret_cast<const bf16x8*>(&rh);
+      cl[ct] = *reinterpret_cast<const bf16x8*>(&rlo);
     }
-  };
-  if (R.r_Tp > 0) load_k(0);
-  for (int k0 = 0; k0 < R.r_Tp; k0 += 16) {
-    const bf16x8 ca[2] = {a[0], a[1]};
-    const bf16x8 ch[4] = {bh[0], bh[1], bh[2], bh[3]}, cl[4] = {bl[0], bl[1], bl[2], bl[3]};
     if (k0 + 16 < R.r_Tp) load_k(k0 + 16);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -358,35 +373,51 @@ __global__ __launch_bounds__(256) void k_decode(DecBatch b) {
   }
   const int bits = R.bits;
   const uint32_t qmask = (1u << bits) - 1u;
-  for (int d0 = 0; d0 < D; d0 += 16) {
+  // the streamed words of one d step (scales, code words), the next step's
+  // loaded during this one's dequantization and MFMAs (Q^T stays in cache)
+  uint32_t sw[2], w0[2], w1[2];
+  auto load_d = [&](int d0) {
     const int dd = d0 + 8 * half;               // this lane's 8 features
     const int g = dd >> 5, bitpos = (dd & 31) * bits;
-    bf16x8 y[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const int64_t t = t0 + 32 * rt + r;
+      sw[rt] = 0u; w0[rt] = 0u; w1[rt] = 0u;
       if (t < b.T) {
         const int64_t gi = (h * b.T + t) * 4 + g;
-        const uint32_t sw = R.scales[gi];
-        const float m16 = bf16_bits_to_f32(static_cast<uint16_t>(sw & 0xffffu));
-        const float s16 = bf16_bits_to_f32(static_cast<uint16_t>(sw >> 16));
+        sw[rt] = R.scales[gi];
         const uint32_t* cw = R.codes + gi * bits;
-        uint64_t stream = cw[bitpos >> 5];
-        if ((bitpos & 31) + 8 * bits > 32) stream |= static_cast<uint64_t>(cw[(bitpos >> 5) + 1]) << 32;
-        stream >>= (bitpos & 31);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t q = static_cast<uint32_t>(stream >> (i * bits)) & qmask;
-          y[rt][i] = static_cast<__bf16>(fmaf(static_cast<float>(q), s16, m16));
-        }
-      } else {
-        y[rt] = zero8();
+        w0[rt] = cw[bitpos >> 5];
+        if ((bitpos & 31) + 8 * bits > 32) w1[rt] = cw[(bitpos >> 5) + 1];
       }
     }
+  };
+  load_d(0);
+  for (int d0 = 0; d0 < D; d0 += 16) {
+    const int dd = d0 + 8 * half;
+    const int bitpos = (dd & 31) * bits;
+    const uint32_t csw[2] = {sw[0], sw[1]}, cw0[2] = {w0[0], w0[1]}, cw1[2] = {w1[0], w1[1]};
+    uint4 cq[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) cq[ct] = *reinterpret_cast<const uint4*>(b.Qt16 + (32 * ct + r) * D + dd);
+    if (d0 + 16 < D) load_d(d0 + 16);
+    bf16x8 y[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const float m16 = bf16_bits_to_f32(static_cast<uint16_t>(csw[rt] & 0xffffu));
+      const float s16 = bf16_bits_to_f32(static_cast<uint16_t>(csw[rt] >> 16));
+      const uint64_t stream = (static_cast<uint64_t>(cw0[rt]) | (static_cast<uint64_t>(cw1[rt]) << 32)) >>
+                              (bitpos & 31);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t q = static_cast<uint32_t>(stream >> (i * bits)) & qmask;
+        y[rt][i] = static_cast<__bf16>(fmaf(static_cast<float>(q), s16, m16));
+      }
+    }
+    // rows past T: scale word 0 gives m16 = s16 = 0, so y = 0
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      const uint4 rq = *reinterpret_cast<const uint4*>(b.Qt16 + (32 * ct + r) * D + dd);
-      const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&rq);
+      const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&cq[ct]);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
         acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(y[rt], bq, acc[rt][ct], 0, 0, 0);
