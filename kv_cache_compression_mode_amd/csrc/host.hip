@@ -231,11 +231,6 @@ int numerical_rank(const double* lam, int len, int64_t n) {
   for (int i = 0; i < len; ++i) c += lam[i] > thr;
   return c;
 }
-double tail(const double* lam, int len, double frob2, int r) {
-  double s = 0.0;
-  for (int i = 0; i < std::min(r, len); ++i) s += lam[i];
-  return std::max(0.0, frob2 - s);
-}
 double rho(int bits) {
   const int L = (1 << bits) - 1;
   return kKappa32 / (12.0 * static_cast<double>(L * L));
@@ -284,6 +279,24 @@ jolt_status plan_dual(const jolt_alloc_req* req, const double* spT, int lenT, co
   const int64_t nT = std::min<int64_t>(s.T, static_cast<int64_t>(s.H) * s.D);
   const int sT = steps_T(req), sD = steps_D(req);
   const int n_groups = (L + G - 1) / G;
+  // prefix sums of every tensor's spectra, accumulated in index order from
+  // 0.0: the residual energy max(0, ||X||^2 - sum_{i<r} lambda_i) in O(1) per choice
+  const int ntens = 2 * L;
+  std::vector<double> preT(static_cast<size_t>(ntens) * (lenT + 1)), preD(static_cast<size_t>(ntens) * (s.D + 1));
+  for (int t = 0; t < ntens; ++t) {
+    double* pt = preT.data() + static_cast<size_t>(t) * (lenT + 1);
+    double* pd = preD.data() + static_cast<size_t>(t) * (s.D + 1);
+    pt[0] = 0.0;
+    for (int i = 0; i < lenT; ++i) pt[i + 1] = pt[i] + spT[static_cast<size_t>(t) * lenT + i];
+    pd[0] = 0.0;
+    for (int i = 0; i < s.D; ++i) pd[i + 1] = pd[i] + spD[static_cast<size_t>(t) * s.D + i];
+  }
+  auto tail_T = [&](int t, double f2, int r) {
+    return std::max(0.0, f2 - preT[static_cast<size_t>(t) * (lenT + 1) + std::min(r, lenT)]);
+  };
+  auto tail_D = [&](int t, double f2, int r) {
+    return std::max(0.0, f2 - preD[static_cast<size_t>(t) * (s.D + 1) + std::min(r, static_cast<int>(s.D))]);
+  };
   struct Unit {
     int first, last;
     std::vector<jolt_choice> menu;
@@ -315,8 +328,7 @@ jolt_status plan_dual(const jolt_alloc_req* req, const double* spT, int lenT, co
           const int t = l * 2 + kind;
           const double f2 = frob2[t];
           if (!(f2 > 0.0)) continue;
-          const double e = (tail(spT + static_cast<size_t>(t) * lenT, lenT, f2, c.r_T) +
-                            tail(spD + static_cast<size_t>(t) * s.D, s.D, f2, c.r_D)) / f2;
+          const double e = (tail_T(t, f2, c.r_T) + tail_D(t, f2, c.r_D)) / f2;
           dist += rho(c.bits) * std::min(1.0, e);
         }
         pts.push_back({nb, dist, i});
