@@ -111,8 +111,7 @@ def main():
         res = jolt.allocate(xs, ratio=cfg.ratio, method=method, bits=cfg.bits, seed=cfg.seed)
         ev[1].record(stream)
         choices = [res.choice_of(i // 2, i % 2) for i in range(len(flat))]
-        factors = [res.factors(i) for i in range(len(flat))]
-        blobs = jolt.encode_many(flat, choices, factors, rot, seed=cfg.seed)
+        blobs = jolt.encode_many(flat, choices, res, rot, seed=cfg.seed)
         ev[2].record(stream)
         dws = torch.empty(decode_ws_bytes(choices), dtype=torch.uint8, device=dev)
         decode_all(blobs, choices, dws)

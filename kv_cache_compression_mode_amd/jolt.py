@@ -212,7 +212,8 @@ def encode_many(xs, choices, factors, rot: torch.Tensor, seed: int = 0, outs=Non
     """Compress several [H, T, 128] tensors of one shape and dtype into device
     records (the same bytes as encode() per tensor, in batched launches).
     factors[i] = (U_T, U_D) fp32 [rows, ld] with unit column stride (or
-    (None, None) for a choice with r_T == 0)."""
+    (None, None) for a choice with r_T == 0); or the Allocation of the cache
+    whose tensors xs are, in order (its factors are read in place)."""
     n = len(xs)
     if n == 0:
         return []
@@ -223,17 +224,38 @@ def encode_many(xs, choices, factors, rot: torch.Tensor, seed: int = 0, outs=Non
     for x in xs:
         if x.shape != x0.shape or x.dtype != x0.dtype or not x.is_contiguous():
             raise ValueError("all tensors must be contiguous with one shape and dtype")
-    blobs = outs if outs is not None else [
-        torch.empty(lib().jolt_blob_bytes(C.byref(shape), ch[i]), dtype=torch.uint8, device=x0.device)
-        for i in range(n)]
-    for f in (f for pair in factors for f in pair):
-        if f is not None and (f.dtype != torch.float32 or f.dim() != 2 or f.stride(1) != 1):
-            raise ValueError("factors must be fp32 [rows, ld] with unit column stride")
+    if outs is not None:
+        blobs = outs
+    else:
+        # one allocation cut into 256-aligned records
+        sizes = [lib().jolt_blob_bytes(C.byref(shape), ch[i]) for i in range(n)]
+        offs, o = [], 0
+        for nb in sizes:
+            offs.append(o)
+            o += (nb + 255) // 256 * 256
+        buf = torch.empty(max(o, 1), dtype=torch.uint8, device=x0.device)
+        blobs = [buf[a:a + nb] for a, nb in zip(offs, sizes)]
     xp = (C.c_void_p * n)(*[x.data_ptr() for x in xs])
-    utp = (C.c_void_p * n)(*[f[0].data_ptr() if f[0] is not None else None for f in factors])
-    udp = (C.c_void_p * n)(*[f[1].data_ptr() if f[1] is not None else None for f in factors])
-    ldt = (C.c_int32 * n)(*[f[0].stride(0) if f[0] is not None else 0 for f in factors])
-    ldd = (C.c_int32 * n)(*[f[1].stride(0) if f[1] is not None else 0 for f in factors])
+    if isinstance(factors, Allocation):
+        if n != 2 * factors.req.n_layers:
+            raise ValueError("an Allocation supplies the factors of its whole cache")
+        utp, udp = (C.c_void_p * n)(), (C.c_void_p * n)()
+        ldt, ldd = (C.c_int32 * n)(), (C.c_int32 * n)()
+        ws_ptr = factors.workspace.data_ptr()
+        ut, ud, ld = C.c_void_p(), C.c_void_p(), C.c_int32()
+        for i in range(n):
+            check(lib().jolt_factors(C.byref(factors.req), ws_ptr, i, C.byref(ut), C.byref(ld), C.byref(ud)),
+                  "jolt_factors")
+            utp[i], udp[i] = ut.value, ud.value
+            ldt[i], ldd[i] = ld.value, factors.req.shape.D
+    else:
+        for f in (f for pair in factors for f in pair):
+            if f is not None and (f.dtype != torch.float32 or f.dim() != 2 or f.stride(1) != 1):
+                raise ValueError("factors must be fp32 [rows, ld] with unit column stride")
+        utp = (C.c_void_p * n)(*[f[0].data_ptr() if f[0] is not None else None for f in factors])
+        udp = (C.c_void_p * n)(*[f[1].data_ptr() if f[1] is not None else None for f in factors])
+        ldt = (C.c_int32 * n)(*[f[0].stride(0) if f[0] is not None else 0 for f in factors])
+        ldd = (C.c_int32 * n)(*[f[1].stride(0) if f[1] is not None else 0 for f in factors])
     bp = (C.c_void_p * n)(*[b.data_ptr() for b in blobs])
     bb = (C.c_size_t * n)(*[b.numel() for b in blobs])
     nws = lib().jolt_encode_many_workspace_bytes(n, C.byref(shape), ch)

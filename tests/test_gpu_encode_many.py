@@ -53,3 +53,29 @@ def test_encode_many_matches_encode(J, dtype):
     torch.cuda.synchronize()
     for a, b in zip(one[::-1], again):
         assert torch.equal(a, b)
+
+
+def test_encode_many_reads_an_allocation(J):
+    """Factors taken from the Allocation in place give the same records as the
+    factor views passed one by one (choices with r_T > 0 and r_T = 0)."""
+    cfg = kvgen.CONFIGS["single_k_t1024_f32"]
+    L = 2
+    xs = []
+    for layer in range(L):
+        for kind in (0, 1):
+            x = kvgen.config_tensor(cfg, layer, kind).astype(np.float32)
+            xs.append(torch.from_numpy(x).to(torch.bfloat16).cuda().contiguous())
+    res = J.allocate([(xs[2 * l], xs[2 * l + 1]) for l in range(L)], ratio=2.0)
+    H, T, D = xs[0].shape
+    choices = [(64, 32, 2), (0, 0, 3), (128, 64, 4), (96, 64, 1)]
+    views = [res.factors(i) if ch[0] > 0 else (None, None) for i, ch in enumerate(choices)]
+    rot = J.rotation(3)
+    sizes = [J.blob_bytes(H, T, D, ch, torch.bfloat16) for ch in choices]
+    zeros = lambda: [torch.zeros(nb, dtype=torch.uint8, device="cuda") for nb in sizes]
+    a = J.encode_many(xs, choices, views, rot, seed=3, outs=zeros())
+    b = J.encode_many(xs, choices, res, rot, seed=3, outs=zeros())
+    torch.cuda.synchronize()
+    for i, (u, v) in enumerate(zip(a, b)):
+        assert torch.equal(u, v), f"record {i} ({choices[i]}) differs"
+    with pytest.raises(ValueError):
+        J.encode_many(xs[:2], choices[:2], res, rot, seed=3)
