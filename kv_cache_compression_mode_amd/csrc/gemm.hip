@@ -528,13 +528,36 @@ __global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
 
 // ---------------------------------------------------------------- misc
 // Sum of squares in fp64, one accumulator per tensor (blockIdx.y).
+// 16-byte loads, four in flight per thread, where the tensor is 16-byte
+// aligned and a multiple of 16 bytes long; element loads otherwise.
 template <typename T>
 __global__ __launch_bounds__(256) void k_sumsq(const void* const* xs, int64_t n, double* out) {
   const T* x = static_cast<const T*>(xs[blockIdx.y]);
+  constexpr int E = 16 / sizeof(T);                     // elements per 16 bytes
   double s = 0.0;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += 256ll * gridDim.x) {
-    const double v = load_as_f32<T>(x, i);
-    s += v * v;
+  const int64_t stride = 256ll * gridDim.x;
+  if ((reinterpret_cast<uintptr_t>(x) & 15) == 0 && n % E == 0) {
+    const int64_t nv = n / E;
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    for (int64_t i0 = blockIdx.x * 256ll + threadIdx.x; i0 < nv; i0 += 4 * stride) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = i0 + u * stride < nv ? xv[i0 + u * stride] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const T* e = reinterpret_cast<const T*>(&v[u]);
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+          const double d = load_as_f32<T>(e, k);
+          s += d * d;
+        }
+      }
+    }
+  } else {
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += stride) {
+      const double v = load_as_f32<T>(x, i);
+      s += v * v;
+    }
   }
   s = wave_sum(s);
   __shared__ double part[4];
