@@ -155,6 +155,25 @@ __global__ __launch_bounds__(NW * 64) void k_chase(float* Bw_g, int n, float* Rf
     }
     if (q.s == 0) px = bload(band, 4u * static_cast<uint32_t>(q.r0 * BWS + 1 + l32 * (BWS + 1)));  // (r0 + l32, j)
   };
+  // Progress ring instead of a workgroup barrier per tick: the band values a
+  // prefetch at tick t reads were last written by the previous sweep (the
+  // previous wave, one tick behind at most) at tick t - 1 or earlier, and
+  // older sweeps only earlier still; so wave w publishes each finished tick
+  // (after its stores) and waits, before prefetching at tick t, for its
+  // predecessor to have finished tick t - 1.  Waits point to strictly
+  // earlier ticks of other waves, so they always end; the spin is bounded
+  // all the same.
+  __shared__ int tick_done[NW];
+  if ((threadIdx.x & 63) == 0) tick_done[wave] = -1;
+  __syncthreads();
+  const int pred = (wave + NW - 1) % NW;
+  auto wait_pred = [&](int t_need) {
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+      if (__hip_atomic_load(&tick_done[pred], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= t_need) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  };
   ChaseClock ck, ckn;
   ck.init(wave, S, n);
   ckn.init(wave, S, n);
@@ -178,7 +197,10 @@ __global__ __launch_bounds__(NW * 64) void k_chase(float* Bw_g, int n, float* Rf
       }
       if (g.s == 0 && lane < SBW) sm.x[lane] = px;
     }
-    if (actn) prefetch(gn);
+    if (actn) {
+      if (t > 0) wait_pred(t - 1);
+      prefetch(gn);
+    }
     if (act) {
       const int L = g.L, r0 = g.r0;
       wave_lds_sync();
@@ -301,7 +323,10 @@ __global__ __launch_bounds__(NW * 64) void k_chase(float* Bw_g, int n, float* Rf
       }
       cur ^= 1;
     }
-    __syncthreads();
+    // this tick's band stores complete, then published
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if ((threadIdx.x & 63) == 0)
+      __hip_atomic_store(&tick_done[wave], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
 
