@@ -145,8 +145,9 @@ jolt_status jolt_factors(const jolt_alloc_req* req, void* ws_dev, int32_t tensor
 
 /* The seeded rotation Q (D x D, Haar: QR of a counter-based Gaussian matrix
  * with diag(R) > 0), prepared on the host in fp64 and uploaded to q_dev
- * (jolt_rotation_bytes(D) bytes: fp32 Q, fp32 Q^T, bf16 Q^T, each section
- * 256-aligned).  Synchronizes `stream`.
+ * (jolt_rotation_bytes(D) bytes: fp32 Q, fp32 Q^T, bf16 Q^T and the three
+ * bf16 parts hi, mid, lo of the fp32 Q (hi + mid + lo = Q exactly, in the
+ * matrix-core fragment order of the encoder), each section 256-aligned).  Synchronizes `stream`.
  * Source: JoLT abstract, "a random orthogonal rotation followed by low-bit
  * quantization". */
 jolt_status jolt_rotation(uint64_t seed, int32_t D, void* q_dev, size_t q_bytes,

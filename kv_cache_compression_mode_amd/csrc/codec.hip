@@ -9,14 +9,8 @@
 // step ((max - offset) / (2^b - 1) rounded toward +inf), codes are
 // rint((y - offset) / step) clamped to [0, 2^b - 1], all in IEEE fp32 with a
 // correctly rounded divide, packed as a little-endian bit stream (code k at
-// bits [k*b, (k+1)*b) of the group's 4b bytes).
-//
-// Layout of one workgroup (256 threads, 4 waves) over a 64-row tile: wave w
-// owns features [32w, 32w + 32) = quantization group w.  In the 32x32 fp32
-// matrix-core accumulator, register i of lane l holds row
-// (i/4)*8 + (l/32)*4 + i%4 and column l%32, so one register across a
-// half-wave is exactly one group: min/max are 5 xor-shuffles and the bit
-// stream is assembled from ballots.
+// bits [k*b, (k+1)*b) of the group's 4b bytes).  One thread quantizes one
+// group, so the group's reductions and its bit stream stay in registers.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -25,223 +19,76 @@ namespace {
 
 constexpr int D = 128;
 
-__device__ __forceinline__ float half_min(float v) {
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float half_max(float v) {
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-// Bit interleaves: bit i of x moves to bit 2i (16 bits), 4i (8 bits), 3i (12 bits).
-__device__ __forceinline__ uint32_t spread2_16(uint32_t x) {
-  x &= 0xFFFFu;
-  x = (x | (x << 8)) & 0x00FF00FFu;
-  x = (x | (x << 4)) & 0x0F0F0F0Fu;
-  x = (x | (x << 2)) & 0x33333333u;
-  return (x | (x << 1)) & 0x55555555u;
-}
-__device__ __forceinline__ uint32_t spread4_8(uint32_t x) {
-  x &= 0xFFu;
-  x = (x | (x << 12)) & 0x000F000Fu;
-  x = (x | (x << 6)) & 0x03030303u;
-  return (x | (x << 3)) & 0x11111111u;
-}
-__device__ __forceinline__ uint64_t spread3_12(uint64_t x) {
-  x &= 0xFFFull;
-  x = (x | (x << 16)) & 0x00000000FF0000FFull;
-  x = (x | (x << 8)) & 0x000000F00F00F00Full;
-  x = (x | (x << 4)) & 0x00000C30C30C30C3ull;
-  return (x | (x << 2)) & 0x0000249249249249ull;
-}
-// Word k (k < bits) of a group's code stream (stream bit s = bit s % bits of
-// code s / bits, word k = stream bits [32k, 32k + 32)) from the per-bit masks
-// m[j] (bit c = bit j of code c).
-__device__ __forceinline__ uint32_t pack_word(const uint32_t (&m)[4], int bits, int k) {
-  switch (bits) {
-    case 1: return m[0];
-    case 2: return spread2_16(m[0] >> (16 * k)) | (spread2_16(m[1] >> (16 * k)) << 1);
-    case 3: {   // codes c0 .. c0 + 11 cover the word; c0 = floor(32k / 3)
-      const int c0 = (32 * k) / 3, sh = 32 * k - 3 * c0;
-      const uint64_t w = spread3_12(m[0] >> c0) | (spread3_12(m[1] >> c0) << 1) | (spread3_12(m[2] >> c0) << 2);
-      return static_cast<uint32_t>(w >> sh);
-    }
-    default:
-      return spread4_8(m[0] >> (8 * k)) | (spread4_8(m[1] >> (8 * k)) << 1) |
-             (spread4_8(m[2] >> (8 * k)) << 2) | (spread4_8(m[3] >> (8 * k)) << 3);
-  }
-}
-
-// Quantize the group held by this half-wave (one value per lane) and write
-// its (offset, step) pair and 4*bits code bytes.  Every lane of the wave must
-// call it (ballots); `valid` masks rows past the tensor end.
-__device__ __forceinline__ void quantize_group(float y, int bits, bool valid, uint32_t* scale_word,
+// The group of 32 values y (one thread): scale word (offset | step << 16)
+// and the B code words.
+template <int B>
+__device__ __forceinline__ void quantize_group(const float (&y)[32], bool store, uint32_t* scale_word,
                                                uint32_t* code_words) {
-  const int lane = threadIdx.x & 63, k = lane & 31, half = lane >> 5;
-  const float mn = half_min(y), mx = half_max(y);
+  float mn = y[0], mx = y[0];
+#pragma unroll
+  for (int c = 1; c < 32; ++c) {
+    mn = fminf(mn, y[c]);
+    mx = fmaxf(mx, y[c]);
+  }
   const uint16_t m16b = bf16_round_down(mn);
   const float m16 = bf16_bits_to_f32(m16b);
-  const float L = static_cast<float>((1 << bits) - 1);
-  const float s32 = __fdiv_rn(mx - m16, L);
-  const uint16_t s16b = bf16_round_up(s32);
+  const float L = static_cast<float>((1 << B) - 1);
+  const uint16_t s16b = bf16_round_up(__fdiv_rn(mx - m16, L));
   const float s16 = bf16_bits_to_f32(s16b);
-  uint32_t code = 0;
+  uint32_t w[B];
+#pragma unroll
+  for (int k = 0; k < B; ++k) w[k] = 0u;
   if (s16 != 0.f) {
-    float t = rintf(__fdiv_rn(y - m16, s16));
-    t = fminf(fmaxf(t, 0.f), L);
-    code = static_cast<uint32_t>(t);
-  }
-  uint32_t mask[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const unsigned long long b = __ballot(j < bits ? ((code >> j) & 1u) : 0u);
-    mask[j] = static_cast<uint32_t>(b >> (32 * half));
-  }
-  if (!valid) return;
-  if (k == 0) *scale_word = static_cast<uint32_t>(m16b) | (static_cast<uint32_t>(s16b) << 16);
-  if (k < bits) code_words[k] = pack_word(mask, bits, k);
-}
-
-// Standalone quantizer: one group per half-wave, 8 groups per workgroup.
-__global__ __launch_bounds__(256) void k_quantize(const float* Y, int64_t ngroups, int bits,
-                                                  uint32_t* scales, uint32_t* codes) {
-  const int64_t g = blockIdx.x * 8ll + (threadIdx.x >> 5);
-  const bool valid = g < ngroups;
-  const float y = valid ? Y[g * 32 + (threadIdx.x & 31)] : 0.f;
-  quantize_group(y, bits, valid, scales + g, codes + g * bits);
-}
-
-template <typename TX>
-__device__ __forceinline__ float load_x(const void* X, int64_t i) {
-  return load_as_f32<TX>(static_cast<const TX*>(X), i);
-}
-
-// One workgroup per 64-row tile of one head (two 32-row blocks).  The
-// reconstruction Ut[t0 .. t0+64) W_h and the rotation R Q^T run on fp32
-// matrix cores (32x32x2, k in increasing order), their B operands (W_h, then
-// Q^T) staged through LDS in chunks of 32 k with the next chunk's loads issued
-// before the current chunk's MFMAs; wave w keeps the two 32x32 blocks of
-// features [32w, 32w + 32), i.e. quantization group w of every row.
-constexpr int ER = 64;        // rows per workgroup
-constexpr int EK = 32;        // K chunk
-constexpr int EWP = D + 4;    // LDS row stride of a staged B chunk (16-byte rows)
-
-template <typename TX>
-__device__ __forceinline__ void encode_tile(const EncodeArgs& a) {
-  __shared__ float Us[EK][ER + 1];                               // Ut chunk, [k][row]
-  __shared__ __attribute__((aligned(16))) float Bs[EK][EWP];     // W_h or Q^T chunk, [k][feature]
-  __shared__ float Rs[ER][D + 1];                                // residual rows
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, half = lane >> 5;
-  const int64_t h = blockIdx.y, t0 = static_cast<int64_t>(blockIdx.x) * ER;
-  const int col = wave * 32 + rl;
-  // B chunk loader: 32 rows x 128 floats, rows kb = (tid >> 5) + 8 i, float4 column 4 (tid & 31)
-  const int bk = tid >> 5, bc = 4 * (tid & 31);
-  float4 rb[4];
-  auto load_b = [&](const float* src, int64_t k0, int64_t kmax) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t k = k0 + bk + 8 * i;
-      rb[i] = k < kmax ? *reinterpret_cast<const float4*>(src + k * D + bc) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  auto store_b = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<float4*>(&Bs[bk + 8 * i][bc]) = rb[i];
-  };
-  f32x16 acc0 = {}, acc1 = {};
-  if (a.r_T > 0) {
-    const float* Wh = a.W + h * a.r_T * D;
-    // Ut chunk loader: row ur = tid >> 2, k = 8 (tid & 3) .. +8
-    const int ur = tid >> 2, uk = 8 * (tid & 3);
-    const int64_t ut = t0 + ur;
-    float ru[8];
-    auto load_u = [&](int64_t k0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int64_t k = k0 + uk + i;
-        ru[i] = (ut < a.T && k < a.r_T) ? bf16_bits_to_f32(a.Ut[ut * a.r_T + k]) : 0.f;
-      }
-    };
-    load_u(0);
-    load_b(Wh, 0, a.r_T);
-    for (int64_t k0 = 0; k0 < a.r_T; k0 += EK) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Us[uk + i][ur] = ru[i];
-      store_b();
-      __syncthreads();
-      if (k0 + EK < a.r_T) {
-        load_u(k0 + EK);
-        load_b(Wh, k0 + EK, a.r_T);
-      }
-#pragma unroll
-      for (int kk = 0; kk < EK; kk += 2) {
-        const int k = kk + half;
-        const float b = Bs[k][col];
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(Us[k][rl], b, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(Us[k][32 + rl], b, acc1, 0, 0, 0);
-      }
-      __syncthreads();
+    for (int c = 0; c < 32; ++c) {
+      const float t = fminf(fmaxf(rintf(__fdiv_rn(y[c] - m16, s16)), 0.f), L);
+      const uint32_t code = static_cast<uint32_t>(t);
+      const int pos = c * B, wi = pos >> 5, sh = pos & 31;
+      w[wi] |= code << sh;
+      if (sh + B > 32) w[wi + 1] |= code >> (32 - sh);
     }
   }
-  // residual R = X - recon, staged in LDS as [row][feature]
-  load_b(a.Qt, 0, D);                            // first Q^T chunk, in flight meanwhile
+  if (!store) return;
+  *scale_word = static_cast<uint32_t>(m16b) | (static_cast<uint32_t>(s16b) << 16);
+  if constexpr (B == 4) {
+    *reinterpret_cast<uint4*>(code_words) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if constexpr (B == 2) {
+    *reinterpret_cast<uint2*>(code_words) = make_uint2(w[0], w[1]);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int m = (i >> 2) * 8 + half * 4 + (i & 3);
-    const int64_t ta = t0 + m, tb = t0 + 32 + m;
-    const float xa = ta < a.T ? load_x<TX>(a.X, (h * a.T + ta) * D + col) : 0.f;
-    const float xb = tb < a.T ? load_x<TX>(a.X, (h * a.T + tb) * D + col) : 0.f;
-    Rs[m][col] = xa - acc0[i];
-    Rs[32 + m][col] = xb - acc1[i];
+    for (int k = 0; k < B; ++k) code_words[k] = w[k];
   }
-  // Y = R Q^T: Y[m][c] = sum_d R[m][d] Qt[d][c]
-  f32x16 y0 = {}, y1 = {};
-  for (int d0 = 0; d0 < D; d0 += EK) {
-    store_b();
-    __syncthreads();
-    if (d0 + EK < D) load_b(a.Qt, d0 + EK, D);
+}
+
+__device__ __forceinline__ void quantize_any(const float (&y)[32], int bits, bool store, uint32_t* scale_word,
+                                             uint32_t* code_words) {
+  switch (bits) {
+    case 1: quantize_group<1>(y, store, scale_word, code_words); break;
+    case 2: quantize_group<2>(y, store, scale_word, code_words); break;
+    case 3: quantize_group<3>(y, store, scale_word, code_words); break;
+    default: quantize_group<4>(y, store, scale_word, code_words); break;
+  }
+}
+
+// Standalone quantizer: one group per thread.
+__global__ __launch_bounds__(256) void k_quantize(const float* Y, int64_t ngroups, int bits, uint32_t* scales,
+                                                  uint32_t* codes) {
+  const int64_t g = blockIdx.x * 256ll + threadIdx.x;
+  if (g >= ngroups) return;
+  const float* src = Y + g * 32;
+  float y[32];
+  if ((reinterpret_cast<uintptr_t>(Y) & 15) == 0) {
 #pragma unroll
-    for (int kk = 0; kk < EK; kk += 2) {
-      const int k = kk + half;
-      const float b = Bs[k][col];
-      y0 = __builtin_amdgcn_mfma_f32_32x32x2f32(Rs[rl][d0 + k], b, y0, 0, 0, 0);
-      y1 = __builtin_amdgcn_mfma_f32_32x32x2f32(Rs[32 + rl][d0 + k], b, y1, 0, 0, 0);
+    for (int q = 0; q < 8; ++q) {
+      const float4 v = reinterpret_cast<const float4*>(src)[q];
+      y[4 * q] = v.x; y[4 * q + 1] = v.y; y[4 * q + 2] = v.z; y[4 * q + 3] = v.w;
     }
-    __syncthreads();
-  }
-  uint32_t* sc = reinterpret_cast<uint32_t*>(a.scales);
-  uint32_t* cd = reinterpret_cast<uint32_t*>(a.codes);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int m = (i >> 2) * 8 + half * 4 + (i & 3);
-    const int64_t ta = t0 + m, tb = t0 + 32 + m;
-    const int64_t ga = (h * a.T + ta) * 4 + wave, gb = (h * a.T + tb) * 4 + wave;   // group indices
-    quantize_group(y0[i], a.bits, ta < a.T, sc + ga, cd + ga * a.bits);
-    quantize_group(y1[i], a.bits, tb < a.T, sc + gb, cd + gb * a.bits);
+    for (int c = 0; c < 32; ++c) y[c] = src[c];
   }
+  quantize_any(y, bits, true, scales + g, codes + g * bits);
 }
-
-template <typename TX>
-__global__ __launch_bounds__(256, 2) void k_encode_residual(EncodeArgs a) {
-  encode_tile<TX>(a);
-}
-// Tensors of one shape in one launch: blockIdx.z selects the tensor's arguments.
-template <typename TX>
-__global__ __launch_bounds__(256, 2) void k_encode_residual_many(const EncodeArgs* list) {
-  const EncodeArgs a = list[blockIdx.z];
-  encode_tile<TX>(a);
-}
-
-// ------------------------------------------------------------------ decode
-// bf16 matrix cores (32x32x16, fp32 accumulate).  Stored factors and core are
-// bf16, so U~_T x W is exact per product once W = G~_h U~_D^T is carried as a
-// hi + lo pair of bf16 (relative error 2^-17); the dequantized residual and Q
-// enter in bf16 (relative 2^-9 each, far below the quantization error they
-// ride on).  Every MFMA operand is one 16-byte load per lane: lane l holds
-// row l%32 and k = 8*(l/32) .. +8 of A, column l%32 and the same k of B.
 
 __device__ __forceinline__ bf16x8 load8_bf16(const uint16_t* base, int64_t idx, int64_t limit,
                                              bool aligned) {
@@ -265,6 +112,366 @@ __device__ __forceinline__ bf16x8 zero8() {
   for (int i = 0; i < 8; ++i) v[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0));
   return v;
 }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 raw) { return *reinterpret_cast<const bf16x8*>(&raw); }
+
+// ------------------------------------------------------------------ encode
+// Both products of the encoder run on bf16 matrix cores (32x32x16, fp32
+// accumulate) over exact three-part splits of their fp32 operands: f = hi +
+// mid + lo with hi = rne_bf16(f), mid = rne_bf16(f - hi) and lo = f - hi - mid,
+// which has at most 8 significant bits and is therefore a bf16 itself.  Every
+// product of two bf16 values is exact in fp32, so the splits cost accuracy
+// only through the terms left out (below 2^-25 relative per product) and the
+// fp32 accumulation, which keeps the large hi x hi terms in an accumulator of
+// their own and adds the small ones in a second.
+
+__device__ __forceinline__ uint16_t rne_bits(float f) {   // finite f
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ void split3(float f, uint16_t& h, uint16_t& m, uint16_t& l) {
+  h = rne_bits(f);
+  const float r1 = f - bf16_bits_to_f32(h);        // exact
+  m = rne_bits(r1);
+  const float r2 = r1 - bf16_bits_to_f32(m);       // exact, <= 8 significant bits
+  l = static_cast<uint16_t>(__float_as_uint(r2) >> 16);
+}
+
+// W_h = G~_h U~_D^T in three bf16 parts, stored in matrix-core fragment
+// order: W3[p][h][cb][ks][lane][e] (cb < 4 blocks of 32 features, ks < r_Tp/16
+// steps of 16 values of k, lane = 32 half + r) holds part p of W_h[k][d] for
+// d = 32 cb + r, k = 16 ks + 8 half + e, so the B operand of one k step of one
+// wave is 1 KB of consecutive bytes; k >= r_T is zero, r_Tp a multiple of 64
+// (whole staged chunks of U~_T in the encoder).
+// One wave per (tensor, head, 32 values of k), K = r_D in steps of 16 on bf16
+// matrix cores (the factors are bf16, so the products are exact and only the
+// fp32 sum rounds).  Tensor j of a launch reads G~_h from Gp[j H + h] and
+// U~_D from Udp[j H + h] (or G0 + h r_T r_D and Ud0 when Gp is null) and
+// writes W3 + j w3_batch.
+__global__ __launch_bounds__(64) void k_enc_w(const uint16_t* const* Gp, const uint16_t* const* Udp,
+                                              const uint16_t* G0, const uint16_t* Ud0, uint16_t* W3,
+                                              int64_t w3_batch, int H, int r_T, int r_D, int r_Tp) {
+  const int lane = threadIdx.x, r = lane & 31, half = lane >> 5;
+  const int k0 = blockIdx.x * 32, h = blockIdx.y, j = blockIdx.z;
+  const uint16_t* G = Gp ? Gp[static_cast<int64_t>(j) * H + h] : G0 + static_cast<int64_t>(h) * r_T * r_D;
+  const uint16_t* Ud = Udp ? Udp[static_cast<int64_t>(j) * H + h] : Ud0;
+  uint16_t* out = W3 + j * w3_batch;
+  const bool ga = (r_D % 8) == 0 && (reinterpret_cast<uintptr_t>(G) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(Ud) & 15) == 0;
+  const int k = k0 + r;
+  f32x16 acc[4] = {};
+  for (int j0 = 0; j0 < r_D; j0 += 16) {
+    const int jj = j0 + 8 * half;
+    const bf16x8 b = k < r_T ? load8_bf16(G + static_cast<int64_t>(k) * r_D, jj, r_D, ga) : zero8();
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const bf16x8 a = load8_bf16(Ud + static_cast<int64_t>(32 * ct + r) * r_D, jj, r_D, ga);
+      acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[ct], 0, 0, 0);
+    }
+  }
+  const int64_t part = static_cast<int64_t>(H) * D * r_Tp;
+  const int KS = r_Tp / 16, ks = k >> 4, fl = ((k >> 3) & 1) * 32, e = k & 7;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int64_t fb = ((static_cast<int64_t>(h) * 4 + ct) * KS + ks) * 512 + e;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int dr = (i >> 2) * 8 + half * 4 + (i & 3);     // feature 32 ct + dr
+      uint16_t hb, mb, lb;
+      split3(acc[ct][i], hb, mb, lb);
+      const int64_t off = fb + (fl + dr) * 8;
+      out[off] = hb;
+      out[part + off] = mb;
+      out[2 * part + off] = lb;
+    }
+  }
+}
+
+// One workgroup (4 waves) per 64-row tile of one head.
+//  1. recon = U~_T[t0 .. t0+64) W_h: wave w computes features [32w, 32w+32)
+//     of both 32-row blocks.  U~_T is staged in LDS in chunks of 64 values
+//     of k (whole 128-byte rows of the chunk, double-buffered, shared by the
+//     waves); the W parts stream from memory in fragment order, two k steps
+//     ahead; hi x hi in one accumulator, the rest in another.
+//  2. recon is staged in LDS; thread (m, g) = (tid / 4, tid % 4) takes its
+//     32 features of group g of row m, forms R = X - recon and stores R's
+//     three bf16 parts in LDS as [part][row][feature].
+//  3. Y = R Q^T with A = the R parts from LDS and B = the Q parts (bf16, in
+//     fragment order like W, in cache), six products per step (hi hi,
+//     hi mid, mid hi, hi lo, lo hi, mid mid).
+//  4. Y is staged in LDS and thread (m, g) quantizes group g of row m.
+constexpr int ER = 64;                         // rows per workgroup
+constexpr int EYS = 144;                       // fp32 row stride of staged recon / Y (group g at 36 g)
+constexpr int ERS = 136;                       // bf16 row stride of the staged R parts
+constexpr int kEncLds = 3 * ER * ERS * 2;      // 52224 bytes >= ER * EYS * 4
+constexpr int EUC = 64;                        // k per staged U~_T chunk
+constexpr int EUS = EUC + 8;                   // bf16 row stride of a staged U~_T chunk
+static_assert(2 * ER * EUS * 2 <= kEncLds, "U~_T chunks fit the staging area");
+
+// UV: rows of U~_T are 16-byte aligned (r_T % 8 == 0 and an aligned base), so
+// a chunk is read with 16-byte loads; otherwise element by element.
+template <typename TX, bool UV>
+__device__ __forceinline__ void encode_tile(const EncodeArgs& a, float* lds_f) {
+  float* st = lds_f;                                          // recon, then Y
+  uint16_t* rp = reinterpret_cast<uint16_t*>(lds_f);          // R parts
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, half = lane >> 5;
+  const int64_t h = blockIdx.y, t0 = static_cast<int64_t>(blockIdx.x) * ER;
+  const int col = wave * 32 + rl;
+  const int qm = tid >> 2, qg = tid & 3;
+  const int64_t qt = t0 + qm;
+  const bool qvalid = qt < a.T;
+  // 1. reconstruction
+  f32x16 hi0 = {}, hi1 = {}, lo0 = {}, lo1 = {};
+  if (a.r_T > 0) {
+    const int64_t rT = a.r_T;
+    const int KS = static_cast<int>(a.r_Tp / 16);
+    const int64_t part = a.H * D * a.r_Tp;
+    const uint16_t* wb = a.W3 + ((h * 4 + wave) * KS) * 512 + lane * 8;
+    // U~_T chunk loader: row ur = tid / 4, k = 16 (tid % 4) .. +16 of the chunk
+    const int ur = tid >> 2, uk = 16 * (tid & 3);
+    const int64_t ut = t0 + ur;
+    const bool urv = ut < a.T;
+    const uint16_t* urow = a.Ut + (urv ? ut : 0) * rT;      // rows past T read row 0, then zero
+    uint4 ru[2];
+    bool uok[2];
+    // branch-free: out-of-range loads read a valid address and are zeroed by a
+    // select when stored (so the loads stay in flight until then)
+    auto load_u = [&](int64_t k0) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int64_t k = k0 + uk + 8 * q;
+        if constexpr (UV) {
+          uok[q] = urv && k < rT;
+          ru[q] = ldg16(urow + (uok[q] ? k : 0));
+        } else {
+          uok[q] = true;
+          uint32_t v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const bool ok = urv && k + e < rT;
+            const uint32_t b = ldg_u16(urow + (ok ? k + e : 0));
+            v[e] = ok ? b : 0u;
+          }
+          ru[q] = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+        }
+      }
+    };
+    auto store_u = [&](int buf) {
+      uint16_t* dst = rp + (buf * ER + ur) * EUS + uk;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {     // a mask per word (a select of uint4 values goes through memory)
+        const uint32_t m = uok[q] ? ~0u : 0u;
+        *reinterpret_cast<uint4*>(dst + 8 * q) = make_uint4(ru[q].x & m, ru[q].y & m, ru[q].z & m, ru[q].w & m);
+      }
+    };
+    const int nks = KS;                            // a multiple of 4 (r_Tp of the encoder: 64 k)
+    // W fragments in a ring of four k steps, loaded two steps ahead (a slot
+    // is refilled only after its step's products are issued)
+    uint4 wf[4][3];
+    auto load_w = [&](int slot, int ks) {         // steps past the end reload the last one (unused)
+      const uint16_t* src = wb + static_cast<int64_t>(ks < nks ? ks : nks - 1) * 512;
+      wf[slot][0] = ldg16(src);
+      wf[slot][1] = ldg16(src + part);
+      wf[slot][2] = ldg16(src + 2 * part);
+    };
+    load_u(0);
+    load_w(0, 0);
+    load_w(1, 1);
+    store_u(0);
+    __syncthreads();
+    for (int c0 = 0; c0 < nks; c0 += EUC / 16) {   // every chunk holds EUC / 16 whole k steps
+      const int buf = (c0 / (EUC / 16)) & 1;
+      const bool more = c0 + EUC / 16 < nks;
+      if (more) load_u(static_cast<int64_t>(c0) * 16 + EUC);
+      const uint16_t* ua = rp + (buf * ER + rl) * EUS + 8 * half;
+#pragma unroll
+      for (int s4 = 0; s4 < EUC / 16; ++s4) {
+        const int ks = c0 + s4;
+        {                                             // ks % 4 == s4: chunks start at multiples of 4
+          const bf16x8 bh = as_bf16x8(wf[s4][0]), bm = as_bf16x8(wf[s4][1]), bl = as_bf16x8(wf[s4][2]);
+          load_w((s4 + 2) & 3, ks + 2);
+          const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const uint4*>(ua + 16 * s4));
+          const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const uint4*>(ua + 32 * EUS + 16 * s4));
+          hi0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bh, hi0, 0, 0, 0);
+          hi1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bh, hi1, 0, 0, 0);
+          lo0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bm, lo0, 0, 0, 0);
+          lo1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bm, lo1, 0, 0, 0);
+          lo0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bl, lo0, 0, 0, 0);
+          lo1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bl, lo1, 0, 0, 0);
+        }
+      }
+      if (more) store_u(buf ^ 1);
+      __syncthreads();
+    }
+  }
+  // this thread's 32 X values (row qt, features 32 qg ..)
+  float x[32];
+  {
+    // rows past T read row 0 and are zeroed below (no divergent loads)
+    const int64_t base = (h * a.T + (qvalid ? qt : 0)) * D + 32 * qg;
+    const TX* src = static_cast<const TX*>(a.X) + base;
+    const bool xv = (reinterpret_cast<uintptr_t>(a.X) & 15) == 0;
+    if constexpr (sizeof(TX) == 2) {
+      if (xv) {
+        uint4 raw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) raw[q] = ldg16(src + 8 * q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t wv[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[8 * q + 2 * e] = __uint_as_float(wv[e] << 16);
+            x[8 * q + 2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) x[c] = bf16_bits_to_f32(ldg_u16(src + c));
+      }
+    } else {
+      if (xv) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint4 v = ldg16(src + 4 * q);
+          x[4 * q] = __uint_as_float(v.x); x[4 * q + 1] = __uint_as_float(v.y);
+          x[4 * q + 2] = __uint_as_float(v.z); x[4 * q + 3] = __uint_as_float(v.w);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) x[c] = __uint_as_float(ldg32(src + c));
+      }
+    }
+  }
+  if (!qvalid) {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) x[c] = 0.f;
+  }
+  if (a.r_T > 0) {
+    // 2. stage recon; thread (m, g) forms its part of R
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = (i >> 2) * 8 + half * 4 + (i & 3);
+      st[m * EYS + wave * 36 + rl] = hi0[i] + lo0[i];
+      st[(32 + m) * EYS + wave * 36 + rl] = hi1[i] + lo1[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(st + qm * EYS + qg * 36 + 4 * q);
+      x[4 * q] -= v.x; x[4 * q + 1] -= v.y; x[4 * q + 2] -= v.z; x[4 * q + 3] -= v.w;
+    }
+    __syncthreads();                              // the R parts overwrite the staged recon
+  }
+  {
+    uint32_t wh[16], wm[16], wl[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      uint16_t h0, m0, l0, h1, m1, l1;
+      split3(x[2 * e], h0, m0, l0);
+      split3(x[2 * e + 1], h1, m1, l1);
+      wh[e] = h0 | (static_cast<uint32_t>(h1) << 16);
+      wm[e] = m0 | (static_cast<uint32_t>(m1) << 16);
+      wl[e] = l0 | (static_cast<uint32_t>(l1) << 16);
+    }
+    uint16_t* row = rp + qm * ERS + 32 * qg;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<uint4*>(row + 8 * q) = make_uint4(wh[4 * q], wh[4 * q + 1], wh[4 * q + 2], wh[4 * q + 3]);
+      *reinterpret_cast<uint4*>(row + ER * ERS + 8 * q) =
+          make_uint4(wm[4 * q], wm[4 * q + 1], wm[4 * q + 2], wm[4 * q + 3]);
+      *reinterpret_cast<uint4*>(row + 2 * ER * ERS + 8 * q) =
+          make_uint4(wl[4 * q], wl[4 * q + 1], wl[4 * q + 2], wl[4 * q + 3]);
+    }
+  }
+  __syncthreads();
+  // 3. rotation
+  f32x16 yh0 = {}, yh1 = {}, yl0 = {}, yl1 = {};
+  {
+    // Q parts in fragment order: [p][cb][ds][lane][e] = part p of Q[32 cb + r][16 ds + 8 half + e]
+    const uint16_t* qb = a.Q3 + wave * (D / 16) * 512 + lane * 8;
+    uint4 qf[4][3];                               // ring of four d steps, two ahead
+    auto load_q = [&](int slot, int ds) {
+      if (ds < D / 16) {
+        const uint16_t* src = qb + ds * 512;
+        qf[slot][0] = ldg16(src);
+        qf[slot][1] = ldg16(src + D * D);
+        qf[slot][2] = ldg16(src + 2 * D * D);
+      }
+    };
+    load_q(0, 0);
+    load_q(1, 1);
+    const uint16_t* ra = rp + rl * ERS + 8 * half;
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      const int d0 = 16 * ds, slot = ds & 3;
+      const bf16x8 qh = as_bf16x8(qf[slot][0]), qm_ = as_bf16x8(qf[slot][1]), ql = as_bf16x8(qf[slot][2]);
+      load_q((ds + 2) & 3, ds + 2);
+      const bf16x8 h0 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + d0));
+      const bf16x8 h1 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + 32 * ERS + d0));
+      const bf16x8 m0 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + ER * ERS + d0));
+      const bf16x8 m1 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + (ER + 32) * ERS + d0));
+      const bf16x8 l0 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + 2 * ER * ERS + d0));
+      const bf16x8 l1 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + (2 * ER + 32) * ERS + d0));
+      yh0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, qh, yh0, 0, 0, 0);
+      yh1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, qh, yh1, 0, 0, 0);
+      yl0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, qm_, yl0, 0, 0, 0);
+      yl1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, qm_, yl1, 0, 0, 0);
+      yl0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(m0, qh, yl0, 0, 0, 0);
+      yl1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(m1, qh, yl1, 0, 0, 0);
+      yl0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, ql, yl0, 0, 0, 0);
+      yl1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, ql, yl1, 0, 0, 0);
+      yl0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l0, qh, yl0, 0, 0, 0);
+      yl1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l1, qh, yl1, 0, 0, 0);
+      yl0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(m0, qm_, yl0, 0, 0, 0);
+      yl1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(m1, qm_, yl1, 0, 0, 0);
+    }
+  }
+  __syncthreads();                                // Y overwrites the R parts
+  // 4. stage Y; thread (m, g) quantizes group g of row m
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m = (i >> 2) * 8 + half * 4 + (i & 3);
+    st[m * EYS + wave * 36 + rl] = yh0[i] + yl0[i];
+    st[(32 + m) * EYS + wave * 36 + rl] = yh1[i] + yl1[i];
+  }
+  __syncthreads();
+  float y[32];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float4 v = *reinterpret_cast<const float4*>(st + qm * EYS + qg * 36 + 4 * q);
+    y[4 * q] = v.x; y[4 * q + 1] = v.y; y[4 * q + 2] = v.z; y[4 * q + 3] = v.w;
+  }
+  const int64_t gi = (h * a.T + qt) * 4 + qg;
+  quantize_any(y, a.bits, qvalid, reinterpret_cast<uint32_t*>(a.scales) + gi,
+               reinterpret_cast<uint32_t*>(a.codes) + gi * a.bits);
+}
+
+template <typename TX>
+__device__ __forceinline__ void encode_any(const EncodeArgs& a) {
+  __shared__ __attribute__((aligned(16))) float lds_f[kEncLds / 4];
+  if (a.r_T % 8 == 0 && (reinterpret_cast<uintptr_t>(a.Ut) & 15) == 0) encode_tile<TX, true>(a, lds_f);
+  else encode_tile<TX, false>(a, lds_f);
+}
+template <typename TX>
+__global__ __launch_bounds__(256, 3) void k_encode_residual(EncodeArgs a) {
+  encode_any<TX>(a);
+}
+// Tensors of one shape in one launch: blockIdx.z selects the tensor's arguments.
+template <typename TX>
+__global__ __launch_bounds__(256, 3) void k_encode_residual_many(const EncodeArgs* list) {
+  const EncodeArgs a = list[blockIdx.z];
+  encode_any<TX>(a);
+}
+
+// ------------------------------------------------------------------ decode
+// bf16 matrix cores (32x32x16, fp32 accumulate).  Stored factors and core are
+// bf16, so U~_T x W is exact per product once W = G~_h U~_D^T is carried as a
+// hi + lo pair of bf16 (relative error 2^-17); the dequantized residual and Q
+// enter in bf16 (relative 2^-9 each, far below the quantization error they
+// ride on).  Every MFMA operand is one 16-byte load per lane: lane l holds
+// row l%32 and k = 8*(l/32) .. +8 of A, column l%32 and the same k of B.
 
 // W_h^T = (G~_h U~_D^T)^T as bf16 hi + lo, [h][d][k] with row stride r_Tp.
 // One wave per (record, head, 32 rows of r_T).
@@ -453,8 +660,19 @@ __global__ void k_header(uint32_t* blob, uint32_t w0, uint32_t w1, uint32_t w2, 
 hipError_t launch_quantize(const float* Y, int64_t rows, int bits, uint16_t* scales, uint8_t* codes,
                            hipStream_t s) {
   const int64_t ng = rows * (D / 32);
-  k_quantize<<<(ng + 7) / 8, 256, 0, s>>>(Y, ng, bits, reinterpret_cast<uint32_t*>(scales),
-                                          reinterpret_cast<uint32_t*>(codes));
+  if (ng == 0) return hipSuccess;
+  k_quantize<<<(ng + 255) / 256, 256, 0, s>>>(Y, ng, bits, reinterpret_cast<uint32_t*>(scales),
+                                              reinterpret_cast<uint32_t*>(codes));
+  return hipGetLastError();
+}
+
+hipError_t launch_enc_w(const uint16_t* const* Gp, const uint16_t* const* Udp, const uint16_t* G0,
+                        const uint16_t* Ud0, uint16_t* W3, int64_t w3_batch, int n, int H, int r_T, int r_D,
+                        int r_Tp, hipStream_t s) {
+  if (n <= 0 || r_T <= 0) return hipSuccess;
+  if (r_Tp % 64 != 0 || r_Tp < r_T) return hipErrorInvalidValue;
+  ProfScope ps("encode_w", s);
+  k_enc_w<<<dim3(r_Tp / 32, H, n), 64, 0, s>>>(Gp, Udp, G0, Ud0, W3, w3_batch, H, r_T, r_D, r_Tp);
   return hipGetLastError();
 }
 

@@ -41,6 +41,24 @@ __device__ __forceinline__ uint16_t bf16_round_up(float f) {
   return static_cast<uint16_t>(hi);
 }
 
+// 16-byte load and store through the global address space: global_load /
+// global_store are counted by vmcnt alone, while the flat instructions that a
+// generic pointer gives also count in lgkmcnt, so an LDS wait would hold on
+// them too.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+  // a plain vector type: copying HIP's uint4 struct would go through a generic reference
+  const u32x4 v = *(const __attribute__((address_space(1))) u32x4*)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ldg32(const void* p) {
+  return *(const __attribute__((address_space(1))) uint32_t*)(p);
+}
+__device__ __forceinline__ uint16_t ldg_u16(const void* p) {
+  return *(const __attribute__((address_space(1))) uint16_t*)(p);
+}
+__device__ __forceinline__ void stg32(void* p, uint32_t v) { *(__attribute__((address_space(1))) uint32_t*)(p) = v; }
+
 template <typename T> __device__ __forceinline__ float load_as_f32(const T* p, int64_t i);
 template <> __device__ __forceinline__ float load_as_f32<float>(const float* p, int64_t i) { return p[i]; }
 template <> __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, int64_t i) {

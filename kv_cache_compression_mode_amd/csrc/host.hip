@@ -898,6 +898,8 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
 }
 
 int64_t rtp_of(int r_T) { return (static_cast<int64_t>(r_T) + 31) / 32 * 32; }
+// the encoder's W parts: k padded to whole 64-value chunks
+int64_t enc_rtp(int r_T) { return (static_cast<int64_t>(r_T) + 63) / 64 * 64; }
 
 size_t decode_ws_one(const jolt_shape* s, jolt_choice c) {
   if (c.r_T == 0) return 0;
@@ -991,7 +993,7 @@ EncManyLayout enc_many_layout(int n, const jolt_shape* shape, const jolt_choice*
     const size_t m = e - b, rT = ch[idx[b]].r_T;
     L.groups.emplace_back(static_cast<int>(b), static_cast<int>(e));
     L.w_off.push_back(off);
-    off += a256(4ull * m * H * rT * D);
+    off += a256(6ull * m * H * D * enc_rtp(static_cast<int>(rT)));
     L.p_off.push_back(off);
     off += a256(4ull * m * rT * HD);
     L.part_off.push_back(off);
@@ -1029,7 +1031,7 @@ int32_t jolt_spectrum_len(const jolt_alloc_req* req) {
 size_t jolt_encode_workspace_bytes(const jolt_shape* shape, jolt_choice c) {
   if (!shape_ok(shape) || !choice_ok(shape, c)) return 0;
   const size_t w = a256(4ull * shape->H * c.r_T * shape->D);
-  return 2 * w + a256(w * encode_ksplit(shape->T)) + 256;
+  return a256(6ull * shape->H * shape->D * enc_rtp(c.r_T)) + w + a256(w * encode_ksplit(shape->T)) + 256;
 }
 
 size_t jolt_decode_workspace_bytes(const jolt_shape* shape, jolt_choice c) {
@@ -1049,7 +1051,7 @@ size_t jolt_decode_many_workspace_bytes(int32_t n, const jolt_shape* shape, cons
 
 size_t jolt_rotation_bytes(int32_t D) {
   if (D != kD) return 0;
-  return a256(4ull * D * D) * 2 + a256(2ull * D * D);
+  return a256(4ull * D * D) * 2 + a256(2ull * D * D) + a256(6ull * D * D);
 }
 
 jolt_status jolt_plan_from_spectra(const jolt_alloc_req* req, const double* spectra_T, int32_t len_T,
@@ -1092,11 +1094,42 @@ jolt_status jolt_rotation(uint64_t seed, int32_t D, void* q_dev, size_t q_bytes,
       u += 0x7fffu + ((u >> 16) & 1u);
       b16[c * D + r] = static_cast<uint16_t>(u >> 16);
     }
+    // exact three-part bf16 split of the fp32 Q: hi = rne(f), mid = rne(f - hi),
+    // lo = f - hi - mid (a bf16 value), stored in matrix-core fragment order
+    // [part][cb][ds][lane][e] = part of Q[32 cb + lane % 32][16 ds + 8 (lane / 32) + e]
+    std::vector<uint16_t> q3(3 * n);
+    auto rne = [](float f) {
+      uint32_t u;
+      std::memcpy(&u, &f, 4);
+      u += 0x7fffu + ((u >> 16) & 1u);
+      return static_cast<uint16_t>(u >> 16);
+    };
+    auto widen = [](uint16_t b) {
+      const uint32_t u = static_cast<uint32_t>(b) << 16;
+      float f;
+      std::memcpy(&f, &u, 4);
+      return f;
+    };
+    for (size_t i = 0; i < n; ++i) {
+      const size_t c = i / D, d = i % D;               // buf[i] = Q[c][d]
+      const size_t o = ((c / 32 * (D / 16) + d / 16) * 64 + (d / 8 % 2) * 32 + c % 32) * 8 + d % 8;
+      const float f = buf[i];
+      const uint16_t h = rne(f);
+      const float r1 = f - widen(h);
+      const uint16_t m = rne(r1);
+      const float r2 = r1 - widen(m);
+      uint32_t u;
+      std::memcpy(&u, &r2, 4);
+      q3[o] = h;
+      q3[n + o] = m;
+      q3[2 * n + o] = static_cast<uint16_t>(u >> 16);
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* base = static_cast<char*>(q_dev);
     ck(hipMemcpyAsync(base, buf.data(), 4 * n, hipMemcpyHostToDevice, s));
     ck(hipMemcpyAsync(base + a256(4 * n), buf.data() + n, 4 * n, hipMemcpyHostToDevice, s));
     ck(hipMemcpyAsync(base + 2 * a256(4 * n), b16.data(), 2 * n, hipMemcpyHostToDevice, s));
+    ck(hipMemcpyAsync(base + 2 * a256(4 * n) + a256(2 * n), q3.data(), 6 * n, hipMemcpyHostToDevice, s));
     ck(hipStreamSynchronize(s));
     return JOLT_OK;
   });
@@ -1201,10 +1234,12 @@ jolt_status jolt_encode(const jolt_shape* shape, const void* x_dev, jolt_choice 
     uint16_t* Ut = reinterpret_cast<uint16_t*>(blob + L.ut);
     uint16_t* Ud = reinterpret_cast<uint16_t*>(blob + L.ud);
     uint16_t* G = reinterpret_cast<uint16_t*>(blob + L.g);
-    float* W = static_cast<float*>(ws_dev);
-    float* P = W + a256(4ull * H * rT * D) / 4;
+    const int64_t rTp = enc_rtp(c.r_T);
+    uint16_t* W3 = static_cast<uint16_t*>(ws_dev);
+    float* P = reinterpret_cast<float*>(static_cast<char*>(ws_dev) + a256(6ull * H * D * rTp));
     const size_t n = static_cast<size_t>(D) * D;
-    const float* Qt = reinterpret_cast<const float*>(static_cast<const char*>(rot_dev) + a256(4 * n));
+    const uint16_t* Q3 = reinterpret_cast<const uint16_t*>(static_cast<const char*>(rot_dev) + 2 * a256(4 * n) +
+                                                           a256(2 * n));
     if (tucker) {
       ck(launch_to_bf16(U_T_dev, ld_T, Ut, T, rT, s));
       ck(launch_to_bf16(U_D_dev, ld_D, Ud, D, rD, s));
@@ -1224,17 +1259,14 @@ jolt_status jolt_encode(const jolt_shape* shape, const void* x_dev, jolt_choice 
       g2.B = Ud; g2.b_dtype = kBF16; g2.bk = plain(rD); g2.bn = plain(1); g2.b_batch = 0;
       g2.C = G; g2.c_dtype = kBF16; g2.c_m = rD; g2.c_n = 1; g2.c_batch = rT * rD;
       ck(launch_gemm(g2, static_cast<int>(H), s));
-      GemmArgs g3 = gemm0();                     // W_h = G~_h U~_D^T  (r_T x D)
-      g3.M = rT; g3.N = D; g3.K = rD;
-      g3.A = G; g3.a_dtype = kBF16; g3.am = plain(rD); g3.ak = plain(1); g3.a_batch = rT * rD;
-      g3.B = Ud; g3.b_dtype = kBF16; g3.bk = plain(1); g3.bn = plain(rD); g3.b_batch = 0;
-      g3.C = W; g3.c_m = D; g3.c_n = 1; g3.c_batch = rT * D;
-      ck(launch_gemm(g3, static_cast<int>(H), s));
+      // W_h = G~_h U~_D^T in three bf16 parts, [part][h][d][k]
+      ck(launch_enc_w(nullptr, nullptr, G, Ud, W3, 0, 1, static_cast<int>(H), static_cast<int>(rT),
+                      static_cast<int>(rD), static_cast<int>(rTp), s));
     }
     EncodeArgs ea{};
     ea.X = x_dev; ea.x_dtype = xdt; ea.H = H; ea.T = T;
-    ea.Ut = tucker ? Ut : nullptr; ea.W = W; ea.r_T = rT;
-    ea.Qt = Qt; ea.bits = c.bits;
+    ea.Ut = tucker ? Ut : nullptr; ea.W3 = tucker ? W3 : nullptr; ea.r_T = rT; ea.r_Tp = tucker ? rTp : 0;
+    ea.Q3 = Q3; ea.bits = c.bits;
     ea.scales = reinterpret_cast<uint16_t*>(blob + L.sc);
     ea.codes = reinterpret_cast<uint8_t*>(blob + L.cd);
     ck(launch_encode_residual(ea, s));
@@ -1279,7 +1311,8 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
     const int xdt = shape->dtype == JOLT_BF16 ? kBF16 : kF32;
     char* ws = static_cast<char*>(ws_dev);
     const size_t nq = static_cast<size_t>(D) * D;
-    const float* Qt = reinterpret_cast<const float*>(static_cast<const char*>(rot_dev) + a256(4 * nq));
+    const uint16_t* Q3 = reinterpret_cast<const uint16_t*>(static_cast<const char*>(rot_dev) + 2 * a256(4 * nq) +
+                                                           a256(2 * nq));
     bool al16 = true;
     for (int i = 0; i < n; ++i)
       al16 = al16 && (reinterpret_cast<uintptr_t>(x_dev[i]) & 15) == 0 && (reinterpret_cast<uintptr_t>(blob_dev[i]) & 15) == 0;
@@ -1296,7 +1329,7 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
     auto slots = [&](size_t k) { const size_t o = np; np += k; return o; };
     struct GroupPtrs { size_t ut_in, ut_out, ud_in, ud_out, pa, pb, g2a, g2b, g2c, g3a, g3b; };
     std::vector<GroupPtrs> gp(L.groups.size());
-    std::vector<float*> Wslot(n, nullptr);
+    std::vector<uint16_t*> Wslot(n, nullptr);
     for (size_t g = 0; g < L.groups.size(); ++g) {
       const int b0 = L.groups[g].first, e0 = L.groups[g].second, m = e0 - b0;
       const jolt_choice c = choices[L.order[b0]];
@@ -1307,7 +1340,8 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
       q.g2a = slots(m * H); q.g2b = slots(m * H); q.g2c = slots(m * H);
       q.g3a = slots(m * H); q.g3b = slots(m * H);
       float* P = reinterpret_cast<float*>(ws + L.p_off[g]);
-      float* W = reinterpret_cast<float*>(ws + L.w_off[g]);
+      uint16_t* W = reinterpret_cast<uint16_t*>(ws + L.w_off[g]);
+      const int64_t rTp = enc_rtp(static_cast<int>(rT));
       for (int j = 0; j < m; ++j) {
         const int i = L.order[b0 + j];
         const BlobLayout B = lay(i);
@@ -1325,7 +1359,7 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
           ptr[q.g3a + k] = blob(i) + B.g + 2ull * h * rT * rD;
           ptr[q.g3b + k] = blob(i) + B.ud;
         }
-        Wslot[i] = W + static_cast<size_t>(j) * H * rT * D;
+        Wslot[i] = W + static_cast<size_t>(j) * 3 * H * D * rTp;
       }
     }
     const size_t blob_slot = slots(n);
@@ -1337,8 +1371,8 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
       ea = EncodeArgs{};
       ea.X = x_dev[i]; ea.x_dtype = xdt; ea.H = H; ea.T = T;
       ea.Ut = c.r_T > 0 ? reinterpret_cast<const uint16_t*>(blob(i) + B.ut) : nullptr;
-      ea.W = Wslot[i]; ea.r_T = c.r_T;
-      ea.Qt = Qt; ea.bits = c.bits;
+      ea.W3 = Wslot[i]; ea.r_T = c.r_T; ea.r_Tp = c.r_T > 0 ? enc_rtp(c.r_T) : 0;
+      ea.Q3 = Q3; ea.bits = c.bits;
       ea.scales = reinterpret_cast<uint16_t*>(blob(i) + B.sc);
       ea.codes = reinterpret_cast<uint8_t*>(blob(i) + B.cd);
       const uint32_t hdr[16] = {kMagic, kVersion, static_cast<uint32_t>(H), static_cast<uint32_t>(T),
@@ -1400,15 +1434,12 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
       g2.c_ptrs = reinterpret_cast<void* const*>(dp(q.g2c)); g2.c_dtype = kBF16; g2.c_m = rD; g2.c_n = 1;
       g2.ptr_align16 = al16 ? 1 : 0;
       ck(launch_gemm(g2, static_cast<int>(m * H), s));
-      GemmArgs g3 = gemm0();                    // W_h = G~_h U~_D^T per (tensor, head)
-      g3.M = rT; g3.N = D; g3.K = rD;
-      g3.a_ptrs = reinterpret_cast<const void* const*>(dp(q.g3a)); g3.a_dtype = kBF16;
-      g3.am = plain(rD); g3.ak = plain(1);
-      g3.b_ptrs = reinterpret_cast<const void* const*>(dp(q.g3b)); g3.b_dtype = kBF16;
-      g3.bk = plain(1); g3.bn = plain(rD);
-      g3.C = ws + L.w_off[g]; g3.c_m = D; g3.c_n = 1; g3.c_batch = rT * D;
-      g3.ptr_align16 = al16 ? 1 : 0;
-      ck(launch_gemm(g3, static_cast<int>(m * H), s));
+      // W_h = G~_h U~_D^T per (tensor, head), in three bf16 parts
+      const int64_t rTp = enc_rtp(static_cast<int>(rT));
+      ck(launch_enc_w(reinterpret_cast<const uint16_t* const*>(dp(q.g3a)),
+                      reinterpret_cast<const uint16_t* const*>(dp(q.g3b)), nullptr, nullptr,
+                      reinterpret_cast<uint16_t*>(ws + L.w_off[g]), 3 * H * D * rTp, m, static_cast<int>(H),
+                      static_cast<int>(rT), static_cast<int>(rD), static_cast<int>(rTp), s));
     }
     ck(launch_encode_residual_many(dargs, n, H, T, xdt, s));
     ck(launch_write_headers(reinterpret_cast<uint32_t* const*>(dp(blob_slot)), dwords, n, s));

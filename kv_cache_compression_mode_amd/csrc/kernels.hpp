@@ -138,13 +138,21 @@ hipError_t finalize_factor_ws(const float* U_cm, int64_t m, int64_t R, int64_t l
 // ---- codec ----
 hipError_t launch_quantize(const float* Y, int64_t rows, int bits, uint16_t* scales, uint8_t* codes,
                            hipStream_t s);
+// W_h = G~_h U~_D^T (D = 128) as three bf16 parts in matrix-core fragment
+// order, W3[p][h][d / 32][k / 16][32 ((k / 8) % 2) + d % 32][k % 8] (k < r_Tp,
+// zero for k >= r_T; r_Tp a multiple of 64), of n tensors: tensor j reads G~_h from Gp[j H + h] and
+// U~_D from Udp[j H + h] (G0 + h r_T r_D and Ud0 when Gp is null) and writes
+// W3 + j w3_batch.  r_Tp is a multiple of 32.
+hipError_t launch_enc_w(const uint16_t* const* Gp, const uint16_t* const* Udp, const uint16_t* G0,
+                        const uint16_t* Ud0, uint16_t* W3, int64_t w3_batch, int n, int H, int r_T, int r_D,
+                        int r_Tp, hipStream_t s);
 // Fused residual -> rotation -> quantization for one tensor (D = 128).
 struct EncodeArgs {
   const void* X; int x_dtype; int64_t H, T;
   const uint16_t* Ut;  // bf16 [T][r_T] (NULL when r_T == 0)
-  const float* W;      // fp32 [H][r_T][128] = G~_h U~_D^T
-  int64_t r_T;
-  const float* Qt;     // fp32 [128][128], Qt[d][c] = Q[c][d]
+  const uint16_t* W3;  // bf16 parts of W_h in fragment order (launch_enc_w)
+  int64_t r_T, r_Tp;
+  const uint16_t* Q3;  // bf16 parts of Q in fragment order, [3][c / 32][d / 16][32 ((d / 8) % 2) + c % 32][d % 8]
   int bits;
   uint16_t* scales;    // [H][T][4][2]
   uint8_t* codes;      // [H][T][4][4*bits]

@@ -96,12 +96,29 @@ def sample_rows(H: int, T: int, n: int, seed: int = 0):
     return hs.astype(np.int64), ts.astype(np.int64)
 
 
+def residual_bound_factors(r_T: int, r_D: int, D: int):
+    """(g_R, g_Y): the kernel's error bounds |d recon| <= g_R |U~_T||G~_h||U~_D|^T
+    and |dY| <= |dR||Q|^T + g_Y |R||Q|^T, in units of 2^-24.
+
+    The encoder forms W_h = G~_h U~_D^T with r_D fp32 additions of exact bf16
+    products, splits fp32 operands exactly into bf16 parts hi + mid + lo
+    (|mid| <= 2^-9 (1 + 2^-8) |f|, |lo| <= 2^-18 |f|) and accumulates in fp32:
+    recon = U~_T hi (r_T terms) + U~_T (mid + lo) (2 r_T terms of total size
+    <= 2^-8 of the first), then one addition -> r_D + r_T + r_T/256 + 1
+    (+ slack); Y = R_hi Q_hi (D terms) + five cross products (5 D terms of
+    total size <= 2^-8) + dropped mid x lo, lo x mid, lo x lo (<= 2^-26) + one
+    addition + the fp32 rounding of Q -> D + 2.5 + 0.25 + 1 + 1.  Bounds:
+    (1 + 2^-5) r_T + r_D + 4 and D + 6."""
+    return (1 + 2.0 ** -5) * r_T + r_D + 4, D + 6
+
+
 def oracle_rows(X_rows: np.ndarray, parts: dict, choice, Q: np.ndarray, hs, ts):
     """Y = fp32((X - U~_T G~_h U~_D^T) Q^T) on the rows, and the per-element
     bound on the kernel's fp32 error (as in the whole-tensor check)."""
     r_T, r_D, _ = choice
     Xr = np.asarray(X_rows, dtype=np.float64)
     absQ = np.abs(Q)
+    gR, gY = residual_bound_factors(r_T, r_D, Q.shape[0])
     if r_T > 0:
         Ut = parts["U_T"][ts]                        # [n, r_T]
         G = parts["G"][hs]                           # [n, r_T, r_D]
@@ -109,13 +126,13 @@ def oracle_rows(X_rows: np.ndarray, parts: dict, choice, Q: np.ndarray, hs, ts):
         recon = np.einsum("nr,nrs,ds->nd", Ut, G, Ud, optimize=True)
         terms = np.einsum("nr,nrs,ds->nd", np.abs(Ut), np.abs(G), np.abs(Ud), optimize=True)
         R = Xr - recon
-        bR = (r_T + r_D + 4) * 2.0 ** -24 * terms
+        bR = gR * 2.0 ** -24 * terms
     else:
         R, recon, terms = Xr, 0.0 * Xr, 0.0 * Xr
         bR = np.zeros_like(Xr)
     bR = bR + 2.0 ** -24 * np.abs(Xr)
     Y = (R @ Q.T).astype(np.float32)
-    bY = bR @ absQ.T + (D + 4) * 2.0 ** -24 * (np.abs(R) @ absQ.T)
+    bY = bR @ absQ.T + gY * 2.0 ** -24 * (np.abs(R) @ absQ.T)
     return Y, bY
 
 

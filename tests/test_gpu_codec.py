@@ -15,7 +15,8 @@ import torch
 import kvgen
 from oracle import alloc, bf16, codec, flash, quant, rng, rotation, tucker
 
-from gpu_util import D, check_bf16_rounding, check_codes, max_sine, parse_blob, resolvable_cuts, to_dev
+from gpu_util import (D, check_bf16_rounding, check_codes, max_sine, parse_blob, residual_bound_factors,
+                      resolvable_cuts, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,24 +91,23 @@ def test_quantizer_empty(J):
 
 def _oracle_from_blob(X, parts, choice, Q, H, T):
     """The oracle's residual and rotation applied to the GPU's stored parts,
-    with a per-element bound on the fp32 error of the kernel's Y.
-
-    recon = U~_T (G~_h U~_D^T) with K = r_T + r_D fp32 accumulation steps and
-    Y = R Q^T with K = D steps: |dY| <= (g_R |U~_T||G~_h||U~_D|^T) |Q|^T
-    + g_Y |R| |Q|^T with g = (K + 4) 2^-24 (standard dot-product bounds).
+    with a per-element bound on the fp32 error of the kernel's Y:
+    |dY| <= (g_R |U~_T||G~_h||U~_D|^T + 2^-24 |X|) |Q|^T + g_Y |R| |Q|^T, the
+    factors of the kernel's arithmetic (gpu_util.residual_bound_factors).
     """
     r_T, r_D, _ = choice
     absQ = np.abs(Q)
+    gR, gY = residual_bound_factors(r_T, r_D, D)
     if r_T > 0:
         R = X - tucker.reconstruct(parts["G"], parts["U_T"], parts["U_D"])
-        bR = (r_T + r_D + 4) * 2.0 ** -24 * tucker.reconstruct(np.abs(parts["G"]), np.abs(parts["U_T"]),
-                                                               np.abs(parts["U_D"]))
+        bR = gR * 2.0 ** -24 * tucker.reconstruct(np.abs(parts["G"]), np.abs(parts["U_T"]),
+                                                  np.abs(parts["U_D"]))
     else:
         R = X
         bR = np.zeros_like(X)
     bR = bR + 2.0 ** -24 * np.abs(X)                       # the subtraction X - recon
     Y = (R.reshape(-1, D) @ Q.T).astype(np.float32).reshape(H, T, D)
-    bY = ((bR.reshape(-1, D) @ absQ.T) + (D + 4) * 2.0 ** -24 * (np.abs(R).reshape(-1, D) @ absQ.T))
+    bY = ((bR.reshape(-1, D) @ absQ.T) + gY * 2.0 ** -24 * (np.abs(R).reshape(-1, D) @ absQ.T))
     return Y, bY.reshape(H, T, D)
 
 
