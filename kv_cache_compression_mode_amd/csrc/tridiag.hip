@@ -92,20 +92,24 @@ struct ChaseLds {
 struct ChaseStep {
   int j, s, r0, L, r1, hi;
   bool last;
+  int64_t ref0;                   // index of the sweep's first reflector
 };
 // sweeps of one wave: j = wave, wave + nw, ...; sweep j runs its steps at
 // ticks S j .. S j + steps(j) - 1 (S nw >= steps(0), so they never overlap)
 struct ChaseClock {
   int j, start, K;
+  int64_t ref0;
   __device__ void init(int wave, int S, int n) {
-    j = wave; start = S * j; K = static_cast<int>(sweep_steps(n, j));
+    j = wave; start = S * j; K = static_cast<int>(sweep_steps(n, j)); ref0 = sweep_offset(n, j);
   }
   // the step at tick t (ticks visited in increasing order)
   __device__ bool at(int t, int nw, int S, int n, ChaseStep& g) {
-    if (t - start >= K && K > 0) { j += nw; start = S * j; K = static_cast<int>(sweep_steps(n, j)); }
+    if (t - start >= K && K > 0) {
+      j += nw; start = S * j; K = static_cast<int>(sweep_steps(n, j)); ref0 = sweep_offset(n, j);
+    }
     const int s = t - start;
     if (s < 0 || s >= K) return false;
-    g.j = j; g.s = s; g.last = (s == K - 1);
+    g.j = j; g.s = s; g.last = (s == K - 1); g.ref0 = ref0;
     g.r0 = j + 1 + s * SBW;
     g.L = min(n - g.r0, SBW);
     g.r1 = g.r0 + g.L;
@@ -126,29 +130,55 @@ __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t off, f
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(off), 0, 0);
 }
 
+// row of register ii in a 32x32 fp32 matrix-core accumulator, less 4 (lane / 32)
+__device__ __forceinline__ constexpr int rofs(int ii) { return (ii >> 2) * 8 + (ii & 3); }
+// v(lane l) + v(lane l ^ 32), the same value in both halves: one lane swap of
+// the halves (v_permlane32_swap) instead of a trip through LDS
+__device__ __forceinline__ float half_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);     // lower half's value + upper half's
+}
+// sum of a[i] b[i], i < 16, as four interleaved chains (short dependency chain)
+template <typename A, typename B>
+__device__ __forceinline__ float dot16(const A& a, const B& b) {
+  float s0 = a[0] * b[0], s1 = a[1] * b[1], s2 = a[2] * b[2], s3 = a[3] * b[3];
+#pragma unroll
+  for (int i = 4; i < 16; i += 4) {
+    s0 = fmaf(a[i], b[i], s0);
+    s1 = fmaf(a[i + 1], b[i + 1], s1);
+    s2 = fmaf(a[i + 2], b[i + 2], s2);
+    s3 = fmaf(a[i + 3], b[i + 3], s3);
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void k_chase(float* Bw_g, int n, float* Rf_g, int64_t rf_stride, int S) {
   extern __shared__ float chase_lds_raw[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = lane >> 5, l32 = lane & 31;
+  const int h = lane >> 5, l32 = lane & 31, h4 = 4 * h;
   ChaseLds& sm = reinterpret_cast<ChaseLds*>(chase_lds_raw)[wave];
   float* Bw = Bw_g + static_cast<int64_t>(blockIdx.x) * n * BWS;
   const __amdgpu_buffer_rsrc_t band = __builtin_amdgcn_make_buffer_rsrc(Bw, 0, n * BWS * 4, 0x00020000);
   float* Rf = Rf_g + blockIdx.x * rf_stride;
   const int last = n - 3;
   const int ticks = last >= 0 ? S * last + static_cast<int>(sweep_steps(n, last)) : 0;
-  // byte offsets of this lane's element in row h * 16 of a block; row ii adds 65 floats
+  // Lane (h, l32) holds column l32 of a 32 x 32 block at rows h4 + rofs(ii),
+  // ii < 16: the accumulator layout of the fp32 matrix cores, so the block
+  // updates (rank one or two) are single 32x32x2 products.  Byte offsets of
+  // this lane's element in row h4 of a block; row r adds 65 floats.
   constexpr uint32_t RS = 4 * (BWS + 1);
-  float pd[16], pb[16], px = 0.f;   // next step: diagonal block rows, below block rows, column
+  f32x16 pd;                        // the diagonal block of the next step (used in place)
+  float pb[16], px = 0.f;           // next step: below block rows, the column it annihilates
   auto prefetch = [&](const ChaseStep& q) {
-    const uint32_t od = 4u * static_cast<uint32_t>(q.r0 * BWS + h * 16 * (BWS + 1) - l32);  // (r0 + a, r0 + l32)
+    const uint32_t od = 4u * static_cast<uint32_t>(q.r0 * BWS + h4 * (BWS + 1) - l32);  // (r0 + a, r0 + l32)
 #pragma unroll
-    for (int ii = 0; ii < 16; ++ii) pd[ii] = bload(band, od + ii * RS);
+    for (int ii = 0; ii < 16; ++ii) pd[ii] = bload(band, od + rofs(ii) * RS);
     if (q.r1 < q.hi) {
-      const uint32_t ob = 4u * static_cast<uint32_t>(q.r1 * BWS + h * 16 * (BWS + 1) + q.L - l32);  // (r1 + a, r0 + l32)
+      const uint32_t ob = 4u * static_cast<uint32_t>(q.r1 * BWS + h4 * (BWS + 1) + q.L - l32);  // (r1 + a, r0 + l32)
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) pb[ii] = bload(band, ob + ii * RS);
+      for (int ii = 0; ii < 16; ++ii) pb[ii] = bload(band, ob + rofs(ii) * RS);
     } else {
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) pb[ii] = 0.f;
@@ -188,19 +218,16 @@ __global__ __launch_bounds__(NW * 64) void k_chase(float* Bw_g, int n, float* Rf
     const bool actn = ckn.at(t + 1, NW, S, n, gn);
     float* Lt = sm.tile[cur];
     float* Ft = sm.tile[cur ^ 1];
-    float dcur[16];
     if (act) {
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) {
-        dcur[ii] = pd[ii];
-        Ft[(h * 16 + ii) * TLD + l32] = pb[ii];     // below block, row-major
-      }
+      for (int ii = 0; ii < 16; ++ii) Ft[(h4 + rofs(ii)) * TLD + l32] = pb[ii];   // below block, row-major
       if (g.s == 0 && lane < SBW) sm.x[lane] = px;
     }
-    if (actn) {
-      if (t > 0) wait_pred(t - 1);
-      prefetch(gn);
-    }
+    // the next step's loads are issued once this step has used the diagonal
+    // block (pd), just before the block below; the step's values and the
+    // wait that orders them are as before
+    float tau = 0.f, vo = 0.f;
+    float vh[16];
     if (act) {
       const int L = g.L, r0 = g.r0;
       wave_lds_sync();
@@ -208,28 +235,34 @@ __global__ __launch_bounds__(NW * 64) void k_chase(float* Bw_g, int n, float* Rf
       float xh[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 x4 = *reinterpret_cast<const float4*>(&sm.x[h * 16 + 4 * q4]);
+        const float4 x4 = *reinterpret_cast<const float4*>(&sm.x[8 * q4 + h4]);   // rows h4 + rofs(4 q4 ..)
         xh[4 * q4] = x4.x; xh[4 * q4 + 1] = x4.y; xh[4 * q4 + 2] = x4.z; xh[4 * q4 + 3] = x4.w;
       }
       const float xo = sm.x[l32];
       const float alpha = sm.x[0];
-      float sig = h ? xh[0] * xh[0] : 0.f;
-#pragma unroll
-      for (int ii = 1; ii < 16; ++ii) sig += xh[ii] * xh[ii];
-      sig += __shfl_xor(sig, 32);                  // same sum in both halves (commutative)
-      float tau = 0.f, beta = alpha, scale = 0.f;
+      const float x0 = xh[0];
+      xh[0] = h ? x0 : 0.f;                        // row 0 (alpha) is not in sigma
+      float sig = dot16(xh, xh);
+      xh[0] = x0;
+      sig = half_sum(sig);
+      float beta = alpha, scale = 0.f;
       if (sig > 0.f) {
-        const float nrm = sqrtf(alpha * alpha + sig);
+        // hardware square root and reciprocals (about 1 ulp): the reflector
+        // needs no correctly rounded quotient, and the chain is the step's
+        // critical path
+        const float nrm = __builtin_amdgcn_sqrtf(fmaf(alpha, alpha, sig));
         beta = alpha >= 0.f ? -nrm : nrm;
-        tau = (beta - alpha) / beta;
-        scale = 1.f / (alpha - beta);
+        tau = (beta - alpha) * __builtin_amdgcn_rcpf(beta);
+        scale = __builtin_amdgcn_rcpf(alpha - beta);
       }
-      float vh[16];                                // v_i, i = h * 16 + ii
+      // the same value in every lane: made wave-uniform, so the branches on it are scalar
+      tau = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(tau)));
+      // v_i, i = h4 + rofs(ii)
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) vh[ii] = xh[ii] * scale;
       if (h == 0) vh[0] = 1.f;
-      const float vo = (l32 == 0) ? 1.f : xo * scale;   // v_{l32}
-      const int64_t ridx = sweep_offset(n, g.j) + g.s;
+      vo = (l32 == 0) ? 1.f : xo * scale;          // v_{l32}
+      const int64_t ridx = g.ref0 + g.s;
       if (lane < SBW) Rf[ridx * RFS + lane] = vo;
       if (lane == 0) Rf[ridx * RFS + SBW] = tau;
       // left block (rows r0.., columns r0-32 .. r0-1) from the left; written back
@@ -237,20 +270,18 @@ __global__ __launch_bounds__(NW * 64) void k_chase(float* Bw_g, int n, float* Rf
         if (h == 0) bstore(band, 4u * static_cast<uint32_t>(r0 * BWS + 1 + l32 * (BWS + 1)),
                            l32 == 0 ? beta : 0.f);
       } else {
-        float li[16];
+        f32x16 li;
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) li[ii] = Lt[(h * 16 + ii) * TLD + l32];
-        float y = 0.f;
+        for (int ii = 0; ii < 16; ++ii) li[ii] = Lt[(h4 + rofs(ii)) * TLD + l32];
+        const float y = half_sum(dot16(vh, li));
+        // L - tau v y^T: A = [v 0], B = [-tau y^T; 0].  Column 0 (lane l32 = 0)
+        // is the annihilated column, zeroed in the tile by the previous step,
+        // so it stays exactly zero; its top entry becomes beta.
+        li = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 0.f : vo, h ? 0.f : -tau * y, li, 0, 0, 0);
+        if (lane == 0) li[0] = beta;
+        const uint32_t ol = 4u * static_cast<uint32_t>(r0 * BWS + h4 * (BWS + 1) + SBW - l32);
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) y += vh[ii] * li[ii];
-        y += __shfl_xor(y, 32);
-        const uint32_t ol = 4u * static_cast<uint32_t>(r0 * BWS + h * 16 * (BWS + 1) + SBW - l32);
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) {
-          float nv = li[ii] - tau * vh[ii] * y;
-          if (l32 == 0) nv = (h == 0 && ii == 0) ? beta : 0.f;
-          bstore(band, ol + ii * RS, nv);
-        }
+        for (int ii = 0; ii < 16; ++ii) bstore(band, ol + rofs(ii) * RS, li[ii]);
       }
       if (tau != 0.f) {
         // diagonal block, symmetric, into the left block's tile
@@ -258,67 +289,70 @@ __global__ __launch_bounds__(NW * 64) void k_chase(float* Bw_g, int n, float* Rf
         wave_lds_sync();
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) {
-          const int a = h * 16 + ii;
-          Ds[a * TLD + l32] = (l32 <= a) ? dcur[ii] : 0.f;
+          const int a = h4 + rofs(ii);
+          Ds[a * TLD + l32] = (l32 <= a) ? pd[ii] : 0.f;
         }
         wave_lds_sync();
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) {
-          const int a = h * 16 + ii;
-          if (l32 < a) Ds[l32 * TLD + a] = dcur[ii];
+          const int a = h4 + rofs(ii);
+          if (l32 < a) Ds[l32 * TLD + a] = pd[ii];
         }
         wave_lds_sync();
         // w = D v (lane: row l32)
-        float wo = 0.f;
+        float drow[16];
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) wo += Ds[l32 * TLD + h * 16 + ii] * vh[ii];
-        wo += __shfl_xor(wo, 32);
+        for (int ii = 0; ii < 16; ++ii) drow[ii] = Ds[l32 * TLD + h4 + rofs(ii)];
+        const float wo = half_sum(dot16(drow, vh));
         if (lane < SBW) sm.w[lane] = wo;
         wave_lds_sync();
         float wh[16];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 w4 = *reinterpret_cast<const float4*>(&sm.w[h * 16 + 4 * q4]);
+          const float4 w4 = *reinterpret_cast<const float4*>(&sm.w[8 * q4 + h4]);
           wh[4 * q4] = w4.x; wh[4 * q4 + 1] = w4.y; wh[4 * q4 + 2] = w4.z; wh[4 * q4 + 3] = w4.w;
         }
-        float gam = 0.f;
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) gam += vh[ii] * wh[ii];
-        gam += __shfl_xor(gam, 32);
+        const float gam = half_sum(dot16(vh, wh));
         // D <- H D H = D - tau (v w^T + w v^T) + tau^2 (v^T w) v v^T  (lane: column l32)
-        const float tgv = tau * tau * gam * vo;
-        const uint32_t od = 4u * static_cast<uint32_t>(r0 * BWS + h * 16 * (BWS + 1) - l32);
+        // as one rank-two product: A = [v w], B = [(tau^2 gam v - tau w)^T; -tau v^T]
+        const f32x16 dm = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? wo : vo, h ? -tau * vo : tau * tau * gam * vo - tau * wo,
+                                                               pd, 0, 0, 0);
+        const uint32_t od = 4u * static_cast<uint32_t>(r0 * BWS + h4 * (BWS + 1) - l32);
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) {
-          const int a = h * 16 + ii;
-          const float nd = dcur[ii] - tau * (vh[ii] * wo + wh[ii] * vo) + tgv * vh[ii];
-          bstore(band, l32 <= a ? od + ii * RS : kOut, nd);
+          const int a = h4 + rofs(ii);
+          bstore(band, l32 <= a ? od + rofs(ii) * RS : kOut, dm[ii]);
         }
       }
+    }
+    if (actn) {
+      if (t > 0) wait_pred(t - 1);
+      prefetch(gn);
+    }
+    if (act) {
       if (g.r1 < g.hi) {
         // below block (rows r1 .., columns r0 .. r1-1) from the right (lane: row l32)
-        float bi[16];
+        f32x16 bi;                                 // the block's transpose: lane = its row l32
         wave_lds_sync();
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) bi[ii] = Ft[l32 * TLD + h * 16 + ii];
+        for (int ii = 0; ii < 16; ++ii) bi[ii] = Ft[l32 * TLD + h4 + rofs(ii)];
         if (tau != 0.f) {
-          float zr = 0.f;
+          const float zr = half_sum(dot16(bi, vh));
+          // B^T - tau v z^T: A = [v 0], B = [-tau z^T; 0]
+          bi = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 0.f : vo, h ? 0.f : -tau * zr, bi, 0, 0, 0);
 #pragma unroll
-          for (int ii = 0; ii < 16; ++ii) zr += bi[ii] * vh[ii];
-          zr += __shfl_xor(zr, 32);
-          const float tz = tau * zr;
-#pragma unroll
-          for (int ii = 0; ii < 16; ++ii) {
-            bi[ii] -= tz * vh[ii];
-            Ft[l32 * TLD + h * 16 + ii] = bi[ii];
-          }
+          for (int ii = 0; ii < 16; ++ii) Ft[l32 * TLD + h4 + rofs(ii)] = bi[ii];
         }
-        if (h == 0) sm.x[l32] = bi[0];             // the next step's column (zero past hi)
+        if (h == 0) {
+          sm.x[l32] = bi[0];                       // the next step's column (zero past hi)
+          // which that step annihilates: zero in the carried tile (its left block)
+          if (!g.last) Ft[l32 * TLD] = 0.f;
+        }
         if (g.last) {
           wave_lds_sync();
-          const uint32_t ob = 4u * static_cast<uint32_t>(g.r1 * BWS + h * 16 * (BWS + 1) + SBW - l32);
+          const uint32_t ob = 4u * static_cast<uint32_t>(g.r1 * BWS + h4 * (BWS + 1) + SBW - l32);
 #pragma unroll
-          for (int ii = 0; ii < 16; ++ii) bstore(band, ob + ii * RS, Ft[(h * 16 + ii) * TLD + l32]);
+          for (int ii = 0; ii < 16; ++ii) bstore(band, ob + rofs(ii) * RS, Ft[(h4 + rofs(ii)) * TLD + l32]);
         }
       }
       cur ^= 1;
