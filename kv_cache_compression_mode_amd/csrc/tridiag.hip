@@ -87,7 +87,6 @@ constexpr uint32_t kOut = 0x80000000u;   // a byte offset past any band (n <= 32
 struct ChaseLds {
   float tile[2][SBW * TLD];       // ping-pong: carried left block / staged below block
   float x[SBW];                   // the column annihilated by the next step
-  float w[SBW];
 };
 struct ChaseStep {
   int j, s, r0, L, r1, hi;
@@ -137,6 +136,22 @@ __device__ __forceinline__ constexpr int rofs(int ii) { return (ii >> 2) * 8 + (
 __device__ __forceinline__ float half_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);     // lower half's value + upper half's
+}
+// the sum of p over each half (32 lanes) of the wave, in every lane of the half:
+// a butterfly within rows of 16 (DPP: lane xor 1, xor 2, rotate by 4 and 8)
+// and a swap of odd and even rows (v_permlane16_swap).  The association of
+// the additions depends on the lane, so callers take one lane's value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum32(float p) {
+  p += dpp_f<0xB1>(p);            // quad_perm [1, 0, 3, 2]
+  p += dpp_f<0x4E>(p);            // quad_perm [2, 3, 0, 1]
+  p += dpp_f<0x124>(p);           // row_ror 4
+  p += dpp_f<0x128>(p);           // row_ror 8
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);     // even row's sum + odd row's
 }
 // sum of a[i] b[i], i < 16, as four interleaved chains (short dependency chain)
 template <typename A, typename B>
@@ -204,6 +219,16 @@ __global__ __launch_bounds__(NW * 64) void k_chase(float* Bw_g, int n, float* Rf
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   };
+  // row a = h4 + rofs(ii) of a block against this lane's column l32: a <= l32, a >= l32
+  uint32_t m_le[16], m_ge[16];
+#pragma unroll
+  for (int ii = 0; ii < 16; ++ii) {
+    m_le[ii] = h4 + rofs(ii) <= l32 ? ~0u : 0u;
+    m_ge[ii] = h4 + rofs(ii) >= l32 ? ~0u : 0u;
+    // opaque to the optimizer: kept as vector registers and combined with
+    // v_bfi, rather than turned back into per-row lane masks in scalar registers
+    asm volatile("" : "+v"(m_le[ii]), "+v"(m_ge[ii]));
+  }
   ChaseClock ck, ckn;
   ck.init(wave, S, n);
   ckn.init(wave, S, n);
@@ -284,44 +309,35 @@ __global__ __launch_bounds__(NW * 64) void k_chase(float* Bw_g, int n, float* Rf
         for (int ii = 0; ii < 16; ++ii) bstore(band, ol + rofs(ii) * RS, li[ii]);
       }
       if (tau != 0.f) {
-        // diagonal block, symmetric, into the left block's tile
+        // diagonal block: pd holds column l32 of its lower triangle (rows
+        // a >= l32; the rest of the column is other band data).  Row l32 of
+        // the block is D[l32][c] = the tile's (l32, c) for c <= l32 (written by
+        // lane c) and D[c][l32] = pd for c > l32: selected bitwise with the
+        // lane's row masks.
         float* Ds = Lt;
         wave_lds_sync();
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) {
-          const int a = h4 + rofs(ii);
-          Ds[a * TLD + l32] = (l32 <= a) ? pd[ii] : 0.f;
-        }
+        for (int ii = 0; ii < 16; ++ii) Ds[(h4 + rofs(ii)) * TLD + l32] = pd[ii];
         wave_lds_sync();
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) {
-          const int a = h4 + rofs(ii);
-          if (l32 < a) Ds[l32 * TLD + a] = pd[ii];
-        }
-        wave_lds_sync();
-        // w = D v (lane: row l32)
         float drow[16];
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) drow[ii] = Ds[l32 * TLD + h4 + rofs(ii)];
-        const float wo = half_sum(dot16(drow, vh));
-        if (lane < SBW) sm.w[lane] = wo;
-        wave_lds_sync();
-        float wh[16];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 w4 = *reinterpret_cast<const float4*>(&sm.w[8 * q4 + h4]);
-          wh[4 * q4] = w4.x; wh[4 * q4 + 1] = w4.y; wh[4 * q4 + 2] = w4.z; wh[4 * q4 + 3] = w4.w;
+        for (int ii = 0; ii < 16; ++ii) {
+          const uint32_t tv = __float_as_uint(Ds[l32 * TLD + h4 + rofs(ii)]);
+          drow[ii] = __uint_as_float((m_le[ii] & tv) | (~m_le[ii] & __float_as_uint(pd[ii])));
         }
-        const float gam = half_sum(dot16(vh, wh));
+        const float wo = half_sum(dot16(drow, vh));     // w = D v (lane: row l32)
+        // gamma = v^T w over the 32 rows, one value for the whole wave
+        const float gam = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sum32(vo * wo))));
         // D <- H D H = D - tau (v w^T + w v^T) + tau^2 (v^T w) v v^T  (lane: column l32)
         // as one rank-two product: A = [v w], B = [(tau^2 gam v - tau w)^T; -tau v^T]
         const f32x16 dm = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? wo : vo, h ? -tau * vo : tau * tau * gam * vo - tau * wo,
                                                                pd, 0, 0, 0);
+        // lower triangle only: the other rows go to an offset past the band (dropped)
         const uint32_t od = 4u * static_cast<uint32_t>(r0 * BWS + h4 * (BWS + 1) - l32);
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) {
-          const int a = h4 + rofs(ii);
-          bstore(band, l32 <= a ? od + rofs(ii) * RS : kOut, dm[ii]);
+          const uint32_t base = ii < 8 ? od : od + 16 * RS;
+          bstore(band, ((m_ge[ii] & base) | (~m_ge[ii] & kOut)) + (rofs(ii) - (ii < 8 ? 0 : 16)) * RS, dm[ii]);
         }
       }
     }
