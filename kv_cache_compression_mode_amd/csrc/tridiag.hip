@@ -417,7 +417,8 @@ __global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double*
   extern __shared__ double sh[];
   double* d = sh;
   double* e2 = sh + n;
-  __shared__ double gl_s, gu_s, piv_s;
+  __shared__ double gl_s, gu_s, piv_s, tol_s;
+  __shared__ int grid_cnt[256];
   const int64_t z = blockIdx.y;
   for (int64_t i = threadIdx.x; i < n; i += 256) {
     d[i] = d_g[z * n + i];
@@ -438,7 +439,19 @@ __global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double*
     gl_s = gl - 2.0 * DBL_EPSILON * span - DBL_MIN;
     gu_s = gu + 2.0 * DBL_EPSILON * span + DBL_MIN;
     piv_s = DBL_MIN * fmax(1.0, emax);
+    // brackets narrower than 1e-12 of the spectrum's span are not refined
+    // further: the tridiagonal itself carries fp32 rounding (~1e-7 of its
+    // norm), and the eigenvalues feed the allocation's energies and the
+    // inverse-iteration shifts, neither of which sees a difference that small
+    tol_s = 1e-12 * (gu - gl);
   }
+  __syncthreads();
+  // a shared first pass: counts at 256 interior points x_i = gl + (gu - gl) (i + 1) / 257
+  // of the whole interval, one per thread, from which every eigenvalue takes
+  // its starting bracket (one count per thread, as a multisection step, but a
+  // 257-way split)
+  const double g0 = gl_s, gw = gu_s - gl_s;
+  grid_cnt[threadIdx.x] = sturm_count(d, e2, n, g0 + gw * (threadIdx.x + 1) * (1.0 / 257.0), piv_s);
   __syncthreads();
   // four threads per eigenvalue (multisection): each evaluates one of four
   // interior points of the bracket, which then shrinks to one fifth
@@ -446,9 +459,14 @@ __global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double*
   const int q = gid >> 2, sub = gid & 3;
   if (q >= R) return;                             // whole groups leave together
   const int64_t k = n - 1 - q;                    // wanted: the k-th smallest (0-based)
-  double lo = gl_s, hi = gu_s;
+  // the first grid point whose count exceeds k (256 if none); counts rise with x
+  int f = 0;
+  for (int span = 256; span > 0; span >>= 1)
+    if (f + span <= 256 && grid_cnt[f + span - 1] <= k) f += span;
+  double lo = f > 0 ? g0 + gw * f * (1.0 / 257.0) : gl_s;            // x_{f-1}
+  double hi = f < 256 ? g0 + gw * (f + 1) * (1.0 / 257.0) : gu_s;     // x_f
   for (int it = 0; it < 100; ++it) {
-    if (hi - lo <= 2.0 * DBL_EPSILON * fmax(fabs(lo), fabs(hi)) + piv_s) break;
+    if (hi - lo <= fmax(2.0 * DBL_EPSILON * fmax(fabs(lo), fabs(hi)), tol_s) + piv_s) break;
     const double w = hi - lo;
     const double x = lo + w * (sub + 1) * 0.2;
     const int cnt = sturm_count(d, e2, n, x, piv_s);
