@@ -448,6 +448,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   const int r = lane & 31, half = lane >> 5;
   f32x16 acc[2][2] = {};
+  f32x16 sum[2][2] = {};          // seq_len > 0: the finished chunks, added in order
   XRegs<AM> ra;
   XRegs<BMODE> rb;
   if (kbeg < kend) {
@@ -485,7 +486,23 @@ __global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
           if constexpr (BS) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bl[j], acc[i][j], 0, 0, 0);
         }
     }
+    if (g.seq_len > 0 && ((k0 + XK - kbeg) % g.seq_len == 0 || k0 + XK >= kend)) {
+      // a chunk done: sum = ((0 + c0) + c1) + ..., the order of the split-K reduction
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          sum[i][j] += acc[i][j];
+          acc[i][j] = f32x16{};
+        }
+    }
     __syncthreads();
+  }
+  if (g.seq_len > 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = sum[i][j];
   }
   if (g.ksplit > 1) {   // partial sums, reduced in a fixed order by k_splitk_reduce
     float* Pp = g.partial + (z * g.ksplit + kz) * g.M * g.N;
@@ -741,6 +758,12 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s) {
     if (xa >= 0 && xb >= 0 && !(xa == kOpF32K && xb == kOpF32K)) {
       x.kchunk = (x.K + x.ksplit - 1) / x.ksplit;
       x.kchunk = (x.kchunk + XK - 1) / XK * XK;
+      x.seq_len = 0;
+      if (x.split_seq && x.ksplit > 1) {            // the chunks in one workgroup, summed in order
+        x.seq_len = x.kchunk;
+        x.ksplit = 1;
+        x.kchunk = x.K;
+      }
       dim3 grid((x.M + XT - 1) / XT, (x.N + XT - 1) / XT, batch * x.ksplit);
       ProfScope ps("gemm_bf16", s);
       account("gemm_bf16");

@@ -1425,6 +1425,9 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
       g1.C = P; g1.c_m = HD; g1.c_n = 1; g1.c_batch = rT * HD;
       g1.ksplit = encode_ksplit(T);
       g1.partial = reinterpret_cast<float*>(ws + L.part_off[g]);
+      // many tensors give enough tiles: the split's chunks are summed inside
+      // each workgroup (the same arithmetic as jolt_encode's split launch)
+      g1.split_seq = 1;
       ck(launch_gemm(g1, m, s));
       GemmArgs g2 = gemm0();                    // G~_h = bf16(P_h U~_D) per (tensor, head)
       g2.M = rT; g2.N = rD; g2.K = D;

@@ -44,6 +44,10 @@ struct GemmArgs {
   // split-K: ksplit > 1 writes partial sums to `partial` ([batch][ksplit][M][N]
   // floats) and reduces them in a fixed order (deterministic)
   int ksplit; float* partial; int64_t kchunk;
+  // split_seq (bf16 tiles): with ksplit > 1, the same K chunks are summed in
+  // the same order inside one workgroup (no partial sums in memory), so the
+  // result is bit-identical to the split launch; seq_len is set by the launcher
+  int split_seq; int64_t seq_len;
   // symmetric operands stored as their lower triangle (fp32 path, plain
   // dimensions only): a_sym reads A(m, k) with m < k from A(k, m); c_lower
   // computes and writes only C(m, n) with m >= n (the launcher may pass -1,
