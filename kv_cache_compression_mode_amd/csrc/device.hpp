@@ -65,6 +65,14 @@ template <> __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_
   return bf16_bits_to_f32(p[i]);
 }
 
+// v(lane l) + v(lane l ^ 32), the same value in both halves of the wave: one
+// lane swap of the halves (v_permlane32_swap, gfx950) instead of a trip
+// through LDS.  Both halves add the lower half's value to the upper half's.
+__device__ __forceinline__ float half_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ----------------------------------------------------- counter-based RNG
 // SplitMix64 (Steele, Lea & Flood 2014): word i of the stream keyed by
 // key = mix64(seed ^ tag) is mix64(key + (i + 1) * GAMMA); normals come from

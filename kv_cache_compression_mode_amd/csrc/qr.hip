@@ -241,8 +241,7 @@ __device__ float qr_reg_factor(float (&p)[64], int mr, int nb, QrRegLds& L) {
         s2 += q.z * p[r + 2];
         s3 += q.w * p[r + 3];
       }
-      float part = (s0 + s1) + (s2 + s3);
-      part += __shfl_xor(part, 32);
+      const float part = half_sum((s0 + s1) + (s2 + s3));
       if (lane < 32) L.red[wave][c] = part;
     }
     __syncthreads();
@@ -255,10 +254,12 @@ __device__ float qr_reg_factor(float (&p)[64], int mr, int nb, QrRegLds& L) {
     const float alpha = L.rowj[par][j];
     float tau = 0.f, beta = alpha, scale = 0.f;
     if (sigma > 0.f) {
-      const float nrm = sqrtf(alpha * alpha + sigma);
+      // hardware square root and reciprocals (about 1 ulp): the column's
+      // critical path, and the reflector needs no correctly rounded quotient
+      const float nrm = __builtin_amdgcn_sqrtf(fmaf(alpha, alpha, sigma));
       beta = alpha >= 0.f ? -nrm : nrm;
-      tau = (beta - alpha) / beta;
-      scale = 1.f / (alpha - beta);
+      tau = (beta - alpha) * __builtin_amdgcn_rcpf(beta);
+      scale = __builtin_amdgcn_rcpf(alpha - beta);
     }
     const float d = L.rowj[par][c] + scale * raw;                // v^T P[:, c]
     if (c == j) vscale = scale;

@@ -131,12 +131,6 @@ __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t off, f
 
 // row of register ii in a 32x32 fp32 matrix-core accumulator, less 4 (lane / 32)
 __device__ __forceinline__ constexpr int rofs(int ii) { return (ii >> 2) * 8 + (ii & 3); }
-// v(lane l) + v(lane l ^ 32), the same value in both halves: one lane swap of
-// the halves (v_permlane32_swap) instead of a trip through LDS
-__device__ __forceinline__ float half_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);     // lower half's value + upper half's
-}
 // the sum of p over each half (32 lanes) of the wave, in every lane of the half:
 // a butterfly within rows of 16 (DPP: lane xor 1, xor 2, rotate by 4 and 8)
 // and a swap of odd and even rows (v_permlane16_swap).  The association of
