@@ -429,11 +429,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t As[AS ? 2 : 1][XT][XKP];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[BS ? 2 : 1][XT][XKP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * XT;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * XT;
+  // Workgroups are dispatched round-robin over the 8 XCDs by linear id; when
+  // the batch dimension is a multiple of 8 the id is remapped so that every
+  // tile of one batch entry runs on the same XCD (its operands stream through
+  // one L2 together rather than through all eight).  A bijection of the ids.
+  uint32_t bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  if (gridDim.z % 8 == 0) {
+    const uint32_t G = gridDim.x * gridDim.y;
+    const uint32_t L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const uint32_t xcd = L % 8, j = L / 8, tile = j % G;
+    bz = xcd + 8 * (j / G);
+    bx = tile % gridDim.x;
+    by = tile / gridDim.x;
+  }
+  const int64_t m0 = static_cast<int64_t>(bx) * XT;
+  const int64_t n0 = static_cast<int64_t>(by) * XT;
   // tile wholly outside the kept triangle (c_lower > 0: m >= n; < 0: m <= n)
   if (g.c_lower > 0 ? m0 + XT <= n0 : (g.c_lower < 0 && n0 + XT <= m0)) return;
-  const int64_t zz = blockIdx.z;
+  const int64_t zz = bz;
   const int64_t z = zz / g.ksplit, kz = zz % g.ksplit;
   const int64_t kbeg = kz * g.kchunk;
   const int64_t kend = (kbeg + g.kchunk < g.K) ? kbeg + g.kchunk : g.K;
