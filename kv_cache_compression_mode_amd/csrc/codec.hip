@@ -212,11 +212,11 @@ static_assert(2 * ER * EUS * 2 <= kEncLds, "U~_T chunks fit the staging area");
 // UV: rows of U~_T are 16-byte aligned (r_T % 8 == 0 and an aligned base), so
 // a chunk is read with 16-byte loads; otherwise element by element.
 template <typename TX, bool UV>
-__device__ __forceinline__ void encode_tile(const EncodeArgs& a, float* lds_f) {
+__device__ __forceinline__ void encode_tile(const EncodeArgs& a, float* lds_f, uint32_t tile, uint32_t head) {
   float* st = lds_f;                                          // recon, then Y
   uint16_t* rp = reinterpret_cast<uint16_t*>(lds_f);          // R parts
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, half = lane >> 5;
-  const int64_t h = blockIdx.y, t0 = static_cast<int64_t>(blockIdx.x) * ER;
+  const int64_t h = head, t0 = static_cast<int64_t>(tile) * ER;
   const int col = wave * 32 + rl;
   const int qm = tid >> 2, qg = tid & 3;
   const int64_t qt = t0 + qm;
@@ -449,20 +449,27 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, float* lds_f) {
 }
 
 template <typename TX>
-__device__ __forceinline__ void encode_any(const EncodeArgs& a) {
+__device__ __forceinline__ void encode_any(const EncodeArgs& a, uint32_t tile, uint32_t head) {
   __shared__ __attribute__((aligned(16))) float lds_f[kEncLds / 4];
-  if (a.r_T % 8 == 0 && (reinterpret_cast<uintptr_t>(a.Ut) & 15) == 0) encode_tile<TX, true>(a, lds_f);
-  else encode_tile<TX, false>(a, lds_f);
+  if (a.r_T % 8 == 0 && (reinterpret_cast<uintptr_t>(a.Ut) & 15) == 0) encode_tile<TX, true>(a, lds_f, tile, head);
+  else encode_tile<TX, false>(a, lds_f, tile, head);
 }
 template <typename TX>
 __global__ __launch_bounds__(256, 3) void k_encode_residual(EncodeArgs a) {
-  encode_any<TX>(a);
+  uint32_t tile, head;
+  xcd_group_2d(tile, head);                        // the row tiles of one head on one XCD
+  encode_any<TX>(a, tile, head);
 }
-// Tensors of one shape in one launch: blockIdx.z selects the tensor's arguments.
+// Tensors of one shape in one launch: grid (row tiles, heads, tensors); all
+// the tiles of one tensor run on one XCD, whose L2 then holds the tensor's W
+// parts and U~_T rows (each used by many tiles).
 template <typename TX>
 __global__ __launch_bounds__(256, 3) void k_encode_residual_many(const EncodeArgs* list) {
-  const EncodeArgs a = list[blockIdx.z];
-  encode_any<TX>(a);
+  uint32_t tensor, idx;
+  xcd_group(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), gridDim.x * gridDim.y, gridDim.z, tensor,
+            idx);
+  const EncodeArgs a = list[tensor];
+  encode_any<TX>(a, idx % gridDim.x, idx / gridDim.x);
 }
 
 // ------------------------------------------------------------------ decode

@@ -65,6 +65,27 @@ template <> __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_
   return bf16_bits_to_f32(p[i]);
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2) by linear id.  For a grid of nb groups of gsize ids each (group-major:
+// a group's ids consecutive), xcd_group gives the group and the index in it
+// of linear id L such that, when nb is a multiple of 8, every id of a group
+// runs on one XCD (a group's shared operands go through one L2); otherwise
+// the plain decomposition.  A bijection either way.
+__device__ __forceinline__ void xcd_group(uint32_t L, uint32_t gsize, uint32_t nb, uint32_t& grp, uint32_t& idx) {
+  if (nb % 8 == 0) {
+    const uint32_t j = L / 8;
+    grp = L % 8 + 8 * (j / gsize);
+    idx = j % gsize;
+  } else {
+    grp = L / gsize;
+    idx = L % gsize;
+  }
+}
+// the same for a 2-D grid: x = the index in a group, y = the group
+__device__ __forceinline__ void xcd_group_2d(uint32_t& x, uint32_t& y) {
+  xcd_group(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x, gridDim.y, y, x);
+}
+
 // v(lane l) + v(lane l ^ 32), the same value in both halves of the wave: one
 // lane swap of the halves (v_permlane32_swap, gfx950) instead of a trip
 // through LDS.  Both halves add the lower half's value to the upper half's.

@@ -697,14 +697,16 @@ __global__ __launch_bounds__(256) void k_cb_apply(int t, int glo, int nchunk, fl
   __shared__ float Zs[CBR][65];          // Z rows x 64 columns
   __shared__ float Wp[2][SBW][65];       // W partial sums, then W2 = T W (in Wp[0])
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
-  const int bi = blockIdx.x / nchunk, ch = blockIdx.x % nchunk;
+  uint32_t bx, by;
+  xcd_group_2d(bx, by);                            // the blocks of one matrix on one XCD
+  const int bi = static_cast<int>(bx) / nchunk, ch = static_cast<int>(bx) % nchunk;
   const int gp = glo + bi, s = t - 2 * gp, G = ng - 1 - gp, jg = G * SBW;
   if (gp >= ng || s < 0 || s >= K0 || s >= sweep_steps(n, jg)) return;
   const int rb = jg + 1 + s * SBW;
   if (rb >= n) return;
   const int rows = min(CBR - 1, n - rb);
   const int c0 = ch * 64, nc = min(64, R - c0);
-  const int64_t z = blockIdx.y;
+  const int64_t z = by;
   const float* Rf = Rf_g + z * rf_stride;
   float* Zz = Z + z * z_batch;
   const int last = n - 3;
@@ -812,8 +814,10 @@ __global__ __launch_bounds__(256) void k_apply_wy(float* Z, int64_t n, int64_t z
   __shared__ float Wp[2][SBW][65];       // W partial sums (two row halves), then W2
   __shared__ float Ts[SBW][SBW + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
-  const int64_t z = blockIdx.y;
-  const int c0 = blockIdx.x * 64, nc = min(64, R - c0);
+  uint32_t bx, by;
+  xcd_group_2d(bx, by);                            // the column blocks of one matrix on one XCD
+  const int64_t z = by;
+  const int c0 = static_cast<int>(bx) * 64, nc = min(64, R - c0);
   float* Zr = Z + z * z_batch + r0;
   const float* V = V_g + z * v_batch;
   {
@@ -933,8 +937,10 @@ __global__ __launch_bounds__(256) void k_symm_v(const float* A, int64_t n, int64
   __shared__ float Ts[SBW][SBW + 1];
   __shared__ float Vb[SBW][SY + 1];      // V rows of this block
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
-  const int64_t z = blockIdx.y;
-  const int ib = blockIdx.x, i0 = SY * ib, nb = (mp + SY - 1) / SY;
+  uint32_t bx, by;
+  xcd_group_2d(bx, by);                            // the blocks of one matrix on one XCD
+  const int64_t z = by;
+  const int ib = static_cast<int>(bx), i0 = SY * ib, nb = (mp + SY - 1) / SY;
   const float* a = A + z * a_batch;
   const float* V = V_g + z * v_batch;
   {
@@ -1057,8 +1063,10 @@ __global__ __launch_bounds__(256) void k_w_form(int mp, const float* V_g, int64_
   __shared__ float Ss[SBW][SBW + 1], Ts[SBW][SBW + 1], S2[SBW][SBW + 1];
   __shared__ float Vr[SY][SBW + 1];
   const int tid = threadIdx.x;
-  const int64_t z = blockIdx.y;
-  const int ib = blockIdx.x, i0 = SY * ib, nb = (mp + SY - 1) / SY;
+  uint32_t bx, by;
+  xcd_group_2d(bx, by);                            // the blocks of one matrix on one XCD
+  const int64_t z = by;
+  const int ib = static_cast<int>(bx), i0 = SY * ib, nb = (mp + SY - 1) / SY;
   const float* V = V_g + z * v_batch;
   float* VW = VW_g + z * vw_batch;
   const float* sp = SP + z * nb * 1024;
@@ -1130,9 +1138,11 @@ __global__ __launch_bounds__(256) void k_syr2k(float* A, int64_t n, int64_t a_ba
   __shared__ float As[2 * SBW][SY + 1];  // [V W] rows of the tile's rows: As[k][r]
   __shared__ float Bs[2 * SBW][SY + 1];  // [W V] rows of the tile's columns: Bs[k][r]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
-  const int64_t z = blockIdx.y;
+  uint32_t bx, by;
+  xcd_group_2d(bx, by);                            // the tiles of one matrix on one XCD
+  const int64_t z = by;
   // tile (bi, bj) from the linear index x = bi (bi + 1) / 2 + bj
-  const int x = blockIdx.x;
+  const int x = static_cast<int>(bx);
   int bi = static_cast<int>((sqrtf(8.f * x + 1.f) - 1.f) * 0.5f);
   while (bi * (bi + 1) / 2 > x) --bi;
   while ((bi + 1) * (bi + 2) / 2 <= x) ++bi;
