@@ -480,8 +480,11 @@ __global__ __launch_bounds__(256, 3) void k_encode_residual_many(const EncodeArg
 // ride on).  Every MFMA operand is one 16-byte load per lane: lane l holds
 // row l%32 and k = 8*(l/32) .. +8 of A, column l%32 and the same k of B.
 
-// W_h^T = (G~_h U~_D^T)^T as bf16 hi + lo, [h][d][k] with row stride r_Tp.
-// One wave per (record, head, 32 rows of r_T).
+// W_h = G~_h U~_D^T as bf16 hi + lo planes in matrix-core fragment order,
+// [h][d / 32][k / 16][32 ((k / 8) % 2) + d % 32][k % 8] (k < r_Tp, r_Tp a
+// multiple of 32), so that one k step of one column tile is 1 KB of
+// consecutive bytes for the decoding wave.  One wave per (record, head, 32
+// rows of r_T).
 __global__ __launch_bounds__(256) void k_make_w(DecBatch b) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tile = blockIdx.x * 4 + wave;
@@ -517,12 +520,13 @@ __global__ __launch_bounds__(256) void k_make_w(DecBatch b) {
   for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int m = (i >> 2) * 8 + half * 4 + (i & 3);
-      const int d = 32 * ct + r;
+      const int m = (i >> 2) * 8 + half * 4 + (i & 3);   // k = k0 + m, feature 32 ct + r
       const float w = acc[ct][i];
       const uint16_t hi = f32_to_bf16_rne(w);
       const uint16_t lo = f32_to_bf16_rne(w - bf16_bits_to_f32(hi));
-      const int64_t off = (static_cast<int64_t>(h) * D + d) * R.r_Tp + k0 + m;
+      const int k = k0 + m;
+      const int64_t off = ((static_cast<int64_t>(h) * 4 + ct) * (R.r_Tp / 16) + (k >> 4)) * 512 +
+                          (((k >> 3) & 1) * 32 + r) * 8 + (k & 7);
       R.Whi[off] = hi;
       R.Wlo[off] = lo;
     }
@@ -569,7 +573,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
     bf16x8 ch[4], cl[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      const int64_t wo = (h * D + 32 * ct + r) * R.r_Tp + kk;
+      const int64_t wo = ((h * 4 + ct) * (R.r_Tp / 16) + (k0 >> 4)) * 512 + lane * 8;   // fragment order
       const uint4 rh = *reinterpret_cast<const uint4*>(R.Whi + wo);
       const uint4 rlo = *reinterpret_cast<const uint4*>(R.Wlo + wo);
       ch[ct] = *reinterpret_cast<const bf16x8*>(&rh);

@@ -173,7 +173,7 @@ struct DecRec {
   const uint16_t* G;       // bf16 [H][r_T][r_D]
   const uint32_t* scales;  // [H][T][4] words (offset | step << 16)
   const uint32_t* codes;   // [H][T][4][bits] words
-  uint16_t* Whi;           // workspace: bf16 [H][D][r_Tp]
+  uint16_t* Whi;           // workspace: bf16 [H][D/32][r_Tp/16][64][8], fragment order
   uint16_t* Wlo;
   void* out;               // [H][T][D]
   int32_t r_T, r_D, r_Tp, bits;
