@@ -94,12 +94,12 @@ __device__ __forceinline__ bf16x8 load8_bf16(const uint16_t* base, int64_t idx, 
                                              bool aligned) {
   bf16x8 v;
   if (aligned && idx + 8 <= limit) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(base + idx);
+    const uint4 raw = ldg16(base + idx);
     v = *reinterpret_cast<const bf16x8*>(&raw);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint16_t b = idx + i < limit ? base[idx + i] : static_cast<uint16_t>(0);
+      const uint16_t b = idx + i < limit ? ldg_u16(base + idx + i) : static_cast<uint16_t>(0);
       v[i] = __builtin_bit_cast(__bf16, b);
     }
   }
@@ -533,30 +533,28 @@ __global__ __launch_bounds__(256) void k_make_w(DecBatch b) {
   }
 }
 
-// One wave per (record, head, 64 rows): X^ rows = U~_T W (hi + lo) + Yhat Q.
+// One wave per (record, head, 64 rows): X^ rows = U~_T W (hi + lo) + Yhat Q,
+// computed transposed (features as the product's rows, tokens as its
+// columns) so that each lane ends with runs of 4 consecutive features of one
+// token; a swap of the wave's halves makes them runs of 8, stored 16 bytes at
+// a time.
 template <typename TO>
 __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
+  // one k step of W (hi, lo planes, 4 column tiles) per buffer, [plane][ct][lane][8]
+  __shared__ __align__(16) uint16_t wl[2][2 * 4 * 64 * 8];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tile = blockIdx.x * 4 + wave;
-  if (tile >= b.tiles_total) return;
-  // the record holding this tile: the last with first tile <= tile (records
-  // are in order, so a binary search)
-  int ri = 0;
-  for (int hi = b.n - 1; ri < hi;) {
-    const int mid = (ri + hi + 1) >> 1;
-    if (b.rec[mid].tile0 <= tile) ri = mid;
-    else hi = mid - 1;
-  }
-  const DecRec& R = b.rec[ri];
-  const int local = tile - R.tile0;
-  const int tilesT = (b.T + 63) / 64;
-  const int64_t h = local / tilesT, t0 = static_cast<int64_t>(local % tilesT) * 64;
+  // a block = 256 rows (4 waves of 64) of one (record, head); the blocks of
+  // one (record, head) share its W and run on one XCD
+  uint32_t xb = blockIdx.x, grp = blockIdx.y;
+  xcd_group_2d(xb, grp);
+  const DecRec& R = b.rec[grp / b.H];
+  const int64_t h = grp % b.H, t0 = static_cast<int64_t>(xb) * 256 + 64 * wave;
   const int r = lane & 31, half = lane >> 5;
   f32x16 acc[2][4] = {};
   const bool ua = (R.r_T % 8) == 0;
-  // U~_T rows of one k step (16 of r_T) streamed from memory, the next
-  // step's loaded during this one's MFMAs; W (hi, lo) is shared by all row
-  // tiles of the head and stays in cache
+  // U~_T rows of one k step (16 of r_T) streamed from memory and W's k step
+  // staged through LDS, both one step ahead of the MFMAs; each thread moves
+  // the hi and lo 16 bytes of (column tile = its wave, its lane)
   bf16x8 a[2];
   auto load_k = [&](int k0) {
     const int kk = k0 + 8 * half;
@@ -566,28 +564,47 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
       a[rt] = t < b.T ? load8_bf16(R.Ut + t * R.r_T, kk, R.r_T, ua) : zero8();
     }
   };
-  if (R.r_Tp > 0) load_k(0);
-  for (int k0 = 0; k0 < R.r_Tp; k0 += 16) {
-    const int kk = k0 + 8 * half;
+  const int nks = R.r_Tp / 16;
+  uint4 wh, wlo;
+  auto load_w = [&](int ks) {
+    const int64_t o = ((h * 4 + wave) * nks + ks) * 512 + lane * 8;   // fragment order
+    wh = ldg16(R.Whi + o);
+    wlo = ldg16(R.Wlo + o);
+  };
+  auto store_w = [&](int buf) {
+    *reinterpret_cast<uint4*>(&wl[buf][(wave * 64 + lane) * 8]) = wh;
+    *reinterpret_cast<uint4*>(&wl[buf][((4 + wave) * 64 + lane) * 8]) = wlo;
+  };
+  if (nks > 0) {
+    load_w(0);
+    load_k(0);
+    store_w(0);
+  }
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    const int buf = ks & 1;
     const bf16x8 ca[2] = {a[0], a[1]};
+    if (ks + 1 < nks) {
+      load_w(ks + 1);
+      load_k(16 * (ks + 1));
+    }
     bf16x8 ch[4], cl[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      const int64_t wo = ((h * 4 + ct) * (R.r_Tp / 16) + (k0 >> 4)) * 512 + lane * 8;   // fragment order
-      const uint4 rh = *reinterpret_cast<const uint4*>(R.Whi + wo);
-      const uint4 rlo = *reinterpret_cast<const uint4*>(R.Wlo + wo);
-      ch[ct] = *reinterpret_cast<const bf16x8*>(&rh);
-      cl[ct] = *reinterpret_cast<const bf16x8*>(&rlo);
+      ch[ct] = *reinterpret_cast<const bf16x8*>(&wl[buf][(ct * 64 + lane) * 8]);
+      cl[ct] = *reinterpret_cast<const bf16x8*>(&wl[buf][((4 + ct) * 64 + lane) * 8]);
     }
-    if (k0 + 16 < R.r_Tp) load_k(k0 + 16);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[rt], ch[ct], acc[rt][ct], 0, 0, 0);
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[rt], cl[ct], acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch[ct], ca[rt], acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cl[ct], ca[rt], acc[rt][ct], 0, 0, 0);
       }
     }
+    // the other buffer was last read in the previous step, before its barrier
+    if (ks + 1 < nks) store_w(buf ^ 1);
+    __syncthreads();
   }
   const int bits = R.bits;
   const uint32_t qmask = (1u << bits) - 1u;
@@ -603,10 +620,10 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
       sw[rt] = 0u; w0[rt] = 0u; w1[rt] = 0u;
       if (t < b.T) {
         const int64_t gi = (h * b.T + t) * 4 + g;
-        sw[rt] = R.scales[gi];
+        sw[rt] = ldg32(R.scales + gi);
         const uint32_t* cw = R.codes + gi * bits;
-        w0[rt] = cw[bitpos >> 5];
-        if ((bitpos & 31) + 8 * bits > 32) w1[rt] = cw[(bitpos >> 5) + 1];
+        w0[rt] = ldg32(cw + (bitpos >> 5));
+        if ((bitpos & 31) + 8 * bits > 32) w1[rt] = ldg32(cw + (bitpos >> 5) + 1);
       }
     }
   };
@@ -617,7 +634,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
     const uint32_t csw[2] = {sw[0], sw[1]}, cw0[2] = {w0[0], w0[1]}, cw1[2] = {w1[0], w1[1]};
     uint4 cq[4];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) cq[ct] = *reinterpret_cast<const uint4*>(b.Qt16 + (32 * ct + r) * D + dd);
+    for (int ct = 0; ct < 4; ++ct) cq[ct] = ldg16(b.Qt16 + (32 * ct + r) * D + dd);
     if (d0 + 16 < D) load_d(d0 + 16);
     bf16x8 y[2];
 #pragma unroll
@@ -638,21 +655,55 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
       const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&cq[ct]);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(y[rt], bq, acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq, y[rt], acc[rt][ct], 0, 0, 0);
     }
   }
+  // acc[rt][ct][i] is feature 32 ct + 8 (i / 4) + 4 half + i % 4 of token
+  // t0 + 32 rt + r
   TO* out = static_cast<TO*>(R.out);
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
+    const int64_t t = t0 + 32 * rt + r;
+    if (t >= b.T) continue;
+    TO* orow = out + (h * b.T + t) * D;
+    if (!b.out16) {   // an output not 16-byte aligned: one element per store
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = 32 * ct + 8 * (i >> 2) + 4 * half + (i & 3);
+          if constexpr (sizeof(TO) == 2) orow[c] = f32_to_bf16_rne(acc[rt][ct][i]);
+          else orow[c] = acc[rt][ct][i];
+        }
+      continue;
+    }
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
+      if constexpr (sizeof(TO) == 2) {
+        // groups 2j and 2j + 1 of 8 features: the lower half gathers group 2j
+        // (its own 4 + the upper half's 4), the upper half group 2j + 1
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t t = t0 + 32 * rt + (i >> 2) * 8 + half * 4 + (i & 3);
-        if (t < b.T) {
-          const int64_t off = (h * b.T + t) * D + 32 * ct + r;
-          if constexpr (sizeof(TO) == 2) out[off] = f32_to_bf16_rne(acc[rt][ct][i]);
-          else out[off] = acc[rt][ct][i];
+        for (int j = 0; j < 2; ++j) {
+          uint32_t p[2][2];
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              const int i = (2 * j + g) * 4 + 2 * w;
+              p[g][w] = static_cast<uint32_t>(f32_to_bf16_rne(acc[rt][ct][i])) |
+                        (static_cast<uint32_t>(f32_to_bf16_rne(acc[rt][ct][i + 1])) << 16);
+            }
+          const auto s0 = __builtin_amdgcn_permlane32_swap(p[0][0], p[1][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(p[0][1], p[1][1], false, false);
+          const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+          stg16(orow + 32 * ct + 8 * (2 * j + half), v);
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x4 v = {__float_as_uint(acc[rt][ct][4 * g]), __float_as_uint(acc[rt][ct][4 * g + 1]),
+                           __float_as_uint(acc[rt][ct][4 * g + 2]), __float_as_uint(acc[rt][ct][4 * g + 3])};
+          stg16(orow + 32 * ct + 8 * g + 4 * half, v);
         }
       }
     }
@@ -713,8 +764,9 @@ hipError_t launch_decode_batch(const DecBatch& b, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   ProfScope ps("decode", s);
-  if (b.out_dtype == kBF16) k_decode<uint16_t><<<(b.tiles_total + 3) / 4, 256, 0, s>>>(b);
-  else k_decode<float><<<(b.tiles_total + 3) / 4, 256, 0, s>>>(b);
+  const dim3 grid((b.T + 255) / 256, b.n * b.H);
+  if (b.out_dtype == kBF16) k_decode<uint16_t><<<grid, 256, 0, s>>>(b);
+  else k_decode<float><<<grid, 256, 0, s>>>(b);
   return hipGetLastError();
 }
 

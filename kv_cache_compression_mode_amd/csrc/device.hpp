@@ -58,6 +58,7 @@ __device__ __forceinline__ uint16_t ldg_u16(const void* p) {
   return *(const __attribute__((address_space(1))) uint16_t*)(p);
 }
 __device__ __forceinline__ void stg32(void* p, uint32_t v) { *(__attribute__((address_space(1))) uint32_t*)(p) = v; }
+__device__ __forceinline__ void stg16(void* p, u32x4 v) { *(__attribute__((address_space(1))) u32x4*)(p) = v; }
 
 template <typename T> __device__ __forceinline__ float load_as_f32(const T* p, int64_t i);
 template <> __device__ __forceinline__ float load_as_f32<float>(const float* p, int64_t i) { return p[i]; }

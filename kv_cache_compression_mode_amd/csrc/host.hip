@@ -913,14 +913,14 @@ void decode_records(int n, const jolt_shape* shape, const jolt_choice* ch, const
   const size_t n2 = static_cast<size_t>(D) * D;
   const uint16_t* Qt16 = reinterpret_cast<const uint16_t*>(static_cast<const char*>(rot_dev) + 2 * a256(4 * n2));
   char* wsp = static_cast<char*>(ws);
-  const int64_t tilesT = (T + 63) / 64;
   for (int i0 = 0; i0 < n; i0 += kDecBatch) {
     DecBatch b{};
     b.n = std::min(kDecBatch, n - i0);
+    b.H = static_cast<int32_t>(H);
     b.T = static_cast<int32_t>(T);
     b.out_dtype = shape->dtype == JOLT_BF16 ? kBF16 : kF32;
     b.Qt16 = Qt16;
-    int tiles = 0, wtiles = 0;
+    int wtiles = 0;
     for (int j = 0; j < b.n; ++j) {
       const jolt_choice c = ch[i0 + j];
       const BlobLayout L = blob_layout(H, T, D, c);
@@ -938,12 +938,11 @@ void decode_records(int n, const jolt_shape* shape, const jolt_choice* ch, const
       R.Whi = reinterpret_cast<uint16_t*>(wsp);
       R.Wlo = reinterpret_cast<uint16_t*>(wsp + (c.r_T ? wb : 0));
       wsp += c.r_T ? 2 * wb : 0;
-      R.tile0 = tiles;
       R.wtile0 = wtiles;
-      tiles += static_cast<int>(H * tilesT);
       wtiles += static_cast<int>(H * (R.r_Tp / 32));
     }
-    b.tiles_total = tiles;
+    b.out16 = 1;
+    for (int j = 0; j < b.n; ++j) b.out16 &= (reinterpret_cast<uintptr_t>(b.rec[j].out) & 15) == 0 ? 1 : 0;
     b.wtiles_total = wtiles;
     ck(launch_decode_batch(b, s));
   }

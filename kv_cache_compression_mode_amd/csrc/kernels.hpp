@@ -177,11 +177,12 @@ struct DecRec {
   uint16_t* Wlo;
   void* out;               // [H][T][D]
   int32_t r_T, r_D, r_Tp, bits;
-  int32_t tile0, wtile0;   // first decode tile / W tile of this record
+  int32_t wtile0;          // first W tile of this record
 };
 struct DecBatch {
   DecRec rec[kDecBatch];
-  int32_t n, T, out_dtype, tiles_total, wtiles_total;
+  int32_t n, H, T, out_dtype, wtiles_total;
+  int32_t out16;            // every record's out is 16-byte aligned
   const uint16_t* Qt16;    // bf16 [D][D], Qt16[c][d] = Q[d][c]
 };
 hipError_t launch_decode_batch(const DecBatch& b, hipStream_t s);

@@ -285,3 +285,25 @@ def test_decode_many_matches_single_records(J, rot, single):
         single_out = J.decode(b, H, T, c, rot)
         assert torch.equal(single_out, o)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("odt", [torch.bfloat16, torch.float32])
+def test_decode_into_unaligned_output(J, rot, single, odt):
+    """An output that starts one element past a 16-byte boundary takes the
+    element-wise store path and holds the same values as an aligned one."""
+    X0, a, Q = single
+    X = codec.round_to(X0, "bf16")
+    H, T, _ = X.shape
+    xd = to_dev(X, "bf16")
+    Ut32 = torch.from_numpy(np.ascontiguousarray(a["U_T"], dtype=np.float32)).cuda()
+    Ud32 = torch.from_numpy(np.ascontiguousarray(a["U_D"], dtype=np.float32)).cuda()
+    c = (96, 112, 3)
+    blob = J.encode(xd, c, Ut32, Ud32, rot)
+    ref = J.decode(blob, H, T, c, rot, dtype=odt)
+    buf = torch.full((H * T * D + 1,), 7.0, dtype=odt, device="cuda")
+    view = buf[1:].view(H, T, D)
+    assert view.data_ptr() % 16 != 0
+    J.decode(blob, H, T, c, rot, dtype=odt, out=view)
+    assert torch.equal(view, ref)
+    assert buf[0].item() == 7.0
+    torch.cuda.synchronize()
