@@ -542,6 +542,8 @@ template <typename TO>
 __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
   // one k step of W (hi, lo planes, 4 column tiles) per buffer, [plane][ct][lane][8]
   __shared__ __align__(16) uint16_t wl[2][2 * 4 * 64 * 8];
+  // Q^T bf16 in fragment order [ct][d / 16][lane][8], read by every wave
+  __shared__ __align__(16) uint16_t ql[4 * 8 * 64 * 8];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // a block = 256 rows (4 waves of 64) of one (record, head); the blocks of
   // one (record, head) share its W and run on one XCD
@@ -575,11 +577,20 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
     *reinterpret_cast<uint4*>(&wl[buf][(wave * 64 + lane) * 8]) = wh;
     *reinterpret_cast<uint4*>(&wl[buf][((4 + wave) * 64 + lane) * 8]) = wlo;
   };
+  // thread i moves the 16-byte fragments i + 256 j of Q^T
+  uint4 qv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = threadIdx.x + 256 * j, l = c & 63;
+    qv[j] = ldg16(b.Qt16 + (32 * (c >> 9) + (l & 31)) * D + 16 * ((c >> 6) & 7) + 8 * (l >> 5));
+  }
   if (nks > 0) {
     load_w(0);
     load_k(0);
-    store_w(0);
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(&ql[(threadIdx.x + 256 * j) * 8]) = qv[j];
+  if (nks > 0) store_w(0);
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
     const int buf = ks & 1;
@@ -609,7 +620,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
   const int bits = R.bits;
   const uint32_t qmask = (1u << bits) - 1u;
   // the streamed words of one d step (scales, code words), the next step's
-  // loaded during this one's dequantization and MFMAs (Q^T stays in cache)
+  // loaded during this one's dequantization and MFMAs (Q^T from LDS)
   uint32_t sw[2], w0[2], w1[2];
   auto load_d = [&](int d0) {
     const int dd = d0 + 8 * half;               // this lane's 8 features
@@ -634,7 +645,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
     const uint32_t csw[2] = {sw[0], sw[1]}, cw0[2] = {w0[0], w0[1]}, cw1[2] = {w1[0], w1[1]};
     uint4 cq[4];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) cq[ct] = ldg16(b.Qt16 + (32 * ct + r) * D + dd);
+    for (int ct = 0; ct < 4; ++ct) cq[ct] = *reinterpret_cast<const uint4*>(&ql[((ct * 8 + (d0 >> 4)) * 64 + lane) * 8]);
     if (d0 + 16 < D) load_d(d0 + 16);
     bf16x8 y[2];
 #pragma unroll
