@@ -540,8 +540,9 @@ __global__ __launch_bounds__(256) void k_make_w(DecBatch b) {
 // a time.
 template <typename TO>
 __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
-  // one k step of W (hi, lo planes, 4 column tiles) per buffer, [plane][ct][lane][8]
-  __shared__ __align__(16) uint16_t wl[2][2 * 4 * 64 * 8];
+  // two k steps of W (hi, lo planes, 4 column tiles) per buffer,
+  // [step][plane][ct][lane][8]
+  __shared__ __align__(16) uint16_t wl[2][2][2 * 4 * 64 * 8];
   // Q^T bf16 in fragment order [ct][d / 16][lane][8], read by every wave
   __shared__ __align__(16) uint16_t ql[4 * 8 * 64 * 8];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -554,28 +555,38 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
   const int r = lane & 31, half = lane >> 5;
   f32x16 acc[2][4] = {};
   const bool ua = (R.r_T % 8) == 0;
-  // U~_T rows of one k step (16 of r_T) streamed from memory and W's k step
-  // staged through LDS, both one step ahead of the MFMAs; each thread moves
-  // the hi and lo 16 bytes of (column tile = its wave, its lane)
-  bf16x8 a[2];
-  auto load_k = [&](int k0) {
-    const int kk = k0 + 8 * half;
+  // a stage = two k steps (32 of r_T; r_Tp is a multiple of 32): U~_T rows
+  // streamed from memory and W staged through LDS, both one stage ahead of
+  // the MFMAs; each thread moves the hi and lo 16 bytes of (column tile = its
+  // wave, its lane) of both steps
+  bf16x8 a[2][2];   // [step][rt]
+  auto load_k = [&](int st) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int64_t t = t0 + 32 * rt + r;
-      a[rt] = t < b.T ? load8_bf16(R.Ut + t * R.r_T, kk, R.r_T, ua) : zero8();
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kk = 32 * st + 16 * sub + 8 * half;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int64_t t = t0 + 32 * rt + r;
+        a[sub][rt] = t < b.T ? load8_bf16(R.Ut + t * R.r_T, kk, R.r_T, ua) : zero8();
+      }
     }
   };
-  const int nks = R.r_Tp / 16;
-  uint4 wh, wlo;
-  auto load_w = [&](int ks) {
-    const int64_t o = ((h * 4 + wave) * nks + ks) * 512 + lane * 8;   // fragment order
-    wh = ldg16(R.Whi + o);
-    wlo = ldg16(R.Wlo + o);
+  const int nks = R.r_Tp / 16, nst = nks / 2;
+  uint4 wh[2], wlo[2];
+  auto load_w = [&](int st) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int64_t o = ((h * 4 + wave) * nks + 2 * st + sub) * 512 + lane * 8;   // fragment order
+      wh[sub] = ldg16(R.Whi + o);
+      wlo[sub] = ldg16(R.Wlo + o);
+    }
   };
   auto store_w = [&](int buf) {
-    *reinterpret_cast<uint4*>(&wl[buf][(wave * 64 + lane) * 8]) = wh;
-    *reinterpret_cast<uint4*>(&wl[buf][((4 + wave) * 64 + lane) * 8]) = wlo;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      *reinterpret_cast<uint4*>(&wl[buf][sub][(wave * 64 + lane) * 8]) = wh[sub];
+      *reinterpret_cast<uint4*>(&wl[buf][sub][((4 + wave) * 64 + lane) * 8]) = wlo[sub];
+    }
   };
   // thread i moves the 16-byte fragments i + 256 j of Q^T
   uint4 qv[8];
@@ -584,37 +595,40 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
     const int c = threadIdx.x + 256 * j, l = c & 63;
     qv[j] = ldg16(b.Qt16 + (32 * (c >> 9) + (l & 31)) * D + 16 * ((c >> 6) & 7) + 8 * (l >> 5));
   }
-  if (nks > 0) {
+  if (nst > 0) {
     load_w(0);
     load_k(0);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(&ql[(threadIdx.x + 256 * j) * 8]) = qv[j];
-  if (nks > 0) store_w(0);
+  if (nst > 0) store_w(0);
   __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    const int buf = ks & 1;
-    const bf16x8 ca[2] = {a[0], a[1]};
-    if (ks + 1 < nks) {
-      load_w(ks + 1);
-      load_k(16 * (ks + 1));
-    }
-    bf16x8 ch[4], cl[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      ch[ct] = *reinterpret_cast<const bf16x8*>(&wl[buf][(ct * 64 + lane) * 8]);
-      cl[ct] = *reinterpret_cast<const bf16x8*>(&wl[buf][((4 + ct) * 64 + lane) * 8]);
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    const bf16x8 ca[2][2] = {{a[0][0], a[0][1]}, {a[1][0], a[1][1]}};
+    if (st + 1 < nst) {
+      load_w(st + 1);
+      load_k(st + 1);
     }
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int sub = 0; sub < 2; ++sub) {
+      bf16x8 ch[4], cl[4];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch[ct], ca[rt], acc[rt][ct], 0, 0, 0);
-        acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cl[ct], ca[rt], acc[rt][ct], 0, 0, 0);
+      for (int ct = 0; ct < 4; ++ct) {
+        ch[ct] = *reinterpret_cast<const bf16x8*>(&wl[buf][sub][(ct * 64 + lane) * 8]);
+        cl[ct] = *reinterpret_cast<const bf16x8*>(&wl[buf][sub][((4 + ct) * 64 + lane) * 8]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch[ct], ca[sub][rt], acc[rt][ct], 0, 0, 0);
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cl[ct], ca[sub][rt], acc[rt][ct], 0, 0, 0);
+        }
       }
     }
-    // the other buffer was last read in the previous step, before its barrier
-    if (ks + 1 < nks) store_w(buf ^ 1);
+    // the other buffer was last read in the previous stage, before its barrier
+    if (st + 1 < nst) store_w(buf ^ 1);
     __syncthreads();
   }
   const int bits = R.bits;
