@@ -192,7 +192,10 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
  * device-side header is not read back).  ws_bytes >=
  * jolt_decode_workspace_bytes.  Asynchronous.
  * Arithmetic: bf16 matrix cores with fp32 accumulation; W = G_h U_D^T is
- * carried as a hi + lo bf16 pair, the dequantized residual and Q in bf16. */
+ * carried as a hi + lo bf16 pair, the dequantized residual and Q in bf16.
+ * xhat_dev [H][T][D] row-major, caller-owned; it needs only the element's own
+ * alignment (outputs on 16-byte boundaries are written 16 bytes at a time,
+ * others one element at a time, with identical values). */
 jolt_status jolt_decode(const jolt_shape* shape, jolt_choice choice,
                         const void* blob_dev, size_t blob_bytes,
                         const void* rot_dev, void* xhat_dev,
