@@ -274,8 +274,8 @@ COMPARE_EXACT = {"mistral7b_t1024_flash"}
 CPU_SAMPLE = {"mistral7b_t4096_2x": 24, "mistral7b_t1024_flash": 64, "llama13b_t4096_2x": 2,
               "mistral7b_t32768_3x": 4}
 
-KERNELS = ("jacobi_update", "jacobi_solve", "jacobi128", "qr_panel", "qr_update", "gemm", "gemm_bf16", "band", "chase",
-           "tri_eig", "chase_back", "band_back", "encode_residual", "decode_w", "decode")
+KERNELS = ("qr_panel", "qr_update", "gemm", "gemm_bf16", "band", "chase", "tri_eig", "chase_back", "band_back",
+           "encode_w", "encode_residual", "quantize", "decode_w", "decode")
 CSRC = os.path.join(ROOT, "kv_cache_compression_mode_amd", "csrc")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 # fp32 vector arithmetic without packed instructions (which the build turns
@@ -307,8 +307,6 @@ ROOF = {
     "gemm_bf16": ("k_gemm_x: 128x128-tile GEMM on bf16 matrix cores (token and feature Grams, factor recovery, "
                   "Rayleigh and core products; fp32 operands enter as bf16 hi + lo)",
                   "k_gemm_x", r"k_gemm_x<", ("gemm.hip", "device.hpp"), MFMA_BF16_PEAK_TFLOPS, "mfma"),
-    "jacobi_update": ("k_jac_update: block-Jacobi rotation of A and V, fp32 matrix cores",
-                      "k_jac_update", r"k_jac_update\b", ("eig.hip", "device.hpp"), MFMA_FP32_PEAK_TFLOPS, "mfma"),
 }
 
 
@@ -388,8 +386,7 @@ def roofline_for(name, st, workload):
     """Roofline of a kernel from its launches in the timed steps: time from HIP
     events around every launch on its stream, algorithmic bytes and flops as
     the launches account them (the GEMM: operands read once and the output
-    written once, 2 M N K flops; the Jacobi update: counted on the device by
-    every workgroup that does work)."""
+    written once, 2 M N K flops)."""
     launches = max(st["launches"], 1)
     avg_ms = st["total_ms"] / launches
     bytes_l = st["bytes"] / launches

@@ -18,14 +18,20 @@
  *     evaluated on); T >= 1, H >= 1.
  *   - Every device buffer (inputs, outputs, compressed records, workspaces)
  *     is allocated and owned by the caller.  The library allocates no device
- *     memory and keeps no state between calls.
+ *     memory (the profiling hooks below excepted) and keeps no device state
+ *     between calls.  On the host it keeps a per-device pool of auxiliary HIP
+ *     streams (non-blocking, default priority), guarded by a mutex: a call
+ *     that forks work onto a second stream leases one for its duration, so
+ *     two calls in flight never share an auxiliary stream, and every event a
+ *     call records is created for that call alone.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously unless the entry point says it synchronizes.
  *   - Arguments are validated before any work is enqueued; on error nothing
  *     is enqueued and no output is written.  No C++ exception crosses the ABI.
  *   - A device-side fault surfaces as JOLT_EHIP from the next call that
- *     synchronizes.  Calls on distinct streams with distinct workspaces may
- *     run concurrently from several host threads.
+ *     synchronizes.  Calls on distinct streams with distinct workspaces and
+ *     output buffers may run concurrently from several host threads (the
+ *     profiling and debug hooks excepted).
  */
 #ifndef JOLT_H
 #define JOLT_H
@@ -64,8 +70,9 @@ typedef struct { int32_t r_T, r_D, bits; } jolt_choice;
 
 /* Allocation request for a whole cache: n_layers layers x {K, V}, all of one
  * shape.  Tensor index i = layer * 2 + kind (kind 0 = K, 1 = V).
- * Source: JoLT abstract, "a single Lagrangian dual ... per layer group and
- * separately for keys and values, under one byte budget". */
+ * Source: JoLT abstract, the sentence on the single Lagrangian dual that
+ * allocates Tucker ranks and residual bit-widths per layer group, keys and
+ * values separately, under one byte budget. */
 typedef struct {
   jolt_shape shape;
   int32_t n_layers;
@@ -148,8 +155,9 @@ jolt_status jolt_factors(const jolt_alloc_req* req, void* ws_dev, int32_t tensor
  * (jolt_rotation_bytes(D) bytes: fp32 Q, fp32 Q^T, bf16 Q^T and the three
  * bf16 parts hi, mid, lo of the fp32 Q (hi + mid + lo = Q exactly, in the
  * matrix-core fragment order of the encoder), each section 256-aligned).  Synchronizes `stream`.
- * Source: JoLT abstract, "a random orthogonal rotation followed by low-bit
- * quantization". */
+ * Source: JoLT abstract, the method sentence (the residual is rotated by a
+ * random orthogonal matrix before low-bit quantization); news article on
+ * JoLT, paragraph 4 (the rotation whitens the residual). */
 jolt_status jolt_rotation(uint64_t seed, int32_t D, void* q_dev, size_t q_bytes,
                           void* stream);
 
@@ -159,7 +167,13 @@ jolt_status jolt_rotation(uint64_t seed, int32_t D, void* q_dev, size_t q_bytes,
  * of 32 with per-group bf16 (offset, step) and packs the codes.  U_T_dev is
  * fp32 [T][ld_T], U_D_dev fp32 [D][ld_D]; rot_dev is a prepared rotation.
  * blob_bytes >= jolt_blob_bytes, ws_bytes >= jolt_encode_workspace_bytes.
- * Asynchronous.  Errors: EINVAL, ENOSPACE, EHIP. */
+ * Every buffer is caller-owned and must stay valid until `stream` has run
+ * the call's work; the record is written on the stream, the inputs only read.
+ * Asynchronous.  Errors: EINVAL, ENOSPACE, EHIP.
+ * Source: JoLT abstract, the method sentences (partial Tucker decomposition
+ * of the token and feature axes only, the head axis left intact; the energy
+ * the truncation drops restored by a randomly rotated low-bit residual);
+ * news article on JoLT, paragraphs 2 and 4. */
 jolt_status jolt_encode(const jolt_shape* shape, const void* x_dev, jolt_choice choice,
                         const float* U_T_dev, int32_t ld_T,
                         const float* U_D_dev, int32_t ld_D,
@@ -188,9 +202,15 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
                              void* ws_dev, size_t ws_bytes, void* stream);
 
 /* Decode one record: X^_h = U_T G_h U_D^T + dequant(codes)_h Q, written to
- * xhat_dev in shape->dtype.  shape/choice must describe the record (the
- * device-side header is not read back).  ws_bytes >=
- * jolt_decode_workspace_bytes.  Asynchronous.
+ * xhat_dev in shape->dtype.
+ * Source: JoLT abstract, the method sentences (the Tucker reconstruction plus
+ * the rotated residual restores the cache; quality is the relative Frobenius
+ * error of this reconstruction).
+ * The decode trusts its caller: shape and choice must be those the record
+ * was encoded with (jolt_header_parse reads them from a host copy of the
+ * header); the device-side header is not read, so a mismatch is not detected
+ * and gives wrong output inside the buffers the arguments describe.  ws_bytes
+ * >= jolt_decode_workspace_bytes.  Asynchronous.
  * Arithmetic: bf16 matrix cores with fp32 accumulation; W = G_h U_D^T is
  * carried as a hi + lo bf16 pair, the dequantized residual and Q in bf16.
  * xhat_dev [H][T][D] row-major, caller-owned; it needs only the element's own
@@ -240,12 +260,20 @@ jolt_status jolt_header_parse(const void* header, size_t bytes, jolt_shape* shap
 const char* jolt_status_str(jolt_status s);
 int32_t jolt_version(void);
 
+/* Testing hook, process-wide and not for concurrent use: the polls a bulge-
+ * chase wave of the eigensolver makes while waiting for its predecessor
+ * before it gives up (default 2^22, restored by a negative value).  A wait
+ * that gives up makes jolt_allocate return JOLT_EHIP; every kernel still
+ * ends normally.  Lets a test force that error path from the host. */
+void jolt_debug_chase_wait_limit(int32_t polls);
+
 /* ------------------------------------------------------------ profiling */
 
 /* Per-kernel statistics of the calls made while profiling was on: launches,
  * summed HIP-event time of those launches on their streams, and the
- * algorithmic HBM bytes and flops of the work they performed (for the Jacobi
- * update: counted on the device, active blocks only). */
+ * algorithmic HBM bytes and flops of the work they performed, as each launch
+ * accounts it on the host (operands read once, outputs written once; the
+ * flops the method needs, not the ones a kernel spends on its own scheme). */
 typedef struct {
   int64_t launches;
   double total_ms;
@@ -256,17 +284,13 @@ typedef struct {
 /* Select the kernels to profile: a comma-separated list of names, "*" for
  * all, NULL or "" to turn profiling off.  Every call synchronizes the device
  * and clears the records.  While on, the library records two HIP events
- * around each launch of a selected kernel on its stream; for "jacobi_update"
- * it also allocates 16 bytes of device counters per workgroup of the largest
- * grid seen (the only device memory the library allocates by itself; freed
- * by the next call).  Not safe with concurrent hot-path calls on other
- * streams.  Kernel names: "jacobi_update", "jacobi_solve", "jacobi128",
- * "qr_panel", "qr_update" (block reflectors applied to tall blocks), "gemm"
- * (fp32 matrix-core products), "gemm_bf16" (bf16 matrix-core products),
- * "band", "chase", "tri_eig", "chase_back",
- * "band_back" (the eigensolver stages), "encode_residual", "decode_w",
- * "decode".  "gemm" and "gemm_bf16" also account their algorithmic bytes and
- * flops. */
+ * around each launch of a selected kernel on its stream (host objects, no
+ * device memory).  Not safe with concurrent hot-path calls on other
+ * streams.  Kernel names: "qr_panel", "qr_update" (block reflectors applied
+ * to tall blocks), "gemm" (fp32 matrix-core products), "gemm_bf16" (bf16
+ * matrix-core products), "band", "chase", "tri_eig", "chase_back",
+ * "band_back" (the eigensolver stages), "encode_w", "encode_residual",
+ * "quantize", "decode_w", "decode". */
 jolt_status jolt_profile_enable(const char* kernels);
 
 /* Synchronizes the device, then reports the statistics of one kernel name

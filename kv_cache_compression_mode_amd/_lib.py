@@ -90,6 +90,7 @@ SIGNATURES = {
                                     C.POINTER(C.c_uint64)]),
     "jolt_status_str": (C.c_char_p, [C.c_int]),
     "jolt_version": (C.c_int32, []),
+    "jolt_debug_chase_wait_limit": (None, [C.c_int32]),
     "jolt_profile_enable": (C.c_int, [C.c_char_p]),
     "jolt_profile_query": (C.c_int, [C.c_char_p, C.POINTER(KernelStats)]),
 }

@@ -628,19 +628,6 @@ __global__ __launch_bounds__(256) void k_to_bf16_many(const float* const* ins, i
   }
 }
 
-// out[z][r + j*ld_out] = in[z][r*ld_in + idx[z][j]] (gather columns, emit column-major).
-__global__ __launch_bounds__(256) void k_gather_cols(const float* in, int64_t ld_in, int64_t in_batch,
-                                                      const int* idx, int64_t idx_batch,
-                                                      float* out, int64_t ld_out, int64_t out_batch,
-                                                      int64_t rows, int64_t ncols) {
-  const int64_t z = blockIdx.y;
-  const int64_t n = rows * ncols;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += 256ll * gridDim.x) {
-    const int64_t j = i / rows, r = i % rows;
-    out[z * out_batch + j * ld_out + r] = in[z * in_batch + r * ld_in + idx[z * idx_batch + j]];
-  }
-}
-
 // Sum of squares of each row of P [rows][cols] (fp64 accumulation).
 __global__ __launch_bounds__(256) void k_row_sumsq(const float* P, int64_t rows, int64_t cols,
                                                     int64_t batch, double* out, int64_t out_batch) {
@@ -849,14 +836,6 @@ hipError_t launch_to_bf16_many(const float* const* ins_dev, int64_t ld_in, uint1
                                int64_t cols, int n, hipStream_t s) {
   if (n <= 0 || rows * cols <= 0) return hipSuccess;
   k_to_bf16_many<<<dim3(grid1(rows * cols), n), 256, 0, s>>>(ins_dev, ld_in, outs_dev, rows, cols);
-  return hipGetLastError();
-}
-
-hipError_t launch_gather_cols(const float* in, int64_t ld_in, int64_t in_batch, const int* idx,
-                              int64_t idx_batch, float* out, int64_t ld_out, int64_t out_batch,
-                              int64_t rows, int64_t ncols, int batch, hipStream_t s) {
-  k_gather_cols<<<dim3(grid1(rows * ncols), batch), 256, 0, s>>>(in, ld_in, in_batch, idx, idx_batch,
-                                                                 out, ld_out, out_batch, rows, ncols);
   return hipGetLastError();
 }
 

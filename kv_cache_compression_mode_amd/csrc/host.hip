@@ -24,7 +24,6 @@ namespace {
 struct ProfRec {
   std::vector<std::pair<int, int>> ev;   // indices into the event pool
   double bytes = 0, flops = 0;           // host-side accounting
-  std::vector<std::pair<unsigned long long*, int64_t>> slots;   // device [count][2] counters
 };
 std::mutex g_prof_mu;
 std::string g_prof_sel;                  // "" off, "*" every kernel, else ",name,name,"
@@ -42,8 +41,6 @@ int pool_event() {
 }
 
 void prof_release() {
-  for (auto& kv : g_prof)
-    for (auto& sl : kv.second.slots) (void)hipFree(sl.first);
   g_prof.clear();
   g_pool_used = 0;
 }
@@ -52,20 +49,6 @@ void prof_release() {
 bool prof_enabled(const char* name) {
   if (g_prof_sel.empty()) return false;
   return g_prof_sel == "*" || g_prof_sel.find("," + std::string(name) + ",") != std::string::npos;
-}
-
-unsigned long long* prof_slots(const char* name, int64_t count) {
-  if (!prof_enabled(name) || count <= 0) return nullptr;
-  std::lock_guard<std::mutex> lk(g_prof_mu);
-  ProfRec& r = g_prof[name];
-  if (r.slots.empty() || r.slots.back().second < count) {
-    unsigned long long* p = nullptr;
-    const size_t bytes = static_cast<size_t>(count) * 2 * sizeof(unsigned long long);
-    if (hipMalloc(&p, bytes) != hipSuccess) return nullptr;
-    if (hipMemset(p, 0, bytes) != hipSuccess) { (void)hipFree(p); return nullptr; }
-    r.slots.emplace_back(p, count);
-  }
-  return r.slots.back().first;
 }
 
 void prof_add_work(const char* name, double bytes, double flops) {
@@ -103,22 +86,6 @@ constexpr int kD = 128;
 constexpr double kKappa32 = 17.60642599755;
 constexpr uint64_t kTagRotation = 0x4A4F4C54524F5431ull;   // "JOLTROT1"
 constexpr uint64_t kTagSketch = 0x4A4F4C54534B5431ull;     // "JOLTSKT1"
-// Jacobi thresholds: rotate when |a_pq| > max(tau_abs_rel * trace, tau_rel * sqrt(|a_pp a_qq|)).
-// An absolute floor near fp32 noise (1e-9 of the trace) keeps the noise-bulk
-// eigenvectors accurate: the truncation residual sits in that bulk.
-constexpr float kTauRel = 2e-6f;
-constexpr float kTauAbsRel = 1e-9f;
-constexpr int kMaxSweeps = 30;
-// A matrix of the block-Jacobi batch is done once its relative off-diagonal
-// Frobenius mass off/fro is below 2^-19, or once it has stopped falling (a
-// sweep removes less than 10% of it) after reaching 2^-12: what is left then
-// sits in entries below the rotation thresholds (about n * kTauAbsRel * trace
-// in total), and further sweeps only rotate pairs at the threshold, which no
-// longer moves the leading invariant subspaces or their captured energy.
-constexpr double kOffRel = 1.0 / (1 << 19);
-constexpr double kOffStall = 1.0 / (1 << 12);
-constexpr double kOffStallRatio = 0.9;
-
 struct HipFail {};
 inline void ck(hipError_t e) {
   if (e != hipSuccess) throw HipFail{};
@@ -414,14 +381,15 @@ struct AllocWS {
   // persistent
   float* UT; float* UD; double* lamT; double* lamD; double* frob2;
   const void** xptrs; uint64_t* tags;
+  int* status;         // device word: bit 0 set when a bounded wait of the eigensolver gave up
   bool x16;            // every input tensor is 16-byte aligned
   // scratch (chunk tensors)
-  float* G; float* V; float* J; int* active; int* rot; float* tauabs; double* offp;
+  float* G; float* V;
   float* GDpart;
   void* syev;
   void* syevD;
-  float* GD; float* GDc; float* VD;
-  int* order; float* Ucm; float* Vr; float* P; double* lam_tmp; float* qtau; int* perm; float* sgn;
+  float* GD; float* GDc;
+  float* Ucm; float* Vr; float* P; double* lam_tmp; float* qtau; int* perm; float* sgn;
   float* Om; float* Y; float* Z; float* Bm; float* Wr; float* Wd;
   // the feature-mode factor's own scratch (it runs beside the token path)
   float* qtauD; double* lamDt; int* permD; float* sgnD;
@@ -459,8 +427,6 @@ Dims dims_of(const jolt_alloc_req* r) {
   return d;
 }
 
-bool eig_jacobi();
-
 // Persistent outputs, the pointer and tag arrays of every tensor, then one
 // or two sets of chunk scratch (lanes): with two, consecutive chunks of half
 // the size alternate between two streams, so one chunk's single-CU-per-tensor
@@ -477,15 +443,15 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base, AllocWS* lane1 = nullpt
   per += static_cast<size_t>(std::max(d.T, d.HD)) * std::max<int64_t>(d.R, 1) * 8 + (1 << 20);
   per += static_cast<size_t>(gram_d_ksplit(d)) * d.D * d.D * 4;
   per += syev_top_work_bytes(d.D, static_cast<int>(d.D), 1);
-  if (!d.flash && d.R > 0) per += syev_top_work_bytes(d.n_pad, static_cast<int>(d.R), 1);
+  if (d.R > 0) per += syev_top_work_bytes(d.flash ? d.ell_pad : d.n_pad, static_cast<int>(d.R), 1);
   // up to 64 tensors (24 GiB of scratch) in flight.  Token eigenproblems of
   // n >= 2048 go in two lanes of half chunks: there the stages around the
   // chase are throughput-bound and overlap it; at smaller n they are
   // latency-bound, and halving the batch only doubles their count (the
-  // Jacobi and randomized paths keep one lane).
+  // randomized path keeps one lane).
   int chunk = static_cast<int>(std::max<size_t>(1, std::min<size_t>(64, (24ull << 30) / per)));
   chunk = std::min(chunk, nt);
-  const int nlanes = (chunk >= 2 && !eig_jacobi() && !d.flash && d.R > 0 && d.n_pad >= 2048) ? 2 : 1;
+  const int nlanes = (chunk >= 2 && !d.flash && d.R > 0 && d.n_pad >= 2048) ? 2 : 1;
   chunk = (chunk + nlanes - 1) / nlanes;
   w.chunk = chunk;
   w.nlanes = nlanes;
@@ -499,24 +465,17 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base, AllocWS* lane1 = nullpt
   w.frob2 = c.take<double>(nt);
   w.xptrs = c.take<const void*>(nt);
   w.tags = c.take<uint64_t>(nt);
+  w.status = c.take<int>(1);
   const int64_t n = d.flash ? d.ell_pad : d.n_pad;
   auto scratch = [&](AllocWS& w) {
     w.G = c.take<float>(static_cast<size_t>(chunk) * n * n);
     w.V = c.take<float>(static_cast<size_t>(chunk) * n * n);
-    w.J = c.take<float>(static_cast<size_t>(chunk) * (n / 64) * 64 * 64);
-    w.active = c.take<int>(static_cast<size_t>(chunk) * (n / 64));
-    w.rot = c.take<int>(chunk);
-    w.tauabs = c.take<float>(chunk);
-    w.offp = c.take<double>(static_cast<size_t>(chunk) * kOffBlocks * 2);
     w.GDpart = c.take<float>(static_cast<size_t>(chunk) * gram_d_ksplit(d) * d.D * d.D);
     w.syevD = c.take<char>(syev_top_work_bytes(d.D, static_cast<int>(d.D), chunk));
-    w.syev = (!d.flash && d.R > 0)
-                 ? static_cast<void*>(c.take<char>(syev_top_work_bytes(d.n_pad, static_cast<int>(d.R), chunk)))
-                 : nullptr;
+    w.syev = d.R > 0 ? static_cast<void*>(c.take<char>(syev_top_work_bytes(n, static_cast<int>(d.R), chunk)))
+                     : nullptr;
     w.GD = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
     w.GDc = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
-    w.VD = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
-    w.order = c.take<int>(static_cast<size_t>(chunk) * std::max<int64_t>(R, d.D));
     w.Ucm = c.take<float>(static_cast<size_t>(chunk) * d.T * R);
     w.Vr = c.take<float>(static_cast<size_t>(chunk) * std::max(d.nT, d.D) * std::max<int64_t>(R, d.D));
     w.P = c.take<float>(static_cast<size_t>(chunk) * R * d.HD);
@@ -558,18 +517,6 @@ GemmArgs gemm0() {
   return g;
 }
 
-// Jacobi to convergence on `batch` n x n matrices in w.G (V -> w.V); host loop
-// over sweeps, stopping when a sweep applies no rotation.
-// The token Gram's eigensolver: two-stage tridiagonal reduction by default,
-// block Jacobi with JOLT_EIG=jacobi.
-bool eig_jacobi() {
-  static const bool on = [] {
-    const char* e = std::getenv("JOLT_EIG");
-    return e && std::strcmp(e, "jacobi") == 0;
-  }();
-  return on;
-}
-
 bool trace_on() {
   static const bool on = [] {
     const char* e = std::getenv("JOLT_TRACE");
@@ -578,127 +525,88 @@ bool trace_on() {
   return on;
 }
 
-void run_jacobi(float* A, float* V, int64_t n, int batch, const AllocWS& w, hipStream_t s) {
-  JacobiWork jw{A, V, n, batch, w.J, w.active, w.rot, w.tauabs};
-  ck(jacobi_init(jw, kTauAbsRel, s));
-  const int nb = static_cast<int>(n / 32);
-  std::vector<int> cnt(batch);
-  std::vector<float> tau(batch);
-  std::vector<double> part(static_cast<size_t>(batch) * kOffBlocks * 2);
-  std::vector<char> done(batch, 0);
-  std::vector<double> prev(batch, INFINITY);
-  ck(hipMemcpyAsync(tau.data(), w.tauabs, sizeof(float) * batch, hipMemcpyDeviceToHost, s));
-  auto t_prev = std::chrono::steady_clock::now();
-  for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
-    ck(hipMemsetAsync(w.rot, 0, sizeof(int) * batch, s));
-    for (int r = 0; r < nb - 1; ++r) ck(jacobi_round(jw, r, kTauRel, s));
-    ck(jacobi_offnorm(A, n, batch, w.offp, s));
-    ck(hipMemcpyAsync(cnt.data(), w.rot, sizeof(int) * batch, hipMemcpyDeviceToHost, s));
-    ck(hipMemcpyAsync(part.data(), w.offp, sizeof(double) * part.size(), hipMemcpyDeviceToHost, s));
-    ck(hipStreamSynchronize(s));
-    int64_t tot = 0;
-    int busy = 0, newly = 0;
-    double worst = 0.0;
-    for (int z = 0; z < batch; ++z) {
-      tot += cnt[z];
-      busy += cnt[z] != 0;
-      double off2 = 0.0, dia2 = 0.0;
-      for (int b = 0; b < kOffBlocks; ++b) {
-        off2 += part[(static_cast<size_t>(z) * kOffBlocks + b) * 2];
-        dia2 += part[(static_cast<size_t>(z) * kOffBlocks + b) * 2 + 1];
-      }
-      const double rel = off2 > 0.0 ? std::sqrt(off2 / (off2 + dia2)) : 0.0;
-      worst = std::max(worst, rel);
-      const bool stalled = rel <= kOffStall && rel >= kOffStallRatio * prev[z];
-      prev[z] = rel;
-      if (!done[z] && (rel <= kOffRel || stalled)) {
-        done[z] = 1;
-        tau[z] = INFINITY;          // no pair of this matrix rotates again
-        ++newly;
-      }
-    }
-    if (trace_on()) {
-      const auto now = std::chrono::steady_clock::now();
-      std::fprintf(stderr,
-                   "[jolt] jacobi n=%lld batch=%d sweep %d: %lld rotations, %d matrices busy, "
-                   "max off/fro %.3e, %.3f ms\n",
-                   static_cast<long long>(n), batch, sweep, static_cast<long long>(tot), busy, worst,
-                   std::chrono::duration<double, std::milli>(now - t_prev).count());
-      t_prev = now;
-    }
-    if (!tot || std::all_of(done.begin(), done.end(), [](char c) { return c != 0; })) break;
-    if (newly) ck(hipMemcpyAsync(w.tauabs, tau.data(), sizeof(float) * batch, hipMemcpyHostToDevice, s));
-  }
+// Host-side HIP objects of one call.  Auxiliary streams (non-blocking,
+// default priority) are leased from a per-device pool and handed back when the
+// call ends, so concurrent calls never share one; events are created for the
+// call alone and destroyed with it, so no call can wait on another's record.
+// The pool is guarded by a mutex.  Device memory is never allocated here.
+struct StreamPool {
+  std::mutex mu;
+  std::map<int, std::vector<hipStream_t>> idle;   // device -> streams not leased
+};
+StreamPool& stream_pool() {
+  static StreamPool p;
+  return p;
 }
 
-// A second stream per device (default priority) for the feature-mode factor,
-// which depends only on the feature Gram and runs beside the token path; fork
-// and join through events.  Created on first use, kept for the process.
-struct AuxStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-AuxStream& aux_stream() {
-  static std::vector<AuxStream> per_dev;
-  int dev = 0;
-  ck(hipGetDevice(&dev));
-  if (static_cast<int>(per_dev.size()) <= dev) per_dev.resize(dev + 1);
-  AuxStream& a = per_dev[dev];
-  if (!a.s) {
-    ck(hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking));
-    ck(hipEventCreateWithFlags(&a.fork, hipEventDisableTiming));
-    ck(hipEventCreateWithFlags(&a.join, hipEventDisableTiming));
+class CallHip {
+ public:
+  CallHip() = default;
+  CallHip(const CallHip&) = delete;
+  CallHip& operator=(const CallHip&) = delete;
+  ~CallHip() {
+    for (hipEvent_t e : events_) (void)hipEventDestroy(e);
+    if (!leased_.empty()) {
+      StreamPool& p = stream_pool();
+      std::lock_guard<std::mutex> lk(p.mu);
+      auto& v = p.idle[dev_];
+      v.insert(v.end(), leased_.begin(), leased_.end());
+    }
   }
-  return a;
-}
-// The second lane's stream (non-blocking, default priority) and its fork / join events.
-AuxStream& lane_stream() {
-  static std::vector<AuxStream> per_dev;
-  int dev = 0;
-  ck(hipGetDevice(&dev));
-  if (static_cast<int>(per_dev.size()) <= dev) per_dev.resize(dev + 1);
-  AuxStream& a = per_dev[dev];
-  if (!a.s) {
-    ck(hipStreamCreateWithFlags(&a.s, hipStreamNonBlocking));
-    ck(hipEventCreateWithFlags(&a.fork, hipEventDisableTiming));
-    ck(hipEventCreateWithFlags(&a.join, hipEventDisableTiming));
+  // A stream no other call holds until this one ends.
+  hipStream_t lease() {
+    if (leased_.empty()) ck(hipGetDevice(&dev_));
+    hipStream_t st = nullptr;
+    {
+      StreamPool& p = stream_pool();
+      std::lock_guard<std::mutex> lk(p.mu);
+      auto& v = p.idle[dev_];
+      if (!v.empty()) {
+        st = v.back();
+        v.pop_back();
+      }
+    }
+    if (!st) ck(hipStreamCreateWithFlags(&st, hipStreamNonBlocking));
+    leased_.push_back(st);
+    return st;
   }
-  return a;
-}
-// Events marking each chunk's band reduction (grown on demand, kept per device).
-hipEvent_t* lane_marks(int count) {
-  static std::vector<std::vector<hipEvent_t>> per_dev;
-  int dev = 0;
-  ck(hipGetDevice(&dev));
-  if (static_cast<int>(per_dev.size()) <= dev) per_dev.resize(dev + 1);
-  std::vector<hipEvent_t>& v = per_dev[dev];
-  while (static_cast<int>(v.size()) < count) {
-    hipEvent_t e;
+  hipEvent_t event() {
+    hipEvent_t e = nullptr;
     ck(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-    v.push_back(e);
+    events_.push_back(e);
+    return e;
   }
-  return v.data();
-}
-// Runs the feature-mode factor on the auxiliary stream after the work queued
-// on s so far (the tridiagonal path; the Jacobi path shares scratch and stays
-// on s); join() makes s wait for it.
+
+ private:
+  int dev_ = 0;
+  std::vector<hipStream_t> leased_;
+  std::vector<hipEvent_t> events_;
+};
+
+// Runs the feature-mode factor on an auxiliary stream of the call after the
+// work queued on s so far; join() makes s wait for it.
 struct FeatureFork {
-  AuxStream* a = nullptr;
+  CallHip& hip;
   hipStream_t s;
-  explicit FeatureFork(hipStream_t s_) : s(s_) {}
+  hipStream_t aux = nullptr;
+  hipEvent_t join_ev = nullptr;
+  FeatureFork(CallHip& h, hipStream_t s_) : hip(h), s(s_) {}
   hipStream_t start() {
-    if (eig_jacobi()) return s;
-    a = &aux_stream();
-    ck(hipEventRecord(a->fork, s));
-    ck(hipStreamWaitEvent(a->s, a->fork, 0));
-    return a->s;
+    aux = hip.lease();
+    const hipEvent_t fork = hip.event();
+    ck(hipEventRecord(fork, s));
+    ck(hipStreamWaitEvent(aux, fork, 0));
+    return aux;
   }
   void done() {
-    if (a) ck(hipEventRecord(a->join, a->s));
+    if (!aux) return;
+    join_ev = hip.event();
+    ck(hipEventRecord(join_ev, aux));
   }
   void join() {
-    if (a) ck(hipStreamWaitEvent(s, a->join, 0));
-    a = nullptr;
+    if (join_ev) ck(hipStreamWaitEvent(s, join_ev, 0));
+    aux = nullptr;
+    join_ev = nullptr;
   }
 };
 
@@ -706,13 +614,7 @@ struct FeatureFork {
 void feature_factor(const Dims& d, int batch, int t0, const AllocWS& w, hipStream_t s) {
   const int64_t D = d.D;
   ck(hipMemcpyAsync(w.GDc, w.GD, sizeof(float) * batch * D * D, hipMemcpyDeviceToDevice, s));
-  if (eig_jacobi()) {
-    ck(jacobi_small128(w.GD, w.VD, batch, kTauRel, kTauAbsRel, kMaxSweeps, s));
-    ck(topk_diag(w.GD, D, batch, static_cast<int>(D), w.order, s));
-    ck(launch_gather_cols(w.VD, D, D * D, w.order, D, w.Vr, D, D * D, D, D, batch, s));
-  } else {
-    ck(syev_top(w.GD, D, batch, static_cast<int>(D), w.Vr, nullptr, w.syevD, s));
-  }
+  ck(syev_top(w.GD, D, batch, static_cast<int>(D), w.Vr, nullptr, w.syevD, s, w.status));
   ck(householder_qr(w.Vr, D, D, D, D * D, batch, w.qtauD, s));
   // Rayleigh quotients diag(U^T G U): W = G U (column-major), then column dots
   GemmArgs g = gemm0();
@@ -742,7 +644,7 @@ void token_finalize(const Dims& d, int batch, int t0, const AllocWS& w, int xdt,
                         T * R, w.lamT + static_cast<size_t>(t0) * R, R, batch, w.perm, w.sgn, s));
 }
 
-void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, hipStream_t s) {
+void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, CallHip& hip, hipStream_t s) {
   const int64_t T = d.T, D = d.D, HD = d.HD, n = d.n_pad, R = d.R;
   const void* const* xp = reinterpret_cast<const void* const*>(w.xptrs);
   ck(hipMemsetAsync(w.G, 0, sizeof(float) * batch * n * n, s));
@@ -759,7 +661,7 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   }
   // column-major; the tridiagonal path reads the lower triangle only
   g.C = w.G; g.c_m = 1; g.c_n = n; g.c_batch = n * n;
-  g.c_lower = eig_jacobi() ? 0 : 1;
+  g.c_lower = 1;
   ck(launch_gemm(g, batch, s));
   if (d.dual) {
     ck(launch_sum_diag_blocks(w.G, d.H, D, w.GD, batch, s));   // n == HD here
@@ -772,43 +674,27 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     gd.ksplit = gram_d_ksplit(d); gd.partial = w.GDpart;
     ck(launch_gemm(gd, batch, s));
   }
-  FeatureFork ff(s);
+  FeatureFork ff(hip, s);
   feature_factor(d, batch, t0, w, ff.start());
   ff.done();
   if (R == 0) {
     ff.join();
     return;
   }
-  // leading eigenvectors V_R of the token Gram, column-major with leading dimension ldv
-  const float* VR;
-  int64_t ldv, vr_batch;
-  bool in_ucm = false;
-  if (eig_jacobi()) {
-    run_jacobi(w.G, w.V, n, batch, w, s);
-    ck(topk_diag(w.G, n, batch, static_cast<int>(R), w.order, s));
-    if (d.dual) {     // n == HD
-      ck(launch_gather_cols(w.V, n, n * n, w.order, R, w.Vr, HD, HD * R, HD, R, batch, s));
-    } else {
-      ck(launch_gather_cols(w.V, n, n * n, w.order, R, w.Ucm, T, T * R, T, R, batch, s));
-      in_ucm = true;
-    }
-    VR = w.Vr; ldv = HD; vr_batch = HD * R;
-  } else {
-    ck(syev_top(w.G, n, batch, static_cast<int>(R), w.V, nullptr, w.syev, s, w.band_done));
-    VR = w.V; ldv = n; vr_batch = n * n;
-  }
-  if (in_ucm) {
-  } else if (d.dual) {
+  // leading eigenvectors V_R of the token Gram: the first R columns of w.V
+  // (column-major, leading dimension n)
+  ck(syev_top(w.G, n, batch, static_cast<int>(R), w.V, nullptr, w.syev, s, w.status, w.band_done));
+  if (d.dual) {
     // U' = X_(T) V_R (T x R, column-major)
     GemmArgs gu = gemm0();
     gu.a_ptrs = xp; gu.a_dtype = xdt; gu.ptr_align16 = w.x16;
     gu.M = T; gu.N = R; gu.K = HD;
     gu.am = plain(D); gu.ak = segmented(D, T * D, 1);
-    gu.B = VR; gu.bk = plain(1); gu.bn = plain(ldv); gu.b_batch = vr_batch;
+    gu.B = w.V; gu.bk = plain(1); gu.bn = plain(n); gu.b_batch = n * n;
     gu.C = w.Ucm; gu.c_m = 1; gu.c_n = T; gu.c_batch = T * R;
     ck(launch_gemm(gu, batch, s));
   } else {
-    ck(copy_cols(VR, ldv, vr_batch, w.Ucm, T, T * R, T, R, batch, s));
+    ck(copy_cols(w.V, n, n * n, w.Ucm, T, T * R, T, R, batch, s));
   }
   ck(householder_qr(w.Ucm, T, R, T, T * R, batch, w.qtau, s));
   token_finalize(d, batch, t0, w, xdt, s);
@@ -816,7 +702,7 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
 }
 
 void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, int q, uint64_t seed,
-                   hipStream_t s) {
+                   CallHip& hip, hipStream_t s) {
   const int64_t T = d.T, D = d.D, HD = d.HD, R = d.R, ell = d.ell, ep = d.ell_pad;
   const void* const* xp = reinterpret_cast<const void* const*>(w.xptrs);
   // feature mode: exact Gram path (a sketch of width D spans all of R^D)
@@ -829,7 +715,7 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     gd.ksplit = gram_d_ksplit(d); gd.partial = w.GDpart;
     ck(launch_gemm(gd, batch, s));
   }
-  FeatureFork ff(s);
+  FeatureFork ff(hip, s);
   feature_factor(d, batch, t0, w, ff.start());
   ff.done();
   if (R == 0) {
@@ -881,9 +767,10 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     g.C = w.G; g.c_m = ep; g.c_n = 1; g.c_batch = ep * ep;
     ck(launch_gemm(g, batch, s));
   }
-  run_jacobi(w.G, w.V, ep, batch, w, s);
-  ck(topk_diag(w.G, ep, batch, static_cast<int>(R), w.order, s));
-  ck(launch_gather_cols(w.V, ep, ep * ep, w.order, R, w.Wr, ell, ell * R, ell, R, batch, s));
+  // top R eigenvectors of the ell x ell (zero-padded) B B^T, by the same
+  // tridiagonal solver as the exact path, then their first ell rows
+  ck(syev_top(w.G, ep, batch, static_cast<int>(R), w.V, nullptr, w.syev, s, w.status));
+  ck(copy_cols(w.V, ep, ep * ep, w.Wr, ell, ell * R, ell, R, batch, s));
   {
     GemmArgs g = gemm0();                       // U = Q W_R (T x R, column-major)
     g.M = T; g.N = R; g.K = ell;
@@ -1152,6 +1039,7 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, v
     const int xdt = req->shape.dtype == JOLT_BF16 ? kBF16 : kF32;
     const int64_t N = d.H * d.T * d.D;
     ck(hipMemsetAsync(w.frob2, 0, sizeof(double) * nt, s));
+    ck(hipMemsetAsync(w.status, 0, sizeof(int), s));
     // every tensor's pointer and sketch tag, uploaded once
     std::vector<const void*> ptrs(x_dev, x_dev + nt);
     std::vector<uint64_t> tags(nt);
@@ -1161,40 +1049,48 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, v
     ck(hipMemcpyAsync(w.tags, tags.data(), sizeof(uint64_t) * nt, hipMemcpyHostToDevice, s));
     ck(hipStreamSynchronize(s));
     // chunks alternate between the lanes: lane 0 on s, lane 1 on a second
-    // stream forked from s and joined back into it
-    AuxStream* ls = nullptr;
+    // stream of this call, forked from s and joined back into it
+    CallHip hip;
+    hipStream_t ls = nullptr;
     if (w.nlanes > 1 && nt > w.chunk) {
-      ls = &lane_stream();
-      ck(hipEventRecord(ls->fork, s));
-      ck(hipStreamWaitEvent(ls->s, ls->fork, 0));
+      ls = hip.lease();
+      const hipEvent_t fork = hip.event();
+      ck(hipEventRecord(fork, s));
+      ck(hipStreamWaitEvent(ls, fork, 0));
     }
     // a chunk on the second lane starts once the previous chunk's band
     // reduction is queued ahead of it, so that chunk's chase (one CU per
     // tensor) runs beside this chunk's matrix-core stages
-    hipEvent_t* marks = ls ? lane_marks(nt / w.chunk + 1) : nullptr;
+    std::vector<hipEvent_t> marks;
+    if (ls)
+      for (int c = 0; c * w.chunk < nt; ++c) marks.push_back(hip.event());
     for (int t0 = 0, c = 0; t0 < nt; t0 += w.chunk, ++c) {
       const int batch = std::min(w.chunk, nt - t0);
       const bool second = ls && (c & 1);
       AllocWS wl = second ? w1 : w;
-      hipStream_t sl = second ? ls->s : s;
+      hipStream_t sl = second ? ls : s;
       wl.xptrs = w.xptrs + t0;
       wl.tags = w.tags + t0;
-      wl.band_done = marks ? marks[c] : nullptr;
-      if (marks && c > 0) ck(hipStreamWaitEvent(sl, marks[c - 1], 0));
+      wl.band_done = ls ? marks[c] : nullptr;
+      if (ls && c > 0) ck(hipStreamWaitEvent(sl, marks[c - 1], 0));
       ck(launch_sumsq(reinterpret_cast<const void* const*>(wl.xptrs), batch, N, xdt, w.frob2 + t0, sl));
-      if (d.flash) analyze_flash(d, batch, t0, wl, xdt, req->power_iters, req->seed, sl);
-      else analyze_exact(d, batch, t0, wl, xdt, sl);
+      if (d.flash) analyze_flash(d, batch, t0, wl, xdt, req->power_iters, req->seed, hip, sl);
+      else analyze_exact(d, batch, t0, wl, xdt, hip, sl);
     }
     if (ls) {
-      ck(hipEventRecord(ls->join, ls->s));
-      ck(hipStreamWaitEvent(s, ls->join, 0));
+      const hipEvent_t join = hip.event();
+      ck(hipEventRecord(join, ls));
+      ck(hipStreamWaitEvent(s, join, 0));
     }
     const int R = static_cast<int>(d.R);
     std::vector<double> lt(static_cast<size_t>(nt) * std::max(R, 1)), ld(static_cast<size_t>(nt) * d.D), f2(nt);
     if (R > 0) ck(hipMemcpyAsync(lt.data(), w.lamT, sizeof(double) * nt * R, hipMemcpyDeviceToHost, s));
     ck(hipMemcpyAsync(ld.data(), w.lamD, sizeof(double) * nt * d.D, hipMemcpyDeviceToHost, s));
     ck(hipMemcpyAsync(f2.data(), w.frob2, sizeof(double) * nt, hipMemcpyDeviceToHost, s));
+    int status = 0;
+    ck(hipMemcpyAsync(&status, w.status, sizeof(int), hipMemcpyDeviceToHost, s));
     ck(hipStreamSynchronize(s));
+    if (status != 0) return JOLT_EHIP;          // an eigensolver wait gave up: the factors are not valid
     for (int i = 0; i < nt; ++i)
       if (!std::isfinite(f2[i])) return JOLT_ERANGE;
     if (plan->spectra_T && R > 0) std::memcpy(plan->spectra_T, lt.data(), sizeof(double) * nt * R);
@@ -1523,6 +1419,8 @@ const char* jolt_status_str(jolt_status s) {
 
 int32_t jolt_version(void) { return static_cast<int32_t>(kVersion); }
 
+void jolt_debug_chase_wait_limit(int32_t polls) { set_chase_spin_limit(polls < 0 ? (1 << 22) : polls); }
+
 jolt_status jolt_profile_enable(const char* kernels) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (hipDeviceSynchronize() != hipSuccess) return JOLT_EHIP;   // no recorded event in flight
@@ -1554,16 +1452,6 @@ jolt_status jolt_profile_query(const char* kernel, jolt_kernel_stats* out) {
     }
     st.bytes = r.bytes;
     st.flops = r.flops;
-    for (const auto& sl : r.slots) {
-      std::vector<unsigned long long> c(static_cast<size_t>(sl.second) * 2);
-      if (hipMemcpy(c.data(), sl.first, c.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost) !=
-          hipSuccess)
-        return JOLT_EHIP;
-      for (size_t i = 0; i < c.size(); i += 2) {
-        st.bytes += static_cast<double>(c[i]);
-        st.flops += static_cast<double>(c[i + 1]);
-      }
-    }
   }
   *out = st;
   return JOLT_OK;

@@ -13,7 +13,6 @@ enum { kBF16 = 0, kF32 = 1 };
 // workgroup, each added to only by the workgroup of that grid position, so
 // launches serialized on one stream accumulate without atomics.
 bool prof_enabled(const char* name);
-unsigned long long* prof_slots(const char* name, int64_t count);   // nullptr when off
 void prof_add_work(const char* name, double bytes, double flops);
 struct ProfScope {
   ProfScope(const char* name, hipStream_t s);
@@ -66,9 +65,6 @@ hipError_t launch_to_bf16(const float* in, int64_t ld_in, uint16_t* out, int64_t
                           hipStream_t s);
 hipError_t launch_to_bf16_many(const float* const* ins_dev, int64_t ld_in, uint16_t* const* outs_dev, int64_t rows,
                                int64_t cols, int n, hipStream_t s);
-hipError_t launch_gather_cols(const float* in, int64_t ld_in, int64_t in_batch, const int* idx,
-                              int64_t idx_batch, float* out, int64_t ld_out, int64_t out_batch,
-                              int64_t rows, int64_t ncols, int batch, hipStream_t s);
 hipError_t launch_row_sumsq(const float* P, int64_t rows, int64_t cols, int64_t batch_stride,
                             int batch, double* out, int64_t out_batch, hipStream_t s);
 hipError_t launch_col_dot(const float* A, const float* B, int64_t m, int64_t ncols, int64_t ld,
@@ -77,28 +73,6 @@ hipError_t launch_pad_copy(const float* in, int64_t n, int64_t in_batch, float* 
                            int batch, hipStream_t s);
 hipError_t launch_sum_diag_blocks(const float* C, int64_t H, int64_t D, float* GD, int batch,
                                   hipStream_t s);
-
-// ---- symmetric eigensolver (block Jacobi) ----
-// A: [batch][n][n] (n multiple of 64), V: [batch][n][n] (initialized by the solver).
-struct JacobiWork {
-  float* A; float* V; int64_t n; int batch;
-  float* J;          // [batch][n/64][64][64]
-  int* active;       // [batch][n/64]
-  int* rot_count;    // [batch]
-  float* tau_abs;    // [batch]
-};
-hipError_t jacobi_init(const JacobiWork& w, float tau_abs_rel, hipStream_t s);
-hipError_t jacobi_round(const JacobiWork& w, int round, float tau_rel, hipStream_t s);
-// Per matrix, kOffBlocks partial sums (off-diagonal squares, diagonal squares)
-// in fp64: part[z][block][2].  The host adds them in a fixed order.
-constexpr int kOffBlocks = 64;
-hipError_t jacobi_offnorm(const float* A, int64_t n, int batch, double* part, hipStream_t s);
-// Scalar Jacobi to convergence on 128 x 128 matrices (one workgroup each):
-// A -> diagonal (in place), V <- eigenvectors.
-hipError_t jacobi_small128(float* A, float* V, int batch, float tau_rel, float tau_abs_rel,
-                           int max_sweeps, hipStream_t s);
-// Indices of the R largest diagonal entries of each A, descending (ties: lower index).
-hipError_t topk_diag(const float* A, int64_t n, int batch, int R, int* idx, hipStream_t s);
 
 // ---- Householder QR, column-major panels [batch][k][ld] (column j at j*ld) ----
 // In place: on return the panel holds the explicit orthonormal Q (m x k, m >= k)
@@ -117,9 +91,13 @@ size_t panel_factor_scratch_floats(int64_t m, int batch);
 // columns (column-major, ld n), eigenvalue-descending; lam (optional, fp64
 // [batch][R]) the eigenvalues.  work: syev_top_work_bytes(n, R, batch).
 size_t syev_top_work_bytes(int64_t n, int R, int batch);
-// band_done, when given, is recorded on s once the band reduction is queued
+// status: a device int the bulge chase ORs 1 into when one of its bounded
+// waits gives up (cleared by the caller, read back at its next sync).
+// band_done, when given, is recorded on s once the band reduction is queued.
 hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam, void* work, hipStream_t s,
-                    hipEvent_t band_done = nullptr);
+                    int* status, hipEvent_t band_done = nullptr);
+// Polls a bulge-chase wave makes before its wait gives up (default 2^22).
+void set_chase_spin_limit(int polls);
 hipError_t copy_cols(const float* in, int64_t ld_in, int64_t in_batch, float* out, int64_t ld_out,
                      int64_t out_batch, int64_t rows, int64_t cols, int batch, hipStream_t s);
 // write_r: when the panel fits one block (m - c0 <= panel_block_rows()), R

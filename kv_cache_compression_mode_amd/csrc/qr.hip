@@ -926,13 +926,10 @@ int64_t panel_block_rows() { return kLeaf; }
 hipError_t panel_factor(float* A, int64_t m, int64_t ld, int64_t bstride, int64_t c0, int nb, int batch,
                         float* Vp, int64_t vstride, float* Tp, int64_t tstride, float* taus, int64_t k,
                         float* scratch, hipStream_t s, int write_r) {
-  static bool lds_attr = false;
-  if (!lds_attr) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_qr_leaf), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(RW * 64 * 33 * sizeof(float)));
-    if (e != hipSuccess) return e;
-    lds_attr = true;
-  }
+  static const hipError_t lds_attr =   // once per process (thread-safe initialization)
+      hipFuncSetAttribute(reinterpret_cast<const void*>(k_qr_leaf), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(RW * 64 * 33 * sizeof(float)));
+  if (lds_attr != hipSuccess) return lds_attr;
   float* Qb = scratch;                                            // [batch][m][32]
   float* Rs = Qb + static_cast<size_t>(batch) * m * 32;           // [batch][kStack]
   float* Qt = Rs + static_cast<size_t>(batch) * kStack;           // [batch][kStack]

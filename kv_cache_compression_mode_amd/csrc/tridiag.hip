@@ -24,6 +24,8 @@
 // (JoLT abstract: Tucker factors from the leading singular vectors of the
 // mode unfoldings); every Householder step is the textbook one (beta =
 // -sign(alpha) ||x||, tau = (beta - alpha) / beta).
+#include <atomic>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -162,7 +164,8 @@ __device__ __forceinline__ float dot16(const A& a, const B& b) {
 }
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void k_chase(float* Bw_g, int n, float* Rf_g, int64_t rf_stride, int S) {
+__global__ __launch_bounds__(NW * 64) void k_chase(float* Bw_g, int n, float* Rf_g, int64_t rf_stride, int S,
+                                                   int* status, int spin_limit) {
   extern __shared__ float chase_lds_raw[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -201,14 +204,20 @@ __global__ __launch_bounds__(NW * 64) void k_chase(float* Bw_g, int n, float* Rf
   // (after its stores) and waits, before prefetching at tick t, for its
   // predecessor to have finished tick t - 1.  Waits point to strictly
   // earlier ticks of other waves, so they always end; the spin is bounded
-  // all the same.
+  // all the same (spin_limit polls): a wait that gives up sets bit 0 of
+  // *status (a vector atomic, read back by the host) and the wave carries
+  // on, so the kernel still ends and the caller sees the failure.
   __shared__ int tick_done[NW];
   if ((threadIdx.x & 63) == 0) tick_done[wave] = -1;
   __syncthreads();
   const int pred = (wave + NW - 1) % NW;
   auto wait_pred = [&](int t_need) {
-    for (int spin = 0; spin < (1 << 22); ++spin) {
+    for (int spin = 0;; ++spin) {
       if (__hip_atomic_load(&tick_done[pred], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= t_need) break;
+      if (spin >= spin_limit) {
+        if (lane == 0) __hip_atomic_fetch_or(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -1268,9 +1277,15 @@ int ksplit_for(int64_t K) {
 
 size_t syev_top_work_bytes(int64_t n, int R, int batch) { return syev_layout(n, R, batch).total; }
 
+namespace {
+std::atomic<int> g_chase_spin_limit{1 << 22};
+}  // namespace
+
+void set_chase_spin_limit(int polls) { g_chase_spin_limit.store(polls < 0 ? 0 : polls); }
+
 hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam_out, void* work,
-                    hipStream_t s, hipEvent_t band_done) {
-  if (n % SBW != 0 || n > 32768 || R < 1 || R > n) return hipErrorInvalidValue;
+                    hipStream_t s, int* status, hipEvent_t band_done) {
+  if (n % SBW != 0 || n > 32768 || R < 1 || R > n || !status) return hipErrorInvalidValue;
   const SyevLayout Lw = syev_layout(n, R, batch);
   char* wb = static_cast<char*>(work);
   float* Vst = reinterpret_cast<float*>(wb + Lw.v_off);
@@ -1376,20 +1391,20 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     int S = static_cast<int>((K0 + nw - 1) / nw);
     if (S < 4) S = 4;
     const size_t lds = static_cast<size_t>(nw) * sizeof(ChaseLds);
-    static bool attr = false;
-    if (!attr) {
-      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chase<8>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, 16 * sizeof(ChaseLds))) != hipSuccess)
-        return e;
-      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chase<16>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, 16 * sizeof(ChaseLds))) != hipSuccess)
-        return e;
-      attr = true;
-    }
+    static const hipError_t attr = [] {   // once per process (thread-safe initialization)
+      hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chase<8>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 16 * sizeof(ChaseLds));
+      if (r == hipSuccess)
+        r = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chase<16>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 16 * sizeof(ChaseLds));
+      return r;
+    }();
+    if (attr != hipSuccess) return attr;
     {
       ProfScope ps("chase", s);
-      if (nw == 8) k_chase<8><<<batch, 8 * 64, lds, s>>>(Bw, static_cast<int>(n), Rf, Lw.nref * RFS, S);
-      else k_chase<16><<<batch, 16 * 64, lds, s>>>(Bw, static_cast<int>(n), Rf, Lw.nref * RFS, S);
+      const int spin = g_chase_spin_limit.load();
+      if (nw == 8) k_chase<8><<<batch, 8 * 64, lds, s>>>(Bw, static_cast<int>(n), Rf, Lw.nref * RFS, S, status, spin);
+      else k_chase<16><<<batch, 16 * 64, lds, s>>>(Bw, static_cast<int>(n), Rf, Lw.nref * RFS, S, status, spin);
       // algorithmic work: the band read and written once, every reflector
       // written once; per step (b = 32) the reflector's two-sided action on the
       // diagonal block (w = D v, D - v w^T - w v^T + c v v^T: 5 b^2 flops), its
@@ -1406,13 +1421,9 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
   // ---- stage 3: top R eigenpairs of the tridiagonal (fp64)
   {
     const size_t lds = static_cast<size_t>(2 * n) * sizeof(double);
-    static bool attr = false;
-    if (!attr) {
-      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bisect),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, 65536)) != hipSuccess)
-        return e;
-      attr = true;
-    }
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_bisect),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
+    if (attr != hipSuccess) return attr;
     if (lds > 65536) return hipErrorInvalidValue;
     const unsigned gx = static_cast<unsigned>((R + IVW - 1) / IVW);
     double* nrm = reinterpret_cast<double*>(wb + Lw.nrm_off);

@@ -36,6 +36,35 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_buf(t: torch.Tensor, device, name: str, nbytes: int = 0) -> None:
+    """A contiguous tensor on `device` holding at least `nbytes` bytes."""
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.device == torch.device(device), f"{name} must be on {device}, not {t.device}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(t.numel() * t.element_size() >= nbytes, f"{name} holds {t.numel() * t.element_size()} bytes, "
+                                                   f"needs {nbytes}")
+
+
+def _check_out(o: torch.Tensor, device, H: int, T: int, dtype: torch.dtype, name: str) -> None:
+    _check_buf(o, device, name)
+    _need(tuple(o.shape) == (H, T, D_FEATURES), f"{name} must have shape {(H, T, D_FEATURES)}, not "
+                                                 f"{tuple(o.shape)}")
+    _need(o.dtype == dtype, f"{name} must be {dtype}, not {o.dtype}")
+
+
+def _check_factor(f: torch.Tensor, device, rows: int, cols: int, name: str) -> None:
+    _need(isinstance(f, torch.Tensor) and f.dtype == torch.float32 and f.dim() == 2 and f.stride(1) == 1,
+          f"{name} must be fp32 [rows, ld] with unit column stride")
+    _need(f.device == torch.device(device), f"{name} must be on {device}")
+    _need(f.shape[0] >= rows and f.shape[1] >= cols and f.stride(0) >= cols,
+          f"{name} {tuple(f.shape)} must have at least {rows} rows and {cols} columns")
+
+
 def make_shape(H: int, T: int, D: int, dtype) -> Shape:
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     return Shape(H, T, D, code)
@@ -186,18 +215,24 @@ def plan_from_spectra(req: AllocReq, spectra_T: np.ndarray, spectra_D: np.ndarra
 def encode(x: torch.Tensor, choice, U_T: torch.Tensor | None, U_D: torch.Tensor | None,
            rot: torch.Tensor, seed: int = 0, out: torch.Tensor | None = None) -> torch.Tensor:
     """Compress one [H, T, 128] tensor into a device record (uint8 tensor)."""
+    _need(x.dim() == 3 and x.shape[2] == D_FEATURES, f"x must be [H, T, {D_FEATURES}]")
+    _check_buf(x, x.device, "x")
     H, T, D = x.shape
     shape = make_shape(H, T, D, x.dtype)
     ch = Choice(*choice)
     nb = lib().jolt_blob_bytes(C.byref(shape), ch)
     if nb == 0:
         check(_lib.JOLT_EINVAL, "jolt_blob_bytes")
+    _check_buf(rot, x.device, "rot", lib().jolt_rotation_bytes(D))
+    if out is not None:
+        _check_buf(out, x.device, "out", nb)
     blob = out if out is not None else torch.empty(nb, dtype=torch.uint8, device=x.device)
     nws = lib().jolt_encode_workspace_bytes(C.byref(shape), ch)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
-    for f in (U_T, U_D):
-        if f is not None and (f.dtype != torch.float32 or f.dim() != 2 or f.stride(1) != 1):
-            raise ValueError("factors must be fp32 [rows, ld] with unit column stride")
+    if choice[0] > 0:
+        _need(U_T is not None and U_D is not None, "a Tucker choice needs both factors")
+        _check_factor(U_T, x.device, T, choice[0], "U_T")
+        _check_factor(U_D, x.device, D, choice[1], "U_D")
     ut = U_T.data_ptr() if U_T is not None else None
     ud = U_D.data_ptr() if U_D is not None else None
     ldt = U_T.stride(0) if U_T is not None else 0
@@ -221,10 +256,16 @@ def encode_many(xs, choices, factors, rot: torch.Tensor, seed: int = 0, outs=Non
     H, T, D = x0.shape
     shape = make_shape(H, T, D, x0.dtype)
     ch = (Choice * n)(*[Choice(*c) for c in choices])
+    _need(x0.dim() == 3 and x0.shape[2] == D_FEATURES, f"tensors must be [H, T, {D_FEATURES}]")
+    _need(len(choices) == n, "one choice per tensor")
     for x in xs:
-        if x.shape != x0.shape or x.dtype != x0.dtype or not x.is_contiguous():
-            raise ValueError("all tensors must be contiguous with one shape and dtype")
+        if x.shape != x0.shape or x.dtype != x0.dtype or not x.is_contiguous() or x.device != x0.device:
+            raise ValueError("all tensors must be contiguous with one shape, dtype and device")
+    _check_buf(rot, x0.device, "rot", lib().jolt_rotation_bytes(D))
     if outs is not None:
+        _need(len(outs) == n, "one output record per tensor")
+        for i, o in enumerate(outs):
+            _check_buf(o, x0.device, f"outs[{i}]", lib().jolt_blob_bytes(C.byref(shape), ch[i]))
         blobs = outs
     else:
         # one allocation cut into 256-aligned records
@@ -249,9 +290,12 @@ def encode_many(xs, choices, factors, rot: torch.Tensor, seed: int = 0, outs=Non
             utp[i], udp[i] = ut.value, ud.value
             ldt[i], ldd[i] = ld.value, factors.req.shape.D
     else:
-        for f in (f for pair in factors for f in pair):
-            if f is not None and (f.dtype != torch.float32 or f.dim() != 2 or f.stride(1) != 1):
-                raise ValueError("factors must be fp32 [rows, ld] with unit column stride")
+        _need(len(factors) == n, "one factor pair per tensor")
+        for i, (c, pair) in enumerate(zip(choices, factors)):
+            if c[0] > 0:
+                _need(pair[0] is not None and pair[1] is not None, "a Tucker choice needs both factors")
+                _check_factor(pair[0], x0.device, T, c[0], f"factors[{i}][0]")
+                _check_factor(pair[1], x0.device, D, c[1], f"factors[{i}][1]")
         utp = (C.c_void_p * n)(*[f[0].data_ptr() if f[0] is not None else None for f in factors])
         udp = (C.c_void_p * n)(*[f[1].data_ptr() if f[1] is not None else None for f in factors])
         ldt = (C.c_int32 * n)(*[f[0].stride(0) if f[0] is not None else 0 for f in factors])
@@ -276,8 +320,17 @@ def decode(blob: torch.Tensor, H: int, T: int, choice, rot: torch.Tensor, dtype=
     """Reconstruct [H, T, 128] from a record."""
     shape = make_shape(H, T, D_FEATURES, dtype)
     ch = Choice(*choice)
+    nb = lib().jolt_blob_bytes(C.byref(shape), ch)
+    if nb == 0:
+        check(_lib.JOLT_EINVAL, "jolt_blob_bytes")
+    _check_buf(blob, blob.device, "blob", nb)
+    _check_buf(rot, blob.device, "rot", lib().jolt_rotation_bytes(D_FEATURES))
+    if out is not None:
+        _check_out(out, blob.device, H, T, dtype, "out")
     xh = out if out is not None else torch.empty((H, T, D_FEATURES), dtype=dtype, device=blob.device)
     nws = lib().jolt_decode_workspace_bytes(C.byref(shape), ch)
+    if workspace is not None:
+        _check_buf(workspace, blob.device, "workspace", nws)
     ws = workspace if workspace is not None else torch.empty(max(nws, 1), dtype=torch.uint8,
                                                               device=blob.device)
     check(lib().jolt_decode(C.byref(shape), ch, blob.data_ptr(), blob.numel(), rot.data_ptr(),
@@ -294,8 +347,15 @@ def decode_many(blobs, H: int, T: int, choices, rot: torch.Tensor, outs, workspa
                 dtype=torch.bfloat16) -> None:
     """Reconstruct several records of one shape into the given output tensors."""
     n = len(blobs)
+    _need(len(choices) == n and len(outs) == n, "one choice and one output per record")
     shape = make_shape(H, T, D_FEATURES, dtype)
     ch = (Choice * n)(*[Choice(*c) for c in choices])
+    dev = workspace.device
+    _check_buf(workspace, dev, "workspace", decode_many_workspace_bytes(H, T, choices, dtype))
+    _check_buf(rot, dev, "rot", lib().jolt_rotation_bytes(D_FEATURES))
+    for i in range(n):
+        _check_buf(blobs[i], dev, f"blobs[{i}]", lib().jolt_blob_bytes(C.byref(shape), ch[i]))
+        _check_out(outs[i], dev, H, T, dtype, f"outs[{i}]")
     bp = (C.c_void_p * n)(*[b.data_ptr() for b in blobs])
     bb = (C.c_size_t * n)(*[b.numel() for b in blobs])
     op = (C.c_void_p * n)(*[o.data_ptr() for o in outs])
@@ -306,6 +366,9 @@ def decode_many(blobs, H: int, T: int, choices, rot: torch.Tensor, outs, workspa
 def quantize(y: torch.Tensor, bits: int):
     """Group quantizer alone: y [rows, 128] fp32 -> (scales [rows, 4, 2] bf16 bits as int16,
     codes [rows, 4, 4*bits] uint8)."""
+    _need(y.dim() == 2 and y.shape[1] == D_FEATURES and y.dtype == torch.float32,
+          f"y must be fp32 [rows, {D_FEATURES}]")
+    _check_buf(y, y.device, "y")
     rows, D = y.shape
     sc = torch.empty((rows, D // 32, 2), dtype=torch.int16, device=y.device)
     cd = torch.empty((rows, D // 32, 4 * bits), dtype=torch.uint8, device=y.device)

@@ -13,14 +13,14 @@ import bench
 FIELDS = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
 
 
-def _csv(path, counter, jac_values, copy_values):
+def _csv(path, counter, kernel_values, copy_values):
     with open(path, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=FIELDS)
         w.writeheader()
         i = 0
-        for v in jac_values:
+        for v in kernel_values:
             w.writerow(dict(Correlation_Id=i, Dispatch_Id=i, Counter_Name=counter, Counter_Value=v,
-                            Kernel_Name="jolt::(anonymous namespace)::k_jac_update(float*, ...)"))
+                            Kernel_Name="void jolt::(anonymous namespace)::k_chase<8>(float*, ...)"))
             i += 1
         for v in copy_values:
             w.writerow(dict(Correlation_Id=i, Dispatch_Id=i, Counter_Name=counter, Counter_Value=v,
@@ -37,7 +37,7 @@ def test_record_and_invalidate(tmp_path):
     src = tmp_path / "k.hip"
     src.write_text("kernel v1")
     rec_path = str(tmp_path / "traffic.json")
-    bench.record_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), copy, "jacobi_update",
+    bench.record_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), copy, "chase",
                          "test_workload", rec_path, (str(src),))
     rec = json.load(open(rec_path))
     assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
