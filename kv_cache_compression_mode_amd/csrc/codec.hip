@@ -735,12 +735,6 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
   }
 }
 
-__global__ void k_header(uint32_t* blob, uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, uint32_t w4,
-                         uint32_t w5, uint32_t w6, uint32_t w7, uint32_t w8, uint32_t w9, uint32_t w10,
-                         uint32_t w11, uint32_t w12, uint32_t w13, uint32_t w14, uint32_t w15) {
-  const uint32_t w[16] = {w0, w1, w2, w3, w4, w5, w6, w7, w8, w9, w10, w11, w12, w13, w14, w15};
-  if (threadIdx.x < 16) blob[threadIdx.x] = w[threadIdx.x];
-}
 
 }  // namespace
 
@@ -748,6 +742,7 @@ hipError_t launch_quantize(const float* Y, int64_t rows, int bits, uint16_t* sca
                            hipStream_t s) {
   const int64_t ng = rows * (D / 32);
   if (ng == 0) return hipSuccess;
+  ProfScope ps("quantize", s);
   k_quantize<<<(ng + 255) / 256, 256, 0, s>>>(Y, ng, bits, reinterpret_cast<uint32_t*>(scales),
                                               reinterpret_cast<uint32_t*>(codes));
   return hipGetLastError();
@@ -795,17 +790,28 @@ hipError_t launch_decode_batch(const DecBatch& b, hipStream_t s) {
   return hipGetLastError();
 }
 
-__global__ void k_header_many(uint32_t* const* blobs, const uint32_t* words) {
-  if (threadIdx.x < 16) blobs[blockIdx.x][threadIdx.x] = words[blockIdx.x * 16 + threadIdx.x];
+// One workgroup of 64 threads per record: words 0..63 of the head (header,
+// then zeros), then the section paddings, one byte per thread.
+__device__ __forceinline__ void write_head(uint32_t* blob, const RecordHead& h) {
+  const int t = threadIdx.x;
+  blob[t] = t < 16 ? h.w[t] : 0u;
+  uint8_t* b = reinterpret_cast<uint8_t*>(blob);
+#pragma unroll
+  for (int j = 0; j < 5; ++j)
+    for (uint32_t k = t; k < h.pad[2 * j + 1]; k += 64) b[h.pad[2 * j] + k] = 0;
 }
-hipError_t launch_write_headers(uint32_t* const* blobs_dev, const uint32_t* words_dev, int n, hipStream_t s) {
+__global__ __launch_bounds__(64) void k_header_many(uint32_t* const* blobs, const RecordHead* heads) {
+  write_head(blobs[blockIdx.x], heads[blockIdx.x]);
+}
+__global__ __launch_bounds__(64) void k_header(uint32_t* blob, RecordHead head) { write_head(blob, head); }
+
+hipError_t launch_write_headers(uint32_t* const* blobs_dev, const RecordHead* heads_dev, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  k_header_many<<<n, 64, 0, s>>>(blobs_dev, words_dev);
+  k_header_many<<<n, 64, 0, s>>>(blobs_dev, heads_dev);
   return hipGetLastError();
 }
-hipError_t launch_write_header(void* blob, const uint32_t* w, hipStream_t s) {
-  k_header<<<1, 64, 0, s>>>(static_cast<uint32_t*>(blob), w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7],
-                            w[8], w[9], w[10], w[11], w[12], w[13], w[14], w[15]);
+hipError_t launch_write_header(void* blob, const RecordHead& head, hipStream_t s) {
+  k_header<<<1, 64, 0, s>>>(static_cast<uint32_t*>(blob), head);
   return hipGetLastError();
 }
 

@@ -174,6 +174,27 @@ BlobLayout blob_layout(int64_t H, int64_t T, int64_t D, jolt_choice c) {
   return L;
 }
 
+// The head of a record: header words and the padding after each section.
+RecordHead record_head(int64_t H, int64_t T, int64_t D, int32_t dtype, jolt_choice c, uint64_t seed) {
+  const BlobLayout L = blob_layout(H, T, D, c);
+  RecordHead h{};
+  const uint32_t w[16] = {kMagic, kVersion, static_cast<uint32_t>(H), static_cast<uint32_t>(T),
+                          static_cast<uint32_t>(D), static_cast<uint32_t>(dtype),
+                          static_cast<uint32_t>(c.r_T), static_cast<uint32_t>(c.r_D),
+                          static_cast<uint32_t>(c.bits), static_cast<uint32_t>(kGroup),
+                          static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), 0, 0, 0, 0};
+  std::memcpy(h.w, w, sizeof(w));
+  const size_t groups = static_cast<size_t>(H * T * D / kGroup);
+  const size_t ends[5] = {L.ut + 2ull * T * c.r_T, L.ud + 2ull * D * c.r_D, L.g + 2ull * H * c.r_T * c.r_D,
+                          L.sc + 4ull * groups, L.cd + 4ull * c.bits * groups};
+  const size_t next[5] = {L.ud, L.g, L.sc, L.cd, L.total};
+  for (int j = 0; j < 5; ++j) {
+    h.pad[2 * j] = static_cast<uint32_t>(ends[j]);
+    h.pad[2 * j + 1] = static_cast<uint32_t>(next[j] - ends[j]);
+  }
+  return h;
+}
+
 bool shape_ok(const jolt_shape* s) {
   return s && s->H >= 1 && s->T >= 1 && s->D == kD && (s->dtype == JOLT_BF16 || s->dtype == JOLT_F32);
 }
@@ -662,7 +683,7 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   // column-major; the tridiagonal path reads the lower triangle only
   g.C = w.G; g.c_m = 1; g.c_n = n; g.c_batch = n * n;
   g.c_lower = 1;
-  ck(launch_gemm(g, batch, s));
+  ck(launch_gemm(g, batch, s, "gram"));
   if (d.dual) {
     ck(launch_sum_diag_blocks(w.G, d.H, D, w.GD, batch, s));   // n == HD here
   } else {
@@ -672,7 +693,7 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     gd.am = plain(1); gd.ak = plain(D); gd.bk = plain(D); gd.bn = plain(1);
     gd.C = w.GD; gd.c_m = D; gd.c_n = 1; gd.c_batch = D * D;
     gd.ksplit = gram_d_ksplit(d); gd.partial = w.GDpart;
-    ck(launch_gemm(gd, batch, s));
+    ck(launch_gemm(gd, batch, s, "gram"));
   }
   FeatureFork ff(hip, s);
   feature_factor(d, batch, t0, w, ff.start());
@@ -713,7 +734,7 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     gd.am = plain(1); gd.ak = plain(D); gd.bk = plain(D); gd.bn = plain(1);
     gd.C = w.GD; gd.c_m = D; gd.c_n = 1; gd.c_batch = D * D;
     gd.ksplit = gram_d_ksplit(d); gd.partial = w.GDpart;
-    ck(launch_gemm(gd, batch, s));
+    ck(launch_gemm(gd, batch, s, "gram"));
   }
   FeatureFork ff(hip, s);
   feature_factor(d, batch, t0, w, ff.start());
@@ -784,6 +805,23 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   ff.join();
 }
 
+// Algorithmic work of the residual path of one tensor (encode or decode):
+// the Tucker reconstruction in its cheaper product order, 2 min(r_T,
+// r_T r_D / D + r_D) flops per element, and the rotation, 2 D; the bytes are
+// the input (or output) once, the codes and scales once, and the record's
+// factors and core once.
+struct PathWork {
+  double bytes, flops;
+};
+PathWork residual_work(int64_t H, int64_t T, int64_t D, jolt_choice c, int elem_bytes) {
+  const double N = static_cast<double>(H * T * D);
+  const double rT = c.r_T, rD = c.r_D;
+  const double rec = c.r_T > 0 ? 2.0 * std::min(rT, rT * rD / static_cast<double>(D) + rD) : 0.0;
+  const double codes = N * (c.bits + 1) / 8.0;          // b-bit codes + bf16 (offset, step) per 32
+  const double facs = 2.0 * (T * rT + D * rD + H * rT * rD);
+  return {N * elem_bytes + codes + facs, N * (rec + 2.0 * D)};
+}
+
 int64_t rtp_of(int r_T) { return (static_cast<int64_t>(r_T) + 31) / 32 * 32; }
 // the encoder's W parts: k padded to whole 64-value chunks
 int64_t enc_rtp(int r_T) { return (static_cast<int64_t>(r_T) + 63) / 64 * 64; }
@@ -831,6 +869,15 @@ void decode_records(int n, const jolt_shape* shape, const jolt_choice* ch, const
     b.out16 = 1;
     for (int j = 0; j < b.n; ++j) b.out16 &= (reinterpret_cast<uintptr_t>(b.rec[j].out) & 15) == 0 ? 1 : 0;
     b.wtiles_total = wtiles;
+    if (prof_enabled("decode")) {
+      double by = 0.0, fl = 0.0;
+      for (int j = 0; j < b.n; ++j) {
+        const PathWork pw = residual_work(H, T, D, ch[i0 + j], shape->dtype == JOLT_BF16 ? 2 : 4);
+        by += pw.bytes;
+        fl += pw.flops;
+      }
+      prof_add_work("decode", by, fl);
+    }
     ck(launch_decode_batch(b, s));
   }
 }
@@ -891,7 +938,7 @@ EncManyLayout enc_many_layout(int n, const jolt_shape* shape, const jolt_choice*
   const size_t nt = idx.size();
   L.n_ptrs = 4 * nt + 2 * nt + 5 * nt * H + static_cast<size_t>(n);
   L.arr_off = off;
-  off += a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n) + a256(4ull * 16 * n);
+  off += a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n) + a256(sizeof(RecordHead) * n);
   L.total = off + 256;
   return L;
 }
@@ -1164,13 +1211,12 @@ jolt_status jolt_encode(const jolt_shape* shape, const void* x_dev, jolt_choice 
     ea.Q3 = Q3; ea.bits = c.bits;
     ea.scales = reinterpret_cast<uint16_t*>(blob + L.sc);
     ea.codes = reinterpret_cast<uint8_t*>(blob + L.cd);
+    if (prof_enabled("encode_residual")) {
+      const PathWork pw = residual_work(H, T, D, c, xdt == kBF16 ? 2 : 4);
+      prof_add_work("encode_residual", pw.bytes - 2.0 * (D * rD + H * rT * rD), pw.flops);
+    }
     ck(launch_encode_residual(ea, s));
-    const uint32_t hdr[16] = {kMagic, kVersion, static_cast<uint32_t>(H), static_cast<uint32_t>(T),
-                              static_cast<uint32_t>(D), static_cast<uint32_t>(shape->dtype),
-                              static_cast<uint32_t>(rT), static_cast<uint32_t>(rD),
-                              static_cast<uint32_t>(c.bits), static_cast<uint32_t>(kGroup),
-                              static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), 0, 0, 0, 0};
-    ck(launch_write_header(blob, hdr, s));
+    ck(launch_write_header(blob, record_head(H, T, D, shape->dtype, c, seed), s));
     return JOLT_OK;
   });
 }
@@ -1216,10 +1262,10 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
     // host images of the pointer arrays, the residual arguments and the header words
     std::vector<const void*> ptr(L.n_ptrs, nullptr);
     std::vector<EncodeArgs> args(n);
-    std::vector<uint32_t> words(static_cast<size_t>(16) * n);
+    std::vector<RecordHead> heads(n);
     void** dptr = reinterpret_cast<void**>(ws + L.arr_off);
     EncodeArgs* dargs = reinterpret_cast<EncodeArgs*>(ws + L.arr_off + a256(8 * L.n_ptrs));
-    uint32_t* dwords = reinterpret_cast<uint32_t*>(ws + L.arr_off + a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n));
+    RecordHead* dheads = reinterpret_cast<RecordHead*>(ws + L.arr_off + a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n));
     size_t np = 0;
     auto slots = [&](size_t k) { const size_t o = np; np += k; return o; };
     struct GroupPtrs { size_t ut_in, ut_out, ud_in, ud_out, pa, pb, g2a, g2b, g2c, g3a, g3b; };
@@ -1270,19 +1316,15 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
       ea.Q3 = Q3; ea.bits = c.bits;
       ea.scales = reinterpret_cast<uint16_t*>(blob(i) + B.sc);
       ea.codes = reinterpret_cast<uint8_t*>(blob(i) + B.cd);
-      const uint32_t hdr[16] = {kMagic, kVersion, static_cast<uint32_t>(H), static_cast<uint32_t>(T),
-                                static_cast<uint32_t>(D), static_cast<uint32_t>(shape->dtype),
-                                static_cast<uint32_t>(c.r_T), static_cast<uint32_t>(c.r_D),
-                                static_cast<uint32_t>(c.bits), static_cast<uint32_t>(kGroup),
-                                static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), 0, 0, 0, 0};
-      std::memcpy(&words[static_cast<size_t>(16) * i], hdr, sizeof(hdr));
+      heads[i] = record_head(H, T, D, shape->dtype, c, seed);
     }
     // one upload of the host images (pageable memory: the call copies before returning)
     {
-      std::vector<char> img(a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n) + a256(4ull * 16 * n), 0);
+      std::vector<char> img(a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n) + a256(sizeof(RecordHead) * n), 0);
       std::memcpy(img.data(), ptr.data(), 8 * L.n_ptrs);
       std::memcpy(img.data() + a256(8 * L.n_ptrs), args.data(), sizeof(EncodeArgs) * n);
-      std::memcpy(img.data() + a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n), words.data(), 4ull * 16 * n);
+      std::memcpy(img.data() + a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n), heads.data(),
+                  sizeof(RecordHead) * n);
       ck(hipMemcpyAsync(dptr, img.data(), img.size(), hipMemcpyHostToDevice, s));
       ck(hipStreamSynchronize(s));
     }
@@ -1339,8 +1381,19 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
                       reinterpret_cast<uint16_t*>(ws + L.w_off[g]), 3 * H * D * rTp, m, static_cast<int>(H),
                       static_cast<int>(rT), static_cast<int>(rD), static_cast<int>(rTp), s));
     }
+    if (prof_enabled("encode_residual")) {
+      // the residual kernel reads X and U~_T and writes codes and scales (the
+      // core and U~_D enter through W, formed beforehand)
+      double by = 0.0, fl = 0.0;
+      for (int i = 0; i < n; ++i) {
+        const PathWork pw = residual_work(H, T, D, choices[i], xdt == kBF16 ? 2 : 4);
+        by += pw.bytes - 2.0 * (D * choices[i].r_D + H * choices[i].r_T * choices[i].r_D);
+        fl += pw.flops;
+      }
+      prof_add_work("encode_residual", by, fl);
+    }
     ck(launch_encode_residual_many(dargs, n, H, T, xdt, s));
-    ck(launch_write_headers(reinterpret_cast<uint32_t* const*>(dp(blob_slot)), dwords, n, s));
+    ck(launch_write_headers(reinterpret_cast<uint32_t* const*>(dp(blob_slot)), dheads, n, s));
     return JOLT_OK;
   });
 }
@@ -1381,6 +1434,8 @@ jolt_status jolt_quantize(const float* y_dev, int64_t rows, int32_t D, int32_t b
   if (rows == 0) return JOLT_OK;                       // nothing to do; pointers may be NULL
   if (!y_dev || !scales_dev || !codes_dev) return JOLT_EINVAL;
   return guard([&]() -> jolt_status {
+    // fp32 rows read once, b-bit codes and the bf16 (offset, step) pair per group written once
+    prof_add_work("quantize", static_cast<double>(rows) * D * (4.0 + (bits + 1) / 8.0), 0.0);
     ck(launch_quantize(y_dev, rows, bits, static_cast<uint16_t*>(scales_dev),
                        static_cast<uint8_t*>(codes_dev), static_cast<hipStream_t>(stream)));
     return JOLT_OK;

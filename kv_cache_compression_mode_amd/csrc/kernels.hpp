@@ -56,7 +56,8 @@ struct GemmArgs {
   int ptr_align16;
 };
 
-hipError_t launch_gemm(const GemmArgs& g, int batch, hipStream_t s);
+// scope: the profiling name of the launch (default "gemm_bf16" or "gemm" by the units it runs on)
+hipError_t launch_gemm(const GemmArgs& g, int batch, hipStream_t s, const char* scope = nullptr);
 hipError_t launch_sumsq(const void* const* xs_dev, int ntensors, int64_t n, int dtype, double* out,
                         hipStream_t s);
 hipError_t launch_sketch(float* out, int64_t rows, int64_t cols, uint64_t seed, const uint64_t* tags,
@@ -164,8 +165,16 @@ struct DecBatch {
   const uint16_t* Qt16;    // bf16 [D][D], Qt16[c][d] = Q[d][c]
 };
 hipError_t launch_decode_batch(const DecBatch& b, hipStream_t s);
-hipError_t launch_write_header(void* blob, const uint32_t* words16, hipStream_t s);
-// 16 words words_dev[i * 16 ..] into the header of blobs_dev[i], i < n
-hipError_t launch_write_headers(uint32_t* const* blobs_dev, const uint32_t* words_dev, int n, hipStream_t s);
+// The 256-byte head of a record (the 64-byte header, zeros to 256) and the
+// padding after each of its five sections, zeroed, so that every byte of a
+// record is defined: pad[2 j] = byte offset, pad[2 j + 1] = length (< 256).
+struct RecordHead {
+  uint32_t w[16];
+  uint32_t pad[10];
+  uint32_t unused[6];
+};
+hipError_t launch_write_header(void* blob, const RecordHead& head, hipStream_t s);
+// heads_dev[i] into blobs_dev[i], i < n
+hipError_t launch_write_headers(uint32_t* const* blobs_dev, const RecordHead* heads_dev, int n, hipStream_t s);
 
 }  // namespace jolt

@@ -132,3 +132,37 @@ def test_binding_rejects_bad_buffers(J):
     out = J.decode(blob, H, T, ch, rot)      # the valid call still works
     torch.cuda.synchronize()
     assert out.shape == (H, T, D)
+
+
+def test_record_reloaded_from_disk_decodes_identically(J, tmp_path):
+    """A record is self-contained bytes: written to a file, read back and
+    uploaded again, it decodes to the same output, and every one of its bytes
+    (header padding and section tails included) is written by the encoder."""
+    from kv_cache_compression_mode_amd import _lib  # noqa: F401
+    H, T = 2, 200                                 # ragged T: sections end off 256-byte boundaries
+    xs = _cache(H, T, 1, seed=15)
+    res = J.allocate(xs, ratio=2.0)
+    rot = J.rotation(0)
+    outs = []
+    for k in (0, 1):
+        ch = res.choice_of(0, k)
+        Ut, Ud = res.factors(k)
+        nb = J.blob_bytes(H, T, D, ch)
+        first = torch.full((nb,), 0xAB, dtype=torch.uint8, device="cuda")
+        second = torch.full((nb,), 0x5C, dtype=torch.uint8, device="cuda")
+        J.encode(xs[0][k], ch, Ut, Ud, rot, out=first)
+        J.encode(xs[0][k], ch, Ut, Ud, rot, out=second)
+        torch.cuda.synchronize()
+        host = first.cpu().numpy()
+        np.testing.assert_array_equal(host, second.cpu().numpy())   # no byte left as it was
+        path = tmp_path / f"rec{k}.bin"
+        host.tofile(path)
+        back = torch.from_numpy(np.fromfile(path, dtype=np.uint8)).cuda()
+        shape, choice, seed = J.header_parse(back[:64].cpu().numpy().tobytes())
+        assert shape == (H, T, D, 0) and choice == tuple(ch) and seed == 0
+        a = J.decode(first, H, T, ch, rot)
+        b = J.decode(back, H, T, choice, rot)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+        outs.append(b)
+    assert all(o.shape == (H, T, D) for o in outs)
