@@ -231,6 +231,27 @@ jolt_status jolt_decode_many(int32_t n, const jolt_shape* shape, const jolt_choi
                              const void* rot_dev, void* const* outs,
                              void* ws_dev, size_t ws_bytes, void* stream);
 
+/* Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): jolt_decode_many without a workspace argument.  Its scratch
+ * (the W = G U_D^T planes of the records of one launch) is a file-scope
+ * device array of jolt_decode_static_scratch_bytes() bytes (32 MiB), one
+ * copy per GPU, held until the process ends; its address is looked up once
+ * per device on the first call there.  The call allocates nothing: no
+ * hipMalloc, no hipFree, no allocating library routine.  Records are
+ * decoded in launches whose planes fit the array (so more launches than
+ * jolt_decode_many when they do not all fit), with the same kernels and
+ * arithmetic: the output is identical.  Errors: EINVAL as jolt_decode_many;
+ * ENOSPACE when a blob is short or one record's planes (2 * 256-aligned
+ * 2 H D ceil32(r_T) bytes) exceed the array.  Every call on one GPU shares
+ * that GPU's array, so calls that overlap in time on one GPU (other streams,
+ * other threads) race on it and must be serialized by the caller.
+ * Asynchronous. */
+size_t jolt_decode_static_scratch_bytes(void);
+jolt_status jolt_decode_many_static(int32_t n, const jolt_shape* shape, const jolt_choice* choices,
+                                    const void* const* blobs, const size_t* blob_bytes,
+                                    const void* rot_dev, void* const* outs, void* stream);
+
 /* Group quantizer alone (rows == 0 is a no-op; pointers may then be NULL):
  * rows x D fp32 rotated residual in y_dev ->
  * scales bf16 [rows][D/32][2] and packed codes [rows][D/32][4*bits].

@@ -80,6 +80,10 @@ SIGNATURES = {
     "jolt_decode_many": (C.c_int, [C.c_int32, C.POINTER(Shape), C.POINTER(Choice), C.POINTER(C.c_void_p),
                                    C.POINTER(C.c_size_t), C.c_void_p, C.POINTER(C.c_void_p), C.c_void_p,
                                    C.c_size_t, C.c_void_p]),
+    "jolt_decode_static_scratch_bytes": (C.c_size_t, []),
+    "jolt_decode_many_static": (C.c_int, [C.c_int32, C.POINTER(Shape), C.POINTER(Choice), C.POINTER(C.c_void_p),
+                                          C.POINTER(C.c_size_t), C.c_void_p, C.POINTER(C.c_void_p),
+                                          C.c_void_p]),
     "jolt_quantize": (C.c_int, [C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p,
                                 C.c_void_p]),
     "jolt_plan_from_spectra": (C.c_int, [C.POINTER(AllocReq), C.POINTER(C.c_double), C.c_int32,

@@ -488,7 +488,7 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base, AllocWS* lane1 = nullpt
   w.tags = c.take<uint64_t>(nt);
   w.status = c.take<int>(1);
   const int64_t n = d.flash ? d.ell_pad : d.n_pad;
-  auto scratch = [&](AllocWS& w) {
+  auto carve_scratch = [&](AllocWS& w) {
     w.G = c.take<float>(static_cast<size_t>(chunk) * n * n);
     w.V = c.take<float>(static_cast<size_t>(chunk) * n * n);
     w.GDpart = c.take<float>(static_cast<size_t>(chunk) * gram_d_ksplit(d) * d.D * d.D);
@@ -518,10 +518,10 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base, AllocWS* lane1 = nullpt
     w.permD = c.take<int>(static_cast<size_t>(chunk) * d.D);
     w.sgnD = c.take<float>(static_cast<size_t>(chunk) * d.D);
   };
-  scratch(w);
+  carve_scratch(w);
   if (nlanes > 1) {
     AllocWS w1 = w;
-    scratch(w1);
+    carve_scratch(w1);
     if (lane1) *lane1 = w1;
   }
   w.bytes = c.off;
@@ -831,55 +831,98 @@ size_t decode_ws_one(const jolt_shape* s, jolt_choice c) {
   return 2 * a256(2ull * s->H * s->D * rtp_of(c.r_T));
 }
 
-// Decode n records of one shape, kDecBatch per launch pair (W prologue + decode).
+// ------------------------------------------------- allocation-free decode
+// Scratch of jolt_decode_many_static: the W planes of the records of one
+// launch pair.  A file-scope device array, one copy per GPU, held until the
+// process ends; host code uses the address hipGetSymbolAddress gives for the
+// current device, never the array's name.
+constexpr size_t kStaticScratchBytes = size_t{32} << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (under a lock) and kept.
+constexpr int kMaxDevices = 64;
+void* static_scratch() {
+  static std::mutex mu;
+  static void* per_dev[kMaxDevices] = {};
+  int dev = 0;
+  ck(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) throw HipFail{};
+  std::lock_guard<std::mutex> lk(mu);
+  if (!per_dev[dev]) {
+    void* p = nullptr;
+    ck(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    per_dev[dev] = p;
+  }
+  return per_dev[dev];
+}
+
+// Decode n records of one shape, up to kDecBatch per launch pair (W
+// prologue + decode).  The W planes of the records of one launch pair are
+// carved in order from ws; ws_cap bounds that carve: when the next record's
+// planes do not fit, the pair launched so far is issued and the carve starts
+// again at ws (the next pair's prologue runs after the previous decode on
+// the stream, so reusing the bytes is ordered).  The caller guarantees that
+// one record's planes fit ws_cap.
+size_t decode_w_bytes(int64_t H, int64_t D, jolt_choice c) {
+  return c.r_T ? 2 * a256(2ull * H * D * rtp_of(c.r_T)) : 0;
+}
+
 void decode_records(int n, const jolt_shape* shape, const jolt_choice* ch, const void* const* blobs,
-                    const void* rot_dev, void* const* outs, void* ws, hipStream_t s) {
+                    const void* rot_dev, void* const* outs, void* ws, size_t ws_cap, hipStream_t s) {
   const int64_t H = shape->H, T = shape->T, D = shape->D;
   const size_t n2 = static_cast<size_t>(D) * D;
   const uint16_t* Qt16 = reinterpret_cast<const uint16_t*>(static_cast<const char*>(rot_dev) + 2 * a256(4 * n2));
-  char* wsp = static_cast<char*>(ws);
-  for (int i0 = 0; i0 < n; i0 += kDecBatch) {
-    DecBatch b{};
-    b.n = std::min(kDecBatch, n - i0);
+  DecBatch b{};
+  size_t used = 0;
+  int wtiles = 0, first = 0;
+  auto issue = [&]() {
+    if (b.n == 0) return;
     b.H = static_cast<int32_t>(H);
     b.T = static_cast<int32_t>(T);
     b.out_dtype = shape->dtype == JOLT_BF16 ? kBF16 : kF32;
     b.Qt16 = Qt16;
-    int wtiles = 0;
-    for (int j = 0; j < b.n; ++j) {
-      const jolt_choice c = ch[i0 + j];
-      const BlobLayout L = blob_layout(H, T, D, c);
-      const char* blob = static_cast<const char*>(blobs[i0 + j]);
-      DecRec& R = b.rec[j];
-      R.Ut = reinterpret_cast<const uint16_t*>(blob + L.ut);
-      R.Ud = reinterpret_cast<const uint16_t*>(blob + L.ud);
-      R.G = reinterpret_cast<const uint16_t*>(blob + L.g);
-      R.scales = reinterpret_cast<const uint32_t*>(blob + L.sc);
-      R.codes = reinterpret_cast<const uint32_t*>(blob + L.cd);
-      R.out = outs[i0 + j];
-      R.r_T = c.r_T; R.r_D = c.r_D; R.bits = c.bits;
-      R.r_Tp = static_cast<int32_t>(rtp_of(c.r_T));
-      const size_t wb = a256(2ull * H * D * R.r_Tp);
-      R.Whi = reinterpret_cast<uint16_t*>(wsp);
-      R.Wlo = reinterpret_cast<uint16_t*>(wsp + (c.r_T ? wb : 0));
-      wsp += c.r_T ? 2 * wb : 0;
-      R.wtile0 = wtiles;
-      wtiles += static_cast<int>(H * (R.r_Tp / 32));
-    }
     b.out16 = 1;
     for (int j = 0; j < b.n; ++j) b.out16 &= (reinterpret_cast<uintptr_t>(b.rec[j].out) & 15) == 0 ? 1 : 0;
     b.wtiles_total = wtiles;
     if (prof_enabled("decode")) {
       double by = 0.0, fl = 0.0;
       for (int j = 0; j < b.n; ++j) {
-        const PathWork pw = residual_work(H, T, D, ch[i0 + j], shape->dtype == JOLT_BF16 ? 2 : 4);
+        const PathWork pw = residual_work(H, T, D, ch[first + j], shape->dtype == JOLT_BF16 ? 2 : 4);
         by += pw.bytes;
         fl += pw.flops;
       }
       prof_add_work("decode", by, fl);
     }
     ck(launch_decode_batch(b, s));
+    b = DecBatch{};
+    used = 0;
+    wtiles = 0;
+  };
+  for (int i = 0; i < n; ++i) {
+    const jolt_choice c = ch[i];
+    const size_t wneed = decode_w_bytes(H, D, c);
+    if (b.n == kDecBatch || (b.n > 0 && used + wneed > ws_cap)) issue();
+    if (b.n == 0) first = i;
+    const BlobLayout L = blob_layout(H, T, D, c);
+    const char* blob = static_cast<const char*>(blobs[i]);
+    DecRec& R = b.rec[b.n++];
+    R.Ut = reinterpret_cast<const uint16_t*>(blob + L.ut);
+    R.Ud = reinterpret_cast<const uint16_t*>(blob + L.ud);
+    R.G = reinterpret_cast<const uint16_t*>(blob + L.g);
+    R.scales = reinterpret_cast<const uint32_t*>(blob + L.sc);
+    R.codes = reinterpret_cast<const uint32_t*>(blob + L.cd);
+    R.out = outs[i];
+    R.r_T = c.r_T; R.r_D = c.r_D; R.bits = c.bits;
+    R.r_Tp = static_cast<int32_t>(rtp_of(c.r_T));
+    char* wsp = static_cast<char*>(ws) + used;
+    R.Whi = reinterpret_cast<uint16_t*>(wsp);
+    R.Wlo = reinterpret_cast<uint16_t*>(wsp + wneed / 2);
+    used += wneed;
+    R.wtile0 = wtiles;
+    wtiles += static_cast<int>(H * (R.r_Tp / 32));
   }
+  issue();
 }
 
 template <typename F>
@@ -1405,7 +1448,7 @@ jolt_status jolt_decode(const jolt_shape* shape, jolt_choice c, const void* blob
   const size_t need = decode_ws_one(shape, c);
   if (need > 0 && (!ws_dev || ws_bytes < need)) return JOLT_ENOSPACE;
   return guard([&]() -> jolt_status {
-    decode_records(1, shape, &c, &blob_dev, rot_dev, &xhat_dev, ws_dev, static_cast<hipStream_t>(stream));
+    decode_records(1, shape, &c, &blob_dev, rot_dev, &xhat_dev, ws_dev, need, static_cast<hipStream_t>(stream));
     return JOLT_OK;
   });
 }
@@ -1423,7 +1466,27 @@ jolt_status jolt_decode_many(int32_t n, const jolt_shape* shape, const jolt_choi
   const size_t need = jolt_decode_many_workspace_bytes(n, shape, choices);
   if (!ws_dev || ws_bytes < need) return JOLT_ENOSPACE;
   return guard([&]() -> jolt_status {
-    decode_records(n, shape, choices, blobs, rot_dev, outs, ws_dev, static_cast<hipStream_t>(stream));
+    decode_records(n, shape, choices, blobs, rot_dev, outs, ws_dev, need, static_cast<hipStream_t>(stream));
+    return JOLT_OK;
+  });
+}
+
+size_t jolt_decode_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+jolt_status jolt_decode_many_static(int32_t n, const jolt_shape* shape, const jolt_choice* choices,
+                                    const void* const* blobs, const size_t* blob_bytes, const void* rot_dev,
+                                    void* const* outs, void* stream) {
+  if (n < 0 || !shape_ok(shape) || !rot_dev) return JOLT_EINVAL;
+  if (n == 0) return JOLT_OK;
+  if (!choices || !blobs || !blob_bytes || !outs) return JOLT_EINVAL;
+  for (int i = 0; i < n; ++i) {
+    if (!choice_ok(shape, choices[i]) || !blobs[i] || !outs[i]) return JOLT_EINVAL;
+    if (blob_bytes[i] < blob_layout(shape->H, shape->T, shape->D, choices[i]).total) return JOLT_ENOSPACE;
+    if (decode_w_bytes(shape->H, shape->D, choices[i]) > kStaticScratchBytes) return JOLT_ENOSPACE;
+  }
+  return guard([&]() -> jolt_status {
+    decode_records(n, shape, choices, blobs, rot_dev, outs, static_scratch(), kStaticScratchBytes,
+                   static_cast<hipStream_t>(stream));
     return JOLT_OK;
   });
 }

@@ -363,6 +363,27 @@ def decode_many(blobs, H: int, T: int, choices, rot: torch.Tensor, outs, workspa
                                  workspace.numel(), _stream(workspace.device)), "jolt_decode_many")
 
 
+def decode_many_static(blobs, H: int, T: int, choices, rot: torch.Tensor, outs, dtype=torch.bfloat16) -> None:
+    """decode_many without a workspace: the library's per-GPU static scratch
+    (no device allocation in the call; overlapping calls on one GPU race)."""
+    n = len(blobs)
+    _need(len(choices) == n and len(outs) == n, "one choice and one output per record")
+    if n == 0:
+        return
+    shape = make_shape(H, T, D_FEATURES, dtype)
+    ch = (Choice * n)(*[Choice(*c) for c in choices])
+    dev = blobs[0].device
+    _check_buf(rot, dev, "rot", lib().jolt_rotation_bytes(D_FEATURES))
+    for i in range(n):
+        _check_buf(blobs[i], dev, f"blobs[{i}]", lib().jolt_blob_bytes(C.byref(shape), ch[i]))
+        _check_out(outs[i], dev, H, T, dtype, f"outs[{i}]")
+    bp = (C.c_void_p * n)(*[b.data_ptr() for b in blobs])
+    bb = (C.c_size_t * n)(*[b.numel() for b in blobs])
+    op = (C.c_void_p * n)(*[o.data_ptr() for o in outs])
+    check(lib().jolt_decode_many_static(n, C.byref(shape), ch, bp, bb, rot.data_ptr(), op, _stream(dev)),
+          "jolt_decode_many_static")
+
+
 def quantize(y: torch.Tensor, bits: int):
     """Group quantizer alone: y [rows, 128] fp32 -> (scales [rows, 4, 2] bf16 bits as int16,
     codes [rows, 4, 4*bits] uint8)."""
