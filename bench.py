@@ -121,25 +121,26 @@ def main():
             record.append(ev)
 
     def run(method, K, profile):
+        """Warmup, then K timed steps.  `profile`: kernel names whose launches
+        are bracketed by HIP events on their launch stream, with their
+        algorithmic work, over the timed region (a few launches per step)."""
         for _ in range(args.warmup):
             step(method)
         torch.cuda.synchronize()
         evs = []
-        # per-launch HIP events on the launch stream around the dominant
-        # kernel, with its algorithmic work, over the timed region
         if profile:
-            jolt.profile_enable(profile)
+            jolt.profile_enable(",".join(profile))
         t0 = time.perf_counter()
         for _ in range(K):
             step(method, evs)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        dom = None
+        stats = {}
         if profile:
-            dom = jolt.profile_query(profile)
+            stats = {name: jolt.profile_query(name) for name in profile}
             jolt.profile_enable(None)
         ph = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(3)]
-        return wall * 1e3 / K, ph, dom
+        return wall * 1e3 / K, ph, stats
 
     def errors():
         """Relative Frobenius error of every tensor (outside the timed region)."""
@@ -176,7 +177,25 @@ def main():
         jolt.profile_enable(None)
         cands = [k for k in ROOF if kstats[k]["launches"] and kstats[k]["bytes"] > 0]
         dominant = max(cands, key=lambda k: kstats[k]["total_ms"]) if cands else None
-    ms_step, (ms_alloc, ms_enc, ms_dec), dom = run(cfg.method, K, dominant)
+    timed = [k for k in TIMED_ROOF if k != dominant] + ([dominant] if dominant else [])
+    ms_step, (ms_alloc, ms_enc, ms_dec), tstats = run(cfg.method, K, None if args.profile_step else timed)
+    # the standalone group quantizer (not on the step's path: the encoder
+    # fuses it) on a synthetic rotated residual of the whole cache's rows
+    q_rows = 2 * L * H * T
+    q_bits = 2
+    qy = torch.randn((q_rows, D), dtype=torch.float32, device=dev)
+    jolt.quantize(qy, q_bits)                   # warmup
+    torch.cuda.synchronize()
+    if not args.profile_step:
+        jolt.profile_enable("quantize")
+    for _ in range(3):
+        jolt.quantize(qy, q_bits)
+    torch.cuda.synchronize()
+    qstats = None
+    if not args.profile_step:
+        qstats = jolt.profile_query("quantize")
+        jolt.profile_enable(None)
+    del qy
     if args.profile_step:
         # a plain copy of known size (read n bytes, write n bytes), against
         # which the FETCH_SIZE / WRITE_SIZE counters are scaled
@@ -233,7 +252,19 @@ def main():
         "plan_bytes": int(res.total_bytes), "budget_bytes": int(res.budget_bytes),
         "rel_err_K_mean": round(float(errs[:, 0].mean()), 6),
         "rel_err_V_mean": round(float(errs[:, 1].mean()), 6),
-        "roofline": roofline_for(dominant, dom, cfg.name) if dom and dom["launches"] else None,
+        "roofline": (roofline_for(dominant, tstats[dominant], cfg.name)
+                     if dominant and tstats.get(dominant, {}).get("launches") else None),
+        # the kernels with roofline targets, timed the same way inside the
+        # timed steps (the quantizer in its own leg on the cache's rows)
+        "roofline_encode": (roofline_for("encode_residual", tstats["encode_residual"], cfg.name)
+                            if tstats.get("encode_residual", {}).get("launches") else None),
+        "roofline_decode_kernel": (roofline_for("decode", tstats["decode"], cfg.name)
+                                   if tstats.get("decode", {}).get("launches") else None),
+        "roofline_quantize": (dict(roofline_for("quantize", qstats, cfg.name),
+                                   workload=f"{q_rows} rows x {D} fp32 (the cache's rows), b = {q_bits}")
+                              if qstats and qstats["launches"] else None),
+        "roofline_gram": (roofline_for("gram", tstats["gram"], cfg.name)
+                          if tstats.get("gram", {}).get("launches") else None),
         "roofline_decode": {"kernel": dec_kernel,
                             "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                             "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
@@ -242,7 +273,8 @@ def main():
         # the other kernels that account their work, from the per-kernel
         # breakdown step (events around every launch, outside the timed steps)
         "roofline_more": {k: roofline_for(k, kstats[k], cfg.name) for k in ROOF
-                          if k != dominant and k in kstats and kstats[k]["launches"] and kstats[k]["bytes"] > 0},
+                          if k != dominant and k not in TIMED_ROOF and k in kstats and kstats[k]["launches"]
+                          and kstats[k]["bytes"] > 0},
         "kernel_ms_per_step": {k: round(v["total_ms"], 3) for k, v in kstats.items()},
         "kernel_launches_per_step": {k: v["launches"] for k, v in kstats.items()},
     }
@@ -274,8 +306,10 @@ COMPARE_EXACT = {"mistral7b_t1024_flash"}
 CPU_SAMPLE = {"mistral7b_t4096_2x": 24, "mistral7b_t1024_flash": 64, "llama13b_t4096_2x": 2,
               "mistral7b_t32768_3x": 4}
 
-KERNELS = ("qr_panel", "qr_update", "gemm", "gemm_bf16", "band", "chase", "tri_eig", "chase_back", "band_back",
-           "encode_w", "encode_residual", "quantize", "decode_w", "decode")
+KERNELS = ("qr_panel", "qr_update", "gemm", "gemm_bf16", "gram", "band", "chase", "tri_eig", "chase_back",
+           "band_back", "encode_w", "encode_residual", "quantize", "decode_w", "decode")
+# kernels with roofline targets, timed inside the timed steps
+TIMED_ROOF = ("gram", "encode_residual", "decode")
 CSRC = os.path.join(ROOT, "kv_cache_compression_mode_amd", "csrc")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 # fp32 vector arithmetic without packed instructions (which the build turns
@@ -304,6 +338,20 @@ ROOF = {
                   "k_wy_upd", r"k_wy_(part|mid|upd)\b", ("qr.hip", "device.hpp"), MFMA_FP32_PEAK_TFLOPS, "mfma"),
     "gemm": ("k_gemm: strided batched 64x64-tile GEMM on fp32 matrix cores (small products)",
              "k_gemm", r"k_gemm(<|_bf16\b)", ("gemm.hip", "device.hpp"), MFMA_FP32_PEAK_TFLOPS, "mfma"),
+    "gram": ("k_gemm_x on the token and feature Grams of the tensors (bf16 matrix cores; a triangle-only "
+             "output counts the symmetric half, M (M + 1) K flops)",
+             "k_gemm_x_gram", None, ("gemm.hip", "device.hpp"), MFMA_BF16_PEAK_TFLOPS, "mfma"),
+    "encode_residual": ("k_encode_residual_many: reconstruction U~_T (G~ U~_D^T), residual, JL rotation R Q^T, "
+                        "group quantization and packing in one pass over X (bf16 matrix cores over exact "
+                        "three-part splits)",
+                        "k_encode_residual_many", r"k_encode_residual(_many)?<", ("codec.hip", "device.hpp"),
+                        MFMA_BF16_PEAK_TFLOPS, "mfma"),
+    "decode": ("k_decode: X^ = U~_T W + Y^ Q with dequantization fused, all records of a launch (bf16 matrix "
+               "cores, W = G~ U~_D^T as bf16 hi + lo)",
+               "k_decode", r"k_decode<", ("codec.hip", "device.hpp"), MFMA_BF16_PEAK_TFLOPS, "mfma"),
+    "quantize": ("k_quantize: group quantizer alone, one group of 32 per thread (fp32 in, b-bit codes and bf16 "
+                 "offset/step out)",
+                 "k_quantize", r"k_quantize\b", ("codec.hip", "device.hpp"), None, "hbm"),
     "gemm_bf16": ("k_gemm_x: 128x128-tile GEMM on bf16 matrix cores (token and feature Grams, factor recovery, "
                   "Rayleigh and core products; fp32 operands enter as bf16 hi + lo)",
                   "k_gemm_x", r"k_gemm_x<", ("gemm.hip", "device.hpp"), MFMA_BF16_PEAK_TFLOPS, "mfma"),
@@ -362,6 +410,8 @@ def _pmc_means(path, counter, symbol, pattern):
 def record_traffic(fetch_csv, write_csv, copy_bytes, name="gemm", workload="mistral7b_t4096_2x",
                    record_path=None, source_paths=None):
     symbol, pattern = ROOF[name][1], ROOF[name][2]
+    if pattern is None:
+        raise SystemExit(f"{name}: its launches share a kernel with other products; no traffic record")
     source_paths = source_paths or kernel_sources(name)
     jf, cf, n = _pmc_means(fetch_csv, "FETCH_SIZE", symbol, pattern)
     jw, cw, _ = _pmc_means(write_csv, "WRITE_SIZE", symbol, pattern)
@@ -395,15 +445,21 @@ def roofline_for(name, st, workload):
     gbps = bytes_l / (avg_ms * 1e-3) / 1e9
     tflops = flops_l / (avg_ms * 1e-3) / 1e12
     peak_tf, kind = ROOF[name][4], ROOF[name][5]
-    ridge = peak_tf * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    ridge = peak_tf * 1e12 / (HBM_PEAK_GBPS * 1e9) if peak_tf else float("inf")
     if ai < ridge:
         bound, achieved, peak, unit = "hbm", gbps, HBM_PEAK_GBPS, "GB/s"
     else:
         bound, achieved, peak, unit = kind, tflops, peak_tf, "TFLOP/s"
-    desc, symbol = ROOF[name][0], ROOF[name][1]
+    desc, symbol, pattern = ROOF[name][0], ROOF[name][1], ROOF[name][2]
+    traffic = (measured_traffic(kernel_sources(name), traffic_file(symbol, workload)) if pattern else None)
+    extra = {"frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
+    if peak_tf:
+        extra["frac_mfma"] = round(tflops / peak_tf, 4)
+    if traffic:
+        extra["traffic_over_algorithmic"] = round(traffic / max(bytes_l, 1.0), 3)
     return {"kernel": desc, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(kernel_sources(name), traffic_file(symbol, workload)),
+            "traffic": traffic, **extra,
             "algorithmic_bytes_per_launch": round(bytes_l),
             "algorithmic_flops_per_launch": round(flops_l),
             "arithmetic_intensity": round(ai, 2), "ridge": round(ridge, 2),
@@ -412,36 +468,59 @@ def roofline_for(name, st, workload):
 
 
 def cpu_baseline(cfg, n_tensors):
-    """The fp64 oracle on a bounded sample of the same workload (host cores)."""
+    """The fp64 oracle on a bounded sample of the same workload (host cores):
+    BLAS threads set to the cores this process may run on; analyze + encode +
+    decode per sampled tensor at a fixed choice, scaled to the whole cache."""
     import numpy as np
 
     import kvgen
     from oracle import alloc, codec, rotation
+    cores = len(os.sched_getaffinity(0))
+    blas, limits = [], None
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = sorted({f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads before)"
+                       for i in threadpool_info() if i.get("user_api") == "blas"})
+        limits = threadpool_limits(limits=cores, user_api="blas")
     except Exception:
-        cores = len(os.sched_getaffinity(0))
+        pass
     cap = alloc.rank_cap_T(cfg.H, cfg.T, cfg.D, cfg.ratio)
+    choice = (cap, 64, 2)
     Q = rotation.rotation(cfg.seed, cfg.D)
-    dt = 0.0
+    t_enc = t_dec = 0.0
+    errs = {0: [], 1: []}
     done = 0
-    for i in range(n_tensors):
-        l, k = i // 2, i % 2
-        X = kvgen.config_tensor(cfg, l, k).astype(np.float64)   # input generation is not timed
-        t0 = time.perf_counter()
-        a = codec.analyze(X, cap, cfg.method, cfg.seed, l, k)
-        e = codec.encode_tensor(X, a["U_T"], a["U_D"], (cap, 64, 2), Q)
-        codec.decode_tensor(e, Q, cfg.dtype)
-        dt += time.perf_counter() - t0
-        done += 1
+    try:
+        for i in range(n_tensors):
+            l, k = i // 2, i % 2
+            X = kvgen.config_tensor(cfg, l, k).astype(np.float64)   # input generation is not timed
+            t0 = time.perf_counter()
+            a = codec.analyze(X, cap, cfg.method, cfg.seed, l, k)
+            e = codec.encode_tensor(X, a["U_T"], a["U_D"], choice, Q)
+            t1 = time.perf_counter()
+            xh = codec.decode_tensor(e, Q, cfg.dtype)
+            t2 = time.perf_counter()
+            t_enc += t1 - t0
+            t_dec += t2 - t1
+            errs[k].append(codec.rel_err(X, xh))
+            done += 1
+    finally:
+        if limits is not None:
+            limits.restore_original_limits()
     frac = done / (2 * cfg.n_layers)
+    out_bytes = done * cfg.H * cfg.T * cfg.D * (2 if cfg.dtype == "bf16" else 4)
+    dt = t_enc + t_dec
     return {"value": round(cfg.T * frac / dt, 2), "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{done} of {2 * cfg.n_layers} tensors (layers 0..{(done - 1) // 2}): analyze "
                       f"({cfg.method} fp64 factors) + encode at (r_T={cap}, r_D=64, b=2) + decode; "
                       f"the dual allocation over the whole cache (milliseconds) is not included; "
-                      f"tokens/s scaled by the sampled fraction of the cache, {dt:.1f} s"}
+                      f"tokens/s scaled by the sampled fraction of the cache, {dt:.1f} s",
+            "blas": blas, "blas_threads": int(cores),
+            "encode_tokens_per_s": round(cfg.T * frac / t_enc, 2),
+            "decode_output_GBps": round(out_bytes / t_dec / 1e9, 4),
+            "rel_err_K_mean": round(float(np.mean(errs[0])), 6) if errs[0] else None,
+            "rel_err_V_mean": round(float(np.mean(errs[1])), 6) if errs[1] else None}
 
 
 if __name__ == "__main__":

@@ -156,5 +156,10 @@ def generate(cfg: CacheConfig, items, workers: int = 8):
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
-    with pool:
+    try:
         yield from pool.imap_unordered(_config_item, items)
+    finally:
+        # let the workers finish and exit on their own (terminating them
+        # makes every worker report an abort)
+        pool.close()
+        pool.join()
