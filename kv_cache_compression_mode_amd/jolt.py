@@ -41,20 +41,34 @@ def _need(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
-def _check_buf(t: torch.Tensor, device, name: str, nbytes: int = 0) -> None:
-    """A contiguous tensor on `device` holding at least `nbytes` bytes."""
+def _check_buf(t: torch.Tensor, device: torch.device, name: str, nbytes: int = 0) -> None:
+    """A contiguous tensor on `device` holding at least `nbytes` bytes (cheap
+    when it holds: this runs per record on the decode's host path)."""
+    if (isinstance(t, torch.Tensor) and t.device == device and t.is_contiguous()
+            and t.numel() * t.element_size() >= nbytes):
+        return
     _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
-    _need(t.device == torch.device(device), f"{name} must be on {device}, not {t.device}")
+    _need(t.device == device, f"{name} must be on {device}, not {t.device}")
     _need(t.is_contiguous(), f"{name} must be contiguous")
-    _need(t.numel() * t.element_size() >= nbytes, f"{name} holds {t.numel() * t.element_size()} bytes, "
-                                                   f"needs {nbytes}")
+    raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
 
 
-def _check_out(o: torch.Tensor, device, H: int, T: int, dtype: torch.dtype, name: str) -> None:
+def _check_out(o: torch.Tensor, device: torch.device, H: int, T: int, dtype: torch.dtype, name: str) -> None:
     _check_buf(o, device, name)
-    _need(tuple(o.shape) == (H, T, D_FEATURES), f"{name} must have shape {(H, T, D_FEATURES)}, not "
-                                                 f"{tuple(o.shape)}")
+    _need(o.shape == (H, T, D_FEATURES), f"{name} must have shape {(H, T, D_FEATURES)}, not {tuple(o.shape)}")
     _need(o.dtype == dtype, f"{name} must be {dtype}, not {o.dtype}")
+
+
+def _blob_sizes(shape: Shape, choices) -> list:
+    """jolt_blob_bytes per record (one library call per distinct choice)."""
+    memo = {}
+    out = []
+    for c in choices:
+        key = tuple(c)
+        if key not in memo:
+            memo[key] = lib().jolt_blob_bytes(C.byref(shape), Choice(*key))
+        out.append(memo[key])
+    return out
 
 
 def _check_factor(f: torch.Tensor, device, rows: int, cols: int, name: str) -> None:
@@ -264,8 +278,8 @@ def encode_many(xs, choices, factors, rot: torch.Tensor, seed: int = 0, outs=Non
     _check_buf(rot, x0.device, "rot", lib().jolt_rotation_bytes(D))
     if outs is not None:
         _need(len(outs) == n, "one output record per tensor")
-        for i, o in enumerate(outs):
-            _check_buf(o, x0.device, f"outs[{i}]", lib().jolt_blob_bytes(C.byref(shape), ch[i]))
+        for i, nb in enumerate(_blob_sizes(shape, choices)):
+            _check_buf(outs[i], x0.device, f"outs[{i}]", nb)
         blobs = outs
     else:
         # one allocation cut into 256-aligned records
@@ -351,10 +365,10 @@ def decode_many(blobs, H: int, T: int, choices, rot: torch.Tensor, outs, workspa
     shape = make_shape(H, T, D_FEATURES, dtype)
     ch = (Choice * n)(*[Choice(*c) for c in choices])
     dev = workspace.device
-    _check_buf(workspace, dev, "workspace", decode_many_workspace_bytes(H, T, choices, dtype))
+    _check_buf(workspace, dev, "workspace", lib().jolt_decode_many_workspace_bytes(n, C.byref(shape), ch))
     _check_buf(rot, dev, "rot", lib().jolt_rotation_bytes(D_FEATURES))
-    for i in range(n):
-        _check_buf(blobs[i], dev, f"blobs[{i}]", lib().jolt_blob_bytes(C.byref(shape), ch[i]))
+    for i, nb in enumerate(_blob_sizes(shape, choices)):
+        _check_buf(blobs[i], dev, f"blobs[{i}]", nb)
         _check_out(outs[i], dev, H, T, dtype, f"outs[{i}]")
     bp = (C.c_void_p * n)(*[b.data_ptr() for b in blobs])
     bb = (C.c_size_t * n)(*[b.numel() for b in blobs])
@@ -374,8 +388,8 @@ def decode_many_static(blobs, H: int, T: int, choices, rot: torch.Tensor, outs, 
     ch = (Choice * n)(*[Choice(*c) for c in choices])
     dev = blobs[0].device
     _check_buf(rot, dev, "rot", lib().jolt_rotation_bytes(D_FEATURES))
-    for i in range(n):
-        _check_buf(blobs[i], dev, f"blobs[{i}]", lib().jolt_blob_bytes(C.byref(shape), ch[i]))
+    for i, nb in enumerate(_blob_sizes(shape, choices)):
+        _check_buf(blobs[i], dev, f"blobs[{i}]", nb)
         _check_out(outs[i], dev, H, T, dtype, f"outs[{i}]")
     bp = (C.c_void_p * n)(*[b.data_ptr() for b in blobs])
     bb = (C.c_size_t * n)(*[b.numel() for b in blobs])
