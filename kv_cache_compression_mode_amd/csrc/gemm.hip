@@ -681,6 +681,15 @@ __global__ __launch_bounds__(256) void k_sum_diag_blocks(const float* C, int64_t
   }
 }
 
+// out[i] = sum over the batch of in[j][i], in batch order (deterministic).
+__global__ __launch_bounds__(256) void k_sum_batch(const float* in, int64_t count, int n, float* out) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < count; i += 256ll * gridDim.x) {
+    float s = 0.f;
+    for (int j = 0; j < n; ++j) s += in[j * count + i];
+    out[i] = s;
+  }
+}
+
 int grid1(int64_t n, int cap = 4096) {
   int64_t b = (n + 255) / 256;
   return static_cast<int>(b < 1 ? 1 : (b > cap ? cap : b));
@@ -744,8 +753,10 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s, const char*
     const bool tri = g.c_lower != 0 && g.M == g.N;
     const double outs = tri ? 0.5 * g.M * (g.M + 1.0) : 1.0 * g.M * g.N;
     const double fl = tri ? 1.0 * g.M * (g.M + 1.0) * g.K : 2.0 * g.M * g.N * g.K;
-    prof_add_work(name, batch * (g.M * g.K * ea + g.K * g.N * eb + outs * ec * (g.beta != 0.f ? 2 : 1)),
-                  fl * batch);
+    // a Gram reads its one operand once (A and B are the same tensor)
+    const bool same = (g.A && g.A == g.B) || (g.a_ptrs && g.a_ptrs == g.b_ptrs);
+    const double in = same ? g.M * g.K * ea : g.M * g.K * ea + g.K * g.N * eb;
+    prof_add_work(name, batch * (in + outs * ec * (g.beta != 0.f ? 2 : 1)), fl * batch);
   };
   // 128 x 128 bf16 matrix-core tiles when the operands allow 16-byte loads
   // (at least one of them bf16); a column-major C is produced as the
@@ -861,6 +872,12 @@ hipError_t launch_col_dot(const float* A, const float* B, int64_t m, int64_t nco
 hipError_t launch_pad_copy(const float* in, int64_t n, int64_t in_batch, float* out, int64_t n_pad,
                            int batch, hipStream_t s) {
   k_pad_copy<<<dim3(grid1(n_pad * n_pad), batch), 256, 0, s>>>(in, n, in_batch, out, n_pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_batch(const float* in, int64_t count, int n, float* out, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  k_sum_batch<<<grid1(count), 256, 0, s>>>(in, count, n, out);
   return hipGetLastError();
 }
 

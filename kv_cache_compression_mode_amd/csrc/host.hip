@@ -925,6 +925,62 @@ void decode_records(int n, const jolt_shape* shape, const jolt_choice* ch, const
   issue();
 }
 
+// The prepared rotation buffer from a D x D orthogonal Q (fp64, row-major,
+// host): fp32 Q, fp32 Q^T, bf16 Q^T and the three exact bf16 parts of the
+// fp32 Q in the encoder's matrix-core fragment order.  Synchronizes s.
+void upload_rotation(const double* Q, int D, void* q_dev, hipStream_t s) {
+  const size_t n = static_cast<size_t>(D) * D;
+  std::vector<float> buf(2 * n);
+  std::vector<uint16_t> b16(n);
+  for (size_t i = 0; i < n; ++i) {
+    const size_t r = i / D, c = i % D;
+    buf[i] = static_cast<float>(Q[i]);
+    buf[n + c * D + r] = static_cast<float>(Q[i]);       // Q^T
+    // bf16 (nearest-even, via the fp32 value) of Q^T: b16[c][r] = Q[r][c]
+    float f = static_cast<float>(Q[i]);
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    b16[c * D + r] = static_cast<uint16_t>(u >> 16);
+  }
+  // exact three-part bf16 split of the fp32 Q: hi = rne(f), mid = rne(f - hi),
+  // lo = f - hi - mid (a bf16 value), stored in matrix-core fragment order
+  // [part][cb][ds][lane][e] = part of Q[32 cb + lane % 32][16 ds + 8 (lane / 32) + e]
+  std::vector<uint16_t> q3(3 * n);
+  auto rne = [](float f) {
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+  };
+  auto widen = [](uint16_t b) {
+    const uint32_t u = static_cast<uint32_t>(b) << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+  };
+  for (size_t i = 0; i < n; ++i) {
+    const size_t c = i / D, d = i % D;               // buf[i] = Q[c][d]
+    const size_t o = ((c / 32 * (D / 16) + d / 16) * 64 + (d / 8 % 2) * 32 + c % 32) * 8 + d % 8;
+    const float f = buf[i];
+    const uint16_t h = rne(f);
+    const float r1 = f - widen(h);
+    const uint16_t m = rne(r1);
+    const float r2 = r1 - widen(m);
+    uint32_t u;
+    std::memcpy(&u, &r2, 4);
+    q3[o] = h;
+    q3[n + o] = m;
+    q3[2 * n + o] = static_cast<uint16_t>(u >> 16);
+  }
+  char* base = static_cast<char*>(q_dev);
+  ck(hipMemcpyAsync(base, buf.data(), 4 * n, hipMemcpyHostToDevice, s));
+  ck(hipMemcpyAsync(base + a256(4 * n), buf.data() + n, 4 * n, hipMemcpyHostToDevice, s));
+  ck(hipMemcpyAsync(base + 2 * a256(4 * n), b16.data(), 2 * n, hipMemcpyHostToDevice, s));
+  ck(hipMemcpyAsync(base + 2 * a256(4 * n) + a256(2 * n), q3.data(), 6 * n, hipMemcpyHostToDevice, s));
+  ck(hipStreamSynchronize(s));
+}
+
 template <typename F>
 jolt_status guard(F&& f) {
   try {
@@ -1056,57 +1112,23 @@ jolt_status jolt_rotation(uint64_t seed, int32_t D, void* q_dev, size_t q_bytes,
   return guard([&]() -> jolt_status {
     std::vector<double> Q(static_cast<size_t>(D) * D);
     rotation_host(seed, D, Q.data());
-    const size_t n = static_cast<size_t>(D) * D;
-    std::vector<float> buf(2 * n);
-    std::vector<uint16_t> b16(n);
-    for (size_t i = 0; i < n; ++i) {
-      const size_t r = i / D, c = i % D;
-      buf[i] = static_cast<float>(Q[i]);
-      buf[n + c * D + r] = static_cast<float>(Q[i]);       // Q^T
-      // bf16 (nearest-even, via the fp32 value) of Q^T: b16[c][r] = Q[r][c]
-      float f = static_cast<float>(Q[i]);
-      uint32_t u;
-      std::memcpy(&u, &f, 4);
-      u += 0x7fffu + ((u >> 16) & 1u);
-      b16[c * D + r] = static_cast<uint16_t>(u >> 16);
+    upload_rotation(Q.data(), D, q_dev, static_cast<hipStream_t>(stream));
+    return JOLT_OK;
+  });
+}
+
+jolt_status jolt_rotation_from(const double* Q, int32_t D, void* q_dev, size_t q_bytes, void* stream) {
+  if (D != kD || !q_dev || !Q) return JOLT_EINVAL;
+  if (q_bytes < jolt_rotation_bytes(D)) return JOLT_ENOSPACE;
+  // orthogonal to fp64 working accuracy: |Q^T Q - I| entrywise below 1e-12
+  for (int i = 0; i < D; ++i)
+    for (int j = 0; j < D; ++j) {
+      double s = 0.0;
+      for (int k = 0; k < D; ++k) s += Q[static_cast<size_t>(k) * D + i] * Q[static_cast<size_t>(k) * D + j];
+      if (!(std::fabs(s - (i == j ? 1.0 : 0.0)) <= 1e-12)) return JOLT_EINVAL;
     }
-    // exact three-part bf16 split of the fp32 Q: hi = rne(f), mid = rne(f - hi),
-    // lo = f - hi - mid (a bf16 value), stored in matrix-core fragment order
-    // [part][cb][ds][lane][e] = part of Q[32 cb + lane % 32][16 ds + 8 (lane / 32) + e]
-    std::vector<uint16_t> q3(3 * n);
-    auto rne = [](float f) {
-      uint32_t u;
-      std::memcpy(&u, &f, 4);
-      u += 0x7fffu + ((u >> 16) & 1u);
-      return static_cast<uint16_t>(u >> 16);
-    };
-    auto widen = [](uint16_t b) {
-      const uint32_t u = static_cast<uint32_t>(b) << 16;
-      float f;
-      std::memcpy(&f, &u, 4);
-      return f;
-    };
-    for (size_t i = 0; i < n; ++i) {
-      const size_t c = i / D, d = i % D;               // buf[i] = Q[c][d]
-      const size_t o = ((c / 32 * (D / 16) + d / 16) * 64 + (d / 8 % 2) * 32 + c % 32) * 8 + d % 8;
-      const float f = buf[i];
-      const uint16_t h = rne(f);
-      const float r1 = f - widen(h);
-      const uint16_t m = rne(r1);
-      const float r2 = r1 - widen(m);
-      uint32_t u;
-      std::memcpy(&u, &r2, 4);
-      q3[o] = h;
-      q3[n + o] = m;
-      q3[2 * n + o] = static_cast<uint16_t>(u >> 16);
-    }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    char* base = static_cast<char*>(q_dev);
-    ck(hipMemcpyAsync(base, buf.data(), 4 * n, hipMemcpyHostToDevice, s));
-    ck(hipMemcpyAsync(base + a256(4 * n), buf.data() + n, 4 * n, hipMemcpyHostToDevice, s));
-    ck(hipMemcpyAsync(base + 2 * a256(4 * n), b16.data(), 2 * n, hipMemcpyHostToDevice, s));
-    ck(hipMemcpyAsync(base + 2 * a256(4 * n) + a256(2 * n), q3.data(), 6 * n, hipMemcpyHostToDevice, s));
-    ck(hipStreamSynchronize(s));
+  return guard([&]() -> jolt_status {
+    upload_rotation(Q, D, q_dev, static_cast<hipStream_t>(stream));
     return JOLT_OK;
   });
 }
@@ -1467,6 +1489,110 @@ jolt_status jolt_decode_many(int32_t n, const jolt_shape* shape, const jolt_choi
   if (!ws_dev || ws_bytes < need) return JOLT_ENOSPACE;
   return guard([&]() -> jolt_status {
     decode_records(n, shape, choices, blobs, rot_dev, outs, ws_dev, need, static_cast<hipStream_t>(stream));
+    return JOLT_OK;
+  });
+}
+
+// ---------------------------------------------- cross-layer SVD baseline
+// Workspace: per-tensor feature Grams and their split-K partials, the summed
+// Gram, its eigenvectors, the eigensolver's scratch, eigenvalues, status.
+struct XlLayout {
+  size_t gram, part, gsum, Z, syev, lam, status, total;
+  int ksplit;
+};
+XlLayout xl_layout(int n, const jolt_shape* sh, int r) {
+  XlLayout L{};
+  const int64_t D = sh->D, K = static_cast<int64_t>(sh->H) * sh->T;
+  L.ksplit = static_cast<int>(std::min<int64_t>(32, std::max<int64_t>(1, (K + 4095) / 4096)));
+  size_t off = 0;
+  L.gram = off; off += a256(4ull * n * D * D);
+  L.part = off; off += a256(4ull * n * L.ksplit * D * D);
+  L.gsum = off; off += a256(4ull * D * D);
+  L.Z = off; off += a256(4ull * D * D);
+  L.syev = off; off += a256(syev_top_work_bytes(D, r, 1));
+  L.lam = off; off += a256(8ull * r);
+  L.status = off; off += 256;
+  L.total = off;
+  return L;
+}
+
+size_t jolt_xl_workspace_bytes(int32_t n, const jolt_shape* shape, int32_t r) {
+  if (n < 1 || !shape_ok(shape) || r < 1 || r > shape->D) return 0;
+  return xl_layout(n, shape, r).total;
+}
+
+jolt_status jolt_xl_encode(int32_t n, const jolt_shape* shape, const void* const* x_dev, int32_t r,
+                           void* basis_dev, void* const* coeff_dev, double* lam_host, void* ws_dev,
+                           size_t ws_bytes, void* stream) {
+  if (n < 1 || !shape_ok(shape) || r < 1 || r > shape->D || !x_dev || !basis_dev || !coeff_dev || !ws_dev)
+    return JOLT_EINVAL;
+  for (int i = 0; i < n; ++i)
+    if (!x_dev[i] || !coeff_dev[i]) return JOLT_EINVAL;
+  const XlLayout L = xl_layout(n, shape, r);
+  if (ws_bytes < L.total) return JOLT_ENOSPACE;
+  return guard([&]() -> jolt_status {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t H = shape->H, T = shape->T, D = shape->D;
+    const int xdt = shape->dtype == JOLT_BF16 ? kBF16 : kF32;
+    char* ws = static_cast<char*>(ws_dev);
+    float* gram = reinterpret_cast<float*>(ws + L.gram);
+    float* gsum = reinterpret_cast<float*>(ws + L.gsum);
+    float* Z = reinterpret_cast<float*>(ws + L.Z);
+    double* lam = reinterpret_cast<double*>(ws + L.lam);
+    int* status = reinterpret_cast<int*>(ws + L.status);
+    uint16_t* basis = static_cast<uint16_t*>(basis_dev);
+    ck(hipMemsetAsync(status, 0, sizeof(int), s));
+    for (int i = 0; i < n; ++i) {           // feature Gram of tensor i: X_(D) X_(D)^T over H T rows
+      GemmArgs g = gemm0();
+      g.A = x_dev[i]; g.B = x_dev[i]; g.a_dtype = g.b_dtype = xdt;
+      g.M = D; g.N = D; g.K = H * T;
+      g.am = plain(1); g.ak = plain(D); g.bk = plain(D); g.bn = plain(1);
+      g.C = gram + static_cast<size_t>(i) * D * D; g.c_m = D; g.c_n = 1;
+      g.ksplit = L.ksplit;
+      g.partial = reinterpret_cast<float*>(ws + L.part) + static_cast<size_t>(i) * L.ksplit * D * D;
+      ck(launch_gemm(g, 1, s, "gram"));
+    }
+    ck(launch_sum_batch(gram, D * D, n, gsum, s));
+    ck(syev_top(gsum, D, 1, r, Z, lam, ws + L.syev, s, status));
+    // basis bf16 [r][D]: row j = eigenvector j (column j of the column-major Z)
+    ck(launch_to_bf16(Z, D, basis, r, D, s));
+    for (int i = 0; i < n; ++i) {           // C_i = bf16(X_i U~)  ([H T][r])
+      GemmArgs g = gemm0();
+      g.A = x_dev[i]; g.a_dtype = xdt; g.am = plain(D); g.ak = plain(1);
+      g.B = basis; g.b_dtype = kBF16; g.bk = plain(1); g.bn = plain(D);
+      g.M = H * T; g.N = r; g.K = D;
+      g.C = coeff_dev[i]; g.c_dtype = kBF16; g.c_m = r; g.c_n = 1;
+      ck(launch_gemm(g, 1, s));
+    }
+    std::vector<double> lh(r);
+    int st = 0;
+    ck(hipMemcpyAsync(lh.data(), lam, sizeof(double) * r, hipMemcpyDeviceToHost, s));
+    ck(hipMemcpyAsync(&st, status, sizeof(int), hipMemcpyDeviceToHost, s));
+    ck(hipStreamSynchronize(s));
+    if (st != 0) return JOLT_EHIP;
+    if (lam_host) std::memcpy(lam_host, lh.data(), sizeof(double) * r);
+    return JOLT_OK;
+  });
+}
+
+jolt_status jolt_xl_decode(int32_t n, const jolt_shape* shape, int32_t r, const void* basis_dev,
+                           const void* const* coeff_dev, void* const* out_dev, void* stream) {
+  if (n < 0 || !shape_ok(shape) || r < 1 || r > shape->D) return JOLT_EINVAL;
+  if (n == 0) return JOLT_OK;
+  if (!basis_dev || !coeff_dev || !out_dev) return JOLT_EINVAL;
+  for (int i = 0; i < n; ++i)
+    if (!coeff_dev[i] || !out_dev[i]) return JOLT_EINVAL;
+  return guard([&]() -> jolt_status {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t H = shape->H, T = shape->T, D = shape->D;
+    for (int i = 0; i < n; ++i) {           // X^_i = C_i U~^T, in the input dtype
+      GemmArgs g = gemm0();
+      g.A = coeff_dev[i]; g.a_dtype = kBF16; g.am = plain(r); g.ak = plain(1);
+      g.B = basis_dev; g.b_dtype = kBF16; g.bk = plain(D); g.bn = plain(1);
+      g.M = H * T; g.N = D; g.K = r;
+      g.C = out_dev[i]; g.c_dtype = shape->dtype == JOLT_BF16 ? kBF16 : kF32; g.c_m = D; g.c_n = 1;
+      ck(launch_gemm(g, 1, s));
+    }
     return JOLT_OK;
   });
 }

@@ -8,10 +8,8 @@ namespace jolt {
 enum { kBF16 = 0, kF32 = 1 };
 
 // ---- opt-in profiling (jolt_profile_enable): HIP events around launches of a
-// selected kernel on its stream, plus device counters (bytes, flops) that a
-// kernel fills with the work it actually performed: one [2] slot per
-// workgroup, each added to only by the workgroup of that grid position, so
-// launches serialized on one stream accumulate without atomics.
+// selected kernel on its stream, and the algorithmic bytes and flops that the
+// host code issuing the launch accounts for it.
 bool prof_enabled(const char* name);
 void prof_add_work(const char* name, double bytes, double flops);
 struct ProfScope {
@@ -74,6 +72,8 @@ hipError_t launch_pad_copy(const float* in, int64_t n, int64_t in_batch, float* 
                            int batch, hipStream_t s);
 hipError_t launch_sum_diag_blocks(const float* C, int64_t H, int64_t D, float* GD, int batch,
                                   hipStream_t s);
+// out[i] = sum_{j < n} in[j * count + i], added in the order j = 0 .. n-1.
+hipError_t launch_sum_batch(const float* in, int64_t count, int n, float* out, hipStream_t s);
 
 // ---- Householder QR, column-major panels [batch][k][ld] (column j at j*ld) ----
 // In place: on return the panel holds the explicit orthonormal Q (m x k, m >= k)
