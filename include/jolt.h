@@ -161,6 +161,14 @@ jolt_status jolt_factors(const jolt_alloc_req* req, void* ws_dev, int32_t tensor
 jolt_status jolt_rotation(uint64_t seed, int32_t D, void* q_dev, size_t q_bytes,
                           void* stream);
 
+/* A prepared rotation from a caller's D x D orthogonal matrix Q (fp64,
+ * row-major, host; |Q^T Q - I| <= 1e-12 entrywise, else EINVAL), in the
+ * layout of jolt_rotation.  With Q = I the residual path quantizes the
+ * unrotated residual: the unrotated quantization baseline.  Synchronizes
+ * `stream`.  Source: as jolt_rotation; the baseline: JoLT abstract, the
+ * sentence naming per-entry quantization among the compared families. */
+jolt_status jolt_rotation_from(const double* Q, int32_t D, void* q_dev, size_t q_bytes, void* stream);
+
 /* Encode one tensor with the given factors: stores bf16 U_T[:, :r_T],
  * U_D[:, :r_D] and core G_h = U_T^T X_h U_D, takes the residual against the
  * stored parts, rotates it (Y = R Q^T along features), quantizes Y in groups
@@ -230,6 +238,28 @@ jolt_status jolt_decode_many(int32_t n, const jolt_shape* shape, const jolt_choi
                              const void* const* blobs, const size_t* blob_bytes,
                              const void* rot_dev, void* const* outs,
                              void* ws_dev, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------- cross-layer SVD baseline */
+
+/* A comparison codec the pages name but do not define (JoLT abstract, the
+ * sentence on cross-layer low-rank factorizations among the compared
+ * families; news article on JoLT, paragraph 3): one feature basis for n
+ * tensors of one shape (a layer group's K or V tensors), the leading r
+ * eigenvectors U of their summed feature Grams sum_i sum_h X_ih^T X_ih
+ * (tridiagonal eigensolver, fp32), stored as bf16 basis_dev [r][D] (row j =
+ * eigenvector j, eigenvalues descending); each tensor stores its
+ * coefficients bf16(X_i U~) as coeff_dev[i] [H][T][r]; reconstruction
+ * X^_i = C_i U~^T in the input dtype.  Bytes: 2 H T r per tensor + 2 D r.
+ * lam_host (optional, [r]): the leading eigenvalues.  ws_bytes >=
+ * jolt_xl_workspace_bytes.  Synchronizes `stream` once, at the end.
+ * Errors: EINVAL, ENOSPACE, EHIP. */
+size_t jolt_xl_workspace_bytes(int32_t n, const jolt_shape* shape, int32_t r);
+jolt_status jolt_xl_encode(int32_t n, const jolt_shape* shape, const void* const* x_dev, int32_t r,
+                           void* basis_dev, void* const* coeff_dev, double* lam_host,
+                           void* ws_dev, size_t ws_bytes, void* stream);
+/* X^_i = C_i U~^T into out_dev[i] ([H][T][D], shape->dtype).  Asynchronous. */
+jolt_status jolt_xl_decode(int32_t n, const jolt_shape* shape, int32_t r, const void* basis_dev,
+                           const void* const* coeff_dev, void* const* out_dev, void* stream);
 
 /* Allocation-free decode, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid

@@ -68,6 +68,7 @@ SIGNATURES = {
     "jolt_factors": (C.c_int, [C.POINTER(AllocReq), C.c_void_p, C.c_int32, C.POINTER(C.c_void_p),
                                C.POINTER(C.c_int32), C.POINTER(C.c_void_p)]),
     "jolt_rotation": (C.c_int, [C.c_uint64, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "jolt_rotation_from": (C.c_int, [C.POINTER(C.c_double), C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]),
     "jolt_encode": (C.c_int, [C.POINTER(Shape), C.c_void_p, Choice, C.c_void_p, C.c_int32, C.c_void_p,
                               C.c_int32, C.c_void_p, C.c_uint64, C.c_void_p, C.c_size_t, C.c_void_p,
                               C.c_size_t, C.c_void_p]),
@@ -80,6 +81,12 @@ SIGNATURES = {
     "jolt_decode_many": (C.c_int, [C.c_int32, C.POINTER(Shape), C.POINTER(Choice), C.POINTER(C.c_void_p),
                                    C.POINTER(C.c_size_t), C.c_void_p, C.POINTER(C.c_void_p), C.c_void_p,
                                    C.c_size_t, C.c_void_p]),
+    "jolt_xl_workspace_bytes": (C.c_size_t, [C.c_int32, C.POINTER(Shape), C.c_int32]),
+    "jolt_xl_encode": (C.c_int, [C.c_int32, C.POINTER(Shape), C.POINTER(C.c_void_p), C.c_int32, C.c_void_p,
+                                 C.POINTER(C.c_void_p), C.POINTER(C.c_double), C.c_void_p, C.c_size_t,
+                                 C.c_void_p]),
+    "jolt_xl_decode": (C.c_int, [C.c_int32, C.POINTER(Shape), C.c_int32, C.c_void_p, C.POINTER(C.c_void_p),
+                                 C.POINTER(C.c_void_p), C.c_void_p]),
     "jolt_decode_static_scratch_bytes": (C.c_size_t, []),
     "jolt_decode_many_static": (C.c_int, [C.c_int32, C.POINTER(Shape), C.POINTER(Choice), C.POINTER(C.c_void_p),
                                           C.POINTER(C.c_size_t), C.c_void_p, C.POINTER(C.c_void_p),

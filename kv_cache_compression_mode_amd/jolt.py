@@ -114,6 +114,19 @@ def rotation(seed: int, D: int = D_FEATURES, device="cuda") -> torch.Tensor:
     return buf
 
 
+def rotation_from(Q: np.ndarray, device="cuda") -> torch.Tensor:
+    """Prepared rotation buffer from a host orthogonal matrix (identity: the
+    unrotated quantizer)."""
+    Qh = np.ascontiguousarray(Q, dtype=np.float64)
+    D = Qh.shape[0]
+    _need(Qh.shape == (D, D), "Q must be square")
+    n = lib().jolt_rotation_bytes(D)
+    buf = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    check(lib().jolt_rotation_from(Qh.ctypes.data_as(C.POINTER(C.c_double)), D, buf.data_ptr(), n,
+                                   _stream(buf.device)), "jolt_rotation_from")
+    return buf
+
+
 def rotation_host(seed: int, D: int = D_FEATURES) -> np.ndarray:
     out = np.empty((D, D), dtype=np.float64)
     check(lib().jolt_rotation_host(seed, D, out.ctypes.data_as(C.POINTER(C.c_double))),
@@ -396,6 +409,52 @@ def decode_many_static(blobs, H: int, T: int, choices, rot: torch.Tensor, outs, 
     op = (C.c_void_p * n)(*[o.data_ptr() for o in outs])
     check(lib().jolt_decode_many_static(n, C.byref(shape), ch, bp, bb, rot.data_ptr(), op, _stream(dev)),
           "jolt_decode_many_static")
+
+
+def xl_encode(xs, r: int):
+    """Cross-layer SVD of tensors of one shape (one layer group's K or V):
+    (basis bf16 [r, 128], coefficients [bf16 [H, T, r] per tensor], leading
+    eigenvalues [r])."""
+    n = len(xs)
+    _need(n >= 1, "at least one tensor")
+    x0 = xs[0]
+    _need(x0.dim() == 3 and x0.shape[2] == D_FEATURES, f"tensors must be [H, T, {D_FEATURES}]")
+    H, T, D = x0.shape
+    for i, x in enumerate(xs):
+        _need(x.shape == x0.shape and x.dtype == x0.dtype, "one shape and dtype")
+        _check_buf(x, x0.device, f"xs[{i}]")
+    shape = make_shape(H, T, D, x0.dtype)
+    basis = torch.empty((r, D), dtype=torch.bfloat16, device=x0.device)
+    coeffs = [torch.empty((H, T, r), dtype=torch.bfloat16, device=x0.device) for _ in range(n)]
+    nws = lib().jolt_xl_workspace_bytes(n, C.byref(shape), r)
+    if nws == 0:
+        check(_lib.JOLT_EINVAL, "jolt_xl_workspace_bytes")
+    ws = torch.empty(nws, dtype=torch.uint8, device=x0.device)
+    lam = np.zeros(r)
+    xp = (C.c_void_p * n)(*[x.data_ptr() for x in xs])
+    cp = (C.c_void_p * n)(*[c.data_ptr() for c in coeffs])
+    check(lib().jolt_xl_encode(n, C.byref(shape), xp, r, basis.data_ptr(), cp,
+                               lam.ctypes.data_as(C.POINTER(C.c_double)), ws.data_ptr(), nws,
+                               _stream(x0.device)), "jolt_xl_encode")
+    return basis, coeffs, lam
+
+
+def xl_decode(basis: torch.Tensor, coeffs, dtype=torch.bfloat16):
+    """X^_i = C_i U~^T for every coefficient tensor, in `dtype`."""
+    n = len(coeffs)
+    r, D = basis.shape
+    H, T, _ = coeffs[0].shape
+    _check_buf(basis, basis.device, "basis", 2 * r * D)
+    for i, c in enumerate(coeffs):
+        _need(c.shape == (H, T, r) and c.dtype == torch.bfloat16, f"coeffs[{i}] must be bf16 {(H, T, r)}")
+        _check_buf(c, basis.device, f"coeffs[{i}]")
+    outs = [torch.empty((H, T, D), dtype=dtype, device=basis.device) for _ in range(n)]
+    shape = make_shape(H, T, D, dtype)
+    cp = (C.c_void_p * n)(*[c.data_ptr() for c in coeffs])
+    op = (C.c_void_p * n)(*[o.data_ptr() for o in outs])
+    check(lib().jolt_xl_decode(n, C.byref(shape), r, basis.data_ptr(), cp, op, _stream(basis.device)),
+          "jolt_xl_decode")
+    return outs
 
 
 def quantize(y: torch.Tensor, bits: int):

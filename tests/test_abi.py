@@ -70,6 +70,21 @@ def test_invalid_arguments_rejected(J):
     assert L.jolt_quantize(None, 4, 128, 2, None, None, None) == jl.JOLT_EINVAL
     assert L.jolt_encode(None, None, jl.Choice(0, 0, 2), None, 0, None, 0, None, 0, None, 0, None, 0,
                          None) == jl.JOLT_EINVAL
+    # a rotation from a matrix that is not orthogonal is refused before any device access
+    import ctypes as C
+    import numpy as np
+    bad = np.eye(128)
+    bad[3, 5] = 1e-6
+    dummy = C.create_string_buffer(16)
+    assert L.jolt_rotation_from(bad.ctypes.data_as(C.POINTER(C.c_double)), 128, C.addressof(dummy),
+                                L.jolt_rotation_bytes(128), None) == jl.JOLT_EINVAL
+    sh = J.make_shape(8, 1024, 128, 0)
+    assert L.jolt_xl_workspace_bytes(4, C.byref(sh), 0) == 0          # r in 1..D
+    assert L.jolt_xl_workspace_bytes(4, C.byref(sh), 129) == 0
+    assert L.jolt_xl_workspace_bytes(0, C.byref(sh), 8) == 0
+    assert L.jolt_xl_encode(0, C.byref(sh), None, 8, None, None, None, None, 0, None) == jl.JOLT_EINVAL
+    assert L.jolt_xl_decode(1, C.byref(sh), 8, None, None, None, None) == jl.JOLT_EINVAL
+    assert L.jolt_decode_many_static(1, C.byref(sh), None, None, None, None, None, None) == jl.JOLT_EINVAL
 
 
 def test_header_parse(J):
