@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--copy-mib", type=int, default=1024,
                    help="size of the calibration copy in --profile-step mode")
     p.add_argument("--traffic-kernel", default="gemm", help="kernel of the --record-traffic record")
+    p.add_argument("--compare", action="store_true",
+                   help="instead of timing: relative errors of JoLT over a 2x..3x budget sweep (K and V "
+                        "separately) and of the comparison codecs at matched bytes, one JSON line")
     p.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="turn the counter_collection.csv files of two rocprofv3 --pmc runs of "
                         "--profile-step (FETCH_SIZE, then WRITE_SIZE) into the traffic record "
@@ -160,6 +163,10 @@ def main():
                 xd = xs[l][k].double()
                 errs.append(float(torch.linalg.vector_norm(xd - pair[k].double()) / torch.linalg.vector_norm(xd)))
         return np.array(errs).reshape(L, 2)
+
+    if args.compare:
+        print(json.dumps(compare_codecs(jolt, cfg, xs, flat, rot, outs, tdt, dev)), flush=True)
+        return
 
     K = 1 if args.profile_step else args.steps
     kstats = {}
@@ -465,6 +472,96 @@ def roofline_for(name, st, workload):
             "arithmetic_intensity": round(ai, 2), "ridge": round(ridge, 2),
             "GBps": round(gbps, 1), "TFLOPs": round(tflops, 2),
             "avg_launch_ms": round(avg_ms, 5), "launches": st["launches"]}
+
+
+SWEEP_RATIOS = (2.0, 2.25, 2.5, 2.75, 3.0)
+
+
+def xl_rank(H, T, D, layers, ratio):
+    """Largest cross-layer SVD rank whose group bytes (2 H T r per tensor +
+    2 D r per group) fit the group's share of the budget."""
+    budget = int(2.0 * H * T * D / ratio) * layers
+    r = 0
+    while r < D and layers * 2 * H * T * (r + 1) + 2 * D * (r + 1) <= budget:
+        r += 1
+    return r
+
+
+def compare_codecs(jolt, cfg, xs, flat, rot, outs, tdt, dev):
+    """Relative Frobenius errors (mean over the cache's K and V tensors) of
+    JoLT across a 2x..3x budget sweep, and of the comparison codecs at
+    matched bytes: rotated and unrotated b-bit quantization (the largest
+    b <= 4 that fits), cross-layer SVD (one feature basis per layer group
+    and kind), and JoLT at the 4-bit quantizer's byte total."""
+    import numpy as np
+    import torch
+    L, H, T, D = cfg.n_layers, cfg.H, cfg.T, cfg.D
+    G = 4
+    n_in = H * T * D
+
+    def decode_into(blobs, choices, q):
+        ws = torch.empty(jolt.decode_many_workspace_bytes(H, T, choices, tdt), dtype=torch.uint8, device=dev)
+        res = {}
+        for l in range(L):                     # two output buffers per layer when streaming
+            jolt.decode_many(blobs[2 * l:2 * l + 2], H, T, choices[2 * l:2 * l + 2], q, outs[:2] if len(outs) == 2
+                             else outs[2 * l:2 * l + 2], ws, dtype=tdt)
+            for k in (0, 1):
+                o = outs[k] if len(outs) == 2 else outs[2 * l + k]
+                xd = xs[l][k].double()
+                res[(l, k)] = float(torch.linalg.vector_norm(xd - o.double()) / torch.linalg.vector_norm(xd))
+        e = np.array([[res[(l, k)] for k in (0, 1)] for l in range(L)])
+        return {"K": round(float(e[:, 0].mean()), 6), "V": round(float(e[:, 1].mean()), 6)}
+
+    def jolt_at(ratio):
+        res = jolt.allocate(xs, ratio=ratio, method=cfg.method, bits=cfg.bits, seed=cfg.seed)
+        choices = [res.choice_of(i // 2, i % 2) for i in range(2 * L)]
+        blobs = jolt.encode_many(flat, choices, res, rot, seed=cfg.seed)
+        e = decode_into(blobs, choices, rot)
+        plan = {}
+        for (g, k), c in sorted(res.choice.items()):
+            plan.setdefault("KV"[k], []).append(list(c))
+        return {"ratio": ratio, "bytes": int(res.total_bytes), "budget": int(res.budget_bytes),
+                "rel_err": e, "plan": plan}
+
+    def quant_at(b, q):
+        choices = [(0, 0, b)] * (2 * L)
+        blobs = jolt.encode_many(flat, choices, [(None, None)] * (2 * L), q, seed=cfg.seed)
+        return {"bits": b, "bytes": int(sum(x.numel() for x in blobs)), "rel_err": decode_into(blobs, choices, q)}
+
+    def xl_at(ratio):
+        r = xl_rank(H, T, D, G, ratio)
+        err = np.zeros((L, 2))
+        nbytes = 0
+        for g0 in range(0, L, G):
+            layers = list(range(g0, min(L, g0 + G)))
+            for k in (0, 1):
+                basis, coeffs, _ = jolt.xl_encode([xs[l][k] for l in layers], r)
+                dec = jolt.xl_decode(basis, coeffs, dtype=tdt)
+                nbytes += 2 * D * r + sum(c.numel() * 2 for c in coeffs)
+                for l, o in zip(layers, dec):
+                    xd = xs[l][k].double()
+                    err[l, k] = float(torch.linalg.vector_norm(xd - o.double()) / torch.linalg.vector_norm(xd))
+                del dec, coeffs
+        return {"rank": r, "bytes": int(nbytes),
+                "rel_err": {"K": round(float(err[:, 0].mean()), 6), "V": round(float(err[:, 1].mean()), 6)}}
+
+    ident = jolt.rotation_from(np.eye(D), device=dev)
+    sweep = [jolt_at(r) for r in SWEEP_RATIOS]
+    b4 = jolt.blob_bytes(H, T, D, (0, 0, 4))
+    r4 = 2.0 * n_in / b4                          # the 4-bit quantizer's compression ratio
+    at2 = {"budget_ratio": 2.0, "jolt": sweep[0],
+           "rotated_quant": quant_at(4, rot), "unrotated_quant": quant_at(4, ident), "cross_layer_svd": xl_at(2.0)}
+    at4 = {"budget_ratio": round(r4, 4), "jolt": jolt_at(r4),
+           "rotated_quant": quant_at(4, rot), "unrotated_quant": quant_at(4, ident), "cross_layer_svd": xl_at(r4)}
+    for m in (at2, at4):
+        j = m["jolt"]["rel_err"]
+        m["error_over_jolt"] = {name: {kv: round(m[name]["rel_err"][kv] / j[kv], 2) for kv in "KV"}
+                                for name in ("rotated_quant", "unrotated_quant", "cross_layer_svd")}
+    return {"metric": "relative Frobenius error (mean over the cache's tensors), JoLT vs comparison codecs",
+            "config": {"workload": cfg.name, "layers": L, "kv_heads": H, "tokens": T, "head_dim": D,
+                       "input_dtype": cfg.dtype, "method": cfg.method},
+            "data": "synthetic (seeded low-rank + noise + outlier channels, model cache shapes)",
+            "sweep": sweep, "matched_bytes_2x": at2, "matched_bytes_4bit": at4}
 
 
 def cpu_baseline(cfg, n_tensors):
