@@ -239,6 +239,28 @@ jolt_status jolt_decode_many(int32_t n, const jolt_shape* shape, const jolt_choi
                              const void* rot_dev, void* const* outs,
                              void* ws_dev, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------ decode fused into attention */
+
+/* Attention of new query vectors over one layer's compressed K and V
+ * records, with the records decoded tile by tile in registers (the decode's
+ * arithmetic) and never written to memory.  Source: JoLT abstract, first
+ * sentence (the KV cache is the dominant serving cost; attention is what
+ * reads it); the consumer is not on the pages: plain scaled dot-product
+ * attention, grouped as in GQA.
+ * shape: the records' (H KV heads, T tokens, D = 128, dtype); choice_k /
+ * choice_v: the records' choices (trusted, as in jolt_decode); q_dev fp32
+ * [H * G][n_new][D] (query head h G + g attends over KV head h), out_dev
+ * fp32 of the same layout: out = softmax(q K^T / sqrt(D)) V.  G * n_new <= 8.
+ * ws_bytes >= jolt_attend_workspace_bytes (the two records' W planes and
+ * per-block softmax partials).  Asynchronous.  Errors: EINVAL, ENOSPACE,
+ * EHIP. */
+size_t jolt_attend_workspace_bytes(const jolt_shape* shape, jolt_choice choice_k, jolt_choice choice_v,
+                                   int32_t G, int32_t n_new);
+jolt_status jolt_attend(const jolt_shape* shape, jolt_choice choice_k, const void* blob_k, size_t blob_k_bytes,
+                        jolt_choice choice_v, const void* blob_v, size_t blob_v_bytes, const void* rot_dev,
+                        const float* q_dev, int32_t G, int32_t n_new, float* out_dev, void* ws_dev,
+                        size_t ws_bytes, void* stream);
+
 /* ------------------------------------------- cross-layer SVD baseline */
 
 /* A comparison codec the pages name but do not define (JoLT abstract, the
@@ -340,8 +362,8 @@ typedef struct {
  * streams.  Kernel names: "qr_panel", "qr_update" (block reflectors applied
  * to tall blocks), "gemm" (fp32 matrix-core products), "gemm_bf16" (bf16
  * matrix-core products), "band", "chase", "tri_eig", "chase_back",
- * "band_back" (the eigensolver stages), "encode_w", "encode_residual",
- * "quantize", "decode_w", "decode". */
+ * "band_back" (the eigensolver stages), "gram" (the Grams), "encode_w",
+ * "encode_residual", "quantize", "decode_w", "decode", "attend". */
 jolt_status jolt_profile_enable(const char* kernels);
 
 /* Synchronizes the device, then reports the statistics of one kernel name

@@ -81,6 +81,10 @@ SIGNATURES = {
     "jolt_decode_many": (C.c_int, [C.c_int32, C.POINTER(Shape), C.POINTER(Choice), C.POINTER(C.c_void_p),
                                    C.POINTER(C.c_size_t), C.c_void_p, C.POINTER(C.c_void_p), C.c_void_p,
                                    C.c_size_t, C.c_void_p]),
+    "jolt_attend_workspace_bytes": (C.c_size_t, [C.POINTER(Shape), Choice, Choice, C.c_int32, C.c_int32]),
+    "jolt_attend": (C.c_int, [C.POINTER(Shape), Choice, C.c_void_p, C.c_size_t, Choice, C.c_void_p, C.c_size_t,
+                              C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t,
+                              C.c_void_p]),
     "jolt_xl_workspace_bytes": (C.c_size_t, [C.c_int32, C.POINTER(Shape), C.c_int32]),
     "jolt_xl_encode": (C.c_int, [C.c_int32, C.POINTER(Shape), C.POINTER(C.c_void_p), C.c_int32, C.c_void_p,
                                  C.POINTER(C.c_void_p), C.POINTER(C.c_double), C.c_void_p, C.c_size_t,

@@ -776,11 +776,16 @@ hipError_t launch_encode_residual_many(const EncodeArgs* list_dev, int n, int64_
   return hipGetLastError();
 }
 
+hipError_t launch_make_w(const DecBatch& b, hipStream_t s) {
+  if (b.wtiles_total <= 0) return hipSuccess;
+  ProfScope ps("decode_w", s);
+  k_make_w<<<(b.wtiles_total + 3) / 4, 256, 0, s>>>(b);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_batch(const DecBatch& b, hipStream_t s) {
-  if (b.wtiles_total > 0) {
-    ProfScope ps("decode_w", s);
-    k_make_w<<<(b.wtiles_total + 3) / 4, 256, 0, s>>>(b);
-    const hipError_t e = hipGetLastError();
+  {
+    const hipError_t e = launch_make_w(b, s);
     if (e != hipSuccess) return e;
   }
   ProfScope ps("decode", s);

@@ -133,14 +133,4 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// Round-robin ("circle method") pairing of n (even) slots: round r in
-// [0, n-1), pair i in [0, n/2).  Slot 0 stays, the others rotate.
-__host__ __device__ __forceinline__ int rr_slot(int k, int r, int n) {
-  return k == 0 ? 0 : 1 + (k - 1 + r) % (n - 1);
-}
-__host__ __device__ __forceinline__ void rr_pair(int i, int r, int n, int* p, int* q) {
-  *p = rr_slot(i, r, n);
-  *q = rr_slot(n - 1 - i, r, n);
-}
-
 }  // namespace jolt

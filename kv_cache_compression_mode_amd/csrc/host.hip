@@ -868,6 +868,28 @@ size_t decode_w_bytes(int64_t H, int64_t D, jolt_choice c) {
   return c.r_T ? 2 * a256(2ull * H * D * rtp_of(c.r_T)) : 0;
 }
 
+// The decode's view of one record: its sections, the W planes at wsp (the
+// record's decode_w_bytes), its first W tile.
+DecRec dec_rec(int64_t H, int64_t T, int64_t D, jolt_choice c, const void* blob_dev, void* out, char* wsp,
+               int wtile0) {
+  const BlobLayout L = blob_layout(H, T, D, c);
+  const char* blob = static_cast<const char*>(blob_dev);
+  DecRec R{};
+  R.Ut = reinterpret_cast<const uint16_t*>(blob + L.ut);
+  R.Ud = reinterpret_cast<const uint16_t*>(blob + L.ud);
+  R.G = reinterpret_cast<const uint16_t*>(blob + L.g);
+  R.scales = reinterpret_cast<const uint32_t*>(blob + L.sc);
+  R.codes = reinterpret_cast<const uint32_t*>(blob + L.cd);
+  R.out = out;
+  R.r_T = c.r_T; R.r_D = c.r_D; R.bits = c.bits;
+  R.r_Tp = static_cast<int32_t>(rtp_of(c.r_T));
+  const size_t wneed = decode_w_bytes(H, D, c);
+  R.Whi = reinterpret_cast<uint16_t*>(wsp);
+  R.Wlo = reinterpret_cast<uint16_t*>(wsp + wneed / 2);
+  R.wtile0 = wtile0;
+  return R;
+}
+
 void decode_records(int n, const jolt_shape* shape, const jolt_choice* ch, const void* const* blobs,
                     const void* rot_dev, void* const* outs, void* ws, size_t ws_cap, hipStream_t s) {
   const int64_t H = shape->H, T = shape->T, D = shape->D;
@@ -904,22 +926,9 @@ void decode_records(int n, const jolt_shape* shape, const jolt_choice* ch, const
     const size_t wneed = decode_w_bytes(H, D, c);
     if (b.n == kDecBatch || (b.n > 0 && used + wneed > ws_cap)) issue();
     if (b.n == 0) first = i;
-    const BlobLayout L = blob_layout(H, T, D, c);
-    const char* blob = static_cast<const char*>(blobs[i]);
     DecRec& R = b.rec[b.n++];
-    R.Ut = reinterpret_cast<const uint16_t*>(blob + L.ut);
-    R.Ud = reinterpret_cast<const uint16_t*>(blob + L.ud);
-    R.G = reinterpret_cast<const uint16_t*>(blob + L.g);
-    R.scales = reinterpret_cast<const uint32_t*>(blob + L.sc);
-    R.codes = reinterpret_cast<const uint32_t*>(blob + L.cd);
-    R.out = outs[i];
-    R.r_T = c.r_T; R.r_D = c.r_D; R.bits = c.bits;
-    R.r_Tp = static_cast<int32_t>(rtp_of(c.r_T));
-    char* wsp = static_cast<char*>(ws) + used;
-    R.Whi = reinterpret_cast<uint16_t*>(wsp);
-    R.Wlo = reinterpret_cast<uint16_t*>(wsp + wneed / 2);
+    R = dec_rec(H, T, D, c, blobs[i], outs[i], static_cast<char*>(ws) + used, wtiles);
     used += wneed;
-    R.wtile0 = wtiles;
     wtiles += static_cast<int>(H * (R.r_Tp / 32));
   }
   issue();
@@ -1593,6 +1602,82 @@ jolt_status jolt_xl_decode(int32_t n, const jolt_shape* shape, int32_t r, const 
       g.C = out_dev[i]; g.c_dtype = shape->dtype == JOLT_BF16 ? kBF16 : kF32; g.c_m = D; g.c_n = 1;
       ck(launch_gemm(g, 1, s));
     }
+    return JOLT_OK;
+  });
+}
+
+// ------------------------------------------------- decode fused into attention
+struct AttnLayout {
+  size_t wk, wv, part, total;
+  int n_blk, nq;
+};
+AttnLayout attn_layout(const jolt_shape* sh, jolt_choice ck, jolt_choice cv, int G, int n_new) {
+  AttnLayout L{};
+  L.nq = G * n_new;
+  L.n_blk = static_cast<int>((static_cast<int64_t>(sh->T) + 255) / 256);
+  size_t off = 0;
+  L.wk = off; off += a256(decode_w_bytes(sh->H, sh->D, ck));
+  L.wv = off; off += a256(decode_w_bytes(sh->H, sh->D, cv));
+  L.part = off; off += a256(4ull * sh->H * L.nq * L.n_blk * (sh->D + 2));
+  L.total = off + 256;
+  return L;
+}
+
+bool attn_args_ok(const jolt_shape* sh, jolt_choice ck, jolt_choice cv, int G, int n_new) {
+  return shape_ok(sh) && choice_ok(sh, ck) && choice_ok(sh, cv) && G >= 1 && n_new >= 1 &&
+         static_cast<int64_t>(G) * n_new <= kAttnMaxQ;
+}
+
+size_t jolt_attend_workspace_bytes(const jolt_shape* shape, jolt_choice choice_k, jolt_choice choice_v, int32_t G,
+                                   int32_t n_new) {
+  if (!attn_args_ok(shape, choice_k, choice_v, G, n_new)) return 0;
+  return attn_layout(shape, choice_k, choice_v, G, n_new).total;
+}
+
+jolt_status jolt_attend(const jolt_shape* shape, jolt_choice choice_k, const void* blob_k, size_t blob_k_bytes,
+                        jolt_choice choice_v, const void* blob_v, size_t blob_v_bytes, const void* rot_dev,
+                        const float* q_dev, int32_t G, int32_t n_new, float* out_dev, void* ws_dev,
+                        size_t ws_bytes, void* stream) {
+  if (!attn_args_ok(shape, choice_k, choice_v, G, n_new)) return JOLT_EINVAL;
+  if (!blob_k || !blob_v || !rot_dev || !q_dev || !out_dev || !ws_dev) return JOLT_EINVAL;
+  const int64_t H = shape->H, T = shape->T, D = shape->D;
+  if (blob_k_bytes < blob_layout(H, T, D, choice_k).total || blob_v_bytes < blob_layout(H, T, D, choice_v).total)
+    return JOLT_ENOSPACE;
+  const AttnLayout L = attn_layout(shape, choice_k, choice_v, G, n_new);
+  if (ws_bytes < L.total) return JOLT_ENOSPACE;
+  return guard([&]() -> jolt_status {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(ws_dev);
+    const size_t n2 = static_cast<size_t>(D) * D;
+    DecBatch b{};
+    b.n = 2;
+    b.H = static_cast<int32_t>(H);
+    b.T = static_cast<int32_t>(T);
+    b.rec[0] = dec_rec(H, T, D, choice_k, blob_k, nullptr, ws + L.wk, 0);
+    b.rec[1] = dec_rec(H, T, D, choice_v, blob_v, nullptr, ws + L.wv,
+                       static_cast<int>(H * (b.rec[0].r_Tp / 32)));
+    b.wtiles_total = static_cast<int>(H * (b.rec[0].r_Tp / 32 + b.rec[1].r_Tp / 32));
+    ck(launch_make_w(b, s));
+    AttnArgs a{};
+    a.k = b.rec[0];
+    a.v = b.rec[1];
+    a.Qt16 = reinterpret_cast<const uint16_t*>(static_cast<const char*>(rot_dev) + 2 * a256(4 * n2));
+    a.q = q_dev;
+    a.out = out_dev;
+    a.part = reinterpret_cast<float*>(ws + L.part);
+    a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(D)));
+    a.H = static_cast<int32_t>(H); a.T = static_cast<int32_t>(T);
+    a.G = G; a.n_new = n_new; a.nq = L.nq; a.n_blk = L.n_blk;
+    if (prof_enabled("attend")) {
+      // the two records read once, the queries read and the outputs written
+      // once; the two reconstructions and 4 D flops per (query vector, token)
+      const int e = shape->dtype == JOLT_BF16 ? 2 : 4;
+      const PathWork pk = residual_work(H, T, D, choice_k, e), pv = residual_work(H, T, D, choice_v, e);
+      const double xbytes = 2.0 * static_cast<double>(H * T * D) * e;    // the inputs / outputs counted there
+      prof_add_work("attend", pk.bytes + pv.bytes - xbytes + 8.0 * H * L.nq * D,
+                    pk.flops + pv.flops + 4.0 * H * L.nq * static_cast<double>(T) * D);
+    }
+    ck(launch_attn_decode(a, s));
     return JOLT_OK;
   });
 }

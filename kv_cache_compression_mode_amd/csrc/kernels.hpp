@@ -165,6 +165,26 @@ struct DecBatch {
   const uint16_t* Qt16;    // bf16 [D][D], Qt16[c][d] = Q[d][c]
 };
 hipError_t launch_decode_batch(const DecBatch& b, hipStream_t s);
+// The W planes of the batch's records alone (the decode's prologue).
+hipError_t launch_make_w(const DecBatch& b, hipStream_t s);
+
+// Decode fused into attention over one layer's K and V records: per KV head
+// h, nq = G * n_new query vectors (the GQA group's query heads times the new
+// tokens), q fp32 [H * G][n_new][D] (query head h G + g reads KV head h),
+// out fp32 of the same layout; part: fp32 [H][nq][n_blk][D + 2] block partials
+// (o[D], max, sum), n_blk = ceil(T / 256).  The records' W planes must be
+// formed beforehand (launch_make_w).
+constexpr int kAttnMaxQ = 8;
+struct AttnArgs {
+  DecRec k, v;
+  const uint16_t* Qt16;    // bf16 [D][D], Qt16[c][d] = Q[d][c]
+  const float* q;
+  float* out;
+  float* part;
+  float scale;             // 1 / sqrt(D)
+  int32_t H, T, G, n_new, nq, n_blk;
+};
+hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s);
 // The 256-byte head of a record (the 64-byte header, zeros to 256) and the
 // padding after each of its five sections, zeroed, so that every byte of a
 // record is defined: pad[2 j] = byte offset, pad[2 j + 1] = length (< 256).

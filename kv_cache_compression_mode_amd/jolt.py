@@ -411,6 +411,42 @@ def decode_many_static(blobs, H: int, T: int, choices, rot: torch.Tensor, outs, 
           "jolt_decode_many_static")
 
 
+def attend_workspace_bytes(H: int, T: int, choice_k, choice_v, G: int, n_new: int,
+                           dtype=torch.bfloat16) -> int:
+    return lib().jolt_attend_workspace_bytes(C.byref(make_shape(H, T, D_FEATURES, dtype)), Choice(*choice_k),
+                                             Choice(*choice_v), G, n_new)
+
+
+def attend(blob_k, choice_k, blob_v, choice_v, H: int, T: int, q: torch.Tensor, G: int, rot: torch.Tensor,
+           dtype=torch.bfloat16, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """softmax(q K^T / sqrt(D)) V over one layer's K and V records, decoded in
+    registers.  q: fp32 [H * G, n_new, 128]; returns fp32 of q's shape."""
+    _need(q.dim() == 3 and q.shape[0] == H * G and q.shape[2] == D_FEATURES and q.dtype == torch.float32,
+          f"q must be fp32 [{H * G}, n_new, {D_FEATURES}]")
+    dev = q.device
+    _check_buf(q, dev, "q")
+    n_new = q.shape[1]
+    shape = make_shape(H, T, D_FEATURES, dtype)
+    ck, cv = Choice(*choice_k), Choice(*choice_v)
+    _check_buf(blob_k, dev, "blob_k", lib().jolt_blob_bytes(C.byref(shape), ck))
+    _check_buf(blob_v, dev, "blob_v", lib().jolt_blob_bytes(C.byref(shape), cv))
+    _check_buf(rot, dev, "rot", lib().jolt_rotation_bytes(D_FEATURES))
+    nws = lib().jolt_attend_workspace_bytes(C.byref(shape), ck, cv, G, n_new)
+    if nws == 0:
+        check(_lib.JOLT_EINVAL, "jolt_attend_workspace_bytes")
+    if workspace is not None:
+        _check_buf(workspace, dev, "workspace", nws)
+    ws = workspace if workspace is not None else torch.empty(nws, dtype=torch.uint8, device=dev)
+    if out is not None:
+        _need(out.shape == q.shape and out.dtype == torch.float32, "out must be fp32 of q's shape")
+        _check_buf(out, dev, "out")
+    o = out if out is not None else torch.empty_like(q)
+    check(lib().jolt_attend(C.byref(shape), ck, blob_k.data_ptr(), blob_k.numel(), cv, blob_v.data_ptr(),
+                            blob_v.numel(), rot.data_ptr(), q.data_ptr(), G, n_new, o.data_ptr(), ws.data_ptr(),
+                            ws.numel(), _stream(dev)), "jolt_attend")
+    return o
+
+
 def xl_encode(xs, r: int):
     """Cross-layer SVD of tensors of one shape (one layer group's K or V):
     (basis bf16 [r, 128], coefficients [bf16 [H, T, r] per tensor], leading

@@ -56,14 +56,19 @@ def encode_tensor(X, U_T, U_D, choice, Q):
                 Y=Y, m16=m16, s16=s16, codes=codes)
 
 
-def decode_tensor(enc, Q, dtype: str) -> np.ndarray:
+def decode_exact(enc, Q) -> np.ndarray:
+    """The decoded tensor in fp64, before rounding to an output dtype."""
     H, T, D = enc["shape"]
     r_T = enc["choice"][0]
     Yh = quant.dequantize(enc["m16"], enc["s16"], enc["codes"])        # [H, T, D]
     Xh = (Yh.reshape(-1, D) @ Q).reshape(H, T, D)
     if r_T > 0:
         Xh = Xh + tucker.reconstruct(enc["G"], enc["U_T"], enc["U_D"])
-    return round_to(Xh, dtype)
+    return Xh
+
+
+def decode_tensor(enc, Q, dtype: str) -> np.ndarray:
+    return round_to(decode_exact(enc, Q), dtype)
 
 
 def rel_err(X, Xh) -> float:

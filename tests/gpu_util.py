@@ -205,3 +205,37 @@ def check_decode_rows(out_rows, parts: dict, choice, Q: np.ndarray, hs, ts, out_
         assert np.all(np.abs(got - exact) <= bound + ulp)
         return 0.0
     return check_bf16_rounding(got, exact, bound, 1.0, max_frac=0.25)
+
+
+def pack_record(enc: dict, dtype_code: int = 0, seed: int = 0) -> np.ndarray:
+    """An oracle encode (``codec.encode_tensor``) as record bytes in the
+    library's documented layout (header, then 256-aligned sections U_T, U_D,
+    core, scales, codes), so that GPU kernels can be fed inputs made by the
+    oracle alone."""
+    from oracle import quant
+    H, T, Dd = enc["shape"]
+    r_T, r_D, b = enc["choice"]
+    groups = H * T * Dd // 32
+    ut = 256
+    ud = ut + a256(2 * T * r_T)
+    g = ud + a256(2 * Dd * r_D)
+    sc = g + a256(2 * H * r_T * r_D)
+    cd = sc + a256(4 * groups)
+    total = cd + a256(4 * b * groups)
+    out = np.zeros(total, dtype=np.uint8)
+    hdr = np.array([0x544C4F4A, 1, H, T, Dd, dtype_code, r_T, r_D, b, 32, seed & 0xffffffff, seed >> 32,
+                    0, 0, 0, 0], dtype=np.uint32)
+    out[:64] = hdr.view(np.uint8)
+
+    def bf(x):
+        u = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32)
+        return (u >> 16).astype(np.uint16)          # exact: the stored values are bf16 already
+
+    if r_T > 0:
+        out[ut:ut + 2 * T * r_T] = bf(enc["U_T"]).reshape(-1).view(np.uint8)
+        out[ud:ud + 2 * Dd * r_D] = bf(enc["U_D"]).reshape(-1).view(np.uint8)
+        out[g:g + 2 * H * r_T * r_D] = bf(enc["G"]).reshape(-1).view(np.uint8)
+    scales = np.stack([bf(enc["m16"]).reshape(-1), bf(enc["s16"]).reshape(-1)], axis=1)
+    out[sc:sc + 4 * groups] = scales.reshape(-1).view(np.uint8)
+    out[cd:cd + 4 * b * groups] = quant.pack(enc["codes"], b).reshape(-1)
+    return out
