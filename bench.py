@@ -93,13 +93,13 @@ def main():
     stream = torch.cuda.current_stream(dev)
     print("[bench] inputs resident", file=sys.stderr, flush=True)
 
-    def decode_all(blobs, choices, dws):
+    def decode_all(blobs, choices, dws, validate=True):
         if streaming:
             for l in range(L):
                 jolt.decode_many(blobs[2 * l:2 * l + 2], H, T, choices[2 * l:2 * l + 2], rot, outs, dws,
-                                 dtype=tdt)
+                                 dtype=tdt, validate=validate)
         else:
-            jolt.decode_many(blobs, H, T, choices, rot, outs, dws, dtype=tdt)
+            jolt.decode_many(blobs, H, T, choices, rot, outs, dws, dtype=tdt, validate=validate)
 
     def decode_ws_bytes(choices):
         if streaming:
@@ -203,6 +203,7 @@ def main():
         qstats = jolt.profile_query("quantize")
         jolt.profile_enable(None)
     del qy
+    attn = attend_leg(jolt, cfg, state, rot, dev, tdt, args.profile_step)
     if args.profile_step:
         # a plain copy of known size (read n bytes, write n bytes), against
         # which the FETCH_SIZE / WRITE_SIZE counters are scaled
@@ -225,9 +226,10 @@ def main():
     dws = torch.empty(decode_ws_bytes(choices), dtype=torch.uint8, device=dev)
     reps = 5
     de0, de1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    decode_all(blobs, choices, dws)                    # the binding checks the buffers once
     de0.record(stream)
     for _ in range(reps):
-        decode_all(blobs, choices, dws)
+        decode_all(blobs, choices, dws, validate=False)
     de1.record(stream)
     torch.cuda.synchronize()
     dec_ms = de0.elapsed_time(de1) / reps
@@ -272,6 +274,7 @@ def main():
                               if qstats and qstats["launches"] else None),
         "roofline_gram": (roofline_for("gram", tstats["gram"], cfg.name)
                           if tstats.get("gram", {}).get("launches") else None),
+        "attend": attn,
         "roofline_decode": {"kernel": dec_kernel,
                             "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                             "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
@@ -314,7 +317,7 @@ CPU_SAMPLE = {"mistral7b_t4096_2x": 24, "mistral7b_t1024_flash": 64, "llama13b_t
               "mistral7b_t32768_3x": 4}
 
 KERNELS = ("qr_panel", "qr_update", "gemm", "gemm_bf16", "gram", "band", "chase", "tri_eig", "chase_back",
-           "band_back", "encode_w", "encode_residual", "quantize", "decode_w", "decode")
+           "band_back", "encode_w", "encode_residual", "quantize", "decode_w", "decode", "attend")
 # kernels with roofline targets, timed inside the timed steps
 TIMED_ROOF = ("gram", "encode_residual", "decode")
 CSRC = os.path.join(ROOT, "kv_cache_compression_mode_amd", "csrc")
@@ -359,6 +362,9 @@ ROOF = {
     "quantize": ("k_quantize: group quantizer alone, one group of 32 per thread (fp32 in, b-bit codes and bf16 "
                  "offset/step out)",
                  "k_quantize", r"k_quantize\b", ("codec.hip", "device.hpp"), None, "hbm"),
+    "attend": ("k_attn_decode: attention of new query vectors over a layer's K and V records, the records "
+               "decoded tile by tile in registers (bf16 matrix cores), block softmax partials",
+               "k_attn_decode", r"k_attn_decode\b", ("attn.hip", "device.hpp"), MFMA_BF16_PEAK_TFLOPS, "mfma"),
     "gemm_bf16": ("k_gemm_x: 128x128-tile GEMM on bf16 matrix cores (token and feature Grams, factor recovery, "
                   "Rayleigh and core products; fp32 operands enter as bf16 hi + lo)",
                   "k_gemm_x", r"k_gemm_x<", ("gemm.hip", "device.hpp"), MFMA_BF16_PEAK_TFLOPS, "mfma"),
@@ -472,6 +478,76 @@ def roofline_for(name, st, workload):
             "arithmetic_intensity": round(ai, 2), "ridge": round(ridge, 2),
             "GBps": round(gbps, 1), "TFLOPs": round(tflops, 2),
             "avg_launch_ms": round(avg_ms, 5), "launches": st["launches"]}
+
+
+def attend_leg(jolt, cfg, state, rot, dev, tdt, quiet):
+    """The decode fused into attention on the encoded cache: one new token's
+    query vectors per layer (GQA group 4 for the 8-KV-head shape, 1 for MHA),
+    every layer's K and V records attended in one call each, against decoding
+    the layer to memory and attending over the decoded K and V with torch's
+    batched products and softmax."""
+    import torch
+    L, H, T, D = cfg.n_layers, cfg.H, cfg.T, cfg.D
+    G = 4 if H == 8 else 1
+    blobs, choices = state["blobs"], state["choices"]
+    q = torch.randn((H * G, 1, D), dtype=torch.float32, device=dev) * 0.3
+    ws = torch.empty(max(jolt.attend_workspace_bytes(H, T, choices[2 * l], choices[2 * l + 1], G, 1, tdt)
+                         for l in range(L)), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+
+    def fused():
+        for l in range(L):
+            jolt.attend(blobs[2 * l], choices[2 * l], blobs[2 * l + 1], choices[2 * l + 1], H, T, q, G, rot,
+                        dtype=tdt, out=out, workspace=ws)
+
+    kv = [torch.empty((H, T, D), dtype=tdt, device=dev) for _ in range(2)]
+    dws = torch.empty(max(jolt.decode_many_workspace_bytes(H, T, choices[2 * l:2 * l + 2], tdt) for l in range(L)),
+                      dtype=torch.uint8, device=dev)
+    # query columns per KV head, [H, D, G] contiguous: every batched product
+    # below takes a contiguous right operand
+    qcol = q.view(H, G, D).transpose(1, 2).contiguous().to(tdt)
+    scale = 1.0 / D ** 0.5
+
+    def unfused():
+        for l in range(L):
+            jolt.decode_many(blobs[2 * l:2 * l + 2], H, T, choices[2 * l:2 * l + 2], rot, kv, dws, dtype=tdt)
+            sc = torch.matmul(kv[0], qcol)                                  # [H, T, G]
+            p = torch.softmax(sc.float() * scale, dim=1).to(tdt)
+            torch.matmul(p.transpose(1, 2).contiguous(), kv[1])             # [H, G, D]
+
+    def timed(fn, reps=3, prof=None):
+        fn()
+        torch.cuda.synchronize()
+        if prof:
+            jolt.profile_enable(prof)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        st = jolt.profile_query(prof) if prof else None
+        if prof:
+            jolt.profile_enable(None)
+        return e0.elapsed_time(e1) / reps, st
+
+    if quiet:
+        fused()
+        torch.cuda.synchronize()
+        return None
+    ms_f, st = timed(fused, prof="attend")
+    ms_u, _ = timed(unfused)
+    rec_bytes = sum(b.numel() - 256 for b in blobs)
+    kv_bytes = 2 * L * H * T * D * (2 if tdt == torch.bfloat16 else 4)
+    line = {"workload": f"{L} layers, one new token, {H * G} query heads over {H} KV heads",
+            "fused_ms_per_cache": round(ms_f, 4), "decode_then_sdpa_ms_per_cache": round(ms_u, 4),
+            "speedup_over_decode_then_sdpa": round(ms_u / ms_f, 3),
+            "records_GBps": round(rec_bytes / (ms_f * 1e-3) / 1e9, 1),
+            "uncompressed_kv_equivalent_GBps": round(kv_bytes / (ms_f * 1e-3) / 1e9, 1)}
+    if st and st["launches"]:
+        line["roofline"] = roofline_for("attend", st, cfg.name)
+    return line
 
 
 SWEEP_RATIOS = (2.0, 2.25, 2.5, 2.75, 3.0)

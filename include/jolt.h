@@ -64,8 +64,8 @@ typedef struct {
 } jolt_shape;
 
 /* Ranks and residual bits of one tensor.  (0, 0, b) = no Tucker part: the
- * whole tensor is the residual.  Otherwise 1 <= r_T <= min(T, H*D),
- * 1 <= r_D <= D.  bits in 1..4. */
+ * whole tensor is the residual.  Otherwise 1 <= r_T <= H*D, 1 <= r_D <= D
+ * (a record may hold fewer tokens than r_T: see jolt_append).  bits in 1..4. */
 typedef struct { int32_t r_T, r_D, bits; } jolt_choice;
 
 /* Allocation request for a whole cache: n_layers layers x {K, V}, all of one
@@ -238,6 +238,27 @@ jolt_status jolt_decode_many(int32_t n, const jolt_shape* shape, const jolt_choi
                              const void* const* blobs, const size_t* blob_bytes,
                              const void* rot_dev, void* const* outs,
                              void* ws_dev, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------- appended tokens */
+
+/* Incremental encode of n_new tokens appended to a tensor already encoded
+ * (base_blob: shape `base`, choice with r_T > 0): the pages are silent on
+ * tokens that arrive after encoding; the reading is folding-in (new rows fit
+ * to fixed factors, as latent semantic indexing adds documents without a new
+ * SVD).  The base's stored U~_D and G~ are kept; the new tokens' token-factor
+ * rows solve min_U ||X_new,(T) - U W||_F, W = [G~_h U~_D^T]_h (r_T x H D),
+ * through the normal equations W W^T = Z diag(lambda) Z^T (the tridiagonal
+ * eigensolver, fp32; only non-positive eigenvalues are dropped); the residual against the stored
+ * parts is rotated and quantized as in jolt_encode.  Output: a record of
+ * shape (H, n_new, D) with the base's choice (jolt_blob_bytes of that shape),
+ * holding copies of U~_D and G~, which decodes (and attends) like any
+ * record.  x_new_dev [H][n_new][D] in base->dtype.  ws_bytes >=
+ * jolt_append_workspace_bytes.  Synchronizes `stream` once, at the end.
+ * Errors: EINVAL, ENOSPACE, EHIP. */
+size_t jolt_append_workspace_bytes(const jolt_shape* base, jolt_choice choice, int32_t n_new);
+jolt_status jolt_append(const jolt_shape* base, jolt_choice choice, const void* base_blob, size_t base_bytes,
+                        const void* x_new_dev, int32_t n_new, const void* rot_dev, uint64_t seed,
+                        void* blob_dev, size_t blob_bytes, void* ws_dev, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------ decode fused into attention */
 

@@ -81,6 +81,9 @@ SIGNATURES = {
     "jolt_decode_many": (C.c_int, [C.c_int32, C.POINTER(Shape), C.POINTER(Choice), C.POINTER(C.c_void_p),
                                    C.POINTER(C.c_size_t), C.c_void_p, C.POINTER(C.c_void_p), C.c_void_p,
                                    C.c_size_t, C.c_void_p]),
+    "jolt_append_workspace_bytes": (C.c_size_t, [C.POINTER(Shape), Choice, C.c_int32]),
+    "jolt_append": (C.c_int, [C.POINTER(Shape), Choice, C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32, C.c_void_p,
+                              C.c_uint64, C.c_void_p, C.c_size_t, C.c_void_p, C.c_size_t, C.c_void_p]),
     "jolt_attend_workspace_bytes": (C.c_size_t, [C.POINTER(Shape), Choice, Choice, C.c_int32, C.c_int32]),
     "jolt_attend": (C.c_int, [C.POINTER(Shape), Choice, C.c_void_p, C.c_size_t, Choice, C.c_void_p, C.c_size_t,
                               C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t,

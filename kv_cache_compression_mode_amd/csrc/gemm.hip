@@ -875,6 +875,48 @@ hipError_t launch_pad_copy(const float* in, int64_t n, int64_t in_batch, float* 
   return hipGetLastError();
 }
 
+// inv[i] = 1 / lam[i] when lam[i] > rel * max_j lam[j], else 0 (one workgroup).
+__global__ __launch_bounds__(256) void k_pinv_scale(const double* lam, int64_t n, double rel, float* inv) {
+  __shared__ double red[256];
+  double m = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 256) m = fmax(m, lam[i]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + o]);
+    __syncthreads();
+  }
+  const double thr = rel * red[0];
+  for (int64_t i = threadIdx.x; i < n; i += 256) inv[i] = lam[i] > thr ? static_cast<float>(1.0 / lam[i]) : 0.f;
+}
+
+// M[j][j] = max_{i < n} M[i][i] for n <= j < np (M: np x np, row stride np,
+// zero outside the leading n x n block): the padding becomes a block of
+// eigenvalues at the top of the spectrum, away from the leading block's.
+__global__ __launch_bounds__(256) void k_pad_diag(float* M, int64_t n, int64_t np) {
+  __shared__ float red[256];
+  float m = 0.f;
+  for (int64_t i = threadIdx.x; i < n; i += 256) m = fmaxf(m, M[i * np + i]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
+    __syncthreads();
+  }
+  for (int64_t j = n + threadIdx.x; j < np; j += 256) M[j * np + j] = red[0];
+}
+
+hipError_t launch_pad_diag(float* M, int64_t n, int64_t np, hipStream_t s) {
+  if (np <= n) return hipSuccess;
+  k_pad_diag<<<1, 256, 0, s>>>(M, n, np);
+  return hipGetLastError();
+}
+
+hipError_t launch_pinv_scale(const double* lam, int64_t n, double rel, float* inv, hipStream_t s) {
+  k_pinv_scale<<<1, 256, 0, s>>>(lam, n, rel, inv);
+  return hipGetLastError();
+}
+
 hipError_t launch_sum_batch(const float* in, int64_t count, int n, float* out, hipStream_t s) {
   if (count <= 0) return hipSuccess;
   k_sum_batch<<<grid1(count), 256, 0, s>>>(in, count, n, out);

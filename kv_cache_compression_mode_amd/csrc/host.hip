@@ -198,11 +198,13 @@ RecordHead record_head(int64_t H, int64_t T, int64_t D, int32_t dtype, jolt_choi
 bool shape_ok(const jolt_shape* s) {
   return s && s->H >= 1 && s->T >= 1 && s->D == kD && (s->dtype == JOLT_BF16 || s->dtype == JOLT_F32);
 }
+// r_T is bounded by H D (the token factor's columns span at most the H D
+// columns of the token unfolding); a record may hold fewer tokens than r_T
+// (tokens appended to an encoded tensor keep its choice).
 bool choice_ok(const jolt_shape* s, jolt_choice c) {
   if (c.bits < 1 || c.bits > 4) return false;
   if (c.r_T == 0 && c.r_D == 0) return true;
-  const int64_t nT = std::min<int64_t>(s->T, static_cast<int64_t>(s->H) * s->D);
-  return c.r_T >= 1 && c.r_T <= nT && c.r_D >= 1 && c.r_D <= s->D;
+  return c.r_T >= 1 && c.r_T <= static_cast<int64_t>(s->H) * s->D && c.r_D >= 1 && c.r_D <= s->D;
 }
 
 // ---------------------------------------------------------- the dual
@@ -1603,6 +1605,148 @@ jolt_status jolt_xl_decode(int32_t n, const jolt_shape* shape, int32_t r, const 
       ck(launch_gemm(g, 1, s));
     }
     return JOLT_OK;
+  });
+}
+
+// -------------------------------------------------- appended tokens (fold-in)
+// Workspace: W fp32 [r_T][H D], M = W W^T (padded to rp = ceil32(r_T)), its
+// eigenvectors Z [rp][rp] (column-major), eigenvalues fp64, pseudo-inverse
+// scales fp32, B = X_new W^T and P = B Z diag(1/lambda) [dT][rp], U_new fp32
+// [dT][r_T], the eigensolver's scratch, the encoder's W parts, status.
+struct AppendLayout {
+  size_t W, M, Z, lam, inv, B, P, U, syev, W3, status, total;
+  int64_t rp;
+};
+AppendLayout append_layout(const jolt_shape* sh, int32_t dT, jolt_choice c) {
+  AppendLayout L{};
+  const int64_t HD = static_cast<int64_t>(sh->H) * sh->D;
+  L.rp = (static_cast<int64_t>(c.r_T) + 31) / 32 * 32;
+  size_t off = 0;
+  L.W = off; off += a256(4ull * c.r_T * HD);
+  L.M = off; off += a256(4ull * L.rp * L.rp);
+  L.Z = off; off += a256(4ull * L.rp * L.rp);
+  L.lam = off; off += a256(8ull * L.rp);
+  L.inv = off; off += a256(4ull * L.rp);
+  L.B = off; off += a256(4ull * dT * L.rp);
+  L.P = off; off += a256(4ull * dT * L.rp);
+  L.U = off; off += a256(4ull * dT * c.r_T);
+  L.syev = off; off += a256(syev_top_work_bytes(L.rp, static_cast<int>(L.rp), 1));
+  L.W3 = off; off += a256(6ull * sh->H * sh->D * enc_rtp(c.r_T));
+  L.status = off; off += 256;
+  L.total = off;
+  return L;
+}
+
+size_t jolt_append_workspace_bytes(const jolt_shape* base, jolt_choice choice, int32_t n_new) {
+  if (!shape_ok(base) || !choice_ok(base, choice) || choice.r_T < 1 || n_new < 1) return 0;
+  return append_layout(base, n_new, choice).total;
+}
+
+jolt_status jolt_append(const jolt_shape* base, jolt_choice choice, const void* base_blob, size_t base_bytes,
+                        const void* x_new_dev, int32_t n_new, const void* rot_dev, uint64_t seed, void* blob_dev,
+                        size_t blob_bytes, void* ws_dev, size_t ws_bytes, void* stream) {
+  if (!shape_ok(base) || !choice_ok(base, choice) || choice.r_T < 1 || n_new < 1) return JOLT_EINVAL;
+  if (!base_blob || !x_new_dev || !rot_dev || !blob_dev || !ws_dev) return JOLT_EINVAL;
+  const int64_t H = base->H, T = base->T, D = base->D, HD = H * D, dT = n_new;
+  const int64_t rT = choice.r_T, rD = choice.r_D;
+  const BlobLayout B0 = blob_layout(H, T, D, choice), B1 = blob_layout(H, dT, D, choice);
+  if (base_bytes < B0.total || blob_bytes < B1.total) return JOLT_ENOSPACE;
+  const AppendLayout L = append_layout(base, n_new, choice);
+  if (ws_bytes < L.total) return JOLT_ENOSPACE;
+  return guard([&]() -> jolt_status {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int xdt = base->dtype == JOLT_BF16 ? kBF16 : kF32;
+    char* ws = static_cast<char*>(ws_dev);
+    const char* b0 = static_cast<const char*>(base_blob);
+    char* b1 = static_cast<char*>(blob_dev);
+    float* W = reinterpret_cast<float*>(ws + L.W);
+    float* M = reinterpret_cast<float*>(ws + L.M);
+    float* Z = reinterpret_cast<float*>(ws + L.Z);
+    double* lam = reinterpret_cast<double*>(ws + L.lam);
+    float* inv = reinterpret_cast<float*>(ws + L.inv);
+    float* Bm = reinterpret_cast<float*>(ws + L.B);
+    float* P = reinterpret_cast<float*>(ws + L.P);
+    float* U = reinterpret_cast<float*>(ws + L.U);
+    int* status = reinterpret_cast<int*>(ws + L.status);
+    const int64_t rp = L.rp;
+    uint16_t* Ut1 = reinterpret_cast<uint16_t*>(b1 + B1.ut);
+    uint16_t* Ud1 = reinterpret_cast<uint16_t*>(b1 + B1.ud);
+    uint16_t* G1 = reinterpret_cast<uint16_t*>(b1 + B1.g);
+    ck(hipMemsetAsync(status, 0, sizeof(int), s));
+    // the new record keeps the base's stored U~_D and G~
+    ck(hipMemcpyAsync(Ud1, b0 + B0.ud, 2ull * D * rD, hipMemcpyDeviceToDevice, s));
+    ck(hipMemcpyAsync(G1, b0 + B0.g, 2ull * H * rT * rD, hipMemcpyDeviceToDevice, s));
+    {                                         // W[:, h D ..] = G~_h U~_D^T  (r_T x D per head)
+      GemmArgs g = gemm0();
+      g.M = rT; g.N = D; g.K = rD;
+      g.A = G1; g.a_dtype = kBF16; g.am = plain(rD); g.ak = plain(1); g.a_batch = rT * rD;
+      g.B = Ud1; g.b_dtype = kBF16; g.bk = plain(1); g.bn = plain(rD); g.b_batch = 0;
+      g.C = W; g.c_m = HD; g.c_n = 1; g.c_batch = D;
+      ck(launch_gemm(g, static_cast<int>(H), s));
+    }
+    ck(hipMemsetAsync(M, 0, 4ull * rp * rp, s));
+    {                                         // M = W W^T (r_T x r_T inside rp x rp zeros)
+      GemmArgs g = gemm0();
+      g.M = rT; g.N = rT; g.K = HD;
+      g.A = W; g.am = plain(HD); g.ak = plain(1);
+      g.B = W; g.bk = plain(1); g.bn = plain(HD);
+      g.C = M; g.c_m = rp; g.c_n = 1;
+      ck(launch_gemm(g, 1, s));
+    }
+    {                                         // B = X_new,(T) W^T  (dT x r_T, row stride rp)
+      GemmArgs g = gemm0();
+      g.M = dT; g.N = rT; g.K = HD;
+      g.A = x_new_dev; g.a_dtype = xdt; g.am = plain(D); g.ak = segmented(D, dT * D, 1);
+      g.B = W; g.bk = plain(1); g.bn = plain(HD);
+      g.C = Bm; g.c_m = rp; g.c_n = 1;
+      ck(launch_gemm(g, 1, s));
+    }
+    // M = Z diag(lambda) Z^T, its padding to rp a diagonal block at the top
+    // of the spectrum (B has zeros there, so it adds nothing); 1/lambda,
+    // guarding only non-positive eigenvalues: the normal equations in fp32
+    // resolve the smallest eigenvalues of these systems (a few 1e-6 of the
+    // largest) to well under 1%, and the error each direction adds scales
+    // with the new tokens' small projection on it
+    ck(launch_pad_diag(M, rT, rp, s));
+    ck(syev_top(M, rp, 1, static_cast<int>(rp), Z, lam, ws + L.syev, s, status));
+    ck(launch_pinv_scale(lam, rp, 0x1p-40, inv, s));
+    {                                         // P = B Z diag(inv)
+      GemmArgs g = gemm0();
+      g.M = dT; g.N = rp; g.K = rT;
+      g.A = Bm; g.am = plain(rp); g.ak = plain(1);
+      g.B = Z; g.bk = plain(1); g.bn = plain(rp);
+      g.col_scale = inv;
+      g.C = P; g.c_m = rp; g.c_n = 1;
+      ck(launch_gemm(g, 1, s));
+    }
+    {                                         // U_new = P Z^T restricted to r_T columns
+      GemmArgs g = gemm0();
+      g.M = dT; g.N = rT; g.K = rp;
+      g.A = P; g.am = plain(rp); g.ak = plain(1);
+      g.B = Z; g.bk = plain(rp); g.bn = plain(1);
+      g.C = U; g.c_m = rT; g.c_n = 1;
+      ck(launch_gemm(g, 1, s));
+    }
+    ck(launch_to_bf16(U, rT, Ut1, dT, rT, s));
+    // the residual against the stored parts, rotated and quantized
+    const int64_t rTp = enc_rtp(choice.r_T);
+    uint16_t* W3 = reinterpret_cast<uint16_t*>(ws + L.W3);
+    ck(launch_enc_w(nullptr, nullptr, G1, Ud1, W3, 0, 1, static_cast<int>(H), static_cast<int>(rT),
+                    static_cast<int>(rD), static_cast<int>(rTp), s));
+    const size_t n = static_cast<size_t>(D) * D;
+    EncodeArgs ea{};
+    ea.X = x_new_dev; ea.x_dtype = xdt; ea.H = H; ea.T = dT;
+    ea.Ut = Ut1; ea.W3 = W3; ea.r_T = rT; ea.r_Tp = rTp;
+    ea.Q3 = reinterpret_cast<const uint16_t*>(static_cast<const char*>(rot_dev) + 2 * a256(4 * n) + a256(2 * n));
+    ea.bits = choice.bits;
+    ea.scales = reinterpret_cast<uint16_t*>(b1 + B1.sc);
+    ea.codes = reinterpret_cast<uint8_t*>(b1 + B1.cd);
+    ck(launch_encode_residual(ea, s));
+    ck(launch_write_header(b1, record_head(H, dT, D, base->dtype, choice, seed), s));
+    int st = 0;
+    ck(hipMemcpyAsync(&st, status, sizeof(int), hipMemcpyDeviceToHost, s));
+    ck(hipStreamSynchronize(s));
+    return st != 0 ? JOLT_EHIP : JOLT_OK;
   });
 }
 

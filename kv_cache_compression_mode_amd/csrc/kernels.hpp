@@ -72,6 +72,11 @@ hipError_t launch_pad_copy(const float* in, int64_t n, int64_t in_batch, float* 
                            int batch, hipStream_t s);
 hipError_t launch_sum_diag_blocks(const float* C, int64_t H, int64_t D, float* GD, int batch,
                                   hipStream_t s);
+// The diagonal of M (np x np) past the leading n x n block set to the
+// block's largest diagonal entry.
+hipError_t launch_pad_diag(float* M, int64_t n, int64_t np, hipStream_t s);
+// inv[i] = 1 / lam[i] for lam[i] > rel * max(lam), else 0 (lam fp64 [n]).
+hipError_t launch_pinv_scale(const double* lam, int64_t n, double rel, float* inv, hipStream_t s);
 // out[i] = sum_{j < n} in[j * count + i], added in the order j = 0 .. n-1.
 hipError_t launch_sum_batch(const float* in, int64_t count, int n, float* out, hipStream_t s);
 

@@ -371,18 +371,22 @@ def decode_many_workspace_bytes(H: int, T: int, choices, dtype=torch.bfloat16) -
 
 
 def decode_many(blobs, H: int, T: int, choices, rot: torch.Tensor, outs, workspace: torch.Tensor,
-                dtype=torch.bfloat16) -> None:
-    """Reconstruct several records of one shape into the given output tensors."""
+                dtype=torch.bfloat16, validate: bool = True) -> None:
+    """Reconstruct several records of one shape into the given output tensors.
+    validate=False skips the per-buffer checks of this binding (for a caller
+    repeating a call whose buffers it has already checked once); the C ABI
+    still checks everything it can see."""
     n = len(blobs)
     _need(len(choices) == n and len(outs) == n, "one choice and one output per record")
     shape = make_shape(H, T, D_FEATURES, dtype)
     ch = (Choice * n)(*[Choice(*c) for c in choices])
     dev = workspace.device
-    _check_buf(workspace, dev, "workspace", lib().jolt_decode_many_workspace_bytes(n, C.byref(shape), ch))
-    _check_buf(rot, dev, "rot", lib().jolt_rotation_bytes(D_FEATURES))
-    for i, nb in enumerate(_blob_sizes(shape, choices)):
-        _check_buf(blobs[i], dev, f"blobs[{i}]", nb)
-        _check_out(outs[i], dev, H, T, dtype, f"outs[{i}]")
+    if validate:
+        _check_buf(workspace, dev, "workspace", lib().jolt_decode_many_workspace_bytes(n, C.byref(shape), ch))
+        _check_buf(rot, dev, "rot", lib().jolt_rotation_bytes(D_FEATURES))
+        for i, nb in enumerate(_blob_sizes(shape, choices)):
+            _check_buf(blobs[i], dev, f"blobs[{i}]", nb)
+            _check_out(outs[i], dev, H, T, dtype, f"outs[{i}]")
     bp = (C.c_void_p * n)(*[b.data_ptr() for b in blobs])
     bb = (C.c_size_t * n)(*[b.numel() for b in blobs])
     op = (C.c_void_p * n)(*[o.data_ptr() for o in outs])
@@ -409,6 +413,35 @@ def decode_many_static(blobs, H: int, T: int, choices, rot: torch.Tensor, outs, 
     op = (C.c_void_p * n)(*[o.data_ptr() for o in outs])
     check(lib().jolt_decode_many_static(n, C.byref(shape), ch, bp, bb, rot.data_ptr(), op, _stream(dev)),
           "jolt_decode_many_static")
+
+
+def append(base_blob: torch.Tensor, H: int, T: int, choice, x_new: torch.Tensor, rot: torch.Tensor, seed: int = 0,
+           out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Record of tokens appended to an encoded tensor (folding-in against the
+    base record's stored factors); x_new [H, n_new, 128] in the base's dtype."""
+    _need(x_new.dim() == 3 and x_new.shape[0] == H and x_new.shape[2] == D_FEATURES,
+          f"x_new must be [{H}, n_new, {D_FEATURES}]")
+    dev = x_new.device
+    _check_buf(x_new, dev, "x_new")
+    n_new = x_new.shape[1]
+    base = make_shape(H, T, D_FEATURES, x_new.dtype)
+    ch = Choice(*choice)
+    _check_buf(base_blob, dev, "base_blob", lib().jolt_blob_bytes(C.byref(base), ch))
+    _check_buf(rot, dev, "rot", lib().jolt_rotation_bytes(D_FEATURES))
+    nb = lib().jolt_blob_bytes(C.byref(make_shape(H, n_new, D_FEATURES, x_new.dtype)), ch)
+    nws = lib().jolt_append_workspace_bytes(C.byref(base), ch, n_new)
+    if nb == 0 or nws == 0:
+        check(_lib.JOLT_EINVAL, "jolt_append_workspace_bytes")
+    if out is not None:
+        _check_buf(out, dev, "out", nb)
+    if workspace is not None:
+        _check_buf(workspace, dev, "workspace", nws)
+    blob = out if out is not None else torch.empty(nb, dtype=torch.uint8, device=dev)
+    ws = workspace if workspace is not None else torch.empty(nws, dtype=torch.uint8, device=dev)
+    check(lib().jolt_append(C.byref(base), ch, base_blob.data_ptr(), base_blob.numel(), x_new.data_ptr(), n_new,
+                            rot.data_ptr(), seed, blob.data_ptr(), blob.numel(), ws.data_ptr(), ws.numel(),
+                            _stream(dev)), "jolt_append")
+    return blob
 
 
 def attend_workspace_bytes(H: int, T: int, choice_k, choice_v, G: int, n_new: int,
