@@ -204,6 +204,7 @@ def main():
         jolt.profile_enable(None)
     del qy
     attn = attend_leg(jolt, cfg, state, rot, dev, tdt, args.profile_step)
+    appended = append_leg(jolt, cfg, state, xs, rot, dev, tdt) if not args.profile_step else None
     if args.profile_step:
         # a plain copy of known size (read n bytes, write n bytes), against
         # which the FETCH_SIZE / WRITE_SIZE counters are scaled
@@ -275,6 +276,7 @@ def main():
         "roofline_gram": (roofline_for("gram", tstats["gram"], cfg.name)
                           if tstats.get("gram", {}).get("launches") else None),
         "attend": attn,
+        "append": appended,
         "roofline_decode": {"kernel": dec_kernel,
                             "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
                             "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
@@ -548,6 +550,45 @@ def attend_leg(jolt, cfg, state, rot, dev, tdt, quiet):
     if st and st["launches"]:
         line["roofline"] = roofline_for("attend", st, cfg.name)
     return line
+
+
+def append_leg(jolt, cfg, state, xs, rot, dev, tdt, n_new=256):
+    """Incremental encode: n_new tokens appended to every tensor of the
+    encoded cache (folding-in against the record's stored factors; a tensor
+    with no Tucker part gets the new tokens quantized alone).  The appended
+    tokens are synthetic rows of the same source: the first n_new tokens of
+    each tensor, rolled by one row, stand in for tokens that arrive later."""
+    import torch
+    L, H, T, D = cfg.n_layers, cfg.H, cfg.T, cfg.D
+    blobs, choices = state["blobs"], state["choices"]
+    news = [torch.roll(xs[i // 2][i % 2][:, :n_new + 1], 1, dims=1)[:, 1:].contiguous() for i in range(2 * L)]
+    outs = [torch.empty(jolt.blob_bytes(H, n_new, D, choices[i], tdt), dtype=torch.uint8, device=dev)
+            for i in range(2 * L)]
+    need = [jolt.append_workspace_bytes(H, T, choices[i], n_new, tdt) for i in range(2 * L) if choices[i][0] > 0]
+    ws = torch.empty(max(need + [1]), dtype=torch.uint8, device=dev)
+
+    def run():
+        for i in range(2 * L):
+            if choices[i][0] > 0:
+                jolt.append(blobs[i], H, T, choices[i], news[i], rot, out=outs[i], workspace=ws)
+            else:
+                jolt.encode(news[i], choices[i], None, None, rot, out=outs[i])
+
+    run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3
+    errs = {0: [], 1: []}
+    for i in range(2 * L):
+        o = jolt.decode(outs[i], H, n_new, choices[i], rot, dtype=tdt)
+        x = news[i].double()
+        errs[i % 2].append(float(torch.linalg.vector_norm(x - o.double()) / torch.linalg.vector_norm(x)))
+    return {"workload": f"{n_new} tokens appended to each of the cache's {2 * L} tensors",
+            "ms_per_cache": round(ms, 3), "tokens_per_s": round(n_new / (ms * 1e-3), 1),
+            "rel_err_K_mean": round(sum(errs[0]) / len(errs[0]), 6),
+            "rel_err_V_mean": round(sum(errs[1]) / len(errs[1]), 6)}
 
 
 SWEEP_RATIOS = (2.0, 2.25, 2.5, 2.75, 3.0)

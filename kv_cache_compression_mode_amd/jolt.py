@@ -415,6 +415,10 @@ def decode_many_static(blobs, H: int, T: int, choices, rot: torch.Tensor, outs, 
           "jolt_decode_many_static")
 
 
+def append_workspace_bytes(H: int, T: int, choice, n_new: int, dtype=torch.bfloat16) -> int:
+    return lib().jolt_append_workspace_bytes(C.byref(make_shape(H, T, D_FEATURES, dtype)), Choice(*choice), n_new)
+
+
 def append(base_blob: torch.Tensor, H: int, T: int, choice, x_new: torch.Tensor, rot: torch.Tensor, seed: int = 0,
            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Record of tokens appended to an encoded tensor (folding-in against the
