@@ -1,8 +1,9 @@
 // Residual, rotation, group quantization and decode kernels (D = 128).
 //
 // JoLT abstract (arXiv 2607.12550v2), method sentence: after the partial
-// Tucker truncation the residual is restored by "a random orthogonal rotation
-// followed by low-bit quantization"; news article paragraph 4: the rotation
+// Tucker truncation, the energy it drops is restored by the residual, rotated
+// by a random orthogonal matrix and then quantized to few bits; news article
+// paragraph 4: the rotation
 // whitens the residual so the quantization error is close to independent and
 // uniform.  Groups are 32 consecutive rotated features of one (head, token)
 // row; each group stores a bf16 offset (min rounded toward -inf) and a bf16

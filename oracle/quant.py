@@ -2,9 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
 
-Source: JoLT abstract (arXiv 2607.12550v2), method sentence ("a random
-orthogonal rotation followed by low-bit quantization"); news article
-paragraph 4 (the rotation makes the quantization error close to independent
+Source: JoLT abstract (arXiv 2607.12550v2), the method sentence (the
+residual is rotated by a random orthogonal matrix, then quantized to few
+bits); news article paragraph 4 (the rotation makes the quantization error close to independent
 and uniform).  Bit-widths b in {1, 2, 3, 4}, groups of 32.
 
 Readings (the pages give no quantizer):

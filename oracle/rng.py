@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
 
-The pages call for "a random orthogonal rotation" (JoLT abstract, the sentence
+The pages call for a random orthogonal rotation (JoLT abstract, the sentence
 introducing the method) and a randomized SVD (abstract, FlashJoLT sentence) but
 fix no generator.  Reading: both sides implement the same published
 counter-based generator independently, so a draw is a pure function of

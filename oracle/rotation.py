@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
 
 Source: JoLT abstract (arXiv 2607.12550v2), the method sentence: the residual
-is "rotated" by a random orthogonal matrix before low-bit quantization; news
+is rotated by a random orthogonal matrix before low-bit quantization; news
 article paragraphs 2 and 4 call it a Johnson-Lindenstrauss rotation that
 whitens the residual.
 
