@@ -149,7 +149,6 @@ __device__ __forceinline__ void reconstruct(const DecRec& R, int64_t h, int64_t 
   }
   // the dequantized, rotated-back residual: + Y^ Q (K = 128 features)
   const int bits = R.bits;
-  const uint32_t qmask = (1u << bits) - 1u;
   for (int d0 = 0; d0 < D; d0 += 16) {
     const int dd = d0 + 8 * half;               // this lane's 8 features
     const int g = dd >> 5, bitpos = (dd & 31) * bits;
@@ -165,14 +164,7 @@ __device__ __forceinline__ void reconstruct(const DecRec& R, int64_t h, int64_t 
         w0 = ldg32(cw + (bitpos >> 5));
         if ((bitpos & 31) + 8 * bits > 32) w1 = ldg32(cw + (bitpos >> 5) + 1);
       }
-      const float m16 = bf16_bits_to_f32(static_cast<uint16_t>(sw & 0xffffu));
-      const float s16 = bf16_bits_to_f32(static_cast<uint16_t>(sw >> 16));
-      const uint64_t stream = (static_cast<uint64_t>(w0) | (static_cast<uint64_t>(w1) << 32)) >> (bitpos & 31);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t qc = static_cast<uint32_t>(stream >> (i * bits)) & qmask;
-        y[rt][i] = static_cast<__bf16>(fmaf(static_cast<float>(qc), s16, m16));
-      }
+      y[rt] = dequant8<bf16x8>(sw, w0, w1, static_cast<uint32_t>(bitpos & 31), static_cast<uint32_t>(bits));
     }
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {

@@ -633,7 +633,6 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
     __syncthreads();
   }
   const int bits = R.bits;
-  const uint32_t qmask = (1u << bits) - 1u;
   // the streamed words of one d step (scales, code words), the next step's
   // loaded during this one's dequantization and MFMAs (Q^T from LDS)
   uint32_t sw[2], w0[2], w1[2];
@@ -664,17 +663,9 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
     if (d0 + 16 < D) load_d(d0 + 16);
     bf16x8 y[2];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const float m16 = bf16_bits_to_f32(static_cast<uint16_t>(csw[rt] & 0xffffu));
-      const float s16 = bf16_bits_to_f32(static_cast<uint16_t>(csw[rt] >> 16));
-      const uint64_t stream = (static_cast<uint64_t>(cw0[rt]) | (static_cast<uint64_t>(cw1[rt]) << 32)) >>
-                              (bitpos & 31);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t q = static_cast<uint32_t>(stream >> (i * bits)) & qmask;
-        y[rt][i] = static_cast<__bf16>(fmaf(static_cast<float>(q), s16, m16));
-      }
-    }
+    for (int rt = 0; rt < 2; ++rt)
+      y[rt] = dequant8<bf16x8>(csw[rt], cw0[rt], cw1[rt], static_cast<uint32_t>(bitpos & 31),
+                               static_cast<uint32_t>(bits));
     // rows past T: scale word 0 gives m16 = s16 = 0, so y = 0
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -698,7 +689,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int c = 32 * ct + 8 * (i >> 2) + 4 * half + (i & 3);
-          if constexpr (sizeof(TO) == 2) orow[c] = f32_to_bf16_rne(acc[rt][ct][i]);
+          if constexpr (sizeof(TO) == 2) orow[c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[rt][ct][i]));
           else orow[c] = acc[rt][ct][i];
         }
       continue;
@@ -716,8 +707,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
 #pragma unroll
             for (int w = 0; w < 2; ++w) {
               const int i = (2 * j + g) * 4 + 2 * w;
-              p[g][w] = static_cast<uint32_t>(f32_to_bf16_rne(acc[rt][ct][i])) |
-                        (static_cast<uint32_t>(f32_to_bf16_rne(acc[rt][ct][i + 1])) << 16);
+              p[g][w] = pack_bf16x2(acc[rt][ct][i], acc[rt][ct][i + 1]);
             }
           const auto s0 = __builtin_amdgcn_permlane32_swap(p[0][0], p[1][0], false, false);
           const auto s1 = __builtin_amdgcn_permlane32_swap(p[0][1], p[1][1], false, false);

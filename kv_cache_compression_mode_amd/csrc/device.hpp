@@ -24,6 +24,31 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Two fp32 values as a packed bf16 pair (lo in the low half), round to
+// nearest even: one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// The 8 dequantized values y = m16 + q * s16 (fp32 fma, then bf16 nearest
+// even) of one lane's 8 consecutive codes: the group's scale word sw
+// (offset | step << 16), the code words w0 (and w1 when the 8 b-bit codes
+// cross a word) holding them from bit sh on.  One funnel shift, then one
+// bit-field extract per code.
+template <typename V8>
+__device__ __forceinline__ V8 dequant8(uint32_t sw, uint32_t w0, uint32_t w1, uint32_t sh, uint32_t bits) {
+  const float m16 = __uint_as_float(sw << 16);
+  const float s16 = __uint_as_float(sw & 0xffff0000u);
+  const uint32_t w = __builtin_amdgcn_alignbit(w1, w0, sh);
+  V8 y;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    y[i] = static_cast<__bf16>(fmaf(static_cast<float>(__builtin_amdgcn_ubfe(w, i * bits, bits)), s16, m16));
+  return y;
+}
+
 // Largest bf16 <= f: truncation rounds toward zero, so a negative inexact
 // value takes one more unit of magnitude.
 __device__ __forceinline__ uint16_t bf16_round_down(float f) {
