@@ -318,7 +318,7 @@ COMPARE_EXACT = {"mistral7b_t1024_flash"}
 CPU_SAMPLE = {"mistral7b_t4096_2x": 24, "mistral7b_t1024_flash": 64, "llama13b_t4096_2x": 2,
               "mistral7b_t32768_3x": 4}
 
-KERNELS = ("qr_panel", "qr_update", "gemm", "gemm_bf16", "gram", "band", "chase", "tri_eig", "chase_back",
+KERNELS = ("qr_panel", "qr_update", "cholqr", "cholqr_gemm", "gemm", "gemm_bf16", "gram", "band", "chase", "tri_eig", "chase_back",
            "band_back", "encode_w", "encode_residual", "quantize", "decode_w", "decode", "attend")
 # kernels with roofline targets, timed inside the timed steps
 TIMED_ROOF = ("gram", "encode_residual", "decode")

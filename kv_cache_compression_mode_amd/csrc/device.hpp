@@ -112,6 +112,13 @@ __device__ __forceinline__ void xcd_group_2d(uint32_t& x, uint32_t& y) {
   xcd_group(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x, gridDim.y, y, x);
 }
 
+// orders one wave's LDS accesses (LDS executes a wave's operations in order)
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // v(lane l) + v(lane l ^ 32), the same value in both halves of the wave: one
 // lane swap of the halves (v_permlane32_swap, gfx950) instead of a trip
 // through LDS.  Both halves add the lower half's value to the upper half's.

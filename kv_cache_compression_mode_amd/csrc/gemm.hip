@@ -305,15 +305,22 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
 //   kOpF32K  fp32, k contiguous: split into bf16 planes hi = rne(x),
 //            lo = rne(x - hi), so x = hi + lo to 2^-17 relative; the product
 //            takes hi B + lo B (or A hi + A lo): exact bf16 products summed in
-//            fp32, ~2^-17 relative error per term (fp32 operands: 2^-24).
+//            fp32, ~2^-17 relative error per term (fp32 operands: 2^-24);
+//   kOpF32M  fp32, rows contiguous: 16-byte loads of four rows at one k,
+//            split the same way and transposed in registers (four rows by
+//            four k per thread) on the way to LDS.
+// Both operands fp32 (split_f32): all four products hi hi + lo hi + hi lo +
+// lo lo (lo is about 2^-8 of x, so lo lo is a 2^-16 term, and one of a
+// fixed sign in a Gram's diagonal: it is kept).
 // The next K tile's global loads are issued before the current tile's MFMAs.
 constexpr int XT = 128, XK = 64, XKP = XK + 8;
-enum { kOpBfK = 0, kOpBfM = 1, kOpF32K = 2 };
+enum { kOpBfK = 0, kOpBfM = 1, kOpF32K = 2, kOpF32M = 3 };
 
 __device__ __forceinline__ int xswz(int row, int chunk) { return chunk ^ ((row >> 3) & 7); }
 
 template <int MODE> struct XRegs { uint4 v[4]; };
 template <> struct XRegs<kOpF32K> { float4 v[8]; };
+template <> struct XRegs<kOpF32M> { float4 v[8]; };
 
 // One operand's addressing: a buffer resource on its batch entry, this
 // thread's byte offsets (rows and in-tile k; kXOut for rows past the end,
@@ -342,6 +349,15 @@ __device__ __forceinline__ void x_addr(XAddr& a, const char* base, const GemmDim
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       a.vo[i] = r < rows ? static_cast<uint32_t>(2 * (rb + (4 * (tid >> 4) + i) * kd.stride)) : kXOut;
+  } else if constexpr (MODE == kOpF32M) {
+    // rows 4 (tid % 32) .. + 3 (rows is a multiple of 4), k = 4 (tid / 32) + 32 h + j, load 4 h + j
+    const int64_t r = r0 + 4 * (tid & 31);
+    const int64_t rb = dim_off(rd, r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t k = 4 * (tid >> 5) + 32 * (i >> 2) + (i & 3);
+      a.vo[i] = r < rows ? static_cast<uint32_t>(4 * (rb + k * kd.stride)) : kXOut;
+    }
   } else {
     constexpr int NR = MODE == kOpBfK ? 4 : 8, SH = MODE == kOpBfK ? 3 : 4;
     constexpr int64_t E = MODE == kOpBfK ? 2 : 4;
@@ -361,9 +377,9 @@ __device__ __forceinline__ void x_next(XAddr& a, const GemmDim& kd) {
 
 template <int MODE>
 __device__ __forceinline__ void x_load(XRegs<MODE>& R, const XAddr& a, const GemmDim& kd) {
-  constexpr int64_t E = MODE == kOpF32K ? 4 : 2;
+  constexpr int64_t E = MODE == kOpF32K || MODE == kOpF32M ? 4 : 2;
   const int so = static_cast<int>(E * x_koff(kd, a));
-  if constexpr (MODE == kOpF32K) {
+  if constexpr (MODE == kOpF32K || MODE == kOpF32M) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(a.rs, static_cast<int>(a.vo[i]), so, 0);
@@ -388,9 +404,19 @@ __device__ __forceinline__ void x_split(float x, uint32_t& hi, uint32_t& lo) {
   hi = h;
   lo = f32_to_bf16_rne(x - bf16_bits_to_f32(h));
 }
+// three planes: x = hi + mid + lo to 2^-24 relative (the fp32 significand)
+__device__ __forceinline__ void x_split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint16_t h = f32_to_bf16_rne(x);
+  const float r = x - bf16_bits_to_f32(h);
+  const uint16_t m = f32_to_bf16_rne(r);
+  hi = h;
+  mid = m;
+  lo = f32_to_bf16_rne(r - bf16_bits_to_f32(m));
+}
 
-template <int MODE>
-__device__ __forceinline__ void x_store(const XRegs<MODE>& R, uint16_t (*Sh)[XKP], uint16_t (*Sl)[XKP], int tid) {
+template <int MODE, int NP = 2>
+__device__ __forceinline__ void x_store(const XRegs<MODE>& R, uint16_t (*Sh)[XKP], uint16_t (*Sl)[XKP],
+                                        uint16_t (*S3)[XKP], int tid) {
   if constexpr (MODE == kOpBfK) {
     const int kc = tid & 7;
 #pragma unroll
@@ -408,26 +434,56 @@ __device__ __forceinline__ void x_store(const XRegs<MODE>& R, uint16_t (*Sh)[XKP
       w.y = x_half(R.v[2], e) | (x_half(R.v[3], e) << 16);
       *reinterpret_cast<uint2*>(&Sh[row][xswz(row, kg >> 1) * 8 + (kg & 1) * 4]) = w;
     }
+  } else if constexpr (MODE == kOpF32M) {
+    const int rg = tid & 31, kq = tid >> 5;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kb = 4 * kq + 32 * h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 4 * rg + e;
+        uint32_t hh[4], ll[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 v = R.v[4 * h + j];
+          x_split(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w, hh[j], ll[j]);
+        }
+        const int col = xswz(row, kb >> 3) * 8 + (kb & 7);
+        *reinterpret_cast<uint2*>(&Sh[row][col]) = make_uint2(hh[0] | (hh[1] << 16), hh[2] | (hh[3] << 16));
+        *reinterpret_cast<uint2*>(&Sl[row][col]) = make_uint2(ll[0] | (ll[1] << 16), ll[2] | (ll[3] << 16));
+      }
+    }
   } else {
     const int kc4 = tid & 15;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = (tid >> 4) + 16 * i;
       uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-      x_split(R.v[i].x, h0, l0); x_split(R.v[i].y, h1, l1);
-      x_split(R.v[i].z, h2, l2); x_split(R.v[i].w, h3, l3);
       const int col = xswz(row, kc4 >> 1) * 8 + (kc4 & 1) * 4;
+      if constexpr (NP == 3) {
+        uint32_t t0, t1, t2, t3;
+        x_split3(R.v[i].x, h0, l0, t0); x_split3(R.v[i].y, h1, l1, t1);
+        x_split3(R.v[i].z, h2, l2, t2); x_split3(R.v[i].w, h3, l3, t3);
+        *reinterpret_cast<uint2*>(&S3[row][col]) = make_uint2(t0 | (t1 << 16), t2 | (t3 << 16));
+      } else {
+        x_split(R.v[i].x, h0, l0); x_split(R.v[i].y, h1, l1);
+        x_split(R.v[i].z, h2, l2); x_split(R.v[i].w, h3, l3);
+      }
       *reinterpret_cast<uint2*>(&Sh[row][col]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
       *reinterpret_cast<uint2*>(&Sl[row][col]) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
     }
   }
 }
 
-template <int AM, int BMODE>
+// NP = 3 (both operands fp32, k contiguous): three planes each, and the six
+// products down to 2^-16 (hi hi, mid hi, hi mid, mid mid, lo hi, hi lo),
+// fp32-grade products for sums whose rounding must not exceed fp32's.
+template <int AM, int BMODE, int NP = 2>
 __global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
-  constexpr bool AS = AM == kOpF32K, BS = BMODE == kOpF32K;
-  __shared__ __attribute__((aligned(16))) uint16_t As[AS ? 2 : 1][XT][XKP];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BS ? 2 : 1][XT][XKP];
+  constexpr bool AS = AM == kOpF32K || AM == kOpF32M, BS = BMODE == kOpF32K || BMODE == kOpF32M;
+  static_assert(NP == 2 || (AM == kOpF32K && BMODE == kOpF32K), "three planes: fp32 k-contiguous operands");
+  __shared__ __attribute__((aligned(16))) uint16_t As[AS ? NP : 1][XT][XKP];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BS ? NP : 1][XT][XKP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Workgroups are dispatched round-robin over the 8 XCDs by linear id; when
   // the batch dimension is a multiple of 8 the id is remapped so that every
@@ -449,7 +505,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
   const int64_t zz = bz;
   const int64_t z = zz / g.ksplit, kz = zz % g.ksplit;
   const int64_t kbeg = kz * g.kchunk;
-  const int64_t kend = (kbeg + g.kchunk < g.K) ? kbeg + g.kchunk : g.K;
+  int64_t kend = (kbeg + g.kchunk < g.K) ? kbeg + g.kchunk : g.K;
+  if (g.a_lower && m0 + XT < kend) kend = m0 + XT;
+  if (g.b_upper && n0 + XT < kend) kend = n0 + XT;
   const size_t ea = AS ? 4 : 2, eb = BS ? 4 : 2;
   const char* Ab = g.a_ptrs ? static_cast<const char*>(g.a_ptrs[z])
                             : static_cast<const char*>(g.A) + z * g.a_batch * static_cast<int64_t>(ea);
@@ -469,8 +527,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
     x_load<BMODE>(rb, pb, g.bk);
   }
   for (int64_t k0 = kbeg; k0 < kend; k0 += XK) {
-    x_store<AM>(ra, As[0], As[AS ? 1 : 0], tid);
-    x_store<BMODE>(rb, Bs[0], Bs[BS ? 1 : 0], tid);
+    x_store<AM, NP>(ra, As[0], As[AS ? 1 : 0], As[AS ? NP - 1 : 0], tid);
+    x_store<BMODE, NP>(rb, Bs[0], Bs[BS ? 1 : 0], Bs[BS ? NP - 1 : 0], tid);
     __syncthreads();
     if (k0 + XK < kend) {
       x_next(pa, g.ak);
@@ -497,6 +555,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
           if constexpr (AS) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], b[j], acc[i][j], 0, 0, 0);
           if constexpr (BS) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bl[j], acc[i][j], 0, 0, 0);
+          if constexpr (AS && BS)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bl[j], acc[i][j], 0, 0, 0);
+          if constexpr (NP == 3) {
+            const int ra_ = wm + 32 * i + r, rb_ = wn + 32 * j + r;
+            const bf16x8 a3 = *reinterpret_cast<const bf16x8*>(&As[NP - 1][ra_][xswz(ra_, ch) * 8]);
+            const bf16x8 b3 = *reinterpret_cast<const bf16x8*>(&Bs[NP - 1][rb_][xswz(rb_, ch) * 8]);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b3, acc[i][j], 0, 0, 0);
+          }
         }
     }
     if (g.seq_len > 0 && ((k0 + XK - kbeg) % g.seq_len == 0 || k0 + XK >= kend)) {
@@ -728,6 +795,9 @@ int x_mode(int dtype, const GemmDim& rd, const GemmDim& kd, int64_t rows, int64_
   if (dtype == kBF16 && rd.stride == 1 && within(rd, XT) && seg16(rd) && mult(rows, 8) && within(kd, XK) &&
       mult(kd.stride, q) && seg16(kd))
     return kOpBfM;
+  if (dtype == kF32 && rd.stride == 1 && within(rd, XT) && seg16(rd) && mult(rows, 4) && within(kd, XK) &&
+      mult(kd.stride, q) && seg16(kd))
+    return kOpF32M;
   return -1;
 }
 
@@ -735,7 +805,8 @@ template <int AM>
 void launch_x_b(const GemmArgs& g, int xb, dim3 grid, hipStream_t s) {
   if (xb == kOpBfK) k_gemm_x<AM, kOpBfK><<<grid, 256, 0, s>>>(g);
   else if (xb == kOpBfM) k_gemm_x<AM, kOpBfM><<<grid, 256, 0, s>>>(g);
-  else if constexpr (AM != kOpF32K) k_gemm_x<AM, kOpF32K><<<grid, 256, 0, s>>>(g);
+  else if (xb == kOpF32K) k_gemm_x<AM, kOpF32K><<<grid, 256, 0, s>>>(g);
+  else if constexpr (AM == kOpF32K) k_gemm_x<kOpF32K, kOpF32M><<<grid, 256, 0, s>>>(g);
 }
 
 }  // namespace
@@ -761,17 +832,23 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s, const char*
   // 128 x 128 bf16 matrix-core tiles when the operands allow 16-byte loads
   // (at least one of them bf16); a column-major C is produced as the
   // row-major C^T = B^T A^T so that its stores run along rows
-  if (!g.a_sym && g.K % XK == 0 && (g.a_dtype == kBF16 || g.b_dtype == kBF16)) {
+  if (!g.a_sym && g.K % XK == 0 && (g.a_dtype == kBF16 || g.b_dtype == kBF16 || g.split_f32)) {
     GemmArgs x = g;
     if (x.c_m == 1 && x.c_n != 1 && !x.col_scale) {
       std::swap(x.M, x.N); std::swap(x.A, x.B); std::swap(x.a_dtype, x.b_dtype);
       std::swap(x.am, x.bn); std::swap(x.ak, x.bk); std::swap(x.a_batch, x.b_batch);
       std::swap(x.a_ptrs, x.b_ptrs); std::swap(x.c_m, x.c_n);
+      std::swap(x.a_lower, x.b_upper);                 // B^T lower <=> B upper
       x.c_lower = -x.c_lower;                          // m >= n of C is m <= n of C^T
     }
     const int xa = x_mode(x.a_dtype, x.am, x.ak, x.M, x.K, x.a_ptrs != nullptr, x.ptr_align16 != 0, x.A, x.a_batch);
     const int xb = x_mode(x.b_dtype, x.bn, x.bk, x.N, x.K, x.b_ptrs != nullptr, x.ptr_align16 != 0, x.B, x.b_batch);
-    if (xa >= 0 && xb >= 0 && !(xa == kOpF32K && xb == kOpF32K)) {
+    // an fp32 operand pairs with bf16 only when it is k contiguous; two fp32
+    // operands (split_f32) need one of them k contiguous
+    const bool fa = xa == kOpF32K || xa == kOpF32M, fb = xb == kOpF32K || xb == kOpF32M;
+    const bool pair_ok = xa >= 0 && xb >= 0 && (fa && fb ? (xa == kOpF32K || xb == kOpF32K) && g.split_f32
+                                                         : xa != kOpF32M && xb != kOpF32M);
+    if (pair_ok) {
       x.kchunk = (x.K + x.ksplit - 1) / x.ksplit;
       x.kchunk = (x.kchunk + XK - 1) / XK * XK;
       x.seq_len = 0;
@@ -786,7 +863,9 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s, const char*
       account(name);
       if (xa == kOpBfK) launch_x_b<kOpBfK>(x, xb, grid, s);
       else if (xa == kOpBfM) launch_x_b<kOpBfM>(x, xb, grid, s);
-      else launch_x_b<kOpF32K>(x, xb, grid, s);
+      else if (xa == kOpF32K && xb == kOpF32K && x.split_f32 == 2) k_gemm_x<kOpF32K, kOpF32K, 3><<<grid, 256, 0, s>>>(x);
+      else if (xa == kOpF32K) launch_x_b<kOpF32K>(x, xb, grid, s);
+      else k_gemm_x<kOpF32M, kOpF32K><<<grid, 256, 0, s>>>(x);
       if (x.ksplit > 1) k_splitk_reduce<<<dim3(grid1(x.M * x.N), batch), 256, 0, s>>>(x);
       return hipGetLastError();
     }

@@ -416,6 +416,9 @@ struct AllocWS {
   float* Om; float* Y; float* Z; float* Bm; float* Wr; float* Wd;
   // the feature-mode factor's own scratch (it runs beside the token path)
   float* qtauD; double* lamDt; int* permD; float* sgnD;
+  // CholeskyQR: a second buffer of the token factor and of the feature factor, and their work
+  float* Ucm2; float* cq; float* Vr2; float* cqD;
+  bool householder;    // re-orthonormalize by Householder QR only (after a CholeskyQR breakdown)
   size_t bytes;
   int chunk;
   int nlanes;          // scratch sets, one per stream (chunks alternate between them)
@@ -466,6 +469,8 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base, AllocWS* lane1 = nullpt
   per += static_cast<size_t>(std::max(d.T, d.HD)) * std::max<int64_t>(d.R, 1) * 8 + (1 << 20);
   per += static_cast<size_t>(gram_d_ksplit(d)) * d.D * d.D * 4;
   per += syev_top_work_bytes(d.D, static_cast<int>(d.D), 1);
+  per += (static_cast<size_t>(d.T) * std::max<int64_t>(d.R, 1) + d.D * d.D) * 4 +
+         (cholesky_qr_work_floats(d.T, std::max<int64_t>(d.R, 1), 1) + cholesky_qr_work_floats(d.D, d.D, 1)) * 4;
   if (d.R > 0) per += syev_top_work_bytes(d.flash ? d.ell_pad : d.n_pad, static_cast<int>(d.R), 1);
   // up to 64 tensors (24 GiB of scratch) in flight.  Token eigenproblems of
   // n >= 2048 go in two lanes of half chunks: there the stages around the
@@ -519,6 +524,10 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base, AllocWS* lane1 = nullpt
     w.lamDt = c.take<double>(static_cast<size_t>(chunk) * d.D);
     w.permD = c.take<int>(static_cast<size_t>(chunk) * d.D);
     w.sgnD = c.take<float>(static_cast<size_t>(chunk) * d.D);
+    w.Ucm2 = c.take<float>(static_cast<size_t>(chunk) * d.T * R);
+    w.cq = c.take<float>(cholesky_qr_work_floats(d.T, R, chunk));
+    w.Vr2 = c.take<float>(static_cast<size_t>(chunk) * d.D * d.D);
+    w.cqD = c.take<float>(cholesky_qr_work_floats(d.D, d.D, chunk));
   };
   carve_scratch(w);
   if (nlanes > 1) {
@@ -633,12 +642,24 @@ struct FeatureFork {
   }
 };
 
+// Orthonormal columns spanning the leading columns of the nearly orthogonal
+// column-major U (m x k, ld m) in place, nested spans kept: two CholeskyQR
+// passes, or Householder QR where k is too wide for them or after one of them
+// broke down (w.householder).
+void orthonormalize(float* U, float* U2, int64_t m, int64_t k, int batch, float* hwork, float* cwork,
+                    const AllocWS& w, hipStream_t s) {
+  if (!w.householder && k <= cholesky_qr_max_k() && m >= k)
+    ck(cholesky_qr(U, U2, m, k, m, m * k, batch, cwork, w.status, s));
+  else
+    ck(householder_qr(U, m, k, m, m * k, batch, hwork, s));
+}
+
 // Feature-mode factor of `batch` tensors from their D x D Grams in w.GD.
 void feature_factor(const Dims& d, int batch, int t0, const AllocWS& w, hipStream_t s) {
   const int64_t D = d.D;
   ck(hipMemcpyAsync(w.GDc, w.GD, sizeof(float) * batch * D * D, hipMemcpyDeviceToDevice, s));
   ck(syev_top(w.GD, D, batch, static_cast<int>(D), w.Vr, nullptr, w.syevD, s, w.status));
-  ck(householder_qr(w.Vr, D, D, D, D * D, batch, w.qtauD, s));
+  orthonormalize(w.Vr, w.Vr2, D, D, batch, w.qtauD, w.cqD, w, s);
   // Rayleigh quotients diag(U^T G U): W = G U (column-major), then column dots
   GemmArgs g = gemm0();
   g.M = D; g.N = D; g.K = D;
@@ -719,7 +740,7 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   } else {
     ck(copy_cols(w.V, n, n * n, w.Ucm, T, T * R, T, R, batch, s));
   }
-  ck(householder_qr(w.Ucm, T, R, T, T * R, batch, w.qtau, s));
+  orthonormalize(w.Ucm, w.Ucm2, T, R, batch, w.qtau, w.cq, w, s);
   token_finalize(d, batch, t0, w, xdt, s);
   ff.join();
 }
@@ -802,7 +823,7 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     g.C = w.Ucm; g.c_m = 1; g.c_n = T; g.c_batch = T * R;
     ck(launch_gemm(g, batch, s));
   }
-  ck(householder_qr(w.Ucm, T, R, T, T * R, batch, w.qtau, s));
+  orthonormalize(w.Ucm, w.Ucm2, T, R, batch, w.qtau, w.cq, w, s);
   token_finalize(d, batch, t0, w, xdt, s);
   ff.join();
 }
@@ -1171,48 +1192,61 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, v
     ck(hipMemcpyAsync(w.xptrs, ptrs.data(), sizeof(void*) * nt, hipMemcpyHostToDevice, s));
     ck(hipMemcpyAsync(w.tags, tags.data(), sizeof(uint64_t) * nt, hipMemcpyHostToDevice, s));
     ck(hipStreamSynchronize(s));
-    // chunks alternate between the lanes: lane 0 on s, lane 1 on a second
-    // stream of this call, forked from s and joined back into it
-    CallHip hip;
-    hipStream_t ls = nullptr;
-    if (w.nlanes > 1 && nt > w.chunk) {
-      ls = hip.lease();
-      const hipEvent_t fork = hip.event();
-      ck(hipEventRecord(fork, s));
-      ck(hipStreamWaitEvent(ls, fork, 0));
-    }
-    // a chunk on the second lane starts once the previous chunk's band
-    // reduction is queued ahead of it, so that chunk's chase (one CU per
-    // tensor) runs beside this chunk's matrix-core stages
-    std::vector<hipEvent_t> marks;
-    if (ls)
-      for (int c = 0; c * w.chunk < nt; ++c) marks.push_back(hip.event());
-    for (int t0 = 0, c = 0; t0 < nt; t0 += w.chunk, ++c) {
-      const int batch = std::min(w.chunk, nt - t0);
-      const bool second = ls && (c & 1);
-      AllocWS wl = second ? w1 : w;
-      hipStream_t sl = second ? ls : s;
-      wl.xptrs = w.xptrs + t0;
-      wl.tags = w.tags + t0;
-      wl.band_done = ls ? marks[c] : nullptr;
-      if (ls && c > 0) ck(hipStreamWaitEvent(sl, marks[c - 1], 0));
-      ck(launch_sumsq(reinterpret_cast<const void* const*>(wl.xptrs), batch, N, xdt, w.frob2 + t0, sl));
-      if (d.flash) analyze_flash(d, batch, t0, wl, xdt, req->power_iters, req->seed, hip, sl);
-      else analyze_exact(d, batch, t0, wl, xdt, hip, sl);
-    }
-    if (ls) {
-      const hipEvent_t join = hip.event();
-      ck(hipEventRecord(join, ls));
-      ck(hipStreamWaitEvent(s, join, 0));
-    }
     const int R = static_cast<int>(d.R);
     std::vector<double> lt(static_cast<size_t>(nt) * std::max(R, 1)), ld(static_cast<size_t>(nt) * d.D), f2(nt);
-    if (R > 0) ck(hipMemcpyAsync(lt.data(), w.lamT, sizeof(double) * nt * R, hipMemcpyDeviceToHost, s));
-    ck(hipMemcpyAsync(ld.data(), w.lamD, sizeof(double) * nt * d.D, hipMemcpyDeviceToHost, s));
-    ck(hipMemcpyAsync(f2.data(), w.frob2, sizeof(double) * nt, hipMemcpyDeviceToHost, s));
-    int status = 0;
-    ck(hipMemcpyAsync(&status, w.status, sizeof(int), hipMemcpyDeviceToHost, s));
-    ck(hipStreamSynchronize(s));
+    // the whole analysis; returns the status word
+    auto analyze_all = [&](bool householder) -> int {
+      w.householder = w1.householder = householder;
+      // chunks alternate between the lanes: lane 0 on s, lane 1 on a second
+      // stream of this call, forked from s and joined back into it
+      CallHip hip;
+      hipStream_t ls = nullptr;
+      if (w.nlanes > 1 && nt > w.chunk) {
+        ls = hip.lease();
+        const hipEvent_t fork = hip.event();
+        ck(hipEventRecord(fork, s));
+        ck(hipStreamWaitEvent(ls, fork, 0));
+      }
+      // a chunk on the second lane starts once the previous chunk's band
+      // reduction is queued ahead of it, so that chunk's chase (one CU per
+      // tensor) runs beside this chunk's matrix-core stages
+      std::vector<hipEvent_t> marks;
+      if (ls)
+        for (int c = 0; c * w.chunk < nt; ++c) marks.push_back(hip.event());
+      for (int t0 = 0, c = 0; t0 < nt; t0 += w.chunk, ++c) {
+        const int batch = std::min(w.chunk, nt - t0);
+        const bool second = ls && (c & 1);
+        AllocWS wl = second ? w1 : w;
+        hipStream_t sl = second ? ls : s;
+        wl.xptrs = w.xptrs + t0;
+        wl.tags = w.tags + t0;
+        wl.band_done = ls ? marks[c] : nullptr;
+        if (ls && c > 0) ck(hipStreamWaitEvent(sl, marks[c - 1], 0));
+        ck(launch_sumsq(reinterpret_cast<const void* const*>(wl.xptrs), batch, N, xdt, w.frob2 + t0, sl));
+        if (d.flash) analyze_flash(d, batch, t0, wl, xdt, req->power_iters, req->seed, hip, sl);
+        else analyze_exact(d, batch, t0, wl, xdt, hip, sl);
+      }
+      if (ls) {
+        const hipEvent_t join = hip.event();
+        ck(hipEventRecord(join, ls));
+        ck(hipStreamWaitEvent(s, join, 0));
+      }
+      if (R > 0) ck(hipMemcpyAsync(lt.data(), w.lamT, sizeof(double) * nt * R, hipMemcpyDeviceToHost, s));
+      ck(hipMemcpyAsync(ld.data(), w.lamD, sizeof(double) * nt * d.D, hipMemcpyDeviceToHost, s));
+      ck(hipMemcpyAsync(f2.data(), w.frob2, sizeof(double) * nt, hipMemcpyDeviceToHost, s));
+      int status = 0;
+      ck(hipMemcpyAsync(&status, w.status, sizeof(int), hipMemcpyDeviceToHost, s));
+      ck(hipStreamSynchronize(s));
+      return status;
+    };
+    int status = analyze_all(false);
+    if (status == 2) {
+      // a CholeskyQR pass met a nearly dependent column (rank-deficient
+      // input): the same analysis again with Householder QR throughout
+      ck(hipMemsetAsync(w.frob2, 0, sizeof(double) * nt, s));
+      ck(hipMemsetAsync(w.status, 0, sizeof(int), s));
+      status = analyze_all(true);
+    }
     if (status != 0) return JOLT_EHIP;          // an eigensolver wait gave up: the factors are not valid
     for (int i = 0; i < nt; ++i)
       if (!std::isfinite(f2[i])) return JOLT_ERANGE;

@@ -52,6 +52,15 @@ struct GemmArgs {
   int a_sym, c_lower;
   // the a_ptrs / b_ptrs entries are 16-byte aligned
   int ptr_align16;
+  // both operands fp32 may run on bf16 matrix cores as hi + lo planes (1:
+  // four products, about 2^-17 relative error per term instead of fp32's
+  // 2^-24) or, both k contiguous, as three planes (2: six products, about
+  // 2^-24)
+  int split_f32;
+  // triangular operands (matrix-core path): A(m, k) = 0 for k > m (a_lower),
+  // B(k, n) = 0 for k > n (b_upper); a tile's K range then ends at its last
+  // row (column)
+  int a_lower, b_upper;
 };
 
 // scope: the profiling name of the launch (default "gemm_bf16" or "gemm" by the units it runs on)
@@ -114,6 +123,18 @@ hipError_t panel_factor(float* A, int64_t m, int64_t ld, int64_t bstride, int64_
                         float* scratch, hipStream_t s, int write_r = 0);
 hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t batch_stride, int batch,
                           float* work, hipStream_t s);
+
+// Thin QR of full-rank tall column-major U (m x k, k <= cholesky_qr_max_k())
+// by two CholeskyQR passes: U <- Q with Q^T Q = I and U = Q R, diag(R) > 0.
+// U2: a second buffer of U's shape (ld, bstride); work:
+// cholesky_qr_work_floats(m, k, batch) floats.  A column nearly dependent on
+// the earlier ones (a pivot below 2^-10 of its original diagonal) ORs 2 into
+// *status, and U then holds no valid factor: the caller repeats with
+// householder_qr.
+int64_t cholesky_qr_max_k();
+size_t cholesky_qr_work_floats(int64_t m, int64_t k, int batch);
+hipError_t cholesky_qr(float* U, float* U2, int64_t m, int64_t k, int64_t ld, int64_t bstride, int batch,
+                       float* work, int* status, hipStream_t s);
 
 // Sort columns by lam descending (ties: lower index), sign-fix (largest |.| entry
 // positive, lowest index on ties) and emit row-major U_out [m][ld_out]; lam_out

@@ -16,6 +16,8 @@
 // that diag(R) >= 0.  Threads run along rows: every panel access is a
 // coalesced column read.
 #include "device.hpp"
+#include <algorithm>
+#include <utility>
 #include "kernels.hpp"
 
 namespace jolt {
@@ -905,6 +907,214 @@ __global__ __launch_bounds__(256) void k_emit(const float* U, int64_t m, int64_t
   }
 }
 
+// ---------------------------------------------------------------- CholeskyQR
+// The thin QR factorization U = Q R of a full-rank tall U (m x k, k <= 256)
+// from its Gram: G = U^T U = L L^T (Cholesky, L lower with positive
+// diagonal), Q = U L^{-T}, R = L^T.  In exact arithmetic this is the
+// factorization with diag(R) > 0, so span(Q[:, :j]) = span(U[:, :j]) for
+// every j.
+//
+// k_chol_inv computes L^{-1} in one pass over the columns.  Element form,
+// step j (the rows above j already final, d = A[j][j] the Schur
+// complement's pivot, s = 1 / sqrt(d)):
+//   rows i > j, columns k != j:  A[i][k] -= A[i][j] b[k] s^2
+//   rows i > j, column j:        A[i][j]  = -A[i][j] s^2
+//   row j, columns k < j:        A[j][k] *= s,   A[j][j] = s,
+// with b[k] = A[k][j] for k > j (column j: the Cholesky update) and A[j][k]
+// for k < j (row j of the inverse so far: its forward substitution); after
+// the last step the lower triangle holds L^{-1}.  Blocked by 32: step J
+// factors the diagonal block, W = L_JJ^{-1} (the element form, one wave, in
+// LDS), then with 32 x 32 fp32 matrix-core products
+//   L_IJ = S_IJ W^T (I > J),  block (I, J) <- -L_IJ W,
+//   X_JK = W Y_JK (K < J: row block J of the inverse, final),
+//   S_IK -= L_IJ L_KJ^T (J < K <= I),  Y_IK -= L_IJ X_JK (K < J < I),
+// each block held in one wave's registers (matrix-core accumulator layout).
+// A pivot not above pivot_rel times its column's original diagonal (a
+// column nearly in the span of the earlier ones) sets bit 1 of *status; the
+// step then continues with the original diagonal, so the results stay
+// finite but are not a factorization.  With minus_identity the output is
+// L^{-1} - I (a correction, for a nearly orthonormal U).  k is padded to a
+// multiple of 32 with an identity block.
+constexpr int kCholMaxK = 256;
+constexpr int CB = 32, CBP = CB + 1, CNB = kCholMaxK / CB;
+constexpr int kCholBlocks = CNB * (CNB + 1) / 2;   // 36 lower blocks, over 8 waves
+constexpr int CW = 8;                                // waves of k_chol_inv
+struct CholLds {
+  float col[CNB][CB][CBP];   // block column J: S_IJ staged, then L_IJ
+  float row[CNB][CB][CBP];   // block row J of the inverse: X_JK (K < J), W = X_JJ
+  float d0[kCholMaxK];       // original diagonal
+};
+
+// row of register i of lane l in the accumulator layout, column l % 32
+__device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+__device__ __forceinline__ void acc_to_tile(const f32x16& a, float (*t)[CBP], int lane) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t[acc_row(i, lane)][lane & 31] = a[i];
+}
+__device__ __forceinline__ f32x16 tile_to_acc(const float (*t)[CBP], int lane) {
+  f32x16 a;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a[i] = t[acc_row(i, lane)][lane & 31];
+  return a;
+}
+// c + sA A B over one 32-block of k; A(m, k) = ta[m][k], B(k, n) = tb[k][n] or (tbt) tb[n][k]
+template <bool TB>
+__device__ __forceinline__ f32x16 mm32(f32x16 c, float sA, const float (*ta)[CBP], const float (*tb)[CBP],
+                                       int lane) {
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int kk = 0; kk < CB; kk += 2) {
+    const float a = sA * ta[r][kk + h];
+    const float b = TB ? tb[r][kk + h] : tb[kk + h][r];
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  return c;
+}
+__device__ __forceinline__ void chol_block_of(int bi, int& I, int& K) {
+  I = 0;
+  while ((I + 1) * (I + 2) / 2 <= bi) ++I;
+  K = bi - I * (I + 1) / 2;
+}
+
+// W <- L^{-1} for the 32 x 32 block W = L L^T (lower triangle read; the
+// upper triangle is zeroed), by one wave: the element form above.  Lane
+// (h, c) owns the elements (2 t + h, c).  A wave's LDS operations execute in
+// program order, so at each step every read (the pivot, row j and column j,
+// the lane's own elements) is issued before any write.  Row pairs above j
+// are final and skipped; the upper triangle is never read for a lower
+// element, so it takes whatever the update gives and is zeroed at the end.
+// The pivot's reciprocal square root is the hardware one (about 1 ulp: a
+// perturbation of the factor far below what the second pass removes).
+__device__ void chol_inv_block(float (*W)[CBP], const float* d0, float pivot_rel, int lane, bool& bad) {
+  const int c = lane & 31, h = lane >> 5;
+  for (int j = 0; j < CB; ++j) {
+    wave_lds_sync();
+    float d = W[j][j];
+    const float dj0 = d0[j];
+    const float* pb = c > j ? &W[c][j] : &W[j][c];      // b[c]: column j below the pivot, row j left of it
+    const float bc = c == j ? 0.f : *pb;
+    float bi[CB / 2], v[CB / 2];
+#pragma unroll
+    for (int t = 0; t < CB / 2; ++t) {
+      if (2 * t + 1 < j) continue;                    // both rows above j
+      bi[t] = W[2 * t + h][j];
+      v[t] = W[2 * t + h][c];
+    }
+    if (!(d > pivot_rel * dj0)) {
+      bad = true;
+      d = dj0 > 0.f ? dj0 : 1.f;
+    }
+    const float sj = __builtin_amdgcn_rsqf(d), s2 = sj * sj;
+    const float g = -bc * s2;
+    const bool cj = c == j;
+    wave_lds_sync();
+#pragma unroll
+    for (int t = 0; t < CB / 2; ++t) {
+      if (2 * t + 1 < j) continue;
+      const int i = 2 * t + h;
+      const float w_gt = cj ? -bi[t] * s2 : fmaf(bi[t], g, v[t]);
+      if (2 * t > j) {
+        W[i][c] = w_gt;                               // both rows below j
+      } else {
+        const float w_eq = cj ? sj : v[t] * sj;
+        W[i][c] = i > j ? w_gt : (i == j ? w_eq : v[t]);
+      }
+    }
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int t = 0; t < CB / 2; ++t) {
+    const int i = 2 * t + h;
+    if (c > i) W[i][c] = 0.f;
+  }
+  wave_lds_sync();
+}
+
+__global__ __launch_bounds__(CW * 64) void k_chol_inv(const float* G, int64_t g_batch, int k, float pivot_rel,
+                                                   float* Linv, int64_t l_batch, int minus_identity, int* status) {
+  __shared__ CholLds sm;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t z = blockIdx.x;
+  const float* Gz = G + z * g_batch;
+  const int nb = (k + CB - 1) / CB, nblk = nb * (nb + 1) / 2;
+  constexpr int NS = (kCholBlocks + CW - 1) / CW;
+  f32x16 acc[NS];
+  int bI[NS], bK[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int bi = wave + CW * s;
+    bI[s] = bK[s] = -1;
+    if (bi >= nblk) continue;
+    chol_block_of(bi, bI[s], bK[s]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int gi = CB * bI[s] + acc_row(i, lane), gk = CB * bK[s] + (lane & 31);
+      acc[s][i] = (gi < k && gk < k) ? Gz[static_cast<int64_t>(gi) * k + gk] : (gi == gk ? 1.f : 0.f);
+      if (bI[s] == bK[s] && gi == gk) sm.d0[gi] = acc[s][i];
+    }
+  }
+  __syncthreads();
+  bool bad = false;
+  for (int J = 0; J < nb; ++J) {
+    float(*W)[CBP] = sm.row[J];
+    // ---- A: the diagonal block's owner factors it: W = L_JJ^{-1}
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (bI[s] != J || bK[s] != J) continue;
+      acc_to_tile(acc[s], W, lane);
+      chol_inv_block(W, sm.d0 + CB * J, pivot_rel, lane, bad);
+      acc[s] = tile_to_acc(W, lane);           // X_JJ = W, final
+    }
+    __syncthreads();
+    // ---- B: block column J of L, its blocks' inverse values; row block J of the inverse
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int I = bI[s], K = bK[s];
+      if (I > J && K == J) {
+        float(*C)[CBP] = sm.col[I];
+        acc_to_tile(acc[s], C, lane);          // S_IJ
+        wave_lds_sync();
+        const f32x16 L = mm32<true>(f32x16{}, 1.f, C, W, lane);   // S_IJ W^T
+        wave_lds_sync();
+        acc_to_tile(L, C, lane);
+        wave_lds_sync();
+        acc[s] = mm32<false>(f32x16{}, -1.f, C, W, lane);          // -L_IJ W
+      } else if (I == J && K < J) {
+        float(*Y)[CBP] = sm.row[K];
+        acc_to_tile(acc[s], Y, lane);          // Y_JK
+        wave_lds_sync();
+        acc[s] = mm32<false>(f32x16{}, 1.f, W, Y, lane);           // X_JK = W Y_JK, final
+        wave_lds_sync();
+        acc_to_tile(acc[s], Y, lane);
+      }
+    }
+    __syncthreads();
+    // ---- C: trailing blocks
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int I = bI[s], K = bK[s];
+      if (I <= J || K == J) continue;
+      if (K > J) acc[s] = mm32<true>(acc[s], -1.f, sm.col[I], sm.col[K], lane);   // S_IK -= L_IJ L_KJ^T
+      else acc[s] = mm32<false>(acc[s], -1.f, sm.col[I], sm.row[K], lane);       // Y_IK -= L_IJ X_JK
+    }
+    __syncthreads();
+  }
+  float* Lz = Linv + z * l_batch;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int I = bI[s], K = bK[s];
+    if (I < 0) continue;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int gi = CB * I + acc_row(i, lane), gk = CB * K + (lane & 31);
+      if (gi < k && gk < k) {
+        Lz[static_cast<int64_t>(gi) * k + gk] = acc[s][i] - (minus_identity && gi == gk ? 1.f : 0.f);
+        if (I != K) Lz[static_cast<int64_t>(gk) * k + gi] = 0.f;    // the mirrored block above the diagonal
+      }
+    }
+  }
+  if (bad) __hip_atomic_fetch_or(status, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 }  // namespace
 
 
@@ -1028,6 +1238,79 @@ hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t bs
   if (blocks > 8192) blocks = 8192;
   k_col_signs<<<dim3(blocks, batch), 256, 0, s>>>(A, m, k, ld, bstride, taus);
   return hipGetLastError();
+}
+
+int cholesky_qr_ksplit(int64_t m) {
+  // the Gram's fp32 sums run over chunks of at most 512 rows, added in a fixed order
+  return static_cast<int>(std::min<int64_t>(16, std::max<int64_t>(1, (m + 511) / 512)));
+}
+
+int64_t cholesky_qr_max_k() { return kCholMaxK; }
+
+size_t cholesky_qr_work_floats(int64_t m, int64_t k, int batch) {
+  return static_cast<size_t>(batch) * (2 + cholesky_qr_ksplit(m)) * k * k;
+}
+
+hipError_t cholesky_qr(float* U, float* U2, int64_t m, int64_t k, int64_t ld, int64_t bstride, int batch,
+                       float* work, int* status, hipStream_t s) {
+  if (k < 1 || k > kCholMaxK || m < k) return hipErrorInvalidValue;
+  const int ks = cholesky_qr_ksplit(m);
+  float* G = work;                                               // [batch][k][k], lower triangle
+  float* Li = G + static_cast<size_t>(batch) * k * k;            // [batch][k][k], L^{-1}
+  float* part = Li + static_cast<size_t>(batch) * k * k;         // [batch][ks][k][k]
+  ProfScope ps("cholqr", s);
+  // algorithmic work per pass: U read twice (Gram, product) and written
+  // once; k (k + 1) m flops for the Gram's triangle, m k (k + 1) for the
+  // triangular product, k^3 / 3 for the factorization and inverse
+  prof_add_work("cholqr", 2.0 * batch * (3.0 * 4.0 * m * k),
+                2.0 * batch * (2.0 * k * (k + 1.0) * m + k * k * (k / 3.0)));
+  hipError_t e;
+  // pass 1: U2 = U L1^{-T}; pass 2 (U2 nearly orthonormal, L2 near I):
+  // U = U2 + U2 (L2^{-T} - I), so that U2's fp32 values pass through exactly
+  // and only the small correction carries the split products' rounding
+  for (int pass = 0; pass < 2; ++pass) {
+    float* src = pass == 0 ? U : U2;
+    float* dst = pass == 0 ? U2 : U;
+    GemmArgs g{};
+    g.alpha = 1.f;
+    g.a_dtype = g.b_dtype = g.c_dtype = kF32;
+    // G = src^T src (row-major, rows m >= columns n)
+    g.M = k; g.N = k; g.K = m;
+    g.A = src; g.am = plain(ld); g.ak = plain(1); g.a_batch = bstride;
+    g.B = src; g.bk = plain(1); g.bn = plain(ld); g.b_batch = bstride;
+    g.C = G; g.c_m = k; g.c_n = 1; g.c_batch = k * k;
+    g.c_lower = 1;
+    // pass 2 measures the departure from orthonormality (about 1e-6): its
+    // Gram needs fp32-grade products even for columns concentrated on a few rows
+    g.split_f32 = pass == 0 ? 1 : 2;
+    if (ks > 1) { g.ksplit = ks; g.partial = part; }
+    if ((e = launch_gemm(g, batch, s, "cholqr_gemm")) != hipSuccess) return e;
+    k_chol_inv<<<batch, CW * 64, 0, s>>>(G, k * k, static_cast<int>(k), 0x1p-10f, Li, k * k, pass, status);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (pass == 1) {
+      // dst = src, then dst += src (L^{-1} - I)^T
+      if (bstride == ld * k) {
+        e = hipMemcpyAsync(dst, src, sizeof(float) * batch * bstride, hipMemcpyDeviceToDevice, s);
+      } else {
+        e = hipMemcpy2DAsync(dst, sizeof(float) * bstride, src, sizeof(float) * bstride, sizeof(float) * ld * k,
+                             batch, hipMemcpyDeviceToDevice, s);
+      }
+      if (e != hipSuccess) return e;
+    }
+    // dst (+)= src B, B(j, n) = L^{-1}[n][j] (pass 2: minus the identity)
+    GemmArgs q{};
+    q.alpha = 1.f;
+    q.beta = pass == 0 ? 0.f : 1.f;
+    q.a_dtype = q.b_dtype = q.c_dtype = kF32;
+    q.M = m; q.N = k; q.K = k;
+    q.A = src; q.am = plain(1); q.ak = plain(ld); q.a_batch = bstride;
+    q.B = Li; q.bk = plain(1); q.bn = plain(k); q.b_batch = k * k;
+    q.C = dst; q.c_m = 1; q.c_n = ld; q.c_batch = bstride;
+    q.split_f32 = 1;
+    q.b_upper = 1;
+    if ((e = launch_gemm(q, batch, s, "cholqr_gemm")) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t finalize_factor_ws(const float* U_cm, int64_t m, int64_t R, int64_t ld_cm, int64_t cm_batch,

@@ -207,6 +207,78 @@ def test_gpu_factors_exact_direct(J, single):
         assert abs((f2 - eg) - (f2 - eo)) <= 5e-3 * (f2 - eo), (r_T, r_D, f2 - eg, f2 - eo)
 
 
+def _qr_launches(J, X):
+    """Allocate on one tensor (keys and values both X) with the QR scopes
+    profiled: (CholeskyQR calls, Householder update calls, result)."""
+    J.profile_enable("cholqr,qr_update")
+    try:
+        res, xd = _alloc_single(J, X, "f32")
+        torch.cuda.synchronize()
+        return J.profile_query("cholqr")["launches"], J.profile_query("qr_update")["launches"], res, xd
+    finally:
+        J.profile_enable(None)
+
+
+def test_full_rank_factors_take_cholesky_qr(J):
+    """The dual token factor of a full-rank tensor (T > H D) is
+    re-orthonormalized by CholeskyQR alone (no Householder update runs), and
+    is orthonormal with the oracle's leading subspaces."""
+    X = kvgen.tensor(2, 512, D, seed=8, layer=1, kind=0, decay=0.85, dtype="f32").astype(np.float64)
+    n_chol, n_hh, res, _ = _qr_launches(J, X)
+    assert n_chol > 0 and n_hh == 0, (n_chol, n_hh)
+    R = res.r_T_cap
+    a = codec.analyze(X, R)
+    Ut = res.factors(0)[0].cpu().numpy().astype(np.float64)
+    assert np.abs(Ut.T @ Ut - np.eye(R)).max() < 1e-5
+    assert np.all(np.abs(res.spectra_T[0] - a["lam_T"][:R]) <= 2e-5 * a["lam_T"][0])
+    for k in resolvable_cuts(a["lam_T"], R, 2 * D):
+        assert max_sine(Ut[:, :k], a["U_T"][:, :k]) <= 1e-3, k
+
+
+def test_rank_deficient_input(J, rot):
+    """An exactly rank-6 tensor (no noise) in the dual regime with a rank cap
+    of 64: the factor is orthonormal, carries the oracle's rank-6 subspace
+    and spectrum (the rest of the spectrum within 2e-5 lambda_1 of zero),
+    and the end-to-end error matches the oracle's record within 1e-4."""
+    X = kvgen.tensor(2, 512, D, seed=9, noise_std=0.0, rank=6, outliers=False, dtype="f32").astype(np.float64)
+    _, _, res, xd = _qr_launches(J, X)
+    R = res.r_T_cap
+    assert R > 6
+    a = codec.analyze(X, R)
+    lam_o, lam_g = a["lam_T"], res.spectra_T[0]
+    assert np.all(np.abs(lam_g - lam_o[:R]) <= 2e-5 * lam_o[0])
+    Ut, Ud = res.factors(0)
+    Utn = Ut.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(Utn))
+    assert np.abs(Utn.T @ Utn - np.eye(R)).max() < 1e-5
+    assert max_sine(Utn[:, :6], a["U_T"][:, :6]) <= 1e-3
+    choice = (8, 16, 2)
+    Q = rotation.rotation(0, D)
+    xh = J.decode(J.encode(xd, choice, Ut, Ud, rot), 2, 512, choice, rot, dtype=torch.float32)
+    err_g = codec.rel_err(X, xh.cpu().numpy())
+    err_o = codec.rel_err(X, codec.decode_tensor(codec.encode_tensor(X, a["U_T"], a["U_D"], choice, Q), Q, "f32"))
+    assert abs(err_g - err_o) < 1e-4, (err_g, err_o)
+
+
+def test_zero_tensor_falls_back_to_householder(J, rot):
+    """An all-zero tensor: its token basis X V_R is zero, the first CholeskyQR
+    pivot is not above its (zero) diagonal, and the analysis is repeated with
+    Householder QR.  Spectra are zero, both factors orthonormal, and the
+    record decodes to zeros."""
+    X = np.zeros((2, 512, D))
+    n_chol, n_hh, res, xd = _qr_launches(J, X)
+    assert n_chol > 0 and n_hh > 0, (n_chol, n_hh)
+    R = res.r_T_cap
+    assert np.all(res.spectra_T[0] == 0.0) and np.all(res.spectra_D[0] == 0.0) and res.frob2[0] == 0.0
+    Ut, Ud = res.factors(0)
+    Utn, Udn = (t.cpu().numpy().astype(np.float64) for t in (Ut, Ud))
+    assert np.abs(Utn.T @ Utn - np.eye(R)).max() < 1e-5
+    assert np.abs(Udn.T @ Udn - np.eye(D)).max() < 1e-5
+    choice = (16, 16, 2)
+    xh = J.decode(J.encode(xd, choice, Ut, Ud, rot), 2, 512, choice, rot, dtype=torch.float32)
+    assert torch.count_nonzero(xh).item() == 0
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 def test_end_to_end_single_tensor(J, rot, single, bits):
     X, a, Q = single
