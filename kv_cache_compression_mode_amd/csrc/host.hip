@@ -673,7 +673,8 @@ void feature_factor(const Dims& d, int batch, int t0, const AllocWS& w, hipStrea
 }
 
 // Token-mode eigenvalues as Rayleigh quotients ||X_(T)^T u_j||^2 of the
-// orthonormal column-major U (T x R), then sort/sign/emit.
+// orthonormal column-major U (T x R), then sort/sign/emit (the randomized
+// path, whose small eigenproblem only approximates the captured energies).
 void token_finalize(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, hipStream_t s) {
   const int64_t T = d.T, HD = d.HD, D = d.D, R = d.R;
   GemmArgs g = gemm0();
@@ -727,7 +728,7 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   }
   // leading eigenvectors V_R of the token Gram: the first R columns of w.V
   // (column-major, leading dimension n)
-  ck(syev_top(w.G, n, batch, static_cast<int>(R), w.V, nullptr, w.syev, s, w.status, w.band_done));
+  ck(syev_top(w.G, n, batch, static_cast<int>(R), w.V, w.lam_tmp, w.syev, s, w.status, w.band_done));
   if (d.dual) {
     // U' = X_(T) V_R (T x R, column-major)
     GemmArgs gu = gemm0();
@@ -741,7 +742,10 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     ck(copy_cols(w.V, n, n * n, w.Ucm, T, T * R, T, R, batch, s));
   }
   orthonormalize(w.Ucm, w.Ucm2, T, R, batch, w.qtau, w.cq, w, s);
-  token_finalize(d, batch, t0, w, xdt, s);
+  // the token spectrum: the eigensolver's eigenvalues of the token Gram
+  // (fp64, descending; the dual Gram shares the nonzero ones)
+  ck(finalize_factor_ws(w.Ucm, T, R, T, T * R, w.lam_tmp, R, w.UT + static_cast<size_t>(t0) * T * R, R, T * R,
+                        w.lamT + static_cast<size_t>(t0) * R, R, batch, w.perm, w.sgn, s));
   ff.join();
 }
 
