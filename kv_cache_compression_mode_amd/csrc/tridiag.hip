@@ -394,11 +394,10 @@ __device__ __forceinline__ int sturm_count(const double* d, const double* e2, in
   if (fabs(q) < pivmin) q = -pivmin;
   cnt += q < 0.0;
   for (int64_t i = 1; i < n; ++i) {
-    // e2 / q through the hardware reciprocal refined by two Newton steps (a
-    // few ulps, as the count needs only the pivot signs); |q| >= pivmin
-    // keeps the reciprocal finite
+    // e2 / q through the hardware reciprocal (about 24 bits) refined by one
+    // Newton step (about 2e-15 relative, measured: the count needs only the
+    // pivot signs); |q| >= pivmin keeps the reciprocal finite
     double r = __builtin_amdgcn_rcp(q);
-    r = __builtin_fma(__builtin_fma(-q, r, 1.0), r, r);
     r = __builtin_fma(__builtin_fma(-q, r, 1.0), r, r);
     q = (d[i] - x) - e2[i - 1] * r;
     if (fabs(q) < pivmin) q = -pivmin;
@@ -409,6 +408,7 @@ __device__ __forceinline__ int sturm_count(const double* d, const double* e2, in
 
 // Top R eigenvalues, descending: lam[q] is the (n-1-q)-th smallest, by
 // bisection to fp64 resolution inside the Gershgorin interval.
+constexpr int BSL = 4;           // threads per eigenvalue (a power of two <= 64)
 __global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double* e_g, int64_t n, int R,
                                                double* lam) {
   extern __shared__ double sh[];
@@ -450,10 +450,10 @@ __global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double*
   const double g0 = gl_s, gw = gu_s - gl_s;
   grid_cnt[threadIdx.x] = sturm_count(d, e2, n, g0 + gw * (threadIdx.x + 1) * (1.0 / 257.0), piv_s);
   __syncthreads();
-  // four threads per eigenvalue (multisection): each evaluates one of four
-  // interior points of the bracket, which then shrinks to one fifth
+  // BSL threads per eigenvalue (multisection): each evaluates one of BSL
+  // interior points of the bracket, which then shrinks to 1 / (BSL + 1)
   const int gid = blockIdx.x * 256 + threadIdx.x;
-  const int q = gid >> 2, sub = gid & 3;
+  const int q = gid / BSL, sub = gid % BSL;
   if (q >= R) return;                             // whole groups leave together
   const int64_t k = n - 1 - q;                    // wanted: the k-th smallest (0-based)
   // the first grid point whose count exceeds k (256 if none); counts rise with x
@@ -465,14 +465,14 @@ __global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double*
   for (int it = 0; it < 100; ++it) {
     if (hi - lo <= fmax(2.0 * DBL_EPSILON * fmax(fabs(lo), fabs(hi)), tol_s) + piv_s) break;
     const double w = hi - lo;
-    const double x = lo + w * (sub + 1) * 0.2;
+    const double x = lo + w * (sub + 1) * (1.0 / (BSL + 1));
     const int cnt = sturm_count(d, e2, n, x, piv_s);
     double nlo = lo, nhi = hi;
     bool found = false;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int ct = __shfl(cnt, (threadIdx.x & 63 & ~3) + t);
-      const double xt = lo + w * (t + 1) * 0.2;
+    for (int t = 0; t < BSL; ++t) {
+      const int ct = __shfl(cnt, (threadIdx.x & 63 & ~(BSL - 1)) + t);
+      const double xt = lo + w * (t + 1) * (1.0 / (BSL + 1));
       if (!found) {
         if (ct > k) { nhi = xt; found = true; }
         else nlo = xt;
@@ -486,7 +486,8 @@ __global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double*
 }
 
 // Eigenvector of eigenvalue lam[q] by inverse iteration (three solves with
-// T - lam I = L D L^T from a fixed pseudo-random start), normalized, fp32
+// T - lam I = L D L^T from a fixed pseudo-random start; the factorization
+// and the first forward substitution share one pass), normalized, fp32
 // out as column q of Z (column-major, ld n).  The factorization keeps the
 // reciprocal pivots, so each solve is multiply-only; intermediate vectors
 // are rescaled on the fly.  Scratch rp / y: [i][q] interleaved (coalesced
@@ -516,49 +517,58 @@ __global__ __launch_bounds__(IVW) void k_invit(const double* d_g, const double* 
   double* y = y_g + z * n * R;
   const double lm = lam[z * R + q];
   const double tiny = fmax(tn, DBL_MIN) * DBL_EPSILON;
-  // L D L^T of T - lam I: pivots p_i = (d_i - lam) - e_{i-1}^2 / p_{i-1}, kept as 1 / p_i
+  // L D L^T of T - lam I: pivots p_i = (d_i - lam) - e_{i-1}^2 / p_{i-1},
+  // kept as 1 / p_i, in the same pass as the first forward solve L u = y0
+  // (l_i = e_{i-1} / p_{i-1}: it needs only the previous pivot)
   {
-    double r = 0.0;
+    double r = 0.0, u = 0.0;
     for (int64_t i0 = 0; i0 < n; i0 += IVC) {
-      double rr[IVC];
+      double rr[IVC], yy[IVC];
 #pragma unroll
       for (int c = 0; c < IVC; ++c) {
         const int64_t i = i0 + c;
+        u = invit_start(q, i) - (i ? e[i - 1] * r * u : 0.0);
+        yy[c] = u;
         double p = (d[i] - lm) - (i ? e[i - 1] * e[i - 1] * r : 0.0);
         if (fabs(p) < tiny) p = tiny;
-        r = __builtin_amdgcn_rcp(p);                 // 1 / p: reciprocal + two Newton steps
-        r = __builtin_fma(__builtin_fma(-p, r, 1.0), r, r);
+        r = __builtin_amdgcn_rcp(p);                 // 1 / p: reciprocal + one Newton step (~2e-15)
         r = __builtin_fma(__builtin_fma(-p, r, 1.0), r, r);
         rr[c] = r;
       }
 #pragma unroll
-      for (int c = 0; c < IVC; ++c) rp[(i0 + c) * R + q] = rr[c];
+      for (int c = 0; c < IVC; ++c) {
+        rp[(i0 + c) * R + q] = rr[c];
+        y[(i0 + c) * R + q] = yy[c];
+      }
     }
   }
-  double sc = 1.0;
+  double sc = 1.0, s2 = 0.0;
   for (int it = 0; it < 3; ++it) {
-    // forward: L u = sc * y   (L unit lower, l_i = e_{i-1} / p_{i-1})
-    double u = 0.0, rprev = 0.0;
-    for (int64_t i0 = 0; i0 < n; i0 += IVC) {
-      double yy[IVC], rr[IVC];
+    if (it > 0) {
+      // forward: L u = sc * y   (L unit lower, l_i = e_{i-1} / p_{i-1})
+      double u = 0.0, rprev = 0.0;
+      for (int64_t i0 = 0; i0 < n; i0 += IVC) {
+        double yy[IVC], rr[IVC];
 #pragma unroll
-      for (int c = 0; c < IVC; ++c) {
-        const int64_t i = i0 + c;
-        yy[c] = it == 0 ? invit_start(q, i) : y[i * R + q];
-        rr[c] = rp[i * R + q];
+        for (int c = 0; c < IVC; ++c) {
+          const int64_t i = i0 + c;
+          yy[c] = y[i * R + q];
+          rr[c] = rp[i * R + q];
+        }
+#pragma unroll
+        for (int c = 0; c < IVC; ++c) {
+          const int64_t i = i0 + c;
+          u = yy[c] * sc - (i ? e[i - 1] * rprev * u : 0.0);
+          yy[c] = u;
+          rprev = rr[c];
+        }
+#pragma unroll
+        for (int c = 0; c < IVC; ++c) y[(i0 + c) * R + q] = yy[c];
       }
-#pragma unroll
-      for (int c = 0; c < IVC; ++c) {
-        const int64_t i = i0 + c;
-        u = yy[c] * sc - (i ? e[i - 1] * rprev * u : 0.0);
-        yy[c] = u;
-        rprev = rr[c];
-      }
-#pragma unroll
-      for (int c = 0; c < IVC; ++c) y[(i0 + c) * R + q] = yy[c];
     }
-    // D L^T x = u:  x_i = (u_i - e_i x_{i+1}) / p_i
+    // D L^T x = u:  x_i = (u_i - e_i x_{i+1}) / p_i; the last pass also sums x^2
     double xs = 0.0, mx = 0.0;
+    s2 = 0.0;
     for (int64_t i0 = n - IVC; i0 >= 0; i0 -= IVC) {
       double yy[IVC], rr[IVC];
 #pragma unroll
@@ -572,24 +582,15 @@ __global__ __launch_bounds__(IVW) void k_invit(const double* d_g, const double* 
         xs = (yy[c] - (i + 1 < n ? e[i] * xs : 0.0)) * rr[c];
         yy[c] = xs;
         mx = fmax(mx, fabs(xs));
+        s2 = fma(xs, xs, s2);
       }
 #pragma unroll
       for (int c = 0; c < IVC; ++c) y[(i0 + c) * R + q] = yy[c];
     }
     sc = mx > 0.0 ? 1.0 / mx : 1.0;
   }
-  double s2 = 0.0;
-  for (int64_t i0 = 0; i0 < n; i0 += IVC) {
-    double yy[IVC];
-#pragma unroll
-    for (int c = 0; c < IVC; ++c) yy[c] = y[(i0 + c) * R + q];
-#pragma unroll
-    for (int c = 0; c < IVC; ++c) {
-      const double t = yy[c] * sc;
-      s2 += t * t;
-    }
-  }
-  nrm_g[z * R + q] = sc / sqrt(s2);
+  // the last solve's x, normalized
+  nrm_g[z * R + q] = s2 > 0.0 ? 1.0 / sqrt(s2) : 0.0;
 }
 
 // Z[:, q] = y[:, q] * nrm[q] as fp32, through a 32 x 32 LDS transpose ([i][q]
@@ -689,118 +690,139 @@ __global__ __launch_bounds__(64) void k_cb_tfac(const float* Rf_g, int64_t rf_st
   }
 }
 
-// The blocks of wavefront step t, one workgroup per (block, 64 columns of Z):
-// W = V^T Z_rows (K split over two wave pairs), W2 = T W, Z_rows -= V W2, on
-// fp32 matrix cores (32x32x2) from LDS.
-__global__ __launch_bounds__(256) void k_cb_apply(int t, int glo, int nchunk, float* Z, int n, int R,
+// Wavefront steps 2u and 2u + 1 in one launch, one workgroup per (group,
+// 64 columns of Z): the group's blocks s0 = 2u - 2 g' and s0 + 1 (those that
+// exist), applied in that order to the 95 rows they span, kept in LDS.  The
+// blocks of group g' - 1 that overlap them have s' <= s0 + 1, so they ran
+// in launches u' < u; the row spans of one launch are disjoint.  Per block:
+// W = V^T Z_rows (K split over two wave pairs), W2 = T W, Z_rows -= V W2,
+// on fp32 matrix cores (32x32x2) from LDS.
+constexpr int CBW = CBR + SBW;    // window rows of a block pair (95, padded to 96)
+__global__ __launch_bounds__(256) void k_cb_apply(int u, int glo, int nchunk, float* Z, int n, int R,
                                                   int64_t z_batch, const float* Rf_g, int64_t rf_stride,
                                                   const float* Tg, int64_t t_stride, int ng, int K0) {
-  __shared__ float Vs[CBR][SBW + 1];     // staircase V[r][i]
-  __shared__ float Ts[SBW][SBW + 1];
-  __shared__ float Zs[CBR][65];          // Z rows x 64 columns
+  __shared__ float Vs[2][CBR][SBW + 1];  // staircases V[r][i] of the two blocks
+  __shared__ float Ts[2][SBW][SBW + 1];
+  __shared__ float Zs[CBW][65];          // window rows x 64 columns
   __shared__ float Wp[2][SBW][65];       // W partial sums, then W2 = T W (in Wp[0])
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
   uint32_t bx, by;
   xcd_group_2d(bx, by);                            // the blocks of one matrix on one XCD
   const int bi = static_cast<int>(bx) / nchunk, ch = static_cast<int>(bx) % nchunk;
-  const int gp = glo + bi, s = t - 2 * gp, G = ng - 1 - gp, jg = G * SBW;
-  if (gp >= ng || s < 0 || s >= K0 || s >= sweep_steps(n, jg)) return;
-  const int rb = jg + 1 + s * SBW;
-  if (rb >= n) return;
-  const int rows = min(CBR - 1, n - rb);
+  const int gp = glo + bi, G = ng - 1 - gp, jg = G * SBW;
+  if (gp >= ng) return;
+  const int smax = min(K0, static_cast<int>(sweep_steps(n, jg)));
+  const int s0 = 2 * u - 2 * gp;
+  const bool has0 = s0 >= 0 && s0 < smax, has1 = s0 + 1 >= 0 && s0 + 1 < smax;
+  if (!has0 && !has1) return;
+  const int rw = jg + 1 + s0 * SBW;                // window row 0 (block s0's first row)
+  // rows the applied blocks span: [lo, hi) of the window
+  const int lo = has0 ? 0 : SBW;
+  const int hi = min(has1 ? CBW - 1 : CBR - 1, n - rw);
   const int c0 = ch * 64, nc = min(64, R - c0);
   const int64_t z = by;
   const float* Rf = Rf_g + z * rf_stride;
   float* Zz = Z + z * z_batch;
   const int last = n - 3;
-  // one phase of loads, every load in flight before the first LDS write: T,
-  // Z, the staircase V[i + r][i] = v_r of sweep jg + i; zeros off the
-  // staircase (disjoint positions)
-  float rt[4], rz[16], rv[4];
-  const float* tb = Tg + z * t_stride + (static_cast<int64_t>(G) * K0 + s) * SBW * SBW;
+  // one phase of loads, every load in flight before the first LDS write: the
+  // T factors, Z, the staircases V[i + r][i] = v_r of sweep jg + i; zeros off
+  // the staircases (disjoint positions)
+  float rt[2][4], rz[24], rv[2][4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) rt[q] = tb[tid + 256 * q];
+  for (int b = 0; b < 2; ++b) {
+    const int sb = s0 + b;
+    const bool ok = b == 0 ? has0 : has1;
+    const float* tb = Tg + z * t_stride + (static_cast<int64_t>(G) * K0 + (ok ? sb : 0)) * SBW * SBW;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int idx = tid + 256 * q, c = idx / CBR, r = idx % CBR;
-    rz[q] = (r < rows && c < nc) ? Zz[static_cast<int64_t>(c0 + c) * n + rb + r] : 0.f;
+    for (int q = 0; q < 4; ++q) {
+      rt[b][q] = ok ? tb[tid + 256 * q] : 0.f;
+      const int idx = tid + 256 * q, i = idx / SBW, r = idx % SBW, j = jg + i;
+      rv[b][q] = (ok && j <= last && sb < sweep_steps(n, j)) ? Rf[(sweep_offset(n, j) + sb) * RFS + r] : 0.f;
+    }
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int idx = tid + 256 * q, i = idx / SBW, r = idx % SBW, j = jg + i;
-    rv[q] = (j <= last && s < sweep_steps(n, j)) ? Rf[(sweep_offset(n, j) + s) * RFS + r] : 0.f;
+  for (int q = 0; q < 24; ++q) {
+    const int idx = tid + 256 * q, c = idx / CBW, r = idx % CBW;
+    rz[q] = (r >= lo && r < hi && c < nc) ? Zz[static_cast<int64_t>(c0 + c) * n + rw + r] : 0.f;
   }
-  for (int idx = tid; idx < CBR * SBW; idx += 256) {
-    const int row = idx / SBW, i = idx % SBW;
-    if (row < i || row >= i + SBW) Vs[row][i] = 0.f;
+  for (int idx = tid; idx < 2 * CBR * SBW; idx += 256) {
+    const int b = idx / (CBR * SBW), row = (idx / SBW) % CBR, i = idx % SBW;
+    if (row < i || row >= i + SBW) Vs[b][row][i] = 0.f;
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q;
+      Ts[b][idx / SBW][idx % SBW] = rt[b][q];
+      const int i = idx / SBW, r = idx % SBW;
+      Vs[b][i + r][i] = rv[b][q];
+    }
+#pragma unroll
+  for (int q = 0; q < 24; ++q) {
     const int idx = tid + 256 * q;
-    Ts[idx / SBW][idx % SBW] = rt[q];
-    const int i = idx / SBW, r = idx % SBW;
-    Vs[i + r][i] = rv[q];
-  }
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int idx = tid + 256 * q;
-    Zs[idx % CBR][idx / CBR] = rz[q];
+    Zs[idx % CBW][idx / CBW] = rz[q];
   }
   __syncthreads();
-  // W = V^T Z: wave w -> columns 32 (w & 1) .., rows of V 32 (w >> 1) ..
-  {
-    const int cb = 32 * (wave & 1), kb = 32 * (wave >> 1);
-    f32x16 acc = {};
 #pragma unroll
-    for (int kk = 0; kk < SBW; kk += 2) {
-      const int k = kb + kk + hf;
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[k][rl], Zs[k][cb + rl], acc, 0, 0, 0);
+  for (int b = 0; b < 2; ++b) {
+    if (b == 0 ? !has0 : !has1) continue;          // uniform over the workgroup
+    const int off = b * SBW;                       // the block's rows: window rows off .. off + 63
+    // W = V^T Z: wave w -> columns 32 (w & 1) .., rows of V 32 (w >> 1) ..
+    {
+      const int cb = 32 * (wave & 1), kb = 32 * (wave >> 1);
+      f32x16 acc = {};
+#pragma unroll
+      for (int kk = 0; kk < SBW; kk += 2) {
+        const int k = kb + kk + hf;
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[b][k][rl], Zs[off + k][cb + rl], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) Wp[wave >> 1][(e >> 2) * 8 + hf * 4 + (e & 3)][cb + rl] = acc[e];
     }
+    __syncthreads();
+    // W2 = T W (T upper), waves 0 and 1; W2 overwrites Wp[0] after the barrier
+    f32x16 w2 = {};
+    if (wave < 2) {
+      const int cb = 32 * wave;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) Wp[wave >> 1][(e >> 2) * 8 + hf * 4 + (e & 3)][cb + rl] = acc[e];
-  }
-  __syncthreads();
-  // W2 = T W (T upper), waves 0 and 1; W2 overwrites Wp[0] after the barrier
-  f32x16 w2 = {};
-  if (wave < 2) {
-    const int cb = 32 * wave;
-#pragma unroll
-    for (int kk = 0; kk < SBW; kk += 2) {
-      const int k = kk + hf;
-      w2 = __builtin_amdgcn_mfma_f32_32x32x2f32(Ts[rl][k], Wp[0][k][cb + rl] + Wp[1][k][cb + rl], w2, 0, 0, 0);
+      for (int kk = 0; kk < SBW; kk += 2) {
+        const int k = kk + hf;
+        w2 = __builtin_amdgcn_mfma_f32_32x32x2f32(Ts[b][rl][k], Wp[0][k][cb + rl] + Wp[1][k][cb + rl], w2, 0, 0, 0);
+      }
     }
-  }
-  __syncthreads();
-  if (wave < 2) {
+    __syncthreads();
+    if (wave < 2) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) Wp[0][(e >> 2) * 8 + hf * 4 + (e & 3)][32 * wave + rl] = w2[e];
-  }
-  __syncthreads();
-  // Z_rows -= V W2: wave w -> rows 32 (w >> 1) .., columns 32 (w & 1) ..
-  {
-    const int rbk = 32 * (wave >> 1), cb = 32 * (wave & 1);
-    f32x16 acc = {};
-#pragma unroll
-    for (int kk = 0; kk < SBW; kk += 2) {
-      const int k = kk + hf;
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[rbk + rl][k], Wp[0][k][cb + rl], acc, 0, 0, 0);
+      for (int e = 0; e < 16; ++e) Wp[0][(e >> 2) * 8 + hf * 4 + (e & 3)][32 * wave + rl] = w2[e];
     }
+    __syncthreads();
+    // Z_rows -= V W2: wave w -> rows 32 (w >> 1) .., columns 32 (w & 1) ..
+    {
+      const int rbk = 32 * (wave >> 1), cb = 32 * (wave & 1);
+      f32x16 acc = {};
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int r = rbk + (e >> 2) * 8 + hf * 4 + (e & 3);
-      Zs[r][cb + rl] -= acc[e];
+      for (int kk = 0; kk < SBW; kk += 2) {
+        const int k = kk + hf;
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[b][rbk + rl][k], Wp[0][k][cb + rl], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = off + rbk + (e >> 2) * 8 + hf * 4 + (e & 3);
+        Zs[r][cb + rl] -= acc[e];
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int idx = tid + 256 * q, c = idx / CBR, r = idx % CBR;
+  for (int q = 0; q < 24; ++q) {
+    const int idx = tid + 256 * q, c = idx / CBW, r = idx % CBW;
     rz[q] = Zs[r][c];
   }
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int idx = tid + 256 * q, c = idx / CBR, r = idx % CBR;
-    if (r < rows && c < nc) Zz[static_cast<int64_t>(c0 + c) * n + rb + r] = rz[q];
+  for (int q = 0; q < 24; ++q) {
+    const int idx = tid + 256 * q, c = idx / CBW, r = idx % CBW;
+    if (r >= lo && r < hi && c < nc) Zz[static_cast<int64_t>(c0 + c) * n + rw + r] = rz[q];
   }
 }
 
@@ -1423,7 +1445,7 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     double* nrm = reinterpret_cast<double*>(wb + Lw.nrm_off);
     {
       ProfScope ps("tri_eig", s);
-      k_bisect<<<dim3(static_cast<unsigned>((4 * R + 255) / 256), batch), 256, lds, s>>>(dd, ee, n, R, lam);
+      k_bisect<<<dim3(static_cast<unsigned>((BSL * R + 255) / 256), batch), 256, lds, s>>>(dd, ee, n, R, lam);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       k_invit<<<dim3(gx, batch), IVW, 0, s>>>(dd, ee, n, R, lam, dp, yv, nrm);
       if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1452,12 +1474,14 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
       if ((e = hipGetLastError()) != hipSuccess) return e;
       const int nchunk = (R + 63) / 64;
       const int tmax = 2 * (ng - 1) + K0 - 1;
-      for (int t = 0; t <= tmax; ++t) {
-        const int glo = t - K0 + 1 > 0 ? (t - K0 + 2) / 2 : 0;
-        const int ghi = t / 2 < ng - 1 ? t / 2 : ng - 1;
+      // wavefront steps 2u and 2u + 1 per launch: groups g' with a block at either
+      for (int u = 0; 2 * u <= tmax; ++u) {
+        const int x = 2 * u - K0 + 1;                // g' >= x / 2, rounded up
+        const int glo = x > 0 ? (x + 1) / 2 : 0;
+        const int ghi = u < ng - 1 ? u : ng - 1;
         if (ghi < glo) continue;
         k_cb_apply<<<dim3(static_cast<unsigned>((ghi - glo + 1) * nchunk), batch), 256, 0, s>>>(
-            t, glo, nchunk, Z, static_cast<int>(n), R, n * n, Rf, Lw.nref * RFS, Tcb, tstr, ng, K0);
+            u, glo, nchunk, Z, static_cast<int>(n), R, n * n, Rf, Lw.nref * RFS, Tcb, tstr, ng, K0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
       }
     }
