@@ -381,7 +381,8 @@ typedef struct {
  * around each launch of a selected kernel on its stream (host objects, no
  * device memory).  Not safe with concurrent hot-path calls on other
  * streams.  Kernel names: "qr_panel", "qr_update" (block reflectors applied
- * to tall blocks), "gemm" (fp32 matrix-core products), "gemm_bf16" (bf16
+ * to tall blocks), "cholqr" (CholeskyQR of the factors, with its products as
+ * "cholqr_gemm"), "gemm" (fp32 matrix-core products), "gemm_bf16" (bf16
  * matrix-core products), "band", "chase", "tri_eig", "chase_back",
  * "band_back" (the eigensolver stages), "gram" (the Grams), "encode_w",
  * "encode_residual", "quantize", "decode_w", "decode", "attend". */

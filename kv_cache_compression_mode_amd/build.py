@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libjolt.so")
-SOURCES = ["gemm.hip", "qr.hip", "tridiag.hip", "codec.hip", "attn.hip", "host.hip"]
+SOURCES = ["gemm.hip", "qr.hip", "tridiag.hip", "codec.hip", "attn.hip", "host.hip", "plan.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
