@@ -826,115 +826,153 @@ __global__ __launch_bounds__(256) void k_cb_apply(int u, int glo, int nchunk, fl
   }
 }
 
-// Panel back-transformation, one launch per panel: Z_r <- (I - V T V^T) Z_r
-// for rows r .. n-1 of the eigenvector block, one workgroup per 64 columns of
-// Z and matrix.  Pass 1 accumulates W = V^T Z_r (32 x 64) over 64-row chunks,
-// W2 = T W, pass 2 streams the chunks again and subtracts V W2; both on fp32
-// matrix cores, the next chunk loaded into registers during the current one.
-__global__ __launch_bounds__(256) void k_apply_wy(float* Z, int64_t n, int64_t z_batch, int64_t r0, int64_t mp,
-                                                  int R, const float* V_g, int64_t v_batch, const float* T_g,
-                                                  int64_t t_batch) {
-  __shared__ float Vs[64][SBW + 1];      // V rows of a chunk
+// Panel back-transformation, K consecutive panels per launch: Z rows r_q ..
+// <- (I - V_q T_q V_q^T) Z rows r_q .. for q = p_hi, p_hi - 1, .., p_hi - K + 1
+// (r_q = 32 (q + 1); panel q's V is m_q x 32, m_q = n - r_q), one workgroup
+// per 64 columns of Z and matrix.  Pass 0 accumulates W = V_{p_hi}^T Z over
+// 64-row chunks; pass i streams the chunks again, subtracts V_q W2_q (W2 =
+// T W) and, from the updated chunk, accumulates the next panel's W: K + 1
+// passes over Z for K panels.  fp32 matrix cores; the next chunk is loaded
+// into registers during the current one.
+__device__ __forceinline__ int64_t panel_voff(int64_t n, int64_t q) {   // panels 0 .. q-1 stacked
+  return SBW * (q * n - SBW * q * (q + 1) / 2);
+}
+__global__ __launch_bounds__(256) void k_apply_wy(float* Z, int64_t n, int64_t z_batch, int R, const float* Vst,
+                                                  int64_t v_batch, const float* Tst, int64_t t_batch, int p_hi,
+                                                  int K) {
+  __shared__ float Vs[2][64][SBW + 1];   // chunk rows of V: [0] the panel applied, [1] the next one
   __shared__ float Zs[64][65];           // Z rows of a chunk x 64 columns
-  __shared__ float Wp[2][SBW][65];       // W partial sums (two row halves), then W2
+  __shared__ float Wp[2][SBW][65];       // W partial sums (two row halves)
+  __shared__ float W2s[SBW][65];         // W2 = T W of the panel applied
   __shared__ float Ts[SBW][SBW + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
   uint32_t bx, by;
   xcd_group_2d(bx, by);                            // the column blocks of one matrix on one XCD
   const int64_t z = by;
   const int c0 = static_cast<int>(bx) * 64, nc = min(64, R - c0);
-  float* Zr = Z + z * z_batch + r0;
-  const float* V = V_g + z * v_batch;
-  {
-    float rt[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) rt[q] = T_g[z * t_batch + tid + 256 * q];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) Ts[(tid + 256 * q) / SBW][(tid + 256 * q) % SBW] = rt[q];
-  }
-  // chunk loader: Z 64 rows x 64 columns (16 per thread), V 64 rows x 32 (8 per thread)
-  float rz[16], rv[8];
-  auto load = [&](int64_t k0) {
+  float* Zz = Z + z * z_batch;
+  const int cb = 32 * (wave & 1), kb = 32 * (wave >> 1);
+  float rz[16], rv[2][8];
+  // chunk loader: Z rows k0 .. k0 + 63 (16 per thread); V rows of panel qa
+  // (applied) and qn (next), zero outside a panel's rows (or qa / qn < 0)
+  auto load = [&](int64_t k0, int64_t zlo, int qa, int qn) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int idx = tid + 256 * q, c = idx >> 6, rr = idx & 63;
-      rz[q] = (k0 + rr < mp && c < nc) ? Zr[static_cast<int64_t>(c0 + c) * n + k0 + rr] : 0.f;
+      const int64_t row = k0 + rr;
+      rz[q] = (row >= zlo && row < n && c < nc) ? Zz[static_cast<int64_t>(c0 + c) * n + row] : 0.f;
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int idx = tid + 256 * q, c = idx >> 6, rr = idx & 63;
-      rv[q] = k0 + rr < mp ? V[static_cast<int64_t>(c) * mp + k0 + rr] : 0.f;
+    for (int b = 0; b < 2; ++b) {
+      const int pq = b == 0 ? qa : qn;
+      const int64_t rq = SBW * (pq + 1), mq = n - rq;
+      const float* V = Vst + z * v_batch + (pq >= 0 ? panel_voff(n, pq) : 0);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int idx = tid + 256 * q, c = idx >> 6, rr = idx & 63;
+        const int64_t row = k0 + rr;
+        rv[b][q] = (pq >= 0 && row >= rq && row < n) ? V[static_cast<int64_t>(c) * mq + (row - rq)] : 0.f;
+      }
     }
   };
-  auto store = [&]() {
+  auto stage = [&]() {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int idx = tid + 256 * q;
       Zs[idx & 63][idx >> 6] = rz[q];
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int idx = tid + 256 * q;
-      Vs[idx & 63][idx >> 6] = rv[q];
-    }
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int idx = tid + 256 * q;
+        Vs[b][idx & 63][idx >> 6] = rv[b][q];
+      }
   };
-  // pass 1: W = V^T Z_r; wave w: columns 32 (w & 1) .., chunk rows 32 (w >> 1) ..
-  const int cb = 32 * (wave & 1), kb = 32 * (wave >> 1);
-  f32x16 acc = {};
-  load(0);
-  for (int64_t k0 = 0; k0 < mp; k0 += 64) {
-    store();
-    __syncthreads();
-    if (k0 + 64 < mp) load(k0 + 64);
+  // W2s = T_q (W partial sums); every wave then sees it after the barrier
+  auto form_w2 = [&](const f32x16& wacc, int q) {
 #pragma unroll
-    for (int kk = 0; kk < SBW; kk += 2) {
-      const int k = kb + kk + hf;
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[k][rl], Zs[k][cb + rl], acc, 0, 0, 0);
+    for (int e = 0; e < 16; ++e) Wp[wave >> 1][(e >> 2) * 8 + hf * 4 + (e & 3)][cb + rl] = wacc[e];
+    {
+      float rt[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rt[i] = Tst[z * t_batch + static_cast<int64_t>(q) * 1024 + tid + 256 * i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ts[(tid + 256 * i) / SBW][(tid + 256 * i) % SBW] = rt[i];
     }
     __syncthreads();
+    if (wave < 2) {
+      f32x16 w2 = {};
+#pragma unroll
+      for (int kk = 0; kk < SBW; kk += 2) {
+        const int k = kk + hf;
+        w2 = __builtin_amdgcn_mfma_f32_32x32x2f32(Ts[rl][k], Wp[0][k][32 * wave + rl] + Wp[1][k][32 * wave + rl],
+                                                   w2, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) W2s[(e >> 2) * 8 + hf * 4 + (e & 3)][32 * wave + rl] = w2[e];
+    }
+    __syncthreads();
+  };
+  // pass 0: W of panel p_hi (V in slot 1 of the loader, as "next")
+  {
+    const int64_t rq = SBW * (p_hi + 1);
+    f32x16 acc = {};
+    const int64_t k0s = rq;
+    load(k0s, rq, -1, p_hi);
+    for (int64_t k0 = k0s; k0 < n; k0 += 64) {
+      stage();
+      __syncthreads();
+      if (k0 + 64 < n) load(k0 + 64, rq, -1, p_hi);
+#pragma unroll
+      for (int kk = 0; kk < SBW; kk += 2) {
+        const int k = kb + kk + hf;
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[1][k][rl], Zs[k][cb + rl], acc, 0, 0, 0);
+      }
+      __syncthreads();
+    }
+    form_w2(acc, p_hi);
   }
+  // passes 1 .. K: apply panel qa = p_hi - i + 1, accumulate W of qn = qa - 1
+  for (int i = 1; i <= K; ++i) {
+    const int qa = p_hi - i + 1, qn = i < K ? qa - 1 : -1;
+    const int64_t ra = SBW * (qa + 1);
+    const int64_t k0s = qn >= 0 ? SBW * (qn + 1) : ra;       // stream from the lower panel's first row
+    f32x16 acc = {};
+    load(k0s, k0s, qa, qn);
+    for (int64_t k0 = k0s; k0 < n; k0 += 64) {
+      stage();
+      __syncthreads();
+      if (k0 + 64 < n) load(k0 + 64, k0s, qa, qn);
+      // Z -= V_qa W2: wave w -> chunk rows 32 (w >> 1) .., columns 32 (w & 1) ..
+      f32x16 d = {};
 #pragma unroll
-  for (int e = 0; e < 16; ++e) Wp[wave >> 1][(e >> 2) * 8 + hf * 4 + (e & 3)][cb + rl] = acc[e];
-  __syncthreads();
-  // W2 = T W (waves 0, 1), into Wp[0] after the barrier
-  f32x16 w2 = {};
-  if (wave < 2) {
+      for (int kk = 0; kk < SBW; kk += 2) {
+        const int k = kk + hf;
+        d = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[0][kb + rl][k], W2s[k][cb + rl], d, 0, 0, 0);
+      }
 #pragma unroll
-    for (int kk = 0; kk < SBW; kk += 2) {
-      const int k = kk + hf;
-      w2 = __builtin_amdgcn_mfma_f32_32x32x2f32(Ts[rl][k], Wp[0][k][32 * wave + rl] + Wp[1][k][32 * wave + rl], w2,
-                                                 0, 0, 0);
+      for (int e = 0; e < 16; ++e) {
+        const int rr = kb + (e >> 2) * 8 + hf * 4 + (e & 3);
+        Zs[rr][cb + rl] -= d[e];
+      }
+      __syncthreads();
+      if (qn >= 0) {
+#pragma unroll
+        for (int kk = 0; kk < SBW; kk += 2) {
+          const int k = kb + kk + hf;
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[1][k][rl], Zs[k][cb + rl], acc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int idx = tid + 256 * q, c = idx >> 6, rr = idx & 63;
+        const int64_t row = k0 + rr;
+        if (row >= ra && row < n && c < nc) Zz[static_cast<int64_t>(c0 + c) * n + row] = Zs[rr][c];
+      }
+      __syncthreads();
     }
-  }
-  __syncthreads();
-  if (wave < 2) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) Wp[0][(e >> 2) * 8 + hf * 4 + (e & 3)][32 * wave + rl] = w2[e];
-  }
-  // pass 2: Z_r -= V W2; wave w: chunk rows 32 (w >> 1) .., columns 32 (w & 1) ..
-  load(0);
-  for (int64_t k0 = 0; k0 < mp; k0 += 64) {
-    __syncthreads();                      // W2 visible; previous chunk's Zs / Vs reads done
-    store();
-    __syncthreads();
-    if (k0 + 64 < mp) load(k0 + 64);
-    f32x16 d = {};
-#pragma unroll
-    for (int kk = 0; kk < SBW; kk += 2) {
-      const int k = kk + hf;
-      d = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[kb + rl][k], Wp[0][k][cb + rl], d, 0, 0, 0);
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int rr = kb + (e >> 2) * 8 + hf * 4 + (e & 3);
-      Zs[rr][cb + rl] -= d[e];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int idx = tid + 256 * q, c = idx >> 6, rr = idx & 63;
-      if (k0 + rr < mp && c < nc) Zr[static_cast<int64_t>(c0 + c) * n + k0 + rr] = Zs[rr][c];
-    }
+    if (qn >= 0) form_w2(acc, qn);
   }
 }
 
@@ -1497,11 +1535,12 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
       }
       prof_add_work("band_back", batch * by, batch * fl);
     }
-    for (int64_t p = Lw.P - 1; p >= 0; --p) {
-      const int64_t r = (p + 1) * SBW, mp = n - r;
-      // Z rows r.. <- (I - V T V^T) Z rows r..
+    // K panels per launch, from the last panel down
+    constexpr int KBB = 4;
+    for (int64_t p = Lw.P - 1; p >= 0; p -= KBB) {
+      const int K = static_cast<int>(p + 1 < KBB ? p + 1 : KBB);
       k_apply_wy<<<dim3(static_cast<unsigned>((R + 63) / 64), batch), 256, 0, s>>>(
-          Z, n, nn, r, mp, R, Vst + voff[p], Lw.vtot, Tst + p * 1024, Lw.P * 1024);
+          Z, n, nn, R, Vst, Lw.vtot, Tst, Lw.P * 1024, static_cast<int>(p), K);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
