@@ -663,14 +663,18 @@ __global__ __launch_bounds__(256) void k_sumsq(const void* const* xs, int64_t n,
   if (threadIdx.x == 0) atomicAdd(out + blockIdx.y, part[0] + part[1] + part[2] + part[3]);
 }
 
-// Gaussian sketch: out[z][i][j] = N(seed, tag ^ (layer<<8|kind), i*cols + j), fp32.
+// Gaussian sketch, stored column-major: element (i, j) of the rows x cols
+// matrix is N(seed, tag ^ (layer<<8|kind), i*cols + j) at out[z][j][i], fp32
+// (its product with the token unfolding then reads it k-contiguous).
 __global__ __launch_bounds__(256) void k_sketch(float* out, int64_t rows, int64_t cols,
                                                  uint64_t seed, const uint64_t* tags) {
   const int64_t n = rows * cols;
   const uint64_t key = mix64(seed ^ tags[blockIdx.y]);
   float* o = out + blockIdx.y * n;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += 256ll * gridDim.x)
-    o[i] = static_cast<float>(rng_normal(key, static_cast<uint64_t>(i)));
+  for (int64_t o_idx = blockIdx.x * 256ll + threadIdx.x; o_idx < n; o_idx += 256ll * gridDim.x) {
+    const int64_t j = o_idx / rows, i = o_idx - j * rows;
+    o[o_idx] = static_cast<float>(rng_normal(key, static_cast<uint64_t>(i * cols + j)));
+  }
 }
 
 // fp32 [rows][ld_in] (first `cols` columns) -> bf16 [rows][cols], RNE.
@@ -806,7 +810,7 @@ void launch_x_b(const GemmArgs& g, int xb, dim3 grid, hipStream_t s) {
   if (xb == kOpBfK) k_gemm_x<AM, kOpBfK><<<grid, 256, 0, s>>>(g);
   else if (xb == kOpBfM) k_gemm_x<AM, kOpBfM><<<grid, 256, 0, s>>>(g);
   else if (xb == kOpF32K) k_gemm_x<AM, kOpF32K><<<grid, 256, 0, s>>>(g);
-  else if constexpr (AM == kOpF32K) k_gemm_x<kOpF32K, kOpF32M><<<grid, 256, 0, s>>>(g);
+  else k_gemm_x<AM, kOpF32M><<<grid, 256, 0, s>>>(g);
 }
 
 }  // namespace
@@ -843,11 +847,9 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s, const char*
     }
     const int xa = x_mode(x.a_dtype, x.am, x.ak, x.M, x.K, x.a_ptrs != nullptr, x.ptr_align16 != 0, x.A, x.a_batch);
     const int xb = x_mode(x.b_dtype, x.bn, x.bk, x.N, x.K, x.b_ptrs != nullptr, x.ptr_align16 != 0, x.B, x.b_batch);
-    // an fp32 operand pairs with bf16 only when it is k contiguous; two fp32
-    // operands (split_f32) need one of them k contiguous
+    // two fp32 operands (split_f32) need one of them k contiguous
     const bool fa = xa == kOpF32K || xa == kOpF32M, fb = xb == kOpF32K || xb == kOpF32M;
-    const bool pair_ok = xa >= 0 && xb >= 0 && (fa && fb ? (xa == kOpF32K || xb == kOpF32K) && g.split_f32
-                                                         : xa != kOpF32M && xb != kOpF32M);
+    const bool pair_ok = xa >= 0 && xb >= 0 && (!(fa && fb) || ((xa == kOpF32K || xb == kOpF32K) && g.split_f32));
     if (pair_ok) {
       x.kchunk = (x.K + x.ksplit - 1) / x.ksplit;
       x.kchunk = (x.kchunk + XK - 1) / XK * XK;
@@ -865,6 +867,8 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s, const char*
       else if (xa == kOpBfM) launch_x_b<kOpBfM>(x, xb, grid, s);
       else if (xa == kOpF32K && xb == kOpF32K && x.split_f32 == 2) k_gemm_x<kOpF32K, kOpF32K, 3><<<grid, 256, 0, s>>>(x);
       else if (xa == kOpF32K) launch_x_b<kOpF32K>(x, xb, grid, s);
+      else if (xb == kOpBfK) k_gemm_x<kOpF32M, kOpBfK><<<grid, 256, 0, s>>>(x);
+      else if (xb == kOpBfM) k_gemm_x<kOpF32M, kOpBfM><<<grid, 256, 0, s>>>(x);
       else k_gemm_x<kOpF32M, kOpF32K><<<grid, 256, 0, s>>>(x);
       if (x.ksplit > 1) k_splitk_reduce<<<dim3(grid1(x.M * x.N), batch), 256, 0, s>>>(x);
       return hipGetLastError();

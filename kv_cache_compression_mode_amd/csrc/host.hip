@@ -573,7 +573,7 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     g.C = out; g.c_m = 1; g.c_n = T; g.c_batch = T * ell;
     ck(launch_gemm(g, batch, s));
   };
-  AY(w.Om, ell, true, w.Y);
+  AY(w.Om, HD, false, w.Y);                 // the sketch is column-major (k contiguous)
   ck(householder_qr(w.Y, T, ell, T, T * ell, batch, w.qtau, s));
   for (int it = 0; it < q; ++it) {
     GemmArgs g = gemm0();                       // Z = X_(T)^T Q (HD x ell, column-major)

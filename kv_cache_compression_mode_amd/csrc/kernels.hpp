@@ -67,6 +67,8 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs& g, int batch, hipStream_t s, const char* scope = nullptr);
 hipError_t launch_sumsq(const void* const* xs_dev, int ntensors, int64_t n, int dtype, double* out,
                         hipStream_t s);
+// Gaussian sketch per tensor, column-major [cols][rows] (element (i, j) is
+// normal number i * cols + j of the tensor's stream).
 hipError_t launch_sketch(float* out, int64_t rows, int64_t cols, uint64_t seed, const uint64_t* tags,
                          int ntensors, hipStream_t s);
 hipError_t launch_to_bf16(const float* in, int64_t ld_in, uint16_t* out, int64_t rows, int64_t cols,
