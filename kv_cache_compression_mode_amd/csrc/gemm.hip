@@ -104,7 +104,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   for (int i = 0; i < 16; ++i) {
     const int64_t m = m0 + wm + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
     const int64_t n = n0 + wn + (lane & 31);
-    cold[i] = (rd_c && kept(m, n)) ? reinterpret_cast<const float*>(Cb)[cz + m * g.c_m + n * g.c_n] : 0.f;
+    const float* Cr = g.c_in ? g.c_in : reinterpret_cast<const float*>(Cb);
+    cold[i] = (rd_c && kept(m, n)) ? Cr[cz + m * g.c_m + n * g.c_n] : 0.f;
   }
   if (kbeg < kend) load(kbeg);
   for (int64_t k0 = kbeg; k0 < kend; k0 += FK) {
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
       const int64_t off = cz + m * g.c_m + n * g.c_n;
       if (g.c_dtype == kF32) {
         float* C = reinterpret_cast<float*>(Cb);
-        if (g.beta != 0.f) v += g.beta * C[off];
+        if (g.beta != 0.f) v += g.beta * (g.c_in ? g.c_in : C)[off];
         C[off] = v;
       } else {
         uint16_t* C = reinterpret_cast<uint16_t*>(Cb);
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
     const int64_t off = (g.c_ptrs ? 0 : z * g.c_batch) + m * g.c_m + n * g.c_n;
     if (g.c_dtype == kF32) {
       float* C = static_cast<float*>(Cz);
-      if (g.beta != 0.f) v += g.beta * C[off];
+      if (g.beta != 0.f) v += g.beta * (g.c_in ? g.c_in : C)[off];
       C[off] = v;
     } else {
       static_cast<uint16_t*>(Cz)[off] = f32_to_bf16_rne(v);
@@ -296,9 +297,11 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
 // Large products on bf16 matrix cores: 128 x 128 output tiles, K tiles of 64,
 // four waves of 64 x 64 (2 x 2 blocks of MFMA 32x32x16).  LDS keeps each
 // operand tile k-contiguous per row ([row][k], 144-byte rows) with the
-// 16-byte chunk index XOR-swizzled by (row / 8) % 8, which keeps the fragment
-// reads (one chunk per lane) and the transposing writes free of bank
-// conflicts.  Operands in memory:
+// 16-byte chunk index XOR-swizzled by (row / 16) % 8.  The fragment reads
+// (one chunk per lane, sixteen consecutive rows per sixteen lanes) then see
+// one swizzle and the odd 144-byte stride alone, which puts sixteen rows on
+// sixteen distinct 16-byte bank groups; the transposing writes (rows 8 apart
+// across lanes) are spread by the swizzle.  Operands in memory:
 //   kOpBfK   bf16, k contiguous: 16-byte loads along k;
 //   kOpBfM   bf16, rows contiguous: 16-byte loads along the rows, transposed
 //            in registers (four k by eight rows per thread) on the way to LDS;
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
 constexpr int XT = 128, XK = 64, XKP = XK + 8;
 enum { kOpBfK = 0, kOpBfM = 1, kOpF32K = 2, kOpF32M = 3 };
 
-__device__ __forceinline__ int xswz(int row, int chunk) { return chunk ^ ((row >> 3) & 7); }
+__device__ __forceinline__ int xswz(int row, int chunk) { return chunk ^ ((row >> 4) & 7); }
 
 template <int MODE> struct XRegs { uint4 v[4]; };
 template <> struct XRegs<kOpF32K> { float4 v[8]; };
@@ -378,7 +381,8 @@ __device__ __forceinline__ void x_next(XAddr& a, const GemmDim& kd) {
 template <int MODE>
 __device__ __forceinline__ void x_load(XRegs<MODE>& R, const XAddr& a, const GemmDim& kd) {
   constexpr int64_t E = MODE == kOpF32K || MODE == kOpF32M ? 4 : 2;
-  const int so = static_cast<int>(E * x_koff(kd, a));
+  // the K tile's offset is the same in every lane: a scalar operand
+  const int so = __builtin_amdgcn_readfirstlane(static_cast<int>(E * x_koff(kd, a)));
   if constexpr (MODE == kOpF32K || MODE == kOpF32M) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -518,35 +522,50 @@ __global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
   x_addr<BMODE>(pb, Bb, g.bn, g.bk, n0, g.N, kbeg, tid);
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   const int r = lane & 31, half = lane >> 5;
+  // in-order chunk sums (seq_len > 0) only where A is bf16: the launcher
+  // never asks them of an fp32 A, whose kernels keep those 64 registers
+  constexpr bool SEQ = !AS;
   f32x16 acc[2][2] = {};
-  f32x16 sum[2][2] = {};          // seq_len > 0: the finished chunks, added in order
-  XRegs<AM> ra;
-  XRegs<BMODE> rb;
+  f32x16 sum[SEQ ? 2 : 1][SEQ ? 2 : 1] = {};   // the finished chunks, added in order
+  // K tiles in flight: two register stages where the registers allow (a
+  // stage is 16 registers per bf16 operand, 32 per fp32 one), so that a
+  // tile's global loads have two tiles of matrix-core work to arrive in
+  constexpr int PF = !BS ? 2 : 1;
+  XRegs<AM> ra[PF];
+  XRegs<BMODE> rb[PF];
+  // Every tile issues its stage's loads: past the last tile the address
+  // stays on the last one (a harmless reload), so that the loads and their
+  // waits follow one pattern on every path through the loop.
   if (kbeg < kend) {
-    x_load<AM>(ra, pa, g.ak);
-    x_load<BMODE>(rb, pb, g.bk);
+#pragma unroll
+    for (int st = 0; st < PF; ++st) {
+      if (st > 0 && kbeg + st * XK < kend) { x_next(pa, g.ak); x_next(pb, g.bk); }
+      x_load<AM>(ra[st], pa, g.ak);
+      x_load<BMODE>(rb[st], pb, g.bk);
+    }
   }
-  for (int64_t k0 = kbeg; k0 < kend; k0 += XK) {
-    x_store<AM, NP>(ra, As[0], As[AS ? 1 : 0], As[AS ? NP - 1 : 0], tid);
-    x_store<BMODE, NP>(rb, Bs[0], Bs[BS ? 1 : 0], Bs[BS ? NP - 1 : 0], tid);
+  int64_t seq_left = g.seq_len;   // K left in the current chunk
+  auto tile = [&](XRegs<AM>& ra_, XRegs<BMODE>& rb_, int64_t k0) {
+    x_store<AM, NP>(ra_, As[0], As[AS ? 1 : 0], As[AS ? NP - 1 : 0], tid);
+    x_store<BMODE, NP>(rb_, Bs[0], Bs[BS ? 1 : 0], Bs[BS ? NP - 1 : 0], tid);
     __syncthreads();
-    if (k0 + XK < kend) {
+    if (k0 + PF * XK < kend) {
       x_next(pa, g.ak);
       x_next(pb, g.bk);
-      x_load<AM>(ra, pa, g.ak);
-      x_load<BMODE>(rb, pb, g.bk);
     }
+    x_load<AM>(ra_, pa, g.ak);
+    x_load<BMODE>(rb_, pb, g.bk);
 #pragma unroll
     for (int kk = 0; kk < XK / 16; ++kk) {
       const int ch = 2 * kk + half;
       bf16x8 a[2], b[2], al[2], bl[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int ra_ = wm + 32 * i + r, rb_ = wn + 32 * i + r;
-        a[i] = *reinterpret_cast<const bf16x8*>(&As[0][ra_][xswz(ra_, ch) * 8]);
-        b[i] = *reinterpret_cast<const bf16x8*>(&Bs[0][rb_][xswz(rb_, ch) * 8]);
-        if constexpr (AS) al[i] = *reinterpret_cast<const bf16x8*>(&As[AS ? 1 : 0][ra_][xswz(ra_, ch) * 8]);
-        if constexpr (BS) bl[i] = *reinterpret_cast<const bf16x8*>(&Bs[BS ? 1 : 0][rb_][xswz(rb_, ch) * 8]);
+        const int ra_r = wm + 32 * i + r, rb_r = wn + 32 * i + r;
+        a[i] = *reinterpret_cast<const bf16x8*>(&As[0][ra_r][xswz(ra_r, ch) * 8]);
+        b[i] = *reinterpret_cast<const bf16x8*>(&Bs[0][rb_r][xswz(rb_r, ch) * 8]);
+        if constexpr (AS) al[i] = *reinterpret_cast<const bf16x8*>(&As[AS ? 1 : 0][ra_r][xswz(ra_r, ch) * 8]);
+        if constexpr (BS) bl[i] = *reinterpret_cast<const bf16x8*>(&Bs[BS ? 1 : 0][rb_r][xswz(rb_r, ch) * 8]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -558,31 +577,42 @@ __global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
           if constexpr (AS && BS)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bl[j], acc[i][j], 0, 0, 0);
           if constexpr (NP == 3) {
-            const int ra_ = wm + 32 * i + r, rb_ = wn + 32 * j + r;
-            const bf16x8 a3 = *reinterpret_cast<const bf16x8*>(&As[NP - 1][ra_][xswz(ra_, ch) * 8]);
-            const bf16x8 b3 = *reinterpret_cast<const bf16x8*>(&Bs[NP - 1][rb_][xswz(rb_, ch) * 8]);
+            const int ra_r = wm + 32 * i + r, rb_r = wn + 32 * j + r;
+            const bf16x8 a3 = *reinterpret_cast<const bf16x8*>(&As[NP - 1][ra_r][xswz(ra_r, ch) * 8]);
+            const bf16x8 b3 = *reinterpret_cast<const bf16x8*>(&Bs[NP - 1][rb_r][xswz(rb_r, ch) * 8]);
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b[j], acc[i][j], 0, 0, 0);
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b3, acc[i][j], 0, 0, 0);
           }
         }
     }
-    if (g.seq_len > 0 && ((k0 + XK - kbeg) % g.seq_len == 0 || k0 + XK >= kend)) {
-      // a chunk done: sum = ((0 + c0) + c1) + ..., the order of the split-K reduction
+    if (SEQ && g.seq_len > 0) {
+      seq_left -= XK;
+      if (seq_left == 0 || k0 + XK >= kend) {
+        // a chunk done: sum = ((0 + c0) + c1) + ..., the order of the split-K reduction
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          sum[i][j] += acc[i][j];
-          acc[i][j] = f32x16{};
-        }
+          for (int j = 0; j < 2; ++j) {
+            sum[SEQ ? i : 0][SEQ ? j : 0] += acc[i][j];
+            acc[i][j] = f32x16{};
+          }
+        seq_left = g.seq_len;
+      }
     }
     __syncthreads();
-  }
-  if (g.seq_len > 0) {
+  };
+  int64_t k0 = kbeg;
+  if constexpr (PF == 2)
+    for (; k0 + XK < kend; k0 += 2 * XK) {
+      tile(ra[0], rb[0], k0);
+      tile(ra[PF - 1], rb[PF - 1], k0 + XK);
+    }
+  for (; k0 < kend; k0 += XK) tile(ra[0], rb[0], k0);
+  if (SEQ && g.seq_len > 0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = sum[i][j];
+      for (int j = 0; j < 2; ++j) acc[i][j] = sum[SEQ ? i : 0][SEQ ? j : 0];
   }
   if (g.ksplit > 1) {   // partial sums, reduced in a fixed order by k_splitk_reduce
     float* Pp = g.partial + (z * g.ksplit + kz) * g.M * g.N;
@@ -614,7 +644,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
           const int64_t off = cz + m * g.c_m + n * g.c_n;
           if (g.c_dtype == kF32) {
             float* C = reinterpret_cast<float*>(Cb);
-            if (g.beta != 0.f) v += g.beta * C[off];
+            if (g.beta != 0.f) v += g.beta * (g.c_in ? g.c_in : C)[off];
             C[off] = v;
           } else {
             reinterpret_cast<uint16_t*>(Cb)[off] = f32_to_bf16_rne(v);
@@ -817,6 +847,7 @@ void launch_x_b(const GemmArgs& g, int xb, dim3 grid, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s, const char* scope) {
   GemmArgs g = g0;
+  if (g.c_in && (g.c_ptrs || g.c_dtype != kF32)) return hipErrorInvalidValue;
   if (g.ksplit < 1 || !g.partial) g.ksplit = 1;
   // algorithmic work: operands read once, C written (and read when beta != 0)
   // once; 2 M N K flops, or for a triangle-only output (a symmetric product
@@ -854,7 +885,8 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s, const char*
       x.kchunk = (x.K + x.ksplit - 1) / x.ksplit;
       x.kchunk = (x.kchunk + XK - 1) / XK * XK;
       x.seq_len = 0;
-      if (x.split_seq && x.ksplit > 1) {            // the chunks in one workgroup, summed in order
+      // the chunks in one workgroup, summed in order (kernels with a bf16 A)
+      if (x.split_seq && x.ksplit > 1 && (xa == kOpBfK || xa == kOpBfM)) {
         x.seq_len = x.kchunk;
         x.ksplit = 1;
         x.kchunk = x.K;

@@ -27,7 +27,7 @@ struct GemmDim {
 inline GemmDim plain(int64_t stride) { return GemmDim{INT64_MAX, 0, stride}; }
 inline GemmDim segmented(int64_t len, int64_t seg, int64_t stride) { return GemmDim{len, seg, stride}; }
 
-// C[z](m, n) = alpha * sum_k A[z](m, k) B[z](k, n) * col_scale[z][n] + beta * C[z](m, n)
+// C[z](m, n) = alpha * sum_k A[z](m, k) B[z](k, n) * col_scale[z][n] + beta * C[z](m, n) (or c_in)
 struct GemmArgs {
   int64_t M, N, K;
   const void* A; int a_dtype; GemmDim am, ak; int64_t a_batch;
@@ -36,6 +36,9 @@ struct GemmArgs {
   const void* const* b_ptrs;
   void* C; int c_dtype; int64_t c_m, c_n, c_batch;
   void* const* c_ptrs;         // optional device array: output base per batch entry
+  // optional fp32 source of the beta term, laid out as C (plain C only):
+  // C = alpha A B + beta c_in, so that C need not hold a copy beforehand
+  const float* c_in;
   float alpha, beta;
   const float* col_scale; int64_t col_scale_batch;
   // split-K: ksplit > 1 writes partial sums to `partial` ([batch][ksplit][M][N]

@@ -1287,20 +1287,12 @@ hipError_t cholesky_qr(float* U, float* U2, int64_t m, int64_t k, int64_t ld, in
     if ((e = launch_gemm(g, batch, s, "cholqr_gemm")) != hipSuccess) return e;
     k_chol_inv<<<batch, CW * 64, 0, s>>>(G, k * k, static_cast<int>(k), 0x1p-10f, Li, k * k, pass, status);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (pass == 1) {
-      // dst = src, then dst += src (L^{-1} - I)^T
-      if (bstride == ld * k) {
-        e = hipMemcpyAsync(dst, src, sizeof(float) * batch * bstride, hipMemcpyDeviceToDevice, s);
-      } else {
-        e = hipMemcpy2DAsync(dst, sizeof(float) * bstride, src, sizeof(float) * bstride, sizeof(float) * ld * k,
-                             batch, hipMemcpyDeviceToDevice, s);
-      }
-      if (e != hipSuccess) return e;
-    }
-    // dst (+)= src B, B(j, n) = L^{-1}[n][j] (pass 2: minus the identity)
+    // dst = src B, B(j, n) = L^{-1}[n][j]; pass 2: dst = src + src (B - I),
+    // the identity's term read from src in the product's epilogue
     GemmArgs q{};
     q.alpha = 1.f;
     q.beta = pass == 0 ? 0.f : 1.f;
+    q.c_in = pass == 0 ? nullptr : src;
     q.a_dtype = q.b_dtype = q.c_dtype = kF32;
     q.M = m; q.N = k; q.K = k;
     q.A = src; q.am = plain(1); q.ak = plain(ld); q.a_batch = bstride;
