@@ -184,7 +184,7 @@ constexpr int RT = kLeaf / 2, RW = RT / 64;
 struct QrRegLds {
   float xs[kLeaf] __attribute__((aligned(16)));   // column j, rows > j
   float rowj[2][32];                              // row j, by the parity of j
-  float red[RW][32];
+  float red[2][RW][32];                           // per-wave partial dots, by the parity of j
   float St[32][33];                               // St[j][l] = v_l^T v_j (l < j)
   float Tl[32][33];
   float Rl[32][33];                               // rows of R
@@ -200,7 +200,7 @@ __device__ float qr_reg_factor(float (&p)[64], int mr, int nb, QrRegLds& L) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int c = t & 31, g = t >> 5, rb = 64 * g;
   const bool live = 128 * wave < mr;
-  if (!live && lane < 32) L.red[wave][c] = 0.f;                  // waves past the panel add nothing
+  if (!live && lane < 32) L.red[0][wave][c] = L.red[1][wave][c] = 0.f;   // waves past the panel add nothing
   float vscale = 0.f;                                          // scale of this column's reflector
 #pragma clang loop unroll(disable)
   for (int j = 0; j < nb; ++j) {
@@ -230,7 +230,12 @@ __device__ float qr_reg_factor(float (&p)[64], int mr, int nb, QrRegLds& L) {
       }
       L.rowj[par][c] = a[0];
     }
-    __syncthreads();
+    // x sits in the wave's own rows (its two row blocks), published by its
+    // own lanes: a wave-level sync orders it.  Row j and the partial dots
+    // cross waves and are read after the barrier below; both are kept by
+    // the parity of j, so a wave that runs ahead into column j + 1 writes
+    // the other copy while slower waves still read column j's.
+    wave_lds_sync();
     float x[64];
     if (live) {
       float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
@@ -244,14 +249,14 @@ __device__ float qr_reg_factor(float (&p)[64], int mr, int nb, QrRegLds& L) {
         s3 += q.w * p[r + 3];
       }
       const float part = half_sum((s0 + s1) + (s2 + s3));
-      if (lane < 32) L.red[wave][c] = part;
+      if (lane < 32) L.red[par][wave][c] = part;
     }
     __syncthreads();
     float raw = 0.f, sigma = 0.f;
 #pragma unroll
     for (int w = 0; w < RW; ++w) {
-      raw += L.red[w][c];
-      sigma += L.red[w][j];
+      raw += L.red[par][w][c];
+      sigma += L.red[par][w][j];
     }
     const float alpha = L.rowj[par][j];
     float tau = 0.f, beta = alpha, scale = 0.f;
@@ -312,8 +317,9 @@ __device__ float qr_reg_factor(float (&p)[64], int mr, int nb, QrRegLds& L) {
 // alpha = P[j][j], tau, beta and d_c = v^T P[:, c] = P[j][c] + scale x^T
 // P[:, c] for its own column.  Columns right of j take P -= tau v d^T; column
 // j keeps x below the diagonal (v = scale_j x, scaled when V is written) and
-// beta on it, so for c < j, v_c^T v_j = scale_c d_c is kept for T.  Two barriers per column; waves whose rows all lie past the panel
-// skip the arithmetic.  T follows the factorization by the forward
+// beta on it, so for c < j, v_c^T v_j = scale_c d_c is kept for T.  One
+// barrier per column (x reaches the threads of its own wave only); waves
+// whose rows all lie past the panel skip the arithmetic.  T follows the factorization by the forward
 // recurrence, T[t][j] = -tau_j sum_{t <= l < j} T[t][l] (v_l^T v_j), T[j][j]
 // = tau_j.  Outputs are those of k_qr_block mode 0, plus (write_r) R in the
 // panel's top rows.
