@@ -1536,7 +1536,7 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
       prof_add_work("band_back", batch * by, batch * fl);
     }
     // K panels per launch, from the last panel down
-    constexpr int KBB = 4;
+    constexpr int KBB = 8;
     for (int64_t p = Lw.P - 1; p >= 0; p -= KBB) {
       const int K = static_cast<int>(p + 1 < KBB ? p + 1 : KBB);
       k_apply_wy<<<dim3(static_cast<unsigned>((R + 63) / 64), batch), 256, 0, s>>>(
