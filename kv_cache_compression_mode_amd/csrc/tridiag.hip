@@ -630,9 +630,12 @@ __global__ __launch_bounds__(256) void k_invit_out(const double* y_g, const doub
 // (g' = 0 for the last group) orders; blocks of one t touch disjoint rows.
 constexpr int CBR = 2 * SBW;      // staircase rows (63) padded to 64
 
-// T of every block: one wave per (G, s).  S = V^T V on fp32 matrix cores
+// V T of every block: one wave per (G, s).  S = V^T V on fp32 matrix cores
 // (the 64 x 32 staircase), then the recurrence with row `lane` of T in
-// registers (lanes 0..31), unrolled so that every S read is independent.
+// registers (lanes 0..31), unrolled so that every S read is independent;
+// the block is stored as V T (64 x 32, row-major), which its application
+// multiplies by V^T Z (so that T is applied once per block, not once per
+// block and column chunk).
 __global__ __launch_bounds__(64) void k_cb_tfac(const float* Rf_g, int64_t rf_stride, int n, int K0, float* Tg,
                                                 int64_t t_stride) {
   __shared__ float Vs[CBR][SBW + 1];     // staircase V[r][i]
@@ -674,8 +677,8 @@ __global__ __launch_bounds__(64) void k_cb_tfac(const float* Rf_g, int64_t rf_st
 #pragma unroll
   for (int e = 0; e < 16; ++e) S[(e >> 2) * 8 + hf * 4 + (e & 3)][rl] = acc[e];
   __syncthreads();
+  float tr[SBW];
   if (lane < SBW) {
-    float tr[SBW];
 #pragma unroll
     for (int i = 0; i < SBW; ++i) {
       float u = 0.f;
@@ -684,9 +687,26 @@ __global__ __launch_bounds__(64) void k_cb_tfac(const float* Rf_g, int64_t rf_st
         if (p >= lane) u += tr[p] * S[p][i];
       tr[i] = i < lane ? 0.f : (i == lane ? tau[i] : -tau[i] * u);
     }
-    float* Tb = Tg + z * t_stride + static_cast<int64_t>(blk) * SBW * SBW + lane * SBW;
+  }
+  // V T (64 x 32), the product the blocks are applied with: T through LDS
+  // (row `lane` from its lane), then two 32 x 32 tiles on fp32 matrix cores
+  __syncthreads();                                 // every read of S done
+  if (lane < SBW) {
 #pragma unroll
-    for (int i = 0; i < SBW; ++i) Tb[i] = tr[i];
+    for (int i = 0; i < SBW; ++i) S[lane][i] = tr[i];
+  }
+  __syncthreads();
+  float* VTb = Tg + z * t_stride + static_cast<int64_t>(blk) * CBR * SBW;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    f32x16 vt = {};
+#pragma unroll
+    for (int kk = 0; kk < SBW; kk += 2) {
+      const int k = kk + hf;
+      vt = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[32 * t + rl][k], S[k][rl], vt, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) VTb[(32 * t + (e >> 2) * 8 + hf * 4 + (e & 3)) * SBW + rl] = vt[e];
   }
 }
 
@@ -695,16 +715,16 @@ __global__ __launch_bounds__(64) void k_cb_tfac(const float* Rf_g, int64_t rf_st
 // exist), applied in that order to the 95 rows they span, kept in LDS.  The
 // blocks of group g' - 1 that overlap them have s' <= s0 + 1, so they ran
 // in launches u' < u; the row spans of one launch are disjoint.  Per block:
-// W = V^T Z_rows (K split over two wave pairs), W2 = T W, Z_rows -= V W2,
-// on fp32 matrix cores (32x32x2) from LDS.
+// W = V^T Z_rows (K split over two wave pairs), Z_rows -= (V T) W, on fp32
+// matrix cores (32x32x2) from LDS.
 constexpr int CBW = CBR + SBW;    // window rows of a block pair (95, padded to 96)
 __global__ __launch_bounds__(256) void k_cb_apply(int u, int glo, int nchunk, float* Z, int n, int R,
                                                   int64_t z_batch, const float* Rf_g, int64_t rf_stride,
                                                   const float* Tg, int64_t t_stride, int ng, int K0) {
   __shared__ float Vs[2][CBR][SBW + 1];  // staircases V[r][i] of the two blocks
-  __shared__ float Ts[2][SBW][SBW + 1];
+  __shared__ float VTs[2][CBR][SBW + 1]; // V T of the two blocks
   __shared__ float Zs[CBW][65];          // window rows x 64 columns
-  __shared__ float Wp[2][SBW][65];       // W partial sums, then W2 = T W (in Wp[0])
+  __shared__ float Wp[2][SBW][65];       // W partial sums (two halves of the rows)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
   uint32_t bx, by;
   xcd_group_2d(bx, by);                            // the blocks of one matrix on one XCD
@@ -725,17 +745,18 @@ __global__ __launch_bounds__(256) void k_cb_apply(int u, int glo, int nchunk, fl
   float* Zz = Z + z * z_batch;
   const int last = n - 3;
   // one phase of loads, every load in flight before the first LDS write: the
-  // T factors, Z, the staircases V[i + r][i] = v_r of sweep jg + i; zeros off
-  // the staircases (disjoint positions)
-  float rt[2][4], rz[24], rv[2][4];
+  // blocks' V T, Z, the staircases V[i + r][i] = v_r of sweep jg + i; zeros
+  // off the staircases (disjoint positions)
+  float rt[2][8], rz[24], rv[2][4];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int sb = s0 + b;
     const bool ok = b == 0 ? has0 : has1;
-    const float* tb = Tg + z * t_stride + (static_cast<int64_t>(G) * K0 + (ok ? sb : 0)) * SBW * SBW;
+    const float* tb = Tg + z * t_stride + (static_cast<int64_t>(G) * K0 + (ok ? sb : 0)) * CBR * SBW;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) rt[b][q] = ok ? tb[tid + 256 * q] : 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      rt[b][q] = ok ? tb[tid + 256 * q] : 0.f;
       const int idx = tid + 256 * q, i = idx / SBW, r = idx % SBW, j = jg + i;
       rv[b][q] = (ok && j <= last && sb < sweep_steps(n, j)) ? Rf[(sweep_offset(n, j) + sb) * RFS + r] : 0.f;
     }
@@ -750,14 +771,19 @@ __global__ __launch_bounds__(256) void k_cb_apply(int u, int glo, int nchunk, fl
     if (row < i || row >= i + SBW) Vs[b][row][i] = 0.f;
   }
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int idx = tid + 256 * q;
+      VTs[b][idx / SBW][idx % SBW] = rt[b][q];
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int idx = tid + 256 * q;
-      Ts[b][idx / SBW][idx % SBW] = rt[b][q];
       const int i = idx / SBW, r = idx % SBW;
       Vs[b][i + r][i] = rv[b][q];
     }
+  }
 #pragma unroll
   for (int q = 0; q < 24; ++q) {
     const int idx = tid + 256 * q;
@@ -781,30 +807,15 @@ __global__ __launch_bounds__(256) void k_cb_apply(int u, int glo, int nchunk, fl
       for (int e = 0; e < 16; ++e) Wp[wave >> 1][(e >> 2) * 8 + hf * 4 + (e & 3)][cb + rl] = acc[e];
     }
     __syncthreads();
-    // W2 = T W (T upper), waves 0 and 1; W2 overwrites Wp[0] after the barrier
-    f32x16 w2 = {};
-    if (wave < 2) {
-      const int cb = 32 * wave;
-#pragma unroll
-      for (int kk = 0; kk < SBW; kk += 2) {
-        const int k = kk + hf;
-        w2 = __builtin_amdgcn_mfma_f32_32x32x2f32(Ts[b][rl][k], Wp[0][k][cb + rl] + Wp[1][k][cb + rl], w2, 0, 0, 0);
-      }
-    }
-    __syncthreads();
-    if (wave < 2) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) Wp[0][(e >> 2) * 8 + hf * 4 + (e & 3)][32 * wave + rl] = w2[e];
-    }
-    __syncthreads();
-    // Z_rows -= V W2: wave w -> rows 32 (w >> 1) .., columns 32 (w & 1) ..
+    // Z_rows -= (V T) W: wave w -> rows 32 (w >> 1) .., columns 32 (w & 1) ..
     {
       const int rbk = 32 * (wave >> 1), cb = 32 * (wave & 1);
       f32x16 acc = {};
 #pragma unroll
       for (int kk = 0; kk < SBW; kk += 2) {
         const int k = kk + hf;
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[b][rbk + rl][k], Wp[0][k][cb + rl], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(VTs[b][rbk + rl][k], Wp[0][k][cb + rl] + Wp[1][k][cb + rl], acc,
+                                                   0, 0, 0);
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -1314,7 +1325,7 @@ SyevLayout syev_layout(int64_t n, int R, int batch) {
   L.nrm_off = take(B * R * 8);
   L.ng = (n - 2 + SBW - 1) / SBW;
   L.K0 = sweep_steps(n, 0);
-  L.cbt_off = take(B * (L.ng > 0 ? L.ng : 1) * (L.K0 > 0 ? L.K0 : 1) * SBW * SBW * 4);
+  L.cbt_off = take(B * (L.ng > 0 ? L.ng : 1) * (L.K0 > 0 ? L.K0 : 1) * CBR * SBW * 4);
   L.sp_off = take(B * ((n + SY - 1) / SY) * 1024 * 4);
   L.total = off;
   return L;
@@ -1500,7 +1511,7 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
   {
     float* Tcb = reinterpret_cast<float*>(wb + Lw.cbt_off);
     const int ng = static_cast<int>(Lw.ng), K0 = static_cast<int>(Lw.K0);
-    const int64_t tstr = Lw.ng * Lw.K0 * SBW * SBW;
+    const int64_t tstr = Lw.ng * Lw.K0 * CBR * SBW;
     if (ng > 0 && K0 > 0) {
       ProfScope ps("chase_back", s);
       // algorithmic work: Z (n x R) read and written once, every reflector
