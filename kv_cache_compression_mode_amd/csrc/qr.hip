@@ -292,15 +292,11 @@ __device__ float qr_reg_factor(float (&p)[64], int mr, int nb, QrRegLds& L) {
     float tr[32];                                              // tr[l] = 0 for l < t
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      float u0 = 0.f, u1 = 0.f;
+      float u[4] = {0.f, 0.f, 0.f, 0.f};                   // four interleaved chains
 #pragma unroll
-      for (int l = 0; l + 1 < j; l += 2) {
-        u0 += tr[l] * L.St[j][l];
-        u1 += tr[l + 1] * L.St[j][l + 1];
-      }
-      if (j & 1) u0 += tr[j - 1] * L.St[j][j - 1];
+      for (int l = 0; l < j; ++l) u[l & 3] = fmaf(tr[l], L.St[j][l], u[l & 3]);
       const float tj = L.tau_s[j];
-      tr[j] = (j >= nb || j < t) ? 0.f : (j == t ? tj : -tj * (u0 + u1));
+      tr[j] = (j >= nb || j < t) ? 0.f : (j == t ? tj : -tj * ((u[0] + u[1]) + (u[2] + u[3])));
       L.Tl[t][j] = tr[j];
     }
   }

@@ -679,13 +679,15 @@ __global__ __launch_bounds__(64) void k_cb_tfac(const float* Rf_g, int64_t rf_st
   __syncthreads();
   float tr[SBW];
   if (lane < SBW) {
+    // T[lane][i] = -tau_i sum_{lane <= p < i} T[lane][p] S[p][i] (T[lane][p] = 0
+    // for p < lane), the sum in four interleaved chains
 #pragma unroll
     for (int i = 0; i < SBW; ++i) {
-      float u = 0.f;
+      float u[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int p = 0; p < i; ++p)
-        if (p >= lane) u += tr[p] * S[p][i];
-      tr[i] = i < lane ? 0.f : (i == lane ? tau[i] : -tau[i] * u);
+      for (int p = 0; p < i; ++p) u[p & 3] = fmaf(tr[p], S[p][i], u[p & 3]);
+      const float us = (u[0] + u[1]) + (u[2] + u[3]);
+      tr[i] = i < lane ? 0.f : (i == lane ? tau[i] : -tau[i] * us);
     }
   }
   // V T (64 x 32), the product the blocks are applied with: T through LDS
