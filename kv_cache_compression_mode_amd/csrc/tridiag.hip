@@ -763,11 +763,18 @@ __global__ __launch_bounds__(256) void k_cb_apply(int u, int glo, int nchunk, fl
       rv[b][q] = (ok && j <= last && sb < sweep_steps(n, j)) ? Rf[(sweep_offset(n, j) + sb) * RFS + r] : 0.f;
     }
   }
+  // the window: thread -> row 32 j + (tid & 31), column 8 q + (tid >> 5)
+  // (q < 8, j < 3): 32 consecutive rows of a column per 32 lanes, and the
+  // offsets step by constants
+  const int zr = tid & 31, zc = tid >> 5;
+  const float* zsrc = Zz + static_cast<int64_t>(c0 + zc) * n + rw + zr;
 #pragma unroll
-  for (int q = 0; q < 24; ++q) {
-    const int idx = tid + 256 * q, c = idx / CBW, r = idx % CBW;
-    rz[q] = (r >= lo && r < hi && c < nc) ? Zz[static_cast<int64_t>(c0 + c) * n + rw + r] : 0.f;
-  }
+  for (int q = 0; q < 8; ++q)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int r = zr + 32 * j;
+      rz[3 * q + j] = (r >= lo && r < hi && zc + 8 * q < nc) ? zsrc[static_cast<int64_t>(8 * q) * n + 32 * j] : 0.f;
+    }
   for (int idx = tid; idx < 2 * CBR * SBW; idx += 256) {
     const int b = idx / (CBR * SBW), row = (idx / SBW) % CBR, i = idx % SBW;
     if (row < i || row >= i + SBW) Vs[b][row][i] = 0.f;
@@ -787,10 +794,9 @@ __global__ __launch_bounds__(256) void k_cb_apply(int u, int glo, int nchunk, fl
     }
   }
 #pragma unroll
-  for (int q = 0; q < 24; ++q) {
-    const int idx = tid + 256 * q;
-    Zs[idx % CBW][idx / CBW] = rz[q];
-  }
+  for (int q = 0; q < 8; ++q)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) Zs[zr + 32 * j][zc + 8 * q] = rz[3 * q + j];
   __syncthreads();
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -828,15 +834,17 @@ __global__ __launch_bounds__(256) void k_cb_apply(int u, int glo, int nchunk, fl
     __syncthreads();
   }
 #pragma unroll
-  for (int q = 0; q < 24; ++q) {
-    const int idx = tid + 256 * q, c = idx / CBW, r = idx % CBW;
-    rz[q] = Zs[r][c];
-  }
+  for (int q = 0; q < 8; ++q)
 #pragma unroll
-  for (int q = 0; q < 24; ++q) {
-    const int idx = tid + 256 * q, c = idx / CBW, r = idx % CBW;
-    if (r >= lo && r < hi && c < nc) Zz[static_cast<int64_t>(c0 + c) * n + rw + r] = rz[q];
-  }
+    for (int j = 0; j < 3; ++j) rz[3 * q + j] = Zs[zr + 32 * j][zc + 8 * q];
+  float* zdst = Zz + static_cast<int64_t>(c0 + zc) * n + rw + zr;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int r = zr + 32 * j;
+      if (r >= lo && r < hi && zc + 8 * q < nc) zdst[static_cast<int64_t>(8 * q) * n + 32 * j] = rz[3 * q + j];
+    }
 }
 
 // Panel back-transformation, K consecutive panels per launch: Z rows r_q ..
