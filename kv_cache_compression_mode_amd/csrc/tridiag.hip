@@ -386,23 +386,45 @@ __global__ __launch_bounds__(256) void k_tri_out(const float* Bw, int64_t n, dou
   }
 }
 
-// Number of eigenvalues of the tridiagonal (d, e2 = e^2) below x (Sturm count).
-__device__ __forceinline__ int sturm_count(const double* d, const double* e2, int64_t n, double x,
-                                           double pivmin) {
-  int cnt = 0;
-  double q = d[0] - x;
-  if (fabs(q) < pivmin) q = -pivmin;
-  cnt += q < 0.0;
-  for (int64_t i = 1; i < n; ++i) {
-    // e2 / q through the hardware reciprocal (about 24 bits) refined by one
-    // Newton step (about 2e-15 relative, measured: the count needs only the
-    // pivot signs); |q| >= pivmin keeps the reciprocal finite
-    double r = __builtin_amdgcn_rcp(q);
-    r = __builtin_fma(__builtin_fma(-q, r, 1.0), r, r);
-    q = (d[i] - x) - e2[i - 1] * r;
-    if (fabs(q) < pivmin) q = -pivmin;
-    cnt += q < 0.0;
+// Number of eigenvalues of the tridiagonal (d, e2 = e^2) below x (Sturm
+// count): by Sylvester's law of inertia, the negative pivots q_i = (d_i - x)
+// - e2_{i-1} / q_{i-1} of L D L^T = T - x I, a vanishing pivot counted as
+// negative.  The pivots are ratios of the leading principal minors, q_i =
+// P_i / P_{i-1} with P_i = (d_i - x) P_{i-1} - e2_{i-1} P_{i-2} (P_{-1} = 1),
+// so q_i < 0 exactly where the signs of P_i and P_{i-1} differ; the minors
+// leave no division on the dependency chain, one fused multiply-add per row
+// (the e2 P_{i-2} term is formed a row earlier).  d, e2 and x come scaled by
+// powers of two so that |d_i - x| < 2 and e2_i < 4: |P| grows at most 6x a
+// row, and every 8 rows both minors are rescaled by a power of two (exact).
+// Each minor takes -pv times its predecessor, pv = max(2^-900, pivmin / 2^ex)
+// (the pivot floor of the unscaled count, far below any pivot that matters
+// unless the whole matrix is at the fp64 floor): a vanishing pivot becomes a
+// tiny negative one, and a zero does not propagate where e2 vanishes.
+__device__ __forceinline__ int sturm_count_minors(const double* d, const double* e2, int64_t n, double x,
+                                                  double kPv) {
+  double pm2 = 1.0;
+  double pm1 = __builtin_fma(-kPv, 1.0, d[0] - x);
+  bool neg = pm1 < 0.0;
+  int cnt = neg;
+  auto row = [&](int64_t i) {
+    const double t = e2[i - 1] * pm2;
+    double p = __builtin_fma(d[i] - x, pm1, -t);
+    p = __builtin_fma(-kPv, pm1, p);
+    const bool ng = p < 0.0;
+    cnt += ng != neg;
+    neg = ng;
+    pm2 = pm1;
+    pm1 = p;
+  };
+  int64_t i = 1;
+  for (; i + 8 <= n; i += 8) {                      // whole blocks of 8 rows, then a rescale
+#pragma unroll
+    for (int u = 0; u < 8; ++u) row(i + u);
+    const int ex = max(__builtin_amdgcn_frexp_exp(pm1), __builtin_amdgcn_frexp_exp(pm2));
+    pm1 = __builtin_amdgcn_ldexp(pm1, -ex);
+    pm2 = __builtin_amdgcn_ldexp(pm2, -ex);
   }
+  for (; i < n; ++i) row(i);                        // at most 7 rows: no rescale needed
   return cnt;
 }
 
@@ -415,6 +437,7 @@ __global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double*
   double* d = sh;
   double* e2 = sh + n;
   __shared__ double gl_s, gu_s, piv_s, tol_s;
+  __shared__ int ex_s;
   __shared__ int grid_cnt[256];
   const int64_t z = blockIdx.y;
   for (int64_t i = threadIdx.x; i < n; i += 256) {
@@ -441,6 +464,16 @@ __global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double*
     // norm), and the eigenvalues feed the allocation's energies and the
     // inverse-iteration shifts, neither of which sees a difference that small
     tol_s = 1e-12 * (gu - gl);
+    // the counts run on T / 2^ex with 2^ex >= max |x| over the interval
+    // (powers of two: the scaled values and every x are exact)
+    ex_s = __builtin_amdgcn_frexp_exp(fmax(fabs(gl_s), fabs(gu_s)));
+  }
+  __syncthreads();
+  const int ex = ex_s;
+  const double pv = fmax(0x1p-900, __builtin_amdgcn_ldexp(piv_s, -ex));
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    d[i] = __builtin_amdgcn_ldexp(d[i], -ex);
+    e2[i] = __builtin_amdgcn_ldexp(e2[i], -2 * ex);
   }
   __syncthreads();
   // a shared first pass: counts at 256 interior points x_i = gl + (gu - gl) (i + 1) / 257
@@ -448,7 +481,8 @@ __global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double*
   // its starting bracket (one count per thread, as a multisection step, but a
   // 257-way split)
   const double g0 = gl_s, gw = gu_s - gl_s;
-  grid_cnt[threadIdx.x] = sturm_count(d, e2, n, g0 + gw * (threadIdx.x + 1) * (1.0 / 257.0), piv_s);
+  grid_cnt[threadIdx.x] =
+      sturm_count_minors(d, e2, n, __builtin_amdgcn_ldexp(g0 + gw * (threadIdx.x + 1) * (1.0 / 257.0), -ex), pv);
   __syncthreads();
   // BSL threads per eigenvalue (multisection): each evaluates one of BSL
   // interior points of the bracket, which then shrinks to 1 / (BSL + 1)
@@ -466,7 +500,7 @@ __global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double*
     if (hi - lo <= fmax(2.0 * DBL_EPSILON * fmax(fabs(lo), fabs(hi)), tol_s) + piv_s) break;
     const double w = hi - lo;
     const double x = lo + w * (sub + 1) * (1.0 / (BSL + 1));
-    const int cnt = sturm_count(d, e2, n, x, piv_s);
+    const int cnt = sturm_count_minors(d, e2, n, __builtin_amdgcn_ldexp(x, -ex), pv);
     double nlo = lo, nhi = hi;
     bool found = false;
 #pragma unroll
