@@ -508,11 +508,19 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     gd.ksplit = gram_d_ksplit(d); gd.partial = w.GDpart;
     ck(launch_gemm(gd, batch, s, "gram"));
   }
+  // the feature path runs on a stream of its own, forked here (its Gram is
+  // complete in stream order); its kernels are enqueued after the token
+  // path's, so that their launches on the host do not hold back the token
+  // path's first kernels
   FeatureFork ff(hip, s);
-  feature_factor(d, batch, t0, w, ff.start());
-  ff.done();
-  if (R == 0) {
+  const hipStream_t fs = ff.start();
+  auto feature = [&] {
+    feature_factor(d, batch, t0, w, fs);
+    ff.done();
     ff.join();
+  };
+  if (R == 0) {
+    feature();
     return;
   }
   // leading eigenvectors V_R of the token Gram: the first R columns of w.V
@@ -535,7 +543,7 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   // (fp64, descending; the dual Gram shares the nonzero ones)
   ck(finalize_factor_ws(w.Ucm, T, R, T, T * R, w.lam_tmp, R, w.UT + static_cast<size_t>(t0) * T * R, R, T * R,
                         w.lamT + static_cast<size_t>(t0) * R, R, batch, w.perm, w.sgn, s));
-  ff.join();
+  feature();
 }
 
 void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, int q, uint64_t seed,
@@ -552,11 +560,19 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     gd.ksplit = gram_d_ksplit(d); gd.partial = w.GDpart;
     ck(launch_gemm(gd, batch, s, "gram"));
   }
+  // the feature path runs on a stream of its own, forked here (its Gram is
+  // complete in stream order); its kernels are enqueued after the token
+  // path's, so that their launches on the host do not hold back the token
+  // path's first kernels
   FeatureFork ff(hip, s);
-  feature_factor(d, batch, t0, w, ff.start());
-  ff.done();
-  if (R == 0) {
+  const hipStream_t fs = ff.start();
+  auto feature = [&] {
+    feature_factor(d, batch, t0, w, fs);
+    ff.done();
     ff.join();
+  };
+  if (R == 0) {
+    feature();
     return;
   }
   ck(launch_sketch(w.Om, HD, ell, seed, w.tags, batch, s));
@@ -618,7 +634,7 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   }
   orthonormalize(w.Ucm, w.Ucm2, T, R, batch, w.qtau, w.cq, w, s);
   token_finalize(d, batch, t0, w, xdt, s);
-  ff.join();
+  feature();
 }
 
 // Algorithmic work of the residual path of one tensor (encode or decode):
