@@ -149,6 +149,12 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev,
  * and U_D fp32 [D][D].  Pure pointer arithmetic, no device access. */
 jolt_status jolt_factors(const jolt_alloc_req* req, void* ws_dev, int32_t tensor,
                          const float** U_T, int32_t* ld_T, const float** U_D);
+/* jolt_factors of tensors first .. first + n - 1 in one call: U_T[i],
+ * ld_T[i] and U_D[i] (arrays of n, caller-owned) describe tensor first + i.
+ * Errors: EINVAL (invalid request, range outside the cache's 2 L tensors,
+ * NULL arrays with n > 0). */
+jolt_status jolt_factors_many(const jolt_alloc_req* req, void* ws_dev, int32_t first, int32_t n,
+                              const float** U_T, int32_t* ld_T, const float** U_D);
 
 /* The seeded rotation Q (D x D, Haar: QR of a counter-based Gaussian matrix
  * with diag(R) > 0), prepared on the host in fp64 and uploaded to q_dev

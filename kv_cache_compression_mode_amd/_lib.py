@@ -67,6 +67,8 @@ SIGNATURES = {
                                 C.c_void_p, C.POINTER(Plan)]),
     "jolt_factors": (C.c_int, [C.POINTER(AllocReq), C.c_void_p, C.c_int32, C.POINTER(C.c_void_p),
                                C.POINTER(C.c_int32), C.POINTER(C.c_void_p)]),
+    "jolt_factors_many": (C.c_int, [C.POINTER(AllocReq), C.c_void_p, C.c_int32, C.c_int32,
+                                    C.POINTER(C.c_void_p), C.POINTER(C.c_int32), C.POINTER(C.c_void_p)]),
     "jolt_rotation": (C.c_int, [C.c_uint64, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]),
     "jolt_rotation_from": (C.c_int, [C.POINTER(C.c_double), C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]),
     "jolt_encode": (C.c_int, [C.POINTER(Shape), C.c_void_p, Choice, C.c_void_p, C.c_int32, C.c_void_p,

@@ -279,10 +279,12 @@ AllocWS carve_alloc(const jolt_alloc_req* r, void* base, AllocWS* lane1 = nullpt
   w.UD = c.take<float>(static_cast<size_t>(nt) * d.D * d.D);
   w.lamT = c.take<double>(static_cast<size_t>(nt) * R);
   w.lamD = c.take<double>(static_cast<size_t>(nt) * d.D);
+  // lamT .. status is one span, read back in one copy; xptrs and tags
+  // another, uploaded in one copy
   w.frob2 = c.take<double>(nt);
+  w.status = c.take<int>(1);
   w.xptrs = c.take<const void*>(nt);
   w.tags = c.take<uint64_t>(nt);
-  w.status = c.take<int>(1);
   const int64_t n = d.flash ? d.ell_pad : d.n_pad;
   auto carve_scratch = [&](AllocWS& w) {
     w.G = c.take<float>(static_cast<size_t>(chunk) * n * n);
@@ -360,6 +362,29 @@ StreamPool& stream_pool() {
   return p;
 }
 
+// Pinned host staging buffers for the small uploads and read-backs of a call
+// (pointer tables, launch arguments, spectra): copies from and to them are
+// plain DMA that never makes the host wait, where a pageable copy stages
+// through the runtime and blocks.  A buffer is leased like a stream and goes
+// back with an event recorded after the last copy that touches it; the next
+// lease waits on that event, so a copy still in flight never sees its memory
+// rewritten.  Buffers come from hipHostMalloc on first need and are kept until
+// the process ends.
+struct PinnedBuf {
+  void* p = nullptr;
+  size_t bytes = 0;
+  hipEvent_t done = nullptr;   // recorded after the buffer's last copy
+  bool armed = false;          // `done` has been recorded at least once
+};
+struct PinnedPool {
+  std::mutex mu;
+  std::map<int, std::vector<PinnedBuf>> idle;   // device -> buffers not leased
+};
+PinnedPool& pinned_pool() {
+  static PinnedPool p;
+  return p;
+}
+
 class CallHip {
  public:
   CallHip() = default;
@@ -373,6 +398,50 @@ class CallHip {
       auto& v = p.idle[dev_];
       v.insert(v.end(), leased_.begin(), leased_.end());
     }
+    if (!pinned_.empty()) {
+      PinnedPool& p = pinned_pool();
+      std::lock_guard<std::mutex> lk(p.mu);
+      auto& v = p.idle[pdev_];
+      v.insert(v.end(), pinned_.begin(), pinned_.end());
+    }
+  }
+  // Pinned host memory of at least `bytes` that no other call holds until
+  // this one ends; a copy that uses it is followed by copied(ptr, stream).
+  void* pinned(size_t bytes) {
+    if (pinned_.empty()) ck(hipGetDevice(&pdev_));
+    PinnedBuf b;
+    {
+      PinnedPool& p = pinned_pool();
+      std::lock_guard<std::mutex> lk(p.mu);
+      auto& v = p.idle[pdev_];
+      int best = -1;
+      for (int i = 0; i < static_cast<int>(v.size()); ++i)
+        if (v[i].bytes >= bytes && (best < 0 || v[i].bytes < v[best].bytes)) best = i;
+      if (best >= 0) {
+        b = v[best];
+        v.erase(v.begin() + best);
+      }
+    }
+    if (b.p) {
+      if (b.armed) ck(hipEventSynchronize(b.done));
+    } else {
+      size_t sz = 64 << 10;
+      while (sz < bytes) sz *= 2;
+      ck(hipHostMalloc(&b.p, sz, hipHostMallocDefault));
+      b.bytes = sz;
+      ck(hipEventCreateWithFlags(&b.done, hipEventDisableTiming));
+    }
+    pinned_.push_back(b);
+    return b.p;
+  }
+  // Marks the end of the copies queued so far on s that touch buffer p.
+  void copied(const void* p, hipStream_t s) {
+    for (PinnedBuf& b : pinned_)
+      if (b.p == p) {
+        ck(hipEventRecord(b.done, s));
+        b.armed = true;
+        return;
+      }
   }
   // A stream no other call holds until this one ends.
   hipStream_t lease() {
@@ -399,9 +468,10 @@ class CallHip {
   }
 
  private:
-  int dev_ = 0;
+  int dev_ = 0, pdev_ = 0;
   std::vector<hipStream_t> leased_;
   std::vector<hipEvent_t> events_;
+  std::vector<PinnedBuf> pinned_;
 };
 
 // Runs the feature-mode factor on an auxiliary stream of the call after the
@@ -993,16 +1063,26 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, v
     const int64_t N = d.H * d.T * d.D;
     ck(hipMemsetAsync(w.frob2, 0, sizeof(double) * nt, s));
     ck(hipMemsetAsync(w.status, 0, sizeof(int), s));
-    // every tensor's pointer and sketch tag, uploaded once
-    std::vector<const void*> ptrs(x_dev, x_dev + nt);
-    std::vector<uint64_t> tags(nt);
-    for (int t = 0; t < nt; ++t)
-      tags[t] = kTagSketch ^ ((static_cast<uint64_t>(t / 2) << 8) | static_cast<uint64_t>(t % 2));
-    ck(hipMemcpyAsync(w.xptrs, ptrs.data(), sizeof(void*) * nt, hipMemcpyHostToDevice, s));
-    ck(hipMemcpyAsync(w.tags, tags.data(), sizeof(uint64_t) * nt, hipMemcpyHostToDevice, s));
-    ck(hipStreamSynchronize(s));
+    CallHip stage;                                // pinned staging of the upload and the read-back
+    // every tensor's pointer and sketch tag, uploaded once (one span of the workspace)
+    {
+      const size_t up = reinterpret_cast<const char*>(w.tags + nt) - reinterpret_cast<const char*>(w.xptrs);
+      char* img = static_cast<char*>(stage.pinned(up));
+      std::memcpy(img, x_dev, sizeof(void*) * nt);
+      uint64_t* tags = reinterpret_cast<uint64_t*>(img + (reinterpret_cast<char*>(w.tags) - reinterpret_cast<char*>(w.xptrs)));
+      for (int t = 0; t < nt; ++t)
+        tags[t] = kTagSketch ^ ((static_cast<uint64_t>(t / 2) << 8) | static_cast<uint64_t>(t % 2));
+      ck(hipMemcpyAsync(w.xptrs, img, up, hipMemcpyHostToDevice, s));
+      stage.copied(img, s);
+    }
     const int R = static_cast<int>(d.R);
-    std::vector<double> lt(static_cast<size_t>(nt) * std::max(R, 1)), ld(static_cast<size_t>(nt) * d.D), f2(nt);
+    // the read-back span: lamT [nt][max(R, 1)], lamD [nt][D], frob2 [nt], status
+    const size_t rb = reinterpret_cast<const char*>(w.status + 1) - reinterpret_cast<const char*>(w.lamT);
+    char* back = static_cast<char*>(stage.pinned(rb));
+    auto host_of = [&](const void* dev) { return back + (static_cast<const char*>(dev) - reinterpret_cast<const char*>(w.lamT)); };
+    const double* lt = reinterpret_cast<const double*>(host_of(w.lamT));
+    const double* ld = reinterpret_cast<const double*>(host_of(w.lamD));
+    const double* f2 = reinterpret_cast<const double*>(host_of(w.frob2));
     // the whole analysis; returns the status word
     auto analyze_all = [&](bool householder) -> int {
       w.householder = w1.householder = householder;
@@ -1040,12 +1120,11 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, v
         ck(hipEventRecord(join, ls));
         ck(hipStreamWaitEvent(s, join, 0));
       }
-      if (R > 0) ck(hipMemcpyAsync(lt.data(), w.lamT, sizeof(double) * nt * R, hipMemcpyDeviceToHost, s));
-      ck(hipMemcpyAsync(ld.data(), w.lamD, sizeof(double) * nt * d.D, hipMemcpyDeviceToHost, s));
-      ck(hipMemcpyAsync(f2.data(), w.frob2, sizeof(double) * nt, hipMemcpyDeviceToHost, s));
-      int status = 0;
-      ck(hipMemcpyAsync(&status, w.status, sizeof(int), hipMemcpyDeviceToHost, s));
+      ck(hipMemcpyAsync(back, w.lamT, rb, hipMemcpyDeviceToHost, s));
+      stage.copied(back, s);
       ck(hipStreamSynchronize(s));
+      int status = 0;
+      std::memcpy(&status, host_of(w.status), sizeof(int));
       return status;
     };
     int status = analyze_all(false);
@@ -1059,10 +1138,11 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, v
     if (status != 0) return JOLT_EHIP;          // an eigensolver wait gave up: the factors are not valid
     for (int i = 0; i < nt; ++i)
       if (!std::isfinite(f2[i])) return JOLT_ERANGE;
-    if (plan->spectra_T && R > 0) std::memcpy(plan->spectra_T, lt.data(), sizeof(double) * nt * R);
-    if (plan->spectra_D) std::memcpy(plan->spectra_D, ld.data(), sizeof(double) * nt * d.D);
-    if (plan->frob2) std::memcpy(plan->frob2, f2.data(), sizeof(double) * nt);
-    return plan_dual(req, lt.data(), std::max(R, 1), ld.data(), f2.data(), plan);
+    if (R == 0) std::memset(host_of(w.lamT), 0, sizeof(double) * nt);   // no token spectra: zero placeholders
+    if (plan->spectra_T && R > 0) std::memcpy(plan->spectra_T, lt, sizeof(double) * nt * R);
+    if (plan->spectra_D) std::memcpy(plan->spectra_D, ld, sizeof(double) * nt * d.D);
+    if (plan->frob2) std::memcpy(plan->frob2, f2, sizeof(double) * nt);
+    return plan_dual(req, lt, std::max(R, 1), ld, f2, plan);
   });
 }
 
@@ -1075,6 +1155,22 @@ jolt_status jolt_factors(const jolt_alloc_req* req, void* ws_dev, int32_t tensor
   if (U_T) *U_T = w.UT + static_cast<size_t>(tensor) * d.T * R;
   if (ld_T) *ld_T = static_cast<int32_t>(R);
   if (U_D) *U_D = w.UD + static_cast<size_t>(tensor) * d.D * d.D;
+  return JOLT_OK;
+}
+
+jolt_status jolt_factors_many(const jolt_alloc_req* req, void* ws_dev, int32_t first, int32_t n, const float** U_T,
+                              int32_t* ld_T, const float** U_D) {
+  if (!req_ok(req) || !ws_dev || first < 0 || n < 0 || first + n > 2 * req->n_layers) return JOLT_EINVAL;
+  if (n > 0 && (!U_T || !ld_T || !U_D)) return JOLT_EINVAL;
+  const AllocWS w = carve_alloc(req, ws_dev);
+  const Dims d = dims_of(req);
+  const int64_t R = std::max<int64_t>(d.R, 1);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t t = first + i;
+    U_T[i] = w.UT + static_cast<size_t>(t) * d.T * R;
+    ld_T[i] = static_cast<int32_t>(R);
+    U_D[i] = w.UD + static_cast<size_t>(t) * d.D * d.D;
+  }
   return JOLT_OK;
 }
 
@@ -1237,15 +1333,17 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
       ea.codes = reinterpret_cast<uint8_t*>(blob(i) + B.cd);
       heads[i] = record_head(H, T, D, shape->dtype, c, seed);
     }
-    // one upload of the host images (pageable memory: the call copies before returning)
+    // one upload of the host images, staged in pinned memory (the copy runs
+    // ahead of the launches below without holding the host)
+    CallHip stage;
     {
-      std::vector<char> img(a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n) + a256(sizeof(RecordHead) * n), 0);
-      std::memcpy(img.data(), ptr.data(), 8 * L.n_ptrs);
-      std::memcpy(img.data() + a256(8 * L.n_ptrs), args.data(), sizeof(EncodeArgs) * n);
-      std::memcpy(img.data() + a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n), heads.data(),
-                  sizeof(RecordHead) * n);
-      ck(hipMemcpyAsync(dptr, img.data(), img.size(), hipMemcpyHostToDevice, s));
-      ck(hipStreamSynchronize(s));
+      const size_t nb = a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n) + a256(sizeof(RecordHead) * n);
+      char* img = static_cast<char*>(stage.pinned(nb));
+      std::memcpy(img, ptr.data(), 8 * L.n_ptrs);
+      std::memcpy(img + a256(8 * L.n_ptrs), args.data(), sizeof(EncodeArgs) * n);
+      std::memcpy(img + a256(8 * L.n_ptrs) + a256(sizeof(EncodeArgs) * n), heads.data(), sizeof(RecordHead) * n);
+      ck(hipMemcpyAsync(dptr, img, nb, hipMemcpyHostToDevice, s));
+      stage.copied(img, s);
     }
     auto dp = [&](size_t slot) { return dptr + slot; };
     for (size_t g = 0; g < L.groups.size(); ++g) {

@@ -139,20 +139,31 @@ jolt_status plan_dual(const jolt_alloc_req* req, const double* spT, int lenT, co
       for (int rt = sT; rt <= RT; rt += sT)
         for (int rd = sD; rd <= RD; rd += sD)
           for (int b = 0; b < req->n_bits; ++b) u.menu.push_back({rt, rd, req->bit_menu[b]});
+      // the menu runs over (r_T, r_D) with the bit widths innermost: each
+      // layer's clipped relative tail is formed once per rank pair and
+      // weighted per width, summed over the layers in order
       std::vector<Pt> pts;
-      for (int i = 0; i < static_cast<int>(u.menu.size()); ++i) {
-        const jolt_choice c = u.menu[i];
-        const int64_t nb = static_cast<int64_t>(u.last - u.first) *
-                           static_cast<int64_t>(blob_layout(s.H, s.T, s.D, c).total);
-        double dist = 0.0;
+      pts.reserve(u.menu.size());
+      std::vector<double> clip(static_cast<size_t>(u.last - u.first));
+      std::vector<char> live(clip.size());
+      for (int i0 = 0; i0 < static_cast<int>(u.menu.size()); i0 += req->n_bits) {
+        const jolt_choice c0 = u.menu[i0];
         for (int l = u.first; l < u.last; ++l) {
           const int t = l * 2 + kind;
           const double f2 = frob2[t];
-          if (!(f2 > 0.0)) continue;
-          const double e = (tail_T(t, f2, c.r_T) + tail_D(t, f2, c.r_D)) / f2;
-          dist += rho(c.bits) * std::min(1.0, e);
+          live[l - u.first] = f2 > 0.0;
+          if (f2 > 0.0) clip[l - u.first] = std::min(1.0, (tail_T(t, f2, c0.r_T) + tail_D(t, f2, c0.r_D)) / f2);
         }
-        pts.push_back({nb, dist, i});
+        for (int i = i0; i < i0 + req->n_bits; ++i) {
+          const jolt_choice c = u.menu[i];
+          const int64_t nb = static_cast<int64_t>(u.last - u.first) *
+                             static_cast<int64_t>(blob_layout(s.H, s.T, s.D, c).total);
+          const double w = rho(c.bits);
+          double dist = 0.0;
+          for (size_t l = 0; l < clip.size(); ++l)
+            if (live[l]) dist += w * clip[l];
+          pts.push_back({nb, dist, i});
+        }
       }
       std::sort(pts.begin(), pts.end(), [](const Pt& a, const Pt& b) {
         if (a.bytes != b.bytes) return a.bytes < b.bytes;

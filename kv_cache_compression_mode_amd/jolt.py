@@ -296,7 +296,7 @@ def encode_many(xs, choices, factors, rot: torch.Tensor, seed: int = 0, outs=Non
         blobs = outs
     else:
         # one allocation cut into 256-aligned records
-        sizes = [lib().jolt_blob_bytes(C.byref(shape), ch[i]) for i in range(n)]
+        sizes = _blob_sizes(shape, choices)
         offs, o = [], 0
         for nb in sizes:
             offs.append(o)
@@ -308,14 +308,9 @@ def encode_many(xs, choices, factors, rot: torch.Tensor, seed: int = 0, outs=Non
         if n != 2 * factors.req.n_layers:
             raise ValueError("an Allocation supplies the factors of its whole cache")
         utp, udp = (C.c_void_p * n)(), (C.c_void_p * n)()
-        ldt, ldd = (C.c_int32 * n)(), (C.c_int32 * n)()
-        ws_ptr = factors.workspace.data_ptr()
-        ut, ud, ld = C.c_void_p(), C.c_void_p(), C.c_int32()
-        for i in range(n):
-            check(lib().jolt_factors(C.byref(factors.req), ws_ptr, i, C.byref(ut), C.byref(ld), C.byref(ud)),
-                  "jolt_factors")
-            utp[i], udp[i] = ut.value, ud.value
-            ldt[i], ldd[i] = ld.value, factors.req.shape.D
+        ldt, ldd = (C.c_int32 * n)(), (C.c_int32 * n)(*([factors.req.shape.D] * n))
+        check(lib().jolt_factors_many(C.byref(factors.req), factors.workspace.data_ptr(), 0, n, utp, ldt, udp),
+              "jolt_factors_many")
     else:
         _need(len(factors) == n, "one factor pair per tensor")
         for i, (c, pair) in enumerate(zip(choices, factors)):

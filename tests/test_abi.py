@@ -158,3 +158,24 @@ def test_dual_infeasible_budget(J):
     with pytest.raises(jl.JoltError) as e:
         J.plan_from_spectra(J.make_req(8, 1024, 128, 0, 4, 2.0), sT, sD, f2)
     assert e.value.status == jl.JOLT_ERANGE
+
+
+def test_factors_many_matches_factors(J):
+    """jolt_factors_many is jolt_factors over a range (pointer arithmetic
+    only: a host address stands in for the workspace, nothing is read)."""
+    L = jl.lib()
+    req = J.make_req(8, 1024, 128, 0, 4, 2.0)
+    base = 1 << 40
+    n = 8
+    ut, ud = (C.c_void_p * 5)(), (C.c_void_p * 5)()
+    ldt = (C.c_int32 * 5)()
+    assert L.jolt_factors_many(C.byref(req), base, 3, 5, ut, ldt, ud) == 0
+    for i in range(5):
+        a, b, ld = C.c_void_p(), C.c_void_p(), C.c_int32()
+        assert L.jolt_factors(C.byref(req), base, 3 + i, C.byref(a), C.byref(ld), C.byref(b)) == 0
+        assert (ut[i], ldt[i], ud[i]) == (a.value, ld.value, b.value)
+    # the range must lie inside the cache's 2 L tensors
+    assert L.jolt_factors_many(C.byref(req), base, n - 2, 3, ut, ldt, ud) == jl.JOLT_EINVAL
+    assert L.jolt_factors_many(C.byref(req), base, -1, 1, ut, ldt, ud) == jl.JOLT_EINVAL
+    assert L.jolt_factors_many(C.byref(req), base, 0, 2, None, ldt, ud) == jl.JOLT_EINVAL
+    assert L.jolt_factors_many(C.byref(req), base, 0, 0, None, None, None) == 0
