@@ -947,7 +947,9 @@ hipError_t launch_gemm(const GemmArgs& g0, int batch, hipStream_t s, const char*
 
 hipError_t launch_sumsq(const void* const* xs_dev, int ntensors, int64_t n, int dtype, double* out,
                         hipStream_t s) {
-  dim3 grid(grid1(n, 1024), ntensors);
+  // at most 128 workgroups per tensor, each thread looping over its share:
+  // few atomic additions per output (they serialize on one address)
+  dim3 grid(grid1(n, 128), ntensors);
   if (dtype == kBF16) k_sumsq<uint16_t><<<grid, 256, 0, s>>>(xs_dev, n, out);
   else k_sumsq<float><<<grid, 256, 0, s>>>(xs_dev, n, out);
   return hipGetLastError();

@@ -501,24 +501,26 @@ struct FeatureFork {
   }
 };
 
-// Orthonormal columns spanning the leading columns of the nearly orthogonal
-// column-major U (m x k, ld m) in place, nested spans kept: two CholeskyQR
-// passes, or Householder QR where k is too wide for them or after one of them
-// broke down (w.householder).
-void orthonormalize(float* U, float* U2, int64_t m, int64_t k, int batch, float* hwork, float* cwork,
+// Orthonormal columns spanning the leading columns of the nearly orthonormal
+// column-major src (m x k, ld m, unit-norm columns up to a few percent) into
+// dst, nested spans kept: one CholeskyQR pass, or Householder QR where k is too
+// wide for it or after it broke down (w.householder; src is then overwritten).
+void orthonormalize(float* src, float* dst, int64_t m, int64_t k, int batch, float* hwork, float* cwork,
                     const AllocWS& w, hipStream_t s) {
-  if (!w.householder && k <= cholesky_qr_max_k() && m >= k)
-    ck(cholesky_qr(U, U2, m, k, m, m * k, batch, cwork, w.status, s));
-  else
-    ck(householder_qr(U, m, k, m, m * k, batch, hwork, s));
+  if (!w.householder && k <= cholesky_qr_max_k() && m >= k) {
+    ck(cholesky_qr(src, dst, m, k, m, m * k, batch, cwork, w.status, s));
+  } else {
+    ck(householder_qr(src, m, k, m, m * k, batch, hwork, s));
+    ck(hipMemcpyAsync(dst, src, sizeof(float) * batch * m * k, hipMemcpyDeviceToDevice, s));
+  }
 }
 
 // Feature-mode factor of `batch` tensors from their D x D Grams in w.GD.
 void feature_factor(const Dims& d, int batch, int t0, const AllocWS& w, hipStream_t s) {
   const int64_t D = d.D;
   ck(hipMemcpyAsync(w.GDc, w.GD, sizeof(float) * batch * D * D, hipMemcpyDeviceToDevice, s));
-  ck(syev_top(w.GD, D, batch, static_cast<int>(D), w.Vr, nullptr, w.syevD, s, w.status));
-  orthonormalize(w.Vr, w.Vr2, D, D, batch, w.qtauD, w.cqD, w, s);
+  ck(syev_top(w.GD, D, batch, static_cast<int>(D), w.Vr2, nullptr, w.syevD, s, w.status));
+  orthonormalize(w.Vr2, w.Vr, D, D, batch, w.qtauD, w.cqD, w, s);
   // Rayleigh quotients diag(U^T G U): W = G U (column-major), then column dots
   GemmArgs g = gemm0();
   g.M = D; g.N = D; g.K = D;
@@ -584,8 +586,16 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   // path's first kernels
   FeatureFork ff(hip, s);
   const hipStream_t fs = ff.start();
+  // the band reduction's end, recorded on s by the eigensolver below
+  const hipEvent_t band_done = R > 0 ? (w.band_done ? w.band_done : hip.event()) : nullptr;
   auto feature = [&] {
+    // the feature factor, then ||X||^2 of every tensor, off the token path's
+    // critical path: once the token band reduction (latency-bound launches)
+    // is done, beside the token bulge chase and eigenpair solve (a few CUs
+    // per tensor, HBM idle)
+    if (band_done) ck(hipStreamWaitEvent(fs, band_done, 0));
     feature_factor(d, batch, t0, w, fs);
+    ck(launch_sumsq(xp, batch, d.H * T * D, xdt, w.frob2 + t0, fs));
     ff.done();
     ff.join();
   };
@@ -595,20 +605,22 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   }
   // leading eigenvectors V_R of the token Gram: the first R columns of w.V
   // (column-major, leading dimension n)
-  ck(syev_top(w.G, n, batch, static_cast<int>(R), w.V, w.lam_tmp, w.syev, s, w.status, w.band_done));
+  // (dual: each column scaled by 1 / sqrt(lambda), so that X_(T) v / sqrt(lambda)
+  // has unit norm and the recovered factor is nearly orthonormal)
+  ck(syev_top(w.G, n, batch, static_cast<int>(R), w.V, w.lam_tmp, w.syev, s, w.status, band_done, d.dual));
   if (d.dual) {
-    // U' = X_(T) V_R (T x R, column-major)
+    // U' = X_(T) V_R Lambda^{-1/2} (T x R, column-major)
     GemmArgs gu = gemm0();
     gu.a_ptrs = xp; gu.a_dtype = xdt; gu.ptr_align16 = w.x16;
     gu.M = T; gu.N = R; gu.K = HD;
     gu.am = plain(D); gu.ak = segmented(D, T * D, 1);
     gu.B = w.V; gu.bk = plain(1); gu.bn = plain(n); gu.b_batch = n * n;
-    gu.C = w.Ucm; gu.c_m = 1; gu.c_n = T; gu.c_batch = T * R;
+    gu.C = w.Ucm2; gu.c_m = 1; gu.c_n = T; gu.c_batch = T * R;
     ck(launch_gemm(gu, batch, s));
   } else {
-    ck(copy_cols(w.V, n, n * n, w.Ucm, T, T * R, T, R, batch, s));
+    ck(copy_cols(w.V, n, n * n, w.Ucm2, T, T * R, T, R, batch, s));
   }
-  orthonormalize(w.Ucm, w.Ucm2, T, R, batch, w.qtau, w.cq, w, s);
+  orthonormalize(w.Ucm2, w.Ucm, T, R, batch, w.qtau, w.cq, w, s);
   // the token spectrum: the eigensolver's eigenvalues of the token Gram
   // (fp64, descending; the dual Gram shares the nonzero ones)
   ck(finalize_factor_ws(w.Ucm, T, R, T, T * R, w.lam_tmp, R, w.UT + static_cast<size_t>(t0) * T * R, R, T * R,
@@ -637,6 +649,8 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   FeatureFork ff(hip, s);
   const hipStream_t fs = ff.start();
   auto feature = [&] {
+    // ||X||^2 of every tensor, off the token path's critical path
+    ck(launch_sumsq(xp, batch, d.H * T * D, xdt, w.frob2 + t0, fs));
     feature_factor(d, batch, t0, w, fs);
     ff.done();
     ff.join();
@@ -699,10 +713,10 @@ void analyze_flash(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     g.M = T; g.N = R; g.K = ell;
     g.A = w.Y; g.am = plain(1); g.ak = plain(T); g.a_batch = T * ell;
     g.B = w.Wr; g.bk = plain(1); g.bn = plain(ell); g.b_batch = ell * R;
-    g.C = w.Ucm; g.c_m = 1; g.c_n = T; g.c_batch = T * R;
+    g.C = w.Ucm2; g.c_m = 1; g.c_n = T; g.c_batch = T * R;
     ck(launch_gemm(g, batch, s));
   }
-  orthonormalize(w.Ucm, w.Ucm2, T, R, batch, w.qtau, w.cq, w, s);
+  orthonormalize(w.Ucm2, w.Ucm, T, R, batch, w.qtau, w.cq, w, s);
   token_finalize(d, batch, t0, w, xdt, s);
   feature();
 }
@@ -1060,7 +1074,6 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, v
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Dims d = dims_of(req);
     const int xdt = req->shape.dtype == JOLT_BF16 ? kBF16 : kF32;
-    const int64_t N = d.H * d.T * d.D;
     ck(hipMemsetAsync(w.frob2, 0, sizeof(double) * nt, s));
     ck(hipMemsetAsync(w.status, 0, sizeof(int), s));
     CallHip stage;                                // pinned staging of the upload and the read-back
@@ -1111,7 +1124,6 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, v
         wl.tags = w.tags + t0;
         wl.band_done = ls ? marks[c] : nullptr;
         if (ls && c > 0) ck(hipStreamWaitEvent(sl, marks[c - 1], 0));
-        ck(launch_sumsq(reinterpret_cast<const void* const*>(wl.xptrs), batch, N, xdt, w.frob2 + t0, sl));
         if (d.flash) analyze_flash(d, batch, t0, wl, xdt, req->power_iters, req->seed, hip, sl);
         else analyze_exact(d, batch, t0, wl, xdt, hip, sl);
       }

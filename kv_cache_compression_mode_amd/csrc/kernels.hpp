@@ -114,8 +114,10 @@ size_t syev_top_work_bytes(int64_t n, int R, int batch);
 // status: a device int the bulge chase ORs 1 into when one of its bounded
 // waits gives up (cleared by the caller, read back at its next sync).
 // band_done, when given, is recorded on s once the band reduction is queued.
+// inv_sqrt_scale: eigenvector j comes out multiplied by 1 / sqrt(lam_j) where
+// lam_j > 0 (so X v_j / sqrt(lam_j) has unit norm for the Gram of X).
 hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam, void* work, hipStream_t s,
-                    int* status, hipEvent_t band_done = nullptr);
+                    int* status, hipEvent_t band_done = nullptr, bool inv_sqrt_scale = false);
 // Polls a bulge-chase wave makes before its wait gives up (default 2^22).
 void set_chase_spin_limit(int polls);
 hipError_t copy_cols(const float* in, int64_t ld_in, int64_t in_batch, float* out, int64_t ld_out,
@@ -129,16 +131,17 @@ hipError_t panel_factor(float* A, int64_t m, int64_t ld, int64_t bstride, int64_
 hipError_t householder_qr(float* A, int64_t m, int64_t k, int64_t ld, int64_t batch_stride, int batch,
                           float* work, hipStream_t s);
 
-// Thin QR of full-rank tall column-major U (m x k, k <= cholesky_qr_max_k())
-// by two CholeskyQR passes: U <- Q with Q^T Q = I and U = Q R, diag(R) > 0.
-// U2: a second buffer of U's shape (ld, bstride); work:
-// cholesky_qr_work_floats(m, k, batch) floats.  A column nearly dependent on
-// the earlier ones (a pivot below 2^-10 of its original diagonal) ORs 2 into
-// *status, and U then holds no valid factor: the caller repeats with
+// Thin QR of a full-rank, nearly orthonormal tall column-major U (m x k,
+// k <= cholesky_qr_max_k(); unit-norm columns up to a few percent) by one
+// CholeskyQR pass: Q (U's shape: ld, bstride) receives the factor with
+// Q^T Q = I and U = Q R, diag(R) > 0; U is read only.  work:
+// cholesky_qr_work_floats(m, k, batch) floats.  A column far from orthogonal
+// to the earlier ones (a pivot below half its original diagonal) ORs 2 into
+// *status, and Q then holds no valid factor: the caller repeats with
 // householder_qr.
 int64_t cholesky_qr_max_k();
 size_t cholesky_qr_work_floats(int64_t m, int64_t k, int batch);
-hipError_t cholesky_qr(float* U, float* U2, int64_t m, int64_t k, int64_t ld, int64_t bstride, int batch,
+hipError_t cholesky_qr(const float* U, float* Q, int64_t m, int64_t k, int64_t ld, int64_t bstride, int batch,
                        float* work, int* status, hipStream_t s);
 
 // Sort columns by lam descending (ties: lower index), sign-fix (largest |.| entry

@@ -986,7 +986,7 @@ __device__ __forceinline__ void chol_block_of(int bi, int& I, int& K) {
 // are final and skipped; the upper triangle is never read for a lower
 // element, so it takes whatever the update gives and is zeroed at the end.
 // The pivot's reciprocal square root is the hardware one (about 1 ulp: a
-// perturbation of the factor far below what the second pass removes).
+// relative perturbation of the factor near 2^-23, below the Gram's own rounding).
 __device__ void chol_inv_block(float (*W)[CBP], const float* d0, float pivot_rel, int lane, bool& bad) {
   const int c = lane & 31, h = lane >> 5;
   for (int j = 0; j < CB; ++j) {
@@ -1253,58 +1253,55 @@ size_t cholesky_qr_work_floats(int64_t m, int64_t k, int batch) {
   return static_cast<size_t>(batch) * (2 + cholesky_qr_ksplit(m)) * k * k;
 }
 
-hipError_t cholesky_qr(float* U, float* U2, int64_t m, int64_t k, int64_t ld, int64_t bstride, int batch,
+hipError_t cholesky_qr(const float* U, float* Q, int64_t m, int64_t k, int64_t ld, int64_t bstride, int batch,
                        float* work, int* status, hipStream_t s) {
   if (k < 1 || k > kCholMaxK || m < k) return hipErrorInvalidValue;
   const int ks = cholesky_qr_ksplit(m);
   float* G = work;                                               // [batch][k][k], lower triangle
-  float* Li = G + static_cast<size_t>(batch) * k * k;            // [batch][k][k], L^{-1}
+  float* Li = G + static_cast<size_t>(batch) * k * k;            // [batch][k][k], L^{-1} - I
   float* part = Li + static_cast<size_t>(batch) * k * k;         // [batch][ks][k][k]
   ProfScope ps("cholqr", s);
-  // algorithmic work per pass: U read twice (Gram, product) and written
-  // once; k (k + 1) m flops for the Gram's triangle, m k (k + 1) for the
-  // triangular product, k^3 / 3 for the factorization and inverse
-  prof_add_work("cholqr", 2.0 * batch * (3.0 * 4.0 * m * k),
-                2.0 * batch * (2.0 * k * (k + 1.0) * m + k * k * (k / 3.0)));
+  // algorithmic work: U read twice (Gram, product), Q written once; k (k + 1) m
+  // flops for the Gram's triangle, m k (k + 1) for the triangular product,
+  // k^3 / 3 for the factorization and inverse
+  prof_add_work("cholqr", batch * (3.0 * 4.0 * m * k), batch * (2.0 * k * (k + 1.0) * m + k * k * (k / 3.0)));
   hipError_t e;
-  // pass 1: U2 = U L1^{-T}; pass 2 (U2 nearly orthonormal, L2 near I):
-  // U = U2 + U2 (L2^{-T} - I), so that U2's fp32 values pass through exactly
-  // and only the small correction carries the split products' rounding
-  for (int pass = 0; pass < 2; ++pass) {
-    float* src = pass == 0 ? U : U2;
-    float* dst = pass == 0 ? U2 : U;
-    GemmArgs g{};
-    g.alpha = 1.f;
-    g.a_dtype = g.b_dtype = g.c_dtype = kF32;
-    // G = src^T src (row-major, rows m >= columns n)
-    g.M = k; g.N = k; g.K = m;
-    g.A = src; g.am = plain(ld); g.ak = plain(1); g.a_batch = bstride;
-    g.B = src; g.bk = plain(1); g.bn = plain(ld); g.b_batch = bstride;
-    g.C = G; g.c_m = k; g.c_n = 1; g.c_batch = k * k;
-    g.c_lower = 1;
-    // pass 2 measures the departure from orthonormality (about 1e-6): its
-    // Gram needs fp32-grade products even for columns concentrated on a few rows
-    g.split_f32 = pass == 0 ? 1 : 2;
-    if (ks > 1) { g.ksplit = ks; g.partial = part; }
-    if ((e = launch_gemm(g, batch, s, "cholqr_gemm")) != hipSuccess) return e;
-    k_chol_inv<<<batch, CW * 64, 0, s>>>(G, k * k, static_cast<int>(k), 0x1p-10f, Li, k * k, pass, status);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // dst = src B, B(j, n) = L^{-1}[n][j]; pass 2: dst = src + src (B - I),
-    // the identity's term read from src in the product's epilogue
-    GemmArgs q{};
-    q.alpha = 1.f;
-    q.beta = pass == 0 ? 0.f : 1.f;
-    q.c_in = pass == 0 ? nullptr : src;
-    q.a_dtype = q.b_dtype = q.c_dtype = kF32;
-    q.M = m; q.N = k; q.K = k;
-    q.A = src; q.am = plain(1); q.ak = plain(ld); q.a_batch = bstride;
-    q.B = Li; q.bk = plain(1); q.bn = plain(k); q.b_batch = k * k;
-    q.C = dst; q.c_m = 1; q.c_n = ld; q.c_batch = bstride;
-    q.split_f32 = 1;
-    q.b_upper = 1;
-    if ((e = launch_gemm(q, batch, s, "cholqr_gemm")) != hipSuccess) return e;
-  }
-  return hipSuccess;
+  // G = U^T U (row-major, rows m >= columns n).  U is nearly orthonormal, so
+  // G departs from I by little and that departure is what L carries: the
+  // Gram takes fp32-grade products (three bf16 planes) even for columns
+  // concentrated on a few rows.
+  GemmArgs g{};
+  g.alpha = 1.f;
+  g.a_dtype = g.b_dtype = g.c_dtype = kF32;
+  g.M = k; g.N = k; g.K = m;
+  g.A = U; g.am = plain(ld); g.ak = plain(1); g.a_batch = bstride;
+  g.B = U; g.bk = plain(1); g.bn = plain(ld); g.b_batch = bstride;
+  g.C = G; g.c_m = k; g.c_n = 1; g.c_batch = k * k;
+  g.c_lower = 1;
+  g.split_f32 = 2;
+  if (ks > 1) { g.ksplit = ks; g.partial = part; }
+  if ((e = launch_gemm(g, batch, s, "cholqr_gemm")) != hipSuccess) return e;
+  // a pivot below half its column's original diagonal (the column's part
+  // outside the span of the earlier ones under sqrt(1/2) of its norm) is
+  // more departure from orthonormality than one pass removes to fp32
+  // accuracy: the caller falls back to Householder QR
+  k_chol_inv<<<batch, CW * 64, 0, s>>>(G, k * k, static_cast<int>(k), 0x1p-1f, Li, k * k, 1, status);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // Q = U + U (L^{-T} - I), B(j, n) = (L^{-1} - I)[n][j]: U's fp32 values pass
+  // through exactly (the identity's term, read in the product's epilogue) and
+  // only the small correction carries the split products' rounding
+  GemmArgs q{};
+  q.alpha = 1.f;
+  q.beta = 1.f;
+  q.c_in = U;
+  q.a_dtype = q.b_dtype = q.c_dtype = kF32;
+  q.M = m; q.N = k; q.K = k;
+  q.A = U; q.am = plain(1); q.ak = plain(ld); q.a_batch = bstride;
+  q.B = Li; q.bk = plain(1); q.bn = plain(k); q.b_batch = k * k;
+  q.C = Q; q.c_m = 1; q.c_n = ld; q.c_batch = bstride;
+  q.split_f32 = 1;
+  q.b_upper = 1;
+  return launch_gemm(q, batch, s, "cholqr_gemm");
 }
 
 hipError_t finalize_factor_ws(const float* U_cm, int64_t m, int64_t R, int64_t ld_cm, int64_t cm_batch,

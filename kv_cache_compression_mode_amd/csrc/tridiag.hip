@@ -519,10 +519,14 @@ __global__ __launch_bounds__(256) void k_bisect(const double* d_g, const double*
   if (sub == 0) lam[z * R + q] = 0.5 * (lo + hi);
 }
 
-// Eigenvector of eigenvalue lam[q] by inverse iteration (three solves with
+// Eigenvector of eigenvalue lam[q] by inverse iteration (two solves with
 // T - lam I = L D L^T from a fixed pseudo-random start; the factorization
 // and the first forward substitution share one pass), normalized, fp32
-// out as column q of Z (column-major, ld n).  The factorization keeps the
+// out as column q of Z (column-major, ld n).  With lam within a few ulps of
+// ||T|| of the eigenvalue, each solve shrinks the other eigenvectors'
+// components relative to this one's by about eps ||T|| / gap (under 1e-7 for
+// the gaps these spectra have): two solves reach fp64 level from a random
+// start, past what the fp32 output keeps.  The factorization keeps the
 // reciprocal pivots, so each solve is multiply-only; intermediate vectors
 // are rescaled on the fly.  Scratch rp / y: [i][q] interleaved (coalesced
 // across q).
@@ -577,7 +581,7 @@ __global__ __launch_bounds__(IVW) void k_invit(const double* d_g, const double* 
     }
   }
   double sc = 1.0, s2 = 0.0;
-  for (int it = 0; it < 3; ++it) {
+  for (int it = 0; it < 2; ++it) {
     if (it > 0) {
       // forward: L u = sc * y   (L unit lower, l_i = e_{i-1} / p_{i-1})
       double u = 0.0, rprev = 0.0;
@@ -629,8 +633,10 @@ __global__ __launch_bounds__(IVW) void k_invit(const double* d_g, const double* 
 
 // Z[:, q] = y[:, q] * nrm[q] as fp32, through a 32 x 32 LDS transpose ([i][q]
 // scratch to column-major Z).
+// With lam_scale, column q is also multiplied by 1 / sqrt(lam_scale[q]) where
+// that eigenvalue is positive (in fp64, before the rounding to fp32).
 __global__ __launch_bounds__(256) void k_invit_out(const double* y_g, const double* nrm_g, int64_t n, int R,
-                                                   float* Z, int64_t z_batch) {
+                                                   float* Z, int64_t z_batch, const double* lam_scale) {
   __shared__ float tile[32][33];
   const int64_t z = blockIdx.z;
   const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 32;
@@ -641,7 +647,12 @@ __global__ __launch_bounds__(256) void k_invit_out(const double* y_g, const doub
   for (int k = 0; k < 4; ++k) {
     const int64_t i = i0 + ty + 8 * k;
     const int q = q0 + tx;
-    tile[ty + 8 * k][tx] = (i < n && q < R) ? static_cast<float>(y[i * R + q] * nrm_g[z * R + q]) : 0.f;
+    double f = 0.0;
+    if (q < R) {
+      f = nrm_g[z * R + q];
+      if (lam_scale && lam_scale[z * R + q] > 0.0) f /= sqrt(lam_scale[z * R + q]);
+    }
+    tile[ty + 8 * k][tx] = (i < n && q < R) ? static_cast<float>(y[i * R + q] * f) : 0.f;
   }
   __syncthreads();
 #pragma unroll
@@ -1393,7 +1404,7 @@ std::atomic<int> g_chase_spin_limit{1 << 22};
 void set_chase_spin_limit(int polls) { g_chase_spin_limit.store(polls < 0 ? 0 : polls); }
 
 hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam_out, void* work,
-                    hipStream_t s, int* status, hipEvent_t band_done) {
+                    hipStream_t s, int* status, hipEvent_t band_done, bool inv_sqrt_scale) {
   if (n % SBW != 0 || n > 32768 || R < 1 || R > n || !status) return hipErrorInvalidValue;
   const SyevLayout Lw = syev_layout(n, R, batch);
   char* wb = static_cast<char*>(work);
@@ -1543,7 +1554,7 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
       k_invit<<<dim3(gx, batch), IVW, 0, s>>>(dd, ee, n, R, lam, dp, yv, nrm);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       k_invit_out<<<dim3(static_cast<unsigned>((n + 31) / 32), static_cast<unsigned>((R + 31) / 32), batch), 256, 0,
-                    s>>>(yv, nrm, n, R, Z, n * n);
+                    s>>>(yv, nrm, n, R, Z, n * n, inv_sqrt_scale ? lam : nullptr);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (lam_out) {
