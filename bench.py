@@ -354,8 +354,8 @@ ROOF = {
              "output counts the symmetric half, M (M + 1) K flops)",
              "k_gemm_x_gram", None, ("gemm.hip", "device.hpp"), MFMA_BF16_PEAK_TFLOPS, "mfma"),
     "encode_residual": ("k_encode_residual_many: reconstruction U~_T (G~ U~_D^T), residual, JL rotation R Q^T, "
-                        "group quantization and packing in one pass over X (bf16 matrix cores over exact "
-                        "three-part splits)",
+                        "group quantization and packing in one pass over X (bf16 matrix cores over two-part "
+                        "splits)",
                         "k_encode_residual_many", r"k_encode_residual(_many)?<", ("codec.hip", "device.hpp"),
                         MFMA_BF16_PEAK_TFLOPS, "mfma"),
     "decode": ("k_decode: X^ = U~_T W + Y^ Q with dequantization fused, all records of a launch (bf16 matrix "

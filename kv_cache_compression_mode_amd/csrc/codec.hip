@@ -118,29 +118,27 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 raw) { return *reinterpret_cas
 
 // ------------------------------------------------------------------ encode
 // Both products of the encoder run on bf16 matrix cores (32x32x16, fp32
-// accumulate) over exact three-part splits of their fp32 operands: f = hi +
-// mid + lo with hi = rne_bf16(f), mid = rne_bf16(f - hi) and lo = f - hi - mid,
-// which has at most 8 significant bits and is therefore a bf16 itself.  Every
-// product of two bf16 values is exact in fp32, so the splits cost accuracy
-// only through the terms left out (below 2^-25 relative per product) and the
-// fp32 accumulation, which keeps the large hi x hi terms in an accumulator of
-// their own and adds the small ones in a second.
+// accumulate) over two-part splits of their fp32 operands: f = hi + lo + r
+// with hi = rne_bf16(f), lo = rne_bf16(f - hi) and |r| <= 2^-18 |f|.  Every
+// product of two bf16 values is exact in fp32; the reconstruction U~_T (hi +
+// lo) of exact bf16 U~_T and the rotation's hi hi + hi lo + lo hi leave out
+// terms below 2^-17 relative per product (lo lo and the remainders r), and
+// the fp32 accumulation keeps the large hi x hi terms in an accumulator of
+// their own and adds the small ones in a second.  That error is some 10^4
+// times below the quantization step the residual then takes.
 
 __device__ __forceinline__ uint16_t rne_bits(float f) {   // finite f
   uint32_t u = __float_as_uint(f);
   u += 0x7fffu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
 }
-__device__ __forceinline__ void split3(float f, uint16_t& h, uint16_t& m, uint16_t& l) {
+__device__ __forceinline__ void split2(float f, uint16_t& h, uint16_t& l) {
   h = rne_bits(f);
-  const float r1 = f - bf16_bits_to_f32(h);        // exact
-  m = rne_bits(r1);
-  const float r2 = r1 - bf16_bits_to_f32(m);       // exact, <= 8 significant bits
-  l = static_cast<uint16_t>(__float_as_uint(r2) >> 16);
+  l = rne_bits(f - bf16_bits_to_f32(h));           // the difference is exact
 }
 
-// W_h = G~_h U~_D^T in three bf16 parts, stored in matrix-core fragment
-// order: W3[p][h][cb][ks][lane][e] (cb < 4 blocks of 32 features, ks < r_Tp/16
+// W_h = G~_h U~_D^T in two bf16 parts, stored in matrix-core fragment
+// order: W2[p][h][cb][ks][lane][e] (cb < 4 blocks of 32 features, ks < r_Tp/16
 // steps of 16 values of k, lane = 32 half + r) holds part p of W_h[k][d] for
 // d = 32 cb + r, k = 16 ks + 8 half + e, so the B operand of one k step of one
 // wave is 1 KB of consecutive bytes; k >= r_T is zero, r_Tp a multiple of 64
@@ -149,15 +147,15 @@ __device__ __forceinline__ void split3(float f, uint16_t& h, uint16_t& m, uint16
 // matrix cores (the factors are bf16, so the products are exact and only the
 // fp32 sum rounds).  Tensor j of a launch reads G~_h from Gp[j H + h] and
 // U~_D from Udp[j H + h] (or G0 + h r_T r_D and Ud0 when Gp is null) and
-// writes W3 + j w3_batch.
+// writes W2 + j w2_batch.
 __global__ __launch_bounds__(64) void k_enc_w(const uint16_t* const* Gp, const uint16_t* const* Udp,
-                                              const uint16_t* G0, const uint16_t* Ud0, uint16_t* W3,
-                                              int64_t w3_batch, int H, int r_T, int r_D, int r_Tp) {
+                                              const uint16_t* G0, const uint16_t* Ud0, uint16_t* W2,
+                                              int64_t w2_batch, int H, int r_T, int r_D, int r_Tp) {
   const int lane = threadIdx.x, r = lane & 31, half = lane >> 5;
   const int k0 = blockIdx.x * 32, h = blockIdx.y, j = blockIdx.z;
   const uint16_t* G = Gp ? Gp[static_cast<int64_t>(j) * H + h] : G0 + static_cast<int64_t>(h) * r_T * r_D;
   const uint16_t* Ud = Udp ? Udp[static_cast<int64_t>(j) * H + h] : Ud0;
-  uint16_t* out = W3 + j * w3_batch;
+  uint16_t* out = W2 + j * w2_batch;
   const bool ga = (r_D % 8) == 0 && (reinterpret_cast<uintptr_t>(G) & 15) == 0 &&
                   (reinterpret_cast<uintptr_t>(Ud) & 15) == 0;
   const int k = k0 + r;
@@ -179,12 +177,11 @@ __global__ __launch_bounds__(64) void k_enc_w(const uint16_t* const* Gp, const u
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int dr = (i >> 2) * 8 + half * 4 + (i & 3);     // feature 32 ct + dr
-      uint16_t hb, mb, lb;
-      split3(acc[ct][i], hb, mb, lb);
+      uint16_t hb, lb;
+      split2(acc[ct][i], hb, lb);
       const int64_t off = fb + (fl + dr) * 8;
       out[off] = hb;
-      out[part + off] = mb;
-      out[2 * part + off] = lb;
+      out[part + off] = lb;
     }
   }
 }
@@ -193,22 +190,23 @@ __global__ __launch_bounds__(64) void k_enc_w(const uint16_t* const* Gp, const u
 //  1. recon = U~_T[t0 .. t0+64) W_h: wave w computes features [32w, 32w+32)
 //     of both 32-row blocks.  U~_T is staged in LDS in chunks of 64 values
 //     of k (whole 128-byte rows of the chunk, double-buffered, shared by the
-//     waves); the W parts stream from memory in fragment order, two k steps
-//     ahead; hi x hi in one accumulator, the rest in another.
+//     waves); the two W parts stream from memory in fragment order, two k
+//     steps ahead; hi in one accumulator, lo in another.
 //  2. recon is staged in LDS; thread (m, g) = (tid / 4, tid % 4) takes its
 //     32 features of group g of row m, forms R = X - recon and stores R's
-//     three bf16 parts in LDS as [part][row][feature].
-//  3. Y = R Q^T with A = the R parts from LDS and B = the Q parts (bf16, in
-//     fragment order like W, in cache), six products per step (hi hi,
-//     hi mid, mid hi, hi lo, lo hi, mid mid).
+//     two bf16 parts in LDS as [part][row][feature].
+//  3. Y = R Q^T with A = the R parts from LDS and B = the first two Q parts
+//     (bf16, in fragment order like W, in cache), three products per step
+//     (hi hi, hi lo, lo hi).
 //  4. Y is staged in LDS and thread (m, g) quantizes group g of row m.
 constexpr int ER = 64;                         // rows per workgroup
 constexpr int EYS = 144;                       // fp32 row stride of staged recon / Y (group g at 36 g)
 constexpr int ERS = 136;                       // bf16 row stride of the staged R parts
-constexpr int kEncLds = 3 * ER * ERS * 2;      // 52224 bytes >= ER * EYS * 4
+constexpr int kEncLds = ER * EYS * 4;          // 36864 bytes: staged recon / Y
 constexpr int EUC = 64;                        // k per staged U~_T chunk
 constexpr int EUS = EUC + 8;                   // bf16 row stride of a staged U~_T chunk
 static_assert(2 * ER * EUS * 2 <= kEncLds, "U~_T chunks fit the staging area");
+static_assert(2 * ER * ERS * 2 <= kEncLds, "the R parts fit the staging area");
 
 // UV: rows of U~_T are 16-byte aligned (r_T % 8 == 0 and an aligned base), so
 // a chunk is read with 16-byte loads; otherwise element by element.
@@ -228,7 +226,7 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, float* lds_f, u
     const int64_t rT = a.r_T;
     const int KS = static_cast<int>(a.r_Tp / 16);
     const int64_t part = a.H * D * a.r_Tp;
-    const uint16_t* wb = a.W3 + ((h * 4 + wave) * KS) * 512 + lane * 8;
+    const uint16_t* wb = a.W2 + ((h * 4 + wave) * KS) * 512 + lane * 8;
     // U~_T chunk loader: row ur = tid / 4, k = 16 (tid % 4) .. +16 of the chunk
     const int ur = tid >> 2, uk = 16 * (tid & 3);
     const int64_t ut = t0 + ur;
@@ -269,12 +267,11 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, float* lds_f, u
     const int nks = KS;                            // a multiple of 4 (r_Tp of the encoder: 64 k)
     // W fragments in a ring of four k steps, loaded two steps ahead (a slot
     // is refilled only after its step's products are issued)
-    uint4 wf[4][3];
+    uint4 wf[4][2];
     auto load_w = [&](int slot, int ks) {         // steps past the end reload the last one (unused)
       const uint16_t* src = wb + static_cast<int64_t>(ks < nks ? ks : nks - 1) * 512;
       wf[slot][0] = ldg16(src);
       wf[slot][1] = ldg16(src + part);
-      wf[slot][2] = ldg16(src + 2 * part);
     };
     load_u(0);
     load_w(0, 0);
@@ -290,14 +287,12 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, float* lds_f, u
       for (int s4 = 0; s4 < EUC / 16; ++s4) {
         const int ks = c0 + s4;
         {                                             // ks % 4 == s4: chunks start at multiples of 4
-          const bf16x8 bh = as_bf16x8(wf[s4][0]), bm = as_bf16x8(wf[s4][1]), bl = as_bf16x8(wf[s4][2]);
+          const bf16x8 bh = as_bf16x8(wf[s4][0]), bl = as_bf16x8(wf[s4][1]);
           load_w((s4 + 2) & 3, ks + 2);
           const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const uint4*>(ua + 16 * s4));
           const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const uint4*>(ua + 32 * EUS + 16 * s4));
           hi0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bh, hi0, 0, 0, 0);
           hi1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bh, hi1, 0, 0, 0);
-          lo0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bm, lo0, 0, 0, 0);
-          lo1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bm, lo1, 0, 0, 0);
           lo0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bl, lo0, 0, 0, 0);
           lo1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bl, lo1, 0, 0, 0);
         }
@@ -366,14 +361,13 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, float* lds_f, u
     __syncthreads();                              // the R parts overwrite the staged recon
   }
   {
-    uint32_t wh[16], wm[16], wl[16];
+    uint32_t wh[16], wl[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      uint16_t h0, m0, l0, h1, m1, l1;
-      split3(x[2 * e], h0, m0, l0);
-      split3(x[2 * e + 1], h1, m1, l1);
+      uint16_t h0, l0, h1, l1;
+      split2(x[2 * e], h0, l0);
+      split2(x[2 * e + 1], h1, l1);
       wh[e] = h0 | (static_cast<uint32_t>(h1) << 16);
-      wm[e] = m0 | (static_cast<uint32_t>(m1) << 16);
       wl[e] = l0 | (static_cast<uint32_t>(l1) << 16);
     }
     uint16_t* row = rp + qm * ERS + 32 * qg;
@@ -381,8 +375,6 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, float* lds_f, u
     for (int q = 0; q < 4; ++q) {
       *reinterpret_cast<uint4*>(row + 8 * q) = make_uint4(wh[4 * q], wh[4 * q + 1], wh[4 * q + 2], wh[4 * q + 3]);
       *reinterpret_cast<uint4*>(row + ER * ERS + 8 * q) =
-          make_uint4(wm[4 * q], wm[4 * q + 1], wm[4 * q + 2], wm[4 * q + 3]);
-      *reinterpret_cast<uint4*>(row + 2 * ER * ERS + 8 * q) =
           make_uint4(wl[4 * q], wl[4 * q + 1], wl[4 * q + 2], wl[4 * q + 3]);
     }
   }
@@ -392,13 +384,12 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, float* lds_f, u
   {
     // Q parts in fragment order: [p][cb][ds][lane][e] = part p of Q[32 cb + r][16 ds + 8 half + e]
     const uint16_t* qb = a.Q3 + wave * (D / 16) * 512 + lane * 8;
-    uint4 qf[4][3];                               // ring of four d steps, two ahead
+    uint4 qf[4][2];                               // ring of four d steps, two ahead
     auto load_q = [&](int slot, int ds) {
       if (ds < D / 16) {
         const uint16_t* src = qb + ds * 512;
         qf[slot][0] = ldg16(src);
         qf[slot][1] = ldg16(src + D * D);
-        qf[slot][2] = ldg16(src + 2 * D * D);
       }
     };
     load_q(0, 0);
@@ -407,26 +398,18 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, float* lds_f, u
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
       const int d0 = 16 * ds, slot = ds & 3;
-      const bf16x8 qh = as_bf16x8(qf[slot][0]), qm_ = as_bf16x8(qf[slot][1]), ql = as_bf16x8(qf[slot][2]);
+      const bf16x8 qh = as_bf16x8(qf[slot][0]), ql = as_bf16x8(qf[slot][1]);
       load_q((ds + 2) & 3, ds + 2);
       const bf16x8 h0 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + d0));
       const bf16x8 h1 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + 32 * ERS + d0));
-      const bf16x8 m0 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + ER * ERS + d0));
-      const bf16x8 m1 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + (ER + 32) * ERS + d0));
-      const bf16x8 l0 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + 2 * ER * ERS + d0));
-      const bf16x8 l1 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + (2 * ER + 32) * ERS + d0));
+      const bf16x8 l0 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + ER * ERS + d0));
+      const bf16x8 l1 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + (ER + 32) * ERS + d0));
       yh0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, qh, yh0, 0, 0, 0);
       yh1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, qh, yh1, 0, 0, 0);
-      yl0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, qm_, yl0, 0, 0, 0);
-      yl1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, qm_, yl1, 0, 0, 0);
-      yl0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(m0, qh, yl0, 0, 0, 0);
-      yl1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(m1, qh, yl1, 0, 0, 0);
       yl0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, ql, yl0, 0, 0, 0);
       yl1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, ql, yl1, 0, 0, 0);
       yl0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l0, qh, yl0, 0, 0, 0);
       yl1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(l1, qh, yl1, 0, 0, 0);
-      yl0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(m0, qm_, yl0, 0, 0, 0);
-      yl1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(m1, qm_, yl1, 0, 0, 0);
     }
   }
   __syncthreads();                                // Y overwrites the R parts
@@ -456,7 +439,7 @@ __device__ __forceinline__ void encode_any(const EncodeArgs& a, uint32_t tile, u
   else encode_tile<TX, false>(a, lds_f, tile, head);
 }
 template <typename TX>
-__global__ __launch_bounds__(256, 3) void k_encode_residual(EncodeArgs a) {
+__global__ __launch_bounds__(256, 4) void k_encode_residual(EncodeArgs a) {
   uint32_t tile, head;
   xcd_group_2d(tile, head);                        // the row tiles of one head on one XCD
   encode_any<TX>(a, tile, head);
@@ -465,7 +448,7 @@ __global__ __launch_bounds__(256, 3) void k_encode_residual(EncodeArgs a) {
 // the tiles of one tensor run on one XCD, whose L2 then holds the tensor's W
 // parts and U~_T rows (each used by many tiles).
 template <typename TX>
-__global__ __launch_bounds__(256, 3) void k_encode_residual_many(const EncodeArgs* list) {
+__global__ __launch_bounds__(256, 4) void k_encode_residual_many(const EncodeArgs* list) {
   uint32_t tensor, idx;
   xcd_group(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), gridDim.x * gridDim.y, gridDim.z, tensor,
             idx);
@@ -740,12 +723,12 @@ hipError_t launch_quantize(const float* Y, int64_t rows, int bits, uint16_t* sca
 }
 
 hipError_t launch_enc_w(const uint16_t* const* Gp, const uint16_t* const* Udp, const uint16_t* G0,
-                        const uint16_t* Ud0, uint16_t* W3, int64_t w3_batch, int n, int H, int r_T, int r_D,
+                        const uint16_t* Ud0, uint16_t* W2, int64_t w2_batch, int n, int H, int r_T, int r_D,
                         int r_Tp, hipStream_t s) {
   if (n <= 0 || r_T <= 0) return hipSuccess;
   if (r_Tp % 64 != 0 || r_Tp < r_T) return hipErrorInvalidValue;
   ProfScope ps("encode_w", s);
-  k_enc_w<<<dim3(r_Tp / 32, H, n), 64, 0, s>>>(Gp, Udp, G0, Ud0, W3, w3_batch, H, r_T, r_D, r_Tp);
+  k_enc_w<<<dim3(r_Tp / 32, H, n), 64, 0, s>>>(Gp, Udp, G0, Ud0, W2, w2_batch, H, r_T, r_D, r_Tp);
   return hipGetLastError();
 }
 

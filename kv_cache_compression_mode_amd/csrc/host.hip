@@ -950,7 +950,7 @@ EncManyLayout enc_many_layout(int n, const jolt_shape* shape, const jolt_choice*
     const size_t m = e - b, rT = ch[idx[b]].r_T;
     L.groups.emplace_back(static_cast<int>(b), static_cast<int>(e));
     L.w_off.push_back(off);
-    off += a256(6ull * m * H * D * enc_rtp(static_cast<int>(rT)));
+    off += a256(4ull * m * H * D * enc_rtp(static_cast<int>(rT)));
     L.p_off.push_back(off);
     off += a256(4ull * m * rT * HD);
     L.part_off.push_back(off);
@@ -988,7 +988,7 @@ int32_t jolt_spectrum_len(const jolt_alloc_req* req) {
 size_t jolt_encode_workspace_bytes(const jolt_shape* shape, jolt_choice c) {
   if (!shape_ok(shape) || !choice_ok(shape, c)) return 0;
   const size_t w = a256(4ull * shape->H * c.r_T * shape->D);
-  return a256(6ull * shape->H * shape->D * enc_rtp(c.r_T)) + w + a256(w * encode_ksplit(shape->T)) + 256;
+  return a256(4ull * shape->H * shape->D * enc_rtp(c.r_T)) + w + a256(w * encode_ksplit(shape->T)) + 256;
 }
 
 size_t jolt_decode_workspace_bytes(const jolt_shape* shape, jolt_choice c) {
@@ -1204,8 +1204,8 @@ jolt_status jolt_encode(const jolt_shape* shape, const void* x_dev, jolt_choice 
     uint16_t* Ud = reinterpret_cast<uint16_t*>(blob + L.ud);
     uint16_t* G = reinterpret_cast<uint16_t*>(blob + L.g);
     const int64_t rTp = enc_rtp(c.r_T);
-    uint16_t* W3 = static_cast<uint16_t*>(ws_dev);
-    float* P = reinterpret_cast<float*>(static_cast<char*>(ws_dev) + a256(6ull * H * D * rTp));
+    uint16_t* W2 = static_cast<uint16_t*>(ws_dev);
+    float* P = reinterpret_cast<float*>(static_cast<char*>(ws_dev) + a256(4ull * H * D * rTp));
     const size_t n = static_cast<size_t>(D) * D;
     const uint16_t* Q3 = reinterpret_cast<const uint16_t*>(static_cast<const char*>(rot_dev) + 2 * a256(4 * n) +
                                                            a256(2 * n));
@@ -1228,13 +1228,13 @@ jolt_status jolt_encode(const jolt_shape* shape, const void* x_dev, jolt_choice 
       g2.B = Ud; g2.b_dtype = kBF16; g2.bk = plain(rD); g2.bn = plain(1); g2.b_batch = 0;
       g2.C = G; g2.c_dtype = kBF16; g2.c_m = rD; g2.c_n = 1; g2.c_batch = rT * rD;
       ck(launch_gemm(g2, static_cast<int>(H), s));
-      // W_h = G~_h U~_D^T in three bf16 parts, [part][h][d][k]
-      ck(launch_enc_w(nullptr, nullptr, G, Ud, W3, 0, 1, static_cast<int>(H), static_cast<int>(rT),
+      // W_h = G~_h U~_D^T in two bf16 parts (hi, lo), [part][h][d][k]
+      ck(launch_enc_w(nullptr, nullptr, G, Ud, W2, 0, 1, static_cast<int>(H), static_cast<int>(rT),
                       static_cast<int>(rD), static_cast<int>(rTp), s));
     }
     EncodeArgs ea{};
     ea.X = x_dev; ea.x_dtype = xdt; ea.H = H; ea.T = T;
-    ea.Ut = tucker ? Ut : nullptr; ea.W3 = tucker ? W3 : nullptr; ea.r_T = rT; ea.r_Tp = tucker ? rTp : 0;
+    ea.Ut = tucker ? Ut : nullptr; ea.W2 = tucker ? W2 : nullptr; ea.r_T = rT; ea.r_Tp = tucker ? rTp : 0;
     ea.Q3 = Q3; ea.bits = c.bits;
     ea.scales = reinterpret_cast<uint16_t*>(blob + L.sc);
     ea.codes = reinterpret_cast<uint8_t*>(blob + L.cd);
@@ -1327,7 +1327,7 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
           ptr[q.g3a + k] = blob(i) + B.g + 2ull * h * rT * rD;
           ptr[q.g3b + k] = blob(i) + B.ud;
         }
-        Wslot[i] = W + static_cast<size_t>(j) * 3 * H * D * rTp;
+        Wslot[i] = W + static_cast<size_t>(j) * 2 * H * D * rTp;
       }
     }
     const size_t blob_slot = slots(n);
@@ -1339,7 +1339,7 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
       ea = EncodeArgs{};
       ea.X = x_dev[i]; ea.x_dtype = xdt; ea.H = H; ea.T = T;
       ea.Ut = c.r_T > 0 ? reinterpret_cast<const uint16_t*>(blob(i) + B.ut) : nullptr;
-      ea.W3 = Wslot[i]; ea.r_T = c.r_T; ea.r_Tp = c.r_T > 0 ? enc_rtp(c.r_T) : 0;
+      ea.W2 = Wslot[i]; ea.r_T = c.r_T; ea.r_Tp = c.r_T > 0 ? enc_rtp(c.r_T) : 0;
       ea.Q3 = Q3; ea.bits = c.bits;
       ea.scales = reinterpret_cast<uint16_t*>(blob(i) + B.sc);
       ea.codes = reinterpret_cast<uint8_t*>(blob(i) + B.cd);
@@ -1403,11 +1403,11 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
       g2.c_ptrs = reinterpret_cast<void* const*>(dp(q.g2c)); g2.c_dtype = kBF16; g2.c_m = rD; g2.c_n = 1;
       g2.ptr_align16 = al16 ? 1 : 0;
       ck(launch_gemm(g2, static_cast<int>(m * H), s));
-      // W_h = G~_h U~_D^T per (tensor, head), in three bf16 parts
+      // W_h = G~_h U~_D^T per (tensor, head), in two bf16 parts (hi, lo)
       const int64_t rTp = enc_rtp(static_cast<int>(rT));
       ck(launch_enc_w(reinterpret_cast<const uint16_t* const*>(dp(q.g3a)),
                       reinterpret_cast<const uint16_t* const*>(dp(q.g3b)), nullptr, nullptr,
-                      reinterpret_cast<uint16_t*>(ws + L.w_off[g]), 3 * H * D * rTp, m, static_cast<int>(H),
+                      reinterpret_cast<uint16_t*>(ws + L.w_off[g]), 2 * H * D * rTp, m, static_cast<int>(H),
                       static_cast<int>(rT), static_cast<int>(rD), static_cast<int>(rTp), s));
     }
     if (prof_enabled("encode_residual")) {
@@ -1567,7 +1567,7 @@ jolt_status jolt_xl_decode(int32_t n, const jolt_shape* shape, int32_t r, const 
 // scales fp32, B = X_new W^T and P = B Z diag(1/lambda) [dT][rp], U_new fp32
 // [dT][r_T], the eigensolver's scratch, the encoder's W parts, status.
 struct AppendLayout {
-  size_t W, M, Z, lam, inv, B, P, U, syev, W3, status, total;
+  size_t W, M, Z, lam, inv, B, P, U, syev, W2, status, total;
   int64_t rp;
 };
 AppendLayout append_layout(const jolt_shape* sh, int32_t dT, jolt_choice c) {
@@ -1584,7 +1584,7 @@ AppendLayout append_layout(const jolt_shape* sh, int32_t dT, jolt_choice c) {
   L.P = off; off += a256(4ull * dT * L.rp);
   L.U = off; off += a256(4ull * dT * c.r_T);
   L.syev = off; off += a256(syev_top_work_bytes(L.rp, static_cast<int>(L.rp), 1));
-  L.W3 = off; off += a256(6ull * sh->H * sh->D * enc_rtp(c.r_T));
+  L.W2 = off; off += a256(4ull * sh->H * sh->D * enc_rtp(c.r_T));
   L.status = off; off += 256;
   L.total = off;
   return L;
@@ -1683,13 +1683,13 @@ jolt_status jolt_append(const jolt_shape* base, jolt_choice choice, const void* 
     ck(launch_to_bf16(U, rT, Ut1, dT, rT, s));
     // the residual against the stored parts, rotated and quantized
     const int64_t rTp = enc_rtp(choice.r_T);
-    uint16_t* W3 = reinterpret_cast<uint16_t*>(ws + L.W3);
-    ck(launch_enc_w(nullptr, nullptr, G1, Ud1, W3, 0, 1, static_cast<int>(H), static_cast<int>(rT),
+    uint16_t* W2 = reinterpret_cast<uint16_t*>(ws + L.W2);
+    ck(launch_enc_w(nullptr, nullptr, G1, Ud1, W2, 0, 1, static_cast<int>(H), static_cast<int>(rT),
                     static_cast<int>(rD), static_cast<int>(rTp), s));
     const size_t n = static_cast<size_t>(D) * D;
     EncodeArgs ea{};
     ea.X = x_new_dev; ea.x_dtype = xdt; ea.H = H; ea.T = dT;
-    ea.Ut = Ut1; ea.W3 = W3; ea.r_T = rT; ea.r_Tp = rTp;
+    ea.Ut = Ut1; ea.W2 = W2; ea.r_T = rT; ea.r_Tp = rTp;
     ea.Q3 = reinterpret_cast<const uint16_t*>(static_cast<const char*>(rot_dev) + 2 * a256(4 * n) + a256(2 * n));
     ea.bits = choice.bits;
     ea.scales = reinterpret_cast<uint16_t*>(b1 + B1.sc);

@@ -101,15 +101,16 @@ def residual_bound_factors(r_T: int, r_D: int, D: int):
     and |dY| <= |dR||Q|^T + g_Y |R||Q|^T, in units of 2^-24.
 
     The encoder forms W_h = G~_h U~_D^T with r_D fp32 additions of exact bf16
-    products, splits fp32 operands exactly into bf16 parts hi + mid + lo
-    (|mid| <= 2^-9 (1 + 2^-8) |f|, |lo| <= 2^-18 |f|) and accumulates in fp32:
-    recon = U~_T hi (r_T terms) + U~_T (mid + lo) (2 r_T terms of total size
-    <= 2^-8 of the first), then one addition -> r_D + r_T + r_T/256 + 1
-    (+ slack); Y = R_hi Q_hi (D terms) + five cross products (5 D terms of
-    total size <= 2^-8) + dropped mid x lo, lo x mid, lo x lo (<= 2^-26) + one
-    addition + the fp32 rounding of Q -> D + 2.5 + 0.25 + 1 + 1.  Bounds:
-    (1 + 2^-5) r_T + r_D + 4 and D + 6."""
-    return (1 + 2.0 ** -5) * r_T + r_D + 4, D + 6
+    products and splits fp32 operands into two bf16 parts, f = hi + lo + r
+    (hi = rne(f), lo = rne(f - hi), |lo| <= 2^-9 (1 + 2^-8) |f|, the dropped
+    |r| <= 2^-18 |f| = 64 units), accumulating in fp32: recon = U~_T hi (r_T
+    terms) + U~_T lo (r_T terms of total size <= 2^-8 of the first) + one
+    addition, and W's remainder r -> r_D + r_T + r_T/256 + 64 + 1 (+ slack);
+    Y = R_hi Q_hi (D terms) + R_hi Q_lo + R_lo Q_hi (2 D terms of total size
+    <= 2^-8) + dropped R_lo Q_lo and the remainders of R and Q (3 x 64) + one
+    addition + the fp32 rounding of Q -> D + D/128 + 192 + 1 + 1.  Bounds:
+    (1 + 2^-5) r_T + r_D + 68 and D + 200."""
+    return (1 + 2.0 ** -5) * r_T + r_D + 68, D + 200
 
 
 def oracle_rows(X_rows: np.ndarray, parts: dict, choice, Q: np.ndarray, hs, ts):
