@@ -28,6 +28,7 @@
 
 #include "device.hpp"
 #include "kernels.hpp"
+#include "qr_reg.hpp"
 
 #include <cfloat>
 #include <vector>
@@ -1261,21 +1262,13 @@ __global__ __launch_bounds__(256) void k_w_form(int mp, const float* V_g, int64_
 }
 
 // A22 -= [V W] [W V]^T on the 64 x 64 tile (bi, bj), bi >= bj, of the lower
-// triangle; the diagonal tiles keep their upper part.
-__global__ __launch_bounds__(256) void k_syr2k(float* A, int64_t n, int64_t a_batch, int mp, const float* VW_g,
-                                               int64_t vw_batch) {
-  __shared__ float As[2 * SBW][SY + 1];  // [V W] rows of the tile's rows: As[k][r]
-  __shared__ float Bs[2 * SBW][SY + 1];  // [W V] rows of the tile's columns: Bs[k][r]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
-  uint32_t bx, by;
-  xcd_group_2d(bx, by);                            // the tiles of one matrix on one XCD
-  const int64_t z = by;
-  // tile (bi, bj) from the linear index x = bi (bi + 1) / 2 + bj
-  const int x = static_cast<int>(bx);
-  int bi = static_cast<int>((sqrtf(8.f * x + 1.f) - 1.f) * 0.5f);
-  while (bi * (bi + 1) / 2 > x) --bi;
-  while ((bi + 1) * (bi + 2) / 2 <= x) ++bi;
-  const int bj = x - bi * (bi + 1) / 2;
+// triangle of matrix z; the diagonal tiles keep their upper part.  256
+// threads (tid < 256, four waves); an inactive caller issues no memory
+// operation but takes the same three barriers as an active one.
+__device__ __forceinline__ void syr2k_tile(float* A, int64_t n, int64_t a_batch, int mp, const float* VW_g,
+                                           int64_t vw_batch, int64_t z, int bi, int bj, int tid, bool active,
+                                           float (*As)[SY + 1], float (*Bs)[SY + 1]) {
+  const int lane = tid & 63, wave = tid >> 6, rl = lane & 31, hf = lane >> 5;
   const int i0 = SY * bi, j0 = SY * bj;
   float* a = A + z * a_batch;
   const float* VW = VW_g + z * vw_batch;
@@ -1283,14 +1276,15 @@ __global__ __launch_bounds__(256) void k_syr2k(float* A, int64_t n, int64_t a_ba
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int idx = tid + 256 * q, c = idx >> 4, r4 = (idx & 15) * 4;
-    rc[q] = (i0 + r4 < mp && j0 + c < mp)
+    rc[q] = (active && i0 + r4 < mp && j0 + c < mp)
                 ? *reinterpret_cast<const float4*>(a + static_cast<int64_t>(j0 + c) * n + i0 + r4)
                 : make_float4(0.f, 0.f, 0.f, 0.f);
     // operand column k = c: [V W] column c at rows i0.., [W V] column c = [V W] column c ^ 32 at rows j0..
-    ra[q] = i0 + r4 < mp ? *reinterpret_cast<const float4*>(VW + static_cast<int64_t>(c) * mp + i0 + r4)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-    rb[q] = j0 + r4 < mp ? *reinterpret_cast<const float4*>(VW + static_cast<int64_t>(c ^ SBW) * mp + j0 + r4)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    ra[q] = (active && i0 + r4 < mp) ? *reinterpret_cast<const float4*>(VW + static_cast<int64_t>(c) * mp + i0 + r4)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    rb[q] = (active && j0 + r4 < mp)
+                ? *reinterpret_cast<const float4*>(VW + static_cast<int64_t>(c ^ SBW) * mp + j0 + r4)
+                : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -1316,7 +1310,7 @@ __global__ __launch_bounds__(256) void k_syr2k(float* A, int64_t n, int64_t a_ba
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int idx = tid + 256 * q, c = idx >> 4, r4 = (idx & 15) * 4;
-    if (i0 + r4 < mp && j0 + c < mp) {
+    if (active && i0 + r4 < mp && j0 + c < mp) {
       const int gc = j0 + c;
       float4 v = rc[q];
       if (i0 + r4 >= gc) v.x -= As[c][r4];
@@ -1326,6 +1320,65 @@ __global__ __launch_bounds__(256) void k_syr2k(float* A, int64_t n, int64_t a_ba
       *reinterpret_cast<float4*>(a + static_cast<int64_t>(gc) * n + i0 + r4) = v;
     }
   }
+}
+
+// tile (bi, bj), bi >= bj, of the lower triangle from its linear index x = bi (bi + 1) / 2 + bj
+__device__ __forceinline__ void tri_tile(int x, int& bi, int& bj) {
+  bi = static_cast<int>((sqrtf(8.f * x + 1.f) - 1.f) * 0.5f);
+  while (bi * (bi + 1) / 2 > x) --bi;
+  while ((bi + 1) * (bi + 2) / 2 <= x) ++bi;
+  bj = x - bi * (bi + 1) / 2;
+}
+
+// Every tile of the lower triangle (col0_only: the tiles (bi, 0) of the first
+// block column, one per workgroup).
+__global__ __launch_bounds__(256) void k_syr2k(float* A, int64_t n, int64_t a_batch, int mp, const float* VW_g,
+                                               int64_t vw_batch, int col0_only) {
+  __shared__ float As[2 * SBW][SY + 1];  // [V W] rows of the tile's rows: As[k][r]
+  __shared__ float Bs[2 * SBW][SY + 1];  // [W V] rows of the tile's columns: Bs[k][r]
+  uint32_t bx, by;
+  xcd_group_2d(bx, by);                            // the tiles of one matrix on one XCD
+  int bi, bj;
+  if (col0_only) { bi = static_cast<int>(bx); bj = 0; }
+  else tri_tile(static_cast<int>(bx), bi, bj);
+  syr2k_tile(A, n, a_batch, mp, VW_g, vw_batch, by, bi, bj, threadIdx.x, true, As, Bs);
+}
+
+// One launch for the tail of panel p's update and the next panel's QR, which
+// do not touch each other's data: workgroups 0 .. batch-1 factor panel p + 1
+// (its columns, the first block column of A22, were updated by k_syr2k's
+// col0_only launch before), the others update the tiles (bi, bj), bj >= 1,
+// two tiles per workgroup (a tile per 256 threads).  The QR workgroups come
+// first in dispatch order, so they start at once and the tiles fill the
+// rest of the chip beside them.
+constexpr size_t kTileLds = 2 * sizeof(float) * 2 * SBW * (SY + 1);   // As + Bs of one tile
+constexpr size_t kBandStepLds = 2 * kTileLds > sizeof(QrRegLds) ? 2 * kTileLds : sizeof(QrRegLds);
+__global__ __launch_bounds__(RT) void k_band_step(float* A, int64_t n, int64_t a_batch, int mp, const float* VW_g,
+                                                  int64_t vw_batch, int ntiles, int npairs, int batch,
+                                                  float* panel, int mp_next, float* Vn, int64_t vstride, float* Tn,
+                                                  int64_t tstride, float* taus) {
+  static_assert(RT == 512, "two 256-thread tiles per workgroup");
+  __shared__ __align__(16) char raw[kBandStepLds];
+  const uint32_t L = blockIdx.x;
+  if (L < static_cast<uint32_t>(batch)) {
+    qr_reg_run(panel, mp_next, n, a_batch, 0, SBW, Vn, vstride, Tn, tstride, taus, SBW, 1, L,
+               *reinterpret_cast<QrRegLds*>(raw));
+    return;
+  }
+  uint32_t z, pair;
+  xcd_group(L - static_cast<uint32_t>(batch), static_cast<uint32_t>(npairs), static_cast<uint32_t>(batch), z, pair);
+  const int half = threadIdx.x >> 8;
+  const int ti = 2 * static_cast<int>(pair) + half;
+  const bool active = ti < ntiles;
+  int bi = 1, bj = 1;
+  if (active) {                                    // the triangle of tiles with bj >= 1, shifted by one
+    tri_tile(ti, bi, bj);
+    ++bi; ++bj;
+  }
+  float* base = reinterpret_cast<float*>(raw + half * kTileLds);
+  auto As = reinterpret_cast<float (*)[SY + 1]>(base);
+  auto Bs = reinterpret_cast<float (*)[SY + 1]>(base + 2 * SBW * (SY + 1));
+  syr2k_tile(A, n, a_batch, mp, VW_g, vw_batch, z, bi, bj, threadIdx.x & 255, active, As, Bs);
 }
 
 __global__ __launch_bounds__(256) void k_copy_cols(const float* in, int64_t ld_in, int64_t in_batch, float* out,
@@ -1465,6 +1518,7 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     }
     prof_add_work("band", batch * by, batch * fl);
   }
+  bool qr_done = false;   // panel p was factored inside the previous panel's band step
   for (int64_t p = 0; p < Lw.P; ++p) {
     const int64_t c = p * SBW, r = c + SBW, mp = n - r;
     float* panel = A + c * n + r;                  // column-major mp x 32 (ld n)
@@ -1474,9 +1528,10 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     // R into the panel's top rows: by the panel kernel when the panel is one
     // block, else as panel_top -= V_top (T^T (V^T panel))
     const bool r_in = mp <= panel_block_rows();
-    if ((e = panel_factor(panel, mp, n, nn, 0, SBW, batch, V, vs, T, ts, taus, SBW, pscr, s, r_in ? 1 : 0)) !=
-        hipSuccess)
+    if (!qr_done && (e = panel_factor(panel, mp, n, nn, 0, SBW, batch, V, vs, T, ts, taus, SBW, pscr, s,
+                                      r_in ? 1 : 0)) != hipSuccess)
       return e;
+    qr_done = false;
     if (!r_in) {
       if ((e = gemm(SBW, SBW, mp, V, plain(mp), plain(1), vs, panel, plain(1), plain(n), nn, S1, SBW, 1, 1024, 1.f,
                     0.f, ksplit_for(mp))) != hipSuccess) return e;
@@ -1493,9 +1548,25 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     if ((e = hipGetLastError()) != hipSuccess) return e;
     k_w_form<<<dim3(nbk, batch), 256, 0, s>>>(static_cast<int>(mp), V, vs, T, ts, VW, vwb, SP);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    k_syr2k<<<dim3(static_cast<unsigned>(nbk * (nbk + 1) / 2), batch), 256, 0, s>>>(A22, n, nn,
-                                                                                  static_cast<int>(mp), VW, vwb);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the next panel (the first block column of A22 below its first 32 rows)
+    // is factored beside the rest of this update when it is one register
+    // block: its block column first, then one launch for both
+    const int64_t mpn = mp - SBW;
+    if (p + 1 < Lw.P && mpn > 0 && mpn <= panel_block_rows()) {
+      k_syr2k<<<dim3(static_cast<unsigned>(nbk), batch), 256, 0, s>>>(A22, n, nn, static_cast<int>(mp), VW, vwb, 1);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      const int ntiles = nbk * (nbk - 1) / 2, npairs = (ntiles + 1) / 2;
+      const unsigned grid = static_cast<unsigned>(batch) * static_cast<unsigned>(1 + npairs);
+      k_band_step<<<grid, RT, 0, s>>>(A22, n, nn, static_cast<int>(mp), VW, vwb, ntiles, npairs, batch,
+                                      A + r * n + r + SBW, static_cast<int>(mpn), Vst + voff[p + 1], vs,
+                                      Tst + (p + 1) * 1024, ts, taus);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      qr_done = true;
+    } else {
+      k_syr2k<<<dim3(static_cast<unsigned>(nbk * (nbk + 1) / 2), batch), 256, 0, s>>>(A22, n, nn,
+                                                                                    static_cast<int>(mp), VW, vwb, 0);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   }
   if (band_done && (e = hipEventRecord(band_done, s)) != hipSuccess) return e;
