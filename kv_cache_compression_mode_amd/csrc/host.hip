@@ -607,7 +607,8 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   // (column-major, leading dimension n)
   // (dual: each column scaled by 1 / sqrt(lambda), so that X_(T) v / sqrt(lambda)
   // has unit norm and the recovered factor is nearly orthonormal)
-  ck(syev_top(w.G, n, batch, static_cast<int>(R), w.V, w.lam_tmp, w.syev, s, w.status, band_done, d.dual));
+  const SyevSide side{hip.lease(), hip.event(), hip.event()};
+  ck(syev_top(w.G, n, batch, static_cast<int>(R), w.V, w.lam_tmp, w.syev, s, w.status, band_done, d.dual, &side));
   if (d.dual) {
     // U' = X_(T) V_R Lambda^{-1/2} (T x R, column-major)
     GemmArgs gu = gemm0();

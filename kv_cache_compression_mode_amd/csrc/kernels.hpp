@@ -116,8 +116,16 @@ size_t syev_top_work_bytes(int64_t n, int R, int batch);
 // band_done, when given, is recorded on s once the band reduction is queued.
 // inv_sqrt_scale: eigenvector j comes out multiplied by 1 / sqrt(lam_j) where
 // lam_j > 0 (so X v_j / sqrt(lam_j) has unit norm for the Gram of X).
+// side, when given: a second stream of the caller and two events of its own,
+// on which the chase back-transformation's block factors are formed beside
+// the tridiagonal eigenpairs (they need the chase's reflectors only).
+struct SyevSide {
+  hipStream_t s;
+  hipEvent_t chase_done, tfac_done;
+};
 hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam, void* work, hipStream_t s,
-                    int* status, hipEvent_t band_done = nullptr, bool inv_sqrt_scale = false);
+                    int* status, hipEvent_t band_done = nullptr, bool inv_sqrt_scale = false,
+                    const SyevSide* side = nullptr);
 // Polls a bulge-chase wave makes before its wait gives up (default 2^22).
 void set_chase_spin_limit(int polls);
 hipError_t copy_cols(const float* in, int64_t ld_in, int64_t in_batch, float* out, int64_t ld_out,

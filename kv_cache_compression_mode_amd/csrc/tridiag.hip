@@ -1457,7 +1457,8 @@ std::atomic<int> g_chase_spin_limit{1 << 22};
 void set_chase_spin_limit(int polls) { g_chase_spin_limit.store(polls < 0 ? 0 : polls); }
 
 hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam_out, void* work,
-                    hipStream_t s, int* status, hipEvent_t band_done, bool inv_sqrt_scale) {
+                    hipStream_t s, int* status, hipEvent_t band_done, bool inv_sqrt_scale,
+                    const SyevSide* side) {
   if (n % SBW != 0 || n > 32768 || R < 1 || R > n || !status) return hipErrorInvalidValue;
   const SyevLayout Lw = syev_layout(n, R, batch);
   char* wb = static_cast<char*>(work);
@@ -1605,6 +1606,20 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
                     static_cast<double>(batch) * Lw.nref * 13.0 * SBW * SBW);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the block factors V T of the chase back-transformation need only the
+    // reflectors: on the side stream, beside the tridiagonal eigenpairs
+    if (side && Lw.ng > 0 && Lw.K0 > 0) {
+      if ((e = hipEventRecord(side->chase_done, s)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(side->s, side->chase_done, 0)) != hipSuccess) return e;
+      {
+        ProfScope ps("chase_back", side->s);
+        k_cb_tfac<<<dim3(static_cast<unsigned>(Lw.ng * Lw.K0), batch), 64, 0, side->s>>>(
+            Rf, Lw.nref * RFS, static_cast<int>(n), static_cast<int>(Lw.K0),
+            reinterpret_cast<float*>(wb + Lw.cbt_off), Lw.ng * Lw.K0 * CBR * SBW);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = hipEventRecord(side->tfac_done, side->s)) != hipSuccess) return e;
+    }
     int64_t tb = (n + 255) / 256;
     k_tri_out<<<dim3(static_cast<unsigned>(tb), batch), 256, 0, s>>>(Bw, n, dd, ee);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1644,9 +1659,13 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
       // read once; each 32-long reflector applied to R columns (4 b R flops)
       prof_add_work("chase_back", static_cast<double>(batch) * (2.0 * n * R * 4 + Lw.nref * RFS * 4.0),
                     static_cast<double>(batch) * Lw.nref * 4.0 * SBW * R);
-      k_cb_tfac<<<dim3(static_cast<unsigned>(ng * K0), batch), 64, 0, s>>>(Rf, Lw.nref * RFS, static_cast<int>(n),
-                                                                         K0, Tcb, tstr);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (side) {
+        if ((e = hipStreamWaitEvent(s, side->tfac_done, 0)) != hipSuccess) return e;
+      } else {
+        k_cb_tfac<<<dim3(static_cast<unsigned>(ng * K0), batch), 64, 0, s>>>(Rf, Lw.nref * RFS,
+                                                                           static_cast<int>(n), K0, Tcb, tstr);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
       const int nchunk = (R + 63) / 64;
       const int tmax = 2 * (ng - 1) + K0 - 1;
       // wavefront steps 2u and 2u + 1 per launch: groups g' with a block at either
