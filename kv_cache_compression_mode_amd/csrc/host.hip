@@ -212,6 +212,10 @@ struct AllocWS {
   int chunk;
   int nlanes;          // scratch sets, one per stream (chunks alternate between them)
   hipEvent_t band_done;  // recorded once the token eigensolver's band reduction is queued
+  // early read-back (exact path, one chunk): the token eigenvalues, feature
+  // spectra and ||X||^2 copied to this pinned host buffer ([batch][R] | [batch][D]
+  // | [batch]) as soon as they are final, early_done recorded after the copies
+  double* early; hipEvent_t eig_done, early_done;
 };
 
 struct Dims {
@@ -596,6 +600,16 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
     if (band_done) ck(hipStreamWaitEvent(fs, band_done, 0));
     feature_factor(d, batch, t0, w, fs);
     ck(launch_sumsq(xp, batch, d.H * T * D, xdt, w.frob2 + t0, fs));
+    if (w.early) {
+      // everything the allocation reads is final here: to the host while the
+      // token path forms its factors
+      ck(hipStreamWaitEvent(fs, w.eig_done, 0));
+      ck(hipMemcpyAsync(w.early, w.lam_tmp, sizeof(double) * batch * R, hipMemcpyDeviceToHost, fs));
+      ck(hipMemcpyAsync(w.early + batch * R, w.lamD + static_cast<size_t>(t0) * D, sizeof(double) * batch * D,
+                        hipMemcpyDeviceToHost, fs));
+      ck(hipMemcpyAsync(w.early + batch * (R + D), w.frob2 + t0, sizeof(double) * batch, hipMemcpyDeviceToHost, fs));
+      ck(hipEventRecord(w.early_done, fs));
+    }
     ff.done();
     ff.join();
   };
@@ -609,6 +623,7 @@ void analyze_exact(const Dims& d, int batch, int t0, const AllocWS& w, int xdt, 
   // has unit norm and the recovered factor is nearly orthonormal)
   const SyevSide side{hip.lease(), hip.event(), hip.event()};
   ck(syev_top(w.G, n, batch, static_cast<int>(R), w.V, w.lam_tmp, w.syev, s, w.status, band_done, d.dual, &side));
+  if (w.early) ck(hipEventRecord(w.eig_done, s));   // w.lam_tmp final (the eigensolver copies it in stream order)
   if (d.dual) {
     // U' = X_(T) V_R Lambda^{-1/2} (T x R, column-major)
     GemmArgs gu = gemm0();
@@ -1097,9 +1112,17 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, v
     const double* lt = reinterpret_cast<const double*>(host_of(w.lamT));
     const double* ld = reinterpret_cast<const double*>(host_of(w.lamD));
     const double* f2 = reinterpret_cast<const double*>(host_of(w.frob2));
+    // The exact path on one chunk reads its spectra back early and forms the
+    // plan on the host while the token factors are still being formed; the
+    // plan is kept when the final read-back holds the same values.
+    const bool early = !d.flash && R > 0 && nt <= w.chunk;
+    double* early_host = nullptr;
+    jolt_status early_rc = JOLT_EINVAL;
+    bool early_ok = false;
     // the whole analysis; returns the status word
     auto analyze_all = [&](bool householder) -> int {
       w.householder = w1.householder = householder;
+      w.early = nullptr;
       // chunks alternate between the lanes: lane 0 on s, lane 1 on a second
       // stream of this call, forked from s and joined back into it
       CallHip hip;
@@ -1113,6 +1136,12 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, v
       // a chunk on the second lane starts once the previous chunk's band
       // reduction is queued ahead of it, so that chunk's chase (one CU per
       // tensor) runs beside this chunk's matrix-core stages
+      if (early && !householder) {
+        early_host = static_cast<double*>(stage.pinned(sizeof(double) * nt * (R + d.D + 1)));
+        w.early = early_host;
+        w.eig_done = hip.event();
+        w.early_done = hip.event();
+      }
       std::vector<hipEvent_t> marks;
       if (ls)
         for (int c = 0; c * w.chunk < nt; ++c) marks.push_back(hip.event());
@@ -1135,13 +1164,27 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, v
       }
       ck(hipMemcpyAsync(back, w.lamT, rb, hipMemcpyDeviceToHost, s));
       stage.copied(back, s);
+      if (w.early) {
+        stage.copied(early_host, s);                 // s has joined the stream of the early copies
+        ck(hipEventSynchronize(w.early_done));
+        const double* ef = early_host + nt * (R + d.D);
+        bool fin = true;
+        for (int i = 0; i < nt; ++i) fin = fin && std::isfinite(ef[i]);
+        if (fin) {
+          early_rc = plan_dual(req, early_host, R, early_host + nt * R, ef, plan);
+          early_ok = true;
+        }
+        w.early = nullptr;
+      }
       ck(hipStreamSynchronize(s));
       int status = 0;
       std::memcpy(&status, host_of(w.status), sizeof(int));
       return status;
     };
     int status = analyze_all(false);
+    bool status_first_pass_only = true;
     if (status == 2) {
+      status_first_pass_only = false;
       // a CholeskyQR pass met a nearly dependent column (rank-deficient
       // input): the same analysis again with Householder QR throughout
       ck(hipMemsetAsync(w.frob2, 0, sizeof(double) * nt, s));
@@ -1155,6 +1198,13 @@ jolt_status jolt_allocate(const jolt_alloc_req* req, const void* const* x_dev, v
     if (plan->spectra_T && R > 0) std::memcpy(plan->spectra_T, lt, sizeof(double) * nt * R);
     if (plan->spectra_D) std::memcpy(plan->spectra_D, ld, sizeof(double) * nt * d.D);
     if (plan->frob2) std::memcpy(plan->frob2, f2, sizeof(double) * nt);
+    // the early plan stands when it was formed from exactly the values read back
+    // at the end (a repeated analysis or any difference forms it again)
+    if (early_ok && status_first_pass_only &&
+        std::memcmp(lt, early_host, sizeof(double) * nt * R) == 0 &&
+        std::memcmp(ld, early_host + nt * R, sizeof(double) * nt * d.D) == 0 &&
+        std::memcmp(f2, early_host + nt * (R + d.D), sizeof(double) * nt) == 0)
+      return early_rc;
     return plan_dual(req, lt, std::max(R, 1), ld, f2, plan);
   });
 }
