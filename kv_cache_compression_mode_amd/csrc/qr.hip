@@ -648,9 +648,20 @@ __global__ __launch_bounds__(256) void k_col_sign(const float* U, int64_t m, int
   const float* col = U + z * bstride + static_cast<int64_t>(perm[z * R + j]) * ld;
   float best = -1.f;
   int64_t bi = 0;
-  for (int64_t i = threadIdx.x; i < m; i += 256) {
-    const float v = fabsf(col[i]);
-    if (v > best) { best = v; bi = i; }
+  if (m % 4 == 0 && ld % 4 == 0 && bstride % 4 == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0) {
+    // 16-byte loads, each thread's four rows scanned in order
+    for (int64_t i = 4 * static_cast<int64_t>(threadIdx.x); i < m; i += 1024) {
+      const float4 q = *reinterpret_cast<const float4*>(col + i);
+      const float v[4] = {fabsf(q.x), fabsf(q.y), fabsf(q.z), fabsf(q.w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (v[e] > best) { best = v[e]; bi = i + e; }
+    }
+  } else {
+    for (int64_t i = threadIdx.x; i < m; i += 256) {
+      const float v = fabsf(col[i]);
+      if (v > best) { best = v; bi = i; }
+    }
   }
   __shared__ float bv[256];
   __shared__ int64_t bx[256];
@@ -672,28 +683,65 @@ __global__ __launch_bounds__(256) void k_col_sign(const float* U, int64_t m, int
 }
 
 // U_out[i][j] = sign[j] * U_cm[perm[j]][i] (row-major out); lam_out[j] = lam[perm[j]].
+// 128 rows x 32 columns per workgroup through an LDS transpose: 16-byte loads
+// along the source columns and 16-byte stores along the output rows where the
+// layouts are 16-byte aligned, single words otherwise.
 __global__ __launch_bounds__(256) void k_emit(const float* U, int64_t m, int64_t ld, int64_t bstride,
                                               const int* perm, const float* sign, int64_t R,
                                               const double* lam, int64_t lam_batch, float* out,
                                               int64_t ld_out, int64_t out_batch, double* lam_out,
                                               int64_t lam_out_batch) {
-  __shared__ float tile[32][33];
+  __shared__ float tile[32][132];                 // [column][row]
   const int64_t z = blockIdx.z;
-  const int64_t i0 = blockIdx.x * 32ll, j0 = blockIdx.y * 32ll;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
-  for (int jj = ty; jj < 32; jj += 8) {
-    const int64_t j = j0 + jj, i = i0 + tx;
-    float v = 0.f;
-    if (j < R && i < m) {
-      const int src = perm[z * R + j];
-      v = sign[z * R + j] * U[z * bstride + static_cast<int64_t>(src) * ld + i];
+  const int64_t i0 = blockIdx.x * 128ll, j0 = blockIdx.y * 32ll;
+  const int tid = threadIdx.x;
+  // loads: thread -> column jj = tid / 8, rows 4 (tid % 8) + 32 q
+  {
+    const int jj = tid >> 3;
+    const int64_t j = j0 + jj;
+    const bool vin = ld % 4 == 0 && bstride % 4 == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0;
+    const float* src = j < R ? U + z * bstride + static_cast<int64_t>(perm[z * R + j]) * ld : nullptr;
+    const float sg = j < R ? sign[z * R + j] : 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int il = 4 * (tid & 7) + 32 * q;
+      const int64_t i = i0 + il;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (src) {
+        if (vin && i + 3 < m) {
+          const float4 x = *reinterpret_cast<const float4*>(src + i);
+          v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = i + e < m ? src[i + e] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[jj][il + e] = sg * v[e];
     }
-    tile[jj][tx] = v;
   }
   __syncthreads();
-  for (int ii = ty; ii < 32; ii += 8) {
-    const int64_t i = i0 + ii, j = j0 + tx;
-    if (i < m && j < R) out[z * out_batch + i * ld_out + j] = tile[tx][ii];
+  // stores: thread -> row ii = tid / 2, columns 16 (tid % 2) .. + 15
+  {
+    const int ii = tid >> 1;
+    const int64_t i = i0 + ii;
+    if (i < m) {
+      float* orow = out + z * out_batch + i * ld_out;
+      const bool vout = ld_out % 4 == 0 && out_batch % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int jl = 16 * (tid & 1) + 4 * q;
+        const int64_t jg = j0 + jl;
+        const float v[4] = {tile[jl][ii], tile[jl + 1][ii], tile[jl + 2][ii], tile[jl + 3][ii]};
+        if (vout && jg + 3 < R) {
+          *reinterpret_cast<float4*>(orow + jg) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (jg + e < R) orow[jg + e] = v[e];
+        }
+      }
+    }
   }
   if (blockIdx.x == 0 && threadIdx.x < 32) {
     const int64_t j = j0 + threadIdx.x;
@@ -1102,7 +1150,7 @@ hipError_t finalize_factor_ws(const float* U_cm, int64_t m, int64_t R, int64_t l
                               int* perm, float* sign, hipStream_t s) {
   k_sort_desc<<<batch, 1024, 0, s>>>(lam, R, lam_batch, perm);
   k_col_sign<<<dim3(R, batch), 256, 0, s>>>(U_cm, m, ld_cm, cm_batch, perm, R, sign);
-  dim3 grid((m + 31) / 32, (R + 31) / 32, batch);
+  dim3 grid((m + 127) / 128, (R + 31) / 32, batch);
   k_emit<<<grid, 256, 0, s>>>(U_cm, m, ld_cm, cm_batch, perm, sign, R, lam, lam_batch, U_out, ld_out,
                               out_batch, lam_out, lam_out_batch);
   return hipGetLastError();
