@@ -91,6 +91,7 @@ struct ChaseLds {
   float tile[2][SBW * TLD];       // ping-pong: carried left block / staged below block
   float x[SBW];                   // the column annihilated by the next step
 };
+constexpr int kChaseLdsClaim = 160 * 1024 - 1024;   // a CU's LDS less the static part
 struct ChaseStep {
   int j, s, r0, L, r1, hi;
   bool last;
@@ -1582,13 +1583,18 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     const int nw = K0 > 32 ? 16 : 8;
     int S = static_cast<int>((K0 + nw - 1) / nw);
     if (S < 4) S = 4;
-    const size_t lds = static_cast<size_t>(nw) * sizeof(ChaseLds);
+    // The chase asks for all of a CU's LDS (its waves use nw * sizeof(ChaseLds)
+    // of it) so that no other workgroup is placed beside it: its ticks are
+    // bound by the CU's memory pipeline, which a neighbour on the CU (the
+    // feature path runs beside the token chase) would share.
+    const size_t lds = kChaseLdsClaim;
+    static_assert(16 * sizeof(ChaseLds) <= kChaseLdsClaim, "the chase's tiles fit its claim");
     static const hipError_t attr = [] {   // once per process (thread-safe initialization)
       hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chase<8>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 16 * sizeof(ChaseLds));
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kChaseLdsClaim);
       if (r == hipSuccess)
         r = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chase<16>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 16 * sizeof(ChaseLds));
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kChaseLdsClaim);
       return r;
     }();
     if (attr != hipSuccess) return attr;
