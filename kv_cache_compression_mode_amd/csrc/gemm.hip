@@ -314,7 +314,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(GemmArgs g) {
 //            four k per thread) on the way to LDS.
 // Both operands fp32 (split_f32): all four products hi hi + lo hi + hi lo +
 // lo lo (lo is about 2^-8 of x, so lo lo is a 2^-16 term, and one of a
-// fixed sign in a Gram's diagonal: it is kept).
+// fixed sign in a Gram's diagonal: it is kept), or (split_f32 = 3, a product
+// that forms a small correction) the first three.
 // The next K tile's global loads are issued before the current tile's MFMAs.
 constexpr int XT = 128, XK = 64, XKP = XK + 8;
 enum { kOpBfK = 0, kOpBfM = 1, kOpF32K = 2, kOpF32M = 3 };
@@ -575,7 +576,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_x(GemmArgs g) {
           if constexpr (AS) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], b[j], acc[i][j], 0, 0, 0);
           if constexpr (BS) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bl[j], acc[i][j], 0, 0, 0);
           if constexpr (AS && BS)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bl[j], acc[i][j], 0, 0, 0);
+            if (g.split_f32 != 3)                  // 3: lo x lo left out (a small correction's product)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bl[j], acc[i][j], 0, 0, 0);
           if constexpr (NP == 3) {
             const int ra_r = wm + 32 * i + r, rb_r = wn + 32 * j + r;
             const bf16x8 a3 = *reinterpret_cast<const bf16x8*>(&As[NP - 1][ra_r][xswz(ra_r, ch) * 8]);

@@ -57,8 +57,9 @@ struct GemmArgs {
   int ptr_align16;
   // both operands fp32 may run on bf16 matrix cores as hi + lo planes (1:
   // four products, about 2^-17 relative error per term instead of fp32's
-  // 2^-24) or, both k contiguous, as three planes (2: six products, about
-  // 2^-24)
+  // 2^-24; 3: the same without lo x lo, 2^-16, for products whose result is a
+  // small correction) or, both k contiguous, as three planes (2: six
+  // products, about 2^-24)
   int split_f32;
   // triangular operands (matrix-core path): A(m, k) = 0 for k > m (a_lower),
   // B(k, n) = 0 for k > n (b_upper); a tile's K range then ends at its last

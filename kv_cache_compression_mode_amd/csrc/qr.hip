@@ -1129,7 +1129,8 @@ hipError_t cholesky_qr(const float* U, float* Q, int64_t m, int64_t k, int64_t l
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // Q = U + U (L^{-T} - I), B(j, n) = (L^{-1} - I)[n][j]: U's fp32 values pass
   // through exactly (the identity's term, read in the product's epilogue) and
-  // only the small correction carries the split products' rounding
+  // only the small correction carries the split products' rounding (lo x lo,
+  // 2^-18 of a correction under 1e-2, left out)
   GemmArgs q{};
   q.alpha = 1.f;
   q.beta = 1.f;
@@ -1139,7 +1140,7 @@ hipError_t cholesky_qr(const float* U, float* Q, int64_t m, int64_t k, int64_t l
   q.A = U; q.am = plain(1); q.ak = plain(ld); q.a_batch = bstride;
   q.B = Li; q.bk = plain(1); q.bn = plain(k); q.b_batch = k * k;
   q.C = Q; q.c_m = 1; q.c_n = ld; q.c_batch = bstride;
-  q.split_f32 = 1;
+  q.split_f32 = 3;
   q.b_upper = 1;
   return launch_gemm(q, batch, s, "cholqr_gemm");
 }
