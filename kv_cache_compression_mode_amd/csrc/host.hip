@@ -1409,21 +1409,7 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
       stage.copied(img, s);
     }
     auto dp = [&](size_t slot) { return dptr + slot; };
-    // the groups' factor casts, cores and W planes are independent (each has its
-    // own workspace): groups past the first run on streams of this call, forked
-    // after the upload and joined before the residual kernel
-    const size_t ng = L.groups.size();
-    std::vector<hipStream_t> gstream(ng, s);
-    if (ng > 1) {
-      const hipEvent_t fork = stage.event();
-      ck(hipEventRecord(fork, s));
-      for (size_t g = 1; g < ng; ++g) {
-        gstream[g] = stage.lease();
-        ck(hipStreamWaitEvent(gstream[g], fork, 0));
-      }
-    }
-    for (size_t g = 0; g < ng; ++g) {
-      const hipStream_t s = gstream[g];
+    for (size_t g = 0; g < L.groups.size(); ++g) {
       const int b0 = L.groups[g].first, e0 = L.groups[g].second, m = e0 - b0;
       const int i0 = L.order[b0];
       const jolt_choice c = choices[i0];
@@ -1474,11 +1460,6 @@ jolt_status jolt_encode_many(int32_t n, const jolt_shape* shape, const jolt_choi
                       reinterpret_cast<const uint16_t* const*>(dp(q.g3b)), nullptr, nullptr,
                       reinterpret_cast<uint16_t*>(ws + L.w_off[g]), 2 * H * D * rTp, m, static_cast<int>(H),
                       static_cast<int>(rT), static_cast<int>(rD), static_cast<int>(rTp), s));
-    }
-    for (size_t g = 1; g < ng; ++g) {
-      const hipEvent_t join = stage.event();
-      ck(hipEventRecord(join, gstream[g]));
-      ck(hipStreamWaitEvent(s, join, 0));
     }
     if (prof_enabled("encode_residual")) {
       // the residual kernel reads X and U~_T and writes codes and scales (the

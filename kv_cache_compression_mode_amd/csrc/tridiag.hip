@@ -1583,11 +1583,13 @@ hipError_t syev_top(float* A, int64_t n, int batch, int R, float* Z, double* lam
     const int nw = K0 > 32 ? 16 : 8;
     int S = static_cast<int>((K0 + nw - 1) / nw);
     if (S < 4) S = 4;
-    // The chase asks for all of a CU's LDS (its waves use nw * sizeof(ChaseLds)
-    // of it) so that no other workgroup is placed beside it: its ticks are
-    // bound by the CU's memory pipeline, which a neighbour on the CU (the
-    // feature path runs beside the token chase) would share.
-    const size_t lds = kChaseLdsClaim;
+    // With 8 waves the chase asks for all of a CU's LDS (its waves use
+    // 8 * sizeof(ChaseLds) of it) so that no other workgroup is placed beside
+    // it: its ticks are bound by the CU's memory pipeline, which a neighbour on
+    // the CU (the feature path runs beside the token chase) would share.  The
+    // 16-wave chase of the larger matrices runs beside the other lane's
+    // stages, which need those CUs (claiming them cost 20% of that step).
+    const size_t lds = nw == 8 ? static_cast<size_t>(kChaseLdsClaim) : static_cast<size_t>(nw) * sizeof(ChaseLds);
     static_assert(16 * sizeof(ChaseLds) <= kChaseLdsClaim, "the chase's tiles fit its claim");
     static const hipError_t attr = [] {   // once per process (thread-safe initialization)
       hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void*>(k_chase<8>),
