@@ -344,14 +344,6 @@ GemmArgs gemm0() {
   return g;
 }
 
-bool trace_on() {
-  static const bool on = [] {
-    const char* e = std::getenv("JOLT_TRACE");
-    return e && e[0] && e[0] != '0';
-  }();
-  return on;
-}
-
 // Host-side HIP objects of one call.  Auxiliary streams (non-blocking,
 // default priority) are leased from a per-device pool and handed back when the
 // call ends, so concurrent calls never share one; events are created for the
