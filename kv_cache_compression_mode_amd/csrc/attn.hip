@@ -92,7 +92,7 @@ __device__ __forceinline__ void reconstruct(const DecRec& R, int64_t h, int64_t 
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const int64_t t = t0 + 32 * rt + r;
-        a[sub][rt] = t < T ? load8(R.Ut + t * R.r_T, kk, R.r_T, ua) : zero8();
+        a[sub][rt] = t < T ? load8(R.Ut() + t * R.r_T, kk, R.r_T, ua) : zero8();
       }
     }
   };
@@ -102,7 +102,7 @@ __device__ __forceinline__ void reconstruct(const DecRec& R, int64_t h, int64_t 
     for (int sub = 0; sub < 2; ++sub) {
       const int64_t o = ((h * 4 + wave) * nks + 2 * st + sub) * 512 + lane * 8;
       wh[sub] = ldg16(R.Whi + o);
-      wlo[sub] = ldg16(R.Wlo + o);
+      wlo[sub] = ldg16(R.Wlo() + o);
     }
   };
   auto store_w = [&](int buf) {
@@ -159,8 +159,8 @@ __device__ __forceinline__ void reconstruct(const DecRec& R, int64_t h, int64_t 
       uint32_t sw = 0u, w0 = 0u, w1 = 0u;       // rows past T: m16 = s16 = 0 gives y = 0
       if (t < T) {
         const int64_t gi = (h * T + t) * 4 + g;
-        sw = ldg32(R.scales + gi);
-        const uint32_t* cw = R.codes + gi * bits;
+        sw = ldg32(R.scales() + gi);
+        const uint32_t* cw = R.codes() + gi * bits;
         w0 = ldg32(cw + (bitpos >> 5));
         if ((bitpos & 31) + 8 * bits > 32) w1 = ldg32(cw + (bitpos >> 5) + 1);
       }

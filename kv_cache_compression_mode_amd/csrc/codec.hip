@@ -492,11 +492,11 @@ __global__ __launch_bounds__(256) void k_make_w(DecBatch b) {
   const bool ga = (R.r_D % 8) == 0;
   for (int j0 = 0; j0 < R.r_D; j0 += 16) {
     const int jj = j0 + 8 * half;
-    const bf16x8 a = arow ? load8_bf16(R.G + (static_cast<int64_t>(h) * R.r_T + k) * R.r_D, jj, R.r_D, ga)
+    const bf16x8 a = arow ? load8_bf16(R.G() + (static_cast<int64_t>(h) * R.r_T + k) * R.r_D, jj, R.r_D, ga)
                           : zero8();
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      const bf16x8 bb = load8_bf16(R.Ud + static_cast<int64_t>(32 * ct + r) * R.r_D, jj, R.r_D, ga);
+      const bf16x8 bb = load8_bf16(R.Ud() + static_cast<int64_t>(32 * ct + r) * R.r_D, jj, R.r_D, ga);
       acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc[ct], 0, 0, 0);
     }
   }
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(256) void k_make_w(DecBatch b) {
       const int64_t off = ((static_cast<int64_t>(h) * 4 + ct) * (R.r_Tp / 16) + (k >> 4)) * 512 +
                           (((k >> 3) & 1) * 32 + r) * 8 + (k & 7);
       R.Whi[off] = hi;
-      R.Wlo[off] = lo;
+      R.Wlo()[off] = lo;
     }
   }
 }
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const int64_t t = t0 + 32 * rt + r;
-        a[sub][rt] = t < b.T ? load8_bf16(R.Ut + t * R.r_T, kk, R.r_T, ua) : zero8();
+        a[sub][rt] = t < b.T ? load8_bf16(R.Ut() + t * R.r_T, kk, R.r_T, ua) : zero8();
       }
     }
   };
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
     for (int sub = 0; sub < 2; ++sub) {
       const int64_t o = ((h * 4 + wave) * nks + 2 * st + sub) * 512 + lane * 8;   // fragment order
       wh[sub] = ldg16(R.Whi + o);
-      wlo[sub] = ldg16(R.Wlo + o);
+      wlo[sub] = ldg16(R.Wlo() + o);
     }
   };
   auto store_w = [&](int buf) {
@@ -628,8 +628,8 @@ __global__ __launch_bounds__(256, 2) void k_decode(DecBatch b) {
       sw[rt] = 0u; w0[rt] = 0u; w1[rt] = 0u;
       if (t < b.T) {
         const int64_t gi = (h * b.T + t) * 4 + g;
-        sw[rt] = ldg32(R.scales + gi);
-        const uint32_t* cw = R.codes + gi * bits;
+        sw[rt] = ldg32(R.scales() + gi);
+        const uint32_t* cw = R.codes() + gi * bits;
         w0[rt] = ldg32(cw + (bitpos >> 5));
         if ((bitpos & 31) + 8 * bits > 32) w1[rt] = ldg32(cw + (bitpos >> 5) + 1);
       }

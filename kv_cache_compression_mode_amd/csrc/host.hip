@@ -797,19 +797,17 @@ size_t decode_w_bytes(int64_t H, int64_t D, jolt_choice c) {
 DecRec dec_rec(int64_t H, int64_t T, int64_t D, jolt_choice c, const void* blob_dev, void* out, char* wsp,
                int wtile0) {
   const BlobLayout L = blob_layout(H, T, D, c);
-  const char* blob = static_cast<const char*>(blob_dev);
   DecRec R{};
-  R.Ut = reinterpret_cast<const uint16_t*>(blob + L.ut);
-  R.Ud = reinterpret_cast<const uint16_t*>(blob + L.ud);
-  R.G = reinterpret_cast<const uint16_t*>(blob + L.g);
-  R.scales = reinterpret_cast<const uint32_t*>(blob + L.sc);
-  R.codes = reinterpret_cast<const uint32_t*>(blob + L.cd);
+  R.blob = static_cast<const char*>(blob_dev);
   R.out = out;
+  R.H = static_cast<int32_t>(H); R.T = static_cast<int32_t>(T);
   R.r_T = c.r_T; R.r_D = c.r_D; R.bits = c.bits;
   R.r_Tp = static_cast<int32_t>(rtp_of(c.r_T));
-  const size_t wneed = decode_w_bytes(H, D, c);
   R.Whi = reinterpret_cast<uint16_t*>(wsp);
-  R.Wlo = reinterpret_cast<uint16_t*>(wsp + wneed / 2);
+  // the device addresses the sections from the record's base: the same layout
+  if (D != 128 || L.ut != 256 || L.ud != R.off_ud() || L.g != R.off_g() || L.sc != R.off_sc() ||
+      L.cd != R.off_cd() || reinterpret_cast<char*>(R.Wlo()) != wsp + decode_w_bytes(H, D, c) / 2)
+    throw HipFail{};
   R.wtile0 = wtile0;
   return R;
 }

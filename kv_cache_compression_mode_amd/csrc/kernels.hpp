@@ -189,19 +189,32 @@ hipError_t launch_encode_residual(const EncodeArgs& a, hipStream_t s);
 // n tensors of one shape (H, T), arguments in a device array
 hipError_t launch_encode_residual_many(const EncodeArgs* list_dev, int n, int64_t H, int64_t T, int x_dtype,
                                        hipStream_t s);
-// Batched decode: up to kDecBatch records of one shape (H, T, D = 128).
-constexpr int kDecBatch = 32;
+// Batched decode: up to kDecBatch records of one shape (H, T, D = 128), all
+// in one launch (the batch travels as the kernel argument, under its 4 KB
+// limit).  A record is addressed by its base: its sections follow the record
+// layout (bf16 U~_T [T][r_T] at byte 256, then U~_D [D][r_D], the core
+// [H][r_T][r_D], the scale words [H][T][4] and the code words [H][T][4][bits],
+// each section starting 256-aligned), which the host checks against the
+// library's layout when it fills the record.
+constexpr int kDecBatch = 64;
 struct DecRec {
-  const uint16_t* Ut;      // bf16 [T][r_T]
-  const uint16_t* Ud;      // bf16 [D][r_D]
-  const uint16_t* G;       // bf16 [H][r_T][r_D]
-  const uint32_t* scales;  // [H][T][4] words (offset | step << 16)
-  const uint32_t* codes;   // [H][T][4][bits] words
-  uint16_t* Whi;           // workspace: bf16 [H][D/32][r_Tp/16][64][8], fragment order
-  uint16_t* Wlo;
+  const char* blob;
   void* out;               // [H][T][D]
+  uint16_t* Whi;           // workspace: bf16 [H][D/32][r_Tp/16][64][8], fragment order; the lo plane follows
+  int32_t H, T;
   int32_t r_T, r_D, r_Tp, bits;
   int32_t wtile0;          // first W tile of this record
+  __host__ __device__ static size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+  __host__ __device__ size_t off_ud() const { return 256 + up256(2ull * T * r_T); }
+  __host__ __device__ size_t off_g() const { return off_ud() + up256(2ull * 128 * r_D); }
+  __host__ __device__ size_t off_sc() const { return off_g() + up256(2ull * H * r_T * r_D); }
+  __host__ __device__ size_t off_cd() const { return off_sc() + up256(4ull * (static_cast<size_t>(H) * T * 128 / 32)); }
+  __host__ __device__ const uint16_t* Ut() const { return reinterpret_cast<const uint16_t*>(blob + 256); }
+  __host__ __device__ const uint16_t* Ud() const { return reinterpret_cast<const uint16_t*>(blob + off_ud()); }
+  __host__ __device__ const uint16_t* G() const { return reinterpret_cast<const uint16_t*>(blob + off_g()); }
+  __host__ __device__ const uint32_t* scales() const { return reinterpret_cast<const uint32_t*>(blob + off_sc()); }
+  __host__ __device__ const uint32_t* codes() const { return reinterpret_cast<const uint32_t*>(blob + off_cd()); }
+  __host__ __device__ uint16_t* Wlo() const { return Whi + up256(2ull * H * 128 * r_Tp) / 2; }
 };
 struct DecBatch {
   DecRec rec[kDecBatch];
@@ -209,6 +222,7 @@ struct DecBatch {
   int32_t out16;            // every record's out is 16-byte aligned
   const uint16_t* Qt16;    // bf16 [D][D], Qt16[c][d] = Q[d][c]
 };
+static_assert(sizeof(DecBatch) <= 4000, "a decode batch is one kernel argument");
 hipError_t launch_decode_batch(const DecBatch& b, hipStream_t s);
 // The W planes of the batch's records alone (the decode's prologue).
 hipError_t launch_make_w(const DecBatch& b, hipStream_t s);
