@@ -6,8 +6,9 @@
  * Joint Tucker and JL-Residual Allocation for LLMs" (arXiv 2607.12550v2),
  * abstract: each layer's K or V cache is a third-order tensor over heads,
  * tokens and features; a partial Tucker decomposition compresses only the
- * token and feature axes; a random orthogonal rotation followed by low-bit
- * quantization restores the energy the truncation drops; one Lagrangian dual
+ * token and feature axes; the energy the truncation drops comes back as a
+ * residual that is rotated by a seeded random orthogonal matrix and then
+ * quantized to few bits; one Lagrangian dual
  * allocates Tucker ranks and residual bit-widths per layer group, separately
  * for keys and values, under one byte budget; FlashJoLT computes the factors
  * with a randomized SVD.

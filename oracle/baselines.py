@@ -5,8 +5,8 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
 Source: JoLT abstract (arXiv 2607.12550v2), the sentences naming the two
 families the method is set against (per-head or cross-layer low-rank
 factorizations, and per-entry quantization); news article on JoLT,
-paragraph 3 (JoLT's error at 2x is an order of magnitude below cross-layer
-SVD and 4-bit quantization).  The pages give neither baseline's definition;
+paragraph 3 (at 2x, JoLT's error is about ten times smaller than that of
+cross-layer SVD or of 4-bit quantization).  The pages give neither baseline's definition;
 these are the readings:
 
 * b-bit quantization: the codec's own residual path with no Tucker part,

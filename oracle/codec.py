@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
 
 Source: JoLT abstract (arXiv 2607.12550v2): partial Tucker on the token and
 feature axes, then a rotated low-bit residual restoring the energy that
-truncation discards; a single Lagrangian dual over ranks and bits per layer
+truncation discards; one Lagrangian-dual allocation of ranks and bits per layer
 group, K and V separate, under one byte budget; quality reported as relative
 Frobenius reconstruction error.
 
